@@ -1,0 +1,174 @@
+"""Pins of the BITNET_PLANES lm_head oracle ("[bitnet] T2: lm_head via
+BITNET_PLANES weight format (WeightForm) + two-stage top-k decode").
+
+What pins it: a NumPy brute force of the exact eight-plane score; the
+bound invariant |S' - S1'| <= B' on every row and the page's truncation
+figure; exactness of the two-stage result whenever the cap does not engage
+(the page says the bound-driven rescoring equals the exact top-k);
+special cases: an exactly-ternary source (planes 1..7 zero, which plane 0
+captures losslessly), a single plane (which reduces to the ternary GEMV with
+scale 3^(7-p)*rowScale), all-zero planes (ties resolved by lowest index).
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_decode_gemv_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+POW3 = np.array([3 ** (7 - p) for p in range(8)], np.int64)
+
+
+def numpy_scores(trits, rs, h):
+    dots = np.einsum("vpk,k->vp", trits.astype(np.int64), h.astype(np.int64))
+    return rs.astype(np.int64) * (dots @ POW3)
+
+
+def numpy_topk(scores, k):
+    order = np.lexsort((np.arange(scores.size), -scores))
+    return order[:k].astype(np.int32), scores[order[:k]]
+
+
+def small_case(V, K, seed):
+    trits, rs, h = synth.lmhead(V, K, seed)
+    return trits, rs, h
+
+
+@pytest.mark.parametrize("V,K,k,seed", [(300, 128, 40, 0), (257, 256, 7, 1), (64, 128, 1, 2),
+                                         (100, 128, 100, 3)])
+def test_brute_matches_numpy(V, K, k, seed):
+    trits, rs, h = small_case(V, K, seed)
+    idx, sc, allsc = oracle.lmhead_brute(trits, rs, h, k, all_scores=True)
+    want = numpy_scores(trits, rs, h)
+    assert (allsc == want).all()
+    wi, ws = numpy_topk(want, k)
+    assert (idx == wi).all() and (sc == ws).all()
+
+
+@pytest.mark.parametrize("V,K,seed", [(300, 128, 0), (290, 256, 5)])
+def test_bound_invariant_and_candidate_superset(V, K, seed):
+    trits, rs, h = small_case(V, K, seed)
+    s1, b = oracle.lmhead_stage1(trits, rs, h)
+    exact = numpy_scores(trits, rs, h)
+    assert (np.abs(exact - s1) <= b).all()
+    habs = int(np.abs(h.astype(np.int64)).sum())
+    assert (b == 40 * np.abs(rs.astype(np.int64)) * habs).all()
+    for k in (1, 10, 40):
+        lower = np.sort(s1 - b)[::-1]
+        lk = lower[k - 1]
+        cand = np.nonzero(s1 + b >= lk)[0]
+        ti, _ = numpy_topk(exact, k)
+        assert len(cand) >= k
+        assert set(ti.tolist()) <= set(cand.tolist())
+        idx, sc, n, capped = oracle.lmhead_two_stage(trits, rs, h, k, cap=V)
+        assert n == len(cand) and capped == 0
+        assert (idx == ti).all() and (sc == exact[ti]).all()
+
+
+def test_page_truncation_figure():
+    vals = {}
+    for line in open(os.path.join(GOLDEN, "planes_bound.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            key, v = line.split()
+            vals[key] = float(v)
+    tail = Fraction(int(vals["tail_numerator"]), int(vals["tail_denominator"]))
+    finite = Fraction(int(vals["finite_numerator"]), int(vals["finite_denominator"]))
+    assert sum(Fraction(1, 3 ** p) for p in range(4, 8)) == finite
+    assert abs(float(tail) * 100 - vals["page_truncation_percent"]) < 0.005
+    assert finite < tail
+    # the oracle's bound, in units of 3^-7 * |rowScale| * sum|h|, is exactly 40/2187
+    trits, rs, h = small_case(80, 128, 9)
+    _, b = oracle.lmhead_stage1(trits, rs, h)
+    habs = int(np.abs(h.astype(np.int64)).sum())
+    for r in range(80):
+        assert Fraction(int(b[r]), 3 ** 7 * int(rs[r]) * habs) == finite
+
+
+def test_planted_peaks_exact_branch():
+    trits, rs, h, peaks = synth.lmhead_planted(600, 256, 4, n_peaks=16)
+    idx, sc, n, capped = oracle.lmhead_two_stage(trits, rs, h, 10, cap=200)
+    bi, bs = oracle.lmhead_brute(trits, rs, h, 10)
+    assert capped == 0 and n <= 200
+    assert (idx == bi).all() and (sc == bs).all()
+    assert set(idx.tolist()) <= set(peaks.tolist())
+
+
+def test_exactly_ternary_source():
+    """Planes 1..7 zero: plane 0 carries the codes, stage 1 is already exact."""
+    trits, rs, h = small_case(200, 128, 6)
+    trits[:, 1:, :] = 0
+    s1, _ = oracle.lmhead_stage1(trits, rs, h)
+    assert (s1 == numpy_scores(trits, rs, h)).all()
+    idx, sc, n, capped = oracle.lmhead_two_stage(trits, rs, h, 20, cap=200)
+    bi, bs = oracle.lmhead_brute(trits, rs, h, 20)
+    assert (idx == bi).all() and (sc == bs).all()
+
+
+def test_single_plane_is_the_ternary_gemv():
+    trits, rs, h = small_case(130, 256, 7)
+    trits[:, 1:, :] = 0
+    rs = (np.arange(130) % 14 + 1).astype(np.int32)   # 2187*rs fits int16
+    _, _, allsc = oracle.lmhead_brute(trits, rs, h, 5, all_scores=True)
+    scale = np.repeat((2187 * rs).astype(np.int16)[:, None], 2, axis=1)
+    y = oracle.ternary_gemv_def(trits[:, 0, :], scale, h)
+    assert (allsc == y).all()
+
+
+def test_all_zero_planes_tie_break():
+    trits = np.zeros((250, 8, 128), np.int8)
+    _, rs, h = small_case(250, 128, 8)
+    idx, sc, n, capped = oracle.lmhead_two_stage(trits, rs, h, 40, cap=200)
+    assert (idx == np.arange(40)).all() and not sc.any()
+    assert n == 250 and capped == 1
+    bi, bs = oracle.lmhead_brute(trits, rs, h, 40)
+    assert (bi == np.arange(40)).all()
+
+
+def test_equal_rows_tie_break_lowest_index():
+    trits, rs, h = small_case(50, 128, 10)
+    trits[30] = trits[7]
+    rs[30] = rs[7]
+    trits[7, 0] = np.sign(h)          # make row 7 (and 30) the best
+    trits[30, 0] = np.sign(h)
+    idx, sc, _, _ = oracle.lmhead_two_stage(trits, rs, h, 3, cap=50)
+    assert idx[0] == 7 and idx[1] == 30 and sc[0] == sc[1]
+
+
+def test_cap_branch_keeps_top_stage1_rows():
+    trits, rs, h = small_case(400, 128, 11)
+    k, cap = 5, 8
+    s1, b = oracle.lmhead_stage1(trits, rs, h)
+    idx, sc, n, capped = oracle.lmhead_two_stage(trits, rs, h, k, cap)
+    lk = np.sort(s1 - b)[::-1][k - 1]
+    cand = np.nonzero(s1 + b >= lk)[0]
+    assert n == len(cand) and n > cap and capped == 1
+    order = np.lexsort((cand, -s1[cand]))
+    kept = cand[order[:cap]]
+    exact = numpy_scores(trits, rs, h)
+    want = kept[np.lexsort((kept, -exact[kept]))][:k]
+    assert (idx == want).all() and (sc == exact[want]).all()
+
+
+def test_planes_pack_layout_positions():
+    V, K = 65, 256
+    trits = np.zeros((V, 8, K), np.int8)
+    trits[0, 0, 0] = 1        # planes03 block (0,0) plane 0 nz byte 0 bit 0
+    trits[1, 3, 9] = -1       # block (0,0) plane 3: 3*2048 + 16 + 1 (nz), +1024 (neg), bit 1
+    trits[64, 2, 130] = 1     # tile 1, g 1: block 3: 3*8192 + 2*2048 + 0*16 + 0 bit 2
+    trits[2, 4, 0] = 1        # planes47 row 2: 2*256 + 0 + 0, bit 0
+    trits[3, 7, 255] = -1     # row 3: 3*256 + 128 + 96 + 15 (nz), +16 (neg), bit 7
+    p03, p47 = oracle.planes_pack(trits)
+    assert p03.size == 128 * K and p47.size == V * K
+    want03 = {0: 0x01, 3 * 2048 + 16 + 1: 0x02, 3 * 2048 + 1024 + 16 + 1: 0x02,
+              3 * 8192 + 2 * 2048: 0x04}
+    want47 = {2 * 256: 0x01, 3 * 256 + 128 + 96 + 15: 0x80, 3 * 256 + 128 + 96 + 16 + 15: 0x80}
+    assert sorted(np.nonzero(p03)[0].tolist()) == sorted(want03)
+    assert sorted(np.nonzero(p47)[0].tolist()) == sorted(want47)
+    for off, v in want03.items():
+        assert p03[off] == v
+    for off, v in want47.items():
+        assert p47[off] == v
