@@ -1,0 +1,67 @@
+"""Build the C-ABI shared library ``libbitstate.so`` for gfx950 (in-tree).
+
+    python -m bit_decode_gemv_amd.build
+
+compiles every source under ``csrc/`` with hipcc into
+``bit_decode_gemv_amd/libbitstate.so``.  The HIP sources are built with packed
+FP32 instructions disabled (the device pass accepts the feature; the host
+pass warns that it does not know it, which is harmless).
+"""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libbitstate.so")
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC]
+HIP_FLAGS = ["-x", "hip", "--offload-arch=" + ARCH, "-Xclang", "-target-feature",
+             "-Xclang", "-packed-fp32-ops"]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(
+        glob.glob(os.path.join(CSRC, "*.cpp")))
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every source, link libbitstate.so; returns its path."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        cmd = [HIPCC] + COMMON_FLAGS
+        if src.endswith(".hip"):
+            cmd += HIP_FLAGS
+        cmd += ["-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed for %s:\n%s" % (src, errs))
+        if errs.strip() and verbose:
+            print(errs, file=sys.stderr)
+        objs.append(obj)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH] + objs + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n%s" % res.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build_library(verbose="-v" in sys.argv))

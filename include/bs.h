@@ -1,0 +1,227 @@
+/*
+ * bs.h -- C ABI of the MI355X (gfx950) ternary decode-GEMV library.
+ *
+ * Pages cited (by title and section):
+ *   [BS] "BitState / HSDR PoC Technical Brief - v0.5"
+ *   [T2] "[bitnet] T2: lm_head via BITNET_PLANES weight format (WeightForm)
+ *         + two-stage top-k decode"
+ *   [IE] "A standalone deterministic integer inference engine for
+ *         BitNet-style LLMs, with Ollama interop"
+ *
+ * Conventions
+ *   - Every entry point returns int32_t status: BS_OK (0) or a negative
+ *     BS_E_* code.  Nothing else crosses the ABI; no exceptions.
+ *   - Arguments are validated on the host before any HIP call.  A failed
+ *     validation leaves every output untouched and enqueues nothing.
+ *   - Codec functions (bs_*pack*, bs_*unpack*) work on HOST memory,
+ *     synchronously, and never touch the GPU.
+ *   - Device entry points take DEVICE pointers owned by the caller, enqueue
+ *     their kernels on `stream` (a hipStream_t passed as void*; NULL = the
+ *     default stream) and return after enqueueing.  Results are valid once
+ *     the stream reaches that point.  The library never allocates or frees
+ *     device memory; scratch space is the caller's `workspace`.
+ *   - Fail-loud overflow contract ([IE] section 3.4): a call whose shapes
+ *     would let an intermediate exceed its integer type returns
+ *     BS_E_OVERFLOW instead of wrapping.
+ *   - All sums are integer, so results are byte-identical whatever the
+ *     launch geometry, split or atomic order ([IE] section 3.2).
+ */
+#ifndef BS_H
+#define BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BS_ABI_VERSION 1
+
+enum {
+    BS_OK = 0,
+    BS_E_NULL = -1,      /* a required pointer is NULL                      */
+    BS_E_SHAPE = -2,     /* a size is non-positive or not a multiple of 128 */
+    BS_E_RANGE = -3,     /* a value is outside its documented range         */
+    BS_E_OVERFLOW = -4,  /* the static bound of the integer types is broken */
+    BS_E_HIP = -5,       /* a HIP call or kernel launch failed              */
+    BS_E_WORKSPACE = -6  /* workspace NULL, too small or misaligned         */
+};
+
+int32_t bs_abi_version(void);
+/* Static string describing a status code (never NULL). */
+const char *bs_status_str(int32_t status);
+
+/* ======================================================================== */
+/* Ternary weight codec ([BS] section 4: each ternary row as two bitplanes,  */
+/* W_nonzero and W_negative; [IE] sections 4.2-4.3: 128-weight groups with  */
+/* one integer scale each).  0.25 byte per weight + 2 bytes per group.       */
+/* ======================================================================== */
+/*
+ * Packed planes layout ("tiled64"), for `rows` x `k` trits, k % 128 == 0:
+ *   rows are padded to R = ceil(rows/64)*64 with all-zero rows;
+ *   G = k/128 groups; block (tile, g) is 2048 bytes at byte offset
+ *   (tile*G + g)*2048, tile in [0, R/64);
+ *   block bytes [0, 1024):    W_nonzero, row 64*tile+j at bytes [16j, 16j+16)
+ *   block bytes [1024, 2048): W_negative, same arrangement;
+ *   weight 128*g + i of the row is bit (i % 8) of byte (i / 8) of its
+ *   16-byte field.  W_negative is a subset of W_nonzero.
+ * Total: R*k/4 bytes.  The 64-row tile is one wavefront: lane j streams row
+ * j with 16-byte loads and the wavefront reads 1 KB contiguous per plane.
+ *
+ * Packed scales layout: int16 at index (tile*G + g)*64 + j holds the scale of
+ * row 64*tile+j, group g; padding rows hold 0.  Total R*G int16.
+ */
+
+/* Bytes of packed planes (R*k/4) or a negative BS_E_* code. */
+int64_t bs_ternary_planes_bytes(int64_t rows, int64_t k);
+/* Number of int16 packed scales (R*k/128) or a negative BS_E_* code. */
+int64_t bs_ternary_scales_count(int64_t rows, int64_t k);
+
+/* t[rows][k] row-major, each in {-1,0,+1} (else BS_E_RANGE, output partly
+ * written).  planes: bs_ternary_planes_bytes(rows,k) bytes, fully written. */
+int32_t bs_ternary_pack(const int8_t *t, int64_t rows, int64_t k, uint8_t *planes);
+/* Inverse of bs_ternary_pack.  A W_negative bit without its W_nonzero bit
+ * is not a ternary code: BS_E_RANGE. */
+int32_t bs_ternary_unpack(const uint8_t *planes, int64_t rows, int64_t k, int8_t *t);
+/* scales[rows][k/128] row-major -> packed[R*k/128] (layout above). */
+int32_t bs_ternary_pack_scales(const int16_t *scales, int64_t rows, int64_t k,
+                               int16_t *packed);
+
+/* ======================================================================== */
+/* bs_ternary_gemv -- exact batch-1 ternary GEMV ([IE] section 4.2)          */
+/* ======================================================================== */
+/*
+ *   y[r] = sum_{g} floor( scale[r][g] * s[r][g] / 2^frac ),
+ *   s[r][g] = sum_{i in group g, t=+1} x[i] - sum_{i in group g, t=-1} x[i]
+ * (the masked signed sum: zero weights drop out), computed exactly:
+ * |s| <= 2^14, |scale*s| <= 2^29 (int32), y accumulated in int64.
+ *
+ *   planes  device, packed planes (layout above), bs_ternary_planes_bytes
+ *   scales  device, packed int16 scales (layout above)
+ *   x       device, int8[k] activations (two's complement, -128 allowed)
+ *   rows    >= 1;  k >= 128, k % 128 == 0, k <= 2^24
+ *   frac    0..62: fractional bits of the fixed-point scale; the floor is
+ *           applied per group, before the sum over groups
+ *   y       device, int64[rows], overwritten
+ *   workspace, workspace_bytes
+ *           device scratch of at least bs_ternary_gemv_workspace_bytes(rows,
+ *           k) bytes, 256-byte aligned.  It must be zero-filled before its
+ *           first use; every completed call leaves it zero-filled again, so
+ *           one workspace serves any sequence of bs_ternary_gemv calls
+ *           ordered on one stream.  Calls that may overlap need separate
+ *           workspaces, and a workspace is not shared with other entry
+ *           points.
+ * Errors: BS_E_NULL, BS_E_SHAPE, BS_E_RANGE (frac), BS_E_WORKSPACE, BS_E_HIP.
+ */
+size_t bs_ternary_gemv_workspace_bytes(int64_t rows, int64_t k);
+int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales, const int8_t *x,
+                        int64_t rows, int64_t k, int32_t frac, int64_t *y,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ======================================================================== */
+/* bs_lns8_phase_gemv -- BitState LNS8 eight-phase GEMV ([BS] sections 3-4)  */
+/* ======================================================================== */
+/*
+ * Weights: ternary, packed exactly as for bs_ternary_gemv (no scales: the
+ * shared scale stays outside the reduction, the factorised variant of [BS]
+ * section 4).  Activations x_lns8[k]: bit 7 = S1 (sign), bits 6..3 = E4
+ * (band 0..15), bits 2..0 = L3 (phase 0..7); code = bits 6..0, code 0 is an
+ * exact zero ([BS] section 3).  The product of a weight t = +-1 (log offset
+ * 0, code 74 = 1.0) with code c has code c and sign S1 XOR [t < 0]; t = 0 or
+ * c = 0 gives no product.  Each product adds +-(1 << E4) to A[r][L3]
+ * ([BS] section 3.1), so
+ *   acc[r][p] = sum over products with phase p of sign * 2^band   (int32)
+ *   s[r]      = 2^-9 * sum_p acc[r][p] * F[p],  F[p] = 2^((p-2)/8)
+ * s is the exact value of that sum over the binary64 F[p] (each F[p]
+ * correctly rounded), rounded once to binary64.
+ *
+ *   path    BS_LNS8_DIRECT (0): per-product routing into A[L3];
+ *           BS_LNS8_POPCOUNT (1): per 64-lane tile and active state s,
+ *           C_s = popcount(A_s & W_nonzero) - 2*popcount(A_s & W_nonzero &
+ *           (sign XOR W_negative)), H[phase][band] += C_s,
+ *           A[p] = sum_b H[p][b] * 2^b ([BS] sections 3.1, 4).
+ *           Both paths return identical bytes.
+ *   rows    >= 1;  k >= 128, k % 128 == 0, k <= 65408 (|A| <= k*2^15 must
+ *           fit int32, else BS_E_OVERFLOW)
+ *   acc     device int32[rows][8], overwritten
+ *   s       device double[rows], or NULL to skip the materialisation
+ *   workspace  as for bs_ternary_gemv (zero-filled before first use, left
+ *           zero-filled, not shared with other entry points), at least
+ *           bs_lns8_workspace_bytes(rows, k) bytes
+ */
+#define BS_LNS8_DIRECT 0
+#define BS_LNS8_POPCOUNT 1
+size_t bs_lns8_workspace_bytes(int64_t rows, int64_t k);
+int32_t bs_lns8_phase_gemv(const uint8_t *planes, const uint8_t *x_lns8, int64_t rows,
+                           int64_t k, int32_t path, int32_t *acc, double *s,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* ======================================================================== */
+/* BITNET_PLANES lm_head ([T2])                                              */
+/* ======================================================================== */
+/*
+ * Each of `vocab` rows holds eight ternary planes T_0..T_7 over `dim`
+ * positions, weighted 3^-p, and an int32 row scale.  Scores are exact int64
+ * in units of 3^-7:
+ *   S'(r) = row_scale[r] * sum_{p=0..7} 3^(7-p) * (T_p[r] . h)
+ *
+ * Packed layouts (dim % 128 == 0, G = dim/128):
+ *   planes03 ("tiled64", streamed by the full-vocabulary scan): rows padded
+ *     to R = ceil(vocab/64)*64; block (tile, g) is 8192 bytes at offset
+ *     (tile*G + g)*8192; plane q (0..3) at block bytes [2048q, 2048q+2048):
+ *     W_nonzero in the first 1024 bytes, W_negative in the next 1024, row
+ *     64*tile+j at 16j.  R*dim bytes.
+ *   planes47 (row-major, gathered for candidate rows only): row r at bytes
+ *     [r*dim, r*dim+dim); group g at r*dim + 128g; plane q (4..7) at
+ *     + 32(q-4): 16 bytes W_nonzero then 16 bytes W_negative.  vocab*dim
+ *     bytes.
+ *   In every 16-byte field weight 128*g + i is bit (i % 8) of byte (i / 8).
+ *
+ * trits[vocab][8][dim] row-major, each in {-1,0,+1}.
+ */
+int64_t bs_planes03_bytes(int64_t vocab, int64_t dim);
+int64_t bs_planes47_bytes(int64_t vocab, int64_t dim);
+int32_t bs_planes_pack(const int8_t *trits, int64_t vocab, int64_t dim,
+                       uint8_t *planes03, uint8_t *planes47);
+
+/*
+ * bs_lmhead_planes_topk -- two-stage exact top-k ([T2], BitNetTwoStageDecode):
+ *   stage 1, every row:  E1 = sum_{p=0..3} 3^(3-p) (T_p . h),
+ *                        S1' = 81 * row_scale * E1,
+ *                        B'  = 40 * |row_scale| * sum|h|   (the page's
+ *                        truncation bound rowScale*(sum_{p=4..7}3^-p)*sum|h|
+ *                        in units of 3^-7), L = S1' - B', U = S1' + B';
+ *   L_k = the top_k-th largest L;  C = { r : U(r) >= L_k };
+ *   if |C| <= max_candidates every row of C is rescored (the result is then
+ *   the exact top-k); otherwise the max_candidates rows of C with the largest
+ *   S1' (lowest index first on ties) are rescored and info[1] = 1;
+ *   rescoring: E2 = sum_{p=4..7} 3^(7-p) (T_p . h), S' = row_scale*(81*E1+E2);
+ *   output: the top_k rescored rows by S' descending, lowest index first on
+ *   ties ([IE] sections 3.2-3.3).
+ *
+ *   planes03, planes47, row_scale (int32[vocab]), h (int8[dim]): device
+ *   vocab >= 1; dim >= 128, dim % 128 == 0, dim <= 10112 (|S'| <= 2^31 *
+ *     3280 * 128 * dim must fit int64, else BS_E_OVERFLOW)
+ *   1 <= top_k <= max_candidates, top_k <= vocab, max_candidates <= 4096
+ *   top_idx int32[top_k], top_score int64[top_k]: device, overwritten
+ *   info    device int32[2]: info[0] = |C|, info[1] = 1 if the cap engaged
+ *   workspace  device scratch of bs_lmhead_workspace_bytes(...) bytes,
+ *     256-byte aligned.  It must be zero-filled before its first use; its
+ *     candidate counter is zero again when a call completes (the rest is
+ *     scratch whose contents do not matter), so one workspace serves any
+ *     sequence of bs_lmhead_planes_topk calls ordered on one stream.  It is
+ *     not shared with other entry points or overlapping calls.
+ */
+size_t bs_lmhead_workspace_bytes(int64_t vocab, int64_t dim, int32_t top_k,
+                                 int32_t max_candidates);
+int32_t bs_lmhead_planes_topk(const uint8_t *planes03, const uint8_t *planes47,
+                              const int32_t *row_scale, const int8_t *h, int64_t vocab,
+                              int64_t dim, int32_t top_k, int32_t max_candidates,
+                              int32_t *top_idx, int64_t *top_score, int32_t *info,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BS_H */

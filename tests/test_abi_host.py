@@ -1,0 +1,138 @@
+"""Host-side checks of the C-ABI library that need no GPU.
+
+* the shared library loads and exports every function include/bs.h declares;
+* the load-time codec (host C++) is byte-identical to the oracle's own
+  implementation of the documented layouts, and rejects invalid input;
+* argument validation returns the documented BS_E_* code before any HIP call
+  (only calls that fail validation are made here, so nothing reaches the
+  GPU runtime).
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import bit_decode_gemv_amd as bs
+import oracle
+from bit_decode_gemv_amd import synth
+
+FAKE = ctypes.c_void_p(1 << 20)          # never dereferenced: validation fails first
+
+
+def test_library_exports_every_header_symbol():
+    lib = bs.lib()
+    names = bs.header_symbols()
+    assert len(names) >= 16
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.bs_abi_version() == 1
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert bs.status_str(code)
+    assert bs.status_str(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("rows,k,seed", [(256, 512, 0), (1, 128, 1), (63, 256, 2), (65, 384, 3),
+                                         (130, 1280, 4)])
+def test_ternary_codec_matches_oracle_layout(rows, k, seed):
+    t, sc, _ = synth.ternary(rows, k, seed, p_zero=1 / 3)
+    p = bs.ternary_pack(t)
+    assert p.size == oracle.pad64(rows) * k // 4
+    assert (p == oracle.ternary_pack(t)).all()
+    assert (bs.ternary_unpack(p, rows, k) == t).all()
+    ps = bs.ternary_pack_scales(sc)
+    assert (ps == oracle.scales_pack(sc)).all()
+
+
+def test_ternary_codec_rejects_invalid():
+    t = np.zeros((4, 128), np.int8)
+    t[2, 5] = -2
+    with pytest.raises(bs.BsError) as e:
+        bs.ternary_pack(t)
+    assert e.value.status == bs.BS_E_RANGE
+    z = bs.ternary_pack(np.zeros((3, 128), np.int8))
+    z[1024 + 16 * 2 + 3] = 0x10          # W_negative without W_nonzero
+    with pytest.raises(bs.BsError) as e:
+        bs.ternary_unpack(z, 3, 128)
+    assert e.value.status == bs.BS_E_RANGE
+    with pytest.raises(bs.BsError) as e:
+        bs.ternary_pack(np.zeros((3, 100), np.int8))
+    assert e.value.status == bs.BS_E_SHAPE
+
+
+@pytest.mark.parametrize("V,K,seed", [(65, 256, 0), (128, 128, 1), (3, 384, 2)])
+def test_planes_codec_matches_oracle_layout(V, K, seed):
+    trits, _, _ = synth.lmhead(V, K, seed)
+    p03, p47 = bs.planes_pack(trits)
+    o03, o47 = oracle.planes_pack(trits)
+    assert (p03 == o03).all() and (p47 == o47).all()
+
+
+def test_sizes():
+    lib = bs.lib()
+    assert lib.bs_ternary_planes_bytes(2560, 2560) == 2560 * 2560 // 4
+    assert lib.bs_ternary_planes_bytes(65, 128) == 128 * 128 // 4
+    assert lib.bs_ternary_scales_count(2560, 2560) == 2560 * 20
+    assert lib.bs_ternary_planes_bytes(10, 100) == bs.BS_E_SHAPE
+    assert lib.bs_planes03_bytes(128256, 2560) == 128256 * 2560
+    assert lib.bs_planes47_bytes(100, 256) == 100 * 256
+    assert lib.bs_ternary_gemv_workspace_bytes(2560, 2560) > 0
+    assert lib.bs_ternary_gemv_workspace_bytes(2560, 2600) == 0
+    assert lib.bs_lns8_workspace_bytes(4096, 4096) > 0
+    assert lib.bs_lmhead_workspace_bytes(128256, 2560, 40, 200) > 0
+    assert lib.bs_lmhead_workspace_bytes(128256, 2560, 201, 200) == 0
+
+
+def _tgemv(planes=FAKE, scales=FAKE, x=FAKE, rows=64, k=128, frac=0, y=FAKE, ws=FAKE,
+           wsn=1 << 20):
+    return bs.lib().bs_ternary_gemv(planes, scales, x, rows, k, frac, y, ws, wsn, None)
+
+
+def test_ternary_gemv_validation():
+    assert _tgemv(planes=None) == bs.BS_E_NULL
+    assert _tgemv(y=None) == bs.BS_E_NULL
+    assert _tgemv(k=100) == bs.BS_E_SHAPE
+    assert _tgemv(k=0) == bs.BS_E_SHAPE
+    assert _tgemv(rows=0) == bs.BS_E_SHAPE
+    assert _tgemv(frac=-1) == bs.BS_E_RANGE
+    assert _tgemv(frac=63) == bs.BS_E_RANGE
+    assert _tgemv(k=(1 << 24) + 128) == bs.BS_E_OVERFLOW
+    assert _tgemv(ws=None) == bs.BS_E_WORKSPACE
+    assert _tgemv(wsn=16) == bs.BS_E_WORKSPACE
+    assert _tgemv(ws=ctypes.c_void_p((1 << 20) + 8)) == bs.BS_E_WORKSPACE
+
+
+def _lns8(planes=FAKE, x=FAKE, rows=64, k=128, path=0, acc=FAKE, s=FAKE, ws=FAKE, wsn=1 << 20):
+    return bs.lib().bs_lns8_phase_gemv(planes, x, rows, k, path, acc, s, ws, wsn, None)
+
+
+def test_lns8_validation():
+    assert _lns8(x=None) == bs.BS_E_NULL
+    assert _lns8(acc=None) == bs.BS_E_NULL
+    assert _lns8(k=64) == bs.BS_E_SHAPE
+    assert _lns8(path=2) == bs.BS_E_RANGE
+    assert _lns8(k=65536) == bs.BS_E_OVERFLOW       # |A| <= k*2^15 would not fit int32
+    assert _lns8(ws=None) == bs.BS_E_WORKSPACE
+    assert _lns8(wsn=8) == bs.BS_E_WORKSPACE
+
+
+def _lmh(V=1000, dim=256, top_k=40, cap=200, ws=FAKE, wsn=1 << 26, **kw):
+    a = dict(p03=FAKE, p47=FAKE, rs=FAKE, h=FAKE, idx=FAKE, score=FAKE, info=FAKE)
+    a.update(kw)
+    return bs.lib().bs_lmhead_planes_topk(a["p03"], a["p47"], a["rs"], a["h"], V, dim, top_k,
+                                          cap, a["idx"], a["score"], a["info"], ws, wsn, None)
+
+
+def test_lmhead_validation():
+    assert _lmh(p47=None) == bs.BS_E_NULL
+    assert _lmh(info=None) == bs.BS_E_NULL
+    assert _lmh(dim=200) == bs.BS_E_SHAPE
+    assert _lmh(top_k=0) == bs.BS_E_RANGE
+    assert _lmh(top_k=201, cap=200) == bs.BS_E_RANGE
+    assert _lmh(V=10, top_k=20, cap=20) == bs.BS_E_RANGE
+    assert _lmh(cap=5000) == bs.BS_E_RANGE
+    assert _lmh(dim=10240) == bs.BS_E_OVERFLOW      # int64 bound of the exact score
+    assert _lmh(ws=None) == bs.BS_E_WORKSPACE
+    assert _lmh(wsn=1024) == bs.BS_E_WORKSPACE

@@ -1,0 +1,88 @@
+"""GPU parity of bs_lmhead_planes_topk against the oracle.
+
+The GPU result (top-k indices, exact int64 scores, |C| and the cap flag)
+must equal the oracle's step-by-step two-stage algorithm bit for bit on every
+input.  Where the cap does not engage the oracle's result equals the brute
+force (pinned in the oracle tests), so the GPU result is then the exact
+top-k; where it engages, agreement with brute force is recorded.
+"""
+import numpy as np
+import pytest
+
+import bit_decode_gemv_amd as bs
+import oracle
+from bit_decode_gemv_amd import synth
+from gpu_util import device, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run(trits, rs, h, top_k, cap, packed=None):
+    import torch
+    dev = device()
+    V, _, K = trits.shape
+    p03, p47 = packed if packed is not None else bs.planes_pack(trits)
+    note("lmhead V=%d K=%d k=%d cap=%d" % (V, K, top_k, cap))
+    idx, sc, info = bs.lmhead_planes_topk(to_dev(p03, dev), to_dev(p47, dev), to_dev(rs, dev),
+                                          to_dev(h, dev), V, K, top_k, cap)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), sc.cpu().numpy(), info.cpu().numpy()
+
+
+def check(trits, rs, h, top_k, cap, packed=None):
+    idx, sc, info = run(trits, rs, h, top_k, cap, packed)
+    widx, wsc, n, capped = oracle.lmhead_two_stage(trits, rs, h, top_k, cap)
+    assert info[0] == n and info[1] == capped, (info, n, capped)
+    assert (idx == widx).all(), (idx[:10], widx[:10])
+    assert (sc == wsc).all()
+    return idx, sc, n, capped
+
+
+@pytest.mark.parametrize("V,K,k,cap,seed", [(300, 128, 40, 200, 0), (257, 256, 7, 50, 1),
+                                             (64, 128, 1, 1, 2), (100, 128, 100, 100, 3),
+                                             (1000, 256, 40, 200, 4), (2049, 384, 16, 32, 5),
+                                             (5000, 128, 40, 4096, 6)])
+def test_small_random(V, K, k, cap, seed):
+    check(*synth.lmhead(V, K, seed), k, cap)
+
+
+def test_planted_exact_branch():
+    trits, rs, h, peaks = synth.lmhead_planted(4000, 512, 1, n_peaks=64)
+    idx, sc, n, capped = check(trits, rs, h, 40, 200)
+    assert capped == 0
+    bi, bsc = oracle.lmhead_brute(trits, rs, h, 40)
+    assert (idx == bi).all() and (sc == bsc).all()
+
+
+def test_exactly_ternary_source():
+    trits, rs, h = synth.lmhead(700, 256, 7)
+    trits[:, 1:, :] = 0
+    idx, sc, _, _ = check(trits, rs, h, 40, 200)
+    bi, bsc = oracle.lmhead_brute(trits, rs, h, 40)
+    assert (idx == bi).all() and (sc == bsc).all()
+
+
+def test_all_zero_planes_ties():
+    trits = np.zeros((450, 8, 128), np.int8)
+    _, rs, h = synth.lmhead(450, 128, 8)
+    idx, sc, n, capped = check(trits, rs, h, 40, 200)
+    assert n == 450 and capped == 1
+    assert (idx == np.arange(40)).all() and not sc.any()
+
+
+def test_negative_row_scales():
+    trits, rs, h = synth.lmhead(600, 256, 9)
+    rs = rs * np.where(np.arange(600) % 3 == 0, -1, 1).astype(np.int32)
+    check(trits, rs, h, 20, 100)
+
+
+@pytest.mark.slow
+def test_full_vocab_config():
+    """vocab 128256 x dim 2560, k = 40, cap = 200, seed 0."""
+    trits, rs, h = synth.lmhead(*synth.LMHEAD_SHAPE, seed=0)
+    idx, sc, n, capped = check(trits, rs, h, 40, 200)
+    bi, bsc = oracle.lmhead_brute(trits, rs, h, 40)
+    same = bool((idx == bi).all() and (sc == bsc).all())
+    print("full vocab: |C| = %d, capped = %d, equals brute force: %s" % (n, capped, same))
+    if not capped:
+        assert same

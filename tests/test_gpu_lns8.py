@@ -1,0 +1,84 @@
+"""GPU parity of bs_lns8_phase_gemv against the oracle.
+
+A[p] (int32) must be bit-exact for both the DIRECT and the POPCOUNT path;
+S (binary64) must agree with the oracle's exact-then-rounded value within
+1e-12 relative, the bound the task sets for the materialised fp64 result.
+Both sides evaluate S as the exact sum over the correctly rounded F[p]
+rounded once, so they are expected to agree bit for bit; the test states
+the 1e-12 bar and reports any inexact row.
+"""
+import numpy as np
+import pytest
+
+import bit_decode_gemv_amd as bs
+import oracle
+from bit_decode_gemv_amd import synth
+from gpu_util import device, note, to_dev
+
+pytestmark = pytest.mark.gpu
+REL_TOL = 1e-12
+
+
+def run(t, x, path):
+    import torch
+    dev = device()
+    rows, k = t.shape
+    planes = to_dev(bs.ternary_pack(t), dev)
+    xd = to_dev(x, dev)
+    note("lns8 rows=%d k=%d path=%d" % (rows, k, path))
+    acc, s = bs.lns8_phase_gemv(planes, xd, rows, k, path)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), s.cpu().numpy()
+
+
+def check(t, x):
+    want_a = oracle.lns8_direct(t, x)
+    want_s = oracle.lns8_materialize(want_a)
+    results = []
+    for path in (bs.LNS8_DIRECT, bs.LNS8_POPCOUNT):
+        a, s = run(t, x, path)
+        bad = np.nonzero((a != want_a).any(1))[0]
+        assert bad.size == 0, "path %d row %d: %s vs %s" % (path, bad[0], a[bad[0]], want_a[bad[0]])
+        err = np.abs(s - want_s)
+        assert (err <= REL_TOL * np.abs(want_s)).all(), "path %d: max rel err %g" % (
+            path, (err / np.maximum(np.abs(want_s), 1e-300)).max())
+        assert ((s == 0) == (want_s == 0)).all()
+        results.append((a, s))
+    # the two paths return identical bytes
+    assert (results[0][0] == results[1][0]).all()
+    assert (results[0][1].view(np.int64) == results[1][1].view(np.int64)).all()
+    return results[0][1], want_s
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_lns8_config(seed):
+    s, want = check(*synth.lns8(4096, 4096, seed))
+    # exact-then-round on both sides: report, and expect, bit equality
+    assert (s.view(np.int64) == want.view(np.int64)).all()
+
+
+@pytest.mark.parametrize("rows,k", [(1, 128), (63, 256), (65, 128), (130, 1024)])
+def test_lns8_ragged(rows, k):
+    check(*synth.lns8(rows, k, seed=rows))
+
+
+def _adversarial():
+    rng = np.random.default_rng(17)
+    k = 512
+    t = rng.integers(-1, 2, (70, k)).astype(np.int8)
+    yield "all_same_code", t, np.full(k, 80, np.uint8)
+    yield "all_zero_code", t, np.zeros(k, np.uint8)
+    yield "zero_code_sign_set", t, np.full(k, 0x80, np.uint8)
+    yield "code_1", t, (rng.integers(0, 2, k).astype(np.uint8) << 7) | 1
+    yield "code_127", t, (rng.integers(0, 2, k).astype(np.uint8) << 7) | 127
+    yield "all_bytes", t, rng.integers(0, 256, k).astype(np.uint8)
+    tc = np.ones((64, k), np.int8)
+    xc = np.full(k, 90, np.uint8)
+    xc[1::2] |= 0x80
+    yield "cancel", tc, xc
+    yield "max_magnitude", -np.ones((64, k), np.int8), np.full(k, 0xFF, np.uint8)
+
+
+@pytest.mark.parametrize("case", list(_adversarial()), ids=lambda c: c[0])
+def test_lns8_adversarial(case):
+    check(case[1], case[2])

@@ -1,0 +1,101 @@
+"""GPU parity of bs_ternary_gemv against the oracle (bit-exact int64).
+
+Covers the tiny case, the BitNet-2B decode projection shapes (seeds 0..4) and
+the larger-K shapes (seeds 0..1) at full size in the launch configuration the
+benchmark times, plus ragged and degenerate cases: single rows, row counts
+off the 64-row tile, K = 128, all-zero weights, x = -128, extreme scales,
+every frac, workspace reuse across shapes, and run-to-run byte identity.
+"""
+import numpy as np
+import pytest
+
+import bit_decode_gemv_amd as bs
+import oracle
+from bit_decode_gemv_amd import synth
+from gpu_util import device, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run(t, sc, x, frac=0, dev=None, ws=None):
+    dev = dev or device()
+    rows, k = t.shape
+    planes = to_dev(bs.ternary_pack(t), dev)
+    scales = to_dev(bs.ternary_pack_scales(sc), dev)
+    xd = to_dev(x, dev)
+    note("ternary_gemv rows=%d k=%d frac=%d" % (rows, k, frac))
+    y = bs.ternary_gemv(planes, scales, xd, rows, k, frac, workspace=ws)
+    import torch
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def check(t, sc, x, frac=0, ws=None):
+    y = run(t, sc, x, frac, ws=ws)
+    want = oracle.ternary_gemv_def(t, sc, x, frac)
+    bad = np.nonzero(y != want)[0]
+    assert bad.size == 0, "first mismatch row %d: got %d want %d (%d bad)" % (
+        bad[0], y[bad[0]], want[bad[0]], bad.size)
+
+
+def test_tiny_config():
+    check(*synth.tiny(0))
+
+
+@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("name", ["q", "k", "gate", "down"])
+def test_bitnet2b_projections(name, seed):
+    rows, k = synth.BITNET2B_SHAPES[name]
+    check(*synth.ternary(rows, k, seed))
+
+
+@pytest.mark.parametrize("seed", range(2))
+@pytest.mark.parametrize("shape", synth.LARGE_K_SHAPES)
+def test_large_k(shape, seed):
+    check(*synth.ternary(shape[0], shape[1], seed))
+
+
+@pytest.mark.parametrize("rows,k", [(1, 128), (63, 128), (65, 256), (130, 384), (1, 2560),
+                                    (127, 6912), (200, 128 * 100)])
+def test_ragged_shapes(rows, k):
+    check(*synth.ternary(rows, k, seed=rows + k, p_zero=1 / 3, act="uniform127"))
+
+
+@pytest.mark.parametrize("frac", [0, 1, 3, 16, 29, 30, 31, 32, 62])
+def test_frac_with_negative_scales(frac):
+    t, _, x = synth.ternary(130, 640, seed=frac, p_zero=1 / 3, act="uniform127")
+    rng = np.random.default_rng(frac)
+    sc = rng.integers(-32768, 32768, (130, 5)).astype(np.int16)
+    check(t, sc, x, frac)
+
+
+def test_degenerate_values():
+    rows, k = 96, 512
+    # all-zero weights
+    check(np.zeros((rows, k), np.int8), np.ones((rows, 4), np.int16),
+          np.full(k, 7, np.int8))
+    # largest magnitudes: t = -1, x = -128, scale = -32768
+    check(-np.ones((rows, k), np.int8), np.full((rows, 4), -32768, np.int16),
+          np.full(k, -128, np.int8))
+    # one-hot activations pin the bit order of the codec on the device
+    t, sc, _ = synth.ternary(rows, k, seed=3, p_zero=1 / 3)
+    for i in (0, 1, 31, 32, 63, 64, 127, 128, 300, 511):
+        x = np.zeros(k, np.int8)
+        x[i] = 1
+        check(t, sc, x)
+
+
+def test_workspace_reuse_and_determinism():
+    import torch
+    dev = device()
+    ws = torch.zeros(bs.lib().bs_ternary_gemv_workspace_bytes(13824, 5120), dtype=torch.uint8,
+                     device=dev)
+    cases = [synth.ternary(13824, 5120, 7), synth.ternary(640, 2560, 8),
+             synth.ternary(2560, 6912, 9), synth.ternary(65, 256, 10)]
+    for t, sc, x in cases:
+        a = run(t, sc, x, ws=ws)
+        b = run(t, sc, x, ws=ws)
+        assert (a == b).all()
+        assert (a == oracle.ternary_gemv_def(t, sc, x)).all()
+    torch.cuda.synchronize()
+    assert not ws.any().item(), "workspace must be left zero-filled"
