@@ -158,14 +158,14 @@ __global__ __launch_bounds__(256) void lmh_filter(const int32_t *__restrict__ ro
     const long long upper = ws.s1[row] + 40LL * (rs < 0 ? -rs : rs) * habs;
     if (upper >= lk) {
         const unsigned int slot = atomicAdd(ws.count, 1u);
-        ws.cand[slot] = row;
+        if (slot < (unsigned int)vocab) ws.cand[slot] = row;
     }
 }
 
 // ----------------------------------------------------------------- finish
 __global__ __launch_bounds__(kFinishThreads) void lmh_finish(
     const uint8_t *__restrict__ planes47, const int32_t *__restrict__ row_scale,
-    const int8_t *__restrict__ h, int groups, int dim, int top_k, int cap,
+    const int8_t *__restrict__ h, int vocab, int groups, int dim, int top_k, int cap,
     int32_t *__restrict__ top_idx, int64_t *__restrict__ top_score, int32_t *__restrict__ info,
     LmhWs ws) {
     __shared__ unsigned int hist[256];
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kFinishThreads) void lmh_finish(
     __shared__ unsigned int nsel;
     extern __shared__ uint32_t hplanes[];     // [groups][8 planes][4 dwords]
 
-    const unsigned int n = *ws.count;
+    const unsigned int n = min(*ws.count, (unsigned int)vocab);
     const bool capped = n > (unsigned int)cap;
 
     // bit planes of h for every group
@@ -307,16 +307,19 @@ struct LmhLayout {
     int nwg;
 };
 
+// The candidate counter is the only word that must be zero on entry.  It sits
+// at offset 0 whatever the shapes, so calls of different shapes can share one
+// workspace: every other region is written before it is read.
 static LmhLayout lmh_layout(int64_t vocab, int32_t top_k) {
     LmhLayout L;
     const int64_t tiles = pad64(vocab) / 64;
     L.nwg = (int)((tiles + kStage1Waves - 1) / kStage1Waves);
     size_t off = 0;
+    L.count = off;   off += kWsAlign;
+    L.scalars = off; off += kWsAlign;
     L.s1 = off;      off += align_up((size_t)vocab * 8, kWsAlign);
     L.e1 = off;      off += align_up((size_t)vocab * 4, kWsAlign);
     L.lower = off;   off += align_up((size_t)L.nwg * (size_t)top_k * 8, kWsAlign);
-    L.scalars = off; off += kWsAlign;
-    L.count = off;   off += kWsAlign;
     L.cand = off;    off += align_up((size_t)vocab * 4, kWsAlign);
     L.total = off;
     return L;
@@ -371,7 +374,8 @@ extern "C" int32_t bs_lmhead_planes_topk(const uint8_t *planes03, const uint8_t 
                        row_scale, (int)vocab, ws);
     BS_LAUNCH_CHECK();
     hipLaunchKernelGGL(lmh_finish, dim3(1), dim3(kFinishThreads), (size_t)groups * 32 * 4, st,
-                       planes47, row_scale, h, groups, (int)dim, top_k, max_candidates,
+                       planes47, row_scale, h, (int)vocab, groups, (int)dim, top_k,
+                       max_candidates,
                        top_idx, top_score, info, ws);
     BS_LAUNCH_CHECK();
     return BS_OK;

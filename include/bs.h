@@ -207,11 +207,12 @@ int32_t bs_planes_pack(const int8_t *trits, int64_t vocab, int64_t dim,
  *   top_idx int32[top_k], top_score int64[top_k]: device, overwritten
  *   info    device int32[2]: info[0] = |C|, info[1] = 1 if the cap engaged
  *   workspace  device scratch of bs_lmhead_workspace_bytes(...) bytes,
- *     256-byte aligned.  It must be zero-filled before its first use; its
- *     candidate counter is zero again when a call completes (the rest is
- *     scratch whose contents do not matter), so one workspace serves any
- *     sequence of bs_lmhead_planes_topk calls ordered on one stream.  It is
- *     not shared with other entry points or overlapping calls.
+ *     256-byte aligned.  Its first 256 bytes are bookkeeping (the candidate
+ *     counter) and must be zero-filled before the first use; every completed
+ *     call leaves them zero again.  The rest is scratch, written before it is
+ *     read, so one workspace serves bs_lmhead_planes_topk calls of any
+ *     shapes ordered on one stream.  It is not shared with other entry points
+ *     or overlapping calls.
  */
 size_t bs_lmhead_workspace_bytes(int64_t vocab, int64_t dim, int32_t top_k,
                                  int32_t max_candidates);

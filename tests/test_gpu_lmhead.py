@@ -86,3 +86,27 @@ def test_full_vocab_config():
     print("full vocab: |C| = %d, capped = %d, equals brute force: %s" % (n, capped, same))
     if not capped:
         assert same
+
+
+def test_workspace_shared_across_shapes():
+    """One workspace serves calls of different shapes: only its first 256
+    bytes (the candidate counter) must be zero on entry, and every call
+    leaves them zero (regression: the counter used to move with the shape
+    and land on scratch left by a larger call)."""
+    import torch
+    dev = device()
+    ws = torch.zeros(bs.lib().bs_lmhead_workspace_bytes(3000, 256, 40, 200), dtype=torch.uint8,
+                     device=dev)
+    for V, K, k, cap, seed in [(3000, 256, 40, 200, 11), (257, 256, 7, 50, 12),
+                               (2000, 128, 40, 200, 13), (300, 128, 40, 200, 14)]:
+        trits, rs, h = synth.lmhead(V, K, seed)
+        p03, p47 = bs.planes_pack(trits)
+        note("lmhead shared workspace V=%d K=%d" % (V, K))
+        idx, sc, info = bs.lmhead_planes_topk(to_dev(p03, dev), to_dev(p47, dev),
+                                              to_dev(rs, dev), to_dev(h, dev), V, K, k, cap,
+                                              workspace=ws)
+        torch.cuda.synchronize()
+        widx, wsc, n, capped = oracle.lmhead_two_stage(trits, rs, h, k, cap)
+        assert (idx.cpu().numpy() == widx).all() and (sc.cpu().numpy() == wsc).all()
+        assert list(info.cpu().numpy()) == [n, capped]
+        assert not ws[:256].any().item()
