@@ -24,8 +24,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libbitstate.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "bs.h")
 
-BS_OK, BS_E_NULL, BS_E_SHAPE, BS_E_RANGE, BS_E_OVERFLOW, BS_E_HIP, BS_E_WORKSPACE = (
-    0, -1, -2, -3, -4, -5, -6)
+BS_OK, BS_E_NULL, BS_E_SHAPE, BS_E_RANGE, BS_E_OVERFLOW, BS_E_HIP, BS_E_WORKSPACE, BS_E_ALIGN = (
+    0, -1, -2, -3, -4, -5, -6, -7)
 LNS8_DIRECT, LNS8_POPCOUNT = 0, 1
 
 _lib = None
@@ -47,8 +47,7 @@ def _declare(lib):
         "bs_ternary_pack": (I32, [P, I64, I64, P]),
         "bs_ternary_unpack": (I32, [P, I64, I64, P]),
         "bs_ternary_pack_scales": (I32, [P, I64, I64, P]),
-        "bs_ternary_gemv_workspace_bytes": (SZ, [I64, I64]),
-        "bs_ternary_gemv": (I32, [P, P, P, I64, I64, I32, P, P, SZ, P]),
+        "bs_ternary_gemv": (I32, [P, P, P, I64, I64, I32, P, P]),
         "bs_lns8_workspace_bytes": (SZ, [I64, I64]),
         "bs_lns8_phase_gemv": (I32, [P, P, I64, I64, I32, P, P, P, SZ, P]),
         "bs_planes03_bytes": (I64, [I64, I64]),
@@ -217,23 +216,22 @@ def _need(t, n, name):
 
 
 def ternary_gemv(planes, scales, x, rows: int, k: int, frac: int = 0, out=None,
-                 workspace=None, stream=None):
+                 stream=None):
     """y = bs_ternary_gemv(planes, scales, x): int64[rows] on x's device."""
     torch = _torch()
     if out is None:
         out = torch.empty(rows, dtype=torch.int64, device=x.device)
-    need = lib().bs_ternary_gemv_workspace_bytes(rows, k)
-    if need == 0:
-        raise BsError(BS_E_SHAPE, "bs_ternary_gemv_workspace_bytes")
-    _need(planes, lib().bs_ternary_planes_bytes(rows, k), "planes")
+    nplanes = lib().bs_ternary_planes_bytes(rows, k)
+    if nplanes < 0:
+        raise BsError(int(nplanes), "bs_ternary_planes_bytes")
+    _need(planes, nplanes, "planes")
     _need(scales, lib().bs_ternary_scales_count(rows, k), "scales")
     _need(x, k, "x")
     _need(out, rows, "y")
-    wp, wn = _ws("ternary_gemv", workspace, need, x.device)
     rc = lib().bs_ternary_gemv(_dptr(planes, torch.uint8, "planes"),
                                _dptr(scales, torch.int16, "scales"),
                                _dptr(x, torch.int8, "x"), rows, k, frac,
-                               _dptr(out, torch.int64, "y"), wp, wn,
+                               _dptr(out, torch.int64, "y"),
                                _stream_handle(stream, x.device))
     _check(rc, "bs_ternary_gemv")
     return out

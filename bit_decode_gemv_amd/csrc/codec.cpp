@@ -23,6 +23,7 @@ extern "C" const char *bs_status_str(int32_t status) {
     case BS_E_OVERFLOW: return "shape breaks the static integer overflow bound";
     case BS_E_HIP: return "HIP runtime or kernel launch error";
     case BS_E_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case BS_E_ALIGN: return "device pointer not aligned as documented";
     default: return "unknown status";
     }
 }

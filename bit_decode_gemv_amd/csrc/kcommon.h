@@ -8,6 +8,15 @@
 
 namespace bs {
 
+// Native 4 x 32-bit vector (global_load_dwordx4), usable with the
+// non-temporal load builtin.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream16(const uint8_t *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Launch a kernel and map any launch error to BS_E_HIP.
 #define BS_LAUNCH_CHECK()                                   \
     do {                                                    \

@@ -17,8 +17,10 @@
 //               code), then C_s = popcount(A_s & W_nz) - 2 popcount(A_s & W_nz
 //               & (sign ^ W_neg)) and A[s & 7] += C_s << (s >> 3): the
 //               histogram H[phase][band] folded into A as it is produced.
-// Split partials meet in a workspace through int32 atomics; the last
-// workgroup of a tile writes A, materialises S and re-zeroes the workspace.
+// Split partials meet in a workspace through int32 atomic adds (order-free:
+// integer addition is associative); the last workgroup of a tile, told by an
+// atomic counter, reads them back with atomic exchanges (which re-zero the
+// workspace), writes A and materialises S.
 #include "kcommon.h"
 
 namespace bs {
@@ -127,12 +129,16 @@ __global__ __launch_bounds__(64) void lns8_kernel(
 #pragma unroll
         for (int p = 0; p < 8; ++p) atomicAdd(&ws_acc[(size_t)row * 8 + p], A[p]);
     }
-    __threadfence();
+    // every atomic of this wavefront is performed before the tile counter
+    // moves; the counter and the accumulators are only touched by atomic
+    // read-modify-writes, so no cache write-back or invalidate is needed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     unsigned int prev = 0;
     if (lane == 0) prev = atomicAdd(&ws_cnt[tile], 1u);
     prev = __builtin_amdgcn_readfirstlane(prev);
     if (prev == (unsigned int)(nsplit - 1)) {
-        __threadfence();
         if (row < rows) {
             int T[8];
 #pragma unroll

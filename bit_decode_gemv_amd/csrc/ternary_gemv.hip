@@ -6,62 +6,233 @@
 // LLMs", section 4.2; the W_nonzero / W_negative planes of "BitState / HSDR
 // PoC Technical Brief - v0.5", section 4).
 //
-// Mapping: one wavefront per (64-row tile, run of `gpb` groups); lane j owns
-// row 64*tile + j and streams its 16-byte W_nonzero and W_negative fields of
-// each group (1 KB contiguous per plane per wavefront).  The activations of a
-// group become eight bit-planes through wavefront ballots and stay in scalar
-// registers, so the inner loop is AND + POPCOUNT against uniform operands:
-// the signed population C = N - 2*Nneg of the brief, per activation bit.
-// Tiles are split along K so that small row counts still fill the 256 CUs;
-// the split partials meet in a workspace accumulator through int64 atomics
-// (order-free because integer addition is associative, integer-engine page
-// section 3.2) and the last workgroup of a tile writes y and re-zeroes the
-// workspace.
+// Mapping.  A workgroup owns R complete rows (R = 64, 32 or 16) and all of
+// K, so no partial sum ever leaves the CU.  Its W wavefronts are split into
+// slices: lane l of wavefront w serves row (l mod R) of the block in slice
+// w*(64/R) + l/R, and slice s takes groups s, s + nslices, s + 2*nslices, ...
+// A lane streams the row's 16-byte W_nonzero and W_negative fields of each of
+// its groups (R lanes of a slice read R*16 contiguous bytes of the tiled
+// layout).  Every weight load of the run is issued first; while they are in
+// flight the workgroup turns the activations into bit planes once, in LDS
+// (encode once, reuse for every row: the brief's section 6 rule).  The inner
+// loop is AND + POPCOUNT of each weight plane against the eight activation
+// bit planes: the signed population C = N - 2*Nneg of the brief's section 4,
+// per activation bit, weighted 2^b (-128 for the sign bit).  Slices meet by
+// cross-lane shuffles inside a wavefront and through LDS across wavefronts;
+// integer sums make the result independent of that order (integer-engine
+// page, section 3.2).  K beyond the LDS plane capacity is walked in chunks.
 #include "kcommon.h"
 
 namespace bs {
 namespace {
 
-__global__ __launch_bounds__(64) void ternary_gemv_kernel(
-    const uint8_t *__restrict__ planes, const int16_t *__restrict__ pscales,
-    const int8_t *__restrict__ x, int rows, int groups, int gpb, int nsplit, int shift,
-    int64_t *__restrict__ y, unsigned long long *__restrict__ ws_acc,
-    unsigned int *__restrict__ ws_cnt) {
-    const int tile = blockIdx.x / nsplit;
-    const int split = blockIdx.x - tile * nsplit;
-    const int lane = threadIdx.x;
-    const int row = tile * 64 + lane;
-    const int g0 = split * gpb;
-    const int g1 = min(groups, g0 + gpb);
+constexpr int kPlaneStride = 9;          // uint4 per group in LDS: 8 planes + 1 pad
+constexpr int kMaxChunkGroups = 216;     // LDS capacity of activation planes, in groups
 
+__device__ __forceinline__ uint64_t transpose8x8(uint64_t q) {
+    // byte i of q = activation of position i; afterwards byte b holds bit b
+    // of the eight positions, position i in bit i
+    uint64_t t;
+    t = (q ^ (q >> 7)) & 0x00AA00AA00AA00AAull;
+    q = q ^ t ^ (t << 7);
+    t = (q ^ (q >> 14)) & 0x0000CCCC0000CCCCull;
+    q = q ^ t ^ (t << 14);
+    t = (q ^ (q >> 28)) & 0x00000000F0F0F0F0ull;
+    q = q ^ t ^ (t << 28);
+    return q;
+}
+
+// Activation bit planes of a chunk of groups, built in two steps so that the
+// activation loads are issued before the weight loads (their data then
+// arrives first and the transposition overlaps the weight latency):
+// load_act() fetches positions 8t..8t+7 of the chunk for thread t (and
+// t + blockDim, ... up to kActPerThread), store_planes() transposes them
+// into LDS: xpl[j*9 + b] holds bit b of the 128 activations of chunk group
+// j, position i at bit i%32 of dword i/32 (the ninth uint4 of each group is
+// padding that spreads neighbouring groups over different LDS banks).
+constexpr int kActPerThread = 4;
+
+__device__ __forceinline__ void load_act(const int8_t *__restrict__ x, int g0, int ng,
+                                         uint2 v[kActPerThread]) {
+#pragma unroll
+    for (int u = 0; u < kActPerThread; ++u) {
+        const int t = threadIdx.x + u * blockDim.x;
+        if (t < ng * 16) v[u] = *reinterpret_cast<const uint2 *>(x + (size_t)g0 * 128 + 8 * t);
+    }
+}
+
+__device__ __forceinline__ void store_planes(const uint2 v[kActPerThread], int ng, uint4 *xpl) {
+    uint8_t *dst = reinterpret_cast<uint8_t *>(xpl);
+#pragma unroll
+    for (int u = 0; u < kActPerThread; ++u) {
+        const int t = threadIdx.x + u * blockDim.x;
+        if (t < ng * 16) {
+            const uint64_t q = transpose8x8((uint64_t)v[u].x | ((uint64_t)v[u].y << 32));
+            const int j = t >> 4, d = (t >> 2) & 3, o = t & 3;
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                dst[((j * kPlaneStride + b) * 4 + d) * 4 + o] = (uint8_t)(q >> (8 * b));
+        }
+    }
+}
+
+// sum_i t_i x_i over one group, from the two weight planes of this lane and
+// the group's activation planes in LDS.  With t_i = nz_i - 2 neg_i (neg a
+// subset of nz) every lane satisfies t_i * m_i = nz_i (m_i xor neg_i) - neg_i,
+// so for activation bit plane b
+//   sum_i t_i m_bi = popcount(nz & (M_b ^ neg)) - popcount(neg),
+// one AND-XOR (a single v_bitop3) and one popcount per 32 weights instead of
+// two of each; over the plane weights w_b (2^b, and -128 for bit 7, summing
+// to -1) the popcount(neg) terms add up to + popcount(neg).
+__device__ __forceinline__ int group_dot_lds(const uint4 &nz, const uint4 &ng,
+                                             const uint4 *__restrict__ xg) {
+    int s = __builtin_popcount(ng.x) + __builtin_popcount(ng.y) + __builtin_popcount(ng.z) +
+            __builtin_popcount(ng.w);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const uint4 m = xg[b];
+        const int q = __builtin_popcount(nz.x & (m.x ^ ng.x)) +
+                      __builtin_popcount(nz.y & (m.y ^ ng.y)) +
+                      __builtin_popcount(nz.z & (m.z ^ ng.z)) +
+                      __builtin_popcount(nz.w & (m.w ^ ng.w));
+        s += (b == 7) ? -q * 128 : q * (1 << b);
+    }
+    return s;
+}
+
+__device__ __forceinline__ int64_t shfl_xor64(int64_t v, int m) {
+    const int lo = __shfl_xor((int)(uint32_t)v, m);
+    const int hi = __shfl_xor((int)(v >> 32), m);
+    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// R rows per block, MAXG groups per slice held in registers per round.
+template <int R, int MAXG>
+__global__ void ternary_rows_kernel(const uint8_t *__restrict__ planes,
+                                    const int16_t *__restrict__ pscales,
+                                    const int8_t *__restrict__ x, int rows, int groups,
+                                    int shift, int64_t *__restrict__ y) {
+    constexpr int S = 64 / R;                       // slices per wavefront
+    __shared__ uint4 xpl[kMaxChunkGroups * kPlaneStride];
+    __shared__ int64_t part[16][R];
+    const int nwaves = blockDim.x >> 6;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rr = lane % R;
+    const int slice = wave * S + lane / R;
+    const int nslices = nwaves * S;
+    const int row = blockIdx.x * R + rr;
+    const int tile = row >> 6, j = row & 63;
+    const bool live = row < rows;
+
+    // a chunk is what the block's threads load in one go (kActPerThread
+    // pieces of 8 positions each), within the LDS capacity
+    const int chunk = min(kMaxChunkGroups, (int)blockDim.x * kActPerThread / 16);
     int64_t acc = 0;
-    for (int g = g0; g < g1; ++g) {
-        const size_t blk = (size_t)tile * groups + g;
-        const uint4 nzv = *reinterpret_cast<const uint4 *>(planes + blk * 2048 + 16 * lane);
-        const uint4 ngv = *reinterpret_cast<const uint4 *>(planes + blk * 2048 + 1024 + 16 * lane);
-        const int sc = pscales[blk * 64 + lane];
-        XPlanes xp;
-        ballot_planes(x + (size_t)g * 128, xp);
-        const uint32_t nz[4] = {nzv.x, nzv.y, nzv.z, nzv.w};
-        const uint32_t ng[4] = {ngv.x, ngv.y, ngv.z, ngv.w};
-        const int s = group_dot(nz, ng, xp);
-        acc += (int64_t)((s * sc) >> shift);   // arithmetic shift = floor
+    for (int c0 = 0; c0 < groups; c0 += chunk) {
+        const int cg = min(chunk, groups - c0);
+        if (c0 > 0) __syncthreads();                    // previous chunk's planes are consumed
+        uint2 act[kActPerThread];
+        load_act(x, c0, cg, act);
+        // rounds of MAXG groups per slice inside the chunk
+        for (int r0 = 0; r0 < cg; r0 += MAXG * nslices) {
+            uint4 wnz[MAXG], wng[MAXG];
+            int sc[MAXG];
+#pragma unroll
+            for (int q = 0; q < MAXG; ++q) {
+                const int g = c0 + r0 + slice + q * nslices;
+                if (live && g < c0 + cg) {
+                    const size_t blk = (size_t)tile * groups + g;
+                    wnz[q] = load_stream16(planes + blk * 2048 + 16 * j);
+                    wng[q] = load_stream16(planes + blk * 2048 + 1024 + 16 * j);
+                    sc[q] = pscales[blk * 64 + j];
+                }
+            }
+            if (r0 == 0) {
+                store_planes(act, cg, xpl);
+                __syncthreads();
+            }
+#pragma unroll
+            for (int q = 0; q < MAXG; ++q) {
+                const int g = c0 + r0 + slice + q * nslices;
+                if (live && g < c0 + cg) {
+                    const int s = group_dot_lds(wnz[q], wng[q], xpl + (g - c0) * kPlaneStride);
+                    acc += (int64_t)((s * sc[q]) >> shift);   // arithmetic shift = floor
+                }
+            }
+        }
     }
+    // slices of one wavefront: lanes rr, rr+R, rr+2R, ...
+#pragma unroll
+    for (int m = R; m < 64; m <<= 1) acc += shfl_xor64(acc, m);
+    if (lane < R) part[wave][lane] = acc;
+    __syncthreads();
+    if (threadIdx.x < R) {
+        int64_t tot = 0;
+        for (int w = 0; w < nwaves; ++w) tot += part[w][threadIdx.x];
+        const int r = blockIdx.x * R + threadIdx.x;
+        if (r < rows) y[r] = tot;
+    }
+}
 
-    if (nsplit == 1) {
-        if (row < rows) y[row] = acc;
-        return;
+struct TernaryCfg {
+    int rows_per_block;   // R: 64, 32 or 16
+    int waves;            // wavefronts per block, 1..16
+    int maxg;             // groups per slice and round held in registers: 1, 2, 4 or 8
+};
+
+template <int R, int G>
+static void launch_rg(int waves, hipStream_t st, const uint8_t *planes, const int16_t *scales,
+                      const int8_t *x, int rows, int groups, int shift, int64_t *y) {
+    const unsigned nblk = (unsigned)((rows + R - 1) / R);
+    hipLaunchKernelGGL((ternary_rows_kernel<R, G>), dim3(nblk), dim3(waves * 64), 0, st, planes,
+                       scales, x, rows, groups, shift, y);
+}
+
+template <int R>
+static bool launch_r(int maxg, int waves, hipStream_t st, const uint8_t *planes,
+                     const int16_t *scales, const int8_t *x, int rows, int groups, int shift,
+                     int64_t *y) {
+    switch (maxg) {
+    case 1: launch_rg<R, 1>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
+    case 2: launch_rg<R, 2>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
+    case 4: launch_rg<R, 4>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
+    case 8: launch_rg<R, 8>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
+    default: return false;
     }
-    if (row < rows) atomicAdd(&ws_acc[row], (unsigned long long)acc);
-    __threadfence();
-    unsigned int prev = 0;
-    if (lane == 0) prev = atomicAdd(&ws_cnt[tile], 1u);
-    prev = __builtin_amdgcn_readfirstlane(prev);
-    if (prev == (unsigned int)(nsplit - 1)) {
-        __threadfence();
-        if (row < rows) y[row] = (int64_t)atomicExch(&ws_acc[row], 0ull);
-        if (lane == 0) atomicExch(&ws_cnt[tile], 0u);
+}
+
+static int32_t launch_ternary(const TernaryCfg &c, const uint8_t *planes, const int16_t *scales,
+                              const int8_t *x, int64_t rows, int64_t k, int32_t frac, int64_t *y,
+                              hipStream_t st) {
+    if (c.waves < 1 || c.waves > 16) return BS_E_RANGE;
+    const int groups = (int)(k / kGroup);
+    const int shift = frac > 31 ? 31 : frac;   // |scale*s| < 2^31: shift 31 is floor
+    bool ok;
+    switch (c.rows_per_block) {
+    case 64: ok = launch_r<64>(c.maxg, c.waves, st, planes, scales, x, (int)rows, groups, shift, y); break;
+    case 32: ok = launch_r<32>(c.maxg, c.waves, st, planes, scales, x, (int)rows, groups, shift, y); break;
+    case 16: ok = launch_r<16>(c.maxg, c.waves, st, planes, scales, x, (int)rows, groups, shift, y); break;
+    default: ok = false;
     }
+    if (!ok) return BS_E_RANGE;
+    BS_LAUNCH_CHECK();
+    return BS_OK;
+}
+
+// Launch shape: the largest block height that still gives one block per CU
+// (256 CUs), then enough wavefronts that each slice holds about two groups.
+static TernaryCfg choose_cfg(int64_t rows, int64_t k) {
+    const int64_t groups = k / kGroup;
+    TernaryCfg c;
+    c.rows_per_block = rows >= 256 * 64 ? 64 : rows >= 256 * 32 ? 32 : 16;
+    const int64_t s = 64 / c.rows_per_block;
+    int64_t waves = (groups + 2 * s - 1) / (2 * s);
+    if (waves < 1) waves = 1;
+    if (waves > 16) waves = 16;
+    c.waves = (int)waves;
+    const int64_t per_slice = (groups + waves * s - 1) / (waves * s);
+    c.maxg = per_slice <= 1 ? 1 : per_slice <= 2 ? 2 : per_slice <= 4 ? 4 : 8;
+    return c;
 }
 
 }  // namespace
@@ -69,38 +240,15 @@ __global__ __launch_bounds__(64) void ternary_gemv_kernel(
 
 using namespace bs;
 
-static size_t ternary_ws_layout(int64_t rows, size_t *cnt_off) {
-    const int64_t R = pad64(rows);
-    const size_t acc_bytes = align_up((size_t)R * 8, kWsAlign);
-    if (cnt_off) *cnt_off = acc_bytes;
-    return acc_bytes + align_up((size_t)(R / 64) * 4, kWsAlign);
-}
-
-extern "C" size_t bs_ternary_gemv_workspace_bytes(int64_t rows, int64_t k) {
-    if (check_rows_k(rows, k, (int64_t)1 << 24) != BS_OK) return 0;
-    return ternary_ws_layout(rows, nullptr);
-}
-
 extern "C" int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales,
                                    const int8_t *x, int64_t rows, int64_t k, int32_t frac,
-                                   int64_t *y, void *workspace, size_t workspace_bytes,
-                                   void *stream) {
+                                   int64_t *y, void *stream) {
     if (!planes || !scales || !x || !y) return BS_E_NULL;
     if (int32_t st = check_rows_k(rows, k, (int64_t)1 << 24)) return st;
     if (frac < 0 || frac > 62) return BS_E_RANGE;
-    size_t cnt_off = 0;
-    const size_t need = ternary_ws_layout(rows, &cnt_off);
-    if (!ws_ok(workspace, workspace_bytes, need)) return BS_E_WORKSPACE;
-
-    const SplitK sk = plan_splitk(rows, k, 2048);
-    // |scale * s| < 2^30, so a shift of 31 already gives floor for any frac >= 31
-    const int shift = frac > 31 ? 31 : frac;
-    unsigned char *ws = static_cast<unsigned char *>(workspace);
-    hipLaunchKernelGGL(ternary_gemv_kernel, dim3((unsigned)(sk.tiles * sk.nsplit)), dim3(64), 0,
-                       (hipStream_t)stream, planes, scales, x, (int)rows, (int)sk.groups,
-                       (int)sk.gpb, (int)sk.nsplit, shift, y,
-                       reinterpret_cast<unsigned long long *>(ws),
-                       reinterpret_cast<unsigned int *>(ws + cnt_off));
-    BS_LAUNCH_CHECK();
-    return BS_OK;
+    if (((uintptr_t)planes & 15) || ((uintptr_t)scales & 1) || ((uintptr_t)x & 7) ||
+        ((uintptr_t)y & 7))
+        return BS_E_ALIGN;
+    return launch_ternary(choose_cfg(rows, k), planes, scales, x, rows, k, frac, y,
+                          (hipStream_t)stream);
 }

@@ -19,7 +19,8 @@
  *     their kernels on `stream` (a hipStream_t passed as void*; NULL = the
  *     default stream) and return after enqueueing.  Results are valid once
  *     the stream reaches that point.  The library never allocates or frees
- *     device memory; scratch space is the caller's `workspace`.
+ *     device memory; entry points that need scratch take the caller's
+ *     `workspace`.
  *   - Fail-loud overflow contract ([IE] section 3.4): a call whose shapes
  *     would let an intermediate exceed its integer type returns
  *     BS_E_OVERFLOW instead of wrapping.
@@ -45,7 +46,8 @@ enum {
     BS_E_RANGE = -3,     /* a value is outside its documented range         */
     BS_E_OVERFLOW = -4,  /* the static bound of the integer types is broken */
     BS_E_HIP = -5,       /* a HIP call or kernel launch failed              */
-    BS_E_WORKSPACE = -6  /* workspace NULL, too small or misaligned         */
+    BS_E_WORKSPACE = -6, /* workspace NULL, too small or misaligned         */
+    BS_E_ALIGN = -7      /* a device pointer lacks its documented alignment */
 };
 
 int32_t bs_abi_version(void);
@@ -97,27 +99,21 @@ int32_t bs_ternary_pack_scales(const int16_t *scales, int64_t rows, int64_t k,
  * (the masked signed sum: zero weights drop out), computed exactly:
  * |s| <= 2^14, |scale*s| <= 2^29 (int32), y accumulated in int64.
  *
- *   planes  device, packed planes (layout above), bs_ternary_planes_bytes
- *   scales  device, packed int16 scales (layout above)
- *   x       device, int8[k] activations (two's complement, -128 allowed)
+ *   planes  device, packed planes (layout above), bs_ternary_planes_bytes,
+ *           16-byte aligned
+ *   scales  device, packed int16 scales (layout above), 2-byte aligned
+ *   x       device, int8[k] activations (two's complement, -128 allowed),
+ *           8-byte aligned
  *   rows    >= 1;  k >= 128, k % 128 == 0, k <= 2^24
  *   frac    0..62: fractional bits of the fixed-point scale; the floor is
  *           applied per group, before the sum over groups
- *   y       device, int64[rows], overwritten
- *   workspace, workspace_bytes
- *           device scratch of at least bs_ternary_gemv_workspace_bytes(rows,
- *           k) bytes, 256-byte aligned.  It must be zero-filled before its
- *           first use; every completed call leaves it zero-filled again, so
- *           one workspace serves any sequence of bs_ternary_gemv calls
- *           ordered on one stream.  Calls that may overlap need separate
- *           workspaces, and a workspace is not shared with other entry
- *           points.
- * Errors: BS_E_NULL, BS_E_SHAPE, BS_E_RANGE (frac), BS_E_WORKSPACE, BS_E_HIP.
+ *   y       device, int64[rows], overwritten, 8-byte aligned
+ *   stream  hipStream_t (as void*) the kernel is enqueued on
+ * No scratch memory: each workgroup owns complete rows.
+ * Errors: BS_E_NULL, BS_E_SHAPE, BS_E_RANGE (frac), BS_E_ALIGN, BS_E_HIP.
  */
-size_t bs_ternary_gemv_workspace_bytes(int64_t rows, int64_t k);
 int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales, const int8_t *x,
-                        int64_t rows, int64_t k, int32_t frac, int64_t *y,
-                        void *workspace, size_t workspace_bytes, void *stream);
+                        int64_t rows, int64_t k, int32_t frac, int64_t *y, void *stream);
 
 /* ======================================================================== */
 /* bs_lns8_phase_gemv -- BitState LNS8 eight-phase GEMV ([BS] sections 3-4)  */
@@ -146,9 +142,13 @@ int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales, const int8
  *           fit int32, else BS_E_OVERFLOW)
  *   acc     device int32[rows][8], overwritten
  *   s       device double[rows], or NULL to skip the materialisation
- *   workspace  as for bs_ternary_gemv (zero-filled before first use, left
- *           zero-filled, not shared with other entry points), at least
- *           bs_lns8_workspace_bytes(rows, k) bytes
+ *   workspace  device scratch of at least bs_lns8_workspace_bytes(rows, k)
+ *           bytes, 256-byte aligned: the split-K accumulators and tile
+ *           counters.  It must be zero-filled before its first use; every
+ *           completed call leaves it zero-filled again, so one workspace
+ *           serves any sequence of calls ordered on one stream.  Calls that
+ *           may overlap need separate workspaces; a workspace is not shared
+ *           with other entry points.
  */
 #define BS_LNS8_DIRECT 0
 #define BS_LNS8_POPCOUNT 1

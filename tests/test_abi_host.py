@@ -22,14 +22,14 @@ FAKE = ctypes.c_void_p(1 << 20)          # never dereferenced: validation fails 
 def test_library_exports_every_header_symbol():
     lib = bs.lib()
     names = bs.header_symbols()
-    assert len(names) >= 16
+    assert len(names) >= 15
     for name in names:
         assert hasattr(lib, name), name
     assert lib.bs_abi_version() == 1
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert bs.status_str(code)
     assert bs.status_str(-99) == "unknown status"
 
@@ -78,16 +78,13 @@ def test_sizes():
     assert lib.bs_ternary_planes_bytes(10, 100) == bs.BS_E_SHAPE
     assert lib.bs_planes03_bytes(128256, 2560) == 128256 * 2560
     assert lib.bs_planes47_bytes(100, 256) == 100 * 256
-    assert lib.bs_ternary_gemv_workspace_bytes(2560, 2560) > 0
-    assert lib.bs_ternary_gemv_workspace_bytes(2560, 2600) == 0
     assert lib.bs_lns8_workspace_bytes(4096, 4096) > 0
     assert lib.bs_lmhead_workspace_bytes(128256, 2560, 40, 200) > 0
     assert lib.bs_lmhead_workspace_bytes(128256, 2560, 201, 200) == 0
 
 
-def _tgemv(planes=FAKE, scales=FAKE, x=FAKE, rows=64, k=128, frac=0, y=FAKE, ws=FAKE,
-           wsn=1 << 20):
-    return bs.lib().bs_ternary_gemv(planes, scales, x, rows, k, frac, y, ws, wsn, None)
+def _tgemv(planes=FAKE, scales=FAKE, x=FAKE, rows=64, k=128, frac=0, y=FAKE):
+    return bs.lib().bs_ternary_gemv(planes, scales, x, rows, k, frac, y, None)
 
 
 def test_ternary_gemv_validation():
@@ -99,9 +96,9 @@ def test_ternary_gemv_validation():
     assert _tgemv(frac=-1) == bs.BS_E_RANGE
     assert _tgemv(frac=63) == bs.BS_E_RANGE
     assert _tgemv(k=(1 << 24) + 128) == bs.BS_E_OVERFLOW
-    assert _tgemv(ws=None) == bs.BS_E_WORKSPACE
-    assert _tgemv(wsn=16) == bs.BS_E_WORKSPACE
-    assert _tgemv(ws=ctypes.c_void_p((1 << 20) + 8)) == bs.BS_E_WORKSPACE
+    assert _tgemv(planes=ctypes.c_void_p((1 << 20) + 8)) == bs.BS_E_ALIGN
+    assert _tgemv(x=ctypes.c_void_p((1 << 20) + 4)) == bs.BS_E_ALIGN
+    assert _tgemv(y=ctypes.c_void_p((1 << 20) + 4)) == bs.BS_E_ALIGN
 
 
 def _lns8(planes=FAKE, x=FAKE, rows=64, k=128, path=0, acc=FAKE, s=FAKE, ws=FAKE, wsn=1 << 20):

@@ -17,21 +17,21 @@ from gpu_util import device, note, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def run(t, sc, x, frac=0, dev=None, ws=None):
+def run(t, sc, x, frac=0, dev=None):
     dev = dev or device()
     rows, k = t.shape
     planes = to_dev(bs.ternary_pack(t), dev)
     scales = to_dev(bs.ternary_pack_scales(sc), dev)
     xd = to_dev(x, dev)
     note("ternary_gemv rows=%d k=%d frac=%d" % (rows, k, frac))
-    y = bs.ternary_gemv(planes, scales, xd, rows, k, frac, workspace=ws)
+    y = bs.ternary_gemv(planes, scales, xd, rows, k, frac)
     import torch
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
 
-def check(t, sc, x, frac=0, ws=None):
-    y = run(t, sc, x, frac, ws=ws)
+def check(t, sc, x, frac=0):
+    y = run(t, sc, x, frac)
     want = oracle.ternary_gemv_def(t, sc, x, frac)
     bad = np.nonzero(y != want)[0]
     assert bad.size == 0, "first mismatch row %d: got %d want %d (%d bad)" % (
@@ -85,17 +85,16 @@ def test_degenerate_values():
         check(t, sc, x)
 
 
-def test_workspace_reuse_and_determinism():
-    import torch
-    dev = device()
-    ws = torch.zeros(bs.lib().bs_ternary_gemv_workspace_bytes(13824, 5120), dtype=torch.uint8,
-                     device=dev)
-    cases = [synth.ternary(13824, 5120, 7), synth.ternary(640, 2560, 8),
-             synth.ternary(2560, 6912, 9), synth.ternary(65, 256, 10)]
-    for t, sc, x in cases:
-        a = run(t, sc, x, ws=ws)
-        b = run(t, sc, x, ws=ws)
+def test_determinism():
+    for t, sc, x in [synth.ternary(13824, 5120, 7), synth.ternary(640, 2560, 8),
+                     synth.ternary(2560, 6912, 9), synth.ternary(65, 256, 10)]:
+        a = run(t, sc, x)
+        b = run(t, sc, x)
         assert (a == b).all()
         assert (a == oracle.ternary_gemv_def(t, sc, x)).all()
-    torch.cuda.synchronize()
-    assert not ws.any().item(), "workspace must be left zero-filled"
+
+
+@pytest.mark.parametrize("k", [128 * 216, 128 * 217, 128 * 450])
+def test_k_beyond_one_lds_chunk(k):
+    """K larger than the activation planes one workgroup keeps in LDS."""
+    check(*synth.ternary(80, k, seed=k, p_zero=1 / 3, act="uniform127"))
