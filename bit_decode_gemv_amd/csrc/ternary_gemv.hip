@@ -12,22 +12,22 @@
 // w*(64/R) + l/R, and slice s takes groups s, s + nslices, s + 2*nslices, ...
 // A lane streams the row's 16-byte W_nonzero and W_negative fields of each of
 // its groups (R lanes of a slice read R*16 contiguous bytes of the tiled
-// layout).  Every weight load of the run is issued first; while they are in
-// flight the workgroup turns the activations into bit planes once, in LDS
-// (encode once, reuse for every row: the brief's section 6 rule).  The inner
-// loop is AND + POPCOUNT of each weight plane against the eight activation
-// bit planes: the signed population C = N - 2*Nneg of the brief's section 4,
-// per activation bit, weighted 2^b (-128 for the sign bit).  Slices meet by
-// cross-lane shuffles inside a wavefront and through LDS across wavefronts;
-// integer sums make the result independent of that order (integer-engine
-// page, section 3.2).  K beyond the LDS plane capacity is walked in chunks.
+// layout).  Work proceeds in rounds of up to MAXG groups per slice: a
+// wavefront issues the activation loads and then every weight load of the
+// round, transposes the activations of its own groups into eight bit planes
+// in a private LDS slot (no workgroup barrier: only the wavefront's own lanes
+// read them), then computes.  The inner loop works on the signed population
+// of the brief's section 4 through the identity t*m = nz*(m xor neg) - neg
+// (t = nz - 2 neg): per 32 weights and activation bit plane b, one
+// AND-XOR (v_bitop3) and one popcount.  Slices meet by cross-lane shuffles
+// inside a wavefront and through LDS across wavefronts; integer sums make
+// the result independent of that order (integer-engine page, section 3.2).
 #include "kcommon.h"
 
 namespace bs {
 namespace {
 
-constexpr int kPlaneStride = 9;          // uint4 per group in LDS: 8 planes + 1 pad
-constexpr int kMaxChunkGroups = 216;     // LDS capacity of activation planes, in groups
+constexpr int kPlaneStride = 9;   // uint4 per group in LDS: 8 planes + 1 pad
 
 __device__ __forceinline__ uint64_t transpose8x8(uint64_t q) {
     // byte i of q = activation of position i; afterwards byte b holds bit b
@@ -42,50 +42,16 @@ __device__ __forceinline__ uint64_t transpose8x8(uint64_t q) {
     return q;
 }
 
-// Activation bit planes of a chunk of groups, built in two steps so that the
-// activation loads are issued before the weight loads (their data then
-// arrives first and the transposition overlaps the weight latency):
-// load_act() fetches positions 8t..8t+7 of the chunk for thread t (and
-// t + blockDim, ... up to kActPerThread), store_planes() transposes them
-// into LDS: xpl[j*9 + b] holds bit b of the 128 activations of chunk group
-// j, position i at bit i%32 of dword i/32 (the ninth uint4 of each group is
-// padding that spreads neighbouring groups over different LDS banks).
-constexpr int kActPerThread = 4;
-
-__device__ __forceinline__ void load_act(const int8_t *__restrict__ x, int g0, int ng,
-                                         uint2 v[kActPerThread]) {
-#pragma unroll
-    for (int u = 0; u < kActPerThread; ++u) {
-        const int t = threadIdx.x + u * blockDim.x;
-        if (t < ng * 16) v[u] = *reinterpret_cast<const uint2 *>(x + (size_t)g0 * 128 + 8 * t);
-    }
-}
-
-__device__ __forceinline__ void store_planes(const uint2 v[kActPerThread], int ng, uint4 *xpl) {
-    uint8_t *dst = reinterpret_cast<uint8_t *>(xpl);
-#pragma unroll
-    for (int u = 0; u < kActPerThread; ++u) {
-        const int t = threadIdx.x + u * blockDim.x;
-        if (t < ng * 16) {
-            const uint64_t q = transpose8x8((uint64_t)v[u].x | ((uint64_t)v[u].y << 32));
-            const int j = t >> 4, d = (t >> 2) & 3, o = t & 3;
-#pragma unroll
-            for (int b = 0; b < 8; ++b)
-                dst[((j * kPlaneStride + b) * 4 + d) * 4 + o] = (uint8_t)(q >> (8 * b));
-        }
-    }
-}
-
 // sum_i t_i x_i over one group, from the two weight planes of this lane and
-// the group's activation planes in LDS.  With t_i = nz_i - 2 neg_i (neg a
+// the group's activation planes xg[0..7] (bit b of the 128 activations,
+// position i at bit i%32 of dword i/32).  With t_i = nz_i - 2 neg_i (neg a
 // subset of nz) every lane satisfies t_i * m_i = nz_i (m_i xor neg_i) - neg_i,
 // so for activation bit plane b
-//   sum_i t_i m_bi = popcount(nz & (M_b ^ neg)) - popcount(neg),
-// one AND-XOR (a single v_bitop3) and one popcount per 32 weights instead of
-// two of each; over the plane weights w_b (2^b, and -128 for bit 7, summing
-// to -1) the popcount(neg) terms add up to + popcount(neg).
-__device__ __forceinline__ int group_dot_lds(const uint4 &nz, const uint4 &ng,
-                                             const uint4 *__restrict__ xg) {
+//   sum_i t_i m_bi = popcount(nz & (M_b ^ neg)) - popcount(neg);
+// over the plane weights w_b (2^b, and -128 for bit 7, summing to -1) the
+// popcount(neg) terms add up to + popcount(neg).
+__device__ __forceinline__ int group_dot(const uint4 &nz, const uint4 &ng,
+                                         const uint4 *__restrict__ xg) {
     int s = __builtin_popcount(ng.x) + __builtin_popcount(ng.y) + __builtin_popcount(ng.z) +
             __builtin_popcount(ng.w);
 #pragma unroll
@@ -106,60 +72,85 @@ __device__ __forceinline__ int64_t shfl_xor64(int64_t v, int m) {
     return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-// R rows per block, MAXG groups per slice held in registers per round.
+// Wait for this wavefront's LDS writes (or reads) to complete; the slot is
+// private to the wavefront, so no workgroup barrier is involved.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt untouched
+    __builtin_amdgcn_wave_barrier();
+}
+
+// R rows per block, up to MAXG groups per slice in flight per round.  The
+// wavefront's LDS slot holds the planes of its (64/R) * MAXG round groups,
+// local index li = q * (64/R) + (slice within the wavefront).
 template <int R, int MAXG>
 __global__ void ternary_rows_kernel(const uint8_t *__restrict__ planes,
                                     const int16_t *__restrict__ pscales,
                                     const int8_t *__restrict__ x, int rows, int groups,
                                     int shift, int64_t *__restrict__ y) {
-    constexpr int S = 64 / R;                       // slices per wavefront
-    __shared__ uint4 xpl[kMaxChunkGroups * kPlaneStride];
+    constexpr int S = 64 / R;                 // slices per wavefront
+    constexpr int LG = S * MAXG;              // groups per wavefront per round
+    constexpr int PASSES = (LG * 16 + 63) / 64;
+    __shared__ uint4 xpl[16][LG * kPlaneStride];
     __shared__ int64_t part[16][R];
     const int nwaves = blockDim.x >> 6;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int rr = lane % R;
-    const int slice = wave * S + lane / R;
+    const int rr = lane % R, sl = lane / R;
     const int nslices = nwaves * S;
+    const int slice0 = wave * S;             // first slice of this wavefront
     const int row = blockIdx.x * R + rr;
     const int tile = row >> 6, j = row & 63;
     const bool live = row < rows;
+    uint4 *const slot = xpl[wave];
+    uint8_t *const slot8 = reinterpret_cast<uint8_t *>(slot);
 
-    // a chunk is what the block's threads load in one go (kActPerThread
-    // pieces of 8 positions each), within the LDS capacity
-    const int chunk = min(kMaxChunkGroups, (int)blockDim.x * kActPerThread / 16);
     int64_t acc = 0;
-    for (int c0 = 0; c0 < groups; c0 += chunk) {
-        const int cg = min(chunk, groups - c0);
-        if (c0 > 0) __syncthreads();                    // previous chunk's planes are consumed
-        uint2 act[kActPerThread];
-        load_act(x, c0, cg, act);
-        // rounds of MAXG groups per slice inside the chunk
-        for (int r0 = 0; r0 < cg; r0 += MAXG * nslices) {
-            uint4 wnz[MAXG], wng[MAXG];
-            int sc[MAXG];
+    for (int r0 = 0; slice0 + r0 * nslices < groups; r0 += MAXG) {
+        // activations of this wavefront's round groups: task = 8 positions
+        uint2 act[PASSES];
 #pragma unroll
-            for (int q = 0; q < MAXG; ++q) {
-                const int g = c0 + r0 + slice + q * nslices;
-                if (live && g < c0 + cg) {
-                    const size_t blk = (size_t)tile * groups + g;
-                    wnz[q] = load_stream16(planes + blk * 2048 + 16 * j);
-                    wng[q] = load_stream16(planes + blk * 2048 + 1024 + 16 * j);
-                    sc[q] = pscales[blk * 64 + j];
-                }
-            }
-            if (r0 == 0) {
-                store_planes(act, cg, xpl);
-                __syncthreads();
-            }
+        for (int p = 0; p < PASSES; ++p) {
+            const int task = lane + 64 * p;
+            const int li = task >> 4;
+            const int g = slice0 + (li % S) + (r0 + li / S) * nslices;
+            if (task < LG * 16 && g < groups)
+                act[p] = *reinterpret_cast<const uint2 *>(x + (size_t)g * 128 + 8 * (task & 15));
+        }
+        uint4 wnz[MAXG], wng[MAXG];
+        int sc[MAXG];
 #pragma unroll
-            for (int q = 0; q < MAXG; ++q) {
-                const int g = c0 + r0 + slice + q * nslices;
-                if (live && g < c0 + cg) {
-                    const int s = group_dot_lds(wnz[q], wng[q], xpl + (g - c0) * kPlaneStride);
-                    acc += (int64_t)((s * sc[q]) >> shift);   // arithmetic shift = floor
-                }
+        for (int q = 0; q < MAXG; ++q) {
+            const int g = slice0 + sl + (r0 + q) * nslices;
+            if (live && g < groups) {
+                const size_t blk = (size_t)tile * groups + g;
+                wnz[q] = load_stream16(planes + blk * 2048 + 16 * j);
+                wng[q] = load_stream16(planes + blk * 2048 + 1024 + 16 * j);
+                sc[q] = pscales[blk * 64 + j];
             }
         }
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const int task = lane + 64 * p;
+            const int li = task >> 4;
+            const int g = slice0 + (li % S) + (r0 + li / S) * nslices;
+            if (task < LG * 16 && g < groups) {
+                const uint64_t t8 = transpose8x8((uint64_t)act[p].x | ((uint64_t)act[p].y << 32));
+                const int piece = task & 15, d = piece >> 2, o = piece & 3;
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    slot8[((li * kPlaneStride + b) * 4 + d) * 4 + o] = (uint8_t)(t8 >> (8 * b));
+            }
+        }
+        wave_lds_fence();
+#pragma unroll
+        for (int q = 0; q < MAXG; ++q) {
+            const int g = slice0 + sl + (r0 + q) * nslices;
+            if (live && g < groups) {
+                const int s = group_dot(wnz[q], wng[q], slot + (q * S + sl) * kPlaneStride);
+                acc += (int64_t)((s * sc[q]) >> shift);   // arithmetic shift = floor
+            }
+        }
+        wave_lds_fence();   // the next round overwrites the slot
     }
     // slices of one wavefront: lanes rr, rr+R, rr+2R, ...
 #pragma unroll
@@ -177,7 +168,7 @@ __global__ void ternary_rows_kernel(const uint8_t *__restrict__ planes,
 struct TernaryCfg {
     int rows_per_block;   // R: 64, 32 or 16
     int waves;            // wavefronts per block, 1..16
-    int maxg;             // groups per slice and round held in registers: 1, 2, 4 or 8
+    int maxg;             // groups per slice and round held in registers: 1, 2 or 4
 };
 
 template <int R, int G>
@@ -196,7 +187,6 @@ static bool launch_r(int maxg, int waves, hipStream_t st, const uint8_t *planes,
     case 1: launch_rg<R, 1>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
     case 2: launch_rg<R, 2>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
     case 4: launch_rg<R, 4>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
-    case 8: launch_rg<R, 8>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
     default: return false;
     }
 }
@@ -231,7 +221,7 @@ static TernaryCfg choose_cfg(int64_t rows, int64_t k) {
     if (waves > 16) waves = 16;
     c.waves = (int)waves;
     const int64_t per_slice = (groups + waves * s - 1) / (waves * s);
-    c.maxg = per_slice <= 1 ? 1 : per_slice <= 2 ? 2 : per_slice <= 4 ? 4 : 8;
+    c.maxg = per_slice <= 1 ? 1 : per_slice <= 2 ? 2 : 4;
     return c;
 }
 
