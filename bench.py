@@ -1,0 +1,360 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-1 ternary decode GEMV hot path on one MI355X.
+
+One step = one BitNet-b1.58-2B-shaped decode layer's seven projection GEMVs
+(q 2560x2560, k 640x2560, v 640x2560, o 2560x2560, gate 6912x2560,
+up 6912x2560, down 2560x6912), each one bs_ternary_gemv call on packed
+ternary planes (0.25 B/weight) plus int16 group scales, int8 activations,
+exact int64 outputs.  Steps walk a pool of distinct layers whose weights total
+more than 1 GiB, so every GEMV streams its weights from HBM rather than the
+256 MB Infinity Cache; inputs are resident in HBM before the timed region.
+
+Timing: the K timed steps are captured once in a HIP graph and replayed on one
+stream between two HIP events (plus a host wall clock).  `value` is the
+weight-stream throughput of the whole job: weight bytes of all K steps over
+the elapsed time.  The roofline entry is for the dominant kernel (the one
+with the largest share of step time): its algorithmic bytes per launch over
+its average launch duration, measured with HIP events around a graph of
+back-to-back launches of that kernel alone on the same stream.
+
+Extra entries ("ops") time the other workloads of the path: the larger-K
+GEMVs, the LNS8 eight-phase GEMV (both reductions) and the BITNET_PLANES
+lm_head top-k.  `cpu_baseline` times the plain C oracle, single-threaded, on
+a bounded sample of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
+       python bench.py --trace-summary <rocprofv3 kernel_trace.csv>
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+METRIC = "ternary GEMV weight-stream GB/s & % HBM peak, batch-1, K=2560..5120"
+LAYER = [("q", 2560, 2560), ("k", 640, 2560), ("v", 640, 2560), ("o", 2560, 2560),
+         ("gate", 6912, 2560), ("up", 6912, 2560), ("down", 2560, 6912)]
+
+
+def weight_bytes(rows: int, k: int) -> int:
+    """Algorithmic weight-stream bytes of one GEMV: planes (k/4 per row) plus
+    int16 scales (2 bytes per 128 weights)."""
+    return rows * k // 4 + rows * (k // 128) * 2
+
+
+def log(msg: str):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """Graph replay timing on one stream with HIP events."""
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+
+    def graph(self, fn, n):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            with torch.cuda.graph(g, stream=self.stream):
+                for i in range(n):
+                    fn(i)
+        return g
+
+    def replay_us(self, g, reps=1):
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record(self.stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) * 1000.0, wall * 1e6
+
+
+def per_launch_us(timer, fn, n=200, reps=5):
+    g = timer.graph(fn, n)
+    timer.replay_us(g)                         # warm
+    us, _ = timer.replay_us(g, reps)
+    return us / (n * reps)
+
+
+def make_pool(torch, bs, synth, dev, rows, k, seed, min_bytes):
+    """Packed planes/scales for one shape, replicated into distinct buffers
+    totalling at least min_bytes."""
+    t, sc, x = synth.ternary(rows, k, seed)
+    p = torch.from_numpy(bs.ternary_pack(t)).to(dev)
+    s = torch.from_numpy(bs.ternary_pack_scales(sc)).to(dev)
+    n = max(2, -(-min_bytes // weight_bytes(rows, k)))
+    return [p.clone() for _ in range(n)], [s.clone() for _ in range(n)], torch.from_numpy(x).to(dev)
+
+
+def cpu_baseline(seconds_target: float):
+    """The oracle's definition-form GEMV, single-threaded, over the step's
+    seven shapes at full size (seed 0), repeated until about seconds_target
+    of CPU time; reported in the metric's unit (weight-stream bytes per
+    second of the packed format the GPU reads)."""
+    import numpy as np
+    import oracle
+    from bit_decode_gemv_amd import synth
+    cases = [synth.ternary(r, k, 0) for _, r, k in LAYER]
+    step_bytes = sum(weight_bytes(r, k) for _, r, k in LAYER)
+    done, t_cpu = 0, 0.0
+    while t_cpu < seconds_target:
+        for t, sc, x in cases:
+            t0 = time.process_time()
+            oracle.ternary_gemv_def(t, sc, x)
+            t_cpu += time.process_time() - t0
+        done += 1
+    gbs = done * step_bytes / t_cpu / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full step(s) (q,k,v,o,gate,up,down at full size, seed 0) through "
+                      "or_ternary_gemv_def on unpacked int8 trits, single thread, %.1f s CPU"
+                      % (done, t_cpu),
+            "cpu_model": _cpu_model(), "ms_per_step": round(1000.0 * t_cpu / done, 2)}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _source_digest():
+    h = hashlib.sha256()
+    path = os.path.join(ROOT, "bit_decode_gemv_amd", "csrc", "ternary_gemv.hip")
+    with open(path, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _recorded_traffic(shape_tag: str):
+    """HBM bytes per launch recorded by rocprofv3 --pmc runs (FETCH_SIZE and
+    WRITE_SIZE, scaled by the copy-kernel calibration), stored as text under
+    profiles/.  Returned only if the kernel source has not changed since."""
+    path = os.path.join(ROOT, "profiles", "ternary_gemv_%s_hbm_traffic.txt" % shape_tag)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != _source_digest():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def run_extras(torch, bs, synth, dev, timer):
+    ops = {}
+    # larger-K GEMVs
+    for rows, k in synth.LARGE_K_SHAPES:
+        ps, ss, x = make_pool(torch, bs, synth, dev, rows, k, 0, 1 << 30)
+        y = torch.empty(rows, dtype=torch.int64, device=dev)
+        us = per_launch_us(timer, lambda i: bs.ternary_gemv(ps[i % len(ps)], ss[i % len(ss)], x,
+                                                            rows, k, out=y), n=100)
+        wb = weight_bytes(rows, k)
+        ops["ternary_gemv_%dx%d" % (rows, k)] = {
+            "us_per_gemv": round(us, 3), "weight_bytes": wb, "GBps": round(wb / us / 1e3, 1),
+            "frac_hbm_peak": round(wb / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del ps, ss
+        log("ternary %dx%d: %.2f us" % (rows, k, us))
+    # LNS8 eight-phase GEMV, 4096 x 4096
+    t8, x8 = synth.lns8(4096, 4096, 0)
+    p8 = torch.from_numpy(bs.ternary_pack(t8)).to(dev)
+    pool8 = [p8.clone() for _ in range(-(-(1 << 30) // p8.numel()))]
+    xd8 = torch.from_numpy(x8).to(dev)
+    acc = torch.empty((4096, 8), dtype=torch.int32, device=dev)
+    s8 = torch.empty(4096, dtype=torch.float64, device=dev)
+    ws8 = torch.zeros(bs.lib().bs_lns8_workspace_bytes(4096, 4096), dtype=torch.uint8, device=dev)
+    for path, name in ((bs.LNS8_DIRECT, "direct"), (bs.LNS8_POPCOUNT, "popcount")):
+        us = per_launch_us(timer, lambda i: bs.lns8_phase_gemv(pool8[i % len(pool8)], xd8, 4096,
+                                                               4096, path, acc=acc, s=s8,
+                                                               workspace=ws8), n=100)
+        ops["lns8_4096x4096_" + name] = {
+            "us_per_gemv": round(us, 3), "weight_bytes": p8.numel(),
+            "GBps": round(p8.numel() / us / 1e3, 1),
+            "frac_hbm_peak": round(p8.numel() / us / 1e3 / HBM_PEAK_GBS, 4),
+            "weights_per_s": round(4096 * 4096 / us * 1e6, 1)}
+        log("lns8 %s: %.2f us" % (name, us))
+    del pool8
+    # BITNET_PLANES lm_head, 128256 x 2560, top-40, cap 200
+    V, K = synth.LMHEAD_SHAPE
+    trits, rs, h = synth.lmhead(V, K, 0)
+    p03, p47 = bs.planes_pack(trits)
+    del trits
+    d03, d47 = torch.from_numpy(p03).to(dev), torch.from_numpy(p47).to(dev)
+    drs, dh = torch.from_numpy(rs).to(dev), torch.from_numpy(h).to(dev)
+    pool03 = [d03] + [d03.clone() for _ in range(3)]       # > 1 GiB of planes 0-3
+    idx = torch.empty(40, dtype=torch.int32, device=dev)
+    sc = torch.empty(40, dtype=torch.int64, device=dev)
+    info = torch.empty(2, dtype=torch.int32, device=dev)
+    wsl = torch.zeros(bs.lib().bs_lmhead_workspace_bytes(V, K, 40, 200), dtype=torch.uint8,
+                      device=dev)
+    us = per_launch_us(timer, lambda i: bs.lmhead_planes_topk(
+        pool03[i % 4], d47, drs, dh, V, K, 40, 200, top_idx=idx, top_score=sc, info=info,
+        workspace=wsl), n=20, reps=3)
+    stage1_bytes = p03.size + rs.nbytes
+    ops["lmhead_planes_topk_128256x2560"] = {
+        "us_per_call": round(us, 3), "stage1_bytes": stage1_bytes,
+        "GBps_stage1_bytes": round(stage1_bytes / us / 1e3, 1),
+        "frac_hbm_peak": round(stage1_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
+        "n_candidates": int(info[0].item()), "capped": int(info[1].item())}
+    log("lm_head: %.2f us" % us)
+    return ops
+
+
+def trace_summary(path: str):
+    """Per (kernel, grid) durations from a rocprofv3 --kernel-trace CSV."""
+    rows = list(csv.DictReader(open(path)))
+    groups = {}
+    for r in rows:
+        name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+        key = (name, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = []
+    for (name, grid, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        out.append("%-70s grid %8d wg %4d calls %6d avg %8.3f us median %8.3f us min %8.3f us"
+                   % (name[:70], grid, wg, len(d), statistics.mean(d) / 1e3,
+                      statistics.median(d) / 1e3, min(d) / 1e3))
+    return "\n".join(out)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extras", action="store_true", help="skip the non-headline workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--trace-summary", help="summarise a rocprofv3 kernel_trace.csv and exit")
+    args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return 0
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the GEMVs would "
+              "shard by rows with one all-gather, or by K with one int64 all-reduce); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    import bit_decode_gemv_amd as bs
+    from bit_decode_gemv_amd import synth
+
+    dev = torch.device("cuda:0")
+    bs.lib()
+    stream = torch.cuda.Stream(device=dev)
+    timer = Timer(torch, stream)
+
+    # layer pool: distinct weights for every layer, > 1 GiB in total
+    step_bytes = sum(weight_bytes(r, k) for _, r, k in LAYER)
+    n_layers = -(-(1 << 30) // step_bytes) + 1
+    log("building %d layers of synthetic BitNet-2B projections (%.1f MB each)" % (
+        n_layers, step_bytes / 1e6))
+    base = {}
+    for li, (name, r, k) in enumerate(LAYER):
+        t, sc, x = synth.ternary(r, k, li)
+        base[name] = (torch.from_numpy(bs.ternary_pack(t)).to(dev),
+                      torch.from_numpy(bs.ternary_pack_scales(sc)).to(dev),
+                      torch.from_numpy(x).to(dev))
+    layers = [{name: (base[name][0].clone(), base[name][1].clone()) for name, _, _ in LAYER}
+              for _ in range(n_layers)]
+    ys = {name: torch.empty(r, dtype=torch.int64, device=dev) for name, r, _ in LAYER}
+
+    def step(i):
+        lay = layers[i % n_layers]
+        for name, r, k in LAYER:
+            p, s = lay[name]
+            bs.ternary_gemv(p, s, base[name][2], r, k, out=ys[name])
+
+    # warmup, then the timed graph of exactly `steps` steps
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize()
+    g = timer.graph(lambda i: step(args.warmup + i), args.steps)
+    timer.replay_us(g)                          # first replay uploads the graph
+    us, wall_us = timer.replay_us(g)
+    ms_per_step = us / 1000.0 / args.steps
+    value = step_bytes * args.steps / (us * 1e-6) / 1e9
+    log("step: %.3f ms (events), %.3f ms (host wall) -> %.1f GB/s" % (
+        ms_per_step, wall_us / 1000.0 / args.steps, value))
+
+    # per-shape launch durations; the dominant kernel is the one with the
+    # largest share of the step
+    shape_us = {}
+    for name, r, k in LAYER:
+        if name in ("v", "up"):          # same shape as k / gate
+            continue
+        shape_us[(r, k)] = per_launch_us(
+            timer, lambda i, name=name, r=r, k=k: bs.ternary_gemv(
+                layers[i % n_layers][name][0], layers[i % n_layers][name][1], base[name][2], r,
+                k, out=ys[name]))
+    counts = {}
+    for _, r, k in LAYER:
+        counts[(r, k)] = counts.get((r, k), 0) + 1
+    dom = max(shape_us, key=lambda s: shape_us[s] * counts[s])
+    dom_us = shape_us[dom]
+    dom_bytes = weight_bytes(*dom)
+    achieved = dom_bytes / dom_us / 1e3
+    tag = "%dx%d" % dom
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": _recorded_traffic(tag),
+                "kernel": "ternary_rows_kernel %s (%d launches per step)" % (tag, counts[dom]),
+                "us_per_launch": round(dom_us, 3), "bytes_per_launch": dom_bytes}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int64",
+        "data": "synthetic",
+        "config": {"workload": "bitnet-b1.58-2B decode projections q,k,v,o,gate,up,down, "
+                               "batch 1, one bs_ternary_gemv launch each",
+                   "shapes": {n: "%dx%d" % (r, k) for n, r, k in LAYER},
+                   "weight_bytes_per_step": step_bytes, "layers_in_pool": n_layers,
+                   "pool_bytes": step_bytes * n_layers, "parallelism": "single GPU",
+                   "frac_hbm_peak_whole_job": round(value / HBM_PEAK_GBS, 4),
+                   "host_wall_ms_per_step": round(wall_us / 1000.0 / args.steps, 5),
+                   "us_per_gemv": {"%dx%d" % s: round(v, 3) for s, v in shape_us.items()}},
+        "roofline": roofline,
+    }
+    if not args.no_extras:
+        out["ops"] = run_extras(torch, bs, synth, dev, timer)
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (~%.0f s)" % args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -209,19 +209,30 @@ static int32_t launch_ternary(const TernaryCfg &c, const uint8_t *planes, const 
     return BS_OK;
 }
 
-// Launch shape: the largest block height that still gives one block per CU
-// (256 CUs), then enough wavefronts that each slice holds about two groups.
+// Launch shape, from a sweep of block heights and wavefront counts on
+// MI355X: 64-row blocks when there are enough tiles to give every CU one
+// block; otherwise 16-row blocks (four slices per wavefront) with one group
+// per slice, or 32-row blocks for long rows with many rows.
 static TernaryCfg choose_cfg(int64_t rows, int64_t k) {
-    const int64_t groups = k / kGroup;
+    const int64_t groups = k / kGroup, tiles = pad64(rows) / 64;
+    auto maxg_for = [](int64_t per) { return per <= 1 ? 1 : per <= 2 ? 2 : 4; };
     TernaryCfg c;
-    c.rows_per_block = rows >= 256 * 64 ? 64 : rows >= 256 * 32 ? 32 : 16;
-    const int64_t s = 64 / c.rows_per_block;
-    int64_t waves = (groups + 2 * s - 1) / (2 * s);
-    if (waves < 1) waves = 1;
-    if (waves > 16) waves = 16;
-    c.waves = (int)waves;
-    const int64_t per_slice = (groups + waves * s - 1) / (waves * s);
-    c.maxg = per_slice <= 1 ? 1 : per_slice <= 2 ? 2 : 4;
+    if (tiles >= 200) {
+        c.rows_per_block = 64;
+        c.waves = 16;
+    } else if (groups <= 64) {
+        c.rows_per_block = 16;
+        int64_t w = (groups + 3) / 4;
+        c.waves = (int)(w < 8 ? 8 : w > 16 ? 16 : w);
+    } else if (rows >= 5000) {
+        c.rows_per_block = 32;
+        c.waves = 16;
+    } else {
+        c.rows_per_block = 16;
+        c.waves = 16;
+    }
+    const int64_t nslices = (int64_t)c.waves * (64 / c.rows_per_block);
+    c.maxg = maxg_for((groups + nslices - 1) / nslices);
     return c;
 }
 
