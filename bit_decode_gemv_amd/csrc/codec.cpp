@@ -8,6 +8,8 @@
 // The codec runs once at load time, on the host, synchronously.
 #include <string.h>
 
+#include <vector>
+
 #include "bs_internal.h"
 
 using namespace bs;
@@ -115,29 +117,38 @@ extern "C" int64_t bs_planes47_bytes(int64_t vocab, int64_t dim) {
     return st ? st : vocab * dim;
 }
 
+// Planes 0-3 and 4-7 of a position are stored as their balanced-ternary
+// digit sums (27, 9, 3, 1 weights): one int8 in [-40, 40] per position for
+// each half, which keeps the four trits and costs the same byte as four pairs
+// of bitplane bits.  The half read by the full-vocabulary scan is tiled in
+// 16-position runs (run c of row j of a 64-row tile at 1024c + 16j of the
+// tile's 8192-byte group block); the other half is row major.
 extern "C" int32_t bs_planes_pack(const int8_t *trits, int64_t vocab, int64_t dim,
                                   uint8_t *planes03, uint8_t *planes47) {
     if (!trits || !planes03 || !planes47) return BS_E_NULL;
     if (int32_t st = codec_shape(vocab, dim)) return st;
     const int64_t G = dim / kGroup, R = pad64(vocab);
     memset(planes03, 0, (size_t)(R * dim));
+    std::vector<int8_t> hi((size_t)dim);
     for (int64_t r = 0; r < vocab; ++r) {
-        const int64_t tile = r / kTileRows, j = r % kTileRows;
-        for (int q = 0; q < 8; ++q) {
-            const int8_t *row = trits + (r * 8 + q) * dim;
-            for (int64_t g = 0; g < G; ++g) {
-                uint8_t *nz, *neg;
-                if (q < 4) {
-                    uint8_t *blk = planes03 + (tile * G + g) * 8192 + 2048 * q;
-                    nz = blk + 16 * j;
-                    neg = blk + 1024 + 16 * j;
-                } else {
-                    nz = planes47 + r * dim + 128 * g + 32 * (q - 4);
-                    neg = nz + 16;
-                }
-                if (!group_masks(row + g * kGroup, nz, neg)) return BS_E_RANGE;
+        const int8_t *tr = trits + r * 8 * dim;
+        int8_t *lo = reinterpret_cast<int8_t *>(planes47 + r * dim);
+        for (int64_t i = 0; i < dim; ++i) {
+            int a = 0, b = 0;
+            for (int q = 0; q < 4; ++q) {
+                const int8_t u = tr[q * dim + i], v = tr[(q + 4) * dim + i];
+                if (u < -1 || u > 1 || v < -1 || v > 1) return BS_E_RANGE;
+                a = 3 * a + u;
+                b = 3 * b + v;
             }
+            hi[(size_t)i] = (int8_t)a;
+            lo[i] = (int8_t)b;
         }
+        const int64_t tile = r / kTileRows, j = r % kTileRows;
+        for (int64_t g = 0; g < G; ++g)
+            for (int c = 0; c < 8; ++c)
+                memcpy(planes03 + (tile * G + g) * 8192 + 1024 * c + 16 * j,
+                       hi.data() + g * kGroup + 16 * c, 16);
     }
     return BS_OK;
 }

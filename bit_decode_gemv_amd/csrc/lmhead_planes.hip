@@ -5,32 +5,71 @@
 // rowScale * (sum_{p=4..7} 3^-p) * sum|h|, rescoring of every row whose
 // upper bound reaches the k-th best lower bound, and the maxCandidates cap).
 //
-// Scores are exact int64 in units of 3^-7.  Four kernels on one stream, no
-// host synchronisation:
-//   1. stage1  -- 8 wavefronts per workgroup, one 64-row tile each (lane =
-//                 row), streaming planes 0-3 (8 KB per tile and group) with
-//                 AND+POPCOUNT against ballot-built bit planes of h; writes
-//                 S1' and E1 per row and the workgroup's top_k lower bounds;
-//   2. select  -- one workgroup: L_k = top_k-th largest of those lists
-//                 (MSB-first radix select on the order-preserving key);
-//   3. filter  -- every row: U >= L_k appends the row to the candidate list;
-//   4. finish  -- one workgroup: apply the cap (radix select of the top cap
-//                 rows by S1' then index), rescore with planes 4-7, bitonic
-//                 sort by (S' desc, index asc), write top-k and info, and
-//                 re-zero the workspace counter.
+// Scores are exact int64 in units of 3^-7.  The planes are stored as digit
+// sums (D03 = sum_{p<4} 3^(3-p) T_p and D47 = sum_{p>=4} 3^(7-p) T_p, one
+// int8 each per position), so E1 = D03 . h and E2 = D47 . h are int8 dot
+// products: four products per v_dot4 instruction instead of bit-plane
+// popcounts.  Four kernels on one stream, no host synchronisation, no global
+// atomics:
+//   stage1  -- 16 wavefronts per workgroup over 8 tiles of 64 rows (lane =
+//              row), two wavefronts per tile splitting the groups; D03 is
+//              streamed with 16-byte non-temporal loads (two groups in flight
+//              per wavefront) against h read through the scalar path.  Writes
+//              E1 and the lower bound L per row, and the largest L of every
+//              tile and of every workgroup;
+//   select  -- one workgroup: L_k = the top_k-th largest L.  The top_k-th
+//              largest workgroup maximum T is a lower bound on L_k (top_k
+//              distinct rows reach it), so only the rows >= T of the tiles
+//              whose maximum reaches T take part, usually a few dozen;
+//   filter  -- every row with U >= L_k becomes a candidate, is rescored at
+//              once (E2 from D47, the wavefront's lanes over its candidates'
+//              16-byte runs) and is stored in its workgroup's region of the
+//              candidate arrays, sorted by (S1' desc, row asc).  Rows that the
+//              cap later drops are rescored for nothing, one read of their
+//              D47 row, which keeps the pass single;
+//   finish  -- one workgroup: the cap (the max_candidates candidates with the
+//              largest S1', lowest row first; the max_candidates-th largest
+//              region head bounds it from below, so only region prefixes are
+//              read), then the top_k of the kept rows by (S' desc, row asc).
 #include "kcommon.h"
 
 namespace bs {
 namespace {
 
-constexpr int kStage1Waves = 8;
-constexpr int kStage1Threads = kStage1Waves * 64;
-constexpr int kFinishThreads = 1024;
+constexpr int kTilesPerBlock = 8;
+constexpr int kWavesPerTile = 2;
+constexpr int kStage1Rows = kTilesPerBlock * 64;                       // 512
+constexpr int kStage1Threads = kTilesPerBlock * kWavesPerTile * 64;    // 1024
+constexpr int kFilterRows = 256;                                       // 4 tiles
+constexpr int kBlockThreads = 1024;     // select and finish
+constexpr int kSelTiles = 1024;         // select: tiles gathered
+constexpr int kSelList = 4096;          // select: pruned bounds kept in LDS
+constexpr int kFinList = 512;           // finish: pruned candidates kept in LDS
+constexpr int kFinKpt = 4;              // finish fallback: candidates per thread in registers
 constexpr int kMaxCap = 4096;
+constexpr int kMaxGroups = 79;          // 10112 / 128
+constexpr int kResU = 4;                // rescoring: 16-byte runs in flight per lane
+constexpr long long kNoRow = (long long)0x8000000000000000ull;
 
 // Order-preserving map of int64 onto uint64.
 __device__ __forceinline__ unsigned long long okey(long long v) {
     return (unsigned long long)v ^ 0x8000000000000000ull;
+}
+
+// Tie-break key: larger for a lower row index.
+__device__ __forceinline__ unsigned long long tie_key(int row) {
+    return 0xFFFFFFFFull - (unsigned)row;
+}
+
+// (key desc, row asc)
+__device__ __forceinline__ bool better(long long ka, int ia, long long kb, int ib) {
+    return ka > kb || (ka == kb && ia < ib);
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt untouched
+    __builtin_amdgcn_wave_barrier();
 }
 
 __device__ __forceinline__ int wave_sum(int v) {
@@ -39,247 +78,588 @@ __device__ __forceinline__ int wave_sum(int v) {
     return v;
 }
 
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+    const unsigned lo = (unsigned)__shfl_xor((int)(unsigned)v, m);
+    const unsigned hi = (unsigned)__shfl_xor((int)(unsigned)(v >> 32), m);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// 16 int8 weights against 16 int8 activations, added to acc.
+__device__ __forceinline__ int dot16(const uint4 &w, int h0, int h1, int h2, int h3, int acc) {
+    acc = __builtin_amdgcn_sdot4((int)w.x, h0, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)w.y, h1, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)w.z, h2, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)w.w, h3, acc, false);
+    return acc;
+}
+
+__device__ __forceinline__ int abs_bytes(int v) {
+    return abs((int)(int8_t)v) + abs((int)(int8_t)(v >> 8)) + abs((int)(int8_t)(v >> 16)) +
+           abs(v >> 24);
+}
+
 struct LmhWs {
-    long long *s1;          // [V]   stage-1 score S1'
-    int *e1;                // [V]   E1
-    long long *lower;       // [nwg * top_k] per-workgroup best lower bounds
     long long *scalars;     // [0] = L_k, [1] = sum|h|
-    unsigned int *count;    // [1]   candidate count (zero between calls)
-    int *cand;              // [V]   candidate rows
+    int *e1;                // [V] E1
+    long long *lower;       // [V] L
+    long long *tile_max;    // [tiles] largest L of each 64-row tile
+    long long *wg_max;      // [nwg] largest L of each stage-1 workgroup
+    int *region_count;      // [nwf] candidates per filter workgroup
+    int *cand;              // [nwf * 256] candidate rows, per-workgroup regions
+    long long *cand_s1;     // [nwf * 256] their S1'
+    long long *cand_s;      // [nwf * 256] their S'
+    int *cc;                // [V] compacted candidates (more regions than one pass scans)
+    long long *cc_s1;       // [V]
+    long long *cc_s;        // [V]
 };
 
 // ---------------------------------------------------------------- stage 1
 __global__ __launch_bounds__(kStage1Threads) void lmh_stage1(
     const uint8_t *__restrict__ planes03, const int32_t *__restrict__ row_scale,
-    const int8_t *__restrict__ h, int vocab, int groups, int dim, int top_k, LmhWs ws) {
-    __shared__ long long lds_l[kStage1Threads];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int32_t *__restrict__ hw, int vocab, int groups, LmhWs ws) {
+    __shared__ int e1_part[kTilesPerBlock * kWavesPerTile][64];
+    __shared__ int habs_part[kTilesPerBlock * kWavesPerTile];
+    __shared__ long long tmax[kTilesPerBlock];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int tloc = wave / kWavesPerTile, half = wave % kWavesPerTile;
     const int tiles = (vocab + 63) / 64;
-    const int tile = blockIdx.x * kStage1Waves + wave;
-    const int row = tile * 64 + lane;
-
-    // sum |h| (each wavefront computes it; all agree)
-    int habs_part = 0;
-    for (int i = lane; i < dim; i += 64) habs_part += abs((int)h[i]);
-    const long long habs = wave_sum(habs_part);
-
-    long long lower = (long long)0x8000000000000000ull;   // "no row"
+    const int tile = blockIdx.x * kTilesPerBlock + tloc;
+    int e1 = 0;
     if (tile < tiles) {
-        int e1 = 0;
-        for (int g = 0; g < groups; ++g) {
-            XPlanes xp;
-            ballot_planes(h + (size_t)g * 128, xp);
-            const uint8_t *blk = planes03 + ((size_t)tile * groups + g) * 8192 + 16 * lane;
+        const uint8_t *tbase = planes03 + (size_t)tile * groups * 8192 + 16 * lane;
+        // this wavefront takes groups half, half + 2, ...; two in flight
+        for (int g0 = half; g0 < groups; g0 += 2 * kWavesPerTile) {
+            const int g1 = g0 + kWavesPerTile;
+            const bool has1 = g1 < groups;
+            uint4 a[8], b[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint4 nzv = *reinterpret_cast<const uint4 *>(blk + 2048 * q);
-                const uint4 ngv = *reinterpret_cast<const uint4 *>(blk + 2048 * q + 1024);
-                const uint32_t nz[4] = {nzv.x, nzv.y, nzv.z, nzv.w};
-                const uint32_t ng[4] = {ngv.x, ngv.y, ngv.z, ngv.w};
-                const int pw = q == 0 ? 27 : q == 1 ? 9 : q == 2 ? 3 : 1;   // 3^(3-q)
-                e1 += pw * group_dot(nz, ng, xp);
+            for (int c = 0; c < 8; ++c) a[c] = load_stream16(tbase + (size_t)g0 * 8192 + 1024 * c);
+            if (has1) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    b[c] = load_stream16(tbase + (size_t)g1 * 8192 + 1024 * c);
+            }
+            const int32_t *ha0 = hw + g0 * 32;      // uniform: scalar loads
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                e1 = dot16(a[c], ha0[4 * c], ha0[4 * c + 1], ha0[4 * c + 2], ha0[4 * c + 3], e1);
+            if (has1) {
+                const int32_t *hb0 = hw + g1 * 32;
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    e1 = dot16(b[c], hb0[4 * c], hb0[4 * c + 1], hb0[4 * c + 2], hb0[4 * c + 3],
+                               e1);
             }
         }
+    }
+    // sum|h| (h is in the caches by now)
+    int ha = 0;
+    for (int w = threadIdx.x; w < groups * 32; w += kStage1Threads) ha += abs_bytes(hw[w]);
+    ha = wave_sum(ha);
+    if (lane == 0) habs_part[wave] = ha;
+    e1_part[wave][lane] = e1;
+    __syncthreads();
+    long long habs = 0;
+#pragma unroll
+    for (int w = 0; w < kTilesPerBlock * kWavesPerTile; ++w) habs += habs_part[w];
+    if (blockIdx.x == 0 && threadIdx.x == 0) ws.scalars[1] = habs;
+    if (threadIdx.x < kStage1Rows) {
+        // wavefront tl holds the rows of tile tl
+        const int tl = threadIdx.x >> 6;
+        const int trow = blockIdx.x * kTilesPerBlock + tl;
+        const int row = trow * 64 + lane;
+        int tot = 0;
+#pragma unroll
+        for (int w = 0; w < kWavesPerTile; ++w) tot += e1_part[tl * kWavesPerTile + w][lane];
+        long long lower = kNoRow;
         if (row < vocab) {
             const long long rs = row_scale[row];
-            const long long s1 = 81LL * rs * (long long)e1;
-            const long long bnd = 40LL * (rs < 0 ? -rs : rs) * habs;
-            ws.s1[row] = s1;
-            ws.e1[row] = e1;
-            lower = s1 - bnd;
+            lower = 81LL * rs * (long long)tot - 40LL * (rs < 0 ? -rs : rs) * habs;
+            ws.e1[row] = tot;
+            ws.lower[row] = lower;
+        }
+        long long mx = lower;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const long long o = (long long)shfl_xor_u64((unsigned long long)mx, off);
+            mx = o > mx ? o : mx;
+        }
+        if (lane == 0) {
+            tmax[tl] = mx;
+            if (trow < tiles) ws.tile_max[trow] = mx;
         }
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) ws.scalars[1] = habs;
-
-    // this workgroup's top_k lower bounds (values only; ties need no order)
-    lds_l[threadIdx.x] = lower;
     __syncthreads();
-    int rank = 0;
-    for (int j = 0; j < kStage1Threads; ++j) {
-        const long long o = lds_l[j];
-        rank += (o > lower) || (o == lower && j < (int)threadIdx.x);
+    if (threadIdx.x == 0) {
+        long long mx = tmax[0];
+#pragma unroll
+        for (int t = 1; t < kTilesPerBlock; ++t) mx = tmax[t] > mx ? tmax[t] : mx;
+        ws.wg_max[blockIdx.x] = mx;
     }
-    long long *out = ws.lower + (size_t)blockIdx.x * top_k;
-    if (rank < top_k) out[rank] = lower;
-    for (int slot = kStage1Threads + threadIdx.x; slot < top_k; slot += kStage1Threads)
-        out[slot] = (long long)0x8000000000000000ull;
 }
 
-// --------------------------------------------- radix select (one workgroup)
-// Finds the `want`-th largest (1-based) of n keys given by key_of(i), with
-// MSB-first 8-bit digits.  Returns the key.  All threads participate.
-template <typename KeyOf>
-__device__ unsigned long long radix_select_desc(int n, unsigned long long want, KeyOf key_of,
-                                                unsigned int *hist, unsigned long long *bc) {
-    unsigned long long prefix = 0, mask = 0;
-    for (int shift = 56; shift >= 0; shift -= 8) {
-        for (int d = threadIdx.x; d < 256; d += blockDim.x) hist[d] = 0;
-        __syncthreads();
-        for (int i = threadIdx.x; i < n; i += blockDim.x) {
-            const unsigned long long k = key_of(i);
-            if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1u);
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            unsigned long long cum = 0;
-            int d = 255;
-            for (; d > 0; --d) {
-                if (cum + hist[d] >= want) break;
-                cum += hist[d];
+// ------------------------------------------ block-wide selection helpers
+// Keys are visited as key_at(i, j) for i = c0 + j * blockDim.x + threadIdx.x
+// (j = 0 .. KPT-1, unrolled, so a caller may map j to a register) over
+// chunks c0 of KPT * blockDim.x keys; valid(i, j) says whether key i takes
+// part.  Every thread of the workgroup calls.
+struct SelShared {
+    unsigned int hist[256];
+    unsigned long long bc[2];
+    unsigned long long mm[2];
+    unsigned int cnt[2];
+};
+
+// The `want`-th largest (1-based) of the valid keys.  The keys are first
+// offset by their minimum, so only the bytes in which they differ are
+// visited, most significant first, with a 256-bin histogram per byte.
+// Histogram increments are combined per wavefront when all its matching
+// lanes share a digit.
+template <int KPT, typename KeyAt, typename Valid>
+__device__ __forceinline__ unsigned long long radix_select_desc(int n, unsigned long long want,
+                                                                KeyAt key_at, Valid valid,
+                                                                SelShared &sh) {
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x == 0) {
+        sh.mm[0] = ~0ull;
+        sh.mm[1] = 0;
+    }
+    unsigned long long lo = ~0ull, hi = 0;
+    for (int c0 = 0; c0 < n; c0 += KPT * (int)blockDim.x) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int i = c0 + j * (int)blockDim.x + (int)threadIdx.x;
+            if (i < n && valid(i, j)) {
+                const unsigned long long k = key_at(i, j);
+                lo = k < lo ? k : lo;
+                hi = k > hi ? k : hi;
             }
-            bc[0] = prefix | ((unsigned long long)d << shift);
-            bc[1] = want - cum;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long l2 = shfl_xor_u64(lo, off), h2 = shfl_xor_u64(hi, off);
+        lo = l2 < lo ? l2 : lo;
+        hi = h2 > hi ? h2 : hi;
+    }
+    __syncthreads();
+    if (lane == 0) {
+        atomicMin(&sh.mm[0], lo);
+        atomicMax(&sh.mm[1], hi);
+    }
+    __syncthreads();
+    const unsigned long long kmin = sh.mm[0], kmax = sh.mm[1];
+    __syncthreads();   // mm is re-initialised by the next call
+    if (kmin >= kmax) return kmin;   // a single distinct value
+    const unsigned long long span = kmax - kmin;
+    unsigned long long prefix = 0, mask = 0;
+    for (int shift = ((63 - __clzll(span)) / 8) * 8; shift >= 0; shift -= 8) {
+        for (int d = threadIdx.x; d < 256; d += blockDim.x) sh.hist[d] = 0;
+        __syncthreads();
+        for (int c0 = 0; c0 < n; c0 += KPT * (int)blockDim.x) {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                const int i = c0 + j * (int)blockDim.x + (int)threadIdx.x;
+                const bool v = i < n && valid(i, j);
+                const unsigned long long k = v ? key_at(i, j) - kmin : 0ull;
+                const bool m = v && (k & mask) == prefix;
+                const int d = (int)((k >> shift) & 255u);
+                const uint64_t bm = __ballot(m);
+                if (bm) {
+                    const int first = __builtin_ctzll(bm);
+                    const int d0 = __shfl(d, first);
+                    if (__ballot(m && d == d0) == bm) {
+                        if (lane == first) atomicAdd(&sh.hist[d0], (unsigned)__popcll(bm));
+                    } else if (m) {
+                        atomicAdd(&sh.hist[d], 1u);
+                    }
+                }
+            }
         }
         __syncthreads();
-        prefix = bc[0];
-        want = bc[1];
-        mask |= 255ull << shift;
+        if (threadIdx.x < 64) {
+            // lane l holds digits 255-4l .. 252-4l (descending)
+            unsigned c[4];
+            unsigned s = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                c[j] = sh.hist[255 - 4 * lane - j];
+                s += c[j];
+            }
+            unsigned incl = s;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const unsigned o = __shfl_up(incl, off);
+                if (lane >= off) incl += o;
+            }
+            unsigned long long pre = incl - s;   // matching keys in higher digits
+            if (lane == 0) {
+                sh.bc[0] = prefix;
+                sh.bc[1] = want;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (pre < want && want <= pre + c[j]) {
+                    sh.bc[0] = prefix | ((unsigned long long)(255 - 4 * lane - j) << shift);
+                    sh.bc[1] = want - pre;
+                }
+                pre += c[j];
+            }
+        }
         __syncthreads();
+        prefix = sh.bc[0];
+        want = sh.bc[1];
+        mask |= 255ull << shift;
     }
-    return prefix;
+    return kmin + prefix;
 }
 
-__global__ __launch_bounds__(kFinishThreads) void lmh_select(int n, int top_k, LmhWs ws) {
-    __shared__ unsigned int hist[256];
-    __shared__ unsigned long long bc[2];
-    const unsigned long long k = radix_select_desc(
-        n, (unsigned long long)top_k,
-        [&](int i) { return okey(ws.lower[i]); }, hist, bc);
-    if (threadIdx.x == 0) ws.scalars[0] = (long long)(k ^ 0x8000000000000000ull);
+// Counts of the keys for which cls(i, j) is 1 and 2.
+template <int KPT, typename Cls>
+__device__ __forceinline__ void block_count2(int n, Cls cls, SelShared &sh, unsigned &c1,
+                                             unsigned &c2) {
+    if (threadIdx.x == 0) {
+        sh.cnt[0] = 0;
+        sh.cnt[1] = 0;
+    }
+    __syncthreads();
+    unsigned a = 0, b = 0;
+    for (int c0 = 0; c0 < n; c0 += KPT * (int)blockDim.x) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int i = c0 + j * (int)blockDim.x + (int)threadIdx.x;
+            const int c = i < n ? cls(i, j) : 0;
+            a += (unsigned)__popcll(__ballot(c == 1));
+            b += (unsigned)__popcll(__ballot(c == 2));
+        }
+    }
+    if ((threadIdx.x & 63) == 0) {
+        atomicAdd(&sh.cnt[0], a);
+        atomicAdd(&sh.cnt[1], b);
+    }
+    __syncthreads();
+    c1 = sh.cnt[0];
+    c2 = sh.cnt[1];
+    __syncthreads();
 }
 
-// ----------------------------------------------------------------- filter
-__global__ __launch_bounds__(256) void lmh_filter(const int32_t *__restrict__ row_scale,
-                                                  int vocab, LmhWs ws) {
-    const int row = blockIdx.x * 256 + threadIdx.x;
-    if (row >= vocab) return;
+// The `want`-th largest (1-based) of n <= blockDim.x keys, thread t holding
+// key t (t < n): every thread ranks its key against an LDS copy.
+__device__ __forceinline__ unsigned long long rank_select_desc(int n, int want,
+                                                               unsigned long long mykey,
+                                                               unsigned long long *lds,
+                                                               unsigned long long *result) {
+    const int t = (int)threadIdx.x;
+    if (t < n) lds[t] = mykey;
+    __syncthreads();
+    if (t < n) {
+        int r = 0;
+#pragma unroll 8
+        for (int j = 0; j < n; ++j) {
+            const unsigned long long o = lds[j];
+            r += (o > mykey) || (o == mykey && j < t);
+        }
+        if (r == want - 1) *result = mykey;
+    }
+    __syncthreads();
+    const unsigned long long v = *result;
+    __syncthreads();   // lds and result reusable
+    return v;
+}
+
+// ----------------------------------------------------------------- select
+__global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles, int nwg,
+                                                            int top_k, LmhWs ws) {
+    __shared__ SelShared sh;
+    __shared__ unsigned long long list[kSelList];
+    __shared__ int tlist[kSelTiles];
+    __shared__ unsigned long long res;
+    __shared__ unsigned int n_t, n_l;
+    const int t = (int)threadIdx.x;
+    if (t == 0) {
+        n_t = 0;
+        n_l = 0;
+    }
+    // T: the top_k-th largest workgroup maximum (0 when there are fewer
+    // workgroups than top_k, which keeps every row)
+    unsigned long long thr = 0;
+    if (nwg >= top_k) {
+        if (nwg <= (int)blockDim.x)
+            thr = rank_select_desc(nwg, top_k, t < nwg ? okey(ws.wg_max[t]) : 0ull, list, &res);
+        else
+            thr = radix_select_desc<4>(
+                nwg, (unsigned long long)top_k, [&](int i, int) { return okey(ws.wg_max[i]); },
+                [](int, int) { return true; }, sh);
+    }
+    __syncthreads();
+    // the tiles whose maximum reaches T
+    for (int c0 = 0; c0 < tiles; c0 += (int)blockDim.x) {
+        const int tt = c0 + t;
+        if (tt < tiles && okey(ws.tile_max[tt]) >= thr) {
+            const unsigned slot = atomicAdd(&n_t, 1u);
+            if (slot < (unsigned)kSelTiles) tlist[slot] = tt;
+        }
+    }
+    __syncthreads();
+    const int nt = (int)n_t;
+    unsigned long long kk = 0;
+    bool done = false;
+    if (nt <= kSelTiles) {
+        // their rows that reach T, four loads in flight per thread
+        for (int c0 = 0; c0 < nt * 64; c0 += 4 * (int)blockDim.x) {
+            unsigned long long k[4];
+            bool v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = c0 + u * (int)blockDim.x + t;
+                const int row = i < nt * 64 ? tlist[i >> 6] * 64 + (i & 63) : vocab;
+                v[u] = row < vocab;
+                k[u] = v[u] ? okey(ws.lower[row]) : 0ull;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (v[u] && k[u] >= thr) {
+                    const unsigned slot = atomicAdd(&n_l, 1u);
+                    if (slot < (unsigned)kSelList) list[slot] = k[u];
+                }
+            }
+        }
+        __syncthreads();
+        const int ln = (int)n_l;
+        if (ln <= (int)blockDim.x) {
+            kk = rank_select_desc(ln, top_k, t < ln ? list[t] : 0ull, list, &res);
+            done = true;
+        } else if (ln <= kSelList) {
+            kk = radix_select_desc<4>(
+                ln, (unsigned long long)top_k, [&](int i, int) { return list[i]; },
+                [](int, int) { return true; }, sh);
+            done = true;
+        }
+    }
+    if (!done)
+        kk = radix_select_desc<4>(
+            vocab, (unsigned long long)top_k, [&](int i, int) { return okey(ws.lower[i]); },
+            [&](int i, int) { return okey(ws.lower[i]) >= thr; }, sh);
+    if (t == 0) ws.scalars[0] = (long long)(kk ^ 0x8000000000000000ull);
+}
+
+// --------------------------------------------------- filter + rescoring
+// One workgroup per 256 rows (four wavefronts, lane = row).  Its candidates
+// go to slots [256 * blockIdx.x, 256 * blockIdx.x + count), sorted by
+// (S1' desc, row asc), and the count to region_count[blockIdx.x].
+__global__ __launch_bounds__(kFilterRows) void lmh_filter(const uint8_t *__restrict__ planes47,
+                                                          const int32_t *__restrict__ row_scale,
+                                                          const int8_t *__restrict__ h,
+                                                          int vocab, int groups, LmhWs ws) {
+    __shared__ uint4 hs[kMaxGroups * 8];   // h, 16 positions per entry
+    __shared__ int rowtab[4][64];
+    __shared__ int e2l[4][64];
+    __shared__ long long cs1[kFilterRows];
+    __shared__ int crow[kFilterRows];
+    __shared__ int wcount[4];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * kFilterRows + (int)threadIdx.x;
+    const uint2 *h2 = reinterpret_cast<const uint2 *>(h);
+    uint2 *hs2 = reinterpret_cast<uint2 *>(hs);
+    for (int t = threadIdx.x; t < groups * 16; t += kFilterRows) hs2[t] = h2[t];
     const long long lk = ws.scalars[0], habs = ws.scalars[1];
-    const long long rs = row_scale[row];
-    const long long upper = ws.s1[row] + 40LL * (rs < 0 ? -rs : rs) * habs;
-    if (upper >= lk) {
-        const unsigned int slot = atomicAdd(ws.count, 1u);
-        if (slot < (unsigned int)vocab) ws.cand[slot] = row;
+    bool cand = false;
+    long long s1 = 0;
+    int e1 = 0, rs = 0;
+    if (row < vocab) {
+        rs = row_scale[row];
+        e1 = ws.e1[row];
+        s1 = 81LL * (long long)rs * (long long)e1;
+        const long long ars = rs < 0 ? -(long long)rs : (long long)rs;
+        cand = s1 + 40LL * ars * habs >= lk;
+    }
+    const int nct = __syncthreads_count(cand);
+    if (threadIdx.x == 0) ws.region_count[blockIdx.x] = nct;
+    if (nct == 0) return;   // whole workgroup
+    const uint64_t m = __ballot(cand);
+    const int nc = __popcll(m);
+    const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (cand) rowtab[wave][pos] = row;
+    e2l[wave][lane] = 0;
+    if (lane == 0) wcount[wave] = nc;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wcount[w];
+    if (cand) {
+        cs1[before + pos] = s1;
+        crow[before + pos] = row;
+    }
+    __syncthreads();
+    int rank = 0;   // position in the region: (S1' desc, row asc)
+    if (cand) {
+        for (int j = 0; j < nct; ++j) rank += better(cs1[j], crow[j], s1, row);
+    }
+    if (nc == 0) return;
+
+    const int nrun = groups * 8;            // 16-byte runs per row
+    const int total = nc * nrun;
+    const size_t dim = (size_t)groups * 128;
+    for (int f0 = 0; f0 < total; f0 += 64 * kResU) {
+        uint4 w[kResU];
+        int cix[kResU], run[kResU];
+#pragma unroll
+        for (int u = 0; u < kResU; ++u) {
+            const int f = f0 + 64 * u + lane;
+            cix[u] = -1;
+            if (f < total) {
+                const int c = f / nrun;
+                const int p = f - c * nrun;
+                w[u] = *reinterpret_cast<const uint4 *>(planes47 + (size_t)rowtab[wave][c] * dim +
+                                                        16 * (size_t)p);
+                cix[u] = c;
+                run[u] = p;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kResU; ++u) {
+            if (cix[u] >= 0) {
+                const uint4 hv = hs[run[u]];
+                atomicAdd(&e2l[wave][cix[u]],
+                          dot16(w[u], (int)hv.x, (int)hv.y, (int)hv.z, (int)hv.w, 0));
+            }
+        }
+    }
+    wave_lds_fence();
+    if (cand) {
+        const size_t slot = (size_t)blockIdx.x * kFilterRows + rank;
+        ws.cand[slot] = row;
+        ws.cand_s1[slot] = s1;
+        ws.cand_s[slot] = (long long)rs * (81LL * (long long)e1 + (long long)e2l[wave][pos]);
     }
 }
 
 // ----------------------------------------------------------------- finish
-__global__ __launch_bounds__(kFinishThreads) void lmh_finish(
-    const uint8_t *__restrict__ planes47, const int32_t *__restrict__ row_scale,
-    const int8_t *__restrict__ h, int vocab, int groups, int dim, int top_k, int cap,
-    int32_t *__restrict__ top_idx, int64_t *__restrict__ top_score, int32_t *__restrict__ info,
-    LmhWs ws) {
-    __shared__ unsigned int hist[256];
-    __shared__ unsigned long long bc[2];
-    __shared__ long long key[kMaxCap];
-    __shared__ int idx[kMaxCap];
-    __shared__ unsigned int nsel;
-    extern __shared__ uint32_t hplanes[];     // [groups][8 planes][4 dwords]
+// Where candidate i (in row order) is stored: in the filter workgroups'
+// regions, found by binary search over the regions' exclusive prefix sums in
+// LDS, or (when there are too many regions for that) in compacted arrays.
+struct CandSrc {
+    const int *ro;          // LDS prefix sums, or nullptr for compacted arrays
+    int nreg;
+    const int *rows;
+    const long long *s1;
+    const long long *s;
+};
 
-    const unsigned int n = min(*ws.count, (unsigned int)vocab);
-    const bool capped = n > (unsigned int)cap;
-
-    // bit planes of h for every group
-    for (int w = threadIdx.x; w < groups * 32; w += blockDim.x) {
-        const int g = w >> 5, b = (w >> 2) & 7, d = w & 3;
-        uint32_t m = 0;
-        for (int i = 0; i < 32; ++i) m |= (uint32_t)((h[g * 128 + 32 * d + i] >> b) & 1) << i;
-        hplanes[w] = m;
+__device__ __forceinline__ size_t cand_slot(const CandSrc &c, int i) {
+    if (!c.ro) return (size_t)i;
+    int lo = 0, hi = c.nreg - 1;   // the last region whose prefix is <= i
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (c.ro[mid] <= i) lo = mid; else hi = mid - 1;
     }
-    if (threadIdx.x == 0) nsel = 0;
-    __syncthreads();
+    return (size_t)lo * kFilterRows + (size_t)(i - c.ro[lo]);
+}
 
-    if (!capped) {
-        for (unsigned int i = threadIdx.x; i < n; i += blockDim.x) idx[i] = ws.cand[i];
-        __syncthreads();
-        if (threadIdx.x == 0) nsel = n;
-    } else {
-        // cap-th largest S1' among the candidates, then the lowest indices
-        // among the rows that tie with it
-        const unsigned long long tau = radix_select_desc(
-            (int)n, (unsigned long long)cap, [&](int i) { return okey(ws.s1[ws.cand[i]]); },
-            hist, bc);
-        __shared__ unsigned int n_gt;
-        if (threadIdx.x == 0) n_gt = 0;
-        __syncthreads();
-        for (unsigned int i = threadIdx.x; i < n; i += blockDim.x)
-            if (okey(ws.s1[ws.cand[i]]) > tau) atomicAdd(&n_gt, 1u);
-        __syncthreads();
-        const unsigned int need_ties = (unsigned int)cap - n_gt;
-        // largest of ~index among ties = smallest index; want the need_ties-th
-        const unsigned long long theta = radix_select_desc(
-            (int)n, (unsigned long long)need_ties,
-            [&](int i) {
-                const int r = ws.cand[i];
-                return okey(ws.s1[r]) == tau ? (unsigned long long)(0xFFFFFFFFu - (unsigned)r) : 0ull;
+template <bool REG>
+__device__ __forceinline__ void finish_body(int n, int top_k, int cap, int32_t *__restrict__ top_idx,
+                                            int64_t *__restrict__ top_score,
+                                            int32_t *__restrict__ info, const CandSrc &src,
+                                            SelShared &sh, long long *tk, int *ti,
+                                            unsigned int *nkept) {
+    constexpr int KPT = kFinKpt;
+    long long r_s1[KPT], r_s[KPT];
+    int r_id[KPT];
+    if constexpr (REG) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int i = j * (int)blockDim.x + (int)threadIdx.x;
+            r_s1[j] = 0;
+            r_s[j] = 0;
+            r_id[j] = 0;
+            if (i < n) {
+                const size_t sl = cand_slot(src, i);
+                r_s1[j] = src.s1[sl];
+                r_s[j] = src.s[sl];
+                r_id[j] = src.rows[sl];
+            }
+        }
+    }
+    auto S1 = [&](int i, int j) -> long long {
+        if constexpr (REG) return r_s1[j]; else return src.s1[cand_slot(src, i)];
+    };
+    auto S = [&](int i, int j) -> long long {
+        if constexpr (REG) return r_s[j]; else return src.s[cand_slot(src, i)];
+    };
+    auto ID = [&](int i, int j) -> int {
+        if constexpr (REG) return r_id[j]; else return src.rows[cand_slot(src, i)];
+    };
+    auto all = [](int, int) { return true; };
+
+    // the rows that are rescored: all of C, or its top `cap` by (S1', index)
+    const bool capped = n > cap;
+    unsigned long long tau = 0, theta = 0;
+    if (capped) {
+        tau = radix_select_desc<KPT>(
+            n, (unsigned long long)cap, [&](int i, int j) { return okey(S1(i, j)); }, all, sh);
+        unsigned gt, eq;
+        block_count2<KPT>(
+            n,
+            [&](int i, int j) {
+                const unsigned long long k = okey(S1(i, j));
+                return k > tau ? 1 : (k == tau ? 2 : 0);
             },
-            hist, bc);
-        for (unsigned int i = threadIdx.x; i < n; i += blockDim.x) {
-            const int r = ws.cand[i];
-            const unsigned long long kk = okey(ws.s1[r]);
-            if (kk > tau || (kk == tau && (unsigned long long)(0xFFFFFFFFu - (unsigned)r) >= theta)) {
-                const unsigned int slot = atomicAdd(&nsel, 1u);
-                if (slot < (unsigned int)kMaxCap) idx[slot] = r;
+            sh, gt, eq);
+        const unsigned need = (unsigned)cap - gt;   // rows tying at tau that are kept
+        if (need < eq)
+            theta = radix_select_desc<KPT>(
+                n, (unsigned long long)need, [&](int i, int j) { return tie_key(ID(i, j)); },
+                [&](int i, int j) { return okey(S1(i, j)) == tau; }, sh);
+    }
+    // the kept rows into LDS
+    if (threadIdx.x == 0) *nkept = 0;
+    __syncthreads();
+    for (int c0 = 0; c0 < n; c0 += KPT * (int)blockDim.x) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int i = c0 + j * (int)blockDim.x + (int)threadIdx.x;
+            if (i < n) {
+                bool keep = true;
+                if (capped) {
+                    const unsigned long long k = okey(S1(i, j));
+                    keep = k > tau || (k == tau && tie_key(ID(i, j)) >= theta);
+                }
+                if (keep) {
+                    const unsigned slot = atomicAdd(nkept, 1u);
+                    if (slot < (unsigned)kMaxCap) {
+                        tk[slot] = S(i, j);
+                        ti[slot] = ID(i, j);
+                    }
+                }
             }
         }
     }
     __syncthreads();
-    const int m = (int)min(nsel, (unsigned int)cap);
-
-    // rescore with planes 4..7: one wavefront per row, lanes over (group, plane)
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
-    for (int c = wave; c < m; c += nwaves) {
-        const int r = idx[c];
-        int part = 0;
-        for (int pair = lane; pair < groups * 4; pair += 64) {
-            const int g = pair >> 2, q = pair & 3;
-            const uint8_t *f = planes47 + (size_t)r * dim + 128 * g + 32 * q;
-            const uint4 nzv = *reinterpret_cast<const uint4 *>(f);
-            const uint4 ngv = *reinterpret_cast<const uint4 *>(f + 16);
-            const uint32_t nz[4] = {nzv.x, nzv.y, nzv.z, nzv.w};
-            const uint32_t ng[4] = {ngv.x, ngv.y, ngv.z, ngv.w};
-            const uint32_t *hp = hplanes + g * 32;
-            int s = 0;
-#pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                int cn = 0, cg = 0;
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    cn += __builtin_popcount(nz[d] & hp[b * 4 + d]);
-                    cg += __builtin_popcount(ng[d] & hp[b * 4 + d]);
-                }
-                const int t = cn - 2 * cg;
-                s += (b == 7) ? -t * 128 : t * (1 << b);
-            }
-            const int pw = q == 0 ? 27 : q == 1 ? 9 : q == 2 ? 3 : 1;    // 3^(7-(q+4))
-            part += pw * s;
-        }
-        const int e2 = wave_sum(part);
-        if (lane == 0) key[c] = (long long)row_scale[r] * (81LL * (long long)ws.e1[r] + e2);
-    }
-    // pad to a power of two with entries that sort last
+    // order them by (S' desc, index asc): bitonic sort over a power of two
+    const int m = (int)min(*nkept, (unsigned)kMaxCap);
     int mp = 1;
     while (mp < m) mp <<= 1;
     for (int i = m + threadIdx.x; i < mp; i += blockDim.x) {
-        key[i] = (long long)0x8000000000000000ull;
-        idx[i] = 0x7FFFFFFF;
+        tk[i] = kNoRow;
+        ti[i] = 0x7FFFFFFF;
     }
     __syncthreads();
-
-    // bitonic sort: (key descending, index ascending)
     for (int size = 2; size <= mp; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
             for (int i = threadIdx.x; i < mp; i += blockDim.x) {
                 const int j = i ^ stride;
                 if (j > i) {
-                    const bool up = (i & size) == 0;    // this run sorts "first = best"
-                    const bool i_first = key[i] > key[j] || (key[i] == key[j] && idx[i] < idx[j]);
-                    if (i_first != up) {
-                        const long long tk = key[i];
-                        key[i] = key[j];
-                        key[j] = tk;
-                        const int ti = idx[i];
-                        idx[i] = idx[j];
-                        idx[j] = ti;
+                    const bool up = (i & size) == 0;   // this run puts the best first
+                    if (better(tk[i], ti[i], tk[j], ti[j]) != up) {
+                        const long long a = tk[i];
+                        tk[i] = tk[j];
+                        tk[j] = a;
+                        const int b = ti[i];
+                        ti[i] = ti[j];
+                        ti[j] = b;
                     }
                 }
             }
@@ -287,14 +667,176 @@ __global__ __launch_bounds__(kFinishThreads) void lmh_finish(
         }
     }
     for (int i = threadIdx.x; i < top_k; i += blockDim.x) {
-        top_idx[i] = idx[i];
-        top_score[i] = key[i];
+        top_idx[i] = ti[i];
+        top_score[i] = tk[i];
     }
     if (threadIdx.x == 0) {
-        info[0] = (int32_t)n;
+        info[0] = n;
         info[1] = capped ? 1 : 0;
-        *ws.count = 0;
     }
+}
+
+// The top_k of the m rows (tk, ti) by (S' desc, row asc): each row's rank
+// among them, those below top_k written at their rank.
+__device__ __forceinline__ void output_by_rank(int m, int top_k, const long long *tk,
+                                               const int *ti, int32_t *__restrict__ top_idx,
+                                               int64_t *__restrict__ top_score) {
+    for (int e = threadIdx.x; e < m; e += blockDim.x) {
+        const long long me = tk[e];
+        const int mi = ti[e];
+        int r = 0;
+#pragma unroll 8
+        for (int j = 0; j < m; ++j) r += better(tk[j], ti[j], me, mi);
+        if (r < top_k) {
+            top_idx[r] = mi;
+            top_score[r] = me;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, int top_k,
+                                                            int cap, int32_t *__restrict__ top_idx,
+                                                            int64_t *__restrict__ top_score,
+                                                            int32_t *__restrict__ info, LmhWs ws) {
+    __shared__ SelShared sh;
+    __shared__ long long tk[kMaxCap];
+    __shared__ int ti[kMaxCap];
+    __shared__ int ro[kBlockThreads];
+    __shared__ long long l1s1[kFinList], l1s[kFinList];
+    __shared__ int l1id[kFinList];
+    __shared__ int wtot[kBlockThreads / 64];
+    __shared__ unsigned int nkept, nl1;
+    __shared__ unsigned long long res;
+    const int t = (int)threadIdx.x;
+    const int wave = t >> 6, lane = t & 63;
+    const int nwaves = kBlockThreads / 64;
+
+    // exclusive prefix sums of the region counts, 1024 regions at a time
+    int n = 0;
+    for (int r0 = 0; r0 < nwf; r0 += kBlockThreads) {
+        const int r = r0 + t;
+        const int c = r < nwf ? ws.region_count[r] : 0;
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        if (lane == 63) wtot[wave] = incl;
+        __syncthreads();
+        int before = n, chunk_total = 0;
+        for (int w = 0; w < nwaves; ++w) {
+            before += w < wave ? wtot[w] : 0;
+            chunk_total += wtot[w];
+        }
+        ro[t] = before + incl - c;
+        n += chunk_total;
+        __syncthreads();
+        if (nwf <= kBlockThreads) break;   // one pass: the candidates stay in their regions
+        // more regions than one pass: copy them into the compacted arrays,
+        // one wavefront per region
+        const int nr = min(kBlockThreads, nwf - r0);
+        for (int k = wave; k < nr; k += nwaves) {
+            const int cnt = ws.region_count[r0 + k], dst = ro[k];
+            const size_t from = (size_t)(r0 + k) * kFilterRows;
+            for (int l = lane; l < cnt; l += 64) {
+                if (dst + l < vocab) {
+                    ws.cc[dst + l] = ws.cand[from + l];
+                    ws.cc_s1[dst + l] = ws.cand_s1[from + l];
+                    ws.cc_s[dst + l] = ws.cand_s[from + l];
+                }
+            }
+        }
+        __syncthreads();   // copies visible to the workgroup, ro and wtot reusable
+    }
+    const bool regions = nwf <= kBlockThreads;
+    CandSrc src;
+    src.ro = regions ? ro : nullptr;
+    src.nreg = regions ? nwf : 0;
+    src.rows = regions ? ws.cand : ws.cc;
+    src.s1 = regions ? ws.cand_s1 : ws.cc_s1;
+    src.s = regions ? ws.cand_s : ws.cc_s;
+    n = min(n, vocab);
+    const bool capped = n > cap;
+    if (t == 0) {
+        info[0] = n;
+        info[1] = capped ? 1 : 0;
+    }
+
+    if (!capped) {
+        // every candidate is rescored: gather them, then rank
+        for (int i = t; i < n; i += blockDim.x) {
+            const size_t sl = cand_slot(src, i);
+            tk[i] = src.s[sl];
+            ti[i] = src.rows[sl];
+        }
+        __syncthreads();
+        output_by_rank(n, top_k, tk, ti, top_idx, top_score);
+        return;
+    }
+    if (regions) {
+        // T: the cap-th largest region head (cap distinct rows reach it; 0
+        // when fewer than cap regions are non-empty)
+        const bool nonempty = t < nwf && (t + 1 < nwf ? ro[t + 1] : n) > ro[t];
+        const int nne = __syncthreads_count(nonempty);
+        unsigned long long thr = 0;
+        if (nne >= cap)
+            thr = rank_select_desc(nwf, cap,
+                                   nonempty ? okey(ws.cand_s1[(size_t)t * kFilterRows]) : 0ull,
+                                   reinterpret_cast<unsigned long long *>(tk), &res);
+        if (t == 0) nl1 = 0;
+        __syncthreads();
+        // the sorted prefix >= T of every region
+        if (t < nwf) {
+            const int cnt = (t + 1 < nwf ? ro[t + 1] : n) - ro[t];
+            const size_t base = (size_t)t * kFilterRows;
+            for (int e0 = 0; e0 < cnt; e0 += 4) {
+                long long v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] = e0 + u < cnt ? ws.cand_s1[base + e0 + u] : kNoRow;
+                bool more = true;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (e0 + u < cnt && okey(v[u]) >= thr) {
+                        const unsigned slot = atomicAdd(&nl1, 1u);
+                        if (slot < (unsigned)kFinList) {
+                            l1s1[slot] = v[u];
+                            l1s[slot] = ws.cand_s[base + e0 + u];
+                            l1id[slot] = ws.cand[base + e0 + u];
+                        }
+                    } else {
+                        more = false;
+                    }
+                }
+                if (!more) break;
+            }
+        }
+        __syncthreads();
+        const int nl = (int)nl1;
+        if (nl <= kFinList) {
+            // rank by (S1' desc, row asc): the first cap are kept, placed at
+            // their rank
+            if (t < nl) {
+                const long long me = l1s1[t];
+                const int mi = l1id[t];
+                int r = 0;
+#pragma unroll 8
+                for (int j = 0; j < nl; ++j) r += better(l1s1[j], l1id[j], me, mi);
+                if (r < cap) {
+                    tk[r] = l1s[t];
+                    ti[r] = mi;
+                }
+            }
+            __syncthreads();
+            output_by_rank(cap, top_k, tk, ti, top_idx, top_score);
+            return;
+        }
+    }
+    // fallback: block-wide radix selections over every candidate
+    if (n <= kFinKpt * kBlockThreads)
+        finish_body<true>(n, top_k, cap, top_idx, top_score, info, src, sh, tk, ti, &nkept);
+    else
+        finish_body<false>(n, top_k, cap, top_idx, top_score, info, src, sh, tk, ti, &nkept);
 }
 
 }  // namespace
@@ -303,34 +845,44 @@ __global__ __launch_bounds__(kFinishThreads) void lmh_finish(
 using namespace bs;
 
 struct LmhLayout {
-    size_t s1, e1, lower, scalars, count, cand, total;
-    int nwg;
+    size_t scalars, e1, lower, tile_max, wg_max, region_count, cand, cand_s1, cand_s, cc, cc_s1,
+        cc_s, total;
+    int tiles, nwg, nwf;
 };
 
-// The candidate counter is the only word that must be zero on entry.  It sits
-// at offset 0 whatever the shapes, so calls of different shapes can share one
-// workspace: every other region is written before it is read.
-static LmhLayout lmh_layout(int64_t vocab, int32_t top_k) {
+// Every region of the workspace is written before it is read, so it needs no
+// initialisation and calls of any shapes may share one workspace.
+static LmhLayout lmh_layout(int64_t vocab) {
     LmhLayout L;
-    const int64_t tiles = pad64(vocab) / 64;
-    L.nwg = (int)((tiles + kStage1Waves - 1) / kStage1Waves);
+    L.tiles = (int)(pad64(vocab) / 64);
+    L.nwg = (L.tiles + kTilesPerBlock - 1) / kTilesPerBlock;
+    L.nwf = (int)((vocab + kFilterRows - 1) / kFilterRows);
+    const size_t slots = (size_t)L.nwf * kFilterRows;
     size_t off = 0;
-    L.count = off;   off += kWsAlign;
-    L.scalars = off; off += kWsAlign;
-    L.s1 = off;      off += align_up((size_t)vocab * 8, kWsAlign);
-    L.e1 = off;      off += align_up((size_t)vocab * 4, kWsAlign);
-    L.lower = off;   off += align_up((size_t)L.nwg * (size_t)top_k * 8, kWsAlign);
-    L.cand = off;    off += align_up((size_t)vocab * 4, kWsAlign);
+    L.scalars = off;      off += kWsAlign;
+    L.e1 = off;           off += align_up((size_t)vocab * 4, kWsAlign);
+    L.lower = off;        off += align_up((size_t)vocab * 8, kWsAlign);
+    L.tile_max = off;     off += align_up((size_t)L.tiles * 8, kWsAlign);
+    L.wg_max = off;       off += align_up((size_t)L.nwg * 8, kWsAlign);
+    L.region_count = off; off += align_up((size_t)L.nwf * 4, kWsAlign);
+    L.cand = off;         off += align_up(slots * 4, kWsAlign);
+    L.cand_s1 = off;      off += align_up(slots * 8, kWsAlign);
+    L.cand_s = off;       off += align_up(slots * 8, kWsAlign);
+    L.cc = off;           off += align_up((size_t)vocab * 4, kWsAlign);
+    L.cc_s1 = off;        off += align_up((size_t)vocab * 8, kWsAlign);
+    L.cc_s = off;         off += align_up((size_t)vocab * 8, kWsAlign);
     L.total = off;
     return L;
 }
 
 // |S'| <= 2^31 * (81*40 + 40) * 128 * dim must fit int64: dim <= 10230; the
-// largest multiple of 128 below that is 10112.
+// largest multiple of 128 below that is 10112 (79 groups).
 static constexpr int64_t kLmhMaxDim = 10112;
+static_assert(kLmhMaxDim / 128 == kMaxGroups, "LDS copy of h sized for the largest dim");
 
 static int32_t lmh_check(int64_t vocab, int64_t dim, int32_t top_k, int32_t cap) {
     if (int32_t st = check_rows_k(vocab, dim, kLmhMaxDim)) return st;
+    if (vocab > ((int64_t)1 << 31) - 1024) return BS_E_SHAPE;
     if (top_k < 1 || cap < top_k || (int64_t)top_k > vocab || cap > kMaxCap) return BS_E_RANGE;
     return BS_OK;
 }
@@ -338,7 +890,7 @@ static int32_t lmh_check(int64_t vocab, int64_t dim, int32_t top_k, int32_t cap)
 extern "C" size_t bs_lmhead_workspace_bytes(int64_t vocab, int64_t dim, int32_t top_k,
                                             int32_t max_candidates) {
     if (lmh_check(vocab, dim, top_k, max_candidates) != BS_OK) return 0;
-    return lmh_layout(vocab, top_k).total;
+    return lmh_layout(vocab).total;
 }
 
 extern "C" int32_t bs_lmhead_planes_topk(const uint8_t *planes03, const uint8_t *planes47,
@@ -350,33 +902,41 @@ extern "C" int32_t bs_lmhead_planes_topk(const uint8_t *planes03, const uint8_t 
     if (!planes03 || !planes47 || !row_scale || !h || !top_idx || !top_score || !info)
         return BS_E_NULL;
     if (int32_t st = lmh_check(vocab, dim, top_k, max_candidates)) return st;
-    const LmhLayout L = lmh_layout(vocab, top_k);
+    if (((uintptr_t)planes03 & 15) || ((uintptr_t)planes47 & 15) || ((uintptr_t)row_scale & 3) ||
+        ((uintptr_t)h & 7) || ((uintptr_t)top_idx & 3) || ((uintptr_t)top_score & 7) ||
+        ((uintptr_t)info & 3))
+        return BS_E_ALIGN;
+    const LmhLayout L = lmh_layout(vocab);
     if (!ws_ok(workspace, workspace_bytes, L.total)) return BS_E_WORKSPACE;
 
     unsigned char *base = static_cast<unsigned char *>(workspace);
     LmhWs ws;
-    ws.s1 = reinterpret_cast<long long *>(base + L.s1);
+    ws.scalars = reinterpret_cast<long long *>(base + L.scalars);
     ws.e1 = reinterpret_cast<int *>(base + L.e1);
     ws.lower = reinterpret_cast<long long *>(base + L.lower);
-    ws.scalars = reinterpret_cast<long long *>(base + L.scalars);
-    ws.count = reinterpret_cast<unsigned int *>(base + L.count);
+    ws.tile_max = reinterpret_cast<long long *>(base + L.tile_max);
+    ws.wg_max = reinterpret_cast<long long *>(base + L.wg_max);
+    ws.region_count = reinterpret_cast<int *>(base + L.region_count);
     ws.cand = reinterpret_cast<int *>(base + L.cand);
+    ws.cand_s1 = reinterpret_cast<long long *>(base + L.cand_s1);
+    ws.cand_s = reinterpret_cast<long long *>(base + L.cand_s);
+    ws.cc = reinterpret_cast<int *>(base + L.cc);
+    ws.cc_s1 = reinterpret_cast<long long *>(base + L.cc_s1);
+    ws.cc_s = reinterpret_cast<long long *>(base + L.cc_s);
 
     hipStream_t st = (hipStream_t)stream;
     const int groups = (int)(dim / 128);
-    hipLaunchKernelGGL(lmh_stage1, dim3(L.nwg), dim3(kStage1Threads), 0, st, planes03,
-                       row_scale, h, (int)vocab, groups, (int)dim, top_k, ws);
+    hipLaunchKernelGGL(lmh_stage1, dim3(L.nwg), dim3(kStage1Threads), 0, st, planes03, row_scale,
+                       reinterpret_cast<const int32_t *>(h), (int)vocab, groups, ws);
     BS_LAUNCH_CHECK();
-    hipLaunchKernelGGL(lmh_select, dim3(1), dim3(kFinishThreads), 0, st, L.nwg * top_k, top_k,
-                       ws);
+    hipLaunchKernelGGL(lmh_select, dim3(1), dim3(kBlockThreads), 0, st, (int)vocab, L.tiles, L.nwg,
+                       top_k, ws);
     BS_LAUNCH_CHECK();
-    hipLaunchKernelGGL(lmh_filter, dim3((unsigned)((vocab + 255) / 256)), dim3(256), 0, st,
-                       row_scale, (int)vocab, ws);
+    hipLaunchKernelGGL(lmh_filter, dim3((unsigned)L.nwf), dim3(kFilterRows), 0, st, planes47,
+                       row_scale, h, (int)vocab, groups, ws);
     BS_LAUNCH_CHECK();
-    hipLaunchKernelGGL(lmh_finish, dim3(1), dim3(kFinishThreads), (size_t)groups * 32 * 4, st,
-                       planes47, row_scale, h, (int)vocab, groups, (int)dim, top_k,
-                       max_candidates,
-                       top_idx, top_score, info, ws);
+    hipLaunchKernelGGL(lmh_finish, dim3(1), dim3(kBlockThreads), 0, st, (int)vocab, L.nwf, top_k,
+                       max_candidates, top_idx, top_score, info, ws);
     BS_LAUNCH_CHECK();
     return BS_OK;
 }

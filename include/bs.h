@@ -166,17 +166,18 @@ int32_t bs_lns8_phase_gemv(const uint8_t *planes, const uint8_t *x_lns8, int64_t
  * in units of 3^-7:
  *   S'(r) = row_scale[r] * sum_{p=0..7} 3^(7-p) * (T_p[r] . h)
  *
- * Packed layouts (dim % 128 == 0, G = dim/128):
- *   planes03 ("tiled64", streamed by the full-vocabulary scan): rows padded
- *     to R = ceil(vocab/64)*64; block (tile, g) is 8192 bytes at offset
- *     (tile*G + g)*8192; plane q (0..3) at block bytes [2048q, 2048q+2048):
- *     W_nonzero in the first 1024 bytes, W_negative in the next 1024, row
- *     64*tile+j at 16j.  R*dim bytes.
- *   planes47 (row-major, gathered for candidate rows only): row r at bytes
- *     [r*dim, r*dim+dim); group g at r*dim + 128g; plane q (4..7) at
- *     + 32(q-4): 16 bytes W_nonzero then 16 bytes W_negative.  vocab*dim
- *     bytes.
- *   In every 16-byte field weight 128*g + i is bit (i % 8) of byte (i / 8).
+ * Packed layouts (dim % 128 == 0, G = dim/128).  The four trits of planes
+ * 0-3 at one position are stored as one int8, the balanced-ternary digit sum
+ * D03 = 27*T_0 + 9*T_1 + 3*T_2 + T_3 in [-40, 40] (which determines them),
+ * and planes 4-7 likewise as D47 = 27*T_4 + 9*T_5 + 3*T_6 + T_7: one byte
+ * per position for each half, as many bits as two bitplanes per plane.
+ *   planes03 (D03, tiled for the full-vocabulary scan): rows padded to
+ *     R = ceil(vocab/64)*64; block (tile, g) is 8192 bytes at offset
+ *     (tile*G + g)*8192; positions 128g + 16c .. 128g + 16c + 15 of row
+ *     64*tile + j are the 16 bytes at block offset 1024c + 16j (c = 0..7).
+ *     R*dim bytes; padding rows are zero.
+ *   planes47 (D47, row-major, gathered for candidate rows only): position i
+ *     of row r at byte r*dim + i.  vocab*dim bytes.
  *
  * trits[vocab][8][dim] row-major, each in {-1,0,+1}.
  */
@@ -200,19 +201,21 @@ int32_t bs_planes_pack(const int8_t *trits, int64_t vocab, int64_t dim,
  *   output: the top_k rescored rows by S' descending, lowest index first on
  *   ties ([IE] sections 3.2-3.3).
  *
- *   planes03, planes47, row_scale (int32[vocab]), h (int8[dim]): device
- *   vocab >= 1; dim >= 128, dim % 128 == 0, dim <= 10112 (|S'| <= 2^31 *
- *     3280 * 128 * dim must fit int64, else BS_E_OVERFLOW)
+ *   planes03, planes47 (16-byte aligned), row_scale (int32[vocab], 4-byte
+ *     aligned), h (int8[dim], 8-byte aligned): device
+ *   1 <= vocab <= 2^31 - 1024; dim >= 128, dim % 128 == 0, dim <= 10112
+ *     (|S'| <= 2^31 * 3280 * 128 * dim must fit int64, else BS_E_OVERFLOW)
  *   1 <= top_k <= max_candidates, top_k <= vocab, max_candidates <= 4096
  *   top_idx int32[top_k], top_score int64[top_k]: device, overwritten
+ *     (4- and 8-byte aligned)
  *   info    device int32[2]: info[0] = |C|, info[1] = 1 if the cap engaged
  *   workspace  device scratch of bs_lmhead_workspace_bytes(...) bytes,
- *     256-byte aligned.  Its first 256 bytes are bookkeeping (the candidate
- *     counter) and must be zero-filled before the first use; every completed
- *     call leaves them zero again.  The rest is scratch, written before it is
- *     read, so one workspace serves bs_lmhead_planes_topk calls of any
- *     shapes ordered on one stream.  It is not shared with other entry points
- *     or overlapping calls.
+ *     256-byte aligned, caller-owned.  Every byte of it is written before it
+ *     is read, so it needs no initialisation and one workspace serves calls
+ *     of any shapes ordered on one stream.  It is not shared with other entry
+ *     points or overlapping calls.
+ * Errors: BS_E_NULL, BS_E_SHAPE, BS_E_OVERFLOW (dim), BS_E_RANGE (top_k,
+ *   max_candidates), BS_E_ALIGN, BS_E_WORKSPACE, BS_E_HIP.
  */
 size_t bs_lmhead_workspace_bytes(int64_t vocab, int64_t dim, int32_t top_k,
                                  int32_t max_candidates);

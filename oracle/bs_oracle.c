@@ -196,14 +196,15 @@ int or_ternary_gemv_masked(const uint8_t *planes, const int16_t *pscale, const i
 
 /* Packed BITNET_PLANES layout, as the public header of the library declares
  * it (implemented here a second time so the library's packer can be checked
- * byte for byte).  Planes 0-3, read by the full-vocabulary scan, are tiled
- * like the ternary planes: rows padded to 64; block (tile, g) = 8192 bytes at
- * offset (tile*G + g)*8192; plane q at bytes [2048q, 2048q+2048) of the
- * block, W_nonzero in its first 1024 bytes and W_negative in the next 1024,
- * row 64*tile+j at 16j.  Planes 4-7, read only for candidate rows, are row
- * major: row r occupies bytes [r*K, r*K + K); group g at r*K + 128g; plane q
- * at + 32(q-4): 16 bytes W_nonzero then 16 bytes W_negative.  Weight i of a
- * group is bit (i%8) of byte (i/8) of a 16-byte field. */
+ * byte for byte).  The four trits of planes 0-3 at one position are stored as
+ * the balanced-ternary digit sum D03 = 27*T0 + 9*T1 + 3*T2 + T3 (an int8 in
+ * [-40, 40], which determines the four trits), and planes 4-7 as
+ * D47 = 27*T4 + 9*T5 + 3*T6 + T7: one byte per position each, the same two
+ * bits per trit as two bitplanes.  D03 is tiled for the full-vocabulary scan:
+ * rows padded to 64; block (tile, g) = 8192 bytes at offset (tile*G + g)*8192;
+ * positions 128g + 16c .. 128g + 16c + 15 of row 64*tile + j at bytes
+ * [1024c + 16j, 1024c + 16j + 16) of the block.  D47, read only for candidate
+ * rows, is row major: position i of row r at byte r*K + i. */
 int or_planes_pack(const int8_t *trits, int64_t V, int64_t K, uint8_t *planes03,
                    uint8_t *planes47)
 {
@@ -213,27 +214,22 @@ int or_planes_pack(const int8_t *trits, int64_t V, int64_t K, uint8_t *planes03,
     memset(planes03, 0, (size_t)(pv * K));
     memset(planes47, 0, (size_t)(V * K));
     for (int64_t r = 0; r < V; r++)
-        for (int p = 0; p < 8; p++)
-            for (int64_t i = 0; i < K; i++) {
+        for (int64_t i = 0; i < K; i++) {
+            int d03 = 0, d47 = 0;
+            for (int p = 0; p < 8; p++) {
                 int8_t w = trits[(r * 8 + p) * K + i];
                 if (w < -1 || w > 1)
                     return OR_E_RANGE;
-                int64_t g = i / 128, bit = i % 128;
-                uint8_t *nzb, *ngb;
-                if (p < 4) {
-                    uint8_t *blk = planes03 + ((r / 64) * groups + g) * 8192 + 2048 * p;
-                    nzb = blk + 16 * (r % 64);
-                    ngb = blk + 1024 + 16 * (r % 64);
-                } else {
-                    uint8_t *blk = planes47 + r * K + 128 * g + 32 * (p - 4);
-                    nzb = blk;
-                    ngb = blk + 16;
-                }
-                if (w != 0)
-                    nzb[bit / 8] |= (uint8_t)(1u << (bit % 8));
-                if (w == -1)
-                    ngb[bit / 8] |= (uint8_t)(1u << (bit % 8));
+                if (p < 4)
+                    d03 = 3 * d03 + w;
+                else
+                    d47 = 3 * d47 + w;
             }
+            int64_t g = i / 128, c = (i % 128) / 16, e = i % 16;
+            planes03[((r / 64) * groups + g) * 8192 + 1024 * c + 16 * (r % 64) + e] =
+                (uint8_t)(int8_t)d03;
+            planes47[r * K + i] = (uint8_t)(int8_t)d47;
+        }
     return OR_OK;
 }
 

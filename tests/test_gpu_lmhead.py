@@ -89,14 +89,15 @@ def test_full_vocab_config():
 
 
 def test_workspace_shared_across_shapes():
-    """One workspace serves calls of different shapes: only its first 256
-    bytes (the candidate counter) must be zero on entry, and every call
-    leaves them zero (regression: the counter used to move with the shape
-    and land on scratch left by a larger call)."""
+    """One workspace serves calls of different shapes and needs no
+    initialisation: it starts filled with 0xFF bytes, and each call leaves
+    scratch that a later call of another shape must not read (regression: a
+    candidate counter once moved with the shape and landed on scratch left by
+    a larger call)."""
     import torch
     dev = device()
-    ws = torch.zeros(bs.lib().bs_lmhead_workspace_bytes(3000, 256, 40, 200), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.full((bs.lib().bs_lmhead_workspace_bytes(3000, 256, 40, 200),), 255,
+                    dtype=torch.uint8, device=dev)
     for V, K, k, cap, seed in [(3000, 256, 40, 200, 11), (257, 256, 7, 50, 12),
                                (2000, 128, 40, 200, 13), (300, 128, 40, 200, 14)]:
         trits, rs, h = synth.lmhead(V, K, seed)
@@ -109,4 +110,35 @@ def test_workspace_shared_across_shapes():
         widx, wsc, n, capped = oracle.lmhead_two_stage(trits, rs, h, k, cap)
         assert (idx.cpu().numpy() == widx).all() and (sc.cpu().numpy() == wsc).all()
         assert list(info.cpu().numpy()) == [n, capped]
-        assert not ws[:256].any().item()
+
+
+@pytest.mark.parametrize("V,cap", [(4096, 4096), (4097, 4096), (5000, 200)])
+def test_all_zero_planes_candidate_counts(V, cap):
+    """Every row ties, so |C| = V: at 4096 candidates the finishing pass holds
+    them in registers, above that it reads them from the workspace."""
+    trits = np.zeros((V, 8, 128), np.int8)
+    _, rs, h = synth.lmhead(V, 128, 15)
+    idx, sc, n, capped = check(trits, rs, h, 40, cap)
+    assert n == V and capped == int(V > cap)
+    assert (idx == np.arange(40)).all() and not sc.any()
+
+
+def test_many_lower_bounds():
+    """top_k = 500 over 40 stage-1 workgroups: 20000 lower bounds, more than
+    the selection pass keeps in registers."""
+    check(*synth.lmhead(20000, 128, 16), 500, 1000)
+
+
+@pytest.mark.parametrize("zero", [False, True])
+def test_more_filter_regions_than_one_pass(zero):
+    """270000 rows: 1055 filter workgroups, more than the finishing pass scans
+    at once, so the candidates are compacted first.  With all-zero planes
+    every row ties: the selection pass then finds every tile at the bound and
+    selects over the whole vocabulary."""
+    V, K = 270000, 128
+    trits, rs, h = synth.lmhead(V, K, 17)
+    if zero:
+        trits[:] = 0
+    idx, sc, n, capped = check(trits, rs, h, 40, 200)
+    if zero:
+        assert n == V and (idx == np.arange(40)).all()

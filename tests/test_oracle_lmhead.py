@@ -154,21 +154,48 @@ def test_cap_branch_keeps_top_stage1_rows():
 
 
 def test_planes_pack_layout_positions():
+    """Hand-placed trits land where the packed layout puts them, as the
+    balanced-ternary digit sums 27*T_0 + 9*T_1 + 3*T_2 + T_3 (planes 0-3) and
+    27*T_4 + 9*T_5 + 3*T_6 + T_7 (planes 4-7)."""
     V, K = 65, 256
     trits = np.zeros((V, 8, K), np.int8)
-    trits[0, 0, 0] = 1        # planes03 block (0,0) plane 0 nz byte 0 bit 0
-    trits[1, 3, 9] = -1       # block (0,0) plane 3: 3*2048 + 16 + 1 (nz), +1024 (neg), bit 1
-    trits[64, 2, 130] = 1     # tile 1, g 1: block 3: 3*8192 + 2*2048 + 0*16 + 0 bit 2
-    trits[2, 4, 0] = 1        # planes47 row 2: 2*256 + 0 + 0, bit 0
-    trits[3, 7, 255] = -1     # row 3: 3*256 + 128 + 96 + 15 (nz), +16 (neg), bit 7
+    trits[0, 0, 0] = 1                    # D03 = 27: tile 0, g 0, run 0, row 0, byte 0
+    trits[1, 3, 9] = -1                   # D03 = -1: run 0, row 1 (16), byte 9
+    trits[64, 2, 130] = 1                 # D03 = 3: tile 1, g 1 (block 3), run 0, row 0, byte 2
+    trits[5, 0:4, 17] = [1, -1, 0, 1]     # D03 = 27 - 9 + 1 = 19: run 1 (1024), row 5 (80), byte 1
+    trits[2, 4, 0] = 1                    # D47 = 27 at 2*256
+    trits[3, 7, 255] = -1                 # D47 = -1 at 3*256 + 255
+    trits[6, 4:8, 100] = -1               # D47 = -40 at 6*256 + 100
     p03, p47 = oracle.planes_pack(trits)
     assert p03.size == 128 * K and p47.size == V * K
-    want03 = {0: 0x01, 3 * 2048 + 16 + 1: 0x02, 3 * 2048 + 1024 + 16 + 1: 0x02,
-              3 * 8192 + 2 * 2048: 0x04}
-    want47 = {2 * 256: 0x01, 3 * 256 + 128 + 96 + 15: 0x80, 3 * 256 + 128 + 96 + 16 + 15: 0x80}
+    want03 = {0: 27, 16 + 9: 0xFF, 3 * 8192 + 2: 3, 1024 + 80 + 1: 19}
+    want47 = {2 * 256: 27, 3 * 256 + 255: 0xFF, 6 * 256 + 100: 256 - 40}
     assert sorted(np.nonzero(p03)[0].tolist()) == sorted(want03)
     assert sorted(np.nonzero(p47)[0].tolist()) == sorted(want47)
     for off, v in want03.items():
         assert p03[off] == v
     for off, v in want47.items():
         assert p47[off] == v
+
+
+def test_planes_digits_keep_every_trit():
+    """The packed digit sums determine the eight trits: balanced-ternary
+    decoding of D03 and D47 gives back planes 0-3 and 4-7."""
+    V, K = 70, 256
+    trits, _, _ = synth.lmhead(V, K, 21)
+    p03, p47 = oracle.planes_pack(trits)
+    blk = p03.view(np.int8).reshape(-1, K // 128, 8, 64, 16)      # tile, g, run, row, byte
+    d03 = blk.transpose(0, 3, 1, 2, 4).reshape(-1, K)[:V].astype(np.int64)
+    d47 = p47.view(np.int8).reshape(V, K).astype(np.int64)
+
+    def digits(d):
+        out = []
+        for _ in range(4):
+            t = (d + 1) % 3 - 1
+            out.append(t)
+            d = (d - t) // 3
+        assert not d.any()
+        return np.stack(out[::-1], axis=1)
+
+    assert (digits(d03) == trits[:, 0:4, :]).all()
+    assert (digits(d47) == trits[:, 4:8, :]).all()
