@@ -24,6 +24,8 @@ a bounded sample of the same step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
        python bench.py --trace-summary <rocprofv3 kernel_trace.csv>
+       python bench.py --traffic-run NxK          (workload of the --pmc runs)
+       python bench.py --traffic-summary FETCH.csv WRITE.csv NxK
 """
 from __future__ import annotations
 
@@ -243,6 +245,76 @@ def trace_summary(path: str):
     return "\n".join(out)
 
 
+CALIB_BYTES = 256 << 20         # the calibration kernel reads and writes this many bytes
+
+
+def traffic_run(shape: str, launches: int = 20):
+    """Workload for the rocprofv3 --pmc runs behind roofline.traffic: three
+    launches of a plain elementwise kernel of known size (int32 negation,
+    CALIB_BYTES read and CALIB_BYTES written: the counter calibration), then
+    `launches` launches of the ternary GEMV of `shape` on distinct weight
+    buffers (> 1 GiB in total, so they stream from HBM)."""
+    import torch
+    import bit_decode_gemv_amd as bs
+    from bit_decode_gemv_amd import synth
+    rows, k = (int(v) for v in shape.split("x"))
+    dev = torch.device("cuda:0")
+    a = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device=dev)
+    b = torch.empty_like(a)
+    ps, ss, x = make_pool(torch, bs, synth, dev, rows, k, 0, 1 << 30)
+    y = torch.empty(rows, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    for i in range(launches):
+        bs.ternary_gemv(ps[i % len(ps)], ss[i % len(ss)], x, rows, k, out=y)
+    torch.cuda.synchronize()
+    log("traffic run done: 3 calibration launches, %d GEMV launches of %s" % (launches, shape))
+
+
+def traffic_summary(fetch_csv: str, write_csv: str, shape: str):
+    """HBM bytes per GEMV launch from two rocprofv3 counter CSVs (FETCH_SIZE,
+    WRITE_SIZE; KiB per dispatch), each scaled by the calibration kernel's
+    reading of the same counter against its known byte count."""
+    rows, k = (int(v) for v in shape.split("x"))
+
+    def per_kernel(path, counter):
+        calib, gemv = [], []
+        for r in csv.DictReader(open(path)):
+            if r.get("Counter_Name") != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0
+            name = r["Kernel_Name"]
+            if "ternary_rows_kernel" in name:
+                gemv.append(v)
+            elif "neg" in name:
+                calib.append(v)
+        return calib, gemv
+
+    fc, fg = per_kernel(fetch_csv, "FETCH_SIZE")
+    wc, wg = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale = CALIB_BYTES / statistics.mean(fc)
+    w_scale = CALIB_BYTES / statistics.mean(wc)
+    fetch = statistics.mean(fg) * f_scale
+    write = statistics.mean(wg) * w_scale
+    lines = [
+        "shape: %s" % shape,
+        "kernel_source_sha256_16: %s" % _source_digest(),
+        "calibration_fetch_counter_bytes: %.0f (known %d, factor %.4f)"
+        % (statistics.mean(fc), CALIB_BYTES, f_scale),
+        "calibration_write_counter_bytes: %.0f (known %d, factor %.4f)"
+        % (statistics.mean(wc), CALIB_BYTES, w_scale),
+        "gemv_launches: %d fetch, %d write" % (len(fg), len(wg)),
+        "fetch_bytes_per_launch: %.0f" % fetch,
+        "write_bytes_per_launch: %.0f" % write,
+        "hbm_bytes_per_launch: %.0f" % (fetch + write),
+        "algorithmic_bytes_per_launch: %d (weights %d + activations %d + outputs %d)"
+        % (weight_bytes(rows, k) + k + 8 * rows, weight_bytes(rows, k), k, 8 * rows),
+    ]
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,9 +324,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--trace-summary", help="summarise a rocprofv3 kernel_trace.csv and exit")
+    ap.add_argument("--traffic-run", metavar="NxK",
+                    help="run the workload of the --pmc traffic measurement and exit")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "NxK"),
+                    help="HBM bytes per launch from the two counter CSVs and exit")
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
+        return 0
+    if args.traffic_summary:
+        print(traffic_summary(*args.traffic_summary))
+        return 0
+    if args.traffic_run:
+        traffic_run(args.traffic_run)
         return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the GEMVs would "

@@ -11,6 +11,7 @@ namespace bs {
 
 constexpr int64_t kGroup = 128;      // weights per scale group
 constexpr int64_t kTileRows = 64;    // rows per tile = lanes per wavefront
+constexpr int64_t kScaleRows = 16;   // rows per block of the packed scales
 constexpr size_t kWsAlign = 256;     // workspace alignment
 
 inline int64_t pad64(int64_t rows) { return (rows + 63) / 64 * 64; }

@@ -103,7 +103,7 @@ extern "C" int32_t bs_ternary_pack_scales(const int16_t *scales, int64_t rows, i
     memset(packed, 0, (size_t)(R * G) * sizeof(int16_t));
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t g = 0; g < G; ++g)
-            packed[((r / kTileRows) * G + g) * kTileRows + r % kTileRows] = scales[r * G + g];
+            packed[((r / kScaleRows) * G + g) * kScaleRows + r % kScaleRows] = scales[r * G + g];
     return BS_OK;
 }
 

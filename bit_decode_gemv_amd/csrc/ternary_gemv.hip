@@ -125,7 +125,7 @@ __global__ void ternary_rows_kernel(const uint8_t *__restrict__ planes,
                 const size_t blk = (size_t)tile * groups + g;
                 wnz[q] = load_stream16(planes + blk * 2048 + 16 * j);
                 wng[q] = load_stream16(planes + blk * 2048 + 1024 + 16 * j);
-                sc[q] = pscales[blk * 64 + j];
+                sc[q] = pscales[((size_t)(row >> 4) * groups + g) * 16 + (row & 15)];
             }
         }
 #pragma unroll

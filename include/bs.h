@@ -71,8 +71,10 @@ const char *bs_status_str(int32_t status);
  * Total: R*k/4 bytes.  The 64-row tile is one wavefront: lane j streams row
  * j with 16-byte loads and the wavefront reads 1 KB contiguous per plane.
  *
- * Packed scales layout: int16 at index (tile*G + g)*64 + j holds the scale of
- * row 64*tile+j, group g; padding rows hold 0.  Total R*G int16.
+ * Packed scales layout: int16 at index ((r/16)*G + g)*16 + r%16 holds the
+ * scale of row r, group g: 16-row blocks, so the 128-byte line of one block
+ * holds four of its groups and no two 16-row workgroups share a line.
+ * Padding rows hold 0.  Total R*G int16.
  */
 
 /* Bytes of packed planes (R*k/4) or a negative BS_E_* code. */

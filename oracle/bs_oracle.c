@@ -97,7 +97,8 @@ int or_ternary_gemv_def(const int8_t *t, const int16_t *scale, const int8_t *x,
  *   bytes [0,1024):    W_nonzero, row 64*tile+j at bytes [16j, 16j+16);
  *   bytes [1024,2048): W_negative, same arrangement;
  *   weight i of group g is bit (i%8) of byte (i/8) of that 16-byte field.
- * Packed scales: int16 at index (tile*G + g)*64 + j, zero for padding rows.
+ * Packed scales: int16 at index ((r/16)*G + g)*16 + r%16 (16-row blocks), zero
+ * for padding rows.
  */
 int64_t or_pad64(int64_t rows) { return (rows + 63) / 64 * 64; }
 
@@ -132,7 +133,7 @@ int or_scales_pack(const int16_t *scale, int64_t rows, int64_t k, int16_t *packe
     memset(packed, 0, (size_t)(prow * groups) * sizeof(int16_t));
     for (int64_t r = 0; r < rows; r++)
         for (int64_t g = 0; g < groups; g++)
-            packed[((r / 64) * groups + g) * 64 + r % 64] = scale[r * groups + g];
+            packed[((r / 16) * groups + g) * 16 + r % 16] = scale[r * groups + g];
     return OR_OK;
 }
 
@@ -186,7 +187,7 @@ int or_ternary_gemv_masked(const uint8_t *planes, const int16_t *pscale, const i
                 if (neg)
                     neg_sum += x[i];
             }
-            int64_t sc = pscale[((r / 64) * groups + g) * 64 + r % 64];
+            int64_t sc = pscale[((r / 16) * groups + g) * 16 + r % 16];
             acc += floor_shift((pos_sum - neg_sum) * sc, frac);
         }
         y[r] = acc;

@@ -174,6 +174,7 @@ def test_scales_pack_positions():
     sc = np.arange(70 * 3, dtype=np.int16).reshape(70, 3)
     ps = oracle.scales_pack(sc)
     assert ps.size == 128 * 3
-    assert ps[(0 * 3 + 2) * 64 + 5] == sc[5, 2]
-    assert ps[(1 * 3 + 1) * 64 + 3] == sc[67, 1]
-    assert ps[(1 * 3 + 0) * 64 + 6] == 0      # padding row 70
+    assert ps[(0 * 3 + 2) * 16 + 5] == sc[5, 2]
+    assert ps[(4 * 3 + 1) * 16 + 3] == sc[67, 1]
+    assert ps[(4 * 3 + 0) * 16 + 6] == 0      # padding row 70
+    assert ps[(7 * 3 + 2) * 16 + 15] == 0     # last padding row 127
