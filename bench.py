@@ -1,13 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the batch-1 ternary decode GEMV hot path on one MI355X.
 
-One step = one BitNet-b1.58-2B-shaped decode layer's seven projection GEMVs
-(q 2560x2560, k 640x2560, v 640x2560, o 2560x2560, gate 6912x2560,
-up 6912x2560, down 2560x6912), each one bs_ternary_gemv call on packed
-ternary planes (0.25 B/weight) plus int16 group scales, int8 activations,
-exact int64 outputs.  Steps walk a pool of distinct layers whose weights total
-more than 1 GiB, so every GEMV streams its weights from HBM rather than the
-256 MB Infinity Cache; inputs are resident in HBM before the timed region.
+One step = one BitNet-b1.58-2B-shaped decode layer's projections: q, k, v
+(2560, 640, 640 rows x 2560), o (2560 x 2560), gate and up (6912 x 2560 each)
+and down (2560 x 6912), on packed ternary planes (0.25 B/weight) plus int16
+group scales, int8 activations, exact int64 outputs.  The projections that
+share an input are stored concatenated by rows, as decode engines store them:
+q|k|v is one 3840 x 2560 matrix and gate|up one 13824 x 2560 matrix, so a step
+is four dependent bs_ternary_gemv launches (qkv, o, gate_up, down) streaming
+the same bytes as the seven separate GEMVs.  The seven-launch form of the same
+step (each projection a row range of the same buffers) is timed as well and
+reported in `config`.  Steps walk a pool of distinct layers whose weights
+total more than 1 GiB, so every GEMV streams its weights from HBM rather than
+the 256 MB Infinity Cache; inputs are resident in HBM before the timed region.
 
 Timing: the K timed steps are captured once in a HIP graph and replayed on one
 stream between two HIP events (plus a host wall clock).  `value` is the
@@ -46,6 +51,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 METRIC = "ternary GEMV weight-stream GB/s & % HBM peak, batch-1, K=2560..5120"
 LAYER = [("q", 2560, 2560), ("k", 640, 2560), ("v", 640, 2560), ("o", 2560, 2560),
          ("gate", 6912, 2560), ("up", 6912, 2560), ("down", 2560, 6912)]
+# launches of one step: (name, member projections stored concatenated by rows)
+FUSED = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")),
+         ("down", ("down",))]
 
 
 def weight_bytes(rows: int, k: int) -> int:
@@ -356,26 +364,58 @@ def main():
     stream = torch.cuda.Stream(device=dev)
     timer = Timer(torch, stream)
 
-    # layer pool: distinct weights for every layer, > 1 GiB in total
+    # layer pool: distinct weights for every layer, > 1 GiB in total.  Each
+    # launch's matrix is its member projections' rows, concatenated; a member
+    # is a row range of it (offsets are multiples of 64 rows, which is a
+    # valid packed matrix in both the plane and the scale layout).
+    import numpy as np
+    shape = {name: (r, k) for name, r, k in LAYER}
+    seed = {name: li for li, (name, _, _) in enumerate(LAYER)}
     step_bytes = sum(weight_bytes(r, k) for _, r, k in LAYER)
     n_layers = -(-(1 << 30) // step_bytes) + 1
     log("building %d layers of synthetic BitNet-2B projections (%.1f MB each)" % (
         n_layers, step_bytes / 1e6))
     base = {}
-    for li, (name, r, k) in enumerate(LAYER):
-        t, sc, x = synth.ternary(r, k, li)
-        base[name] = (torch.from_numpy(bs.ternary_pack(t)).to(dev),
-                      torch.from_numpy(bs.ternary_pack_scales(sc)).to(dev),
-                      torch.from_numpy(x).to(dev))
-    layers = [{name: (base[name][0].clone(), base[name][1].clone()) for name, _, _ in LAYER}
+    for fname, members in FUSED:
+        parts = [synth.ternary(*shape[m], seed[m]) for m in members]
+        t = np.concatenate([pt[0] for pt in parts])
+        sc = np.concatenate([pt[1] for pt in parts])
+        k = shape[members[0]][1]
+        base[fname] = (torch.from_numpy(bs.ternary_pack(t)).to(dev),
+                       torch.from_numpy(bs.ternary_pack_scales(sc)).to(dev),
+                       torch.from_numpy(parts[0][2]).to(dev), t.shape[0], k)
+        del t, sc, parts
+    layers = [{f: (base[f][0].clone(), base[f][1].clone()) for f, _ in FUSED}
               for _ in range(n_layers)]
-    ys = {name: torch.empty(r, dtype=torch.int64, device=dev) for name, r, _ in LAYER}
+    ys = {f: torch.empty(base[f][3], dtype=torch.int64, device=dev) for f, _ in FUSED}
+    member_of = {}
+    for fname, members in FUSED:
+        row0 = 0
+        for m in members:
+            member_of[m] = (fname, row0)
+            row0 += shape[m][0]
+
+    def launch_fused(i, fname):
+        p, s = layers[i % n_layers][fname]
+        _, _, x, r, k = base[fname]
+        bs.ternary_gemv(p, s, x, r, k, out=ys[fname])
+
+    def launch_member(i, m):
+        fname, row0 = member_of[m]
+        p, s = layers[i % n_layers][fname]
+        x, k = base[fname][2], base[fname][4]
+        r = shape[m][0]
+        pv = p[row0 * k // 4:(row0 + r) * k // 4]
+        sv = s[row0 * (k // 128):(row0 + r) * (k // 128)]
+        bs.ternary_gemv(pv, sv, x, r, k, out=ys[fname][row0:row0 + r])
 
     def step(i):
-        lay = layers[i % n_layers]
-        for name, r, k in LAYER:
-            p, s = lay[name]
-            bs.ternary_gemv(p, s, base[name][2], r, k, out=ys[name])
+        for fname, _ in FUSED:
+            launch_fused(i, fname)
+
+    def step7(i):
+        for m, _, _ in LAYER:
+            launch_member(i, m)
 
     # warmup, then the timed graph of exactly `steps` steps
     with torch.cuda.stream(stream):
@@ -387,31 +427,34 @@ def main():
     us, wall_us = timer.replay_us(g)
     ms_per_step = us / 1000.0 / args.steps
     value = step_bytes * args.steps / (us * 1e-6) / 1e9
-    log("step: %.3f ms (events), %.3f ms (host wall) -> %.1f GB/s" % (
+    log("step (4 launches): %.3f ms (events), %.3f ms (host wall) -> %.1f GB/s" % (
         ms_per_step, wall_us / 1000.0 / args.steps, value))
+    del g
+    g7 = timer.graph(lambda i: step7(args.warmup + i), args.steps)
+    timer.replay_us(g7)
+    us7, _ = timer.replay_us(g7)
+    value7 = step_bytes * args.steps / (us7 * 1e-6) / 1e9
+    log("step (7 launches): %.3f ms -> %.1f GB/s" % (us7 / 1000.0 / args.steps, value7))
+    del g7
 
-    # per-shape launch durations; the dominant kernel is the one with the
-    # largest share of the step
-    shape_us = {}
-    for name, r, k in LAYER:
-        if name in ("v", "up"):          # same shape as k / gate
-            continue
-        shape_us[(r, k)] = per_launch_us(
-            timer, lambda i, name=name, r=r, k=k: bs.ternary_gemv(
-                layers[i % n_layers][name][0], layers[i % n_layers][name][1], base[name][2], r,
-                k, out=ys[name]))
-    counts = {}
-    for _, r, k in LAYER:
-        counts[(r, k)] = counts.get((r, k), 0) + 1
-    dom = max(shape_us, key=lambda s: shape_us[s] * counts[s])
-    dom_us = shape_us[dom]
-    dom_bytes = weight_bytes(*dom)
+    # per-launch durations: the step's four launches and the seven members;
+    # the dominant kernel is the step launch with the largest share
+    launch_us = {f: per_launch_us(timer, lambda i, f=f: launch_fused(i, f)) for f, _ in FUSED}
+    member_us = {}
+    for m, r, k in LAYER:
+        if "%dx%d" % (r, k) not in member_us:
+            member_us["%dx%d" % (r, k)] = round(per_launch_us(
+                timer, lambda i, m=m: launch_member(i, m)), 3)
+    dom = max(launch_us, key=lambda f: launch_us[f])
+    dom_us = launch_us[dom]
+    dom_rows, dom_k = base[dom][3], base[dom][4]
+    dom_bytes = weight_bytes(dom_rows, dom_k)
     achieved = dom_bytes / dom_us / 1e3
-    tag = "%dx%d" % dom
+    tag = "%dx%d" % (dom_rows, dom_k)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": _recorded_traffic(tag),
-                "kernel": "ternary_rows_kernel %s (%d launches per step)" % (tag, counts[dom]),
+                "kernel": "ternary_rows_kernel %s (%s, 1 launch per step)" % (tag, dom),
                 "us_per_launch": round(dom_us, 3), "bytes_per_launch": dom_bytes}
 
     out = {
@@ -420,13 +463,17 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int64",
         "data": "synthetic",
         "config": {"workload": "bitnet-b1.58-2B decode projections q,k,v,o,gate,up,down, "
-                               "batch 1, one bs_ternary_gemv launch each",
-                   "shapes": {n: "%dx%d" % (r, k) for n, r, k in LAYER},
+                               "batch 1; q|k|v and gate|up stored concatenated by rows: "
+                               "4 dependent bs_ternary_gemv launches per step",
+                   "launches": {f: "%dx%d" % (base[f][3], base[f][4]) for f, _ in FUSED},
                    "weight_bytes_per_step": step_bytes, "layers_in_pool": n_layers,
                    "pool_bytes": step_bytes * n_layers, "parallelism": "single GPU",
                    "frac_hbm_peak_whole_job": round(value / HBM_PEAK_GBS, 4),
                    "host_wall_ms_per_step": round(wall_us / 1000.0 / args.steps, 5),
-                   "us_per_gemv": {"%dx%d" % s: round(v, 3) for s, v in shape_us.items()}},
+                   "us_per_launch": {f: round(v, 3) for f, v in launch_us.items()},
+                   "seven_launch_step": {"ms_per_step": round(us7 / 1000.0 / args.steps, 5),
+                                         "GBps": round(value7, 1),
+                                         "us_per_gemv": member_us}},
         "roofline": roofline,
     }
     if not args.no_extras:

@@ -66,10 +66,25 @@ __device__ __forceinline__ int group_dot(const uint4 &nz, const uint4 &ng,
     return s;
 }
 
-__device__ __forceinline__ int64_t shfl_xor64(int64_t v, int m) {
-    const int lo = __shfl_xor((int)(uint32_t)v, m);
-    const int hi = __shfl_xor((int)(v >> 32), m);
-    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+// v summed with the lane 16 (SWAP32 false) or 32 (true) apart, in every lane:
+// the gfx950 permlane swaps exchange 16-lane rows (odd rows of one operand
+// with even rows of the other) or 32-lane halves at VALU rate; with both
+// operands v, the two results are v and its partner, whose sum is wanted.
+// int64 goes as two 32-bit halves.
+template <bool SWAP32>
+__device__ __forceinline__ int64_t add_partner(int64_t v) {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)((uint64_t)v >> 32);
+    uint32_t l0, l1, h0, h1;
+    if constexpr (SWAP32) {
+        const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+        const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+        l0 = l[0]; l1 = l[1]; h0 = h[0]; h1 = h[1];
+    } else {
+        const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+        const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+        l0 = l[0]; l1 = l[1]; h0 = h[0]; h1 = h[1];
+    }
+    return (int64_t)(((uint64_t)h0 << 32) | l0) + (int64_t)(((uint64_t)h1 << 32) | l1);
 }
 
 // Wait for this wavefront's LDS writes (or reads) to complete; the slot is
@@ -153,8 +168,8 @@ __global__ void ternary_rows_kernel(const uint8_t *__restrict__ planes,
         wave_lds_fence();   // the next round overwrites the slot
     }
     // slices of one wavefront: lanes rr, rr+R, rr+2R, ...
-#pragma unroll
-    for (int m = R; m < 64; m <<= 1) acc += shfl_xor64(acc, m);
+    if constexpr (R == 16) acc = add_partner<false>(acc);
+    if constexpr (R <= 32) acc = add_partner<true>(acc);
     if (lane < R) part[wave][lane] = acc;
     __syncthreads();
     if (threadIdx.x < R) {
@@ -211,19 +226,19 @@ static int32_t launch_ternary(const TernaryCfg &c, const uint8_t *planes, const 
 
 // Launch shape, from a sweep of block heights and wavefront counts on
 // MI355X: 64-row blocks when there are enough tiles to give every CU one
-// block; otherwise 16-row blocks (four slices per wavefront) with one group
-// per slice, or 32-row blocks for long rows with many rows.
+// block and rows are long; otherwise 16-row blocks (four slices per
+// wavefront) with one group per slice (8 wavefronts up to 32 groups, 16
+// beyond), or 32-row blocks for long rows with many rows.
 static TernaryCfg choose_cfg(int64_t rows, int64_t k) {
     const int64_t groups = k / kGroup, tiles = pad64(rows) / 64;
     auto maxg_for = [](int64_t per) { return per <= 1 ? 1 : per <= 2 ? 2 : 4; };
     TernaryCfg c;
-    if (tiles >= 200) {
+    if (tiles >= 200 && groups >= 40) {
         c.rows_per_block = 64;
         c.waves = 16;
     } else if (groups <= 64) {
         c.rows_per_block = 16;
-        int64_t w = (groups + 3) / 4;
-        c.waves = (int)(w < 8 ? 8 : w > 16 ? 16 : w);
+        c.waves = groups <= 32 ? 8 : 16;
     } else if (rows >= 5000) {
         c.rows_per_block = 32;
         c.waves = 16;
