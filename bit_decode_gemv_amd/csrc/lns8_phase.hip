@@ -7,9 +7,10 @@
 // product adds +-(1 << E4) to one of eight int32 accumulators A[L3]; the row
 // result S = 2^-9 * sum_p A[p] * F[p] is materialised once per row.
 //
-// Mapping: as for the ternary GEMV, one wavefront per (64-row tile, run of
-// groups), lane j = row 64*tile + j, the activation codes uniform across the
-// wave.  Two reductions, identical in result:
+// Mapping: a workgroup owns one 64-row tile (lane j of every wavefront =
+// row 64*tile + j, so the activation codes are uniform across a wavefront)
+// and a run of 128-weight groups, one or more per wavefront.  Two
+// reductions, identical in result:
 //   DIRECT   -- per product position (uniform), route +-(1 << E4) to A[L3];
 //   POPCOUNT -- per 64-lane tile, enumerate the active states s with a
 //               ballot loop (AMD has no match-any: find the first remaining
@@ -17,10 +18,11 @@
 //               code), then C_s = popcount(A_s & W_nz) - 2 popcount(A_s & W_nz
 //               & (sign ^ W_neg)) and A[s & 7] += C_s << (s >> 3): the
 //               histogram H[phase][band] folded into A as it is produced.
-// Split partials meet in a workspace through int32 atomic adds (order-free:
-// integer addition is associative); the last workgroup of a tile, told by an
-// atomic counter, reads them back with atomic exchanges (which re-zero the
-// workspace), writes A and materialises S.
+// The wavefronts' A[8] meet in LDS (integer addition is associative, so the
+// order is free).  When K is split over several workgroups per tile, each
+// writes its partial A to the workspace with plain stores and a second
+// kernel sums the partials, writes A and materialises S: no atomics, and the
+// kernel boundary makes every partial visible across the XCDs.
 #include "kcommon.h"
 
 namespace bs {
@@ -57,99 +59,145 @@ __device__ __forceinline__ void add_phase(int A[8], int p, int v) {
     }
 }
 
+// One unit of work: 64 positions (half h of group g) for the wavefront's 64
+// rows.  Lane j holds row j's W_nonzero / W_negative bits of those positions
+// (bit i = position 64h + i) and, for the ballots, the activation byte of
+// position 64h + j.
 template <int PATH>
-__global__ __launch_bounds__(64) void lns8_kernel(
+__device__ __forceinline__ void lns8_unit(const uint8_t *__restrict__ planes,
+                                          const uint8_t *__restrict__ x, int tile, int groups,
+                                          int u, int lane, int A[8]) {
+    const int g = u >> 1, h = u & 1;
+    const size_t blk = (size_t)tile * groups + g;
+    const uint2 nzv = *reinterpret_cast<const uint2 *>(planes + blk * 2048 + 16 * lane + 8 * h);
+    const uint2 ngv = *reinterpret_cast<const uint2 *>(planes + blk * 2048 + 1024 + 16 * lane + 8 * h);
+    const uint64_t wnz = (uint64_t)nzv.x | ((uint64_t)nzv.y << 32);
+    const uint64_t wng = (uint64_t)ngv.x | ((uint64_t)ngv.y << 32);
+    const int b = x[(size_t)g * 128 + 64 * h + lane];
+    const int code = b & 0x7F;
+    if (PATH == BS_LNS8_DIRECT) {
+        // Every product is routed on its own.  Lane j first turns position
+        // j's byte into its signed weight w_j = (-1)^S1 * 2^E4 (0 for code
+        // 0); then for each phase p the positions with phase p (a ballot
+        // mask) are walked one by one, and position i adds w_i * t_i to A[p]
+        // of every row, t_i = nz_i - 2 neg_i the row's trit there (so the
+        // product sign is S1 xor [t < 0]).  The walk takes positions 0..31 and
+        // 32..63 from the two 32-bit words in turn.
+        const int mag = code ? 1 << (code >> 3) : 0;
+        const int wv = (b & 0x80) ? -mag : mag;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const uint64_t m = __ballot(code != 0 && (code & 7) == p);
+            int anz = 0, ang = 0;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const uint32_t nzw = half ? nzv.y : nzv.x, ngw = half ? ngv.y : ngv.x;
+                uint32_t mh = (uint32_t)(m >> (32 * half));
+                while (mh) {
+                    const int i = __builtin_ctz(mh);
+                    mh &= mh - 1;
+                    const int w = __builtin_amdgcn_readlane(wv, 32 * half + i);
+                    // bit * w with a 24-bit multiply-add (|w| <= 2^15)
+                    anz = __mul24((int)__builtin_amdgcn_ubfe(nzw, i, 1), w) + anz;
+                    ang = __mul24((int)__builtin_amdgcn_ubfe(ngw, i, 1), w) + ang;
+                }
+            }
+            A[p] += anz - 2 * ang;
+        }
+    } else {
+        const uint64_t sign = __ballot(b >> 7);
+        const uint64_t pneg = wnz & (sign ^ wng);
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            uint64_t rem = __ballot(code != 0 && (code & 7) == p);
+            while (rem) {
+                const int first = __builtin_ctzll(rem);
+                const int st = lane_value(code, first);
+                const uint64_t as = __ballot(code == st);
+                rem &= ~as;
+                const int cs = __popcll(as & wnz) - 2 * __popcll(as & pneg);
+                A[p] += cs * (1 << (st >> 3));
+            }
+        }
+    }
+}
+
+// One workgroup per (64-row tile, split): wavefront w takes the units (64
+// positions each, two per group) [(split * W + w) * upw, ... + upw).
+template <int PATH>
+__global__ __launch_bounds__(1024) void lns8_kernel(
     const uint8_t *__restrict__ planes, const uint8_t *__restrict__ x, int rows, int groups,
-    int gpb, int nsplit, int32_t *__restrict__ acc_out, double *__restrict__ s_out,
-    int *__restrict__ ws_acc, unsigned int *__restrict__ ws_cnt) {
+    int upw, int nsplit, int32_t *__restrict__ acc_out, double *__restrict__ s_out,
+    int *__restrict__ partial) {
+    __shared__ int red[16][8][64];
     const int tile = blockIdx.x / nsplit;
     const int split = blockIdx.x - tile * nsplit;
-    const int lane = threadIdx.x;
-    const int row = tile * 64 + lane;
-    const int g0 = split * gpb;
-    const int g1 = min(groups, g0 + gpb);
+    const int nw = blockDim.x >> 6;
+    // uniform: the activation bytes of DIRECT then come through scalar loads
+    // and the phase routing is a scalar branch
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int u0 = (split * nw + wave) * upw;
+    const int u1 = min(2 * groups, u0 + upw);
 
     int A[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int g = g0; g < g1; ++g) {
-        const size_t blk = (size_t)tile * groups + g;
-        const uint4 nzv = *reinterpret_cast<const uint4 *>(planes + blk * 2048 + 16 * lane);
-        const uint4 ngv = *reinterpret_cast<const uint4 *>(planes + blk * 2048 + 1024 + 16 * lane);
-        const uint32_t nz[4] = {nzv.x, nzv.y, nzv.z, nzv.w};
-        const uint32_t ng[4] = {ngv.x, ngv.y, ngv.z, ngv.w};
-        const uint8_t *xg = x + (size_t)g * 128;
-        if (PATH == BS_LNS8_DIRECT) {
-#pragma unroll 1
-            for (int d = 0; d < 4; ++d) {
-#pragma unroll 4
-                for (int i = 0; i < 32; ++i) {
-                    const int b = xg[32 * d + i];        // uniform activation byte
-                    const int code = b & 0x7F;
-                    if (code == 0) continue;
-                    const int nzb = (nz[d] >> i) & 1;
-                    const int ngb = (ng[d] >> i) & 1;
-                    // +1, -1 or 0: the product sign is S1 xor [t < 0]
-                    const int c = nzb - 2 * (nzb & (ngb ^ (b >> 7)));
-                    add_phase(A, code & 7, c * (1 << (code >> 3)));
-                }
+    for (int u = u0; u < u1; ++u) lns8_unit<PATH>(planes, x, tile, groups, u, lane, A);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) red[wave][p][lane] = A[p];
+    __syncthreads();
+    // pair (p, j) sums phase p of row j over the wavefronts; the 512 pairs
+    // are shared out over however many threads the workgroup has
+    for (int idx = threadIdx.x; idx < 512; idx += blockDim.x) {
+        const int p = idx >> 6, j = idx & 63;
+        int t = 0;
+        for (int w = 0; w < nw; ++w) t += red[w][p][j];
+        red[0][p][j] = t;   // wavefront 0's entry of this pair is read only here
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int row = tile * 64 + threadIdx.x;
+        int T[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) T[p] = red[0][p][threadIdx.x];
+        if (nsplit == 1) {
+            if (row < rows) {
+#pragma unroll
+                for (int p = 0; p < 8; ++p) acc_out[(size_t)row * 8 + p] = T[p];
+                if (s_out) s_out[row] = materialize(T);
             }
         } else {
-#pragma unroll 1
-            for (int h = 0; h < 2; ++h) {
-                const uint64_t wnz = (uint64_t)nz[2 * h] | ((uint64_t)nz[2 * h + 1] << 32);
-                const uint64_t wng = (uint64_t)ng[2 * h] | ((uint64_t)ng[2 * h + 1] << 32);
-                const int b = xg[64 * h + lane];         // lane = position in the tile
-                const int code = b & 0x7F;
-                const uint64_t sign = __ballot(b >> 7);
-                const uint64_t pneg = wnz & (sign ^ wng);
-#pragma unroll
-                for (int p = 0; p < 8; ++p) {
-                    uint64_t rem = __ballot(code != 0 && (code & 7) == p);
-                    while (rem) {
-                        const int first = __builtin_ctzll(rem);
-                        const int s = lane_value(code, first);
-                        const uint64_t as = __ballot(code == s);
-                        rem &= ~as;
-                        const int cs = __popcll(as & wnz) - 2 * __popcll(as & pneg);
-                        A[p] += cs * (1 << (s >> 3));
-                    }
-                }
-            }
+            const size_t padded_rows = (size_t)(gridDim.x / nsplit) * 64;
+            int4 *dst = reinterpret_cast<int4 *>(partial + ((size_t)split * padded_rows + row) * 8);
+            dst[0] = make_int4(T[0], T[1], T[2], T[3]);
+            dst[1] = make_int4(T[4], T[5], T[6], T[7]);
         }
     }
+}
 
-    if (nsplit == 1) {
-        if (row < rows) {
-#pragma unroll
-            for (int p = 0; p < 8; ++p) acc_out[(size_t)row * 8 + p] = A[p];
-            if (s_out) s_out[row] = materialize(A);
-        }
-        return;
-    }
+// Sum of the nsplit partials: thread (row, p) adds phase p of one row over
+// the splits (four loads in flight); the rows' eight sums meet in LDS for S.
+__global__ __launch_bounds__(256) void lns8_combine(const int *__restrict__ partial, int rows,
+                                                   int padded_rows, int nsplit,
+                                                   int32_t *__restrict__ acc_out,
+                                                   double *__restrict__ s_out) {
+    __shared__ int sums[32][8];
+    const int idx = blockIdx.x * 256 + threadIdx.x;   // = row * 8 + p
+    const int row = idx >> 3, p = idx & 7;
+    int t = 0;
     if (row < rows) {
+        int sp = 0;
+        for (; sp + 4 <= nsplit; sp += 4) {
+            int v[4];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) atomicAdd(&ws_acc[(size_t)row * 8 + p], A[p]);
-    }
-    // every atomic of this wavefront is performed before the tile counter
-    // moves; the counter and the accumulators are only touched by atomic
-    // read-modify-writes, so no cache write-back or invalidate is needed
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    unsigned int prev = 0;
-    if (lane == 0) prev = atomicAdd(&ws_cnt[tile], 1u);
-    prev = __builtin_amdgcn_readfirstlane(prev);
-    if (prev == (unsigned int)(nsplit - 1)) {
-        if (row < rows) {
-            int T[8];
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                T[p] = atomicExch(&ws_acc[(size_t)row * 8 + p], 0);
-                acc_out[(size_t)row * 8 + p] = T[p];
-            }
-            if (s_out) s_out[row] = materialize(T);
+            for (int u = 0; u < 4; ++u) v[u] = partial[((size_t)(sp + u) * padded_rows + row) * 8 + p];
+            t += v[0] + v[1] + v[2] + v[3];
         }
-        if (lane == 0) atomicExch(&ws_cnt[tile], 0u);
+        for (; sp < nsplit; ++sp) t += partial[((size_t)sp * padded_rows + row) * 8 + p];
+        acc_out[idx] = t;
     }
+    sums[threadIdx.x >> 3][p] = t;
+    __syncthreads();
+    if (s_out && p == 0 && row < rows) s_out[row] = materialize(sums[threadIdx.x >> 3]);
 }
 
 }  // namespace
@@ -161,16 +209,41 @@ using namespace bs;
 // below that is 65408.
 static constexpr int64_t kLns8MaxK = 65408;
 
-static size_t lns8_ws_layout(int64_t rows, size_t *cnt_off) {
-    const int64_t R = pad64(rows);
-    const size_t acc_bytes = align_up((size_t)R * 8 * 4, kWsAlign);
-    if (cnt_off) *cnt_off = acc_bytes;
-    return acc_bytes + align_up((size_t)(R / 64) * 4, kWsAlign);
+// Launch shape: about 4096 wavefronts in all (four per SIMD, to hide the
+// scalar/vector dependency chains of the per-product loop), up to 16 per
+// workgroup, each with at least one 64-position unit; K is split over
+// workgroups only when one workgroup per tile cannot hold them.
+struct Lns8Plan {
+    int64_t tiles, groups;
+    int waves, upw, nsplit;
+};
+
+static Lns8Plan lns8_plan(int64_t rows, int64_t k) {
+    Lns8Plan pl;
+    pl.tiles = pad64(rows) / 64;
+    pl.groups = k / kGroup;
+    const int64_t units = 2 * pl.groups;
+    int64_t want = (4096 + pl.tiles - 1) / pl.tiles;   // wavefronts per tile
+    if (want < 1) want = 1;
+    if (want > units) want = units;
+    pl.waves = (int)(want < 16 ? want : 16);
+    int64_t nsplit = (want + pl.waves - 1) / pl.waves;
+    pl.upw = (int)((units + pl.waves * nsplit - 1) / (pl.waves * nsplit));
+    pl.nsplit = (int)((units + (int64_t)pl.waves * pl.upw - 1) / ((int64_t)pl.waves * pl.upw));
+    return pl;
+}
+
+// Workspace: the partial accumulators, int32[nsplit][R][8] (none when K is
+// not split).  Written before they are read: no initialisation needed.
+static size_t lns8_ws_bytes(int64_t rows, int64_t k) {
+    const Lns8Plan pl = lns8_plan(rows, k);
+    const size_t part = pl.nsplit > 1 ? (size_t)pl.nsplit * (size_t)pad64(rows) * 8 * 4 : 0;
+    return align_up(part > 0 ? part : 1, kWsAlign);
 }
 
 extern "C" size_t bs_lns8_workspace_bytes(int64_t rows, int64_t k) {
     if (check_rows_k(rows, k, kLns8MaxK) != BS_OK) return 0;
-    return lns8_ws_layout(rows, nullptr);
+    return lns8_ws_bytes(rows, k);
 }
 
 extern "C" int32_t bs_lns8_phase_gemv(const uint8_t *planes, const uint8_t *x_lns8,
@@ -180,17 +253,23 @@ extern "C" int32_t bs_lns8_phase_gemv(const uint8_t *planes, const uint8_t *x_ln
     if (!planes || !x_lns8 || !acc) return BS_E_NULL;
     if (int32_t st = check_rows_k(rows, k, kLns8MaxK)) return st;
     if (path != BS_LNS8_DIRECT && path != BS_LNS8_POPCOUNT) return BS_E_RANGE;
-    size_t cnt_off = 0;
-    const size_t need = lns8_ws_layout(rows, &cnt_off);
-    if (!ws_ok(workspace, workspace_bytes, need)) return BS_E_WORKSPACE;
+    if (((uintptr_t)planes & 15) || ((uintptr_t)x_lns8 & 3) || ((uintptr_t)acc & 3) ||
+        ((uintptr_t)s & 7))
+        return BS_E_ALIGN;
+    if (!ws_ok(workspace, workspace_bytes, lns8_ws_bytes(rows, k))) return BS_E_WORKSPACE;
 
-    const SplitK sk = plan_splitk(rows, k, 2048);
-    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    const Lns8Plan pl = lns8_plan(rows, k);
+    hipStream_t st = (hipStream_t)stream;
+    int *partial = static_cast<int *>(workspace);
     auto kern = path == BS_LNS8_DIRECT ? lns8_kernel<BS_LNS8_DIRECT> : lns8_kernel<BS_LNS8_POPCOUNT>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(sk.tiles * sk.nsplit)), dim3(64), 0,
-                       (hipStream_t)stream, planes, x_lns8, (int)rows, (int)sk.groups,
-                       (int)sk.gpb, (int)sk.nsplit, acc, s, reinterpret_cast<int *>(ws),
-                       reinterpret_cast<unsigned int *>(ws + cnt_off));
+    hipLaunchKernelGGL(kern, dim3((unsigned)(pl.tiles * pl.nsplit)), dim3(pl.waves * 64), 0, st,
+                       planes, x_lns8, (int)rows, (int)pl.groups, pl.upw, pl.nsplit, acc, s,
+                       partial);
     BS_LAUNCH_CHECK();
+    if (pl.nsplit > 1) {
+        hipLaunchKernelGGL(lns8_combine, dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, st,
+                           partial, (int)rows, (int)pad64(rows), pl.nsplit, acc, s);
+        BS_LAUNCH_CHECK();
+    }
     return BS_OK;
 }

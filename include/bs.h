@@ -142,15 +142,16 @@ int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales, const int8
  *           Both paths return identical bytes.
  *   rows    >= 1;  k >= 128, k % 128 == 0, k <= 65408 (|A| <= k*2^15 must
  *           fit int32, else BS_E_OVERFLOW)
- *   acc     device int32[rows][8], overwritten
+ *   planes  device, 16-byte aligned; x_lns8 device uint8[k], 4-byte aligned
+ *   acc     device int32[rows][8], overwritten, 4-byte aligned
  *   s       device double[rows], or NULL to skip the materialisation
  *   workspace  device scratch of at least bs_lns8_workspace_bytes(rows, k)
- *           bytes, 256-byte aligned: the split-K accumulators and tile
- *           counters.  It must be zero-filled before its first use; every
- *           completed call leaves it zero-filled again, so one workspace
- *           serves any sequence of calls ordered on one stream.  Calls that
- *           may overlap need separate workspaces; a workspace is not shared
- *           with other entry points.
+ *           bytes, 256-byte aligned, caller-owned: the partial accumulators
+ *           when K is split over several workgroups.  Every byte is written
+ *           before it is read, so it needs no initialisation; calls that may
+ *           overlap need separate workspaces.
+ * Errors: BS_E_NULL, BS_E_SHAPE, BS_E_OVERFLOW (k), BS_E_RANGE (path),
+ *   BS_E_ALIGN, BS_E_WORKSPACE, BS_E_HIP.
  */
 #define BS_LNS8_DIRECT 0
 #define BS_LNS8_POPCOUNT 1

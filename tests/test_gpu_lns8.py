@@ -82,3 +82,19 @@ def _adversarial():
 @pytest.mark.parametrize("case", list(_adversarial()), ids=lambda c: c[0])
 def test_lns8_adversarial(case):
     check(case[1], case[2])
+
+
+@pytest.mark.parametrize("rows,k", [(64, 65408), (200, 8192), (2000, 128), (70, 2048)])
+def test_lns8_split_and_long_rows(rows, k):
+    """K split over several workgroups per tile (partials combined by a
+    second kernel) and the largest K whose |A| fits int32; 2000 x 128 keeps
+    one wavefront per tile."""
+    check(*synth.lns8(rows, k, seed=k + rows))
+
+
+def test_lns8_max_k_extremes():
+    """k = 65408 with every product +2^15 into one phase: |A| reaches
+    65408 * 2^15 = 2^31 - 2^22, the int32 bound the shape limit keeps."""
+    k = 65408
+    t = np.ones((64, k), np.int8)
+    check(t, np.full(k, 127, np.uint8))
