@@ -269,7 +269,7 @@ __device__ __forceinline__ unsigned long long radix_select_desc(int n, unsigned 
                 const uint64_t bm = __ballot(m);
                 if (bm) {
                     const int first = __builtin_ctzll(bm);
-                    const int d0 = __shfl(d, first);
+                    const int d0 = __builtin_amdgcn_readlane(d, first);
                     if (__ballot(m && d == d0) == bm) {
                         if (lane == first) atomicAdd(&sh.hist[d0], (unsigned)__popcll(bm));
                     } else if (m) {
@@ -345,25 +345,56 @@ __device__ __forceinline__ void block_count2(int n, Cls cls, SelShared &sh, unsi
     __syncthreads();
 }
 
+// Ranks of n <= 1024 entries: beats(j, e) says whether entry j comes before
+// entry e in a strict total order; use(e, rank) runs once per entry with its
+// rank.  The pairwise comparisons are shared out over the whole workgroup:
+// entries are padded to a multiple of 64 (npad), P = blockDim / npad threads
+// per entry each take a 1/P share of j (a wavefront's share is uniform), and
+// the partial ranks meet in rk (int[blockDim] in LDS).
+template <typename Beats, typename Use>
+__device__ __forceinline__ void block_rank(int n, Beats beats, Use use, int *rk) {
+    const int npad = (n + 63) & ~63;
+    const int P = (int)blockDim.x / npad;
+    const int t = (int)threadIdx.x, e = t % npad;
+    const int part = __builtin_amdgcn_readfirstlane(t / npad);   // uniform: npad % 64 == 0
+    const int chunk = (n + P - 1) / P;
+    int r = 0;
+    if (part < P) {
+        const int j0 = part * chunk, j1 = min(n, j0 + chunk);
+        if (e < n) {
+#pragma unroll 8
+            for (int j = j0; j < j1; ++j) r += beats(j, e) ? 1 : 0;
+        }
+    }
+    if (t < npad * P) rk[t] = r;
+    __syncthreads();
+    if (t < n) {
+        int tot = 0;
+        for (int q = 0; q < P; ++q) tot += rk[q * npad + t];
+        use(t, tot);
+    }
+    __syncthreads();
+}
+
 // The `want`-th largest (1-based) of n <= blockDim.x keys, thread t holding
-// key t (t < n): every thread ranks its key against an LDS copy.
+// key t (t < n).
 __device__ __forceinline__ unsigned long long rank_select_desc(int n, int want,
                                                                unsigned long long mykey,
-                                                               unsigned long long *lds,
+                                                               unsigned long long *lds, int *rk,
                                                                unsigned long long *result) {
     const int t = (int)threadIdx.x;
     if (t < n) lds[t] = mykey;
     __syncthreads();
-    if (t < n) {
-        int r = 0;
-#pragma unroll 8
-        for (int j = 0; j < n; ++j) {
-            const unsigned long long o = lds[j];
-            r += (o > mykey) || (o == mykey && j < t);
-        }
-        if (r == want - 1) *result = mykey;
-    }
-    __syncthreads();
+    block_rank(
+        n,
+        [&](int j, int e) {
+            const unsigned long long o = lds[j], m = lds[e];
+            return o > m || (o == m && j < e);
+        },
+        [&](int e, int r) {
+            if (r == want - 1) *result = lds[e];
+        },
+        rk);
     const unsigned long long v = *result;
     __syncthreads();   // lds and result reusable
     return v;
@@ -375,6 +406,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
     __shared__ SelShared sh;
     __shared__ unsigned long long list[kSelList];
     __shared__ int tlist[kSelTiles];
+    __shared__ int rk[kBlockThreads];
     __shared__ unsigned long long res;
     __shared__ unsigned int n_t, n_l;
     const int t = (int)threadIdx.x;
@@ -387,7 +419,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
     unsigned long long thr = 0;
     if (nwg >= top_k) {
         if (nwg <= (int)blockDim.x)
-            thr = rank_select_desc(nwg, top_k, t < nwg ? okey(ws.wg_max[t]) : 0ull, list, &res);
+            thr = rank_select_desc(nwg, top_k, t < nwg ? okey(ws.wg_max[t]) : 0ull, list, rk, &res);
         else
             thr = radix_select_desc<4>(
                 nwg, (unsigned long long)top_k, [&](int i, int) { return okey(ws.wg_max[i]); },
@@ -428,8 +460,26 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
         }
         __syncthreads();
         const int ln = (int)n_l;
-        if (ln <= (int)blockDim.x) {
-            kk = rank_select_desc(ln, top_k, t < ln ? list[t] : 0ull, list, &res);
+        if (ln <= 64) {
+            // one wavefront ranks the list: lane e against every entry j,
+            // broadcast with readlane
+            if (t < 64) {
+                const unsigned long long me = t < ln ? list[t] : 0ull;
+                const uint32_t mlo = (uint32_t)me, mhi = (uint32_t)(me >> 32);
+                int r = 0;
+                for (int j = 0; j < ln; ++j) {
+                    const unsigned long long o =
+                        ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)mhi, j) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)mlo, j);
+                    r += (o > me) || (o == me && j < t);
+                }
+                if (t < ln && r == top_k - 1) res = me;
+            }
+            __syncthreads();
+            kk = res;
+            done = true;
+        } else if (ln <= (int)blockDim.x) {
+            kk = rank_select_desc(ln, top_k, t < ln ? list[t] : 0ull, list, rk, &res);
             done = true;
         } else if (ln <= kSelList) {
             kk = radix_select_desc<4>(
@@ -677,20 +727,24 @@ __device__ __forceinline__ void finish_body(int n, int top_k, int cap, int32_t *
 }
 
 // The top_k of the m rows (tk, ti) by (S' desc, row asc): each row's rank
-// among them, those below top_k written at their rank.
+// among them, those below top_k written at their rank.  rk: int[blockDim].
 __device__ __forceinline__ void output_by_rank(int m, int top_k, const long long *tk,
                                                const int *ti, int32_t *__restrict__ top_idx,
-                                               int64_t *__restrict__ top_score) {
-    for (int e = threadIdx.x; e < m; e += blockDim.x) {
-        const long long me = tk[e];
-        const int mi = ti[e];
-        int r = 0;
-#pragma unroll 8
-        for (int j = 0; j < m; ++j) r += better(tk[j], ti[j], me, mi);
+                                               int64_t *__restrict__ top_score, int *rk) {
+    auto put = [&](int e, int r) {
         if (r < top_k) {
-            top_idx[r] = mi;
-            top_score[r] = me;
+            top_idx[r] = ti[e];
+            top_score[r] = tk[e];
         }
+    };
+    if (m <= (int)blockDim.x) {
+        block_rank(m, [&](int j, int e) { return better(tk[j], ti[j], tk[e], ti[e]); }, put, rk);
+        return;
+    }
+    for (int e = threadIdx.x; e < m; e += blockDim.x) {
+        int r = 0;
+        for (int j = 0; j < m; ++j) r += better(tk[j], ti[j], tk[e], ti[e]);
+        put(e, r);
     }
 }
 
@@ -771,7 +825,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
             ti[i] = src.rows[sl];
         }
         __syncthreads();
-        output_by_rank(n, top_k, tk, ti, top_idx, top_score);
+        output_by_rank(n, top_k, tk, ti, top_idx, top_score, ro);   // ro no longer needed
         return;
     }
     if (regions) {
@@ -780,10 +834,13 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
         const bool nonempty = t < nwf && (t + 1 < nwf ? ro[t + 1] : n) > ro[t];
         const int nne = __syncthreads_count(nonempty);
         unsigned long long thr = 0;
-        if (nne >= cap)
-            thr = rank_select_desc(nwf, cap,
-                                   nonempty ? okey(ws.cand_s1[(size_t)t * kFilterRows]) : 0ull,
-                                   reinterpret_cast<unsigned long long *>(tk), &res);
+        if (nne >= cap) {
+            const unsigned long long head =
+                nonempty ? okey(ws.cand_s1[(size_t)t * kFilterRows]) : 0ull;
+            thr = radix_select_desc<1>(
+                nwf, (unsigned long long)cap, [&](int, int) { return head; },
+                [&](int, int) { return nonempty; }, sh);
+        }
         if (t == 0) nl1 = 0;
         __syncthreads();
         // the sorted prefix >= T of every region
@@ -816,19 +873,16 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
         if (nl <= kFinList) {
             // rank by (S1' desc, row asc): the first cap are kept, placed at
             // their rank
-            if (t < nl) {
-                const long long me = l1s1[t];
-                const int mi = l1id[t];
-                int r = 0;
-#pragma unroll 8
-                for (int j = 0; j < nl; ++j) r += better(l1s1[j], l1id[j], me, mi);
-                if (r < cap) {
-                    tk[r] = l1s[t];
-                    ti[r] = mi;
-                }
-            }
-            __syncthreads();
-            output_by_rank(cap, top_k, tk, ti, top_idx, top_score);
+            block_rank(
+                nl, [&](int j, int e) { return better(l1s1[j], l1id[j], l1s1[e], l1id[e]); },
+                [&](int e, int r) {
+                    if (r < cap) {
+                        tk[r] = l1s[e];
+                        ti[r] = l1id[e];
+                    }
+                },
+                ro);   // the region prefix sums are no longer needed
+            output_by_rank(cap, top_k, tk, ti, top_idx, top_score, ro);
             return;
         }
     }
