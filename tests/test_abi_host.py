@@ -133,3 +133,36 @@ def test_lmhead_validation():
     assert _lmh(dim=10240) == bs.BS_E_OVERFLOW      # int64 bound of the exact score
     assert _lmh(ws=None) == bs.BS_E_WORKSPACE
     assert _lmh(wsn=1024) == bs.BS_E_WORKSPACE
+
+
+def test_alignment_validation():
+    """Every device pointer's documented alignment is checked on the host."""
+    off = lambda n: ctypes.c_void_p((1 << 20) + n)
+    assert _lns8(planes=off(8)) == bs.BS_E_ALIGN
+    assert _lns8(x=off(2)) == bs.BS_E_ALIGN
+    assert _lns8(acc=off(2)) == bs.BS_E_ALIGN
+    assert _lns8(s=off(4)) == bs.BS_E_ALIGN
+    assert _lmh(p03=off(8)) == bs.BS_E_ALIGN
+    assert _lmh(p47=off(4)) == bs.BS_E_ALIGN
+    assert _lmh(rs=off(2)) == bs.BS_E_ALIGN
+    assert _lmh(h=off(4)) == bs.BS_E_ALIGN
+    assert _lmh(idx=off(2)) == bs.BS_E_ALIGN
+    assert _lmh(score=off(4)) == bs.BS_E_ALIGN
+    assert _lmh(info=off(2)) == bs.BS_E_ALIGN
+    assert _lmh(ws=off(128)) == bs.BS_E_WORKSPACE    # the workspace is 256-byte aligned
+
+
+def test_lmhead_vocab_limit():
+    assert _lmh(V=(1 << 31) - 1023) == bs.BS_E_SHAPE
+    assert bs.lib().bs_lmhead_workspace_bytes((1 << 31) - 1023, 256, 40, 200) == 0
+
+
+def test_workspace_sizes_follow_the_launch_plans():
+    lib = bs.lib()
+    # LNS8: partials only when K is split over workgroups (int32[nsplit][R][8])
+    assert lib.bs_lns8_workspace_bytes(2000, 128) == 256
+    assert lib.bs_lns8_workspace_bytes(4096, 4096) == 4 * 4096 * 8 * 4
+    assert lib.bs_lns8_workspace_bytes(64, 65408) == 64 * 64 * 8 * 4
+    # lm_head: grows with the vocabulary, not with top_k beyond the bounds
+    a = lib.bs_lmhead_workspace_bytes(128256, 2560, 40, 200)
+    assert a == lib.bs_lmhead_workspace_bytes(128256, 2560, 200, 200) > 128256 * 40

@@ -1,0 +1,61 @@
+"""Host-side checks of bench.py's contract paths that need no GPU: the
+one-GPU rule, and the parsers behind the profiles/ summaries (kernel trace
+and --pmc traffic), fed small synthetic CSV files."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def _write(path, fields, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_trace_summary(tmp_path):
+    p = tmp_path / "kernel_trace.csv"
+    fields = ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"]
+    rows = [{"Kernel_Name": "void bs::(anonymous namespace)::ternary_rows_kernel<16, 1>(x)",
+             "Grid_Size_X": 1024, "Workgroup_Size_X": 512, "Start_Timestamp": 1000 * i,
+             "End_Timestamp": 1000 * i + d} for i, d in enumerate([3000, 4000, 5000])]
+    _write(p, fields, rows)
+    out = bench.trace_summary(str(p))
+    assert "void bs::ternary_rows_kernel<16, 1>" in out
+    assert "calls      3" in out and "avg    4.000 us" in out and "min    3.000 us" in out
+
+
+def test_traffic_summary(tmp_path):
+    fields = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    calib = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>"
+    gemv = "void bs::(anonymous namespace)::ternary_rows_kernel<16, 1>(args)"
+    half = bench.CALIB_BYTES / 1024 / 2          # FETCH_SIZE reads half the known bytes
+    _write(tmp_path / "f.csv", fields,
+           [{"Kernel_Name": calib, "Counter_Name": "FETCH_SIZE", "Counter_Value": half}] * 3 +
+           [{"Kernel_Name": gemv, "Counter_Name": "FETCH_SIZE", "Counter_Value": 1000.0}] * 4)
+    _write(tmp_path / "w.csv", fields,
+           [{"Kernel_Name": calib, "Counter_Name": "WRITE_SIZE",
+             "Counter_Value": bench.CALIB_BYTES / 1024}] * 3 +
+           [{"Kernel_Name": gemv, "Counter_Name": "WRITE_SIZE", "Counter_Value": 20.0}] * 4)
+    out = bench.traffic_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "640x2560")
+    vals = dict(line.split(": ", 1) for line in out.splitlines())
+    assert float(vals["fetch_bytes_per_launch"]) == pytest.approx(2 * 1000 * 1024)
+    assert float(vals["write_bytes_per_launch"]) == pytest.approx(20 * 1024)
+    assert float(vals["hbm_bytes_per_launch"]) == pytest.approx(2 * 1000 * 1024 + 20 * 1024)
+    assert vals["kernel_source_sha256_16"] == bench._source_digest()
