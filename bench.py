@@ -137,7 +137,45 @@ def cpu_baseline(seconds_target: float):
             "sample": "%d full step(s) (q,k,v,o,gate,up,down at full size, seed 0) through "
                       "or_ternary_gemv_def on unpacked int8 trits, single thread, %.1f s CPU"
                       % (done, t_cpu),
-            "cpu_model": _cpu_model(), "ms_per_step": round(1000.0 * t_cpu / done, 2)}
+            "cpu_model": _cpu_model(), "ms_per_step": round(1000.0 * t_cpu / done, 2),
+            "per_config": _oracle_per_config()}
+
+
+def _oracle_per_config():
+    """The oracle's other entry points, single-threaded, each timed once on
+    one seeded input (median of 3 where it takes under a second)."""
+    import numpy as np
+    import oracle
+    from bit_decode_gemv_amd import synth
+
+    def med(fn, reps):
+        ts = []
+        for _ in range(reps):
+            t0 = time.process_time()
+            fn()
+            ts.append(time.process_time() - t0)
+        return statistics.median(ts)
+
+    out = {}
+    t, sc, x = synth.tiny(0)
+    out["ternary_256x512_us"] = round(1e6 * med(lambda: oracle.ternary_gemv_def(t, sc, x), 3), 1)
+    t, sc, x = synth.ternary(13824, 5120, 0)
+    sec = med(lambda: oracle.ternary_gemv_def(t, sc, x), 3)
+    out["ternary_13824x5120_us"] = round(1e6 * sec, 1)
+    out["ternary_13824x5120_GBps"] = round(weight_bytes(13824, 5120) / sec / 1e9, 4)
+    t8, x8 = synth.lns8(4096, 4096, 0)
+    out["lns8_4096x4096_direct_us"] = round(1e6 * med(lambda: oracle.lns8_direct(t8, x8), 3), 1)
+    out["lns8_4096x4096_popcount_us"] = round(
+        1e6 * med(lambda: oracle.lns8_popcount(t8, x8), 1), 1)
+    V = 16384
+    trits, rs, h = synth.lmhead(V, 2560, 0)
+    scale = synth.LMHEAD_SHAPE[0] / V
+    out["lmhead_two_stage_us_scaled_from_16384_rows"] = round(
+        1e6 * scale * med(lambda: oracle.lmhead_two_stage(trits, rs, h, 40, 200), 1), 1)
+    out["lmhead_brute_us_scaled_from_16384_rows"] = round(
+        1e6 * scale * med(lambda: oracle.lmhead_brute(trits, rs, h, 40), 1), 1)
+    del np
+    return out
 
 
 def _cpu_model():
@@ -176,6 +214,48 @@ def _recorded_traffic(shape_tag: str):
         return int(float(vals["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def context(torch, dev, timer):
+    """The empty-launch floor (a one-element fill, back to back in a graph)
+    and a 1 GiB read through torch's float32 sum, for scale."""
+    one = torch.zeros(1, dtype=torch.int32, device=dev)
+    floor_us = per_launch_us(timer, lambda i: one.fill_(i), n=200)
+    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    acc = torch.empty(1, dtype=torch.float32, device=dev)
+    # eager, not graph-captured (a multi-block reduction may record memset nodes)
+    with torch.cuda.stream(timer.stream):
+        torch.sum(big, dim=0, keepdim=True, out=acc)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(timer.stream)
+        for _ in range(10):
+            torch.sum(big, dim=0, keepdim=True, out=acc)
+        e1.record(timer.stream)
+    torch.cuda.synchronize()
+    read_us = e0.elapsed_time(e1) * 1000.0 / 10
+    del big
+    return {"launch_floor_us": round(floor_us, 3),
+            "read_1GiB_GBps": round((1 << 30) / read_us / 1e3, 1),
+            "read_1GiB_note": "torch.sum over 2^28 float32 (a reduction, so a lower bound on "
+                              "the read ceiling), 10 eager launches between HIP events"}
+
+
+def activation_reuse_sweep(torch, bs, synth, dev, timer, k=2560):
+    """us and weight-stream GB/s of one launch as the rows sharing one staged
+    activation vector grow (K = 2560): where the kernel turns bandwidth-bound."""
+    out = {}
+    for rows in (64, 256, 1024, 2560, 6912, 13824, 27648, 55296):
+        ps, ss, x = make_pool(torch, bs, synth, dev, rows, k, 0, 1 << 30)
+        y = torch.empty(rows, dtype=torch.int64, device=dev)
+        us = per_launch_us(timer, lambda i: bs.ternary_gemv(ps[i % len(ps)], ss[i % len(ss)], x,
+                                                            rows, k, out=y), n=100)
+        wb = weight_bytes(rows, k)
+        out[str(rows)] = {"us": round(us, 3), "GBps": round(wb / us / 1e3, 1)}
+        del ps, ss
+    log("activation-reuse sweep: " + ", ".join("%s rows %.0f GB/s" % (r, v["GBps"])
+                                                for r, v in out.items()))
+    return out
 
 
 def run_extras(torch, bs, synth, dev, timer):
@@ -478,6 +558,9 @@ def main():
     }
     if not args.no_extras:
         out["ops"] = run_extras(torch, bs, synth, dev, timer)
+        out["ops"]["activation_reuse_sweep_k2560"] = activation_reuse_sweep(
+            torch, bs, synth, dev, timer)
+        out["context"] = context(torch, dev, timer)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (~%.0f s)" % args.cpu_seconds)
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
