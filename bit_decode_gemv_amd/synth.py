@@ -18,7 +18,9 @@ LLaMA-like projections; the models themselves are not used):
 * ``lns8``     -- iid uniform trits and LNS8 activation bytes: sign bit
   uniform, code 0 with probability 0.05, else uniform in 60..100;
 * ``lmhead``   -- eight iid uniform trit planes per row, int32 row scales
-  uniform in [1, 4096], int8 hidden state from rounded N(0, 32^2).
+  uniform in [1, 4096], int8 hidden state from rounded N(0, 32^2);
+* ``q1``       -- iid equiprobable signs {-1, +1}, int16 group scales uniform
+  in [1, 4096], int8 activations from rounded N(0, 32^2).
 """
 from __future__ import annotations
 
@@ -75,6 +77,16 @@ def ternary(rows: int, k: int, seed: int, p_zero: float = 0.4, act: str = "norma
     else:
         raise ValueError(act)
     return t, scales, x
+
+
+def q1(rows: int, k: int, seed: int):
+    """(s int8[rows][k] in {-1, +1}, scales int16[rows][k/128], x int8[k])."""
+    if k % GROUP:
+        raise ValueError("k must be a multiple of 128")
+    rs_, rsc, rx = _streams(seed, 3)
+    s = rs_.integers(0, 2, size=(rows, k), dtype=np.int8) * 2 - 1
+    scales = rsc.integers(1, 4097, size=(rows, k // GROUP), dtype=np.int16)
+    return s.astype(np.int8), scales, _act_normal32(rx, k)
 
 
 def tiny(seed: int = 0):

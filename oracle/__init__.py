@@ -51,7 +51,7 @@ def _load():
                      "or_ternary_unpack", "or_ternary_gemv_masked", "or_lns8_direct",
                      "or_lns8_tile64", "or_lns8_popcount", "or_lns8_fp64_dot",
                      "or_lmhead_brute", "or_lmhead_two_stage", "or_lmhead_stage1",
-                     "or_planes_pack"):
+                     "or_planes_pack", "or_q1_gemv_def", "or_q1_pack", "or_q1_gemv_masked"):
             getattr(lib, name).restype = ctypes.c_int
         lib.or_pad64.restype = ctypes.c_int64
         lib.or_pad64.argtypes = [ctypes.c_int64]
@@ -228,6 +228,44 @@ def lns8_materialize(acc: np.ndarray) -> np.ndarray:
             s += int(acc[r, p]) * fs[p]
         out[r] = float(s * scale)
     return out
+
+
+# --------------------------------------------------------------------------
+# Q1_0 ("A standalone deterministic integer inference engine for BitNet-style
+# LLMs", section 4.1)
+# --------------------------------------------------------------------------
+
+def q1_gemv_def(s, scale, x, frac: int = 0):
+    """Definition: sum_g floorshift((sum_i s_i x_i) * scale[r][g], frac)."""
+    s = np.ascontiguousarray(s, dtype=np.int8)
+    scale = np.ascontiguousarray(scale, dtype=np.int16)
+    x = np.ascontiguousarray(x, dtype=np.int8)
+    rows, k = s.shape
+    y = np.empty(rows, dtype=np.int64)
+    _check(_load().or_q1_gemv_def(_p(s), _p(scale), _p(x), _i64(rows), _i64(k), frac, _p(y)),
+           "q1_gemv_def")
+    return y
+
+
+def q1_pack(s):
+    """signs[rows][k] in {-1, +1} -> packed bits (1 = +1), tiled like one
+    ternary plane."""
+    s = np.ascontiguousarray(s, dtype=np.int8)
+    rows, k = s.shape
+    bits = np.zeros(pad64(rows) * k // 8, dtype=np.uint8)
+    _check(_load().or_q1_pack(_p(s), _i64(rows), _i64(k), _p(bits)), "q1_pack")
+    return bits
+
+
+def q1_gemv_masked(bits, pscale, x, rows: int, k: int, frac: int = 0):
+    """The page's masked form 2*pos_sum - block_total on packed bits/scales."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint8)
+    pscale = np.ascontiguousarray(pscale, dtype=np.int16)
+    x = np.ascontiguousarray(x, dtype=np.int8)
+    y = np.empty(rows, dtype=np.int64)
+    _check(_load().or_q1_gemv_masked(_p(bits), _p(pscale), _p(x), _i64(rows), _i64(k), frac,
+                                     _p(y)), "q1_gemv_masked")
+    return y
 
 
 # --------------------------------------------------------------------------

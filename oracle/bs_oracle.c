@@ -235,6 +235,93 @@ int or_planes_pack(const int8_t *trits, int64_t V, int64_t K, uint8_t *planes03,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Q1_0 weight apply ("A standalone deterministic integer inference engine   */
+/* for BitNet-style LLMs", section 4.1): signs in {-1, +1}, one int scale   */
+/* per 128-weight group, a per-group floor shift, then the sum over groups. */
+/* ------------------------------------------------------------------------ */
+
+/* Definition form: out[r] = sum_g floorshift((sum_i s_i x_i) * scale[r][g], frac). */
+int or_q1_gemv_def(const int8_t *s, const int16_t *scale, const int8_t *x, int64_t rows,
+                   int64_t k, int frac, int64_t *y)
+{
+    if (rows < 0 || k < 0 || k % 128 != 0)
+        return OR_E_SHAPE;
+    if (frac < 0 || frac > 62)
+        return OR_E_RANGE;
+    int64_t groups = k / 128;
+    for (int64_t r = 0; r < rows; r++) {
+        int64_t acc = 0;
+        for (int64_t g = 0; g < groups; g++) {
+            int64_t sum = 0;
+            for (int64_t i = g * 128; i < g * 128 + 128; i++) {
+                int8_t w = s[r * k + i];
+                if (w != 1 && w != -1)
+                    return OR_E_RANGE;
+                sum += (int64_t)w * (int64_t)x[i];
+            }
+            acc += floor_shift(sum * (int64_t)scale[r * groups + g], frac);
+        }
+        y[r] = acc;
+    }
+    return OR_OK;
+}
+
+/* Packed Q1_0 signs, as the public header of the library declares them: one
+ * bit per weight, 1 for +1 and 0 for -1, tiled like the ternary W_nonzero
+ * plane alone: rows padded to 64; block (tile, g) = 1024 bytes at offset
+ * (tile*G + g)*1024; row 64*tile+j at 16j; weight i of the group is bit
+ * (i%8) of byte (i/8).  Padding rows are zero. */
+int or_q1_pack(const int8_t *s, int64_t rows, int64_t k, uint8_t *bits)
+{
+    if (rows < 0 || k % 128 != 0)
+        return OR_E_SHAPE;
+    int64_t groups = k / 128;
+    memset(bits, 0, (size_t)(or_pad64(rows) * k / 8));
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t i = 0; i < k; i++) {
+            int8_t w = s[r * k + i];
+            if (w != 1 && w != -1)
+                return OR_E_RANGE;
+            if (w == 1) {
+                int64_t g = i / 128, bit = i % 128;
+                bits[((r / 64) * groups + g) * 1024 + 16 * (r % 64) + bit / 8] |=
+                    (uint8_t)(1u << (bit % 8));
+            }
+        }
+    return OR_OK;
+}
+
+/* The page's masked form, read from the packed bits and packed scales:
+ * block_total_g = sum_i x_i over the group (once, shared by every row),
+ * pos_sum = sum of x_i over the set bits, signed_sum = 2 pos_sum -
+ * block_total. */
+int or_q1_gemv_masked(const uint8_t *bits, const int16_t *pscale, const int8_t *x,
+                      int64_t rows, int64_t k, int frac, int64_t *y)
+{
+    if (rows < 0 || k % 128 != 0)
+        return OR_E_SHAPE;
+    if (frac < 0 || frac > 62)
+        return OR_E_RANGE;
+    int64_t groups = k / 128;
+    for (int64_t r = 0; r < rows; r++) {
+        int64_t acc = 0;
+        for (int64_t g = 0; g < groups; g++) {
+            int64_t block_total = 0, pos_sum = 0;
+            const uint8_t *f = bits + ((r / 64) * groups + g) * 1024 + 16 * (r % 64);
+            for (int i = 0; i < 128; i++) {
+                block_total += x[g * 128 + i];
+                if ((f[i / 8] >> (i % 8)) & 1)
+                    pos_sum += x[g * 128 + i];
+            }
+            int64_t sc = pscale[((r / 16) * groups + g) * 16 + r % 16];
+            acc += floor_shift((2 * pos_sum - block_total) * sc, frac);
+        }
+        y[r] = acc;
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* LNS8 eight-phase accumulation ([BS] §3, §3.1, §4, §7 Phase A)              */
 /* ------------------------------------------------------------------------ */
 /*
