@@ -272,6 +272,25 @@ def run_extras(torch, bs, synth, dev, timer):
             "frac_hbm_peak": round(wb / us / 1e3 / HBM_PEAK_GBS, 4)}
         del ps, ss
         log("ternary %dx%d: %.2f us" % (rows, k, us))
+    # Q1_0 (one sign bit per weight): the four launches of a BitNet-2B layer
+    # and the largest K in range
+    q1_bytes = lambda r, k: r * k // 8 + r * (k // 128) * 2
+    for rows, k in [(3840, 2560), (2560, 2560), (13824, 2560), (2560, 6912), (13824, 5120)]:
+        sgn, sc, x = synth.q1(rows, k, 0)
+        b = torch.from_numpy(bs.q1_pack(sgn)).to(dev)
+        s = torch.from_numpy(bs.ternary_pack_scales(sc)).to(dev)
+        n = max(2, -(-(1 << 30) // q1_bytes(rows, k)))
+        bp, sp = [b.clone() for _ in range(n)], [s.clone() for _ in range(n)]
+        xd = torch.from_numpy(x).to(dev)
+        y = torch.empty(rows, dtype=torch.int64, device=dev)
+        us = per_launch_us(timer, lambda i: bs.q1_gemv(bp[i % n], sp[i % n], xd, rows, k,
+                                                       out=y), n=100)
+        wb = q1_bytes(rows, k)
+        ops["q1_gemv_%dx%d" % (rows, k)] = {
+            "us_per_gemv": round(us, 3), "weight_bytes": wb, "GBps": round(wb / us / 1e3, 1),
+            "frac_hbm_peak": round(wb / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del bp, sp
+        log("q1 %dx%d: %.2f us" % (rows, k, us))
     # LNS8 eight-phase GEMV, 4096 x 4096
     t8, x8 = synth.lns8(4096, 4096, 0)
     p8 = torch.from_numpy(bs.ternary_pack(t8)).to(dev)

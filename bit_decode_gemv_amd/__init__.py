@@ -8,8 +8,8 @@ missing, every call raises.
 Names follow the C ABI declared in ``include/bs.h``:
 
 * codec (host, NumPy arrays): ``ternary_pack``, ``ternary_unpack``,
-  ``ternary_pack_scales``, ``planes_pack``;
-* device (torch tensors on a HIP device): ``ternary_gemv``,
+  ``ternary_pack_scales``, ``q1_pack``, ``planes_pack``;
+* device (torch tensors on a HIP device): ``ternary_gemv``, ``q1_gemv``,
   ``lns8_phase_gemv``, ``lmhead_planes_topk``.
 """
 from __future__ import annotations
@@ -48,6 +48,9 @@ def _declare(lib):
         "bs_ternary_unpack": (I32, [P, I64, I64, P]),
         "bs_ternary_pack_scales": (I32, [P, I64, I64, P]),
         "bs_ternary_gemv": (I32, [P, P, P, I64, I64, I32, P, P]),
+        "bs_q1_planes_bytes": (I64, [I64, I64]),
+        "bs_q1_pack": (I32, [P, I64, I64, P]),
+        "bs_q1_gemv": (I32, [P, P, P, I64, I64, I32, P, P]),
         "bs_lns8_workspace_bytes": (SZ, [I64, I64]),
         "bs_lns8_phase_gemv": (I32, [P, P, I64, I64, I32, P, P, P, SZ, P]),
         "bs_planes03_bytes": (I64, [I64, I64]),
@@ -107,6 +110,18 @@ def ternary_pack(t: np.ndarray) -> np.ndarray:
         raise BsError(int(n), "bs_ternary_planes_bytes")
     out = np.empty(n, dtype=np.uint8)
     _check(lib().bs_ternary_pack(_np_ptr(t), rows, k, _np_ptr(out)), "bs_ternary_pack")
+    return out
+
+
+def q1_pack(signs: np.ndarray) -> np.ndarray:
+    """int8 signs [rows][k] in {-1, +1} -> packed sign bits (uint8)."""
+    signs = np.ascontiguousarray(signs, dtype=np.int8)
+    rows, k = signs.shape
+    n = lib().bs_q1_planes_bytes(rows, k)
+    if n < 0:
+        raise BsError(int(n), "bs_q1_planes_bytes")
+    out = np.empty(n, dtype=np.uint8)
+    _check(lib().bs_q1_pack(_np_ptr(signs), rows, k, _np_ptr(out)), "bs_q1_pack")
     return out
 
 
@@ -235,6 +250,25 @@ def ternary_gemv(planes, scales, x, rows: int, k: int, frac: int = 0, out=None,
                                _dptr(out, torch.int64, "y"),
                                _stream_handle(stream, x.device))
     _check(rc, "bs_ternary_gemv")
+    return out
+
+
+def q1_gemv(bits, scales, x, rows: int, k: int, frac: int = 0, out=None, stream=None):
+    """y = bs_q1_gemv(bits, scales, x): int64[rows] on x's device."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(rows, dtype=torch.int64, device=x.device)
+    nbits = lib().bs_q1_planes_bytes(rows, k)
+    if nbits < 0:
+        raise BsError(int(nbits), "bs_q1_planes_bytes")
+    _need(bits, nbits, "bits")
+    _need(scales, lib().bs_ternary_scales_count(rows, k), "scales")
+    _need(x, k, "x")
+    _need(out, rows, "y")
+    rc = lib().bs_q1_gemv(_dptr(bits, torch.uint8, "bits"), _dptr(scales, torch.int16, "scales"),
+                          _dptr(x, torch.int8, "x"), rows, k, frac, _dptr(out, torch.int64, "y"),
+                          _stream_handle(stream, x.device))
+    _check(rc, "bs_q1_gemv")
     return out
 
 

@@ -107,6 +107,31 @@ extern "C" int32_t bs_ternary_pack_scales(const int16_t *scales, int64_t rows, i
     return BS_OK;
 }
 
+extern "C" int64_t bs_q1_planes_bytes(int64_t rows, int64_t k) {
+    int32_t st = codec_shape(rows, k);
+    return st ? st : pad64(rows) * k / 8;
+}
+
+// One sign bit per weight (1 = +1) in the tiled layout of one ternary plane.
+extern "C" int32_t bs_q1_pack(const int8_t *signs, int64_t rows, int64_t k, uint8_t *bits) {
+    if (!signs || !bits) return BS_E_NULL;
+    if (int32_t st = codec_shape(rows, k)) return st;
+    const int64_t G = k / kGroup, R = pad64(rows);
+    memset(bits, 0, (size_t)(R * k / 8));
+    for (int64_t r = 0; r < rows; ++r) {
+        const int8_t *row = signs + r * k;
+        for (int64_t g = 0; g < G; ++g) {
+            uint8_t *f = bits + ((r / kTileRows) * G + g) * 1024 + 16 * (r % kTileRows);
+            for (int i = 0; i < 128; ++i) {
+                const int8_t v = row[g * kGroup + i];
+                if (v == 1) f[i >> 3] |= (uint8_t)(1u << (i & 7));
+                else if (v != -1) return BS_E_RANGE;
+            }
+        }
+    }
+    return BS_OK;
+}
+
 extern "C" int64_t bs_planes03_bytes(int64_t vocab, int64_t dim) {
     int32_t st = codec_shape(vocab, dim);
     return st ? st : pad64(vocab) * dim;

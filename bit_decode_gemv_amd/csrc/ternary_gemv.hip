@@ -22,6 +22,13 @@
 // AND-XOR (v_bitop3) and one popcount.  Slices meet by cross-lane shuffles
 // inside a wavefront and through LDS across wavefronts; integer sums make
 // the result independent of that order (integer-engine page, section 3.2).
+//
+// bs_q1_gemv runs the same kernel on Q1_0 weights (integer-engine page,
+// section 4.1): one sign bit per weight (1 = +1, 0 = -1) in the layout of the
+// ternary W_nonzero plane, signed_sum = 2 * pos_sum - block_total, where
+// block_total (the group's sum of x, shared by every row) is reduced across
+// the group's 16 staging lanes and kept beside the group's bit planes in LDS,
+// and pos_sum = sum_b 2^b popcount(bits & M_b) (-128 for b = 7).
 #include "kcommon.h"
 
 namespace bs {
@@ -66,6 +73,19 @@ __device__ __forceinline__ int group_dot(const uint4 &nz, const uint4 &ng,
     return s;
 }
 
+// Q1_0: 2 * pos_sum - block_total for one group; xg[8].x holds block_total.
+__device__ __forceinline__ int q1_group_dot(const uint4 &bits, const uint4 *__restrict__ xg) {
+    int pos = 0;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const uint4 m = xg[b];
+        const int q = __builtin_popcount(bits.x & m.x) + __builtin_popcount(bits.y & m.y) +
+                      __builtin_popcount(bits.z & m.z) + __builtin_popcount(bits.w & m.w);
+        pos += (b == 7) ? -q * 128 : q * (1 << b);
+    }
+    return 2 * pos - (int)xg[8].x;
+}
+
 // v summed with the lane 16 (SWAP32 false) or 32 (true) apart, in every lane:
 // the gfx950 permlane swaps exchange 16-lane rows (odd rows of one operand
 // with even rows of the other) or 32-lane halves at VALU rate; with both
@@ -98,7 +118,7 @@ __device__ __forceinline__ void wave_lds_fence() {
 // R rows per block, up to MAXG groups per slice in flight per round.  The
 // wavefront's LDS slot holds the planes of its (64/R) * MAXG round groups,
 // local index li = q * (64/R) + (slice within the wavefront).
-template <int R, int MAXG>
+template <int R, int MAXG, bool Q1>
 __global__ void ternary_rows_kernel(const uint8_t *__restrict__ planes,
                                     const int16_t *__restrict__ pscales,
                                     const int8_t *__restrict__ x, int rows, int groups,
@@ -138,8 +158,12 @@ __global__ void ternary_rows_kernel(const uint8_t *__restrict__ planes,
             const int g = slice0 + sl + (r0 + q) * nslices;
             if (live && g < groups) {
                 const size_t blk = (size_t)tile * groups + g;
-                wnz[q] = load_stream16(planes + blk * 2048 + 16 * j);
-                wng[q] = load_stream16(planes + blk * 2048 + 1024 + 16 * j);
+                if constexpr (Q1) {
+                    wnz[q] = load_stream16(planes + blk * 1024 + 16 * j);
+                } else {
+                    wnz[q] = load_stream16(planes + blk * 2048 + 16 * j);
+                    wng[q] = load_stream16(planes + blk * 2048 + 1024 + 16 * j);
+                }
                 sc[q] = pscales[((size_t)(row >> 4) * groups + g) * 16 + (row & 15)];
             }
         }
@@ -148,12 +172,26 @@ __global__ void ternary_rows_kernel(const uint8_t *__restrict__ planes,
             const int task = lane + 64 * p;
             const int li = task >> 4;
             const int g = slice0 + (li % S) + (r0 + li / S) * nslices;
-            if (task < LG * 16 && g < groups) {
+            const bool valid = task < LG * 16 && g < groups;
+            if (valid) {
                 const uint64_t t8 = transpose8x8((uint64_t)act[p].x | ((uint64_t)act[p].y << 32));
                 const int piece = task & 15, d = piece >> 2, o = piece & 3;
 #pragma unroll
                 for (int b = 0; b < 8; ++b)
                     slot8[((li * kPlaneStride + b) * 4 + d) * 4 + o] = (uint8_t)(t8 >> (8 * b));
+            }
+            if constexpr (Q1) {
+                // block_total: the 16 lanes of a group (task & 15 = lane & 15)
+                int sum8 = 0;
+                if (valid) {
+                    const uint64_t raw = (uint64_t)act[p].x | ((uint64_t)act[p].y << 32);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) sum8 += (int)(int8_t)(raw >> (8 * i));
+                }
+#pragma unroll
+                for (int m = 8; m >= 1; m >>= 1) sum8 += __shfl_xor(sum8, m, 16);
+                if (valid && (task & 15) == 0)
+                    reinterpret_cast<int *>(slot + li * kPlaneStride + 8)[0] = sum8;
             }
         }
         wave_lds_fence();
@@ -161,7 +199,10 @@ __global__ void ternary_rows_kernel(const uint8_t *__restrict__ planes,
         for (int q = 0; q < MAXG; ++q) {
             const int g = slice0 + sl + (r0 + q) * nslices;
             if (live && g < groups) {
-                const int s = group_dot(wnz[q], wng[q], slot + (q * S + sl) * kPlaneStride);
+                const uint4 *xg = slot + (q * S + sl) * kPlaneStride;
+                int s;
+                if constexpr (Q1) s = q1_group_dot(wnz[q], xg);
+                else s = group_dot(wnz[q], wng[q], xg);
                 acc += (int64_t)((s * sc[q]) >> shift);   // arithmetic shift = floor
             }
         }
@@ -186,37 +227,39 @@ struct TernaryCfg {
     int maxg;             // groups per slice and round held in registers: 1, 2 or 4
 };
 
-template <int R, int G>
+template <int R, int G, bool Q1>
 static void launch_rg(int waves, hipStream_t st, const uint8_t *planes, const int16_t *scales,
                       const int8_t *x, int rows, int groups, int shift, int64_t *y) {
     const unsigned nblk = (unsigned)((rows + R - 1) / R);
-    hipLaunchKernelGGL((ternary_rows_kernel<R, G>), dim3(nblk), dim3(waves * 64), 0, st, planes,
-                       scales, x, rows, groups, shift, y);
+    hipLaunchKernelGGL((ternary_rows_kernel<R, G, Q1>), dim3(nblk), dim3(waves * 64), 0, st,
+                       planes, scales, x, rows, groups, shift, y);
 }
 
-template <int R>
+template <int R, bool Q1>
 static bool launch_r(int maxg, int waves, hipStream_t st, const uint8_t *planes,
                      const int16_t *scales, const int8_t *x, int rows, int groups, int shift,
                      int64_t *y) {
     switch (maxg) {
-    case 1: launch_rg<R, 1>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
-    case 2: launch_rg<R, 2>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
-    case 4: launch_rg<R, 4>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
+    case 1: launch_rg<R, 1, Q1>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
+    case 2: launch_rg<R, 2, Q1>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
+    case 4: launch_rg<R, 4, Q1>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
     default: return false;
     }
 }
 
+template <bool Q1>
 static int32_t launch_ternary(const TernaryCfg &c, const uint8_t *planes, const int16_t *scales,
                               const int8_t *x, int64_t rows, int64_t k, int32_t frac, int64_t *y,
                               hipStream_t st) {
     if (c.waves < 1 || c.waves > 16) return BS_E_RANGE;
     const int groups = (int)(k / kGroup);
     const int shift = frac > 31 ? 31 : frac;   // |scale*s| < 2^31: shift 31 is floor
+    const int n = (int)rows;
     bool ok;
     switch (c.rows_per_block) {
-    case 64: ok = launch_r<64>(c.maxg, c.waves, st, planes, scales, x, (int)rows, groups, shift, y); break;
-    case 32: ok = launch_r<32>(c.maxg, c.waves, st, planes, scales, x, (int)rows, groups, shift, y); break;
-    case 16: ok = launch_r<16>(c.maxg, c.waves, st, planes, scales, x, (int)rows, groups, shift, y); break;
+    case 64: ok = launch_r<64, Q1>(c.maxg, c.waves, st, planes, scales, x, n, groups, shift, y); break;
+    case 32: ok = launch_r<32, Q1>(c.maxg, c.waves, st, planes, scales, x, n, groups, shift, y); break;
+    case 16: ok = launch_r<16, Q1>(c.maxg, c.waves, st, planes, scales, x, n, groups, shift, y); break;
     default: ok = false;
     }
     if (!ok) return BS_E_RANGE;
@@ -256,15 +299,28 @@ static TernaryCfg choose_cfg(int64_t rows, int64_t k) {
 
 using namespace bs;
 
-extern "C" int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales,
-                                   const int8_t *x, int64_t rows, int64_t k, int32_t frac,
-                                   int64_t *y, void *stream) {
+static int32_t gemv_check(const uint8_t *planes, const int16_t *scales, const int8_t *x,
+                          int64_t rows, int64_t k, int32_t frac, const int64_t *y) {
     if (!planes || !scales || !x || !y) return BS_E_NULL;
     if (int32_t st = check_rows_k(rows, k, (int64_t)1 << 24)) return st;
     if (frac < 0 || frac > 62) return BS_E_RANGE;
     if (((uintptr_t)planes & 15) || ((uintptr_t)scales & 1) || ((uintptr_t)x & 7) ||
         ((uintptr_t)y & 7))
         return BS_E_ALIGN;
-    return launch_ternary(choose_cfg(rows, k), planes, scales, x, rows, k, frac, y,
-                          (hipStream_t)stream);
+    return BS_OK;
+}
+
+extern "C" int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales,
+                                   const int8_t *x, int64_t rows, int64_t k, int32_t frac,
+                                   int64_t *y, void *stream) {
+    if (int32_t st = gemv_check(planes, scales, x, rows, k, frac, y)) return st;
+    return launch_ternary<false>(choose_cfg(rows, k), planes, scales, x, rows, k, frac, y,
+                                 (hipStream_t)stream);
+}
+
+extern "C" int32_t bs_q1_gemv(const uint8_t *bits, const int16_t *scales, const int8_t *x,
+                              int64_t rows, int64_t k, int32_t frac, int64_t *y, void *stream) {
+    if (int32_t st = gemv_check(bits, scales, x, rows, k, frac, y)) return st;
+    return launch_ternary<true>(choose_cfg(rows, k), bits, scales, x, rows, k, frac, y,
+                                (hipStream_t)stream);
 }

@@ -118,6 +118,27 @@ int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales, const int8
                         int64_t rows, int64_t k, int32_t frac, int64_t *y, void *stream);
 
 /* ======================================================================== */
+/* bs_q1_gemv -- Q1_0 weight apply ([IE] section 4.1)                        */
+/* ======================================================================== */
+/*
+ * Weights are signs s in {-1, +1}, one bit each (1 = +1, 0 = -1), packed like
+ * the ternary W_nonzero plane alone: rows padded to R = ceil(rows/64)*64;
+ * block (tile, g) = 1024 bytes at offset (tile*G + g)*1024, row 64*tile+j at
+ * 16j, weight i of the group bit (i%8) of byte (i/8).  R*k/8 bytes.  Scales
+ * use the packed-scale layout of bs_ternary_gemv (bs_ternary_pack_scales).
+ *   y[r] = sum_g floor( scale[r][g] * (2 * pos[r][g] - total[g]) / 2^frac ),
+ *   pos[r][g] = sum of x over the group's positions with s = +1,
+ *   total[g]  = sum of x over the group (shared by every row).
+ * Arguments, alignment, limits and errors as for bs_ternary_gemv.
+ */
+int64_t bs_q1_planes_bytes(int64_t rows, int64_t k);
+/* signs[rows][k] in {-1, +1} (host) -> bits[R*k/8]; any other value gives
+ * BS_E_RANGE. */
+int32_t bs_q1_pack(const int8_t *signs, int64_t rows, int64_t k, uint8_t *bits);
+int32_t bs_q1_gemv(const uint8_t *bits, const int16_t *scales, const int8_t *x, int64_t rows,
+                   int64_t k, int32_t frac, int64_t *y, void *stream);
+
+/* ======================================================================== */
 /* bs_lns8_phase_gemv -- BitState LNS8 eight-phase GEMV ([BS] sections 3-4)  */
 /* ======================================================================== */
 /*

@@ -166,3 +166,28 @@ def test_workspace_sizes_follow_the_launch_plans():
     # lm_head: grows with the vocabulary, not with top_k beyond the bounds
     a = lib.bs_lmhead_workspace_bytes(128256, 2560, 40, 200)
     assert a == lib.bs_lmhead_workspace_bytes(128256, 2560, 200, 200) > 128256 * 40
+
+
+@pytest.mark.parametrize("rows,k,seed", [(1, 128, 0), (64, 256, 1), (65, 384, 2), (130, 2560, 3)])
+def test_q1_codec_matches_oracle_layout(rows, k, seed):
+    s, _, _ = synth.q1(rows, k, seed)
+    assert (bs.q1_pack(s) == oracle.q1_pack(s)).all()
+    assert bs.lib().bs_q1_planes_bytes(rows, k) == -(-rows // 64) * 64 * k // 8
+    bad = s.copy()
+    bad[0, 5] = 0
+    with pytest.raises(bs.BsError) as e:
+        bs.q1_pack(bad)
+    assert e.value.status == bs.BS_E_RANGE
+
+
+def _q1(bits=FAKE, scales=FAKE, x=FAKE, rows=64, k=256, frac=0, y=FAKE):
+    return bs.lib().bs_q1_gemv(bits, scales, x, rows, k, frac, y, None)
+
+
+def test_q1_gemv_validation():
+    assert _q1(bits=None) == bs.BS_E_NULL
+    assert _q1(k=100) == bs.BS_E_SHAPE
+    assert _q1(frac=63) == bs.BS_E_RANGE
+    assert _q1(k=(1 << 24) + 128) == bs.BS_E_OVERFLOW
+    assert _q1(bits=ctypes.c_void_p((1 << 20) + 8)) == bs.BS_E_ALIGN
+    assert _q1(x=ctypes.c_void_p((1 << 20) + 4)) == bs.BS_E_ALIGN
