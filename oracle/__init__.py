@@ -14,6 +14,9 @@ are written here in pure Python with integers and ``fractions``:
   rounded by the same integer method, but from the code's own exponent;
 * ``lns8_materialize`` -- S = 2^-9 * sum_p A[p]*F[p] of section 3.1, the
   exact rational sum over the binary64 F values, rounded once.
+
+The pure fractional-LNS reduction of section 5.2 lives in ``flns_oracle.c``;
+its tables are evaluated in binary128 (libquadmath) and rounded to nearest.
 """
 from __future__ import annotations
 
@@ -26,16 +29,18 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "bs_oracle.c")
+_SRC_FLNS = os.path.join(_HERE, "flns_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile the C oracle with gcc (-O2, no intrinsics) into liboracle.so."""
+    """Compile the C oracle with gcc (-O2, no intrinsics) into liboracle.so.
+    flns_oracle.c uses GCC's binary128 (libquadmath), hence gnu11."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared",
-                               "-fPIC", _SRC, "-o", tmp, "-lm"])
+        subprocess.check_call(["gcc", "-O2", "-std=gnu11", "-Wall", "-Wextra", "-shared",
+                               "-fPIC", _SRC, _SRC_FLNS, "-o", tmp, "-lquadmath", "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -43,15 +48,17 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or (
-                os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
+                os.path.getmtime(_SRC), os.path.getmtime(_SRC_FLNS)):
             build(force=True)
         lib = ctypes.CDLL(_LIB_PATH)
         for name in ("or_ternary_gemv_def", "or_ternary_pack", "or_scales_pack",
                      "or_ternary_unpack", "or_ternary_gemv_masked", "or_lns8_direct",
                      "or_lns8_tile64", "or_lns8_popcount", "or_lns8_fp64_dot",
                      "or_lmhead_brute", "or_lmhead_two_stage", "or_lmhead_stage1",
-                     "or_planes_pack", "or_q1_gemv_def", "or_q1_pack", "or_q1_gemv_masked"):
+                     "or_planes_pack", "or_q1_gemv_def", "or_q1_pack", "or_q1_gemv_masked",
+                     "or_flns_tables", "or_flns_log_scale", "or_flns_add", "or_flns_tree",
+                     "or_flns_gemv"):
             getattr(lib, name).restype = ctypes.c_int
         lib.or_pad64.restype = ctypes.c_int64
         lib.or_pad64.argtypes = [ctypes.c_int64]
@@ -323,3 +330,90 @@ def lmhead_stage1(trits, row_scale, h):
     _check(_load().or_lmhead_stage1(_p(trits), _p(row_scale), _p(h), _i64(V), _i64(K),
                                     _p(s1), _p(b)), "lmhead_stage1")
     return s1, b
+
+
+# --------------------------------------------------------------------------
+# Pure fractional-LNS reduction (BitState/HSDR brief v0.5, section 5.2 and
+# section 7 Phase A); the C side documents the coordinates and the order.
+# --------------------------------------------------------------------------
+
+_flns_cache = {}
+
+
+def flns_tables(f: int) -> dict:
+    """The fold and pair-add tables for f fractional bits, built in
+    binary128: {"lc": int32[129], "kp": int32[n_kp], "km": int32[n_km]
+    (km[0] unused), "N": 8*2^f, "margin": least distance of an entry from a
+    rounding tie}."""
+    if f not in _flns_cache:
+        N = 8 << f
+        cap = N * (f + 8)
+        lc = np.zeros(129, dtype=np.int32)
+        kp = np.zeros(cap, dtype=np.int32)
+        km = np.zeros(cap, dtype=np.int32)
+        n_kp = ctypes.c_int64(0)
+        n_km = ctypes.c_int64(0)
+        margin = ctypes.c_double(0)
+        _check(_load().or_flns_tables(ctypes.c_int(f), _p(lc), _p(kp), _i64(cap),
+                                      ctypes.byref(n_kp), _p(km), ctypes.byref(n_km),
+                                      ctypes.byref(margin)), "flns_tables")
+        _flns_cache[f] = {"lc": lc, "kp": kp[:n_kp.value].copy(), "km": km[:n_km.value].copy(),
+                          "N": N, "margin": margin.value}
+    return _flns_cache[f]
+
+
+def _flns_tab_args(f: int):
+    tb = flns_tables(f)
+    kp = tb["kp"] if tb["kp"].size else np.zeros(1, dtype=np.int32)
+    km = tb["km"] if tb["km"].size else np.zeros(1, dtype=np.int32)
+    return (_p(kp), _i64(tb["kp"].size), _p(km), _i64(tb["km"].size))
+
+
+def flns_log_scale(f: int, d: int) -> int:
+    """round(8*2^f * log2 d): the log-domain offset of the shared scale d."""
+    out = ctypes.c_int64(0)
+    _check(_load().or_flns_log_scale(ctypes.c_int(f), ctypes.c_uint32(d), ctypes.byref(out)),
+           "flns_log_scale")
+    return out.value
+
+
+def flns_add(f: int, a, b):
+    """One pair add of (sign, coordinate) values (sign -1/0/+1)."""
+    so = ctypes.c_int(0)
+    lo = ctypes.c_int64(0)
+    _check(_load().or_flns_add(*_flns_tab_args(f), ctypes.c_int(a[0]), _i64(a[1]),
+                               ctypes.c_int(b[0]), _i64(b[1]), ctypes.byref(so),
+                               ctypes.byref(lo)), "flns_add")
+    return so.value, lo.value
+
+
+def flns_tree(f: int, signs, lams):
+    """The balanced pairwise reduction of explicit leaves."""
+    signs = np.ascontiguousarray(signs, dtype=np.intc)
+    lams = np.ascontiguousarray(lams, dtype=np.int64)
+    so = ctypes.c_int(0)
+    lo = ctypes.c_int64(0)
+    _check(_load().or_flns_tree(*_flns_tab_args(f), _p(signs), _p(lams), _i64(signs.size),
+                                ctypes.byref(so), ctypes.byref(lo)), "flns_tree")
+    return so.value, lo.value
+
+
+def flns_gemv(t, x, f: int, scale_d: int = 1) -> np.ndarray:
+    """The whole pure-LNS row reduction: int32 out[rows][2] = (sign, L)."""
+    t = np.ascontiguousarray(t, dtype=np.int8)
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    rows, k = t.shape
+    tb = flns_tables(f)
+    out = np.zeros((rows, 2), dtype=np.int32)
+    _check(_load().or_flns_gemv(_p(t), _p(x), _i64(rows), _i64(k), ctypes.c_int(f),
+                                ctypes.c_uint32(scale_d), _p(tb["lc"]), *_flns_tab_args(f),
+                                _p(out)), "flns_gemv")
+    return out
+
+
+def flns_value(out: np.ndarray, f: int) -> np.ndarray:
+    """binary64 magnitude of (sign, L) results: sign * 2^((L/2^f - 74)/8).
+    For error measurement only (libm exp2)."""
+    out = np.asarray(out)
+    lam = out[:, 1].astype(np.float64) / float(1 << f)
+    return out[:, 0].astype(np.float64) * np.exp2((lam - 74.0) / 8.0)
