@@ -8,9 +8,9 @@ missing, every call raises.
 Names follow the C ABI declared in ``include/bs.h``:
 
 * codec (host, NumPy arrays): ``ternary_pack``, ``ternary_unpack``,
-  ``ternary_pack_scales``, ``q1_pack``, ``planes_pack``;
+  ``ternary_pack_scales``, ``q1_pack``, ``planes_pack``, ``flns_table``;
 * device (torch tensors on a HIP device): ``ternary_gemv``, ``q1_gemv``,
-  ``lns8_phase_gemv``, ``lmhead_planes_topk``.
+  ``lns8_phase_gemv``, ``flns_phase_gemv``, ``lmhead_planes_topk``.
 """
 from __future__ import annotations
 
@@ -53,6 +53,10 @@ def _declare(lib):
         "bs_q1_gemv": (I32, [P, P, P, I64, I64, I32, P, P]),
         "bs_lns8_workspace_bytes": (SZ, [I64, I64]),
         "bs_lns8_phase_gemv": (I32, [P, P, I64, I64, I32, P, P, P, SZ, P]),
+        "bs_flns_table_bytes": (I64, [I32]),
+        "bs_flns_table_build": (I32, [I32, P, I64]),
+        "bs_flns_workspace_bytes": (SZ, [I64, I64]),
+        "bs_flns_phase_gemv": (I32, [P, P, I64, I64, I32, ctypes.c_uint32, P, I64, P, P, SZ, P]),
         "bs_planes03_bytes": (I64, [I64, I64]),
         "bs_planes47_bytes": (I64, [I64, I64]),
         "bs_planes_pack": (I32, [P, I64, I64, P, P]),
@@ -165,6 +169,17 @@ def planes_pack(trits: np.ndarray):
     _check(lib().bs_planes_pack(_np_ptr(trits), vocab, dim, _np_ptr(p03), _np_ptr(p47)),
            "bs_planes_pack")
     return p03, p47
+
+
+def flns_table(frac_bits: int) -> np.ndarray:
+    """The pure fractional-LNS table blob for frac_bits (host uint8); copy it
+    to the device as is for ``flns_phase_gemv``."""
+    n = lib().bs_flns_table_bytes(int(frac_bits))
+    if n <= 0:
+        raise BsError(BS_E_RANGE, "bs_flns_table_bytes")
+    blob = np.zeros(n, dtype=np.uint8)
+    _check(lib().bs_flns_table_build(int(frac_bits), _np_ptr(blob), n), "bs_flns_table_build")
+    return blob
 
 
 # ------------------------------------------------------------------ device
@@ -298,6 +313,30 @@ def lns8_phase_gemv(planes, x_lns8, rows: int, k: int, path: int = LNS8_DIRECT, 
                                   wp, wn, _stream_handle(stream, dev))
     _check(rc, "bs_lns8_phase_gemv")
     return acc, s
+
+
+def flns_phase_gemv(planes, x_lns8, rows: int, k: int, frac_bits: int, table, scale_d: int = 1,
+                    out=None, workspace=None, stream=None):
+    """out int32[rows][2] = (sign, L) of the pure fractional-LNS reduction;
+    ``table`` is the device copy of ``flns_table(frac_bits)``."""
+    torch = _torch()
+    dev = x_lns8.device
+    if out is None:
+        out = torch.empty((rows, 2), dtype=torch.int32, device=dev)
+    need = lib().bs_flns_workspace_bytes(rows, k)
+    if need == 0:
+        raise BsError(BS_E_SHAPE, "bs_flns_workspace_bytes")
+    _need(planes, lib().bs_ternary_planes_bytes(rows, k), "planes")
+    _need(x_lns8, k, "x_lns8")
+    _need(out, rows * 2, "out")
+    wp, wn = _ws("flns_phase_gemv", workspace, need, dev)
+    rc = lib().bs_flns_phase_gemv(_dptr(planes, torch.uint8, "planes"),
+                                  _dptr(x_lns8, torch.uint8, "x_lns8"), rows, k, int(frac_bits),
+                                  int(scale_d), _dptr(table, torch.uint8, "table"),
+                                  table.numel(), _dptr(out, torch.int32, "out"), wp, wn,
+                                  _stream_handle(stream, dev))
+    _check(rc, "bs_flns_phase_gemv")
+    return out
 
 
 def lmhead_planes_topk(planes03, planes47, row_scale, h, vocab: int, dim: int,

@@ -182,6 +182,71 @@ int32_t bs_lns8_phase_gemv(const uint8_t *planes, const uint8_t *x_lns8, int64_t
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /* ======================================================================== */
+/* bs_flns_phase_gemv -- pure fractional-LNS reduction ([BS] section 5.2)    */
+/* ======================================================================== */
+/*
+ * The same products as bs_lns8_phase_gemv (ternary planes x LNS8 bytes),
+ * reduced without a linear accumulator ([BS] section 5.2, section 7 Phase A):
+ *
+ * Coordinates.  Code k stands for 2^((k-74)/8).  The internal coordinate
+ * keeps frac_bits = f fractional bits of a code unit: the integer L stands
+ * for 2^((L/2^f - 74)/8), N = 8*2^f units per octave.  A value is zero or
+ * (sign, L).
+ * Steps, per row:
+ *   1. per Tile128 j (positions 128j..128j+127, = group j) and code c, the
+ *      signed state population C_j[c] = sum of (-1)^(S1 xor [t < 0]) over the
+ *      positions with code c and t != 0 (|C| <= 128);
+ *   2. fold: C != 0 becomes (sign C, c*2^f + round(N*log2|C|));
+ *   3. per phase p, the leaves (j, band b), c = 8b + p, at index 16j + b
+ *      (zero where C = 0) reduce by a balanced pairwise tree (element m of
+ *      a level is the sum of elements 2m and 2m+1 of the level below, an
+ *      unpaired last element moves up unchanged); every sum is the pair
+ *      add of [BS] section 5.2: with a the operand of larger L and
+ *      D = L_a - L_b, same signs give L_a + round(N*log2(1 + 2^(-D/N))),
+ *      opposite signs give exact zero for D = 0, else
+ *      L_a + round(N*log2(1 - 2^(-D/N))); the sign is a's; zero is the
+ *      identity;
+ *   4. the eight phase results reduce by the same tree (8 -> 4 -> 2 -> 1);
+ *   5. a non-zero result adds round(N*log2 d) for the shared scale d.
+ * Each rounding is to the nearest integer; none of the rounded real values
+ * is a tie.  The corrections come from tables built on the host
+ * (bs_flns_table_build) and copied to the device by the caller.
+ *
+ *   planes, x_lns8, rows, k  as bs_lns8_phase_gemv (k <= 65408)
+ *   frac_bits  f, 0..BS_FLNS_MAX_FRAC
+ *   scale_d    shared positive scale d >= 1 (1 = none)
+ *   table      device copy of the blob from bs_flns_table_build(frac_bits),
+ *              16-byte aligned; table_bytes = bs_flns_table_bytes(frac_bits)
+ *              (the size identifies f: a table for another f is rejected)
+ *   out        device int32[rows][2], 8-byte aligned: (sign, L) per row,
+ *              sign -1 / 0 / +1, L = 0 when the result is zero
+ *   workspace  device scratch of bs_flns_workspace_bytes(rows, k) bytes,
+ *              256-byte aligned, caller-owned, no initialisation needed;
+ *              calls that may overlap need separate workspaces
+ * Errors: BS_E_NULL, BS_E_SHAPE, BS_E_OVERFLOW (k), BS_E_RANGE (frac_bits,
+ *   scale_d = 0, table_bytes not that of frac_bits), BS_E_ALIGN,
+ *   BS_E_WORKSPACE, BS_E_HIP.
+ */
+#define BS_FLNS_MAX_FRAC 12
+
+/* Bytes of the table blob for frac_bits, or 0 when frac_bits is outside
+ * 0..BS_FLNS_MAX_FRAC.  Host only. */
+int64_t bs_flns_table_bytes(int32_t frac_bits);
+
+/* Fill the blob in host memory: the fold table round(N*log2 n), n = 1..128,
+ * and the pair-add corrections round(N*log2(1 +- 2^(-D/N))) up to the first
+ * D where they round to 0.  Host only, synchronous.  Errors: BS_E_NULL,
+ * BS_E_RANGE (frac_bits; an entry this host cannot round unambiguously),
+ * BS_E_SHAPE (table_bytes != bs_flns_table_bytes(frac_bits)). */
+int32_t bs_flns_table_build(int32_t frac_bits, void *table, int64_t table_bytes);
+
+size_t bs_flns_workspace_bytes(int64_t rows, int64_t k);
+int32_t bs_flns_phase_gemv(const uint8_t *planes, const uint8_t *x_lns8, int64_t rows,
+                           int64_t k, int32_t frac_bits, uint32_t scale_d, const void *table,
+                           int64_t table_bytes, int32_t *out, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* ======================================================================== */
 /* BITNET_PLANES lm_head ([T2])                                              */
 /* ======================================================================== */
 /*
