@@ -211,8 +211,7 @@ def _stream_handle(stream, device):
 
 class Workspace:
     """Zero-filled device scratch, one per (entry point, device), grown on
-    demand.  The LNS8 entry point leaves its bookkeeping zero again before it
-    returns and the lm_head one writes every workspace byte before reading it,
+    demand.  Every entry point writes each workspace byte before reading it,
     so one buffer serves every call of that entry point ordered on one
     stream; entry points never share a buffer."""
 

@@ -4,14 +4,16 @@
 // cancellation, balanced trees, the log-domain scale).
 //
 // Values.  In registers a log-domain value is one int32, e = 2*L + s (s = 1
-// for a negative value), and INT32_MIN stands for zero.  The pair add sorts
-// by L, looks up one correction (same-sign table, or opposite-sign table
-// behind it) and adds it to L; the sign bit rides along.  L stays far inside
-// +-2^29: at most 2^f (127 + 8 log2 K + 8 log2 d) above, and each of at most
-// 16 tree levels can lower it by |km[1]| < 2^(f+4) below.
+// for a negative value); zero is a coordinate far below every real one (see
+// kZ).  The pair add sorts by L, looks up one correction (same-sign table,
+// or opposite-sign table behind it) and adds it to L; the sign bit rides
+// along.  For f <= 12 a real L stays inside (-2^24, 2^22): at most
+// 2^f (127 + 8 log2 K + 8 log2 d) above, and each of at most 16 tree levels
+// can lower it by |km[1]| ~ N (log2 N + 0.53) < 2^(f+7) below.
 //
-// Mapping.  Kernel A: a workgroup of eight wavefronts per (64-row tile, run
-// of eight Tile128s); lane j of every wavefront is row 64*tile + j, so the
+// Mapping.  Kernel A: a workgroup of sixteen wavefronts per (64-row tile, run
+// of eight Tile128s), two per Tile128 with four phases each; lane j of every
+// wavefront is row 64*tile + j, so the
 // activation bytes of a Tile128 are uniform across the wavefront.  Per code
 // c the two 64-position halves are selected by ballots (scalar masks); the
 // signed population of each row is popcount(mask & positive products) -
@@ -22,10 +24,14 @@
 // LDS.  With more than eight Tile128s, each workgroup writes its eight phase
 // partials per row to the workspace and kernel B (lanes = workgroups of one
 // row, shuffles) finishes the tile tree, then the phase tree and the scale.
-// The kernel boundary makes the partials visible across XCDs.
+// The kernel boundary makes the partials visible across XCDs (a last-arrival
+// reduction inside kernel A, with agent-scope fences, measured 3-4x slower:
+// the L2 write-backs cost more than a second launch).
 //
 // Tables.  For frac_bits <= 8 the corrections are int16 and staged in LDS
-// (at most 102,640 bytes); above, they are read from the device blob.
+// (at most 102,656 bytes); above, they are read from the
+// device blob.  Table reads never sit behind a branch: an index past the
+// table reads slot 0 and the value is discarded, so reads overlap.
 #include <limits.h>
 
 #include <type_traits>
@@ -36,25 +42,65 @@
 namespace bs {
 namespace {
 
-constexpr int kZ = INT_MIN;   // encoded zero
+// Zero is the coordinate -2^29 with sign +: every real L lies above -2^24
+// (the bound above), so against a real operand D exceeds every table and
+// the pair add returns the real operand unchanged, as the identity must.
+// Sums of zeros stay below -2^28 (at most +N per tree level), which is how
+// a result is recognised as zero at the end; only exact cancellation
+// creates a new zero.
+constexpr int kZ = -(1 << 30);
+constexpr int kZeroBelow = -(1 << 29);   // encoded values below this are zero
 constexpr int kTilesPerWg = 8;
+constexpr int kWavesPerWg = 16;   // two per Tile128, four phases each
 
-// The pair add of two encoded values (zero = identity).  Symmetric in a, b.
+// The pair add of two encoded values.  Symmetric in a, b.  On encoded
+// values max() picks the operand of larger L (equal L: equal values, or a
+// cancelling pair), and (hi|1) - (lo|1) = 2D whatever the signs.  The
+// tables are two runs of S entries (same sign, then opposite sign) whose
+// last slots are zero, so clamping D to S - 1 replaces the range test, and
+// the byte offset of entry D of 2-byte entries is 2D itself.  a ^ b == 1
+// is equal L with opposite signs: exact cancellation.  Every conditional
+// selects between named values, so nothing is emitted as a branch and the
+// table read stays in flight.
 template <typename E>
-__device__ __forceinline__ int lns_add(int a, int b, const E *__restrict__ lut, int nkp,
-                                       int nkm) {
-    const int la = a >> 1, lb = b >> 1;
-    const bool a_hi = la >= lb;
-    const int hi = a_hi ? a : b;
-    const int d = a_hi ? la - lb : lb - la;
-    const bool same = ((a ^ b) & 1) == 0;
-    const bool in = same ? d < nkp : d < nkm;
-    const int corr = in ? (int)lut[same ? d : nkp + d] : 0;
-    int out = hi + 2 * corr;
-    out = (!same && d == 0) ? kZ : out;
-    out = a == kZ ? b : out;
-    out = b == kZ ? a : out;
-    return out;
+__device__ __forceinline__ int lns_add(int a, int b, const E *__restrict__ lut, int S) {
+    const int hi = max(a, b), lo = min(a, b);
+    const int x = a ^ b;
+    const int d2 = (hi | 1) - (lo | 1);
+    const int d2c = min(d2, 2 * S - 2);
+    const int run = __mul24(x & 1, 2 * S);
+    const int byte = (d2c + run) * (int)(sizeof(E) / 2);
+    const int corr = (int)*reinterpret_cast<const E *>(reinterpret_cast<const char *>(lut) + byte);
+    const int sum = hi + 2 * corr;
+    return x == 1 ? kZ : sum;
+}
+
+// Stage n 16-byte words of the table into LDS with every load of a thread
+// issued before its first store.
+__device__ __forceinline__ void stage16(uint4 *__restrict__ dst, const uint4 *__restrict__ src,
+                                        int n) {
+    const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
+    u32x4 *d4 = reinterpret_cast<u32x4 *>(dst);
+    for (int base = threadIdx.x; base < n; base += 8 * blockDim.x) {
+        u32x4 t0 = {}, t1 = {}, t2 = {}, t3 = {}, t4 = {}, t5 = {}, t6 = {}, t7 = {};
+        const int st = blockDim.x;
+        if (base < n) t0 = s4[base];
+        if (base + st < n) t1 = s4[base + st];
+        if (base + 2 * st < n) t2 = s4[base + 2 * st];
+        if (base + 3 * st < n) t3 = s4[base + 3 * st];
+        if (base + 4 * st < n) t4 = s4[base + 4 * st];
+        if (base + 5 * st < n) t5 = s4[base + 5 * st];
+        if (base + 6 * st < n) t6 = s4[base + 6 * st];
+        if (base + 7 * st < n) t7 = s4[base + 7 * st];
+        if (base < n) d4[base] = t0;
+        if (base + st < n) d4[base + st] = t1;
+        if (base + 2 * st < n) d4[base + 2 * st] = t2;
+        if (base + 3 * st < n) d4[base + 3 * st] = t3;
+        if (base + 4 * st < n) d4[base + 4 * st] = t4;
+        if (base + 5 * st < n) d4[base + 5 * st] = t5;
+        if (base + 6 * st < n) d4[base + 6 * st] = t6;
+        if (base + 7 * st < n) d4[base + 7 * st] = t7;
+    }
 }
 
 // A tree node: its per-lane value and whether any leaf below it is live
@@ -65,11 +111,10 @@ struct Node {
 };
 
 template <typename E>
-__device__ __forceinline__ Node join(Node a, Node b, const E *__restrict__ lut, int nkp,
-                                     int nkm) {
+__device__ __forceinline__ Node join(Node a, Node b, const E *__restrict__ lut, int S) {
     if (!b.live) return a;
     if (!a.live) return b;
-    return Node{lns_add(a.e, b.e, lut, nkp, nkm), true};
+    return Node{lns_add(a.e, b.e, lut, S), true};
 }
 
 // Per-lane state of one Tile128: the two activation codes each lane holds
@@ -80,74 +125,81 @@ struct TileState {
     uint64_t pos0, neg0, pos1, neg1;
 };
 
-// Leaf of code c: the folded signed population, or dead when no position
-// of the tile has code c.
-__device__ __forceinline__ Node leaf(int c, int f, const TileState &ts,
-                                     const int32_t *__restrict__ fold) {
+// Signed population of code c in the wavefront's Tile128 (per lane = row);
+// the caller has checked that the tile holds code c.
+__device__ __forceinline__ int population(int c, const TileState &ts) {
     const uint64_t m0 = __ballot(ts.code0 == c);
     const uint64_t m1 = __ballot(ts.code1 == c);
-    if ((m0 | m1) == 0) return Node{kZ, false};
-    const int cnt = __popcll(m0 & ts.pos0) - __popcll(m0 & ts.neg0) + __popcll(m1 & ts.pos1) -
-                    __popcll(m1 & ts.neg1);
-    const int n = cnt < 0 ? -cnt : cnt;
-    const int e = cnt == 0 ? kZ : 2 * ((c << f) + fold[n]) + (cnt < 0 ? 1 : 0);
-    return Node{e, true};
+    return __popcll(m0 & ts.pos0) - __popcll(m0 & ts.neg0) + __popcll(m1 & ts.pos1) -
+           __popcll(m1 & ts.neg1);
 }
 
 // Final encoding: scale, then (sign, L).
 __device__ __forceinline__ int2 finish(int e, int ld) {
-    if (e == kZ) return make_int2(0, 0);
+    if (e < kZeroBelow) return make_int2(0, 0);
     e += 2 * ld;
     return make_int2((e & 1) ? -1 : 1, e >> 1);
 }
 
 // The 8 -> 4 -> 2 -> 1 tree over the phase results.
 template <typename E>
-__device__ __forceinline__ int phase_tree(const int v[8], const E *__restrict__ lut, int nkp,
-                                          int nkm) {
-    const int a = lns_add(lns_add(v[0], v[1], lut, nkp, nkm), lns_add(v[2], v[3], lut, nkp, nkm),
-                          lut, nkp, nkm);
-    const int b = lns_add(lns_add(v[4], v[5], lut, nkp, nkm), lns_add(v[6], v[7], lut, nkp, nkm),
-                          lut, nkp, nkm);
-    return lns_add(a, b, lut, nkp, nkm);
+__device__ __forceinline__ int phase_tree(const int v[8], const E *__restrict__ lut, int S) {
+    const int a = lns_add(lns_add(v[0], v[1], lut, S), lns_add(v[2], v[3], lut, S), lut, S);
+    const int b = lns_add(lns_add(v[4], v[5], lut, S), lns_add(v[6], v[7], lut, S), lut, S);
+    return lns_add(a, b, lut, S);
 }
 
 template <bool SMALL>
 using LutT = typename std::conditional<SMALL, int16_t, int32_t>::type;
 
 template <bool SMALL>
-__global__ __launch_bounds__(512) void flns_tile_kernel(
+__global__ __launch_bounds__(1024) void flns_tile_kernel(
     const uint8_t *__restrict__ planes, const uint8_t *__restrict__ x, int rows, int groups,
-    int f, const uint8_t *__restrict__ table, int nkp, int nkm, int ld, int nsplit,
+    int f, const uint8_t *__restrict__ table, int S, int ld, int nsplit,
     int32_t *__restrict__ out, int *__restrict__ partial) {
     using E = LutT<SMALL>;
-    __shared__ int32_t s_fold[kFlnsFoldSlots];
-    __shared__ uint4 s_lut4[SMALL ? (kFlnsSmallMaxEntries * 2 + 15) / 16 : 1];
+    __shared__ int32_t s_fold[kFlnsFoldSlots];   // entries 0..128 (|cnt| <= 128)
+    __shared__ uint4 s_lut4[SMALL ? kFlnsSmallMaxEntries * 2 / 16 : 1];
     __shared__ int s_x[kTilesPerWg][8][64];
+    __shared__ uint32_t s_present[kTilesPerWg][4];   // codes present in each Tile128
 
     const int rtile = blockIdx.x / nsplit;
     const int q = blockIdx.x - rtile * nsplit;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
+    const int slot = wave & (kTilesPerWg - 1), half = wave >> 3;
+    const int j = q * kTilesPerWg + slot;   // Tile128 = 128-weight group j
+    const bool has_tile = j < groups;       // uniform
 
+    if (threadIdx.x < kTilesPerWg * 4) s_present[threadIdx.x >> 2][threadIdx.x & 3] = 0;
+    uint4 nz = make_uint4(0, 0, 0, 0), ng = nz;
+    int b0 = 0, b1 = 0;
+    if (has_tile) {
+        const size_t blk = (size_t)rtile * groups + j;
+        nz = *reinterpret_cast<const uint4 *>(planes + blk * 2048 + 16 * lane);
+        ng = *reinterpret_cast<const uint4 *>(planes + blk * 2048 + 1024 + 16 * lane);
+        b0 = x[(size_t)j * 128 + lane];
+        b1 = x[(size_t)j * 128 + 64 + lane];
+    }
     const int32_t *g_fold = reinterpret_cast<const int32_t *>(table + kFlnsHdrBytes);
     for (int i = threadIdx.x; i < kFlnsFoldSlots; i += blockDim.x) s_fold[i] = g_fold[i];
-    if constexpr (SMALL) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(table + kFlnsCorrOff);
-        const int n16 = ((nkp + nkm) * 2 + 15) / 16;
-        for (int i = threadIdx.x; i < n16; i += blockDim.x) s_lut4[i] = src[i];
+    if constexpr (SMALL)
+        stage16(s_lut4, reinterpret_cast<const uint4 *>(table + kFlnsCorrOff), (2 * S * 2 + 15) / 16);
+    __syncthreads();
+    // the set of codes in each Tile128, once for all the rows of the tile
+    if (has_tile && half == 0) {
+        const int c0 = b0 & 0x7F, c1 = b1 & 0x7F;
+        if (c0) atomicOr(&s_present[slot][c0 >> 5], 1u << (c0 & 31));
+        if (c1) atomicOr(&s_present[slot][c1 >> 5], 1u << (c1 & 31));
     }
     __syncthreads();
     const E *lut = SMALL ? reinterpret_cast<const E *>(s_lut4)
                          : reinterpret_cast<const E *>(table + kFlnsCorrOff);
 
-    const int j = q * kTilesPerWg + wave;   // Tile128 = 128-weight group j
-    if (j < groups) {
-        const size_t blk = (size_t)rtile * groups + j;
-        const uint4 nz = *reinterpret_cast<const uint4 *>(planes + blk * 2048 + 16 * lane);
-        const uint4 ng = *reinterpret_cast<const uint4 *>(planes + blk * 2048 + 1024 + 16 * lane);
-        const int b0 = x[(size_t)j * 128 + lane];
-        const int b1 = x[(size_t)j * 128 + 64 + lane];
+    if (has_tile) {
+        uint32_t pres[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pres[w] = __builtin_amdgcn_readfirstlane(s_present[slot][w]);
         const uint64_t s0 = __ballot(b0 >> 7), s1 = __ballot(b1 >> 7);
         const uint64_t nz0 = (uint64_t)nz.x | ((uint64_t)nz.y << 32);
         const uint64_t nz1 = (uint64_t)nz.z | ((uint64_t)nz.w << 32);
@@ -162,47 +214,72 @@ __global__ __launch_bounds__(512) void flns_tile_kernel(
         ts.neg1 = nz1 & (s1 ^ ng1);
         ts.pos1 = nz1 & ~(s1 ^ ng1);
 #pragma unroll 1
-        for (int p = 0; p < 8; ++p) {
-            Node v[16];
-            v[0] = p == 0 ? Node{kZ, false} : leaf(p, f, ts, s_fold);   // code 0 is zero
+        for (int p = 4 * half; p < 4 * half + 4; ++p) {
+            // the bands present in the tile (code 8b + p; code 0 is never
+            // present), their populations, their fold reads back to back,
+            // then the leaves
+            uint32_t live = 0;   // uniform
 #pragma unroll
-            for (int b = 1; b < 16; ++b) v[b] = leaf(8 * b + p, f, ts, s_fold);
+            for (int b = 0; b < 16; ++b)
+                live |= ((pres[b >> 2] >> (8 * (b & 3) + p)) & 1u) << b;
+            int cnt[16];
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+                cnt[b] = 0;
+                if ((live >> b) & 1) cnt[b] = population(8 * b + p, ts);
+            }
+            int fv[16];
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+                fv[b] = 0;
+                if ((live >> b) & 1) fv[b] = s_fold[abs(cnt[b])];
+            }
+            Node v[16];
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+                v[b] = Node{kZ, ((live >> b) & 1) != 0};
+                if (v[b].live) {
+                    const int neg = cnt[b] < 0 ? 1 : 0;
+                    const int val = 2 * (((8 * b + p) << f) + fv[b]) + neg;
+                    v[b].e = cnt[b] == 0 ? kZ : val;
+                }
+            }
 #pragma unroll
             for (int w = 8; w >= 1; w >>= 1)
 #pragma unroll
-                for (int m = 0; m < w; ++m) v[m] = join(v[2 * m], v[2 * m + 1], lut, nkp, nkm);
-            s_x[wave][p][lane] = v[0].live ? v[0].e : kZ;
+                for (int m = 0; m < w; ++m) v[m] = join(v[2 * m], v[2 * m + 1], lut, S);
+            s_x[slot][p][lane] = v[0].live ? v[0].e : kZ;
         }
     } else {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) s_x[wave][p][lane] = kZ;
+        for (int p = 4 * half; p < 4 * half + 4; ++p) s_x[slot][p][lane] = kZ;
     }
     __syncthreads();
 
-    // The workgroup's eight Tile128s per (phase, row): thread t takes phase
-    // t / 64 of row t % 64.
+    // The workgroup's eight Tile128s per (phase, row): thread t < 512 takes
+    // phase t / 64 of row t % 64.
     const int p = threadIdx.x >> 6;
-    int v[kTilesPerWg];
-#pragma unroll
-    for (int w = 0; w < kTilesPerWg; ++w) v[w] = s_x[w][p][lane];
-    const int r = lns_add(
-        lns_add(lns_add(v[0], v[1], lut, nkp, nkm), lns_add(v[2], v[3], lut, nkp, nkm), lut, nkp,
-                nkm),
-        lns_add(lns_add(v[4], v[5], lut, nkp, nkm), lns_add(v[6], v[7], lut, nkp, nkm), lut, nkp,
-                nkm),
-        lut, nkp, nkm);
     const int row = rtile * 64 + lane;
+    int r = kZ;
+    if (threadIdx.x < 512) {
+        int v[kTilesPerWg];
+#pragma unroll
+        for (int w = 0; w < kTilesPerWg; ++w) v[w] = s_x[w][p][lane];
+        r = lns_add(lns_add(lns_add(v[0], v[1], lut, S), lns_add(v[2], v[3], lut, S), lut, S),
+                    lns_add(lns_add(v[4], v[5], lut, S), lns_add(v[6], v[7], lut, S), lut, S),
+                    lut, S);
+    }
     if (nsplit == 1) {
         __syncthreads();
-        s_x[0][p][lane] = r;
+        if (threadIdx.x < 512) s_x[0][p][lane] = r;
         __syncthreads();
         if (threadIdx.x < 64 && row < rows) {
             int ph[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) ph[k] = s_x[0][k][lane];
-            *reinterpret_cast<int2 *>(out + 2 * (size_t)row) = finish(phase_tree(ph, lut, nkp, nkm), ld);
+            *reinterpret_cast<int2 *>(out + 2 * (size_t)row) = finish(phase_tree(ph, lut, S), ld);
         }
-    } else {
+    } else if (threadIdx.x < 512) {
         const size_t padded_rows = (size_t)(gridDim.x / nsplit) * 64;
         partial[((size_t)q * padded_rows + row) * 8 + p] = r;
     }
@@ -212,12 +289,13 @@ __global__ __launch_bounds__(512) void flns_tile_kernel(
 // phase tree and the scale.  P (a power of two >= nsplit, <= 64) lanes per
 // row, lane i holding workgroup i's eight phase partials (zero past nsplit);
 // level s pairs lanes i and i ^ s, which is the balanced pairwise tree.
-template <typename E>
-__global__ __launch_bounds__(256) void flns_combine(const int *__restrict__ partial, int rows,
-                                                   int padded_rows, int nsplit, int P,
-                                                   const uint8_t *__restrict__ table, int nkp,
-                                                   int nkm, int ld, int32_t *__restrict__ out) {
-    const E *lut = reinterpret_cast<const E *>(table + kFlnsCorrOff);
+template <bool SMALL>
+__global__ __launch_bounds__(1024) void flns_combine(const int *__restrict__ partial, int rows,
+                                                    int padded_rows, int nsplit, int P,
+                                                    const uint8_t *__restrict__ table, int S,
+                                                    int ld, int32_t *__restrict__ out) {
+    using E = LutT<SMALL>;
+    __shared__ uint4 s_lut4[SMALL ? kFlnsSmallMaxEntries * 2 / 16 : 1];
     const int gid = blockIdx.x * blockDim.x + threadIdx.x;
     const int row = gid / P;
     const int q = gid - row * P;
@@ -231,12 +309,18 @@ __global__ __launch_bounds__(256) void flns_combine(const int *__restrict__ part
 #pragma unroll
         for (int p = 0; p < 8; ++p) v[p] = kZ;
     }
+    if constexpr (SMALL) {
+        stage16(s_lut4, reinterpret_cast<const uint4 *>(table + kFlnsCorrOff), (2 * S * 2 + 15) / 16);
+        __syncthreads();
+    }
+    const E *lut = SMALL ? reinterpret_cast<const E *>(s_lut4)
+                         : reinterpret_cast<const E *>(table + kFlnsCorrOff);
     for (int s = 1; s < P; s <<= 1) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) v[p] = lns_add(v[p], __shfl_xor(v[p], s), lut, nkp, nkm);
+        for (int p = 0; p < 8; ++p) v[p] = lns_add(v[p], __shfl_xor(v[p], s), lut, S);
     }
     if (q == 0 && row < rows)
-        *reinterpret_cast<int2 *>(out + 2 * (size_t)row) = finish(phase_tree(v, lut, nkp, nkm), ld);
+        *reinterpret_cast<int2 *>(out + 2 * (size_t)row) = finish(phase_tree(v, lut, S), ld);
 }
 
 }  // namespace
@@ -249,6 +333,8 @@ static constexpr int64_t kFlnsMaxK = 65408;
 
 static int64_t flns_nsplit(int64_t k) { return (k / kGroup + kTilesPerWg - 1) / kTilesPerWg; }
 
+// Workspace: the partials int32[nsplit][R][8] when K is split over several
+// workgroups per row tile.  Written before they are read: no initialisation.
 static size_t flns_ws_bytes(int64_t rows, int64_t k) {
     const int64_t ns = flns_nsplit(k);
     const size_t part = ns > 1 ? (size_t)ns * (size_t)pad64(rows) * 8 * 4 : 0;
@@ -276,30 +362,31 @@ extern "C" int32_t bs_flns_phase_gemv(const uint8_t *planes, const uint8_t *x_ln
         return BS_E_ALIGN;
     if (!ws_ok(workspace, workspace_bytes, flns_ws_bytes(rows, k))) return BS_E_WORKSPACE;
     const bool small = frac_bits <= kFlnsSmallMaxFrac;
-    if (small && sz.n_kp + sz.n_km > kFlnsSmallMaxEntries) return BS_E_RANGE;
+    if (small && 2 * sz.stride > kFlnsSmallMaxEntries) return BS_E_RANGE;
 
     const int64_t tiles = pad64(rows) / 64;
     const int64_t groups = k / kGroup;
     const int nsplit = (int)flns_nsplit(k);
     // both grids within the 2^32 threads of one launch
-    if (tiles * nsplit * kTilesPerWg * 64 >= ((int64_t)1 << 32) ||
+    // both grids within the 2^32 threads of one launch
+    if (tiles * nsplit * kWavesPerWg * 64 >= ((int64_t)1 << 32) ||
         rows * 64 >= ((int64_t)1 << 32))
         return BS_E_SHAPE;
     hipStream_t st = (hipStream_t)stream;
     const uint8_t *tb = static_cast<const uint8_t *>(table);
     int *partial = static_cast<int *>(workspace);
     auto kern = small ? flns_tile_kernel<true> : flns_tile_kernel<false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * nsplit)), dim3(kTilesPerWg * 64), 0, st,
-                       planes, x_lns8, (int)rows, (int)groups, (int)frac_bits, tb, (int)sz.n_kp,
-                       (int)sz.n_km, (int)ld, nsplit, out, partial);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * nsplit)), dim3(kWavesPerWg * 64), 0, st,
+                       planes, x_lns8, (int)rows, (int)groups, (int)frac_bits, tb, (int)sz.stride,
+                       (int)ld, nsplit, out, partial);
     BS_LAUNCH_CHECK();
     if (nsplit > 1) {
         int P = 1;
         while (P < nsplit) P <<= 1;
         const int64_t threads = rows * P;
-        auto comb = small ? flns_combine<int16_t> : flns_combine<int32_t>;
-        hipLaunchKernelGGL(comb, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, partial,
-                           (int)rows, (int)pad64(rows), nsplit, P, tb, (int)sz.n_kp, (int)sz.n_km,
+        auto comb = small ? flns_combine<true> : flns_combine<false>;
+        hipLaunchKernelGGL(comb, dim3((unsigned)((threads + 1023) / 1024)), dim3(1024), 0, st,
+                           partial, (int)rows, (int)pad64(rows), nsplit, P, tb, (int)sz.stride,
                            (int)ld, out);
         BS_LAUNCH_CHECK();
     }

@@ -69,8 +69,9 @@ bool flns_sizes(int f, FlnsSizes *s) {
     if (n_kp < 0 || n_km < 0) return false;
     s->n_kp = n_kp;
     s->n_km = n_km;
+    s->stride = (n_kp > n_km ? n_kp : n_km) + 1;
     s->elem = f <= kFlnsSmallMaxFrac ? 2 : 4;
-    s->bytes = (int64_t)align_up((size_t)(kFlnsCorrOff + (n_kp + n_km) * s->elem), 16);
+    s->bytes = (int64_t)align_up((size_t)(kFlnsCorrOff + 2 * s->stride * s->elem), 16);
     return true;
 }
 
@@ -96,7 +97,7 @@ extern "C" int32_t bs_flns_table_build(int32_t frac_bits, void *table, int64_t t
     uint8_t *base = static_cast<uint8_t *>(table);
     memset(base, 0, (size_t)s.bytes);
     int32_t hdr[16] = {kFlnsMagic, frac_bits, (int32_t)s.n_kp, (int32_t)s.n_km, (int32_t)s.elem,
-                       (int32_t)s.bytes};
+                       (int32_t)s.bytes, (int32_t)s.stride};
     memcpy(base, hdr, sizeof hdr);
     const int64_t N = (int64_t)8 << frac_bits;
     int32_t fold[kFlnsFoldSlots] = {0};
@@ -124,7 +125,7 @@ extern "C" int32_t bs_flns_table_build(int32_t frac_bits, void *table, int64_t t
     for (int64_t D = 1; D < s.n_km; ++D) {
         int64_t v;
         if (!round_checked(km_real(D, N), &v) || v == 0) return BS_E_RANGE;
-        put(s.n_kp + D, v);
+        put(s.stride + D, v);
     }
     return BS_OK;
 }

@@ -19,17 +19,20 @@ FAKE = ctypes.c_void_p(1 << 20)          # never dereferenced: validation fails 
 
 
 def _unpack(blob):
+    """(header, fold table, kp, km, padding past each table)."""
     hdr = blob[:64].view(np.int32)
-    nkp, nkm, elem = int(hdr[2]), int(hdr[3]), int(hdr[4])
+    nkp, nkm, elem, S = int(hdr[2]), int(hdr[3]), int(hdr[4]), int(hdr[6])
+    assert S == max(nkp, nkm) + 1
     fold = blob[64:64 + 132 * 4].view(np.int32)
-    corr = blob[592:592 + (nkp + nkm) * elem].view(np.int16 if elem == 2 else np.int32)
-    return hdr, fold, corr[:nkp], corr[nkp:]
+    corr = blob[592:592 + 2 * S * elem].view(np.int16 if elem == 2 else np.int32)
+    pad = np.concatenate([corr[nkp:S], corr[S + nkm:2 * S]])
+    return hdr, fold, corr[:nkp], corr[S:S + nkm], pad
 
 
 @pytest.mark.parametrize("f", range(0, 13))
 def test_table_blob_equals_oracle_tables(f):
     blob = bs.flns_table(f)
-    hdr, fold, kp, km = _unpack(blob)
+    hdr, fold, kp, km, pad = _unpack(blob)
     tb = oracle.flns_tables(f)
     assert hdr[0] == 0x534E4C46 and hdr[1] == f and hdr[5] == blob.size
     assert hdr[4] == (2 if f <= 8 else 4)
@@ -38,6 +41,7 @@ def test_table_blob_equals_oracle_tables(f):
     assert np.array_equal(kp, tb["kp"])
     assert km.size == tb["km"].size
     assert np.array_equal(km[1:], tb["km"][1:])
+    assert (pad == 0).all() and pad.size >= 2      # a clamped index reads a zero correction
 
 
 def test_table_bytes_and_build_errors():

@@ -95,3 +95,20 @@ def test_flns_adversarial(case, f):
     if case[0] in ("all_zero_code", "zero_code_sign_set", "cancel_in_tile",
                    "cancel_across_tiles", "zero_weights"):
         assert (got == 0).all()
+
+
+def test_flns_repeated_calls_share_a_workspace():
+    """One workspace serves back-to-back calls of different shapes (one with
+    fewer rows, one with a single workgroup per tile), every result exact."""
+    import torch
+    dev = device()
+    ws = torch.zeros(int(bs.lib().bs_flns_workspace_bytes(300, 4096)), dtype=torch.uint8,
+                     device=dev)
+    for rows, k, seed in ((300, 4096, 1), (300, 4096, 2), (130, 2048, 3), (300, 4096, 4)):
+        t, x = synth.lns8(rows, k, seed)
+        want = oracle.flns_gemv(t, x, 8)
+        note("flns repeated rows=%d k=%d" % (rows, k))
+        out = bs.flns_phase_gemv(to_dev(bs.ternary_pack(t), dev), to_dev(x, dev), rows, k, 8,
+                                 table_dev(8, dev), workspace=ws)
+        torch.cuda.synchronize()
+        assert (out.cpu().numpy() == want).all()
