@@ -23,7 +23,14 @@
 // inside a wavefront and through LDS across wavefronts; integer sums make
 // the result independent of that order (integer-engine page, section 3.2).
 //
-// bs_q1_gemv runs the same kernel on Q1_0 weights (integer-engine page,
+// Tall matrices (many 64-row tiles, few groups per row) use a second
+// mapping: one workgroup per 64-row tile, lane l of every wavefront serving
+// row 64*tile + l, wavefront w taking groups w, w + W, ...  The activations
+// a wavefront needs are then uniform across it, and their bit planes come
+// from sixteen ballots into scalar registers: no LDS staging, and the LDS
+// only meets the W partial sums per row at the end.
+//
+// bs_q1_gemv runs the same kernels on Q1_0 weights (integer-engine page,
 // section 4.1): one sign bit per weight (1 = +1, 0 = -1) in the layout of the
 // ternary W_nonzero plane, signed_sum = 2 * pos_sum - block_total, where
 // block_total (the group's sum of x, shared by every row) is reduced across
@@ -84,6 +91,40 @@ __device__ __forceinline__ int q1_group_dot(const uint4 &bits, const uint4 *__re
         pos += (b == 7) ? -q * 128 : q * (1 << b);
     }
     return 2 * pos - (int)xg[8].x;
+}
+
+// The same two sums against scalar-register activation planes (tile
+// mapping): xp.w[b][d] is uniform across the wavefront.
+__device__ __forceinline__ int tile_dot(const uint4 &nz, const uint4 &ng, const XPlanes &xp) {
+    int s = __builtin_popcount(ng.x) + __builtin_popcount(ng.y) + __builtin_popcount(ng.z) +
+            __builtin_popcount(ng.w);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const int q = __builtin_popcount(nz.x & (xp.w[b][0] ^ ng.x)) +
+                      __builtin_popcount(nz.y & (xp.w[b][1] ^ ng.y)) +
+                      __builtin_popcount(nz.z & (xp.w[b][2] ^ ng.z)) +
+                      __builtin_popcount(nz.w & (xp.w[b][3] ^ ng.w));
+        s += (b == 7) ? -q * 128 : q * (1 << b);
+    }
+    return s;
+}
+
+// Q1_0: 2 * pos_sum - block_total; block_total = sum_b w_b popcount(X_b) is
+// uniform, so the scalar unit counts it.
+__device__ __forceinline__ int tile_q1_dot(const uint4 &bits, const XPlanes &xp) {
+    int pos = 0, total = 0;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const int q = __builtin_popcount(bits.x & xp.w[b][0]) +
+                      __builtin_popcount(bits.y & xp.w[b][1]) +
+                      __builtin_popcount(bits.z & xp.w[b][2]) +
+                      __builtin_popcount(bits.w & xp.w[b][3]);
+        const int t = __builtin_popcount(xp.w[b][0]) + __builtin_popcount(xp.w[b][1]) +
+                      __builtin_popcount(xp.w[b][2]) + __builtin_popcount(xp.w[b][3]);
+        pos += (b == 7) ? -q * 128 : q * (1 << b);
+        total += (b == 7) ? -t * 128 : t * (1 << b);
+    }
+    return 2 * pos - total;
 }
 
 // v summed with the lane 16 (SWAP32 false) or 32 (true) apart, in every lane:
@@ -221,7 +262,55 @@ __global__ void ternary_rows_kernel(const uint8_t *__restrict__ planes,
     }
 }
 
+// One workgroup per 64-row tile and all of K; W wavefronts (W <= 16), lane l
+// of each serving row 64*tile + l.  Wavefront w takes groups w, w + W, ...
+// with one group's loads in flight at a time (more wavefronts, not deeper
+// per-wavefront queues, measured faster).  Rows past `rows` (the tile's zero
+// padding) load nothing and store nothing.
+template <bool Q1>
+__global__ void ternary_tile_kernel(const uint8_t *__restrict__ planes,
+                                    const int16_t *__restrict__ pscales,
+                                    const int8_t *__restrict__ x, int rows, int groups,
+                                    int shift, int64_t *__restrict__ y) {
+    __shared__ int64_t part[16][64];
+    const int nwaves = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int tile = blockIdx.x;
+    const int row = tile * 64 + lane;
+    const bool live = row < rows;
+    int64_t acc = 0;
+    for (int g = wave; g < groups; g += nwaves) {
+        const size_t blk = (size_t)tile * groups + g;
+        const int xa = x[(size_t)g * 128 + lane];
+        const int xb = x[(size_t)g * 128 + 64 + lane];
+        uint4 nz = make_uint4(0, 0, 0, 0), ng = make_uint4(0, 0, 0, 0);
+        int sc = 0;
+        if (live) {
+            if constexpr (Q1) {
+                nz = load_stream16(planes + blk * 1024 + 16 * lane);
+            } else {
+                nz = load_stream16(planes + blk * 2048 + 16 * lane);
+                ng = load_stream16(planes + blk * 2048 + 1024 + 16 * lane);
+            }
+            sc = pscales[((size_t)(row >> 4) * groups + g) * 16 + (row & 15)];
+        }
+        XPlanes xp;
+        ballot_planes(xa, xb, xp);
+        const int s = Q1 ? tile_q1_dot(nz, xp) : tile_dot(nz, ng, xp);
+        acc += (int64_t)(__mul24(s, sc) >> shift);   // |s * sc| <= 2^29; >> = floor
+    }
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        int64_t tot = 0;
+        for (int w = 0; w < nwaves; ++w) tot += part[w][threadIdx.x];
+        if (live) y[row] = tot;
+    }
+}
+
 struct TernaryCfg {
+    bool tile;            // tile mapping (ternary_tile_kernel) with `waves` wavefronts
     int rows_per_block;   // R: 64, 32 or 16
     int waves;            // wavefronts per block, 1..16
     int maxg;             // groups per slice and round held in registers: 1, 2 or 4
@@ -255,6 +344,12 @@ static int32_t launch_ternary(const TernaryCfg &c, const uint8_t *planes, const 
     const int groups = (int)(k / kGroup);
     const int shift = frac > 31 ? 31 : frac;   // |scale*s| < 2^31: shift 31 is floor
     const int n = (int)rows;
+    if (c.tile) {
+        hipLaunchKernelGGL((ternary_tile_kernel<Q1>), dim3((unsigned)(pad64(rows) / 64)),
+                           dim3(c.waves * 64), 0, st, planes, scales, x, n, groups, shift, y);
+        BS_LAUNCH_CHECK();
+        return BS_OK;
+    }
     bool ok;
     switch (c.rows_per_block) {
     case 64: ok = launch_r<64, Q1>(c.maxg, c.waves, st, planes, scales, x, n, groups, shift, y); break;
@@ -267,15 +362,25 @@ static int32_t launch_ternary(const TernaryCfg &c, const uint8_t *planes, const 
     return BS_OK;
 }
 
-// Launch shape, from a sweep of block heights and wavefront counts on
-// MI355X: 64-row blocks when there are enough tiles to give every CU one
-// block and rows are long; otherwise 16-row blocks (four slices per
-// wavefront) with one group per slice (8 wavefronts up to 32 groups, 16
-// beyond), or 32-row blocks for long rows with many rows.
+// Launch shape, from sweeps of both mappings on MI355X: the tile mapping
+// (16 wavefronts) for tall matrices with up to 48 groups per row (150+
+// tiles at up to 24 groups, 200+ beyond); otherwise row blocks: 64-row
+// blocks when there are enough tiles to give every CU one block and rows are
+// long; otherwise 16-row blocks (four slices per wavefront) with one group
+// per slice (8 wavefronts up to 32 groups, 16 beyond), or 32-row blocks for
+// long rows with many rows.
 static TernaryCfg choose_cfg(int64_t rows, int64_t k) {
     const int64_t groups = k / kGroup, tiles = pad64(rows) / 64;
     auto maxg_for = [](int64_t per) { return per <= 1 ? 1 : per <= 2 ? 2 : 4; };
     TernaryCfg c;
+    c.tile = false;
+    if (tiles >= 150 && groups <= 48 && (groups <= 24 || tiles >= 200)) {
+        c.tile = true;
+        c.waves = (int)(groups < 16 ? groups : 16);
+        c.rows_per_block = 64;
+        c.maxg = 1;
+        return c;
+    }
     if (tiles >= 200 && groups >= 40) {
         c.rows_per_block = 64;
         c.waves = 16;

@@ -41,15 +41,17 @@ def test_large_k(shape):
 
 
 @pytest.mark.parametrize("rows,k", [(1, 128), (63, 128), (65, 256), (130, 384), (127, 6912),
-                                    (200, 128 * 100), (80, 128 * 217)])
+                                    (200, 128 * 100), (80, 128 * 217), (9600, 2560),
+                                    (13800, 2560), (12863, 6144), (14000, 128)])
 def test_ragged(rows, k):
     check(*synth.q1(rows, k, rows + k))
 
 
+@pytest.mark.parametrize("rows", [130, 9700])
 @pytest.mark.parametrize("frac", [0, 1, 16, 31, 32, 62])
-def test_frac_with_negative_scales(frac):
-    s, _, x = synth.q1(130, 640, frac)
-    sc = np.random.default_rng(frac).integers(-32768, 32768, (130, 5)).astype(np.int16)
+def test_frac_with_negative_scales(frac, rows):
+    s, _, x = synth.q1(rows, 640, frac)
+    sc = np.random.default_rng(frac).integers(-32768, 32768, (rows, 5)).astype(np.int16)
     check(s, sc, x, frac)
 
 

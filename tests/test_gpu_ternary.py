@@ -49,6 +49,23 @@ def test_bitnet2b_projections(name, seed):
     check(*synth.ternary(rows, k, seed))
 
 
+@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("rows", [3840, 13824])
+def test_fused_launches(rows, seed):
+    """The benchmark's launches: q|k|v (3840 x 2560) and gate|up (13824 x 2560)
+    stored concatenated by rows."""
+    check(*synth.ternary(rows, 2560, seed))
+
+
+@pytest.mark.parametrize("rows,k", [(9600, 2560), (9601, 3072), (12800, 3200), (12863, 6144),
+                                    (13800, 2560), (12800, 640), (14000, 128)])
+def test_tile_mapping_edges(rows, k):
+    """Around the tall-matrix (one workgroup per 64-row tile) launch bounds:
+    150 tiles, 24 groups, 200 tiles with more groups, 48 groups, a ragged last
+    tile, fewer groups than wavefronts."""
+    check(*synth.ternary(rows, k, seed=rows ^ k, p_zero=1 / 3, act="uniform127"))
+
+
 @pytest.mark.parametrize("seed", range(2))
 @pytest.mark.parametrize("shape", synth.LARGE_K_SHAPES)
 def test_large_k(shape, seed):
@@ -61,16 +78,21 @@ def test_ragged_shapes(rows, k):
     check(*synth.ternary(rows, k, seed=rows + k, p_zero=1 / 3, act="uniform127"))
 
 
+@pytest.mark.parametrize("rows", [130, 9700])
 @pytest.mark.parametrize("frac", [0, 1, 3, 16, 29, 30, 31, 32, 62])
-def test_frac_with_negative_scales(frac):
-    t, _, x = synth.ternary(130, 640, seed=frac, p_zero=1 / 3, act="uniform127")
+def test_frac_with_negative_scales(frac, rows):
+    t, _, x = synth.ternary(rows, 640, seed=frac, p_zero=1 / 3, act="uniform127")
     rng = np.random.default_rng(frac)
-    sc = rng.integers(-32768, 32768, (130, 5)).astype(np.int16)
+    sc = rng.integers(-32768, 32768, (rows, 5)).astype(np.int16)
     check(t, sc, x, frac)
 
 
 def test_degenerate_values():
-    rows, k = 96, 512
+    for rows, k in ((96, 512), (9664, 512)):
+        _degenerate(rows, k)
+
+
+def _degenerate(rows, k):
     # all-zero weights
     check(np.zeros((rows, k), np.int8), np.ones((rows, 4), np.int16),
           np.full(k, 7, np.int8))
