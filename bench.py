@@ -309,7 +309,64 @@ def run_extras(torch, bs, synth, dev, timer):
             "frac_hbm_peak": round(p8.numel() / us / 1e3 / HBM_PEAK_GBS, 4),
             "weights_per_s": round(4096 * 4096 / us * 1e6, 1)}
         log("lns8 %s: %.2f us" % (name, us))
+    # pure fractional-LNS reduction of the same products, by internal
+    # precision: time per call and the error of the decoded result against the
+    # exact dyadic S of the linear path above (sign * 2^((L/2^f - 74)/8))
+    import numpy as np
+    s_exact = s8.clone()
+    bs.lns8_phase_gemv(p8, xd8, 4096, 4096, bs.LNS8_DIRECT, acc=acc, s=s_exact, workspace=ws8)
+    torch.cuda.synchronize()
+    s_ref = s_exact.cpu().numpy()
+    wsf = torch.zeros(bs.lib().bs_flns_workspace_bytes(4096, 4096), dtype=torch.uint8, device=dev)
+    outf = torch.empty((4096, 2), dtype=torch.int32, device=dev)
+    flns = {}
+    for f in (0, 2, 4, 8, 12):
+        tb = torch.from_numpy(bs.flns_table(f)).to(dev)
+        us = per_launch_us(timer, lambda i: bs.flns_phase_gemv(pool8[i % len(pool8)], xd8, 4096,
+                                                               4096, f, tb, out=outf,
+                                                               workspace=wsf), n=50, reps=3)
+        bs.flns_phase_gemv(p8, xd8, 4096, 4096, f, tb, out=outf, workspace=wsf)
+        torch.cuda.synchronize()
+        o = outf.cpu().numpy().astype(np.float64)
+        val = o[:, 0] * np.exp2((o[:, 1] / float(1 << f) - 74.0) / 8.0) * (o[:, 0] != 0)
+        big = np.abs(s_ref) >= 1e-3 * np.median(np.abs(s_ref))
+        rel = np.abs(val[big] - s_ref[big]) / np.abs(s_ref[big])
+        flns["f%d" % f] = {"us_per_gemv": round(us, 3),
+                           "GBps": round(p8.numel() / us / 1e3, 1),
+                           "rel_err_median": float("%.3g" % np.median(rel)),
+                           "rel_err_p99": float("%.3g" % np.quantile(rel, 0.99)),
+                           "rel_err_max": float("%.3g" % rel.max()),
+                           "rows_compared": int(big.sum())}
+        log("flns f=%d: %.2f us, median rel err %.3g" % (f, us, np.median(rel)))
+    ops["flns_4096x4096"] = {"error_vs": "exact dyadic S of the linear eight-phase path "
+                                         "(rows with |S| >= 1e-3 x median |S|)", **flns}
     del pool8
+    # steps either side of the GEMVs: absmax int8 quantisation of the
+    # activation vector (the q|k|v and down inputs), LNS8 encoding of the
+    # eight-phase input, and the candidate sampler on a top-40 (one launch
+    # each; a decode step runs them once per vector)
+    rng = np.random.default_rng(0)
+    for k in (2560, 6912):
+        xq = torch.from_numpy(rng.integers(-(1 << 40), 1 << 40, k).astype(np.int64)).to(dev)
+        qo = torch.empty(k, dtype=torch.int8, device=dev)
+        am = torch.empty(1, dtype=torch.int64, device=dev)
+        stq = torch.empty(1, dtype=torch.int32, device=dev)
+        us = per_launch_us(timer, lambda i: bs.act_quant_i8(xq, q=qo, absmax=am, status=stq),
+                           n=100)
+        ops["act_quant_i8_k%d" % k] = {"us_per_call": round(us, 3)}
+    xe = torch.from_numpy((rng.standard_normal(4096) * 2.0 ** 20).astype(np.int64)).to(dev)
+    eo = torch.empty(4096, dtype=torch.uint8, device=dev)
+    ops["lns8_encode_k4096"] = {"us_per_call": round(per_launch_us(
+        timer, lambda i: bs.lns8_encode(xe, 16, out=eo), n=100), 3)}
+    ci = torch.from_numpy(rng.permutation(128256)[:40].astype(np.int32)).to(dev)
+    cs = torch.from_numpy(np.sort(rng.integers(0, 1 << 30, 40))[::-1].copy()).to(dev)
+    res = torch.empty(6, dtype=torch.int64, device=dev)
+    ops["sample_candidates_n40"] = {"us_per_call": round(per_launch_us(
+        timer, lambda i: bs.sample_candidates(ci, cs, bs.SAMPLE_DRAW, beta_q16=1 << 10, seed=1,
+                                              position=i, result=res), n=100), 3)}
+    log("edges: quant %.2f us, encode %.2f us, sample %.2f us" % (
+        ops["act_quant_i8_k2560"]["us_per_call"], ops["lns8_encode_k4096"]["us_per_call"],
+        ops["sample_candidates_n40"]["us_per_call"]))
     # BITNET_PLANES lm_head, 128256 x 2560, top-40, cap 200
     V, K = synth.LMHEAD_SHAPE
     trits, rs, h = synth.lmhead(V, K, 0)

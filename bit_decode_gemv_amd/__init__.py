@@ -62,6 +62,11 @@ def _declare(lib):
         "bs_planes_pack": (I32, [P, I64, I64, P, P]),
         "bs_lmhead_workspace_bytes": (SZ, [I64, I64, I32, I32]),
         "bs_lmhead_planes_topk": (I32, [P, P, P, P, I64, I64, I32, I32, P, P, P, P, SZ, P]),
+        "bs_act_quant_i8": (I32, [P, I64, P, P, P, P]),
+        "bs_lns8_encode": (I32, [P, I64, I32, P, P]),
+        "bs_lns8_encode_edges": (I32, [I32, P]),
+        "bs_sample_candidates": (I32, [P, P, I32, I32, ctypes.c_uint32, ctypes.c_uint32,
+                                       ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -369,3 +374,73 @@ def lmhead_planes_topk(planes03, planes47, row_scale, h, vocab: int, dim: int,
         wp, wn, _stream_handle(stream, dev))
     _check(rc, "bs_lmhead_planes_topk")
     return top_idx, top_score, info
+
+
+# ------------------------------------------------- steps around the GEMVs
+
+SAMPLE_GREEDY, SAMPLE_DRAW = 0, 1
+
+
+def lns8_encode_edges(frac: int) -> np.ndarray:
+    """Host: the encoder's integer code edges for frac (uint64[128])."""
+    e = np.zeros(128, dtype=np.uint64)
+    _check(lib().bs_lns8_encode_edges(int(frac), _np_ptr(e)), "bs_lns8_encode_edges")
+    return e
+
+
+def act_quant_i8(x, q=None, absmax=None, status=None, stream=None):
+    """(q int8[k], absmax int64[1], status int32[1]) on x's device."""
+    torch = _torch()
+    dev = x.device
+    k = x.numel()
+    if q is None:
+        q = torch.empty(k, dtype=torch.int8, device=dev)
+    if absmax is None:
+        absmax = torch.empty(1, dtype=torch.int64, device=dev)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    _need(q, k, "q")
+    _need(absmax, 1, "absmax")
+    _need(status, 1, "status")
+    rc = lib().bs_act_quant_i8(_dptr(x, torch.int64, "x"), k, _dptr(q, torch.int8, "q"),
+                               _dptr(absmax, torch.int64, "absmax"),
+                               _dptr(status, torch.int32, "status"), _stream_handle(stream, dev))
+    _check(rc, "bs_act_quant_i8")
+    return q, absmax, status
+
+
+def lns8_encode(x, frac: int, out=None, stream=None):
+    """LNS8 bytes (uint8[k]) of the int64 fixed-point vector x."""
+    torch = _torch()
+    dev = x.device
+    k = x.numel()
+    if out is None:
+        out = torch.empty(k, dtype=torch.uint8, device=dev)
+    _need(out, k, "out")
+    rc = lib().bs_lns8_encode(_dptr(x, torch.int64, "x"), k, int(frac),
+                              _dptr(out, torch.uint8, "out"), _stream_handle(stream, dev))
+    _check(rc, "bs_lns8_encode")
+    return out
+
+
+def sample_candidates(idx, score, mode: int, beta_q16: int = 1 << 16, top_p_q16: int = 1 << 16,
+                      min_p_q16: int = 0, seed: int = 0, position: int = 0, n: int = None,
+                      result=None, stream=None):
+    """int64[6] on the device: token, rank, kept ranks, kept total, draw,
+    SHA-256 attempts."""
+    torch = _torch()
+    dev = score.device
+    n = score.numel() if n is None else int(n)
+    if result is None:
+        result = torch.empty(6, dtype=torch.int64, device=dev)
+    _need(idx, n, "idx")
+    _need(score, n, "score")
+    _need(result, 6, "result")
+    rc = lib().bs_sample_candidates(_dptr(idx, torch.int32, "idx"),
+                                    _dptr(score, torch.int64, "score"), n, int(mode),
+                                    int(beta_q16), int(top_p_q16), int(min_p_q16),
+                                    int(seed) & ((1 << 64) - 1), int(position) & ((1 << 64) - 1),
+                                    _dptr(result, torch.int64, "result"),
+                                    _stream_handle(stream, dev))
+    _check(rc, "bs_sample_candidates")
+    return result

@@ -314,6 +314,87 @@ int32_t bs_lmhead_planes_topk(const uint8_t *planes03, const uint8_t *planes47,
                               int32_t *top_idx, int64_t *top_score, int32_t *info,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* ======================================================================== */
+/* Activation encoders upstream of the GEMVs                                 */
+/* ======================================================================== */
+/*
+ * bs_act_quant_i8 -- per-token absmax quantisation to int8 ([IE] section
+ * 4.4: BitNet quantises activations per token, absmax -> int8; section 3.1:
+ * activations are int64 fixed point):
+ *   A = max_i |x_i|,  q_i = sgn(x_i) * floor((254 |x_i| + A) / (2 A))
+ * i.e. 127 x / A rounded half away from zero (q = 0 when A = 0); the
+ * dequantised value is q * A / 127 in x's fixed point.
+ *   x       device int64[k], 8-byte aligned; |x_i| <= 2^55
+ *   q       device int8[k] (the activation vector of bs_ternary_gemv)
+ *   absmax  device int64[1], 8-byte aligned: A, or -1 when the bound breaks
+ *   status  device int32[1], 4-byte aligned: BS_OK, or BS_E_OVERFLOW when
+ *           some |x_i| > 2^55 (fail loud, [IE] section 3.4: then every q_i
+ *           is 0); read it after the stream synchronises
+ * Errors (host): BS_E_NULL, BS_E_SHAPE (k < 1 or k > 2^31), BS_E_ALIGN,
+ *   BS_E_HIP.
+ */
+int32_t bs_act_quant_i8(const int64_t *x, int64_t k, int8_t *q, int64_t *absmax,
+                        int32_t *status, void *stream);
+
+/*
+ * bs_lns8_encode -- int64 fixed-point activations (frac fractional bits) to
+ * LNS8 bytes S1|E4|L3 ([BS] section 3: code k stands for 2^((k-74)/8), code 0
+ * is exact zero; section 9: LNS8 saturation / underflow).  For v = x/2^frac
+ * the code is the nearest integer to 74 + 8 log2|v| (never a tie), 127 above
+ * the top code (saturation), and the zero byte 0x00 when it is below 1
+ * (underflow to zero); bit 7 is the sign of a non-zero code.  The output is
+ * the x_lns8 operand of bs_lns8_phase_gemv / bs_flns_phase_gemv.
+ *   x      device int64[k], 8-byte aligned
+ *   frac   0..62
+ *   out    device uint8[k]
+ * Errors: BS_E_NULL, BS_E_SHAPE, BS_E_RANGE (frac), BS_E_ALIGN, BS_E_HIP.
+ *
+ * bs_lns8_encode_edges -- the integer code edges the encoder uses, on the
+ * host: edges[c] (c = 1..127) = the least |x| whose code is at least c,
+ * ceil(2^(frac + (2c - 149)/16)), or UINT64_MAX when above 2^63; edges[0]
+ * = 0.  Host only.  Errors: BS_E_NULL, BS_E_RANGE.
+ */
+int32_t bs_lns8_encode(const int64_t *x, int64_t k, int32_t frac, uint8_t *out, void *stream);
+int32_t bs_lns8_encode_edges(int32_t frac, uint64_t *edges /* host [128] */);
+
+/* ======================================================================== */
+/* Candidate sampler downstream of the lm_head ([T2] ScoredToken /          */
+/* sampleFromCandidates; [IE] section 3.3 integer samplers)                 */
+/* ======================================================================== */
+/*
+ * bs_sample_candidates -- one token from n scored candidates (e.g. the
+ * top_idx / top_score of bs_lmhead_planes_topk).  Candidates rank by (score
+ * desc, index asc, input position asc).
+ *   mode BS_SAMPLE_GREEDY: rank 0 (argmax, lowest index on ties).
+ *   mode BS_SAMPLE_DRAW: rank r gets the Q31 weight
+ *       w_r = P(t mod 2^16) >> (t >> 16),  t = (score_0 - score_r) * beta_q16
+ *     (0 once t >> 16 >= 32), P(u) ~ 2^31 * 2^(-u / 2^16) the integer cubic
+ *     2^31 - ((A1 - ((A2 - ((A3 u) >> 16)) u >> 16)) u >> 16) with A1 =
+ *     1484817034, A2 = 495114803, A3 = 84039593 (a minimax fit, P(0) = 1 and
+ *     P(1) = 1/2 exactly, relative error < 1.1e-4): beta_q16 is the base-2
+ *     inverse temperature in Q16 (0 = uniform).  Top-p keeps the ranks whose
+ *     preceding cumulative weight is below top_p_q16/2^16 of the total,
+ *     min-p those whose weight is at least min_p_q16/2^16 of w_0.  The draw
+ *     is Lemire's bounded integer in [0, kept total) from the first 8 bytes
+ *     (big endian) of SHA-256(seed_le64 || position_le64 || attempt_le32),
+ *     attempt = 0, 1, ... (at most 16); the token is the first rank whose
+ *     cumulative weight exceeds it.
+ *   idx, score  device int32[n] (4-byte aligned), int64[n] (8-byte aligned)
+ *   n           1..1024
+ *   top_p_q16   1..65536 (65536 = off); min_p_q16 0..65536 (0 = off)
+ *   result      device int64[6], 8-byte aligned: token, rank, kept ranks,
+ *               kept weight total, draw, SHA-256 attempts (greedy: token,
+ *               0, 1, 0, 0, 0); token and rank -1 when no attempt was
+ *               accepted (probability below 2^-300)
+ * Errors: BS_E_NULL, BS_E_SHAPE (n), BS_E_RANGE (mode, top_p, min_p),
+ *   BS_E_ALIGN, BS_E_HIP.
+ */
+#define BS_SAMPLE_GREEDY 0
+#define BS_SAMPLE_DRAW 1
+int32_t bs_sample_candidates(const int32_t *idx, const int64_t *score, int32_t n, int32_t mode,
+                             uint32_t beta_q16, uint32_t top_p_q16, uint32_t min_p_q16,
+                             uint64_t seed, uint64_t position, int64_t *result, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -144,13 +144,14 @@ def sample_candidates(idx, score, mode: int, beta: int = 1 << 16, top_p: int = 1
                       min_p: int = 0, seed: int = 0, position: int = 0) -> dict:
     """One token from the candidates (idx int32, score int64).  Returns the
     token, its rank in (score desc, index asc) order, the number of kept
-    ranks, the kept weight total and the bounded draw."""
+    ranks, the kept weight total, the bounded draw and the SHA-256 attempts
+    it took."""
     cand = sorted(zip((int(s) for s in score), (int(i) for i in idx)),
                   key=lambda p: (-p[0], p[1]))
     if not cand:
         raise ValueError("no candidates")
     if mode == SAMPLE_GREEDY:
-        return {"token": cand[0][1], "rank": 0, "kept": 1, "total": 0, "draw": 0}
+        return {"token": cand[0][1], "rank": 0, "kept": 1, "total": 0, "draw": 0, "attempts": 0}
     s0 = cand[0][0]
     w = [weight_q31(s0 - s, beta) for s, _ in cand]
     wall = sum(w)
@@ -161,11 +162,12 @@ def sample_candidates(idx, score, mode: int, beta: int = 1 << 16, top_p: int = 1
         kept = r + 1
         cum += wr
     total = sum(w[:kept])
-    v, _ = lemire_bounded(seed, position, total)
+    v, attempts = lemire_bounded(seed, position, total)
     run = 0
     for r in range(kept):
         run += w[r]
         if run > v:
-            return {"token": cand[r][1], "rank": r, "kept": kept, "total": total, "draw": v}
+            return {"token": cand[r][1], "rank": r, "kept": kept, "total": total, "draw": v,
+                    "attempts": attempts}
     raise AssertionError("unreachable")
 

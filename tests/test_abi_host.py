@@ -191,3 +191,53 @@ def test_q1_gemv_validation():
     assert _q1(k=(1 << 24) + 128) == bs.BS_E_OVERFLOW
     assert _q1(bits=ctypes.c_void_p((1 << 20) + 8)) == bs.BS_E_ALIGN
     assert _q1(x=ctypes.c_void_p((1 << 20) + 4)) == bs.BS_E_ALIGN
+
+
+# ---- steps around the GEMVs (host checks)
+
+@pytest.mark.parametrize("frac", [0, 1, 9, 16, 30, 47, 62])
+def test_lns8_encode_edges_match_oracle(frac):
+    """Each library code edge is the least magnitude whose oracle code reaches
+    that code: code(edge) >= c and code(edge - 1) < c."""
+    from oracle import edges as oe
+    e = bs.lns8_encode_edges(frac)
+    assert e[0] == 0
+    assert (np.diff(e[1:].astype(object)) >= 0).all()
+    for c in range(1, 128):
+        t = int(e[c])
+        if t == (1 << 64) - 1:
+            assert oe.lns8_code(1 << 63, frac) < c
+            continue
+        assert t <= 1 << 63
+        assert oe.lns8_code(t, frac) >= c
+        assert t == 1 or oe.lns8_code(t - 1, frac) < c
+
+
+def test_edges_steps_validation():
+    lib = bs.lib()
+    assert lib.bs_act_quant_i8(None, 8, FAKE, FAKE, FAKE, None) == bs.BS_E_NULL
+    assert lib.bs_act_quant_i8(FAKE, 0, FAKE, FAKE, FAKE, None) == bs.BS_E_SHAPE
+    assert lib.bs_act_quant_i8(ctypes.c_void_p((1 << 20) + 4), 8, FAKE, FAKE, FAKE,
+                               None) == bs.BS_E_ALIGN
+    assert lib.bs_act_quant_i8(FAKE, 8, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 2),
+                               None) == bs.BS_E_ALIGN
+    assert lib.bs_lns8_encode(FAKE, 8, 63, FAKE, None) == bs.BS_E_RANGE
+    assert lib.bs_lns8_encode(FAKE, 8, -1, FAKE, None) == bs.BS_E_RANGE
+    assert lib.bs_lns8_encode(None, 8, 0, FAKE, None) == bs.BS_E_NULL
+    assert lib.bs_lns8_encode(FAKE, 0, 0, FAKE, None) == bs.BS_E_SHAPE
+    assert lib.bs_lns8_encode_edges(63, None) == bs.BS_E_NULL
+    assert lib.bs_lns8_encode_edges(63, FAKE) == bs.BS_E_RANGE
+
+    def smp(n=40, mode=1, top_p=65536, min_p=0, idx=FAKE, score=FAKE, res=FAKE):
+        return lib.bs_sample_candidates(idx, score, n, mode, 1 << 16, top_p, min_p, 1, 2, res,
+                                        None)
+    assert smp(idx=None) == bs.BS_E_NULL
+    assert smp(res=None) == bs.BS_E_NULL
+    assert smp(n=0) == bs.BS_E_SHAPE
+    assert smp(n=1025) == bs.BS_E_SHAPE
+    assert smp(mode=2) == bs.BS_E_RANGE
+    assert smp(top_p=0) == bs.BS_E_RANGE
+    assert smp(top_p=65537) == bs.BS_E_RANGE
+    assert smp(min_p=65537) == bs.BS_E_RANGE
+    assert smp(score=ctypes.c_void_p((1 << 20) + 4)) == bs.BS_E_ALIGN
+    assert smp(idx=ctypes.c_void_p((1 << 20) + 2)) == bs.BS_E_ALIGN
