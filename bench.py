@@ -450,7 +450,7 @@ def traffic_summary(fetch_csv: str, write_csv: str, shape: str):
                 continue
             v = float(r["Counter_Value"]) * 1024.0
             name = r["Kernel_Name"]
-            if "ternary_rows_kernel" in name:
+            if "ternary_rows_kernel" in name or "ternary_tile_kernel" in name:
                 gemv.append(v)
             elif "neg" in name:
                 calib.append(v)
@@ -610,7 +610,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": _recorded_traffic(tag),
-                "kernel": "ternary_rows_kernel %s (%s, 1 launch per step)" % (tag, dom),
+                "kernel": "bs_ternary_gemv %s (%s, 1 launch per step)" % (tag, dom),
                 "us_per_launch": round(dom_us, 3), "bytes_per_launch": dom_bytes}
 
     out = {
