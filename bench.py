@@ -7,8 +7,10 @@ and down (2560 x 6912), on packed ternary planes (0.25 B/weight) plus int16
 group scales, int8 activations, exact int64 outputs.  The projections that
 share an input are stored concatenated by rows, as decode engines store them:
 q|k|v is one 3840 x 2560 matrix and gate|up one 13824 x 2560 matrix, so a step
-is four dependent bs_ternary_gemv launches (qkv, o, gate_up, down) streaming
-the same bytes as the seven separate GEMVs.  The seven-launch form of the same
+is four dependent launches (qkv, o, gate_up, down) streaming the same bytes as
+the seven separate GEMVs.  q|k|v and gate|up write fresh outputs
+(bs_ternary_gemv); o and down add into the residual stream, as a decoder
+layer's output projections do (bs_ternary_gemv_acc, y += W x).  The seven-launch form of the same
 step (each projection a row range of the same buffers) is timed as well and
 reported in `config`.  Steps walk a pool of distinct layers whose weights
 total more than 1 GiB, so every GEMV streams its weights from HBM rather than
@@ -54,6 +56,7 @@ LAYER = [("q", 2560, 2560), ("k", 640, 2560), ("v", 640, 2560), ("o", 2560, 2560
 # launches of one step: (name, member projections stored concatenated by rows)
 FUSED = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")),
          ("down", ("down",))]
+RESIDUAL = ("o", "down")        # output projections: y += W x into the residual stream
 
 
 def weight_bytes(rows: int, k: int) -> int:
@@ -543,7 +546,9 @@ def main():
         del t, sc, parts
     layers = [{f: (base[f][0].clone(), base[f][1].clone()) for f, _ in FUSED}
               for _ in range(n_layers)]
-    ys = {f: torch.empty(base[f][3], dtype=torch.int64, device=dev) for f, _ in FUSED}
+    # outputs; the residual-stream accumulators start at zero and only grow by
+    # |W x| < 2^35 per step, far from int64's range over the run
+    ys = {f: torch.zeros(base[f][3], dtype=torch.int64, device=dev) for f, _ in FUSED}
     member_of = {}
     for fname, members in FUSED:
         row0 = 0
@@ -554,7 +559,10 @@ def main():
     def launch_fused(i, fname):
         p, s = layers[i % n_layers][fname]
         _, _, x, r, k = base[fname]
-        bs.ternary_gemv(p, s, x, r, k, out=ys[fname])
+        if fname in RESIDUAL:
+            bs.ternary_gemv_acc(p, s, x, r, k, ys[fname])
+        else:
+            bs.ternary_gemv(p, s, x, r, k, out=ys[fname])
 
     def launch_member(i, m):
         fname, row0 = member_of[m]
@@ -563,7 +571,10 @@ def main():
         r = shape[m][0]
         pv = p[row0 * k // 4:(row0 + r) * k // 4]
         sv = s[row0 * (k // 128):(row0 + r) * (k // 128)]
-        bs.ternary_gemv(pv, sv, x, r, k, out=ys[fname][row0:row0 + r])
+        if fname in RESIDUAL:
+            bs.ternary_gemv_acc(pv, sv, x, r, k, ys[fname][row0:row0 + r])
+        else:
+            bs.ternary_gemv(pv, sv, x, r, k, out=ys[fname][row0:row0 + r])
 
     def step(i):
         for fname, _ in FUSED:
@@ -610,7 +621,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": _recorded_traffic(tag),
-                "kernel": "bs_ternary_gemv %s (%s, 1 launch per step)" % (tag, dom),
+                "kernel": "%s %s (%s, 1 launch per step)" % (
+                    "bs_ternary_gemv_acc" if dom in RESIDUAL else "bs_ternary_gemv", tag, dom),
                 "us_per_launch": round(dom_us, 3), "bytes_per_launch": dom_bytes}
 
     out = {
@@ -620,7 +632,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "bitnet-b1.58-2B decode projections q,k,v,o,gate,up,down, "
                                "batch 1; q|k|v and gate|up stored concatenated by rows: "
-                               "4 dependent bs_ternary_gemv launches per step",
+                               "4 dependent launches per step (qkv, gate_up: bs_ternary_gemv; "
+                               "o, down: bs_ternary_gemv_acc into the residual stream)",
                    "launches": {f: "%dx%d" % (base[f][3], base[f][4]) for f, _ in FUSED},
                    "weight_bytes_per_step": step_bytes, "layers_in_pool": n_layers,
                    "pool_bytes": step_bytes * n_layers, "parallelism": "single GPU",

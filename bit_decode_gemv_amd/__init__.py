@@ -48,6 +48,7 @@ def _declare(lib):
         "bs_ternary_unpack": (I32, [P, I64, I64, P]),
         "bs_ternary_pack_scales": (I32, [P, I64, I64, P]),
         "bs_ternary_gemv": (I32, [P, P, P, I64, I64, I32, P, P]),
+        "bs_ternary_gemv_acc": (I32, [P, P, P, I64, I64, I32, P, P]),
         "bs_q1_planes_bytes": (I64, [I64, I64]),
         "bs_q1_pack": (I32, [P, I64, I64, P]),
         "bs_q1_gemv": (I32, [P, P, P, I64, I64, I32, P, P]),
@@ -270,6 +271,25 @@ def ternary_gemv(planes, scales, x, rows: int, k: int, frac: int = 0, out=None,
                                _stream_handle(stream, x.device))
     _check(rc, "bs_ternary_gemv")
     return out
+
+
+def ternary_gemv_acc(planes, scales, x, rows: int, k: int, y, frac: int = 0, stream=None):
+    """y += bs_ternary_gemv(planes, scales, x) in place (int64[rows] on x's
+    device); returns y."""
+    torch = _torch()
+    nplanes = lib().bs_ternary_planes_bytes(rows, k)
+    if nplanes < 0:
+        raise BsError(int(nplanes), "bs_ternary_planes_bytes")
+    _need(planes, nplanes, "planes")
+    _need(scales, lib().bs_ternary_scales_count(rows, k), "scales")
+    _need(x, k, "x")
+    _need(y, rows, "y")
+    rc = lib().bs_ternary_gemv_acc(_dptr(planes, torch.uint8, "planes"),
+                                   _dptr(scales, torch.int16, "scales"),
+                                   _dptr(x, torch.int8, "x"), rows, k, int(frac),
+                                   _dptr(y, torch.int64, "y"), _stream_handle(stream, x.device))
+    _check(rc, "bs_ternary_gemv_acc")
+    return y
 
 
 def q1_gemv(bits, scales, x, rows: int, k: int, frac: int = 0, out=None, stream=None):

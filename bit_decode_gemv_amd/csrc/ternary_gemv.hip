@@ -28,7 +28,10 @@
 // row 64*tile + l, wavefront w taking groups w, w + W, ...  The activations
 // a wavefront needs are then uniform across it, and their bit planes come
 // from sixteen ballots into scalar registers: no LDS staging, and the LDS
-// only meets the W partial sums per row at the end.
+// only meets the W partial sums per row at the end.  bs_ternary_gemv_acc
+// (y += W x, the residual-stream update of a decoder layer) runs the same
+// mapping split over runs of groups, each workgroup adding its rows' partial
+// sums to y with int64 atomics, so short matrices still fill the GPU.
 //
 // bs_q1_gemv runs the same kernels on Q1_0 weights (integer-engine page,
 // section 4.1): one sign bit per weight (1 = +1, 0 = -1) in the layout of the
@@ -262,25 +265,30 @@ __global__ void ternary_rows_kernel(const uint8_t *__restrict__ planes,
     }
 }
 
-// One workgroup per 64-row tile and all of K; W wavefronts (W <= 16), lane l
-// of each serving row 64*tile + l.  Wavefront w takes groups w, w + W, ...
-// with one group's loads in flight at a time (more wavefronts, not deeper
-// per-wavefront queues, measured faster).  Rows past `rows` (the tile's zero
+// One workgroup per (64-row tile, run of cg groups), W wavefronts (W <= 16),
+// lane l of each serving row 64*tile + l; wavefront w takes the run's groups
+// w, w + W, ... with one group's loads in flight at a time (more wavefronts,
+// not deeper per-wavefront queues, measured faster).  The W partial sums per
+// row meet in LDS; then the row's sum is stored (ACC false: one run covers
+// all of K) or added to y with one int64 atomic per row and workgroup (ACC
+// true: y += W x; the runs of a tile add in any order, exactly, since
+// integer addition is associative).  Rows past `rows` (the tile's zero
 // padding) load nothing and store nothing.
-template <bool Q1>
+template <bool Q1, bool ACC>
 __global__ void ternary_tile_kernel(const uint8_t *__restrict__ planes,
                                     const int16_t *__restrict__ pscales,
-                                    const int8_t *__restrict__ x, int rows, int groups,
-                                    int shift, int64_t *__restrict__ y) {
+                                    const int8_t *__restrict__ x, int rows, int groups, int cg,
+                                    int nruns, int shift, int64_t *__restrict__ y) {
     __shared__ int64_t part[16][64];
     const int nwaves = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int tile = blockIdx.x;
+    const int tile = blockIdx.x / nruns, run = blockIdx.x % nruns;
+    const int g0 = run * cg, g1 = min(groups, g0 + cg);
     const int row = tile * 64 + lane;
     const bool live = row < rows;
     int64_t acc = 0;
-    for (int g = wave; g < groups; g += nwaves) {
+    for (int g = g0 + wave; g < g1; g += nwaves) {
         const size_t blk = (size_t)tile * groups + g;
         const int xa = x[(size_t)g * 128 + lane];
         const int xb = x[(size_t)g * 128 + 64 + lane];
@@ -305,7 +313,11 @@ __global__ void ternary_tile_kernel(const uint8_t *__restrict__ planes,
     if (threadIdx.x < 64) {
         int64_t tot = 0;
         for (int w = 0; w < nwaves; ++w) tot += part[w][threadIdx.x];
-        if (live) y[row] = tot;
+        if (live) {
+            if constexpr (ACC) atomicAdd(reinterpret_cast<unsigned long long *>(y + row),
+                                         (unsigned long long)tot);
+            else y[row] = tot;
+        }
     }
 }
 
@@ -345,8 +357,9 @@ static int32_t launch_ternary(const TernaryCfg &c, const uint8_t *planes, const 
     const int shift = frac > 31 ? 31 : frac;   // |scale*s| < 2^31: shift 31 is floor
     const int n = (int)rows;
     if (c.tile) {
-        hipLaunchKernelGGL((ternary_tile_kernel<Q1>), dim3((unsigned)(pad64(rows) / 64)),
-                           dim3(c.waves * 64), 0, st, planes, scales, x, n, groups, shift, y);
+        hipLaunchKernelGGL((ternary_tile_kernel<Q1, false>), dim3((unsigned)(pad64(rows) / 64)),
+                           dim3(c.waves * 64), 0, st, planes, scales, x, n, groups, groups, 1,
+                           shift, y);
         BS_LAUNCH_CHECK();
         return BS_OK;
     }
@@ -399,6 +412,36 @@ static TernaryCfg choose_cfg(int64_t rows, int64_t k) {
     return c;
 }
 
+// y += W x: the tile mapping, split over runs of cg groups per workgroup.
+// Tall matrices with few groups keep one run per tile (cg = K/128, the
+// store-free tile kernel's shape); otherwise runs of four groups, four
+// wavefronts (one group each), when that still gives 150+ workgroups, else
+// runs of one group and one wavefront (sweeps on MI355X: 2560x2560 2.70 us,
+// 2560x6912 3.48 us, 6912x2560 3.32 us, against 2.96 / 3.85 / 3.55 us for the
+// storing kernel).  Runs grow so the grid stays below 2^24 workgroups.
+template <bool Q1>
+static int32_t launch_acc(const uint8_t *planes, const int16_t *scales, const int8_t *x,
+                          int64_t rows, int64_t k, int32_t frac, int64_t *y, hipStream_t st) {
+    const int64_t groups = k / kGroup, tiles = pad64(rows) / 64;
+    const int shift = frac > 31 ? 31 : frac;
+    int64_t cg, waves;
+    if (tiles >= 150 && groups <= 48 && (groups <= 24 || tiles >= 200)) {
+        cg = groups;
+        waves = groups < 16 ? groups : 16;
+    } else {
+        cg = tiles * ((groups + 3) / 4) >= 150 ? 4 : 1;
+        const int64_t min_cg = (tiles * groups + ((int64_t)1 << 24) - 1) >> 24;
+        if (cg < min_cg) cg = min_cg;
+        waves = cg < 16 ? cg : 16;
+    }
+    const int64_t nruns = (groups + cg - 1) / cg;
+    hipLaunchKernelGGL((ternary_tile_kernel<Q1, true>), dim3((unsigned)(tiles * nruns)),
+                       dim3((unsigned)waves * 64), 0, st, planes, scales, x, (int)rows,
+                       (int)groups, (int)cg, (int)nruns, shift, y);
+    BS_LAUNCH_CHECK();
+    return BS_OK;
+}
+
 }  // namespace
 }  // namespace bs
 
@@ -428,4 +471,11 @@ extern "C" int32_t bs_q1_gemv(const uint8_t *bits, const int16_t *scales, const 
     if (int32_t st = gemv_check(bits, scales, x, rows, k, frac, y)) return st;
     return launch_ternary<true>(choose_cfg(rows, k), bits, scales, x, rows, k, frac, y,
                                 (hipStream_t)stream);
+}
+
+extern "C" int32_t bs_ternary_gemv_acc(const uint8_t *planes, const int16_t *scales,
+                                       const int8_t *x, int64_t rows, int64_t k, int32_t frac,
+                                       int64_t *y, void *stream) {
+    if (int32_t st = gemv_check(planes, scales, x, rows, k, frac, y)) return st;
+    return launch_acc<false>(planes, scales, x, rows, k, frac, y, (hipStream_t)stream);
 }

@@ -117,6 +117,23 @@ int32_t bs_ternary_pack_scales(const int16_t *scales, int64_t rows, int64_t k,
 int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales, const int8_t *x,
                         int64_t rows, int64_t k, int32_t frac, int64_t *y, void *stream);
 
+/*
+ * bs_ternary_gemv_acc -- y += W x with the arithmetic of bs_ternary_gemv (the
+ * same planes, scales, x, frac and per-group floor): the residual-stream
+ * update of a decoder layer, whose output projections add into the running
+ * hidden state.  Each workgroup adds its rows' partial sums over a run of
+ * groups to y with int64 atomics; integer addition is associative ([IE]
+ * section 3.2), so the result is exact and independent of their order.
+ *   y  device int64[rows], 8-byte aligned, read and written; the caller keeps
+ *      |y + W x| below 2^63 ([IE] section 3.4: the bound is the caller's,
+ *      who holds the accumulator)
+ * Concurrent calls on one y are allowed (they add); other readers of y must
+ * be ordered after the call.  Errors as bs_ternary_gemv.
+ */
+int32_t bs_ternary_gemv_acc(const uint8_t *planes, const int16_t *scales, const int8_t *x,
+                            int64_t rows, int64_t k, int32_t frac, int64_t *y, void *stream);
+
+
 /* ======================================================================== */
 /* bs_q1_gemv -- Q1_0 weight apply ([IE] section 4.1)                        */
 /* ======================================================================== */

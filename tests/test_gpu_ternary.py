@@ -120,3 +120,54 @@ def test_determinism():
 def test_k_beyond_one_lds_chunk(k):
     """K larger than the activation planes one workgroup keeps in LDS."""
     check(*synth.ternary(80, k, seed=k, p_zero=1 / 3, act="uniform127"))
+
+
+def check_acc(t, sc, x, frac=0, times=1, seed=0):
+    """y0 + times * (W x) through bs_ternary_gemv_acc, against the oracle."""
+    import torch
+    dev = device()
+    rows, k = t.shape
+    y0 = np.random.default_rng(seed).integers(-(1 << 50), 1 << 50, rows).astype(np.int64)
+    planes = to_dev(bs.ternary_pack(t), dev)
+    scales = to_dev(bs.ternary_pack_scales(sc), dev)
+    xd = to_dev(x, dev)
+    y = to_dev(y0, dev)
+    note("ternary_gemv_acc rows=%d k=%d frac=%d times=%d" % (rows, k, frac, times))
+    for _ in range(times):
+        bs.ternary_gemv_acc(planes, scales, xd, rows, k, y, frac)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    want = y0 + times * oracle.ternary_gemv_def(t, sc, x, frac)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, "first mismatch row %d: got %d want %d (%d bad)" % (
+        bad[0], got[bad[0]], want[bad[0]], bad.size)
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("rows,k", [(2560, 2560), (2560, 6912), (640, 2560), (3840, 2560),
+                                    (13824, 2560), (6912, 2560)])
+def test_acc_bitnet2b_shapes(rows, k, seed):
+    """y += W x on the decode layer's shapes (o and down add into the residual)."""
+    check_acc(*synth.ternary(rows, k, seed), seed=seed)
+
+
+@pytest.mark.parametrize("shape", synth.LARGE_K_SHAPES)
+def test_acc_large_k(shape):
+    check_acc(*synth.ternary(shape[0], shape[1], 1), seed=1)
+
+
+@pytest.mark.parametrize("rows,k", [(1, 128), (63, 128), (65, 256), (130, 384), (200, 12800),
+                                    (80, 128 * 450), (9700, 640), (13800, 2560)])
+def test_acc_ragged_and_repeated(rows, k):
+    t, sc, x = synth.ternary(rows, k, seed=rows + k, p_zero=1 / 3, act="uniform127")
+    check_acc(t, sc, x, times=3, seed=rows)
+
+
+@pytest.mark.parametrize("frac", [0, 3, 31, 62])
+def test_acc_frac_and_extremes(frac):
+    t, _, x = synth.ternary(2560, 1280, seed=frac, p_zero=1 / 3, act="uniform127")
+    sc = np.random.default_rng(frac).integers(-32768, 32768, (2560, 10)).astype(np.int16)
+    check_acc(t, sc, x, frac, seed=frac)
+    rows, k = 640, 2560
+    check_acc(-np.ones((rows, k), np.int8), np.full((rows, 20), -32768, np.int16),
+              np.full(k, -128, np.int8), frac, times=2)
