@@ -283,8 +283,10 @@ __global__ void ternary_tile_kernel(const uint8_t *__restrict__ planes,
     const int nwaves = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int tile = blockIdx.x / nruns, run = blockIdx.x % nruns;
-    const int g0 = run * cg, g1 = min(groups, g0 + cg);
+    // the storing kernel's one run per tile needs no division
+    const int tile = ACC ? (int)blockIdx.x / nruns : (int)blockIdx.x;
+    const int g0 = ACC ? ((int)blockIdx.x - tile * nruns) * cg : 0;
+    const int g1 = ACC ? min(groups, g0 + cg) : groups;
     const int row = tile * 64 + lane;
     const bool live = row < rows;
     int64_t acc = 0;
