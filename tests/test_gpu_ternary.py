@@ -171,3 +171,26 @@ def test_acc_frac_and_extremes(frac):
     rows, k = 640, 2560
     check_acc(-np.ones((rows, k), np.int8), np.full((rows, 20), -32768, np.int16),
               np.full(k, -128, np.int8), frac, times=2)
+
+
+@pytest.mark.parametrize("rows,k", [(13824, 2560), (2560, 6912), (640, 2560), (11008, 4096),
+                                    (5120, 13824)])
+def test_launch_geometry_invariance(rows, k):
+    """The storing kernels (row blocks or one workgroup per tile) and the
+    accumulating kernel (runs of groups over many workgroups, atomics) split
+    the same sum differently; integer addition makes their bytes identical
+    (integer-engine page, sections 3.2 and 11)."""
+    import torch
+    dev = device()
+    t, sc, x = synth.ternary(rows, k, seed=rows % 97)
+    planes = to_dev(bs.ternary_pack(t), dev)
+    scales = to_dev(bs.ternary_pack_scales(sc), dev)
+    xd = to_dev(x, dev)
+    note("launch geometry rows=%d k=%d" % (rows, k))
+    y_store = bs.ternary_gemv(planes, scales, xd, rows, k)
+    y_acc = torch.zeros(rows, dtype=torch.int64, device=dev)
+    bs.ternary_gemv_acc(planes, scales, xd, rows, k, y_acc)
+    torch.cuda.synchronize()
+    a, b = y_store.cpu().numpy(), y_acc.cpu().numpy()
+    assert a.tobytes() == b.tobytes()
+    assert (a == oracle.ternary_gemv_def(t, sc, x)).all()
