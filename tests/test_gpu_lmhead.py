@@ -142,3 +142,8 @@ def test_more_filter_regions_than_one_pass(zero):
     idx, sc, n, capped = check(trits, rs, h, 40, 200)
     if zero:
         assert n == V and (idx == np.arange(40)).all()
+
+
+def test_max_dim():
+    """dim = 10112, the largest the int64 score bound allows (79 groups)."""
+    check(*synth.lmhead(300, 10112, 17), 40, 200)

@@ -66,3 +66,9 @@ def test_extremes():
         xo = np.zeros(k, np.int8)
         xo[i] = 1
         check(s, sc, xo)
+
+
+def test_max_k():
+    """K = 2^24, the largest the int64 accumulation bound allows."""
+    s, sc, x = synth.q1(1, 1 << 24, 24)
+    check(s, np.full_like(sc, -32768), x)

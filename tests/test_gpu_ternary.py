@@ -194,3 +194,14 @@ def test_launch_geometry_invariance(rows, k):
     a, b = y_store.cpu().numpy(), y_acc.cpu().numpy()
     assert a.tobytes() == b.tobytes()
     assert (a == oracle.ternary_gemv_def(t, sc, x)).all()
+
+
+def test_max_k():
+    """K = 2^24, the largest the int64 accumulation bound allows: one row, the
+    storing and the accumulating kernels."""
+    k = 1 << 24
+    t, sc, x = synth.ternary(1, k, seed=24, p_zero=1 / 3, act="uniform127")
+    sc = np.full_like(sc, -32768)
+    x[::3] = -128
+    check(t, sc, x)
+    check_acc(t, sc, x, seed=24)
