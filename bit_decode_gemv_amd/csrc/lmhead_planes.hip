@@ -11,16 +11,17 @@
 // products: four products per v_dot4 instruction instead of bit-plane
 // popcounts.  Four kernels on one stream, no host synchronisation, no global
 // atomics:
-//   stage1  -- 16 wavefronts per workgroup over 8 tiles of 64 rows (lane =
-//              row), two wavefronts per tile splitting the groups; D03 is
-//              streamed with 16-byte non-temporal loads (two groups in flight
-//              per wavefront) against h read through the scalar path.  Writes
-//              E1 and the lower bound L per row, and the largest L of every
-//              tile and of every workgroup;
+//   stage1  -- 16 wavefronts per workgroup over 4 tiles of 64 rows (lane =
+//              row), four wavefronts per tile splitting the groups; D03 is
+//              streamed with 16-byte non-temporal loads (one 8 KiB group of a
+//              tile per wavefront step) against h read through the scalar
+//              path.  Writes E1 and the lower bound L per row, and the
+//              largest L of every tile and of every workgroup;
 //   select  -- one workgroup: L_k = the top_k-th largest L.  The top_k-th
-//              largest workgroup maximum T is a lower bound on L_k (top_k
-//              distinct rows reach it), so only the rows >= T of the tiles
-//              whose maximum reaches T take part, usually a few dozen;
+//              largest maximum T over blocks of 8 tiles is a lower bound on
+//              L_k (top_k distinct rows reach it), so only the rows >= T of
+//              the tiles whose maximum reaches T take part, usually a few
+//              dozen;
 //   filter  -- every row with U >= L_k becomes a candidate, is rescored at
 //              once (E2 from D47, the wavefront's lanes over its candidates'
 //              16-byte runs) and is stored in its workgroup's region of the
@@ -36,9 +37,9 @@
 namespace bs {
 namespace {
 
-constexpr int kTilesPerBlock = 8;
-constexpr int kWavesPerTile = 2;
-constexpr int kStage1Rows = kTilesPerBlock * 64;                       // 512
+constexpr int kTilesPerBlock = 4;
+constexpr int kWavesPerTile = 4;
+constexpr int kStage1Rows = kTilesPerBlock * 64;                       // 256
 constexpr int kStage1Threads = kTilesPerBlock * kWavesPerTile * 64;    // 1024
 constexpr int kFilterRows = 256;                                       // 4 tiles
 constexpr int kBlockThreads = 1024;     // select and finish
@@ -129,29 +130,15 @@ __global__ __launch_bounds__(kStage1Threads) void lmh_stage1(
     int e1 = 0;
     if (tile < tiles) {
         const uint8_t *tbase = planes03 + (size_t)tile * groups * 8192 + 16 * lane;
-        // this wavefront takes groups half, half + 2, ...; two in flight
-        for (int g0 = half; g0 < groups; g0 += 2 * kWavesPerTile) {
-            const int g1 = g0 + kWavesPerTile;
-            const bool has1 = g1 < groups;
-            uint4 a[8], b[8];
+        // this wavefront takes groups half, half + kWavesPerTile, ...
+        for (int g = half; g < groups; g += kWavesPerTile) {
+            uint4 a[8];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) a[c] = load_stream16(tbase + (size_t)g0 * 8192 + 1024 * c);
-            if (has1) {
-#pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    b[c] = load_stream16(tbase + (size_t)g1 * 8192 + 1024 * c);
-            }
-            const int32_t *ha0 = hw + g0 * 32;      // uniform: scalar loads
+            for (int c = 0; c < 8; ++c) a[c] = load_stream16(tbase + (size_t)g * 8192 + 1024 * c);
+            const int32_t *hg = hw + g * 32;      // uniform: scalar loads
 #pragma unroll
             for (int c = 0; c < 8; ++c)
-                e1 = dot16(a[c], ha0[4 * c], ha0[4 * c + 1], ha0[4 * c + 2], ha0[4 * c + 3], e1);
-            if (has1) {
-                const int32_t *hb0 = hw + g1 * 32;
-#pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    e1 = dot16(b[c], hb0[4 * c], hb0[4 * c + 1], hb0[4 * c + 2], hb0[4 * c + 3],
-                               e1);
-            }
+                e1 = dot16(a[c], hg[4 * c], hg[4 * c + 1], hg[4 * c + 2], hg[4 * c + 3], e1);
         }
     }
     // sum|h| (h is in the caches by now)
@@ -414,15 +401,22 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
         n_t = 0;
         n_l = 0;
     }
-    // T: the top_k-th largest workgroup maximum (0 when there are fewer
-    // workgroups than top_k, which keeps every row)
+    // T: the top_k-th largest maximum over blocks of two stage-1 workgroups
+    // (0 when there are fewer blocks than top_k, which keeps every row).
+    // Pairing keeps the ranked set at one key per 8 tiles.
+    const int nblk = (nwg + 1) / 2;
+    auto blk_key = [&](int i) {
+        const unsigned long long a = okey(ws.wg_max[2 * i]);
+        const unsigned long long b = 2 * i + 1 < nwg ? okey(ws.wg_max[2 * i + 1]) : 0ull;
+        return a > b ? a : b;
+    };
     unsigned long long thr = 0;
-    if (nwg >= top_k) {
-        if (nwg <= (int)blockDim.x)
-            thr = rank_select_desc(nwg, top_k, t < nwg ? okey(ws.wg_max[t]) : 0ull, list, rk, &res);
+    if (nblk >= top_k) {
+        if (nblk <= (int)blockDim.x)
+            thr = rank_select_desc(nblk, top_k, t < nblk ? blk_key(t) : 0ull, list, rk, &res);
         else
             thr = radix_select_desc<4>(
-                nwg, (unsigned long long)top_k, [&](int i, int) { return okey(ws.wg_max[i]); },
+                nblk, (unsigned long long)top_k, [&](int i, int) { return blk_key(i); },
                 [](int, int) { return true; }, sh);
     }
     __syncthreads();

@@ -59,72 +59,75 @@ __device__ __forceinline__ uint64_t transpose8x8(uint64_t q) {
     return q;
 }
 
+__device__ __forceinline__ uint32_t word(const uint4 &v, int d) {
+    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+}
+
+// sum_b w_b sum_d popcount(f(b, d)) with plane weights w_b = 2^b for b < 7
+// and -128 for b = 7, as a Horner scheme from the top plane down: the running
+// sum doubles between planes and the four counts of a plane chain into it
+// through the count instruction's addend (plane 7 enters as -2 * its count,
+// which the six doublings that follow bring to -128).  One count per 32
+// weights and plane, plus one doubling per plane.
+template <typename F>
+__device__ __forceinline__ int weighted_plane_count(F f) {
+    int q = 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) q = bcnt_add(f(7, d), q);
+    int s = -2 * q;
+#pragma unroll
+    for (int b = 6; b >= 0; --b) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) s = bcnt_add(f(b, d), s);
+        if (b > 0) s *= 2;
+    }
+    return s;
+}
+
 // sum_i t_i x_i over one group, from the two weight planes of this lane and
-// the group's activation planes xg[0..7] (bit b of the 128 activations,
-// position i at bit i%32 of dword i/32).  With t_i = nz_i - 2 neg_i (neg a
-// subset of nz) every lane satisfies t_i * m_i = nz_i (m_i xor neg_i) - neg_i,
-// so for activation bit plane b
+// the group's activation planes (bit b of the 128 activations, position i at
+// bit i%32 of word i/32).  With t_i = nz_i - 2 neg_i (neg a subset of nz)
+// every lane satisfies t_i * m_i = nz_i (m_i xor neg_i) - neg_i, so for
+// activation bit plane b
 //   sum_i t_i m_bi = popcount(nz & (M_b ^ neg)) - popcount(neg);
 // over the plane weights w_b (2^b, and -128 for bit 7, summing to -1) the
-// popcount(neg) terms add up to + popcount(neg).
+// popcount(neg) terms add up to + popcount(neg).  xg[b] holds plane b (LDS
+// staging of the row-block kernel).
 __device__ __forceinline__ int group_dot(const uint4 &nz, const uint4 &ng,
                                          const uint4 *__restrict__ xg) {
-    int s = __builtin_popcount(ng.x) + __builtin_popcount(ng.y) + __builtin_popcount(ng.z) +
-            __builtin_popcount(ng.w);
+    int s = weighted_plane_count(
+        [&](int b, int d) { return word(nz, d) & (word(xg[b], d) ^ word(ng, d)); });
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const uint4 m = xg[b];
-        const int q = __builtin_popcount(nz.x & (m.x ^ ng.x)) +
-                      __builtin_popcount(nz.y & (m.y ^ ng.y)) +
-                      __builtin_popcount(nz.z & (m.z ^ ng.z)) +
-                      __builtin_popcount(nz.w & (m.w ^ ng.w));
-        s += (b == 7) ? -q * 128 : q * (1 << b);
-    }
+    for (int d = 0; d < 4; ++d) s = bcnt_add(word(ng, d), s);
     return s;
 }
 
 // Q1_0: 2 * pos_sum - block_total for one group; xg[8].x holds block_total.
 __device__ __forceinline__ int q1_group_dot(const uint4 &bits, const uint4 *__restrict__ xg) {
-    int pos = 0;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const uint4 m = xg[b];
-        const int q = __builtin_popcount(bits.x & m.x) + __builtin_popcount(bits.y & m.y) +
-                      __builtin_popcount(bits.z & m.z) + __builtin_popcount(bits.w & m.w);
-        pos += (b == 7) ? -q * 128 : q * (1 << b);
-    }
+    const int pos =
+        weighted_plane_count([&](int b, int d) { return word(bits, d) & word(xg[b], d); });
     return 2 * pos - (int)xg[8].x;
 }
 
 // The same two sums against scalar-register activation planes (tile
 // mapping): xp.w[b][d] is uniform across the wavefront.
 __device__ __forceinline__ int tile_dot(const uint4 &nz, const uint4 &ng, const XPlanes &xp) {
-    int s = __builtin_popcount(ng.x) + __builtin_popcount(ng.y) + __builtin_popcount(ng.z) +
-            __builtin_popcount(ng.w);
+    int s = weighted_plane_count(
+        [&](int b, int d) { return word(nz, d) & (xp.w[b][d] ^ word(ng, d)); });
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const int q = __builtin_popcount(nz.x & (xp.w[b][0] ^ ng.x)) +
-                      __builtin_popcount(nz.y & (xp.w[b][1] ^ ng.y)) +
-                      __builtin_popcount(nz.z & (xp.w[b][2] ^ ng.z)) +
-                      __builtin_popcount(nz.w & (xp.w[b][3] ^ ng.w));
-        s += (b == 7) ? -q * 128 : q * (1 << b);
-    }
+    for (int d = 0; d < 4; ++d) s = bcnt_add(word(ng, d), s);
     return s;
 }
 
 // Q1_0: 2 * pos_sum - block_total; block_total = sum_b w_b popcount(X_b) is
 // uniform, so the scalar unit counts it.
 __device__ __forceinline__ int tile_q1_dot(const uint4 &bits, const XPlanes &xp) {
-    int pos = 0, total = 0;
+    const int pos = weighted_plane_count([&](int b, int d) { return word(bits, d) & xp.w[b][d]; });
+    int total = 0;
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-        const int q = __builtin_popcount(bits.x & xp.w[b][0]) +
-                      __builtin_popcount(bits.y & xp.w[b][1]) +
-                      __builtin_popcount(bits.z & xp.w[b][2]) +
-                      __builtin_popcount(bits.w & xp.w[b][3]);
         const int t = __builtin_popcount(xp.w[b][0]) + __builtin_popcount(xp.w[b][1]) +
                       __builtin_popcount(xp.w[b][2]) + __builtin_popcount(xp.w[b][3]);
-        pos += (b == 7) ? -q * 128 : q * (1 << b);
         total += (b == 7) ? -t * 128 : t * (1 << b);
     }
     return 2 * pos - total;
@@ -273,7 +276,7 @@ __global__ void ternary_rows_kernel(const uint8_t *__restrict__ planes,
 // all of K) or added to y with one int64 atomic per row and workgroup (ACC
 // true: y += W x; the runs of a tile add in any order, exactly, since
 // integer addition is associative).  Rows past `rows` (the tile's zero
-// padding) load nothing and store nothing.
+// padding) are computed like the others and not stored.
 template <bool Q1, bool ACC>
 __global__ void ternary_tile_kernel(const uint8_t *__restrict__ planes,
                                     const int16_t *__restrict__ pscales,
@@ -289,22 +292,24 @@ __global__ void ternary_tile_kernel(const uint8_t *__restrict__ planes,
     const int g1 = ACC ? min(groups, g0 + cg) : groups;
     const int row = tile * 64 + lane;
     const bool live = row < rows;
+    // this tile's planes, its four 16-row scale blocks, and x: the group
+    // steps a uniform (scalar) offset, the lane's part is fixed
+    constexpr uint32_t kBlk = Q1 ? 1024 : 2048;
+    const __amdgpu_buffer_rsrc_t rp =
+        buffer_rsrc(planes + (size_t)tile * groups * kBlk, (uint32_t)groups * kBlk);
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(pscales + (size_t)tile * 64 * groups, (uint32_t)groups * 128);
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)groups * 128);
+    const uint32_t sc_off = (uint32_t)(((lane >> 4) * groups * 16 + (lane & 15)) * 2);
     int64_t acc = 0;
     for (int g = g0 + wave; g < g1; g += nwaves) {
-        const size_t blk = (size_t)tile * groups + g;
-        const int xa = x[(size_t)g * 128 + lane];
-        const int xb = x[(size_t)g * 128 + 64 + lane];
-        uint4 nz = make_uint4(0, 0, 0, 0), ng = make_uint4(0, 0, 0, 0);
-        int sc = 0;
-        if (live) {
-            if constexpr (Q1) {
-                nz = load_stream16(planes + blk * 1024 + 16 * lane);
-            } else {
-                nz = load_stream16(planes + blk * 2048 + 16 * lane);
-                ng = load_stream16(planes + blk * 2048 + 1024 + 16 * lane);
-            }
-            sc = pscales[((size_t)(row >> 4) * groups + g) * 16 + (row & 15)];
-        }
+        // padding rows (lane >= rows - 64 * tile) read the tile's zero rows
+        const int xa = buffer_load_i8(rx, lane, g * 128);
+        const int xb = buffer_load_i8(rx, 64 + lane, g * 128);
+        const uint4 nz = buffer_load_stream16(rp, 16 * lane, g * kBlk);
+        uint4 ng = make_uint4(0, 0, 0, 0);
+        if constexpr (!Q1) ng = buffer_load_stream16(rp, 1024 + 16 * lane, g * kBlk);
+        const int sc = buffer_load_i16(rs, sc_off, g * 32);
         XPlanes xp;
         ballot_planes(xa, xb, xp);
         const int s = Q1 ? tile_q1_dot(nz, xp) : tile_dot(nz, ng, xp);
