@@ -105,19 +105,41 @@ __device__ __forceinline__ void lns8_unit(const uint8_t *__restrict__ planes,
             A[p] += anz - 2 * ang;
         }
     } else {
+        // pneg: the lanes' positions whose product sign is negative, S1 xor
+        // [t < 0] where t != 0.  With t' = nz - 2 pneg (the product signs) and
+        // any position mask M, sum_{i in M} t'_i = popcount(nz & (M ^ pneg)) -
+        // popcount(pneg) (per position t'm = nz (m ^ pneg) - pneg, as in the
+        // ternary GEMV), so a state costs one bitop3 and one count per 32
+        // positions; the -popcount(pneg) terms of a phase's states add up to
+        // -popcount(pneg) * sum_s 2^band(s), whose sum the scalar unit keeps.
         const uint64_t sign = __ballot(b >> 7);
         const uint64_t pneg = wnz & (sign ^ wng);
+        const uint32_t nz0 = (uint32_t)wnz, nz1 = (uint32_t)(wnz >> 32);
+        uint32_t pn0 = (uint32_t)pneg, pn1 = (uint32_t)(pneg >> 32);
+        // opaque to the compiler, which would otherwise fold the nz & of
+        // pneg into nz & (M ^ sign ^ neg) and spend an xor and an and per
+        // word instead of one bitop3
+        asm volatile("" : "+v"(pn0));
+        asm volatile("" : "+v"(pn1));
+        const int npn = bcnt_add(pn1, bcnt_add(pn0, 0));
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
             uint64_t rem = __ballot(code != 0 && (code & 7) == p);
+            int sum = 0;
+            uint32_t bands = 0;   // uniform: sum of 2^band over the phase's states
             while (rem) {
                 const int first = __builtin_ctzll(rem);
                 const int st = lane_value(code, first);
                 const uint64_t as = __ballot(code == st);
                 rem &= ~as;
-                const int cs = __popcll(as & wnz) - 2 * __popcll(as & pneg);
-                A[p] += cs * (1 << (st >> 3));
+                const int band = st >> 3;
+                const int c = bcnt_add(nz1 & ((uint32_t)(as >> 32) ^ pn1),
+                                       bcnt_add(nz0 & ((uint32_t)as ^ pn0), 0));
+                sum += c << band;
+                bands += 1u << band;
             }
+            // |sum|, npn * bands <= 64 * 64 * 2^15 = 2^27
+            A[p] += sum - __mul24(npn, (int)bands);
         }
     }
 }
