@@ -46,19 +46,6 @@ __device__ __forceinline__ double materialize(const int A[8]) {
     return ldexp((double)t, -62);
 }
 
-__device__ __forceinline__ void add_phase(int A[8], int p, int v) {
-    switch (p) {
-    case 0: A[0] += v; break;
-    case 1: A[1] += v; break;
-    case 2: A[2] += v; break;
-    case 3: A[3] += v; break;
-    case 4: A[4] += v; break;
-    case 5: A[5] += v; break;
-    case 6: A[6] += v; break;
-    default: A[7] += v; break;
-    }
-}
-
 // One unit of work: 64 positions (half h of group g) for the wavefront's 64
 // rows.  Lane j holds row j's W_nonzero / W_negative bits of those positions
 // (bit i = position 64h + i) and, for the ballots, the activation byte of
