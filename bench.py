@@ -192,10 +192,15 @@ def _cpu_model():
 
 
 def _source_digest():
+    """Digest of the GEMV kernel's source: its file and the headers it
+    includes (shared device helpers, status codes, the ABI header)."""
     h = hashlib.sha256()
-    path = os.path.join(ROOT, "bit_decode_gemv_amd", "csrc", "ternary_gemv.hip")
-    with open(path, "rb") as f:
-        h.update(f.read())
+    for rel in (("bit_decode_gemv_amd", "csrc", "ternary_gemv.hip"),
+                ("bit_decode_gemv_amd", "csrc", "kcommon.h"),
+                ("bit_decode_gemv_amd", "csrc", "bs_internal.h"),
+                ("include", "bs.h")):
+        with open(os.path.join(ROOT, *rel), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 

@@ -38,8 +38,8 @@ typedef short short2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void ballot_planes(int xa, int xb, XPlanes &xp) {
     short2v p;
-    p.x = (short)(xa << 8);
-    p.y = (short)(xb << 8);
+    p.x = (short)((uint32_t)xa << 8);   // the byte's bit 7 at the 16-bit sign
+    p.y = (short)((uint32_t)xb << 8);
 #pragma unroll
     for (int b = 7; b >= 0; --b) {
         const uint64_t m0 = __ballot(p.x < 0);

@@ -59,3 +59,21 @@ def test_traffic_summary(tmp_path):
     assert float(vals["write_bytes_per_launch"]) == pytest.approx(20 * 1024)
     assert float(vals["hbm_bytes_per_launch"]) == pytest.approx(2 * 1000 * 1024 + 20 * 1024)
     assert vals["kernel_source_sha256_16"] == bench._source_digest()
+
+
+def test_source_digest_covers_included_headers(tmp_path, monkeypatch):
+    """The recorded HBM traffic is dropped once the GEMV kernel changes; a
+    change to a header the kernel includes is such a change."""
+    import shutil
+    for rel in (("bit_decode_gemv_amd", "csrc", "ternary_gemv.hip"),
+                ("bit_decode_gemv_amd", "csrc", "kcommon.h"),
+                ("bit_decode_gemv_amd", "csrc", "bs_internal.h"),
+                ("include", "bs.h")):
+        dst = tmp_path.joinpath(*rel)
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(bench.ROOT, *rel), dst)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    before = bench._source_digest()
+    with open(tmp_path / "bit_decode_gemv_amd" / "csrc" / "kcommon.h", "a") as f:
+        f.write("\n// edit\n")
+    assert bench._source_digest() != before
