@@ -754,7 +754,6 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     __shared__ int l1id[kFinList];
     __shared__ int wtot[kBlockThreads / 64];
     __shared__ unsigned int nkept, nl1;
-    __shared__ unsigned long long res;
     const int t = (int)threadIdx.x;
     const int wave = t >> 6, lane = t & 63;
     const int nwaves = kBlockThreads / 64;

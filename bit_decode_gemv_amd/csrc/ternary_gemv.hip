@@ -6,13 +6,13 @@
 // LLMs", section 4.2; the W_nonzero / W_negative planes of "BitState / HSDR
 // PoC Technical Brief - v0.5", section 4).
 //
-// Mapping.  A workgroup owns R complete rows (R = 64, 32 or 16) and all of
-// K, so no partial sum ever leaves the CU.  Its W wavefronts are split into
+// Mapping.  A workgroup owns R complete rows (R = 32 or 16) and all of K,
+// so no partial sum ever leaves the CU.  Its W wavefronts are split into
 // slices: lane l of wavefront w serves row (l mod R) of the block in slice
 // w*(64/R) + l/R, and slice s takes groups s, s + nslices, s + 2*nslices, ...
 // A lane streams the row's 16-byte W_nonzero and W_negative fields of each of
 // its groups (R lanes of a slice read R*16 contiguous bytes of the tiled
-// layout).  Work proceeds in rounds of up to MAXG groups per slice: a
+// layout).  Work proceeds in rounds of MAXG (1 or 2) groups per slice: a
 // wavefront issues the activation loads and then every weight load of the
 // round, transposes the activations of its own groups into eight bit planes
 // in a private LDS slot (no workgroup barrier: only the wavefront's own lanes
@@ -330,9 +330,9 @@ __global__ void ternary_tile_kernel(const uint8_t *__restrict__ planes,
 
 struct TernaryCfg {
     bool tile;            // tile mapping (ternary_tile_kernel) with `waves` wavefronts
-    int rows_per_block;   // R: 64, 32 or 16
+    int rows_per_block;   // R: 32 or 16 (64 for the tile mapping)
     int waves;            // wavefronts per block, 1..16
-    int maxg;             // groups per slice and round held in registers: 1, 2 or 4
+    int maxg;             // groups per slice and round held in registers: 1 or 2
 };
 
 template <int R, int G, bool Q1>
@@ -350,7 +350,6 @@ static bool launch_r(int maxg, int waves, hipStream_t st, const uint8_t *planes,
     switch (maxg) {
     case 1: launch_rg<R, 1, Q1>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
     case 2: launch_rg<R, 2, Q1>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
-    case 4: launch_rg<R, 4, Q1>(waves, st, planes, scales, x, rows, groups, shift, y); return true;
     default: return false;
     }
 }
@@ -372,7 +371,6 @@ static int32_t launch_ternary(const TernaryCfg &c, const uint8_t *planes, const 
     }
     bool ok;
     switch (c.rows_per_block) {
-    case 64: ok = launch_r<64, Q1>(c.maxg, c.waves, st, planes, scales, x, n, groups, shift, y); break;
     case 32: ok = launch_r<32, Q1>(c.maxg, c.waves, st, planes, scales, x, n, groups, shift, y); break;
     case 16: ok = launch_r<16, Q1>(c.maxg, c.waves, st, planes, scales, x, n, groups, shift, y); break;
     default: ok = false;
@@ -382,40 +380,38 @@ static int32_t launch_ternary(const TernaryCfg &c, const uint8_t *planes, const 
     return BS_OK;
 }
 
-// Launch shape, from sweeps of both mappings on MI355X: the tile mapping
-// (16 wavefronts) for tall matrices with up to 48 groups per row (150+
-// tiles at up to 24 groups, 200+ beyond); otherwise row blocks: 64-row
-// blocks when there are enough tiles to give every CU one block and rows are
-// long; otherwise 16-row blocks (four slices per wavefront) with one group
-// per slice (8 wavefronts up to 32 groups, 16 beyond), or 32-row blocks for
-// long rows with many rows.
-static TernaryCfg choose_cfg(int64_t rows, int64_t k) {
+// Launch shape, from sweeps of every (mapping, rows per block, wavefronts,
+// groups per slice) on MI355X with cold weights.  The tile mapping (16
+// wavefronts, one workgroup per 64-row tile) for tall matrices: at least
+// 150 tiles with up to 32 groups per row (Q1_0: 30), or at least 200 tiles
+// with up to 64 groups (Q1_0: 48).  Otherwise row blocks with one group per
+// slice and round (more rounds measured faster than more groups in flight
+// per round): 16-row blocks with 8 wavefronts up to 32 groups; beyond that
+// 32-row blocks with 16 wavefronts for 5000 rows or more (Q1_0, whose group
+// is half the bytes: two groups per slice), else 16-row blocks with 16.
+static TernaryCfg choose_cfg(int64_t rows, int64_t k, bool q1) {
     const int64_t groups = k / kGroup, tiles = pad64(rows) / 64;
-    auto maxg_for = [](int64_t per) { return per <= 1 ? 1 : per <= 2 ? 2 : 4; };
     TernaryCfg c;
     c.tile = false;
-    if (tiles >= 150 && groups <= 48 && (groups <= 24 || tiles >= 200)) {
+    c.maxg = 1;
+    const int64_t tile_groups = q1 ? 30 : 32, tall_groups = q1 ? 48 : 64;
+    if (tiles >= 150 && (groups <= tile_groups || (tiles >= 200 && groups <= tall_groups))) {
         c.tile = true;
         c.waves = (int)(groups < 16 ? groups : 16);
         c.rows_per_block = 64;
-        c.maxg = 1;
         return c;
     }
-    if (tiles >= 200 && groups >= 40) {
-        c.rows_per_block = 64;
-        c.waves = 16;
-    } else if (groups <= 64) {
+    if (groups <= 32) {
         c.rows_per_block = 16;
-        c.waves = groups <= 32 ? 8 : 16;
+        c.waves = 8;
     } else if (rows >= 5000) {
         c.rows_per_block = 32;
         c.waves = 16;
+        c.maxg = q1 ? 2 : 1;
     } else {
         c.rows_per_block = 16;
         c.waves = 16;
     }
-    const int64_t nslices = (int64_t)c.waves * (64 / c.rows_per_block);
-    c.maxg = maxg_for((groups + nslices - 1) / nslices);
     return c;
 }
 
@@ -469,14 +465,14 @@ extern "C" int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales,
                                    const int8_t *x, int64_t rows, int64_t k, int32_t frac,
                                    int64_t *y, void *stream) {
     if (int32_t st = gemv_check(planes, scales, x, rows, k, frac, y)) return st;
-    return launch_ternary<false>(choose_cfg(rows, k), planes, scales, x, rows, k, frac, y,
+    return launch_ternary<false>(choose_cfg(rows, k, false), planes, scales, x, rows, k, frac, y,
                                  (hipStream_t)stream);
 }
 
 extern "C" int32_t bs_q1_gemv(const uint8_t *bits, const int16_t *scales, const int8_t *x,
                               int64_t rows, int64_t k, int32_t frac, int64_t *y, void *stream) {
     if (int32_t st = gemv_check(bits, scales, x, rows, k, frac, y)) return st;
-    return launch_ternary<true>(choose_cfg(rows, k), bits, scales, x, rows, k, frac, y,
+    return launch_ternary<true>(choose_cfg(rows, k, true), bits, scales, x, rows, k, frac, y,
                                 (hipStream_t)stream);
 }
 

@@ -40,6 +40,16 @@ def test_large_k(shape):
     check(*synth.q1(shape[0], shape[1], 0))
 
 
+@pytest.mark.parametrize("rows,k", [(9600, 3840), (9601, 3968), (12800, 6144), (12801, 6272),
+                                    (4999, 4224), (5000, 4224), (5001, 12800)])
+def test_mapping_edges(rows, k):
+    """Around the Q1_0 launch-shape bounds: the tile mapping at 150 tiles up to
+    30 groups (30 and 31) and at 200 tiles up to 48 (48 and 49), the two-group
+    rounds of 32-row blocks from 5000 rows beyond 32 groups (4999 and 5000,
+    a ragged last block, and more groups than one round's slots)."""
+    check(*synth.q1(rows, k, rows ^ k))
+
+
 @pytest.mark.parametrize("rows,k", [(1, 128), (63, 128), (65, 256), (130, 384), (127, 6912),
                                     (200, 128 * 100), (80, 128 * 217), (9600, 2560),
                                     (13800, 2560), (12863, 6144), (14000, 128)])

@@ -58,11 +58,14 @@ def test_fused_launches(rows, seed):
 
 
 @pytest.mark.parametrize("rows,k", [(9600, 2560), (9601, 3072), (12800, 3200), (12863, 6144),
-                                    (13800, 2560), (12800, 640), (14000, 128)])
+                                    (13800, 2560), (12800, 640), (14000, 128),
+                                    (9536, 4096), (9600, 4096), (9601, 4224), (12800, 8192),
+                                    (12737, 8320), (4999, 4224), (5000, 4224)])
 def test_tile_mapping_edges(rows, k):
-    """Around the tall-matrix (one workgroup per 64-row tile) launch bounds:
-    150 tiles, 24 groups, 200 tiles with more groups, 48 groups, a ragged last
-    tile, fewer groups than wavefronts."""
+    """Around the launch-shape bounds: the tile mapping from 150 tiles (149
+    and 150 at 32 groups, 33 groups at 151 tiles) and at 200 tiles up to 64
+    groups (64 and 65), the row-block shapes either side of 5000 rows beyond
+    32 groups, ragged last tiles and blocks, fewer groups than wavefronts."""
     check(*synth.ternary(rows, k, seed=rows ^ k, p_zero=1 / 3, act="uniform127"))
 
 
