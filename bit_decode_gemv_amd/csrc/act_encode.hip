@@ -51,25 +51,28 @@ __device__ uint64_t block_max_u64(uint64_t v, uint64_t *red) {
     return m;
 }
 
-// floor(num / den) for num < 2^63, den > 0 and a quotient below 2^7: a
-// binary64 estimate from the reciprocal of den, settled by exact integer
-// checks (the estimate is within one of the quotient).
-__device__ __forceinline__ uint64_t small_quotient(uint64_t num, uint64_t den, double rden) {
-    int64_t q = (int64_t)((double)num * rden);
-    q = q < 0 ? 0 : (q > 200 ? 200 : q);
-    while (q > 0 && (uint64_t)q * den > num) --q;
-    while ((uint64_t)(q + 1) * den <= num) ++q;
-    return (uint64_t)q;
-}
-
 // Each thread holds up to kPerThread values in registers between the two
 // passes (max, then quantise), loaded together so their latencies overlap;
 // longer vectors stream through a loop.
 constexpr int kPerThread = 16;
 
-__device__ __forceinline__ int8_t quant_one(int64_t v, uint64_t a, double rden) {
-    const int m8 = a != 0 ? (int)small_quotient(254 * abs_u64(v) + a, 2 * a, rden) : 0;
-    return (int8_t)(v < 0 ? -m8 : m8);
+// q = floor((254 m + a) / (2a)) = floor(127 m / a + 1/2) for 0 <= m <= a <=
+// 2^55, a > 0 (so q is in [0, 127]).  Estimate: binary32 m (the high word is
+// below 2^24, so only the low word's conversion and the sum round, relative
+// error < 2^-23) times s127 = 127 / a (relative error < 2^-22) plus 1/2; the
+// product is below 128 with an error below 2^-14, so the estimate is within
+// one of q, and one exact integer check each way settles it (254 m + a and
+// 2a (q + 1) stay below 2^63).
+__device__ __forceinline__ int8_t quant_one(int64_t v, uint64_t a, float s127) {
+    if (a == 0) return 0;
+    const uint64_t m = abs_u64(v);
+    const float fm = (float)(uint32_t)(m >> 32) * 4294967296.0f + (float)(uint32_t)m;
+    int q = (int)(fm * s127 + 0.5f);
+    q = q < 0 ? 0 : (q > 127 ? 127 : q);
+    const uint64_t num = 254 * m + a, den = 2 * a;
+    const uint64_t t = den * (uint64_t)q;
+    q = t > num ? q - 1 : (t + den <= num ? q + 1 : q);
+    return (int8_t)(v < 0 ? -q : q);
 }
 
 __global__ void act_quant_kernel(const int64_t *__restrict__ x, int64_t k,
@@ -105,15 +108,15 @@ __global__ void act_quant_kernel(const int64_t *__restrict__ x, int64_t k,
         }
         return;
     }
-    const double rden = a != 0 ? 1.0 / (double)(2 * a) : 0.0;
+    const float s127 = a != 0 ? 127.0f / (float)a : 0.0f;
     if (held) {
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
             const int64_t i = threadIdx.x + (int64_t)j * blockDim.x;
-            if (i < k) q[i] = quant_one(v[j], a, rden);
+            if (i < k) q[i] = quant_one(v[j], a, s127);
         }
     } else {
-        for (int64_t i = threadIdx.x; i < k; i += blockDim.x) q[i] = quant_one(x[i], a, rden);
+        for (int64_t i = threadIdx.x; i < k; i += blockDim.x) q[i] = quant_one(x[i], a, s127);
     }
     if (threadIdx.x == 0) {
         *absmax = (int64_t)a;
