@@ -49,10 +49,17 @@ __constant__ uint32_t kSha256K[64] = {
 __constant__ uint32_t kSha256H0[8] = {0x6a09e667, 0xbb67ae85, 0x3c6ef372, 0xa54ff53a,
                                       0x510e527f, 0x9b05688c, 0x1f83d9ab, 0x5be0cd19};
 
-// Rotate right as a 64-bit shift of x:x, which the scalar unit executes
-// directly when x is wave-uniform (there is no 32-bit scalar rotate).
+// Rotate right (one v_alignbit_b32 on vector registers).
 __device__ __forceinline__ uint32_t rotr(uint32_t x, int n) {
-    return (uint32_t)(((((uint64_t)x) << 32) | x) >> n);
+    return (x >> n) | (x << (32 - n));
+}
+
+// a ^ b ^ c as one v_bitop3_b32 (truth table 0x96); the compiler would emit
+// two xors.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t r;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
 }
 
 // First 8 digest bytes (as a big-endian integer) of SHA-256 over the 20-byte
@@ -83,15 +90,15 @@ __device__ uint64_t sha256_draw(uint64_t seed, uint64_t position, uint32_t attem
             wi = w[i];
         } else {
             const uint32_t w15 = w[(i - 15) & 15], w2 = w[(i - 2) & 15];
-            const uint32_t s0 = rotr(w15, 7) ^ rotr(w15, 18) ^ (w15 >> 3);
-            const uint32_t s1 = rotr(w2, 17) ^ rotr(w2, 19) ^ (w2 >> 10);
+            const uint32_t s0 = xor3(rotr(w15, 7), rotr(w15, 18), w15 >> 3);
+            const uint32_t s1 = xor3(rotr(w2, 17), rotr(w2, 19), w2 >> 10);
             wi = w[i & 15] + s0 + w[(i - 7) & 15] + s1;
             w[i & 15] = wi;
         }
-        const uint32_t S1 = rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 25);
+        const uint32_t S1 = xor3(rotr(e, 6), rotr(e, 11), rotr(e, 25));
         const uint32_t ch = (e & f) ^ (~e & g);
         const uint32_t t1 = h + S1 + ch + kSha256K[i] + wi;
-        const uint32_t S0 = rotr(a, 2) ^ rotr(a, 13) ^ rotr(a, 22);
+        const uint32_t S0 = xor3(rotr(a, 2), rotr(a, 13), rotr(a, 22));
         const uint32_t mj = (a & b) ^ (a & c) ^ (b & c);
         const uint32_t t2 = S0 + mj;
         h = g; g = f; f = e; e = d + t1;
@@ -181,23 +188,29 @@ __global__ void sample_kernel(const int32_t *__restrict__ idx, const int64_t *__
     const int kept = kept_sh;
     const uint64_t total = cum[kept - 1];
     if (t < 64) {
-        // the whole first wavefront runs the draw on wave-uniform values, so
-        // the digest rounds go to the scalar unit
-        const uint64_t tot = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(total >> 32)) << 32) |
-                             (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)total);
-        uint64_t v = UINT64_MAX;
-        int used = 0;
-        for (int a = 0; a < kMaxDraws; ++a) {
-            const uint64_t u = sha256_draw(seed, position, (uint32_t)a);
-            const uint64_t lo = u * tot;
-            used = a + 1;
-            if (lo < tot && lo < ((uint64_t)0 - tot) % tot) continue;   // rejected
-            v = __umul64hi(u, tot);
-            break;
+        // lane a of the first wavefront hashes attempt a (one digest's
+        // rounds on the vector unit: rotates, three-input xors and the
+        // choose/majority functions are one instruction each there); the
+        // first attempt that Lemire's method accepts is the draw, and the
+        // attempts it used are its index + 1, as if taken one by one
+        const uint64_t tot = total;
+        const uint64_t u = sha256_draw(seed, position, (uint32_t)t);
+        const uint64_t lo = u * tot;
+        bool reject = lo < tot;
+        if (__ballot(reject)) {
+            const uint64_t thr = ((uint64_t)0 - tot) % tot;   // uniform; needed rarely
+            reject = reject && lo < thr;
         }
+        const uint64_t ok = __ballot(!reject && t < kMaxDraws);
+        // every lane computes its bounded value, so the accepted lane's can be
+        // read from the whole wavefront
+        const uint64_t hi = __umul64hi(u, tot);
+        const int first = ok ? __builtin_ctzll(ok) : 0;
+        const uint32_t vlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)hi, first);
+        const uint32_t vhi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(hi >> 32), first);
         if (t == 0) {
-            draw_sh = v;
-            used_sh = used;
+            draw_sh = ok ? ((uint64_t)vhi << 32) | vlo : UINT64_MAX;
+            used_sh = ok ? first + 1 : kMaxDraws;
             pick_sh = -1;
         }
     }

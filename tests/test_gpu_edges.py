@@ -181,3 +181,22 @@ def test_sampler_after_lmhead():
     for p, o in enumerate(outs):
         assert o.cpu().numpy().tolist() == _want(widx, wsc, oe.SAMPLE_DRAW, beta=1 << 4, seed=9,
                                                  position=p)
+
+
+def test_sampler_rejected_first_draw():
+    """Keys whose first draw is rejected (tests/golden/sampler_rejection.json):
+    the kernel hashes the attempts in parallel lanes and must report the
+    second attempt's value and two attempts used, as the oracle does."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "sampler_rejection.json")
+    with open(path) as f:
+        g = json.load(f)
+    idx = np.arange(g["first_index"], g["first_index"] + g["n"], dtype=np.int32)
+    score = np.full(g["n"], g["score"], np.int64)
+    for c in g["cases"]:
+        want = _want(idx, score, oe.SAMPLE_DRAW, beta=0, seed=c["seed"], position=c["position"])
+        got = _sample(idx, score, mode=bs.SAMPLE_DRAW, beta_q16=0, seed=c["seed"],
+                      position=c["position"])
+        assert got == want
+        assert got[5] == c["attempts"] == 2 and got[4] == c["draw"]

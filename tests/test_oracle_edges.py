@@ -226,3 +226,26 @@ def test_draw_distribution_follows_weights():
     p = np.array([8, 4, 2, 1]) / 15.0
     chi2 = float(((counts - n * p) ** 2 / (n * p)).sum())
     assert chi2 < 16.3          # 3 degrees of freedom, p = 0.001
+
+
+def test_sampler_rejection_golden():
+    """tests/golden/sampler_rejection.json (written by make_sampler_rejection.py
+    beside it): keys whose first draw Lemire's method rejects.  2^33 = -1 mod 683,
+    so 2^64 mod (683 * 2^31) = 682 * 2^31, and each key's first draw falls
+    below it."""
+    import json
+    path = os.path.join(os.path.dirname(__file__), "golden", "sampler_rejection.json")
+    with open(path) as f:
+        g = json.load(f)
+    total = g["n"] << 31
+    assert g["total"] == total and pow(2, 33, 683) == 682
+    assert (1 << 64) % total == 682 << 31
+    idx = list(range(g["first_index"], g["first_index"] + g["n"]))
+    for c in g["cases"]:
+        lo = (edges.draw_u64(c["seed"], c["position"], 0) * total) % (1 << 64)
+        assert lo < (1 << 64) % total                     # the first attempt is rejected
+        o = edges.sample_candidates(idx, [g["score"]] * g["n"], edges.SAMPLE_DRAW, beta=0,
+                                    seed=c["seed"], position=c["position"])
+        assert (o["attempts"], o["draw"], o["token"], o["rank"]) == (
+            c["attempts"], c["draw"], c["token"], c["rank"])
+        assert o["draw"] == (edges.draw_u64(c["seed"], c["position"], 1) * total) >> 64
