@@ -118,20 +118,28 @@ __device__ __forceinline__ Node join(Node a, Node b, const E *__restrict__ lut, 
 }
 
 // Per-lane state of one Tile128: the two activation codes each lane holds
-// (positions lane and 64 + lane) and the row's positive / negative product
-// masks of the two halves.
+// (positions lane and 64 + lane), the row's non-zero weights nz and its
+// negative products neg (a subset of nz) as four 32-bit words (positions
+// 0-31, 32-63, 64-95, 96-127), and popcount(neg).
 struct TileState {
     int code0, code1;
-    uint64_t pos0, neg0, pos1, neg1;
+    uint32_t nz[4], neg[4];
+    int nneg;
 };
 
 // Signed population of code c in the wavefront's Tile128 (per lane = row);
-// the caller has checked that the tile holds code c.
+// the caller has checked that the tile holds code c.  With the product
+// signs t' = nz - 2 neg, sum_{i in M} t'_i = popcount(nz & (M ^ neg)) -
+// popcount(neg) for any position mask M (per position t'm = nz (m ^ neg) -
+// neg): one bitop3 and one chained count per 32 positions.
 __device__ __forceinline__ int population(int c, const TileState &ts) {
     const uint64_t m0 = __ballot(ts.code0 == c);
     const uint64_t m1 = __ballot(ts.code1 == c);
-    return __popcll(m0 & ts.pos0) - __popcll(m0 & ts.neg0) + __popcll(m1 & ts.pos1) -
-           __popcll(m1 & ts.neg1);
+    int s = bcnt_add(ts.nz[0] & ((uint32_t)m0 ^ ts.neg[0]), 0);
+    s = bcnt_add(ts.nz[1] & ((uint32_t)(m0 >> 32) ^ ts.neg[1]), s);
+    s = bcnt_add(ts.nz[2] & ((uint32_t)m1 ^ ts.neg[2]), s);
+    s = bcnt_add(ts.nz[3] & ((uint32_t)(m1 >> 32) ^ ts.neg[3]), s);
+    return s - ts.nneg;
 }
 
 // Final encoding: scale, then (sign, L).
@@ -201,18 +209,20 @@ __global__ __launch_bounds__(1024) void flns_tile_kernel(
 #pragma unroll
         for (int w = 0; w < 4; ++w) pres[w] = __builtin_amdgcn_readfirstlane(s_present[slot][w]);
         const uint64_t s0 = __ballot(b0 >> 7), s1 = __ballot(b1 >> 7);
-        const uint64_t nz0 = (uint64_t)nz.x | ((uint64_t)nz.y << 32);
-        const uint64_t nz1 = (uint64_t)nz.z | ((uint64_t)nz.w << 32);
-        const uint64_t ng0 = (uint64_t)ng.x | ((uint64_t)ng.y << 32);
-        const uint64_t ng1 = (uint64_t)ng.z | ((uint64_t)ng.w << 32);
         TileState ts;
         ts.code0 = b0 & 0x7F;
         ts.code1 = b1 & 0x7F;
         // a product is negative iff S1 xor [t < 0]
-        ts.neg0 = nz0 & (s0 ^ ng0);
-        ts.pos0 = nz0 & ~(s0 ^ ng0);
-        ts.neg1 = nz1 & (s1 ^ ng1);
-        ts.pos1 = nz1 & ~(s1 ^ ng1);
+        ts.nz[0] = nz.x; ts.nz[1] = nz.y; ts.nz[2] = nz.z; ts.nz[3] = nz.w;
+        ts.neg[0] = nz.x & ((uint32_t)s0 ^ ng.x);
+        ts.neg[1] = nz.y & ((uint32_t)(s0 >> 32) ^ ng.y);
+        ts.neg[2] = nz.z & ((uint32_t)s1 ^ ng.z);
+        ts.neg[3] = nz.w & ((uint32_t)(s1 >> 32) ^ ng.w);
+        // opaque to the compiler, which would otherwise fold the nz & into
+        // each state's mask and spend an xor and an and per word
+#pragma unroll
+        for (int w = 0; w < 4; ++w) asm volatile("" : "+v"(ts.neg[w]));
+        ts.nneg = bcnt_add(ts.neg[3], bcnt_add(ts.neg[2], bcnt_add(ts.neg[1], bcnt_add(ts.neg[0], 0))));
 #pragma unroll 1
         for (int p = 4 * half; p < 4 * half + 4; ++p) {
             // the bands present in the tile (code 8b + p; code 0 is never
