@@ -217,9 +217,9 @@ def _stream_handle(stream, device):
 
 class Workspace:
     """Zero-filled device scratch, one per (entry point, device), grown on
-    demand.  Every entry point writes each workspace byte before reading it,
-    so one buffer serves every call of that entry point ordered on one
-    stream; entry points never share a buffer."""
+    demand.  No entry point's result depends on a workspace byte the same
+    call did not write, so one buffer serves every call of that entry point
+    ordered on one stream; entry points never share a buffer."""
 
     _cache = {}
 

@@ -45,6 +45,7 @@ constexpr int kFilterRows = 256;                                       // 4 tile
 constexpr int kBlockThreads = 1024;     // select and finish
 constexpr int kSelTiles = 1024;         // select: tiles gathered
 constexpr int kSelList = 4096;          // select: pruned bounds kept in LDS
+constexpr int kSelPre = 2;              // select: tile maxima per thread loaded up front
 constexpr int kFinList = 512;           // finish: pruned candidates kept in LDS
 constexpr int kFinKpt = 4;              // finish fallback: candidates per thread in registers
 constexpr int kMaxCap = 4096;
@@ -401,6 +402,14 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
         n_t = 0;
         n_l = 0;
     }
+    // the first kSelPre * blockDim tile maxima, loaded now so their latency
+    // overlaps the workgroup maxima's and the threshold selection
+    unsigned long long tpre[kSelPre];
+#pragma unroll
+    for (int u = 0; u < kSelPre; ++u) {
+        const int tt = u * (int)blockDim.x + t;
+        tpre[u] = tt < tiles ? okey(ws.tile_max[tt]) : 0ull;
+    }
     // T: the top_k-th largest maximum over blocks of two stage-1 workgroups
     // (0 when there are fewer blocks than top_k, which keeps every row).
     // Pairing keeps the ranked set at one key per 8 tiles.
@@ -421,12 +430,17 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
     }
     __syncthreads();
     // the tiles whose maximum reaches T
-    for (int c0 = 0; c0 < tiles; c0 += (int)blockDim.x) {
-        const int tt = c0 + t;
-        if (tt < tiles && okey(ws.tile_max[tt]) >= thr) {
+    auto take_tile = [&](int tt, unsigned long long key) {
+        if (tt < tiles && key >= thr) {
             const unsigned slot = atomicAdd(&n_t, 1u);
             if (slot < (unsigned)kSelTiles) tlist[slot] = tt;
         }
+    };
+#pragma unroll
+    for (int u = 0; u < kSelPre; ++u) take_tile(u * (int)blockDim.x + t, tpre[u]);
+    for (int c0 = kSelPre * (int)blockDim.x; c0 < tiles; c0 += (int)blockDim.x) {
+        const int tt = c0 + t;
+        take_tile(tt, tt < tiles ? okey(ws.tile_max[tt]) : 0ull);
     }
     __syncthreads();
     const int nt = (int)n_t;
@@ -758,6 +772,10 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     const int wave = t >> 6, lane = t & 63;
     const int nwaves = kBlockThreads / 64;
 
+    // region t's head (its largest S1'), loaded beside the counts so the
+    // cap bound below waits on no further load; an empty region's slot holds
+    // an earlier call's bytes and is not used
+    const long long head_pre = t < nwf ? ws.cand_s1[(size_t)t * kFilterRows] : 0;
     // exclusive prefix sums of the region counts, 1024 regions at a time
     int n = 0;
     for (int r0 = 0; r0 < nwf; r0 += kBlockThreads) {
@@ -828,8 +846,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
         const int nne = __syncthreads_count(nonempty);
         unsigned long long thr = 0;
         if (nne >= cap) {
-            const unsigned long long head =
-                nonempty ? okey(ws.cand_s1[(size_t)t * kFilterRows]) : 0ull;
+            const unsigned long long head = nonempty ? okey(head_pre) : 0ull;
             thr = radix_select_desc<1>(
                 nwf, (unsigned long long)cap, [&](int, int) { return head; },
                 [&](int, int) { return nonempty; }, sh);
