@@ -134,9 +134,20 @@ __global__ void sample_kernel(const int32_t *__restrict__ idx, const int64_t *__
     __shared__ uint64_t draw_sh;
     __shared__ int kept_sh, pick_sh, used_sh;
     const int t = threadIdx.x;
+    int64_t my_s = 0;
+    int32_t my_i = 0;
     if (t < n) {
-        s_in[t] = score[t];
-        i_in[t] = idx[t];
+        my_s = score[t];
+        my_i = idx[t];
+    }
+    // The draw sources do not depend on the candidates: lane a of the first
+    // wavefront hashes attempt a (SHA-256 of seed, position, a) while the
+    // candidate loads are in flight.
+    uint64_t u = 0;
+    if (mode != 0 && t < 64) u = sha256_draw(seed, position, (uint32_t)t);
+    if (t < n) {
+        s_in[t] = my_s;
+        i_in[t] = my_i;
     }
     __syncthreads();
     if (t < n) {
@@ -188,13 +199,12 @@ __global__ void sample_kernel(const int32_t *__restrict__ idx, const int64_t *__
     const int kept = kept_sh;
     const uint64_t total = cum[kept - 1];
     if (t < 64) {
-        // lane a of the first wavefront hashes attempt a (one digest's
-        // rounds on the vector unit: rotates, three-input xors and the
-        // choose/majority functions are one instruction each there); the
-        // first attempt that Lemire's method accepts is the draw, and the
-        // attempts it used are its index + 1, as if taken one by one
+        // lane a holds attempt a's source (its digest's rounds ran on the
+        // vector unit: rotates, three-input xors and the choose/majority
+        // functions are one instruction each there); the first attempt that
+        // Lemire's method accepts is the draw, and the attempts it used are
+        // its index + 1, as if taken one by one
         const uint64_t tot = total;
-        const uint64_t u = sha256_draw(seed, position, (uint32_t)t);
         const uint64_t lo = u * tot;
         bool reject = lo < tot;
         if (__ballot(reject)) {
