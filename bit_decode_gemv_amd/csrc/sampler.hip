@@ -151,13 +151,22 @@ __global__ void sample_kernel(const int32_t *__restrict__ idx, const int64_t *__
     }
     __syncthreads();
     if (t < n) {
-        const int64_t s = s_in[t];
-        const int32_t id = i_in[t];
+        const int64_t s = my_s;
+        const int32_t id = my_i;
+        auto beats = [&](int64_t sj, int32_t ij, int j) {
+            return (sj > s) || (sj == s && (ij < id || (ij == id && j < t)));
+        };
         int r = 0;
-        for (int j = 0; j < n; ++j) {
-            const int64_t sj = s_in[j];
-            const int32_t ij = i_in[j];
-            r += (sj > s) || (sj == s && (ij < id || (ij == id && j < t)));
+        if (blockDim.x == 64) {
+            // one wavefront: candidate j straight from lane j's registers
+            for (int j = 0; j < n; ++j) {
+                const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)my_s, j);
+                const uint32_t hi =
+                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)my_s >> 32), j);
+                r += beats((int64_t)(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readlane(my_i, j), j);
+            }
+        } else {
+            for (int j = 0; j < n; ++j) r += beats(s_in[j], i_in[j], j);
         }
         s_rk[r] = s;
         i_rk[r] = id;
