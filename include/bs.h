@@ -101,9 +101,11 @@ int32_t bs_ternary_pack_scales(const int16_t *scales, int64_t rows, int64_t k,
  * (the masked signed sum: zero weights drop out), computed exactly:
  * |s| <= 2^14, |scale*s| <= 2^29 (int32), y accumulated in int64.
  *
- *   planes  device, packed planes (layout above), bs_ternary_planes_bytes,
- *           16-byte aligned
- *   scales  device, packed int16 scales (layout above), 2-byte aligned
+ *   planes  device, packed planes (layout above), all
+ *           bs_ternary_planes_bytes of them (the kernels read the padding
+ *           rows of the last tile), 16-byte aligned
+ *   scales  device, packed int16 scales (layout above), all
+ *           bs_ternary_scales_count of them, 2-byte aligned
  *   x       device, int8[k] activations (two's complement, -128 allowed),
  *           8-byte aligned
  *   rows    >= 1;  k >= 128, k % 128 == 0, k <= 2^24
