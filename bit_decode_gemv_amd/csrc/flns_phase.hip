@@ -378,7 +378,6 @@ extern "C" int32_t bs_flns_phase_gemv(const uint8_t *planes, const uint8_t *x_ln
     const int64_t groups = k / kGroup;
     const int nsplit = (int)flns_nsplit(k);
     // both grids within the 2^32 threads of one launch
-    // both grids within the 2^32 threads of one launch
     if (tiles * nsplit * kWavesPerWg * 64 >= ((int64_t)1 << 32) ||
         rows * 64 >= ((int64_t)1 << 32))
         return BS_E_SHAPE;
