@@ -15,23 +15,28 @@
 //              row), four wavefronts per tile splitting the groups; D03 is
 //              streamed with 16-byte non-temporal loads (one 8 KiB group of a
 //              tile per wavefront step) against h read through the scalar
-//              path.  Writes E1 and the lower bound L per row, and the
-//              largest L of every tile and of every workgroup;
+//              path.  Writes E1 and the lower bound L per row, the largest L
+//              of every tile and of every workgroup, and the largest S1' of
+//              every tile;
 //   select  -- one workgroup: L_k = the top_k-th largest L.  The top_k-th
 //              largest maximum T over blocks of 8 tiles is a lower bound on
 //              L_k (top_k distinct rows reach it), so only the rows >= T of
 //              the tiles whose maximum reaches T take part, usually a few
-//              dozen;
-//   filter  -- every row with U >= L_k becomes a candidate, is rescored at
-//              once (E2 from D47, the wavefront's lanes over its candidates'
-//              16-byte runs) and is stored in its workgroup's region of the
-//              candidate arrays, sorted by (S1' desc, row asc).  Rows that the
-//              cap later drops are rescored for nothing, one read of their
-//              D47 row, which keeps the pass single;
+//              dozen.  Then T1, a lower bound on the max_candidates-th largest
+//              S1' from a histogram of the tiles' S1' maxima: when T1 >= L_k
+//              every row with S1' >= T1 is a candidate and the cap lies among
+//              them;
+//   filter  -- every row with U >= L_k becomes a candidate; those with
+//              S1' >= T1 (all of them when select found no T1) are rescored
+//              at once (E2 from D47, the wavefront's lanes over its
+//              candidates' 16-byte runs) and stored in the workgroup's region
+//              of the candidate arrays, sorted by (S1' desc, row asc);
 //   finish  -- one workgroup: the cap (the max_candidates candidates with the
-//              largest S1', lowest row first; the max_candidates-th largest
-//              region head bounds it from below, so only region prefixes are
-//              read), then the top_k of the kept rows by (S' desc, row asc).
+//              largest S1', lowest row first) among the stored rows (when
+//              there are more than fit one LDS list, the max_candidates-th
+//              largest region head bounds it from below, so only region
+//              prefixes are read), then the top_k of the kept rows by
+//              (S' desc, row asc).
 #include "kcommon.h"
 
 namespace bs {
@@ -101,12 +106,15 @@ __device__ __forceinline__ int abs_bytes(int v) {
 }
 
 struct LmhWs {
-    long long *scalars;     // [0] = L_k, [1] = sum|h|
+    long long *scalars;     // [0] = L_k, [1] = sum|h|, [2] = T1: candidates with S1' < T1
+                            // are not rescored (kNoRow: every candidate is)
     int *e1;                // [V] E1
     long long *lower;       // [V] L
     long long *tile_max;    // [tiles] largest L of each 64-row tile
     long long *wg_max;      // [nwg] largest L of each stage-1 workgroup
+    long long *tile_max_s1; // [tiles] largest S1' of each 64-row tile
     int *region_count;      // [nwf] candidates per filter workgroup
+    int *region_kept;       // [nwf] candidates rescored and stored per filter workgroup
     int *cand;              // [nwf * 256] candidate rows, per-workgroup regions
     long long *cand_s1;     // [nwf * 256] their S1'
     long long *cand_s;      // [nwf * 256] their S'
@@ -161,22 +169,28 @@ __global__ __launch_bounds__(kStage1Threads) void lmh_stage1(
         int tot = 0;
 #pragma unroll
         for (int w = 0; w < kWavesPerTile; ++w) tot += e1_part[tl * kWavesPerTile + w][lane];
-        long long lower = kNoRow;
+        long long lower = kNoRow, s1 = kNoRow;
         if (row < vocab) {
             const long long rs = row_scale[row];
-            lower = 81LL * rs * (long long)tot - 40LL * (rs < 0 ? -rs : rs) * habs;
+            s1 = 81LL * rs * (long long)tot;
+            lower = s1 - 40LL * (rs < 0 ? -rs : rs) * habs;
             ws.e1[row] = tot;
             ws.lower[row] = lower;
         }
-        long long mx = lower;
+        long long mx = lower, mx1 = s1;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
             const long long o = (long long)shfl_xor_u64((unsigned long long)mx, off);
+            const long long o1 = (long long)shfl_xor_u64((unsigned long long)mx1, off);
             mx = o > mx ? o : mx;
+            mx1 = o1 > mx1 ? o1 : mx1;
         }
         if (lane == 0) {
             tmax[tl] = mx;
-            if (trow < tiles) ws.tile_max[trow] = mx;
+            if (trow < tiles) {
+                ws.tile_max[trow] = mx;
+                ws.tile_max_s1[trow] = mx1;
+            }
         }
     }
     __syncthreads();
@@ -390,7 +404,7 @@ __device__ __forceinline__ unsigned long long rank_select_desc(int n, int want,
 
 // ----------------------------------------------------------------- select
 __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles, int nwg,
-                                                            int top_k, LmhWs ws) {
+                                                            int top_k, int cap, LmhWs ws) {
     __shared__ SelShared sh;
     __shared__ unsigned long long list[kSelList];
     __shared__ int tlist[kSelTiles];
@@ -404,11 +418,12 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
     }
     // the first kSelPre * blockDim tile maxima, loaded now so their latency
     // overlaps the workgroup maxima's and the threshold selection
-    unsigned long long tpre[kSelPre];
+    unsigned long long tpre[kSelPre], tpre1[kSelPre];   // L and S1' tile maxima
 #pragma unroll
     for (int u = 0; u < kSelPre; ++u) {
         const int tt = u * (int)blockDim.x + t;
         tpre[u] = tt < tiles ? okey(ws.tile_max[tt]) : 0ull;
+        tpre1[u] = tt < tiles ? okey(ws.tile_max_s1[tt]) : 0ull;
     }
     // T: the top_k-th largest maximum over blocks of two stage-1 workgroups
     // (0 when there are fewer blocks than top_k, which keeps every row).
@@ -500,13 +515,85 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
         kk = radix_select_desc<4>(
             vocab, (unsigned long long)top_k, [&](int i, int) { return okey(ws.lower[i]); },
             [&](int i, int) { return okey(ws.lower[i]) >= thr; }, sh);
-    if (t == 0) ws.scalars[0] = (long long)(kk ^ 0x8000000000000000ull);
+    const long long lk = (long long)(kk ^ 0x8000000000000000ull);
+    if (t == 0) ws.scalars[0] = lk;
+
+    // T1, a lower bound on the cap-th largest S1' over all rows: the lower
+    // edge of the histogram bin (256 bins over the span of the tile maxima of
+    // S1') in which the count of tile maxima from the top reaches cap; at
+    // least cap rows (one per tile) reach it.  If T1 >= L_k, every row with
+    // S1' >= T1 is a candidate (U >= S1' >= L_k), so the capped set (the cap
+    // candidates with the largest S1') lies among those rows, and the filter
+    // rescores only them.  Otherwise T1 = kNoRow: every candidate is.
+    long long t1 = kNoRow;
+    if (cap < vocab && tiles >= cap && tiles <= kSelPre * (int)blockDim.x) {
+        __syncthreads();   // the L_k selection's LDS is reusable
+        if (t == 0) {
+            sh.mm[0] = ~0ull;
+            sh.mm[1] = 0;
+        }
+        if (t < 256) sh.hist[t] = 0;
+        unsigned long long lo = ~0ull, hi = 0;
+#pragma unroll
+        for (int u = 0; u < kSelPre; ++u) {
+            if (u * (int)blockDim.x + t < tiles) {
+                lo = tpre1[u] < lo ? tpre1[u] : lo;
+                hi = tpre1[u] > hi ? tpre1[u] : hi;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const unsigned long long l2 = shfl_xor_u64(lo, off), h2 = shfl_xor_u64(hi, off);
+            lo = l2 < lo ? l2 : lo;
+            hi = h2 > hi ? h2 : hi;
+        }
+        __syncthreads();
+        if ((t & 63) == 0) {
+            atomicMin(&sh.mm[0], lo);
+            atomicMax(&sh.mm[1], hi);
+        }
+        __syncthreads();
+        const unsigned long long kmin = sh.mm[0], span = sh.mm[1] - kmin;
+        const int shift = span >> 8 ? 64 - __clzll(span) - 8 : 0;   // bins of 2^shift keys
+#pragma unroll
+        for (int u = 0; u < kSelPre; ++u)
+            if (u * (int)blockDim.x + t < tiles)
+                atomicAdd(&sh.hist[(int)((tpre1[u] - kmin) >> shift)], 1u);
+        __syncthreads();
+        if (t < 64) {
+            // lane l holds bins 255-4l .. 252-4l; counts from the top
+            unsigned c[4], sum = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                c[j] = sh.hist[255 - 4 * t - j];
+                sum += c[j];
+            }
+            unsigned incl = sum;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const unsigned o = (unsigned)__shfl_up((int)incl, off);
+                if (t >= off) incl += o;
+            }
+            unsigned run = incl - sum;   // tile maxima in the bins above this lane's
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (run < (unsigned)cap && run + c[j] >= (unsigned)cap)
+                    sh.bc[0] = kmin + ((unsigned long long)(255 - 4 * t - j) << shift);
+                run += c[j];
+            }
+        }
+        __syncthreads();
+        const long long b1 = (long long)(sh.bc[0] ^ 0x8000000000000000ull);
+        if (b1 >= lk) t1 = b1;
+    }
+    if (t == 0) ws.scalars[2] = t1;
 }
 
 // --------------------------------------------------- filter + rescoring
 // One workgroup per 256 rows (four wavefronts, lane = row).  Its candidates
-// go to slots [256 * blockIdx.x, 256 * blockIdx.x + count), sorted by
-// (S1' desc, row asc), and the count to region_count[blockIdx.x].
+// with S1' >= T1 are rescored and go to slots [256 * blockIdx.x,
+// 256 * blockIdx.x + kept), sorted by (S1' desc, row asc); the number of
+// candidates goes to region_count[blockIdx.x], kept to region_kept.
 __global__ __launch_bounds__(kFilterRows) void lmh_filter(const uint8_t *__restrict__ planes47,
                                                           const int32_t *__restrict__ row_scale,
                                                           const int8_t *__restrict__ h,
@@ -523,7 +610,7 @@ __global__ __launch_bounds__(kFilterRows) void lmh_filter(const uint8_t *__restr
     const uint2 *h2 = reinterpret_cast<const uint2 *>(h);
     uint2 *hs2 = reinterpret_cast<uint2 *>(hs);
     for (int t = threadIdx.x; t < groups * 16; t += kFilterRows) hs2[t] = h2[t];
-    const long long lk = ws.scalars[0], habs = ws.scalars[1];
+    const long long lk = ws.scalars[0], habs = ws.scalars[1], t1 = ws.scalars[2];
     bool cand = false;
     long long s1 = 0;
     int e1 = 0, rs = 0;
@@ -534,8 +621,13 @@ __global__ __launch_bounds__(kFilterRows) void lmh_filter(const uint8_t *__restr
         const long long ars = rs < 0 ? -(long long)rs : (long long)rs;
         cand = s1 + 40LL * ars * habs >= lk;
     }
+    const int ncand = __syncthreads_count(cand);
+    cand = cand && s1 >= t1;
     const int nct = __syncthreads_count(cand);
-    if (threadIdx.x == 0) ws.region_count[blockIdx.x] = nct;
+    if (threadIdx.x == 0) {
+        ws.region_count[blockIdx.x] = ncand;
+        ws.region_kept[blockIdx.x] = nct;
+    }
     if (nct == 0) return;   // whole workgroup
     const uint64_t m = __ballot(cand);
     const int nc = __popcll(m);
@@ -619,8 +711,7 @@ __device__ __forceinline__ size_t cand_slot(const CandSrc &c, int i) {
 
 template <bool REG>
 __device__ __forceinline__ void finish_body(int n, int top_k, int cap, int32_t *__restrict__ top_idx,
-                                            int64_t *__restrict__ top_score,
-                                            int32_t *__restrict__ info, const CandSrc &src,
+                                            int64_t *__restrict__ top_score, const CandSrc &src,
                                             SelShared &sh, long long *tk, int *ti,
                                             unsigned int *nkept) {
     constexpr int KPT = kFinKpt;
@@ -728,10 +819,6 @@ __device__ __forceinline__ void finish_body(int n, int top_k, int cap, int32_t *
         top_idx[i] = ti[i];
         top_score[i] = tk[i];
     }
-    if (threadIdx.x == 0) {
-        info[0] = n;
-        info[1] = capped ? 1 : 0;
-    }
 }
 
 // The top_k of the m rows (tk, ti) by (S' desc, row asc): each row's rank
@@ -768,6 +855,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     __shared__ int l1id[kFinList];
     __shared__ int wtot[kBlockThreads / 64];
     __shared__ unsigned int nkept, nl1;
+    __shared__ int ncand_sh;
     const int t = (int)threadIdx.x;
     const int wave = t >> 6, lane = t & 63;
     const int nwaves = kBlockThreads / 64;
@@ -776,11 +864,14 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     // cap bound below waits on no further load; an empty region's slot holds
     // an earlier call's bytes and is not used
     const long long head_pre = t < nwf ? ws.cand_s1[(size_t)t * kFilterRows] : 0;
-    // exclusive prefix sums of the region counts, 1024 regions at a time
+    // exclusive prefix sums of the regions' stored counts, 1024 regions at a
+    // time, and the number of candidates
+    if (t == 0) ncand_sh = 0;
     int n = 0;
     for (int r0 = 0; r0 < nwf; r0 += kBlockThreads) {
         const int r = r0 + t;
-        const int c = r < nwf ? ws.region_count[r] : 0;
+        const int c = r < nwf ? ws.region_kept[r] : 0;
+        const int ca = wave_sum(r < nwf ? ws.region_count[r] : 0);
         int incl = c;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -789,6 +880,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
         }
         if (lane == 63) wtot[wave] = incl;
         __syncthreads();
+        if (lane == 0) atomicAdd(&ncand_sh, ca);
         int before = n, chunk_total = 0;
         for (int w = 0; w < nwaves; ++w) {
             before += w < wave ? wtot[w] : 0;
@@ -802,7 +894,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
         // one wavefront per region
         const int nr = min(kBlockThreads, nwf - r0);
         for (int k = wave; k < nr; k += nwaves) {
-            const int cnt = ws.region_count[r0 + k], dst = ro[k];
+            const int cnt = ws.region_kept[r0 + k], dst = ro[k];
             const size_t from = (size_t)(r0 + k) * kFilterRows;
             for (int l = lane; l < cnt; l += 64) {
                 if (dst + l < vocab) {
@@ -821,15 +913,17 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     src.rows = regions ? ws.cand : ws.cc;
     src.s1 = regions ? ws.cand_s1 : ws.cc_s1;
     src.s = regions ? ws.cand_s : ws.cc_s;
+    // n rows were rescored: every candidate, or (T1 above kNoRow) those with
+    // S1' >= T1, at least cap rows among which the capped set lies
     n = min(n, vocab);
-    const bool capped = n > cap;
+    const int ncand = min(ncand_sh, vocab);
     if (t == 0) {
-        info[0] = n;
-        info[1] = capped ? 1 : 0;
+        info[0] = ncand;
+        info[1] = ncand > cap ? 1 : 0;
     }
 
-    if (!capped) {
-        // every candidate is rescored: gather them, then rank
+    if (n <= cap) {
+        // every rescored row is kept: gather them, then rank
         for (int i = t; i < n; i += blockDim.x) {
             const size_t sl = cand_slot(src, i);
             tk[i] = src.s[sl];
@@ -841,11 +935,12 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     }
     if (regions) {
         // T: the cap-th largest region head (cap distinct rows reach it; 0
-        // when fewer than cap regions are non-empty)
+        // when fewer than cap regions are non-empty, or when every row fits
+        // the list below)
         const bool nonempty = t < nwf && (t + 1 < nwf ? ro[t + 1] : n) > ro[t];
         const int nne = __syncthreads_count(nonempty);
         unsigned long long thr = 0;
-        if (nne >= cap) {
+        if (nne >= cap && n > kFinList) {
             const unsigned long long head = nonempty ? okey(head_pre) : 0ull;
             thr = radix_select_desc<1>(
                 nwf, (unsigned long long)cap, [&](int, int) { return head; },
@@ -898,9 +993,9 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     }
     // fallback: block-wide radix selections over every candidate
     if (n <= kFinKpt * kBlockThreads)
-        finish_body<true>(n, top_k, cap, top_idx, top_score, info, src, sh, tk, ti, &nkept);
+        finish_body<true>(n, top_k, cap, top_idx, top_score, src, sh, tk, ti, &nkept);
     else
-        finish_body<false>(n, top_k, cap, top_idx, top_score, info, src, sh, tk, ti, &nkept);
+        finish_body<false>(n, top_k, cap, top_idx, top_score, src, sh, tk, ti, &nkept);
 }
 
 }  // namespace
@@ -909,8 +1004,8 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
 using namespace bs;
 
 struct LmhLayout {
-    size_t scalars, e1, lower, tile_max, wg_max, region_count, cand, cand_s1, cand_s, cc, cc_s1,
-        cc_s, total;
+    size_t scalars, e1, lower, tile_max, wg_max, tile_max_s1, region_count,
+        region_kept, cand, cand_s1, cand_s, cc, cc_s1, cc_s, total;
     int tiles, nwg, nwf;
 };
 
@@ -928,7 +1023,9 @@ static LmhLayout lmh_layout(int64_t vocab) {
     L.lower = off;        off += align_up((size_t)vocab * 8, kWsAlign);
     L.tile_max = off;     off += align_up((size_t)L.tiles * 8, kWsAlign);
     L.wg_max = off;       off += align_up((size_t)L.nwg * 8, kWsAlign);
+    L.tile_max_s1 = off;  off += align_up((size_t)L.tiles * 8, kWsAlign);
     L.region_count = off; off += align_up((size_t)L.nwf * 4, kWsAlign);
+    L.region_kept = off;  off += align_up((size_t)L.nwf * 4, kWsAlign);
     L.cand = off;         off += align_up(slots * 4, kWsAlign);
     L.cand_s1 = off;      off += align_up(slots * 8, kWsAlign);
     L.cand_s = off;       off += align_up(slots * 8, kWsAlign);
@@ -980,7 +1077,9 @@ extern "C" int32_t bs_lmhead_planes_topk(const uint8_t *planes03, const uint8_t 
     ws.lower = reinterpret_cast<long long *>(base + L.lower);
     ws.tile_max = reinterpret_cast<long long *>(base + L.tile_max);
     ws.wg_max = reinterpret_cast<long long *>(base + L.wg_max);
+    ws.tile_max_s1 = reinterpret_cast<long long *>(base + L.tile_max_s1);
     ws.region_count = reinterpret_cast<int *>(base + L.region_count);
+    ws.region_kept = reinterpret_cast<int *>(base + L.region_kept);
     ws.cand = reinterpret_cast<int *>(base + L.cand);
     ws.cand_s1 = reinterpret_cast<long long *>(base + L.cand_s1);
     ws.cand_s = reinterpret_cast<long long *>(base + L.cand_s);
@@ -994,7 +1093,7 @@ extern "C" int32_t bs_lmhead_planes_topk(const uint8_t *planes03, const uint8_t 
                        reinterpret_cast<const int32_t *>(h), (int)vocab, groups, ws);
     BS_LAUNCH_CHECK();
     hipLaunchKernelGGL(lmh_select, dim3(1), dim3(kBlockThreads), 0, st, (int)vocab, L.tiles, L.nwg,
-                       top_k, ws);
+                       top_k, max_candidates, ws);
     BS_LAUNCH_CHECK();
     hipLaunchKernelGGL(lmh_filter, dim3((unsigned)L.nwf), dim3(kFilterRows), 0, st, planes47,
                        row_scale, h, (int)vocab, groups, ws);

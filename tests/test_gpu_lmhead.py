@@ -147,3 +147,65 @@ def test_more_filter_regions_than_one_pass(zero):
 def test_max_dim():
     """dim = 10112, the largest the int64 score bound allows (79 groups)."""
     check(*synth.lmhead(300, 10112, 17), 40, 200)
+
+
+# The selection kernel may name a bound T1 <= the cap-th largest S1' such that
+# every row with S1' >= T1 is a candidate; the filter then rescores only those
+# rows.  T1 is the workspace's third int64 (INT64_MIN when every candidate is
+# rescored); the cases below pin which way each input goes, so each branch of
+# the finishing pass is reached, and check the result against the oracle.
+_NO_T1 = -(1 << 63)
+
+
+def _copies_of_top(V, K, seed, n, levels=None):
+    """n random rows replaced by the row with the largest S1' (its trits; its
+    row scale, or one drawn from `levels`): ties and near-ties at the top."""
+    trits, rs, h = synth.lmhead(V, K, seed)
+    s1, _ = oracle.lmhead_stage1(trits, rs, h)
+    top = int(np.argmax(s1))
+    rng = np.random.default_rng(seed + 7)
+    rows = rng.choice(V, n, replace=False)
+    trits[rows] = trits[top]
+    rs[rows] = rs[top] if levels is None else rng.choice(levels, n).astype(np.int32)
+    return trits, rs, h
+
+
+@pytest.mark.parametrize("case", ["rand_k10_cap64", "rand_k10_cap100", "levels_head_prune",
+                                  "ties_list_overflow", "zero_few_regions", "zero_many",
+                                  "rand_bound_below_lk"])
+def test_rescore_bound_branches(case):
+    import torch
+    trits = None
+    if case == "rand_k10_cap64":          # T1 named, ~72 rows rescored
+        (trits, rs, h), k, cap, named = synth.lmhead(20000, 2560, 33), 10, 64, True
+    elif case == "rand_k10_cap100":       # T1 named, ~119 rows rescored
+        (trits, rs, h), k, cap, named = synth.lmhead(30000, 2560, 43), 10, 100, True
+    elif case == "levels_head_prune":     # 600 rescored; region heads prune to ~200
+        trits, rs, h = _copies_of_top(20000, 2560, 71, 600, [4094, 4095, 4096])
+        k, cap, named = 10, 64, True
+    elif case == "ties_list_overflow":    # 600 exact ties: past the LDS list
+        trits, rs, h = _copies_of_top(20000, 2560, 51, 600)
+        k, cap, named = 10, 64, True
+    elif case == "zero_few_regions":      # every row ties, 12 regions < cap
+        _, rs, h = synth.lmhead(3000, 128, 52)
+        trits, k, cap, named = np.zeros((3000, 8, 128), np.int8), 10, 40, True
+    elif case == "zero_many":             # every row ties, 20000 rescored
+        _, rs, h = synth.lmhead(20000, 128, 53)
+        trits, k, cap, named = np.zeros((20000, 8, 128), np.int8), 10, 40, True
+    else:                                 # enough tiles, but T1 < L_k
+        (trits, rs, h), k, cap, named = synth.lmhead(13000, 2560, 31), 40, 200, False
+    dev = device()
+    V, _, K = trits.shape
+    p03, p47 = bs.planes_pack(trits)
+    ws = torch.zeros(bs.lib().bs_lmhead_workspace_bytes(V, K, k, cap), dtype=torch.uint8,
+                     device=dev)
+    note("lmhead rescore bound %s V=%d K=%d k=%d cap=%d" % (case, V, K, k, cap))
+    idx, sc, info = bs.lmhead_planes_topk(to_dev(p03, dev), to_dev(p47, dev), to_dev(rs, dev),
+                                          to_dev(h, dev), V, K, k, cap, workspace=ws)
+    torch.cuda.synchronize()
+    t1 = int(ws[:24].view(torch.int64)[2].item())
+    assert (t1 != _NO_T1) == named, t1
+    widx, wsc, n, capped = oracle.lmhead_two_stage(trits, rs, h, k, cap)
+    assert list(info.cpu().numpy()) == [n, capped]
+    assert (idx.cpu().numpy() == widx).all()
+    assert (sc.cpu().numpy() == wsc).all()
