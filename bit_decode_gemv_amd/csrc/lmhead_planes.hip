@@ -53,7 +53,9 @@ constexpr int kSelList = 4096;          // select: pruned bounds kept in LDS
 constexpr int kSelPre = 2;              // select: tile maxima per thread loaded up front
 constexpr int kFinList = 512;           // finish: pruned candidates kept in LDS
 constexpr int kFinKpt = 4;              // finish fallback: candidates per thread in registers
+constexpr int kFinSpec = 2;             // finish: entries per region loaded up front
 constexpr int kMaxCap = 4096;
+static_assert(kMaxCap >= kBlockThreads + kFinList, "finish: ranks and the dropped list share ti");
 constexpr int kMaxGroups = 79;          // 10112 / 128
 constexpr int kResU = 4;                // rescoring: 16-byte runs in flight per lane
 constexpr long long kNoRow = (long long)0x8000000000000000ull;
@@ -374,6 +376,43 @@ __device__ __forceinline__ void block_rank(int n, Beats beats, Use use, int *rk)
         int tot = 0;
         for (int q = 0; q < P; ++q) tot += rk[q * npad + t];
         use(t, tot);
+    }
+    __syncthreads();
+}
+
+// block_rank under two orders at once: use(e, rank1, rank2) runs on thread e
+// (e < n).  rk1, rk2: int[blockDim] in LDS.
+template <typename Beats1, typename Beats2, typename Use>
+__device__ __forceinline__ void block_rank2(int n, Beats1 beats1, Beats2 beats2, Use use, int *rk1,
+                                            int *rk2) {
+    const int npad = (n + 63) & ~63;
+    const int P = (int)blockDim.x / npad;
+    const int t = (int)threadIdx.x, e = t % npad;
+    const int part = __builtin_amdgcn_readfirstlane(t / npad);   // uniform: npad % 64 == 0
+    const int chunk = (n + P - 1) / P;
+    int r1 = 0, r2 = 0;
+    if (part < P) {
+        const int j0 = part * chunk, j1 = min(n, j0 + chunk);
+        if (e < n) {
+#pragma unroll 8
+            for (int j = j0; j < j1; ++j) {
+                r1 += beats1(j, e) ? 1 : 0;
+                r2 += beats2(j, e) ? 1 : 0;
+            }
+        }
+    }
+    if (t < npad * P) {
+        rk1[t] = r1;
+        rk2[t] = r2;
+    }
+    __syncthreads();
+    if (t < n) {
+        int a = 0, b = 0;
+        for (int q = 0; q < P; ++q) {
+            a += rk1[q * npad + t];
+            b += rk2[q * npad + t];
+        }
+        use(t, a, b);
     }
     __syncthreads();
 }
@@ -860,18 +899,30 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     const int wave = t >> 6, lane = t & 63;
     const int nwaves = kBlockThreads / 64;
 
-    // region t's head (its largest S1'), loaded beside the counts so the
-    // cap bound below waits on no further load; an empty region's slot holds
-    // an earlier call's bytes and is not used
-    const long long head_pre = t < nwf ? ws.cand_s1[(size_t)t * kFilterRows] : 0;
+    // region t's counts, then its first kFinSpec stored entries (its head,
+    // the largest S1', first), loaded while the prefix sums below run, so the
+    // cap bound and the gather wait on no further load for regions that hold
+    // no more; entries past a region's count are not loaded
+    const int kept0 = t < nwf ? ws.region_kept[t] : 0;
+    const int count0 = t < nwf ? ws.region_count[t] : 0;
+    long long sp_s1[kFinSpec], sp_s[kFinSpec];
+    int sp_id[kFinSpec];
+#pragma unroll
+    for (int u = 0; u < kFinSpec; ++u) {
+        const size_t sl = (size_t)t * kFilterRows + u;
+        sp_s1[u] = u < kept0 ? ws.cand_s1[sl] : 0;
+        sp_s[u] = u < kept0 ? ws.cand_s[sl] : 0;
+        sp_id[u] = u < kept0 ? ws.cand[sl] : 0;
+    }
+    const long long head_pre = sp_s1[0];
     // exclusive prefix sums of the regions' stored counts, 1024 regions at a
     // time, and the number of candidates
     if (t == 0) ncand_sh = 0;
     int n = 0;
     for (int r0 = 0; r0 < nwf; r0 += kBlockThreads) {
         const int r = r0 + t;
-        const int c = r < nwf ? ws.region_kept[r] : 0;
-        const int ca = wave_sum(r < nwf ? ws.region_count[r] : 0);
+        const int c = r0 == 0 ? kept0 : (r < nwf ? ws.region_kept[r] : 0);
+        const int ca = wave_sum(r0 == 0 ? count0 : (r < nwf ? ws.region_count[r] : 0));
         int incl = c;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -952,11 +1003,24 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
         if (t < nwf) {
             const int cnt = (t + 1 < nwf ? ro[t + 1] : n) - ro[t];
             const size_t base = (size_t)t * kFilterRows;
-            for (int e0 = 0; e0 < cnt; e0 += 4) {
+            bool more = true;
+#pragma unroll
+            for (int u = 0; u < kFinSpec; ++u) {
+                if (more && u < cnt && okey(sp_s1[u]) >= thr) {
+                    const unsigned slot = atomicAdd(&nl1, 1u);
+                    if (slot < (unsigned)kFinList) {
+                        l1s1[slot] = sp_s1[u];
+                        l1s[slot] = sp_s[u];
+                        l1id[slot] = sp_id[u];
+                    }
+                } else {
+                    more = false;
+                }
+            }
+            for (int e0 = kFinSpec; more && e0 < cnt; e0 += 4) {
                 long long v[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) v[u] = e0 + u < cnt ? ws.cand_s1[base + e0 + u] : kNoRow;
-                bool more = true;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     if (e0 + u < cnt && okey(v[u]) >= thr) {
@@ -967,27 +1031,44 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
                             l1id[slot] = ws.cand[base + e0 + u];
                         }
                     } else {
-                        more = false;
+                        more = false;   // the region is sorted: the rest are below T
                     }
                 }
-                if (!more) break;
             }
         }
         __syncthreads();
         const int nl = (int)nl1;
         if (nl <= kFinList) {
-            // rank by (S1' desc, row asc): the first cap are kept, placed at
-            // their rank
-            block_rank(
+            // the ranks by (S1' desc, row asc) and by (S' desc, row asc) in
+            // one pass: the cap keeps the entries whose first rank is below
+            // cap, and a kept entry's output rank is its second rank less the
+            // dropped entries that precede it by (S', row)
+            int *dropped = ti + kBlockThreads;   // ti's first kBlockThreads: ranks
+            int r1 = cap, r2 = 0;
+            auto use = [&](int e, int a, int b) {
+                r1 = a;
+                r2 = b;
+                if (a >= cap) dropped[atomicAdd(&nkept, 1u)] = e;
+            };
+            if (t == 0) nkept = 0;               // here: the number dropped
+            block_rank2(
                 nl, [&](int j, int e) { return better(l1s1[j], l1id[j], l1s1[e], l1id[e]); },
-                [&](int e, int r) {
-                    if (r < cap) {
-                        tk[r] = l1s[e];
-                        ti[r] = l1id[e];
-                    }
-                },
-                ro);   // the region prefix sums are no longer needed
-            output_by_rank(cap, top_k, tk, ti, top_idx, top_score, ro);
+                [&](int j, int e) { return better(l1s[j], l1id[j], l1s[e], l1id[e]); }, use, ro,
+                ti);   // the region prefix sums are no longer needed
+            if (r1 < cap) {   // thread t < nl holds entry t
+                const int nd = (int)nkept;
+                const long long me = l1s[t];
+                const int my_id = l1id[t];
+                int r = r2;
+                for (int d = 0; d < nd; ++d) {
+                    const int j = dropped[d];
+                    r -= better(l1s[j], l1id[j], me, my_id) ? 1 : 0;
+                }
+                if (r < top_k) {
+                    top_idx[r] = my_id;
+                    top_score[r] = me;
+                }
+            }
             return;
         }
     }

@@ -209,3 +209,18 @@ def test_rescore_bound_branches(case):
     assert list(info.cpu().numpy()) == [n, capped]
     assert (idx.cpu().numpy() == widx).all()
     assert (sc.cpu().numpy() == wsc).all()
+
+
+@pytest.mark.parametrize("case", ["vocab_over_2p17", "score_span_over_2p47"])
+def test_finish_ranked_list_edges(case):
+    """Capped inputs whose gathered list the finishing pass ranks directly
+    (at most 512 rows): a vocabulary above 2^17 rows, and row scales near
+    2^31 so S1' spans about 2^53."""
+    if case == "vocab_over_2p17":       # 118 candidates, cap 100
+        (trits, rs, h), k, cap = synth.lmhead(140000, 128, 81), 40, 100
+    else:                               # row scales near 2^31: S1' spans ~2^53
+        trits, _, h = synth.lmhead(3000, 256, 82)
+        rs = np.random.default_rng(83).integers(1 << 28, (1 << 31) - 1, 3000).astype(np.int32)
+        k, cap = 20, 50
+    _, _, n, capped = check(trits, rs, h, k, cap)
+    assert capped == 1 and n <= 512, n
