@@ -441,6 +441,35 @@ __device__ __forceinline__ unsigned long long rank_select_desc(int n, int want,
     return v;
 }
 
+// The lower edge of the bin, in a 256-bin histogram of keys (bin b holds
+// kmin + [b << shift, (b + 1) << shift)), in which the count from the top
+// reaches want: at least `want` keys reach it.  One wavefront calls; the
+// histogram must hold at least `want` keys.  Lane l takes bins 255-4l ..
+// 252-4l.
+__device__ __forceinline__ void hist_edge(const unsigned *hist, unsigned want,
+                                          unsigned long long kmin, int shift, int lane,
+                                          unsigned long long *out) {
+    unsigned c[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        c[j] = hist[255 - 4 * lane - j];
+        sum += c[j];
+    }
+    unsigned incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const unsigned o = (unsigned)__shfl_up((int)incl, off);
+        if (lane >= off) incl += o;
+    }
+    unsigned run = incl - sum;   // keys in the bins above this lane's
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (run < want && run + c[j] >= want)
+            *out = kmin + ((unsigned long long)(255 - 4 * lane - j) << shift);
+        run += c[j];
+    }
+}
+
 // ----------------------------------------------------------------- select
 __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles, int nwg,
                                                             int top_k, int cap, LmhWs ws) {
@@ -450,6 +479,8 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
     __shared__ int rk[kBlockThreads];
     __shared__ unsigned long long res;
     __shared__ unsigned int n_t, n_l;
+    __shared__ unsigned int hist1[256];
+    __shared__ unsigned long long mm1[2], edge[2];
     const int t = (int)threadIdx.x;
     if (t == 0) {
         n_t = 0;
@@ -464,17 +495,83 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
         tpre[u] = tt < tiles ? okey(ws.tile_max[tt]) : 0ull;
         tpre1[u] = tt < tiles ? okey(ws.tile_max_s1[tt]) : 0ull;
     }
-    // T: the top_k-th largest maximum over blocks of two stage-1 workgroups
-    // (0 when there are fewer blocks than top_k, which keeps every row).
-    // Pairing keeps the ranked set at one key per 8 tiles.
+    // Two bounds from histograms of the tile maxima (all of them in
+    // registers when tiles <= kSelPre * blockDim; 256 bins over the span of
+    // each set): T, the lower edge of the bin in which the count of the
+    // tiles' largest L from the top reaches top_k, is a lower bound on L_k
+    // (top_k distinct rows reach it); T1 likewise over the tiles' largest S1'
+    // with cap (used below).  With more tiles, T is the top_k-th largest
+    // maximum over blocks of two stage-1 workgroups.  T = 0, which keeps
+    // every row, when there are fewer tiles (blocks) than top_k.
+    const bool in_regs = tiles <= kSelPre * (int)blockDim.x;
+    const bool want_t1 = in_regs && cap < vocab && tiles >= cap;
+    unsigned long long thr = 0, t1key = 0;
     const int nblk = (nwg + 1) / 2;
-    auto blk_key = [&](int i) {
-        const unsigned long long a = okey(ws.wg_max[2 * i]);
-        const unsigned long long b = 2 * i + 1 < nwg ? okey(ws.wg_max[2 * i + 1]) : 0ull;
-        return a > b ? a : b;
-    };
-    unsigned long long thr = 0;
-    if (nblk >= top_k) {
+    if (in_regs) {
+        if (t == 0) {
+            sh.mm[0] = ~0ull;
+            sh.mm[1] = 0;
+            mm1[0] = ~0ull;
+            mm1[1] = 0;
+        }
+        if (t < 256) {
+            sh.hist[t] = 0;
+            hist1[t] = 0;
+        }
+        unsigned long long lo = ~0ull, hi = 0, lo1 = ~0ull, hi1 = 0;
+#pragma unroll
+        for (int u = 0; u < kSelPre; ++u) {
+            if (u * (int)blockDim.x + t < tiles) {
+                lo = tpre[u] < lo ? tpre[u] : lo;
+                hi = tpre[u] > hi ? tpre[u] : hi;
+                lo1 = tpre1[u] < lo1 ? tpre1[u] : lo1;
+                hi1 = tpre1[u] > hi1 ? tpre1[u] : hi1;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            unsigned long long o = shfl_xor_u64(lo, off);
+            lo = o < lo ? o : lo;
+            o = shfl_xor_u64(hi, off);
+            hi = o > hi ? o : hi;
+            o = shfl_xor_u64(lo1, off);
+            lo1 = o < lo1 ? o : lo1;
+            o = shfl_xor_u64(hi1, off);
+            hi1 = o > hi1 ? o : hi1;
+        }
+        __syncthreads();
+        if ((t & 63) == 0 && t < tiles) {
+            atomicMin(&sh.mm[0], lo);
+            atomicMax(&sh.mm[1], hi);
+            atomicMin(&mm1[0], lo1);
+            atomicMax(&mm1[1], hi1);
+        }
+        __syncthreads();
+        const unsigned long long kmin = sh.mm[0], span = sh.mm[1] - kmin;
+        const unsigned long long kmin1 = mm1[0], span1 = mm1[1] - kmin1;
+        const int shift = span >> 8 ? 64 - __clzll(span) - 8 : 0;   // bins of 2^shift keys
+        const int shift1 = span1 >> 8 ? 64 - __clzll(span1) - 8 : 0;
+#pragma unroll
+        for (int u = 0; u < kSelPre; ++u) {
+            if (u * (int)blockDim.x + t < tiles) {
+                atomicAdd(&sh.hist[(int)((tpre[u] - kmin) >> shift)], 1u);
+                atomicAdd(&hist1[(int)((tpre1[u] - kmin1) >> shift1)], 1u);
+            }
+        }
+        __syncthreads();
+        const int wave = t >> 6;
+        if (wave == 0 && tiles >= top_k)
+            hist_edge(sh.hist, (unsigned)top_k, kmin, shift, t & 63, &edge[0]);
+        if (wave == 1 && want_t1) hist_edge(hist1, (unsigned)cap, kmin1, shift1, t & 63, &edge[1]);
+        __syncthreads();
+        if (tiles >= top_k) thr = edge[0];
+        if (want_t1) t1key = edge[1];
+    } else if (nblk >= top_k) {
+        auto blk_key = [&](int i) {
+            const unsigned long long a = okey(ws.wg_max[2 * i]);
+            const unsigned long long b = 2 * i + 1 < nwg ? okey(ws.wg_max[2 * i + 1]) : 0ull;
+            return a > b ? a : b;
+        };
         if (nblk <= (int)blockDim.x)
             thr = rank_select_desc(nblk, top_k, t < nblk ? blk_key(t) : 0ull, list, rk, &res);
         else
@@ -557,72 +654,15 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
     const long long lk = (long long)(kk ^ 0x8000000000000000ull);
     if (t == 0) ws.scalars[0] = lk;
 
-    // T1, a lower bound on the cap-th largest S1' over all rows: the lower
-    // edge of the histogram bin (256 bins over the span of the tile maxima of
-    // S1') in which the count of tile maxima from the top reaches cap; at
-    // least cap rows (one per tile) reach it.  If T1 >= L_k, every row with
-    // S1' >= T1 is a candidate (U >= S1' >= L_k), so the capped set (the cap
-    // candidates with the largest S1') lies among those rows, and the filter
-    // rescores only them.  Otherwise T1 = kNoRow: every candidate is.
+    // T1 (from the histogram above) is a lower bound on the cap-th largest
+    // S1' over all rows: at least cap rows (one per tile) reach it.  If
+    // T1 >= L_k, every row with S1' >= T1 is a candidate (U >= S1' >= L_k), so
+    // the capped set (the cap candidates with the largest S1') lies among
+    // those rows, and the filter rescores only them.  Otherwise T1 = kNoRow:
+    // every candidate is.
     long long t1 = kNoRow;
-    if (cap < vocab && tiles >= cap && tiles <= kSelPre * (int)blockDim.x) {
-        __syncthreads();   // the L_k selection's LDS is reusable
-        if (t == 0) {
-            sh.mm[0] = ~0ull;
-            sh.mm[1] = 0;
-        }
-        if (t < 256) sh.hist[t] = 0;
-        unsigned long long lo = ~0ull, hi = 0;
-#pragma unroll
-        for (int u = 0; u < kSelPre; ++u) {
-            if (u * (int)blockDim.x + t < tiles) {
-                lo = tpre1[u] < lo ? tpre1[u] : lo;
-                hi = tpre1[u] > hi ? tpre1[u] : hi;
-            }
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const unsigned long long l2 = shfl_xor_u64(lo, off), h2 = shfl_xor_u64(hi, off);
-            lo = l2 < lo ? l2 : lo;
-            hi = h2 > hi ? h2 : hi;
-        }
-        __syncthreads();
-        if ((t & 63) == 0) {
-            atomicMin(&sh.mm[0], lo);
-            atomicMax(&sh.mm[1], hi);
-        }
-        __syncthreads();
-        const unsigned long long kmin = sh.mm[0], span = sh.mm[1] - kmin;
-        const int shift = span >> 8 ? 64 - __clzll(span) - 8 : 0;   // bins of 2^shift keys
-#pragma unroll
-        for (int u = 0; u < kSelPre; ++u)
-            if (u * (int)blockDim.x + t < tiles)
-                atomicAdd(&sh.hist[(int)((tpre1[u] - kmin) >> shift)], 1u);
-        __syncthreads();
-        if (t < 64) {
-            // lane l holds bins 255-4l .. 252-4l; counts from the top
-            unsigned c[4], sum = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                c[j] = sh.hist[255 - 4 * t - j];
-                sum += c[j];
-            }
-            unsigned incl = sum;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const unsigned o = (unsigned)__shfl_up((int)incl, off);
-                if (t >= off) incl += o;
-            }
-            unsigned run = incl - sum;   // tile maxima in the bins above this lane's
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (run < (unsigned)cap && run + c[j] >= (unsigned)cap)
-                    sh.bc[0] = kmin + ((unsigned long long)(255 - 4 * t - j) << shift);
-                run += c[j];
-            }
-        }
-        __syncthreads();
-        const long long b1 = (long long)(sh.bc[0] ^ 0x8000000000000000ull);
+    if (want_t1) {
+        const long long b1 = (long long)(t1key ^ 0x8000000000000000ull);
         if (b1 >= lk) t1 = b1;
     }
     if (t == 0) ws.scalars[2] = t1;
