@@ -25,6 +25,7 @@
 #include <string.h>
 
 #include "kcommon.h"
+#include "dpp.h"
 
 namespace bs {
 namespace {
@@ -36,29 +37,12 @@ __device__ __forceinline__ uint64_t abs_u64(int64_t v) {
     return v < 0 ? (uint64_t)0 - (uint64_t)v : (uint64_t)v;
 }
 
-// v against its DPP-moved copy (CTRL: the data-parallel-primitive lane
-// pattern; ROWS: the 16-lane rows written), per 32-bit half; lanes the
-// pattern gives no source keep their own value.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
-    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROWS, 0xF, false);
-    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROWS, 0xF, false);
-    const uint64_t o = ((uint64_t)ohi << 32) | olo;
-    return o > v ? o : v;
-}
-
 // Largest value over the block, in every thread.  Within a wavefront by
 // DPP moves (row shifts by 1, 2, 4, 8, then lane 15 broadcast into the next
 // row and lane 31 into the upper two): lane 63 ends with the maximum, with
 // no LDS round trip per step.
 __device__ uint64_t block_max_u64(uint64_t v, uint64_t *red) {
-    v = dpp_max_u64<0x111, 0xF>(v);   // row_shr:1
-    v = dpp_max_u64<0x112, 0xF>(v);   // row_shr:2
-    v = dpp_max_u64<0x114, 0xF>(v);   // row_shr:4
-    v = dpp_max_u64<0x118, 0xF>(v);   // row_shr:8
-    v = dpp_max_u64<0x142, 0xA>(v);   // row_bcast:15, rows 1 and 3
-    v = dpp_max_u64<0x143, 0xC>(v);   // row_bcast:31, rows 2 and 3
+    v = wave_max_u64_lane63(v);
     const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     if ((threadIdx.x & 63) == 63) red[wave] = v;
     __syncthreads();

@@ -38,6 +38,7 @@
 //              prefixes are read), then the top_k of the kept rows by
 //              (S' desc, row asc).
 #include "kcommon.h"
+#include "dpp.h"
 
 namespace bs {
 namespace {
@@ -380,10 +381,59 @@ __device__ __forceinline__ void block_rank(int n, Beats beats, Use use, int *rk)
     __syncthreads();
 }
 
-// block_rank under two orders at once: use(e, rank1, rank2) runs on thread e
-// (e < n).  rk1, rk2: int[blockDim] in LDS.
-template <typename Beats1, typename Beats2, typename Use>
-__device__ __forceinline__ void block_rank2(int n, Beats1 beats1, Beats2 beats2, Use use, int *rk1,
+// The workgroup maxima of four 64-bit values, in every thread (a minimum is
+// the complement of the maximum of complements), over the first `nactive`
+// wavefronts' values.  Each of those reduces by DPP moves and its lane 63
+// writes a slot; wavefront 0 folds the slots (lane = 16 * value + slot, row
+// shifts), since a fold in every thread would repeat the same VALU work in
+// all of the workgroup's wavefronts; every thread then reads the results.
+// Every thread calls; NW (<= 16) wavefronts; red, fin in LDS, reusable after
+// the next barrier.
+template <int NW>
+__device__ __forceinline__ void block_max4(unsigned long long v[4], int nactive,
+                                           unsigned long long (*red)[4],
+                                           unsigned long long *fin) {
+    static_assert(NW <= 16, "one slot per lane of a 16-lane row");
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (wave < nactive) {   // uniform per wavefront
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = wave_max_u64_lane63(v[k]);
+        if (lane == 63) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) red[wave][k] = v[k];
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int w = lane & 15;
+        unsigned long long x = w < nactive ? red[w][lane >> 4] : 0ull;
+        x = dpp_max_u64<0x111, 0xF>(x);   // row_shr:1
+        x = dpp_max_u64<0x112, 0xF>(x);   // row_shr:2
+        x = dpp_max_u64<0x114, 0xF>(x);   // row_shr:4
+        x = dpp_max_u64<0x118, 0xF>(x);   // row_shr:8
+        if (w == 15) fin[lane >> 4] = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = fin[k];
+}
+
+// r + (a > b) for unsigned 64-bit a, b: the compare into VCC and an add of
+// the carry (the compiler otherwise turns each compare into a 0/1 value,
+// packs eight of them and counts the bits: about four instructions more).
+__device__ __forceinline__ int add_gt_u64(int r, unsigned long long a, unsigned long long b) {
+    asm("v_cmp_gt_u64_e32 vcc, %1, %2\n\tv_addc_co_u32_e32 %0, vcc, 0, %0, vcc"
+        : "+v"(r)
+        : "v"(a), "v"(b)
+        : "vcc");
+    return r;
+}
+
+// block_rank under two orders at once: step1(j, e, r) and step2(j, e, r)
+// return r plus whether entry j precedes entry e in each order; use(e,
+// rank1, rank2) runs on thread e (e < n).  rk1, rk2: int[blockDim] in LDS.
+template <typename Step1, typename Step2, typename Use>
+__device__ __forceinline__ void block_rank2(int n, Step1 step1, Step2 step2, Use use, int *rk1,
                                             int *rk2) {
     const int npad = (n + 63) & ~63;
     const int P = (int)blockDim.x / npad;
@@ -396,8 +446,8 @@ __device__ __forceinline__ void block_rank2(int n, Beats1 beats1, Beats2 beats2,
         if (e < n) {
 #pragma unroll 8
             for (int j = j0; j < j1; ++j) {
-                r1 += beats1(j, e) ? 1 : 0;
-                r2 += beats2(j, e) ? 1 : 0;
+                r1 = step1(j, e, r1);
+                r2 = step2(j, e, r2);
             }
         }
     }
@@ -480,7 +530,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
     __shared__ unsigned long long res;
     __shared__ unsigned int n_t, n_l;
     __shared__ unsigned int hist1[256];
-    __shared__ unsigned long long mm1[2], edge[2];
+    __shared__ unsigned long long red4[kBlockThreads / 64][4], fin4[4], edge[2];
     const int t = (int)threadIdx.x;
     if (t == 0) {
         n_t = 0;
@@ -508,12 +558,6 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
     unsigned long long thr = 0, t1key = 0;
     const int nblk = (nwg + 1) / 2;
     if (in_regs) {
-        if (t == 0) {
-            sh.mm[0] = ~0ull;
-            sh.mm[1] = 0;
-            mm1[0] = ~0ull;
-            mm1[1] = 0;
-        }
         if (t < 256) {
             sh.hist[t] = 0;
             hist1[t] = 0;
@@ -528,27 +572,11 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
                 hi1 = tpre1[u] > hi1 ? tpre1[u] : hi1;
             }
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            unsigned long long o = shfl_xor_u64(lo, off);
-            lo = o < lo ? o : lo;
-            o = shfl_xor_u64(hi, off);
-            hi = o > hi ? o : hi;
-            o = shfl_xor_u64(lo1, off);
-            lo1 = o < lo1 ? o : lo1;
-            o = shfl_xor_u64(hi1, off);
-            hi1 = o > hi1 ? o : hi1;
-        }
-        __syncthreads();
-        if ((t & 63) == 0 && t < tiles) {
-            atomicMin(&sh.mm[0], lo);
-            atomicMax(&sh.mm[1], hi);
-            atomicMin(&mm1[0], lo1);
-            atomicMax(&mm1[1], hi1);
-        }
-        __syncthreads();
-        const unsigned long long kmin = sh.mm[0], span = sh.mm[1] - kmin;
-        const unsigned long long kmin1 = mm1[0], span1 = mm1[1] - kmin1;
+        unsigned long long mx[4] = {hi, ~lo, hi1, ~lo1};
+        // (also orders the histograms' clearing)
+        block_max4<kBlockThreads / 64>(mx, min(kBlockThreads / 64, (tiles + 63) / 64), red4, fin4);
+        const unsigned long long kmin = ~mx[1], span = mx[0] - kmin;
+        const unsigned long long kmin1 = ~mx[3], span1 = mx[2] - kmin1;
         const int shift = span >> 8 ? 64 - __clzll(span) - 8 : 0;   // bins of 2^shift keys
         const int shift1 = span1 >> 8 ? 64 - __clzll(span1) - 8 : 0;
 #pragma unroll
@@ -932,6 +960,8 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     __shared__ int ro[kBlockThreads];
     __shared__ long long l1s1[kFinList], l1s[kFinList];
     __shared__ int l1id[kFinList];
+    __shared__ unsigned long long pk1[kFinList], pk2[kFinList];
+    __shared__ unsigned long long red4[kBlockThreads / 64][4], fin4[4];
     __shared__ int wtot[kBlockThreads / 64];
     __shared__ unsigned int nkept, nl1;
     __shared__ int ncand_sh;
@@ -1091,10 +1121,44 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
                 if (a >= cap) dropped[atomicAdd(&nkept, 1u)] = e;
             };
             if (t == 0) nkept = 0;               // here: the number dropped
-            block_rank2(
-                nl, [&](int j, int e) { return better(l1s1[j], l1id[j], l1s1[e], l1id[e]); },
-                [&](int j, int e) { return better(l1s[j], l1id[j], l1s[e], l1id[e]); }, use, ro,
-                ti);   // the region prefix sums are no longer needed
+            // Each order as one 64-bit key when the list allows it:
+            // ((okey(score) - least) << 17) | (2^17 - 1 - row) orders by
+            // (score desc, row asc) when the scores span less than 2^47 and
+            // rows are below 2^17, and a comparison is then one compare.
+            unsigned long long mx[4] = {0, 0, 0, 0};
+            if (t < nl) {
+                const unsigned long long a1 = okey(l1s1[t]), a2 = okey(l1s[t]);
+                mx[0] = a1;
+                mx[1] = ~a1;
+                mx[2] = a2;
+                mx[3] = ~a2;
+            }
+            block_max4<kBlockThreads / 64>(mx, (nl + 63) / 64, red4, fin4);
+            const unsigned long long base1 = ~mx[1], base2 = ~mx[3];
+            const bool packed = vocab <= (1 << 17) && mx[0] - base1 < (1ull << 47) &&
+                                mx[2] - base2 < (1ull << 47);
+            if (packed) {
+                if (t < nl) {
+                    const unsigned long long tie = (unsigned long long)((1 << 17) - 1 - l1id[t]);
+                    pk1[t] = ((okey(l1s1[t]) - base1) << 17) | tie;
+                    pk2[t] = ((okey(l1s[t]) - base2) << 17) | tie;
+                }
+                __syncthreads();
+                block_rank2(
+                    nl, [&](int j, int e, int r) { return add_gt_u64(r, pk1[j], pk1[e]); },
+                    [&](int j, int e, int r) { return add_gt_u64(r, pk2[j], pk2[e]); }, use, ro,
+                    ti);   // the region prefix sums are no longer needed
+            } else {
+                block_rank2(
+                    nl,
+                    [&](int j, int e, int r) {
+                        return r + (better(l1s1[j], l1id[j], l1s1[e], l1id[e]) ? 1 : 0);
+                    },
+                    [&](int j, int e, int r) {
+                        return r + (better(l1s[j], l1id[j], l1s[e], l1id[e]) ? 1 : 0);
+                    },
+                    use, ro, ti);
+            }
             if (r1 < cap) {   // thread t < nl holds entry t
                 const int nd = (int)nkept;
                 const long long me = l1s[t];
