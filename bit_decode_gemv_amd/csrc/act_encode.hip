@@ -37,20 +37,6 @@ __device__ __forceinline__ uint64_t abs_u64(int64_t v) {
     return v < 0 ? (uint64_t)0 - (uint64_t)v : (uint64_t)v;
 }
 
-// Largest value over the block, in every thread.  Within a wavefront by
-// DPP moves (row shifts by 1, 2, 4, 8, then lane 15 broadcast into the next
-// row and lane 31 into the upper two): lane 63 ends with the maximum, with
-// no LDS round trip per step.
-__device__ uint64_t block_max_u64(uint64_t v, uint64_t *red) {
-    v = wave_max_u64_lane63(v);
-    const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    if ((threadIdx.x & 63) == 63) red[wave] = v;
-    __syncthreads();
-    uint64_t m = 0;
-    for (int w = 0; w < nw; ++w) m = red[w] > m ? red[w] : m;
-    return m;
-}
-
 // Each thread holds up to kPerThread values in registers between the two
 // passes (max, then quantise), loaded together so their latencies overlap;
 // longer vectors stream through a loop.
@@ -78,7 +64,7 @@ __device__ __forceinline__ int8_t quant_one(int64_t v, uint64_t a, float s127) {
 __global__ void act_quant_kernel(const int64_t *__restrict__ x, int64_t k,
                                  int8_t *__restrict__ q, int64_t *__restrict__ absmax,
                                  int32_t *__restrict__ status) {
-    __shared__ uint64_t red[16];
+    __shared__ uint64_t red[16], fin;
     const bool held = k <= (int64_t)kPerThread * blockDim.x;
     int64_t v[kPerThread];
     uint64_t m = 0;
@@ -99,7 +85,7 @@ __global__ void act_quant_kernel(const int64_t *__restrict__ x, int64_t k,
             m = a > m ? a : m;
         }
     }
-    const uint64_t a = block_max_u64(m, red);
+    const uint64_t a = block_max_u64(m, red, &fin);
     if (a > kActAbsMax) {   // fail loud: no quantised values, the status says why
         for (int64_t i = threadIdx.x; i < k; i += blockDim.x) q[i] = 0;
         if (threadIdx.x == 0) {

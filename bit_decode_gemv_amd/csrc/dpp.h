@@ -30,4 +30,27 @@ __device__ __forceinline__ uint64_t wave_max_u64_lane63(uint64_t v) {
     return v;
 }
 
+// The workgroup maximum of v (workgroups of up to 16 wavefronts), in every
+// thread: each wavefront's by DPP moves, its lane 63 writing a slot;
+// wavefront 0 folds the slots in one 16-lane row and every thread reads the
+// result (a fold in every thread would repeat the same VALU work in all of
+// the workgroup's wavefronts).  Every thread calls; red[16] and fin[1] in
+// LDS, reusable after the next barrier.
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *red, uint64_t *fin) {
+    v = wave_max_u64_lane63(v);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+    if (lane == 63) red[wave] = v;
+    __syncthreads();
+    if (wave == 0) {
+        uint64_t x = lane < nw ? red[lane < 16 ? lane : 0] : 0;
+        x = dpp_max_u64<0x111, 0xF>(x);   // row_shr:1
+        x = dpp_max_u64<0x112, 0xF>(x);   // row_shr:2
+        x = dpp_max_u64<0x114, 0xF>(x);   // row_shr:4
+        x = dpp_max_u64<0x118, 0xF>(x);   // row_shr:8
+        if (lane == 15) *fin = x;
+    }
+    __syncthreads();
+    return *fin;
+}
+
 }  // namespace bs
