@@ -24,8 +24,10 @@
 // initial value are derived from the cube and square roots of the first
 // primes, as the standard defines them).
 //
-// One workgroup of up to 1024 threads, thread i holding candidate i; every
-// step is integer, so the result is the oracle's bit for bit.
+// One workgroup of up to 1024 threads, thread i holding candidate i, plus
+// one wavefront that hashes the draw sources while the candidates are ranked
+// (when 960 or fewer candidates leave room for it); every step is integer,
+// so the result is the oracle's bit for bit.
 #include "kcommon.h"
 
 namespace bs {
@@ -134,22 +136,34 @@ __global__ void sample_kernel(const int32_t *__restrict__ idx, const int64_t *__
     __shared__ uint64_t draw_sh;
     __shared__ int kept_sh, pick_sh, used_sh;
     const int t = threadIdx.x;
+    // candidates take threads [0, nc); the draw sources take the wavefront
+    // from thread hw: its own, after the candidates' (its hashing then runs
+    // on another SIMD while the candidates are ranked), when the workgroup
+    // has room for it, else the first
+    const int nc = (n + 63) & ~63;
+    const int hw = (int)blockDim.x > nc ? nc : 0;
     int64_t my_s = 0;
     int32_t my_i = 0;
     if (t < n) {
         my_s = score[t];
         my_i = idx[t];
     }
-    // The draw sources do not depend on the candidates: lane a of the first
+    // The draw sources do not depend on the candidates: lane a of the hashing
     // wavefront hashes attempt a (SHA-256 of seed, position, a) while the
-    // candidate loads are in flight.
-    uint64_t u = 0;
-    if (mode != 0 && t < 64) u = sha256_draw(seed, position, (uint32_t)t);
-    if (t < n) {
-        s_in[t] = my_s;
-        i_in[t] = my_i;
+    // candidates are ranked.  With at most 64 candidates the ranking reads
+    // them from lane registers, so no barrier comes before it and the two
+    // meet only at the barrier after the ranking; otherwise the candidates go
+    // to LDS first.
+    const bool one_wave = n <= 64;
+    if (!one_wave) {
+        if (t < n) {
+            s_in[t] = my_s;
+            i_in[t] = my_i;
+        }
+        __syncthreads();
     }
-    __syncthreads();
+    uint64_t u = 0;
+    if (mode != 0 && t >= hw && t < hw + 64) u = sha256_draw(seed, position, (uint32_t)(t - hw));
     if (t < n) {
         const int64_t s = my_s;
         const int32_t id = my_i;
@@ -157,8 +171,8 @@ __global__ void sample_kernel(const int32_t *__restrict__ idx, const int64_t *__
             return (sj > s) || (sj == s && (ij < id || (ij == id && j < t)));
         };
         int r = 0;
-        if (blockDim.x == 64) {
-            // one wavefront: candidate j straight from lane j's registers
+        if (one_wave) {
+            // candidate j straight from lane j's registers
             for (int j = 0; j < n; ++j) {
                 const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)my_s, j);
                 const uint32_t hi =
@@ -186,13 +200,28 @@ __global__ void sample_kernel(const int32_t *__restrict__ idx, const int64_t *__
     // weights in rank order and their inclusive prefix sums
     uint64_t w = 0;
     if (t < n) w = weight_q31((uint64_t)s_rk[0] - (uint64_t)s_rk[t], beta);
-    cum[t] = w;
-    __syncthreads();
-    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-        const uint64_t add = t >= off ? cum[t - off] : 0;
+    if (nc == 64) {
+        // one wavefront of candidates: an inclusive scan by lane shuffles
+        if (t < 64) {
+            uint64_t incl = w;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)incl, off);
+                const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(incl >> 32), off);
+                if (t >= off) incl += ((uint64_t)hi << 32) | lo;
+            }
+            cum[t] = incl;
+        }
         __syncthreads();
-        cum[t] += add;
+    } else {
+        cum[t] = w;
         __syncthreads();
+        for (int off = 1; off < nc; off <<= 1) {
+            const uint64_t add = t >= off ? cum[t - off] : 0;
+            __syncthreads();
+            cum[t] += add;
+            __syncthreads();
+        }
     }
     const uint64_t wall = cum[n - 1];
     const uint64_t w0 = (uint64_t)1 << 31;   // rank 0: d = 0
@@ -207,7 +236,7 @@ __global__ void sample_kernel(const int32_t *__restrict__ idx, const int64_t *__
     __syncthreads();
     const int kept = kept_sh;
     const uint64_t total = cum[kept - 1];
-    if (t < 64) {
+    if (t >= hw && t < hw + 64) {
         // lane a holds attempt a's source (its digest's rounds ran on the
         // vector unit: rotates, three-input xors and the choose/majority
         // functions are one instruction each there); the first attempt that
@@ -220,14 +249,14 @@ __global__ void sample_kernel(const int32_t *__restrict__ idx, const int64_t *__
             const uint64_t thr = ((uint64_t)0 - tot) % tot;   // uniform; needed rarely
             reject = reject && lo < thr;
         }
-        const uint64_t ok = __ballot(!reject && t < kMaxDraws);
+        const uint64_t ok = __ballot(!reject && t - hw < kMaxDraws);
         // every lane computes its bounded value, so the accepted lane's can be
         // read from the whole wavefront
         const uint64_t hi = __umul64hi(u, tot);
         const int first = ok ? __builtin_ctzll(ok) : 0;
         const uint32_t vlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)hi, first);
         const uint32_t vhi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(hi >> 32), first);
-        if (t == 0) {
+        if (t == hw) {
             draw_sh = ok ? ((uint64_t)vhi << 32) | vlo : UINT64_MAX;
             used_sh = ok ? first + 1 : kMaxDraws;
             pick_sh = -1;
@@ -263,7 +292,9 @@ extern "C" int32_t bs_sample_candidates(const int32_t *idx, const int64_t *score
     if (top_p_q16 < 1 || top_p_q16 > 65536 || min_p_q16 > 65536) return BS_E_RANGE;
     if (((uintptr_t)idx & 3) || ((uintptr_t)score & 7) || ((uintptr_t)result & 7))
         return BS_E_ALIGN;
-    const int threads = (n + 63) / 64 * 64;
+    // the candidates' wavefronts and, when there is room, one more for the
+    // draw sources
+    const int threads = (n + 63) / 64 * 64 + ((n + 63) / 64 * 64 < kMaxCand ? 64 : 0);
     hipLaunchKernelGGL(sample_kernel, dim3(1), dim3(threads), 0, (hipStream_t)stream, idx, score,
                        n, mode, beta_q16, top_p_q16, min_p_q16, seed, position, result);
     BS_LAUNCH_CHECK();
