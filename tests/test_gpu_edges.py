@@ -133,8 +133,12 @@ def _want(idx, score, mode, **kw):
     return [o["token"], o["rank"], o["kept"], o["total"], o["draw"], o["attempts"]]
 
 
-@pytest.mark.parametrize("n,seed", [(1, 0), (40, 1), (200, 2), (1024, 3), (77, 4)])
+@pytest.mark.parametrize("n,seed", [(1, 0), (40, 1), (200, 2), (1024, 3), (77, 4), (64, 5),
+                                    (65, 6), (960, 7), (961, 8)])
 def test_sampler_matches_oracle(n, seed):
+    """64/65: the last one-wavefront ranking and the first through LDS;
+    960/961: the last workgroup with a wavefront of its own for the hashing
+    and the first that hashes in the candidates' first wavefront."""
     rng = np.random.default_rng(seed)
     idx = rng.permutation(200000)[:n].astype(np.int32)
     score = rng.integers(-40, 40, n).astype(np.int64) * (1 << 10)
