@@ -647,25 +647,10 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
         }
         __syncthreads();
         const int ln = (int)n_l;
-        if (ln <= 64) {
-            // one wavefront ranks the list: lane e against every entry j,
-            // broadcast with readlane
-            if (t < 64) {
-                const unsigned long long me = t < ln ? list[t] : 0ull;
-                const uint32_t mlo = (uint32_t)me, mhi = (uint32_t)(me >> 32);
-                int r = 0;
-                for (int j = 0; j < ln; ++j) {
-                    const unsigned long long o =
-                        ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)mhi, j) << 32) |
-                        (uint32_t)__builtin_amdgcn_readlane((int)mlo, j);
-                    r += (o > me) || (o == me && j < t);
-                }
-                if (t < ln && r == top_k - 1) res = me;
-            }
-            __syncthreads();
-            kk = res;
-            done = true;
-        } else if (ln <= (int)blockDim.x) {
+        if (ln <= (int)blockDim.x) {
+            // pairwise ranks shared out over the workgroup (faster, measured,
+            // than one wavefront walking the list with lane broadcasts even
+            // for a few dozen entries)
             kk = rank_select_desc(ln, top_k, t < ln ? list[t] : 0ull, list, rk, &res);
             done = true;
         } else if (ln <= kSelList) {

@@ -24,8 +24,9 @@
 // initial value are derived from the cube and square roots of the first
 // primes, as the standard defines them).
 //
-// One workgroup of up to 1024 threads, thread i holding candidate i, plus
-// one wavefront that hashes the draw sources while the candidates are ranked
+// One workgroup of up to 1024 threads, thread i holding candidate i (with
+// at most 64 candidates, four wavefronts share their ranking), plus one
+// wavefront that hashes the draw sources while the candidates are ranked
 // (when 960 or fewer candidates leave room for it); every step is integer,
 // so the result is the oracle's bit for bit.
 #include "kcommon.h"
@@ -34,6 +35,7 @@ namespace bs {
 namespace {
 
 constexpr int kMaxCand = 1024;
+constexpr int kRankWaves = 4;   // wavefronts sharing the ranking of at most 64 candidates
 constexpr int kMaxDraws = 16;
 constexpr int64_t kA1 = 1484817034, kA2 = 495114803, kA3 = 84039593;
 
@@ -133,20 +135,25 @@ __global__ void sample_kernel(const int32_t *__restrict__ idx, const int64_t *__
     __shared__ int64_t s_rk[kMaxCand];
     __shared__ int32_t i_rk[kMaxCand];
     __shared__ uint64_t cum[kMaxCand];
+    __shared__ int rk_part[kRankWaves][64];
     __shared__ uint64_t draw_sh;
     __shared__ int kept_sh, pick_sh, used_sh;
     const int t = threadIdx.x;
-    // candidates take threads [0, nc); the draw sources take the wavefront
-    // from thread hw: its own, after the candidates' (its hashing then runs
+    // Candidates take threads [0, nc), thread i holding candidate i; with at
+    // most 64 (one wavefront) kRankWaves wavefronts each hold all of them
+    // (lane i: candidate i) and share the ranking.  The draw sources take the
+    // wavefront from thread hw: its own, after those (its hashing then runs
     // on another SIMD while the candidates are ranked), when the workgroup
-    // has room for it, else the first
+    // has room for it, else the first.
+    const bool one_wave = n <= 64;
     const int nc = (n + 63) & ~63;
-    const int hw = (int)blockDim.x > nc ? nc : 0;
+    const int hw = one_wave ? 64 * kRankWaves : ((int)blockDim.x > nc ? nc : 0);
+    const int cand = one_wave ? (t < 64 * kRankWaves ? (t & 63) : n) : t;
     int64_t my_s = 0;
     int32_t my_i = 0;
-    if (t < n) {
-        my_s = score[t];
-        my_i = idx[t];
+    if (cand < n) {
+        my_s = score[cand];
+        my_i = idx[cand];
     }
     // The draw sources do not depend on the candidates: lane a of the hashing
     // wavefront hashes attempt a (SHA-256 of seed, position, a) while the
@@ -154,7 +161,6 @@ __global__ void sample_kernel(const int32_t *__restrict__ idx, const int64_t *__
     // them from lane registers, so no barrier comes before it and the two
     // meet only at the barrier after the ranking; otherwise the candidates go
     // to LDS first.
-    const bool one_wave = n <= 64;
     if (!one_wave) {
         if (t < n) {
             s_in[t] = my_s;
@@ -164,24 +170,42 @@ __global__ void sample_kernel(const int32_t *__restrict__ idx, const int64_t *__
     }
     uint64_t u = 0;
     if (mode != 0 && t >= hw && t < hw + 64) u = sha256_draw(seed, position, (uint32_t)(t - hw));
-    if (t < n) {
-        const int64_t s = my_s;
-        const int32_t id = my_i;
-        auto beats = [&](int64_t sj, int32_t ij, int j) {
-            return (sj > s) || (sj == s && (ij < id || (ij == id && j < t)));
-        };
-        int r = 0;
-        if (one_wave) {
-            // candidate j straight from lane j's registers
-            for (int j = 0; j < n; ++j) {
-                const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)my_s, j);
-                const uint32_t hi =
-                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)my_s >> 32), j);
-                r += beats((int64_t)(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readlane(my_i, j), j);
+    // rank: the candidates before this one by (score desc, index asc,
+    // input position asc)
+    const int64_t s = my_s;
+    const int32_t id = my_i;
+    auto beats = [&](int64_t sj, int32_t ij, int j) {
+        return (sj > s) || (sj == s && (ij < id || (ij == id && j < cand)));
+    };
+    if (one_wave) {
+        // wavefront w compares against candidates [w * chunk, (w + 1) * chunk),
+        // each straight from lane j's registers
+        if (t < 64 * kRankWaves) {
+            const int w = t >> 6, chunk = (n + kRankWaves - 1) / kRankWaves;
+            const int j0 = w * chunk, j1 = min(n, j0 + chunk);
+            int r = 0;
+            if (cand < n) {
+                for (int j = j0; j < j1; ++j) {
+                    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)my_s, j);
+                    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(
+                        (int)(uint32_t)((uint64_t)my_s >> 32), j);
+                    r += beats((int64_t)(((uint64_t)hi << 32) | lo),
+                               __builtin_amdgcn_readlane(my_i, j), j);
+                }
             }
-        } else {
-            for (int j = 0; j < n; ++j) r += beats(s_in[j], i_in[j], j);
+            rk_part[w][t & 63] = r;
         }
+        __syncthreads();
+        if (t < n) {
+            int r = 0;
+#pragma unroll
+            for (int w = 0; w < kRankWaves; ++w) r += rk_part[w][t];
+            s_rk[r] = s;
+            i_rk[r] = id;
+        }
+    } else if (t < n) {
+        int r = 0;
+        for (int j = 0; j < n; ++j) r += beats(s_in[j], i_in[j], j);
         s_rk[r] = s;
         i_rk[r] = id;
     }
@@ -292,9 +316,10 @@ extern "C" int32_t bs_sample_candidates(const int32_t *idx, const int64_t *score
     if (top_p_q16 < 1 || top_p_q16 > 65536 || min_p_q16 > 65536) return BS_E_RANGE;
     if (((uintptr_t)idx & 3) || ((uintptr_t)score & 7) || ((uintptr_t)result & 7))
         return BS_E_ALIGN;
-    // the candidates' wavefronts and, when there is room, one more for the
-    // draw sources
-    const int threads = (n + 63) / 64 * 64 + ((n + 63) / 64 * 64 < kMaxCand ? 64 : 0);
+    // the candidates' wavefronts (kRankWaves for at most 64 candidates) and,
+    // when there is room, one more for the draw sources
+    const int nc = (n + 63) / 64 * 64;
+    const int threads = n <= 64 ? 64 * kRankWaves + 64 : nc + (nc < kMaxCand ? 64 : 0);
     hipLaunchKernelGGL(sample_kernel, dim3(1), dim3(threads), 0, (hipStream_t)stream, idx, score,
                        n, mode, beta_q16, top_p_q16, min_p_q16, seed, position, result);
     BS_LAUNCH_CHECK();
