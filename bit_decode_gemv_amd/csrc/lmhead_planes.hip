@@ -947,6 +947,8 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     __shared__ int l1id[kFinList];
     __shared__ unsigned long long pk1[kFinList], pk2[kFinList];
     __shared__ unsigned long long red4[kBlockThreads / 64][4], fin4[4];
+    __shared__ int l2[kFinList];
+    __shared__ int fast_fail;
     __shared__ int wtot[kBlockThreads / 64];
     __shared__ unsigned int nkept, nl1;
     __shared__ int ncand_sh;
@@ -1106,6 +1108,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
                 if (a >= cap) dropped[atomicAdd(&nkept, 1u)] = e;
             };
             if (t == 0) nkept = 0;               // here: the number dropped
+            if (t < 256) sh.hist[t] = 0;         // for the S' bound below
             // Each order as one 64-bit key when the list allows it:
             // ((okey(score) - least) << 17) | (2^17 - 1 - row) orders by
             // (score desc, row asc) when the scores span less than 2^47 and
@@ -1122,6 +1125,71 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
             const unsigned long long base1 = ~mx[1], base2 = ~mx[3];
             const bool packed = vocab <= (1 << 17) && mx[0] - base1 < (1ull << 47) &&
                                 mx[2] - base2 < (1ull << 47);
+            // The top_k by S' first: T2, the lower edge of the histogram bin
+            // (256 bins over the gathered rows' S' span) in which the count
+            // from the top reaches top_k; the m rows >= T2 are ranked among
+            // themselves by (S', row) and each by (S1', row) among all nl
+            // gathered rows.  When every one of them ranked below top_k by S'
+            // is within the cap, those are the output (the cap keeps them, and
+            // every other gathered row, kept or not, is below them by S');
+            // otherwise both orders are ranked over all nl rows below.
+            {
+                const unsigned long long span2 = mx[2] - base2;
+                const int shift2 = span2 >> 8 ? 64 - __clzll(span2) - 8 : 0;
+                if (t < nl) atomicAdd(&sh.hist[(int)((okey(l1s[t]) - base2) >> shift2)], 1u);
+                if (t == 0) {
+                    nl1 = 0;   // here: the rows >= T2
+                    fast_fail = 0;
+                }
+                __syncthreads();
+                if (t < 64) hist_edge(sh.hist, (unsigned)top_k, base2, shift2, t, &sh.bc[0]);
+                __syncthreads();
+                const unsigned long long t2 = sh.bc[0];
+                if (t < nl && okey(l1s[t]) >= t2) l2[atomicAdd(&nl1, 1u)] = t;
+                __syncthreads();
+                const int m = (int)nl1;   // >= top_k
+                if (m <= 256) {
+                    const int npad = (m + 63) & ~63;
+                    const int P = (int)blockDim.x / npad;
+                    const int e = t % npad;
+                    const int part = __builtin_amdgcn_readfirstlane(t / npad);
+                    int a = 0, b = 0;
+                    if (part < P && e < m) {
+                        const int q = l2[e];
+                        const long long q1 = l1s1[q], q2 = l1s[q];
+                        const int qid = l1id[q];
+                        const int c1 = (nl + P - 1) / P, c2 = (m + P - 1) / P;
+                        for (int j = part * c1; j < min(nl, (part + 1) * c1); ++j)
+                            a += better(l1s1[j], l1id[j], q1, qid) ? 1 : 0;
+                        for (int p2 = part * c2; p2 < min(m, (part + 1) * c2); ++p2) {
+                            const int j = l2[p2];
+                            b += better(l1s[j], l1id[j], q2, qid) ? 1 : 0;
+                        }
+                    }
+                    if (t < npad * P) {
+                        ro[t] = a;
+                        ti[t] = b;
+                    }
+                    __syncthreads();
+                    int ra = 0, rb = 0;
+                    if (t < m) {
+                        for (int q = 0; q < P; ++q) {
+                            ra += ro[q * npad + t];
+                            rb += ti[q * npad + t];
+                        }
+                        if (rb < top_k && ra >= cap) fast_fail = 1;
+                    }
+                    __syncthreads();
+                    if (!fast_fail) {
+                        if (t < m && rb < top_k) {
+                            const int q = l2[t];
+                            top_idx[rb] = l1id[q];
+                            top_score[rb] = l1s[q];
+                        }
+                        return;
+                    }
+                }
+            }
             if (packed) {
                 if (t < nl) {
                     const unsigned long long tie = (unsigned long long)((1 << 17) - 1 - l1id[t]);

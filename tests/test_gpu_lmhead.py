@@ -41,7 +41,11 @@ def check(trits, rs, h, top_k, cap, packed=None):
 @pytest.mark.parametrize("V,K,k,cap,seed", [(300, 128, 40, 200, 0), (257, 256, 7, 50, 1),
                                              (64, 128, 1, 1, 2), (100, 128, 100, 100, 3),
                                              (1000, 256, 40, 200, 4), (2049, 384, 16, 32, 5),
-                                             (5000, 128, 40, 4096, 6)])
+                                             (5000, 128, 40, 4096, 6),
+                                             # the top-k by S' includes a row the cap
+                                             # drops (the finishing pass falls back to
+                                             # ranking every gathered row) / does not
+                                             (4000, 256, 20, 20, 91), (3000, 256, 10, 10, 92)])
 def test_small_random(V, K, k, cap, seed):
     check(*synth.lmhead(V, K, seed), k, cap)
 
