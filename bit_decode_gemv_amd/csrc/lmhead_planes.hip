@@ -949,7 +949,8 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     __shared__ unsigned long long red4[kBlockThreads / 64][4], fin4[4];
     __shared__ int l2[kFinList];
     __shared__ int fast_fail;
-    __shared__ int wtot[kBlockThreads / 64];
+    __shared__ int wtot[kBlockThreads / 64], wcand[kBlockThreads / 64];
+    __shared__ int wpre[kBlockThreads / 64 + 1];
     __shared__ unsigned int nkept, nl1;
     __shared__ int ncand_sh;
     const int t = (int)threadIdx.x;
@@ -973,7 +974,8 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     }
     const long long head_pre = sp_s1[0];
     // exclusive prefix sums of the regions' stored counts, 1024 regions at a
-    // time, and the number of candidates
+    // time, and the number of candidates (wavefront 0 scans the wavefronts'
+    // totals once for all)
     if (t == 0) ncand_sh = 0;
     int n = 0;
     for (int r0 = 0; r0 < nwf; r0 += kBlockThreads) {
@@ -987,15 +989,26 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
             if (lane >= off) incl += o;
         }
         if (lane == 63) wtot[wave] = incl;
+        if (lane == 0) wcand[wave] = ca;
         __syncthreads();
-        if (lane == 0) atomicAdd(&ncand_sh, ca);
-        int before = n, chunk_total = 0;
-        for (int w = 0; w < nwaves; ++w) {
-            before += w < wave ? wtot[w] : 0;
-            chunk_total += wtot[w];
+        if (wave == 0) {
+            const int x = lane < nwaves ? wtot[lane] : 0;
+            const int y = wave_sum(lane < nwaves ? wcand[lane] : 0);
+            int inc = x;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int o = __shfl_up(inc, off);
+                if (lane >= off) inc += o;
+            }
+            if (lane < nwaves) wpre[lane] = inc - x;
+            if (lane == 63) {
+                wpre[nwaves] = inc;
+                ncand_sh += y;
+            }
         }
-        ro[t] = before + incl - c;
-        n += chunk_total;
+        __syncthreads();
+        ro[t] = n + wpre[wave] + incl - c;
+        n += wpre[nwaves];
         __syncthreads();
         if (nwf <= kBlockThreads) break;   // one pass: the candidates stay in their regions
         // more regions than one pass: copy them into the compacted arrays,
