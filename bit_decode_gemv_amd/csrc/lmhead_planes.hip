@@ -18,14 +18,14 @@
 //              path.  Writes E1 and the lower bound L per row, the largest L
 //              of every tile and of every workgroup, and the largest S1' of
 //              every tile;
-//   select  -- one workgroup: L_k = the top_k-th largest L.  The top_k-th
-//              largest maximum T over blocks of 8 tiles is a lower bound on
-//              L_k (top_k distinct rows reach it), so only the rows >= T of
-//              the tiles whose maximum reaches T take part, usually a few
-//              dozen.  Then T1, a lower bound on the max_candidates-th largest
-//              S1' from a histogram of the tiles' S1' maxima: when T1 >= L_k
-//              every row with S1' >= T1 is a candidate and the cap lies among
-//              them;
+//   select  -- one workgroup: L_k = the top_k-th largest L.  Histograms of
+//              the tiles' maxima give T, a lower bound on L_k (at least
+//              top_k tiles, so top_k distinct rows, reach it), so only the
+//              rows >= T of the tiles whose maximum reaches T take part,
+//              usually a few dozen (above 2048 tiles T comes from the block
+//              maxima instead); and T1, a lower bound on the
+//              max_candidates-th largest S1': when T1 >= L_k every row with
+//              S1' >= T1 is a candidate and the cap lies among them;
 //   filter  -- every row with U >= L_k becomes a candidate; those with
 //              S1' >= T1 (all of them when select found no T1) are rescored
 //              at once (E2 from D47, the wavefront's lanes over its
@@ -36,7 +36,9 @@
 //              there are more than fit one LDS list, the max_candidates-th
 //              largest region head bounds it from below, so only region
 //              prefixes are read), then the top_k of the kept rows by
-//              (S' desc, row asc).
+//              (S' desc, row asc): first among the rows a histogram bound on
+//              S' names, which is the answer when the cap keeps them all,
+//              else by ranking every gathered row in both orders.
 #include "kcommon.h"
 #include "dpp.h"
 
