@@ -715,39 +715,66 @@ __global__ __launch_bounds__(kFilterRows) void lmh_filter(const uint8_t *__restr
         const long long ars = rs < 0 ? -(long long)rs : (long long)rs;
         cand = s1 + 40LL * ars * habs >= lk;
     }
+    const bool keep = cand && s1 >= t1;
+    // this wavefront's rows to rescore, and the first pass of their planes
+    // 4-7 loads, issued before the workgroup-wide steps below so that their
+    // latency overlaps them
+    const uint64_t m = __ballot(keep);
+    const int nc = __popcll(m);
+    const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (keep) rowtab[wave][pos] = row;
+    e2l[wave][lane] = 0;
+    wave_lds_fence();
+    const int nrun = groups * 8;            // 16-byte runs per row
+    const int total = nc * nrun;
+    const size_t dim = (size_t)groups * 128;
+    uint4 w0[kResU];
+    int cix0[kResU], run0[kResU];
+#pragma unroll
+    for (int u = 0; u < kResU; ++u) {
+        const int f = 64 * u + lane;
+        cix0[u] = -1;
+        if (f < total) {
+            const int c = f / nrun;
+            const int p = f - c * nrun;
+            w0[u] = *reinterpret_cast<const uint4 *>(planes47 + (size_t)rowtab[wave][c] * dim +
+                                                     16 * (size_t)p);
+            cix0[u] = c;
+            run0[u] = p;
+        }
+    }
     const int ncand = __syncthreads_count(cand);
-    cand = cand && s1 >= t1;
-    const int nct = __syncthreads_count(cand);
+    const int nct = __syncthreads_count(keep);
     if (threadIdx.x == 0) {
         ws.region_count[blockIdx.x] = ncand;
         ws.region_kept[blockIdx.x] = nct;
     }
-    if (nct == 0) return;   // whole workgroup
-    const uint64_t m = __ballot(cand);
-    const int nc = __popcll(m);
-    const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    if (cand) rowtab[wave][pos] = row;
-    e2l[wave][lane] = 0;
+    if (nct == 0) return;   // whole workgroup (no loads were issued)
     if (lane == 0) wcount[wave] = nc;
     __syncthreads();
     int before = 0;
     for (int w = 0; w < wave; ++w) before += wcount[w];
-    if (cand) {
+    if (keep) {
         cs1[before + pos] = s1;
         crow[before + pos] = row;
     }
     __syncthreads();
     int rank = 0;   // position in the region: (S1' desc, row asc)
-    if (cand) {
+    if (keep) {
         for (int j = 0; j < nct; ++j) rank += better(cs1[j], crow[j], s1, row);
     }
     if (nc == 0) return;
 
-    const int nrun = groups * 8;            // 16-byte runs per row
-    const int total = nc * nrun;
-    const size_t dim = (size_t)groups * 128;
-    for (int f0 = 0; f0 < total; f0 += 64 * kResU) {
+#pragma unroll
+    for (int u = 0; u < kResU; ++u) {
+        if (cix0[u] >= 0) {
+            const uint4 hv = hs[run0[u]];
+            atomicAdd(&e2l[wave][cix0[u]],
+                      dot16(w0[u], (int)hv.x, (int)hv.y, (int)hv.z, (int)hv.w, 0));
+        }
+    }
+    for (int f0 = 64 * kResU; f0 < total; f0 += 64 * kResU) {
         uint4 w[kResU];
         int cix[kResU], run[kResU];
 #pragma unroll
@@ -773,7 +800,7 @@ __global__ __launch_bounds__(kFilterRows) void lmh_filter(const uint8_t *__restr
         }
     }
     wave_lds_fence();
-    if (cand) {
+    if (keep) {
         const size_t slot = (size_t)blockIdx.x * kFilterRows + rank;
         ws.cand[slot] = row;
         ws.cand_s1[slot] = s1;
