@@ -446,8 +446,17 @@ __device__ __forceinline__ void block_rank2(int n, Step1 step1, Step2 step2, Use
     if (part < P) {
         const int j0 = part * chunk, j1 = min(n, j0 + chunk);
         if (e < n) {
-#pragma unroll 8
-            for (int j = j0; j < j1; ++j) {
+            // eight at a time, written out: the compiler will not unroll
+            // loops holding inline assembly by a count that needs a remainder
+            int j = j0;
+            for (; j + 8 <= j1; j += 8) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    r1 = step1(j + k, e, r1);
+                    r2 = step2(j + k, e, r2);
+                }
+            }
+            for (; j < j1; ++j) {
                 r1 = step1(j, e, r1);
                 r2 = step2(j, e, r2);
             }
