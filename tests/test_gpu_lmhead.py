@@ -207,8 +207,20 @@ def test_rescore_bound_branches(case):
     idx, sc, info = bs.lmhead_planes_topk(to_dev(p03, dev), to_dev(p47, dev), to_dev(rs, dev),
                                           to_dev(h, dev), V, K, k, cap, workspace=ws)
     torch.cuda.synchronize()
-    t1 = int(ws[:24].view(torch.int64)[2].item())
+    lk_gpu, habs_gpu, t1 = (int(v) for v in ws[:24].view(torch.int64).cpu().tolist())
     assert (t1 != _NO_T1) == named, t1
+    # the intermediate values against the oracle's stage 1: sum|h| and L_k
+    # exactly, and a named T1 where the rescoring argument needs it (every row
+    # with S1' >= T1 a candidate, at least cap rows reaching it, so the cap
+    # lies among them)
+    s1, bnd = oracle.lmhead_stage1(trits, rs, h)
+    assert habs_gpu == int(np.abs(h.astype(np.int64)).sum())
+    lk = int(np.sort(s1 - bnd)[::-1][k - 1])
+    assert lk_gpu == lk
+    if named:
+        assert t1 >= lk
+        assert int((s1 >= t1).sum()) >= cap
+        assert t1 <= int(np.sort(s1)[::-1][cap - 1])
     widx, wsc, n, capped = oracle.lmhead_two_stage(trits, rs, h, k, cap)
     assert list(info.cpu().numpy()) == [n, capped]
     assert (idx.cpu().numpy() == widx).all()
