@@ -15,6 +15,7 @@ from bit_decode_gemv_amd import synth
 from gpu_util import device, note, to_dev
 
 pytestmark = pytest.mark.gpu
+_NO_T1 = -(1 << 63)   # the workspace's T1 when every candidate is rescored
 
 
 def run(trits, rs, h, top_k, cap, packed=None):
@@ -82,9 +83,27 @@ def test_negative_row_scales():
 
 @pytest.mark.slow
 def test_full_vocab_config():
-    """vocab 128256 x dim 2560, k = 40, cap = 200, seed 0."""
+    """vocab 128256 x dim 2560, k = 40, cap = 200, seed 0; the benchmark's
+    lm_head workload, where the select kernel names the rescoring bound T1
+    (its intermediate values are checked against the oracle's stage 1)."""
+    import torch
     trits, rs, h = synth.lmhead(*synth.LMHEAD_SHAPE, seed=0)
-    idx, sc, n, capped = check(trits, rs, h, 40, 200)
+    V, _, K = trits.shape
+    dev = device()
+    ws = torch.zeros(bs.lib().bs_lmhead_workspace_bytes(V, K, 40, 200), dtype=torch.uint8,
+                     device=dev)
+    p03, p47 = bs.planes_pack(trits)
+    note("lmhead full vocab V=%d K=%d" % (V, K))
+    bs.lmhead_planes_topk(to_dev(p03, dev), to_dev(p47, dev), to_dev(rs, dev), to_dev(h, dev),
+                          V, K, 40, 200, workspace=ws)
+    torch.cuda.synchronize()
+    lk_gpu, habs_gpu, t1 = (int(v) for v in ws[:24].view(torch.int64).cpu().tolist())
+    s1, bnd = oracle.lmhead_stage1(trits, rs, h)
+    assert habs_gpu == int(np.abs(h.astype(np.int64)).sum())
+    assert lk_gpu == int(np.sort(s1 - bnd)[::-1][39])
+    assert t1 != _NO_T1 and t1 >= lk_gpu and int((s1 >= t1).sum()) >= 200
+    assert t1 <= int(np.sort(s1)[::-1][199])
+    idx, sc, n, capped = check(trits, rs, h, 40, 200, packed=(p03, p47))
     bi, bsc = oracle.lmhead_brute(trits, rs, h, 40)
     same = bool((idx == bi).all() and (sc == bsc).all())
     print("full vocab: |C| = %d, capped = %d, equals brute force: %s" % (n, capped, same))
@@ -158,7 +177,6 @@ def test_max_dim():
 # rows.  T1 is the workspace's third int64 (INT64_MIN when every candidate is
 # rescored); the cases below pin which way each input goes, so each branch of
 # the finishing pass is reached, and check the result against the oracle.
-_NO_T1 = -(1 << 63)
 
 
 def _copies_of_top(V, K, seed, n, levels=None):
