@@ -76,8 +76,12 @@ __global__ void act_quant_kernel(const int64_t *__restrict__ x, int64_t k,
         }
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
-            const uint64_t a = abs_u64(v[j]);
-            m = a > m ? a : m;
+            // slots past k are skipped, by whole wavefronts where none holds a
+            // value, rather than folded in as zeros
+            if (threadIdx.x + (int64_t)j * blockDim.x < k) {
+                const uint64_t a = abs_u64(v[j]);
+                m = a > m ? a : m;
+            }
         }
     } else {
         for (int64_t i = threadIdx.x; i < k; i += blockDim.x) {
