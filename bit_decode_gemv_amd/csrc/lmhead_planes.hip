@@ -1097,7 +1097,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
         // when fewer than cap regions are non-empty, or when every row fits
         // the list below)
         const bool nonempty = t < nwf && (t + 1 < nwf ? ro[t + 1] : n) > ro[t];
-        const int nne = __syncthreads_count(nonempty);
+        const int nne = n > kFinList ? __syncthreads_count(nonempty) : 0;   // n is uniform
         unsigned long long thr = 0;
         if (nne >= cap && n > kFinList) {
             const unsigned long long head = nonempty ? okey(head_pre) : 0ull;
