@@ -63,6 +63,7 @@ def _declare(lib):
         "bs_planes_pack": (I32, [P, I64, I64, P, P]),
         "bs_lmhead_workspace_bytes": (SZ, [I64, I64, I32, I32]),
         "bs_lmhead_planes_topk": (I32, [P, P, P, P, I64, I64, I32, I32, P, P, P, P, SZ, P]),
+        "bs_lmhead_planes_topk_noalloc": (I32, [P, P, P, P, I64, I64, I32, I32, P, P, P, P]),
         "bs_act_quant_i8": (I32, [P, I64, P, P, P, P]),
         "bs_lns8_encode": (I32, [P, I64, I32, P, P]),
         "bs_lns8_encode_edges": (I32, [I32, P]),
@@ -393,6 +394,41 @@ def lmhead_planes_topk(planes03, planes47, row_scale, h, vocab: int, dim: int,
         _dptr(top_score, torch.int64, "top_score"), _dptr(info, torch.int32, "info"),
         wp, wn, _stream_handle(stream, dev))
     _check(rc, "bs_lmhead_planes_topk")
+    return top_idx, top_score, info
+
+
+LMHEAD_NOALLOC_MAX_VOCAB = 262144     # BS_LMHEAD_NOALLOC_MAX_VOCAB
+
+
+def lmhead_planes_topk_noalloc(planes03, planes47, row_scale, h, vocab: int, dim: int,
+                               top_k: int = 40, max_candidates: int = 200, top_idx=None,
+                               top_score=None, info=None, stream=None):
+    """bs_lmhead_planes_topk_noalloc: the lm_head top-k with the library's own
+    device scratch (no workspace).  Outputs as ``lmhead_planes_topk``; pass
+    preallocated ``top_idx``/``top_score``/``info`` to allocate nothing here
+    either."""
+    torch = _torch()
+    dev = h.device
+    if top_idx is None:
+        top_idx = torch.empty(top_k, dtype=torch.int32, device=dev)
+    if top_score is None:
+        top_score = torch.empty(top_k, dtype=torch.int64, device=dev)
+    if info is None:
+        info = torch.empty(2, dtype=torch.int32, device=dev)
+    _need(planes03, lib().bs_planes03_bytes(vocab, dim), "planes03")
+    _need(planes47, lib().bs_planes47_bytes(vocab, dim), "planes47")
+    _need(row_scale, vocab, "row_scale")
+    _need(h, dim, "h")
+    _need(top_idx, top_k, "top_idx")
+    _need(top_score, top_k, "top_score")
+    _need(info, 2, "info")
+    rc = lib().bs_lmhead_planes_topk_noalloc(
+        _dptr(planes03, torch.uint8, "planes03"), _dptr(planes47, torch.uint8, "planes47"),
+        _dptr(row_scale, torch.int32, "row_scale"), _dptr(h, torch.int8, "h"), vocab, dim,
+        top_k, max_candidates, _dptr(top_idx, torch.int32, "top_idx"),
+        _dptr(top_score, torch.int64, "top_score"), _dptr(info, torch.int32, "info"),
+        _stream_handle(stream, dev))
+    _check(rc, "bs_lmhead_planes_topk_noalloc")
     return top_idx, top_score, info
 
 

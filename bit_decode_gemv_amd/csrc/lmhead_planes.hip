@@ -39,6 +39,8 @@
 //              (S' desc, row asc): first among the rows a histogram bound on
 //              S' names, which is the answer when the cap keeps them all,
 //              else by ranking every gathered row in both orders.
+#include <mutex>
+
 #include "kcommon.h"
 #include "dpp.h"
 
@@ -1298,29 +1300,32 @@ struct LmhLayout {
     int tiles, nwg, nwf;
 };
 
+static constexpr size_t align_ws(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
 // Every region of the workspace is written before it is read, so it needs no
-// initialisation and calls of any shapes may share one workspace.
-static LmhLayout lmh_layout(int64_t vocab) {
-    LmhLayout L;
-    L.tiles = (int)(pad64(vocab) / 64);
+// initialisation and calls of any shapes may share one workspace.  The total
+// grows with vocab.
+static constexpr LmhLayout lmh_layout(int64_t vocab) {
+    LmhLayout L{};
+    L.tiles = (int)((vocab + 63) / 64);
     L.nwg = (L.tiles + kTilesPerBlock - 1) / kTilesPerBlock;
     L.nwf = (int)((vocab + kFilterRows - 1) / kFilterRows);
     const size_t slots = (size_t)L.nwf * kFilterRows;
     size_t off = 0;
     L.scalars = off;      off += kWsAlign;
-    L.e1 = off;           off += align_up((size_t)vocab * 4, kWsAlign);
-    L.lower = off;        off += align_up((size_t)vocab * 8, kWsAlign);
-    L.tile_max = off;     off += align_up((size_t)L.tiles * 8, kWsAlign);
-    L.wg_max = off;       off += align_up((size_t)L.nwg * 8, kWsAlign);
-    L.tile_max_s1 = off;  off += align_up((size_t)L.tiles * 8, kWsAlign);
-    L.region_count = off; off += align_up((size_t)L.nwf * 4, kWsAlign);
-    L.region_kept = off;  off += align_up((size_t)L.nwf * 4, kWsAlign);
-    L.cand = off;         off += align_up(slots * 4, kWsAlign);
-    L.cand_s1 = off;      off += align_up(slots * 8, kWsAlign);
-    L.cand_s = off;       off += align_up(slots * 8, kWsAlign);
-    L.cc = off;           off += align_up((size_t)vocab * 4, kWsAlign);
-    L.cc_s1 = off;        off += align_up((size_t)vocab * 8, kWsAlign);
-    L.cc_s = off;         off += align_up((size_t)vocab * 8, kWsAlign);
+    L.e1 = off;           off += align_ws((size_t)vocab * 4);
+    L.lower = off;        off += align_ws((size_t)vocab * 8);
+    L.tile_max = off;     off += align_ws((size_t)L.tiles * 8);
+    L.wg_max = off;       off += align_ws((size_t)L.nwg * 8);
+    L.tile_max_s1 = off;  off += align_ws((size_t)L.tiles * 8);
+    L.region_count = off; off += align_ws((size_t)L.nwf * 4);
+    L.region_kept = off;  off += align_ws((size_t)L.nwf * 4);
+    L.cand = off;         off += align_ws(slots * 4);
+    L.cand_s1 = off;      off += align_ws(slots * 8);
+    L.cand_s = off;       off += align_ws(slots * 8);
+    L.cc = off;           off += align_ws((size_t)vocab * 4);
+    L.cc_s1 = off;        off += align_ws((size_t)vocab * 8);
+    L.cc_s = off;         off += align_ws((size_t)vocab * 8);
     L.total = off;
     return L;
 }
@@ -1343,12 +1348,10 @@ extern "C" size_t bs_lmhead_workspace_bytes(int64_t vocab, int64_t dim, int32_t 
     return lmh_layout(vocab).total;
 }
 
-extern "C" int32_t bs_lmhead_planes_topk(const uint8_t *planes03, const uint8_t *planes47,
-                                         const int32_t *row_scale, const int8_t *h,
-                                         int64_t vocab, int64_t dim, int32_t top_k,
-                                         int32_t max_candidates, int32_t *top_idx,
-                                         int64_t *top_score, int32_t *info, void *workspace,
-                                         size_t workspace_bytes, void *stream) {
+static int32_t lmh_args(const uint8_t *planes03, const uint8_t *planes47,
+                        const int32_t *row_scale, const int8_t *h, int64_t vocab, int64_t dim,
+                        int32_t top_k, int32_t max_candidates, const int32_t *top_idx,
+                        const int64_t *top_score, const int32_t *info) {
     if (!planes03 || !planes47 || !row_scale || !h || !top_idx || !top_score || !info)
         return BS_E_NULL;
     if (int32_t st = lmh_check(vocab, dim, top_k, max_candidates)) return st;
@@ -1356,10 +1359,16 @@ extern "C" int32_t bs_lmhead_planes_topk(const uint8_t *planes03, const uint8_t 
         ((uintptr_t)h & 7) || ((uintptr_t)top_idx & 3) || ((uintptr_t)top_score & 7) ||
         ((uintptr_t)info & 3))
         return BS_E_ALIGN;
-    const LmhLayout L = lmh_layout(vocab);
-    if (!ws_ok(workspace, workspace_bytes, L.total)) return BS_E_WORKSPACE;
+    return BS_OK;
+}
 
-    unsigned char *base = static_cast<unsigned char *>(workspace);
+// The four kernels on `stream`, with the scratch regions of lmh_layout(vocab)
+// at `base` (256-byte aligned, device memory of at least L.total bytes).
+static int32_t lmh_launch(const uint8_t *planes03, const uint8_t *planes47,
+                          const int32_t *row_scale, const int8_t *h, int64_t vocab, int64_t dim,
+                          int32_t top_k, int32_t max_candidates, int32_t *top_idx,
+                          int64_t *top_score, int32_t *info, unsigned char *base,
+                          const LmhLayout &L, hipStream_t st) {
     LmhWs ws;
     ws.scalars = reinterpret_cast<long long *>(base + L.scalars);
     ws.e1 = reinterpret_cast<int *>(base + L.e1);
@@ -1376,7 +1385,6 @@ extern "C" int32_t bs_lmhead_planes_topk(const uint8_t *planes03, const uint8_t 
     ws.cc_s1 = reinterpret_cast<long long *>(base + L.cc_s1);
     ws.cc_s = reinterpret_cast<long long *>(base + L.cc_s);
 
-    hipStream_t st = (hipStream_t)stream;
     const int groups = (int)(dim / 128);
     hipLaunchKernelGGL(lmh_stage1, dim3(L.nwg), dim3(kStage1Threads), 0, st, planes03, row_scale,
                        reinterpret_cast<const int32_t *>(h), (int)vocab, groups, ws);
@@ -1391,4 +1399,85 @@ extern "C" int32_t bs_lmhead_planes_topk(const uint8_t *planes03, const uint8_t 
                        max_candidates, top_idx, top_score, info, ws);
     BS_LAUNCH_CHECK();
     return BS_OK;
+}
+
+extern "C" int32_t bs_lmhead_planes_topk(const uint8_t *planes03, const uint8_t *planes47,
+                                         const int32_t *row_scale, const int8_t *h,
+                                         int64_t vocab, int64_t dim, int32_t top_k,
+                                         int32_t max_candidates, int32_t *top_idx,
+                                         int64_t *top_score, int32_t *info, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+    if (int32_t st = lmh_args(planes03, planes47, row_scale, h, vocab, dim, top_k,
+                              max_candidates, top_idx, top_score, info))
+        return st;
+    const LmhLayout L = lmh_layout(vocab);
+    if (!ws_ok(workspace, workspace_bytes, L.total)) return BS_E_WORKSPACE;
+    return lmh_launch(planes03, planes47, row_scale, h, vocab, dim, top_k, max_candidates,
+                      top_idx, top_score, info, static_cast<unsigned char *>(workspace), L,
+                      (hipStream_t)stream);
+}
+
+// ------------------------------------------------ allocation-free variant
+//
+// The scratch of bs_lmhead_planes_topk_noalloc lives in this file-scope
+// device array, sized for the largest vocabulary the variant accepts; every
+// GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: host
+// code only ever passes the address that hipGetSymbolAddress returned for
+// the device, looked up once per device (with that device current) on the
+// variant's first call there.
+constexpr int64_t kLmhNoAllocMaxVocab = BS_LMHEAD_NOALLOC_MAX_VOCAB;
+constexpr size_t kLmhScratchBytes = lmh_layout(kLmhNoAllocMaxVocab).total;
+static_assert(kLmhScratchBytes % kWsAlign == 0, "scratch is a whole number of regions");
+
+static __device__ __align__(256) unsigned char scratch[kLmhScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // per device; written once under the mutex
+
+// The device address of `scratch` on device `dev`, looked up on first use.
+int32_t scratch_for(int dev, unsigned char **out) {
+    if (dev < 0 || dev >= kMaxDevices) return BS_E_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return BS_E_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return BS_E_HIP;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return BS_E_HIP;
+        if (e != hipSuccess || p == nullptr || ((uintptr_t)p % kWsAlign) != 0) return BS_E_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<unsigned char *>(g_scratch_ptr[dev]);
+    return BS_OK;
+}
+}  // namespace
+
+extern "C" int32_t bs_lmhead_planes_topk_noalloc(const uint8_t *planes03,
+                                                 const uint8_t *planes47,
+                                                 const int32_t *row_scale, const int8_t *h,
+                                                 int64_t vocab, int64_t dim, int32_t top_k,
+                                                 int32_t max_candidates, int32_t *top_idx,
+                                                 int64_t *top_score, int32_t *info,
+                                                 void *stream) {
+    if (int32_t st = lmh_args(planes03, planes47, row_scale, h, vocab, dim, top_k,
+                              max_candidates, top_idx, top_score, info))
+        return st;
+    if (vocab > kLmhNoAllocMaxVocab) return BS_E_WORKSPACE;
+    const LmhLayout L = lmh_layout(vocab);
+    if (L.total > kLmhScratchBytes) return BS_E_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    int dev = -1;
+    if (st != nullptr) {
+        if (hipStreamGetDevice(st, &dev) != hipSuccess) return BS_E_HIP;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return BS_E_HIP;
+    }
+    unsigned char *base = nullptr;
+    if (int32_t rc = scratch_for(dev, &base)) return rc;
+    return lmh_launch(planes03, planes47, row_scale, h, vocab, dim, top_k, max_candidates,
+                      top_idx, top_score, info, base, L, st);
 }

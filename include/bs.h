@@ -20,7 +20,8 @@
  *     default stream) and return after enqueueing.  Results are valid once
  *     the stream reaches that point.  The library never allocates or frees
  *     device memory; entry points that need scratch take the caller's
- *     `workspace`.
+ *     `workspace` (bs_lmhead_planes_topk_noalloc uses a device array of the
+ *     library's own instead).
  *   - Fail-loud overflow contract ([IE] section 3.4): a call whose shapes
  *     would let an intermediate exceed its integer type returns
  *     BS_E_OVERFLOW instead of wrapping.
@@ -332,6 +333,32 @@ int32_t bs_lmhead_planes_topk(const uint8_t *planes03, const uint8_t *planes47,
                               int64_t dim, int32_t top_k, int32_t max_candidates,
                               int32_t *top_idx, int64_t *top_score, int32_t *info,
                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * bs_lmhead_planes_topk_noalloc -- bs_lmhead_planes_topk for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same computation, arguments,
+ * outputs and errors, without the workspace arguments.  Its scratch is a
+ * file-scope device array of the library, sized for
+ * vocab <= BS_LMHEAD_NOALLOC_MAX_VOCAB (13,713,664 bytes; each GPU the library
+ * runs on holds its own copy until the process ends).  The call allocates
+ * nothing: no hipMalloc, hipFree or allocating library routine.  Its first
+ * call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress; a HIP failure there gives BS_E_HIP).  Every byte of
+ * the scratch is written before it is read, so it needs no clearing and the
+ * contents left by an earlier call do not matter.
+ *   vocab   additionally <= BS_LMHEAD_NOALLOC_MAX_VOCAB, else BS_E_WORKSPACE
+ *   stream  the device is the stream's (the current device for NULL)
+ * All calls on one GPU share its one scratch array: calls that may overlap on
+ * one GPU (different streams, or different host threads without ordering)
+ * race and give undefined results; order them on one stream.
+ */
+#define BS_LMHEAD_NOALLOC_MAX_VOCAB 262144
+int32_t bs_lmhead_planes_topk_noalloc(const uint8_t *planes03, const uint8_t *planes47,
+                                      const int32_t *row_scale, const int8_t *h, int64_t vocab,
+                                      int64_t dim, int32_t top_k, int32_t max_candidates,
+                                      int32_t *top_idx, int64_t *top_score, int32_t *info,
+                                      void *stream);
 
 /* ======================================================================== */
 /* Activation encoders upstream of the GEMVs                                 */
