@@ -328,6 +328,218 @@ __global__ void ternary_tile_kernel(const uint8_t *__restrict__ planes,
     }
 }
 
+// v summed with the lane 8 apart within each 16-lane row (DPP row rotate by
+// 8: lane i of a row reads lane (i + 8) mod 16, its xor-8 partner).
+__device__ __forceinline__ int64_t add_partner8(int64_t v) {
+    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)((uint64_t)v >> 32);
+    const uint32_t l = (uint32_t)__builtin_amdgcn_mov_dpp(lo, 0x128, 0xF, 0xF, false);
+    const uint32_t h = (uint32_t)__builtin_amdgcn_mov_dpp(hi, 0x128, 0xF, 0xF, false);
+    return v + (int64_t)(((uint64_t)h << 32) | l);
+}
+
+__device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+    return make_uint2(v.x, v.y);
+}
+
+// Pipelined mapping.  A workgroup owns R rows of one 64-row tile (R = 8, 16,
+// 32 or 64) and all of K; its NW wavefronts hold S = 64/R slices each, lane l of
+// wavefront w serving row (l mod R) in slice w*S + l/R, and slice s takes the
+// groups s, s + NW*S, ... (NG of them).  Phases:
+//   1. every lane loads its share of x (8 bytes per chunk) and then the
+//      weights of its first D groups: vmcnt retires loads in order, so the
+//      activations can be used while the weights are still in flight;
+//   2. the workgroup turns x into bit planes in LDS (one 8x8 bit transpose
+//      per 8 positions; group g's plane b at xpl[g*9 + b], position i of the
+//      group at bit i%32 of word i/32), then one barrier;
+//   3. group q of the slice is computed while the loads of groups q+1..q+D
+//      are in flight.
+// Every load is unconditional: the buffer resources bound each one to its
+// tile, its scale block and x, and a load past the end reads zero, so the
+// wait counts are static and a padding slot contributes 0.  Slices of a
+// wavefront meet by lane permutations, wavefronts in LDS.
+template <int R, int NW, int NG, int D>
+__global__ __launch_bounds__(NW * 64) void ternary_pipe_kernel(
+    const uint8_t *__restrict__ planes, const int16_t *__restrict__ pscales,
+    const int8_t *__restrict__ x, int rows, int groups, int shift, int64_t *__restrict__ y) {
+    constexpr int S = 64 / R, NS = NW * S, NT = NW * 64;
+    constexpr int MAXG = NS * NG;                    // groups the slots cover
+    constexpr int XP = (MAXG * 16 + NT - 1) / NT;    // 8-position chunks per thread
+    static_assert(R == 8 || R == 16 || R == 32 || R == 64, "row block");
+    static_assert(D >= 1 && D <= NG, "pipeline depth");
+    __shared__ uint4 xpl[(MAXG + 1) * kPlaneStride];  // + one slot for chunks past K
+    __shared__ int64_t part[NW][R];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int sl = wave * S + lane / R;
+    const int row0 = (int)blockIdx.x * R;
+    const int tile = row0 >> 6;
+    const int j = (row0 & 63) + lane % R;            // row within the tile
+    const __amdgpu_buffer_rsrc_t rp =
+        buffer_rsrc(planes + (size_t)tile * groups * 2048, (uint32_t)groups * 2048);
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(pscales + (size_t)tile * 64 * groups, (uint32_t)groups * 128);
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)groups * 128);
+    const uint32_t w_off = 16u * j;
+    const uint32_t sc_off = (uint32_t)(((j >> 4) * groups * 16 + (j & 15)) * 2);
+
+    uint2 xv[XP];
+#pragma unroll
+    for (int p = 0; p < XP; ++p) xv[p] = buffer_load8(rx, 8u * (threadIdx.x + p * NT));
+    __builtin_amdgcn_sched_barrier(0);
+    // the first D groups: scales, then planes (the compiler schedules a lone
+    // scale load, NG = 1, after the barrier below; measured faster there)
+    uint4 nz[NG], ng[NG];
+    int sc[NG];
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+        if (q < D) sc[q] = buffer_load_i16(rs, sc_off + (uint32_t)(sl + q * NS) * 32u, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+        if (q < D) {
+            const uint32_t g = (uint32_t)(sl + q * NS);
+            nz[q] = buffer_load_stream16(rp, g * 2048u + w_off, 0);
+            ng[q] = buffer_load_stream16(rp, g * 2048u + 1024u + w_off, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < XP; ++p) {
+        const int c = threadIdx.x + p * NT;
+        const uint64_t t8 = transpose8x8((uint64_t)xv[p].x | ((uint64_t)xv[p].y << 32));
+        const int gi = c < groups * 16 ? (c >> 4) : MAXG;
+        uint8_t *dst = reinterpret_cast<uint8_t *>(xpl + gi * kPlaneStride) + (c & 15);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) dst[b * 16] = (uint8_t)(t8 >> (8 * b));
+    }
+    __syncthreads();
+    int64_t acc = 0;
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+        if (q + D < NG) {
+            const uint32_t g = (uint32_t)(sl + (q + D) * NS);
+            nz[q + D] = buffer_load_stream16(rp, g * 2048u + w_off, 0);
+            ng[q + D] = buffer_load_stream16(rp, g * 2048u + 1024u + w_off, 0);
+            sc[q + D] = buffer_load_i16(rs, sc_off + g * 32u, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int g = sl + q * NS;
+        const uint4 *xg = xpl + (g < groups ? g : 0) * kPlaneStride;   // padding: any group
+        uint4 xr[8];                      // all eight planes in flight at once
+#pragma unroll
+        for (int b = 0; b < 8; ++b) xr[b] = xg[b];
+        const int s = group_dot(nz[q], ng[q], xr);
+        acc += (int64_t)(__mul24(s, sc[q]) >> shift);   // |s * sc| <= 2^29; >> = floor
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (S == 8) acc = add_partner8(acc);
+    if constexpr (S >= 4) acc = add_partner<false>(acc);
+    if constexpr (S >= 2) acc = add_partner<true>(acc);
+    if (lane < R) part[wave][lane] = acc;
+    __syncthreads();
+    if (threadIdx.x < R) {
+        int64_t tot = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) tot += part[w][threadIdx.x];
+        const int r = row0 + (int)threadIdx.x;
+        if (r < rows) y[r] = tot;
+    }
+}
+
+// Launch shape of the pipelined kernel, from sweeps of (R, wavefronts,
+// groups per slice) on MI355X with cold weights, every configuration checked
+// bit-exact.  Short matrices want many small workgroups (8 rows, one group
+// per slice); taller ones longer per-slice pipelines (3 to 6 groups) on 16-
+// or 32-row blocks; the winners per K range:
+//   K <= 3072:  <= 4096 rows 8-row blocks, 1 group per slice; <= 9000 rows
+//               32-row blocks of 4 wavefronts; taller 16-row blocks of one
+//               wavefront with up to 6 groups per slice;
+//   K <= 5120:  from 6400 rows 32-row blocks of 4 wavefronts, else 16-row
+//               blocks with 2 groups per slice;
+//   K <= 8192:  16-row blocks with 2 groups per slice;
+//   K <= 12288: 16-row blocks of 8 wavefronts, 3 groups per slice;
+//   K <= 16384: 32-row blocks of 9 wavefronts, 6 to 8 groups per slice.
+// Measured per launch (events, back-to-back): 2560x2560 3.10 -> 2.68 us,
+// 6912x2560 3.60 -> 3.24, 11008x4096 4.70 -> 4.39, 13824x5120 5.28 -> 5.08,
+// 2560x6912 3.92 -> 3.34, 5120x13824 7.02 -> 6.44 against the row-block and
+// tile kernels.
+struct PipeCfg {
+    int R, NW, NG;
+};
+
+constexpr int kPipeMaxGroups = 128;   // K <= 16384; larger K takes the row-block kernel
+
+static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+static PipeCfg choose_pipe(int64_t rows, int64_t groups) {
+    if (groups <= 24) {
+        if (rows <= 4096) return {8, cdiv(groups, 8), 1};
+        if (rows <= 9000) return {32, 4, cdiv(groups, 8)};
+        return {16, 1, cdiv(groups, 4)};
+    }
+    if (groups <= 40) {
+        if (rows >= 6400) return {32, 4, cdiv(groups, 8)};
+        return {16, cdiv(groups, 8), 2};
+    }
+    if (groups <= 64) return {16, cdiv(groups, 8), 2};
+    if (groups <= 96) return {16, 8, 3};
+    return {32, 9, cdiv(groups, 18)};
+}
+
+template <int R, int NW, int NG>
+static void launch_pipe1(hipStream_t st, const uint8_t *planes, const int16_t *scales,
+                         const int8_t *x, int rows, int groups, int shift, int64_t *y) {
+    constexpr int D = NG < 2 ? NG : 2;
+    const unsigned nblk = (unsigned)((rows + R - 1) / R);
+    hipLaunchKernelGGL((ternary_pipe_kernel<R, NW, NG, D>), dim3(nblk), dim3(NW * 64), 0, st,
+                       planes, scales, x, rows, groups, shift, y);
+}
+
+// Dispatch over NW (R, NG fixed) or over NG (R, NW fixed), LO..HI.
+template <int R, int NG, int NW, int HI>
+static bool pipe_by_nw(int nw, hipStream_t st, const uint8_t *p, const int16_t *s,
+                       const int8_t *x, int rows, int groups, int shift, int64_t *y) {
+    if constexpr (NW > HI) {
+        return false;
+    } else {
+        if (nw == NW) {
+            launch_pipe1<R, NW, NG>(st, p, s, x, rows, groups, shift, y);
+            return true;
+        }
+        return pipe_by_nw<R, NG, NW + 1, HI>(nw, st, p, s, x, rows, groups, shift, y);
+    }
+}
+
+template <int R, int NW, int NG, int HI>
+static bool pipe_by_ng(int ng, hipStream_t st, const uint8_t *p, const int16_t *s,
+                       const int8_t *x, int rows, int groups, int shift, int64_t *y) {
+    if constexpr (NG > HI) {
+        return false;
+    } else {
+        if (ng == NG) {
+            launch_pipe1<R, NW, NG>(st, p, s, x, rows, groups, shift, y);
+            return true;
+        }
+        return pipe_by_ng<R, NW, NG + 1, HI>(ng, st, p, s, x, rows, groups, shift, y);
+    }
+}
+
+static bool launch_pipe(const PipeCfg &c, hipStream_t st, const uint8_t *p, const int16_t *s,
+                        const int8_t *x, int rows, int groups, int shift, int64_t *y) {
+    if (c.R == 8 && c.NG == 1) return pipe_by_nw<8, 1, 1, 3>(c.NW, st, p, s, x, rows, groups, shift, y);
+    if (c.R == 32 && c.NW == 4) return pipe_by_ng<32, 4, 1, 5>(c.NG, st, p, s, x, rows, groups, shift, y);
+    if (c.R == 16 && c.NW == 1) return pipe_by_ng<16, 1, 1, 6>(c.NG, st, p, s, x, rows, groups, shift, y);
+    if (c.R == 16 && c.NG == 2) return pipe_by_nw<16, 2, 1, 8>(c.NW, st, p, s, x, rows, groups, shift, y);
+    if (c.R == 16 && c.NW == 8 && c.NG == 3) {
+        launch_pipe1<16, 8, 3>(st, p, s, x, rows, groups, shift, y);
+        return true;
+    }
+    if (c.R == 32 && c.NW == 9) return pipe_by_ng<32, 9, 6, 8>(c.NG, st, p, s, x, rows, groups, shift, y);
+    return false;
+}
+
 struct TernaryCfg {
     bool tile;            // tile mapping (ternary_tile_kernel) with `waves` wavefronts
     int rows_per_block;   // R: 32 or 16 (64 for the tile mapping)
@@ -465,6 +677,15 @@ extern "C" int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales,
                                    const int8_t *x, int64_t rows, int64_t k, int32_t frac,
                                    int64_t *y, void *stream) {
     if (int32_t st = gemv_check(planes, scales, x, rows, k, frac, y)) return st;
+    const int64_t groups = k / kGroup;
+    if (groups <= kPipeMaxGroups) {
+        const int shift = frac > 31 ? 31 : frac;   // |scale*s| < 2^31: shift 31 is floor
+        if (!launch_pipe(choose_pipe(rows, groups), (hipStream_t)stream, planes, scales, x,
+                         (int)rows, (int)groups, shift, y))
+            return BS_E_RANGE;
+        BS_LAUNCH_CHECK();
+        return BS_OK;
+    }
     return launch_ternary<false>(choose_cfg(rows, k, false), planes, scales, x, rows, k, frac, y,
                                  (hipStream_t)stream);
 }

@@ -69,6 +69,27 @@ def test_tile_mapping_edges(rows, k):
     check(*synth.ternary(rows, k, seed=rows ^ k, p_zero=1 / 3, act="uniform127"))
 
 
+@pytest.mark.parametrize("rows,k", [(1024, 2560), (1025, 2560), (8191, 2560), (8192, 2560),
+                                    (8192, 8192), (8192, 8320), (8255, 1024), (2000, 16384),
+                                    (2000, 16512), (1023, 128 * 127), (300, 16384),
+                                    (7, 2560), (9, 1152), (17, 4224), (1, 16384)])
+def test_pipelined_launch_rule(rows, k):
+    """Either side of the pipelined kernel's launch-shape bounds: 8-row blocks
+    up to 1024 rows, the 64-row workgroups from 8192 rows up to 64 groups,
+    16-row blocks otherwise, up to 128 groups (129 takes the row-block
+    kernel); ragged blocks and tiles."""
+    check(*synth.ternary(rows, k, seed=rows + k, p_zero=1 / 3, act="uniform127"))
+
+
+@pytest.mark.parametrize("groups", [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 40, 63, 64, 65,
+                                    86, 100, 108, 120, 127, 128])
+@pytest.mark.parametrize("rows", [40, 1500, 8200])
+def test_pipelined_wavefront_counts(groups, rows):
+    """Every wavefront count and groups-per-slice of the pipelined kernel
+    (padding slots past K, partly filled last rounds)."""
+    check(*synth.ternary(rows, 128 * groups, seed=groups * 7 + rows, p_zero=0.4))
+
+
 @pytest.mark.parametrize("seed", range(2))
 @pytest.mark.parametrize("shape", synth.LARGE_K_SHAPES)
 def test_large_k(shape, seed):
