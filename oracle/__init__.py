@@ -36,11 +36,13 @@ _lib = None
 
 def build(force: bool = True) -> str:
     """Compile the C oracle with gcc (-O2, no intrinsics) into liboracle.so.
-    flns_oracle.c uses GCC's binary128 (libquadmath), hence gnu11."""
+    flns_oracle.c uses GCC's binary128 (libquadmath), hence gnu11; -fopenmp
+    only for the row-parallel forms of the CPU baseline."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=gnu11", "-Wall", "-Wextra", "-shared",
-                               "-fPIC", _SRC, _SRC_FLNS, "-o", tmp, "-lquadmath", "-lm"])
+        subprocess.check_call(["gcc", "-O2", "-std=gnu11", "-Wall", "-Wextra", "-fopenmp",
+                               "-shared", "-fPIC", _SRC, _SRC_FLNS, "-o", tmp, "-lquadmath",
+                               "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -58,7 +60,8 @@ def _load():
                      "or_lmhead_brute", "or_lmhead_two_stage", "or_lmhead_stage1",
                      "or_planes_pack", "or_q1_gemv_def", "or_q1_pack", "or_q1_gemv_masked",
                      "or_flns_tables", "or_flns_log_scale", "or_flns_add", "or_flns_tree",
-                     "or_flns_gemv"):
+                     "or_flns_gemv", "or_ternary_gemv_def_mt", "or_lns8_direct_mt",
+                     "or_lmhead_brute_mt", "or_max_threads"):
             getattr(lib, name).restype = ctypes.c_int
         lib.or_pad64.restype = ctypes.c_int64
         lib.or_pad64.argtypes = [ctypes.c_int64]
@@ -98,6 +101,28 @@ def ternary_gemv_def(t: np.ndarray, scales: np.ndarray, x: np.ndarray, frac: int
     y = np.zeros(rows, dtype=np.int64)
     _check(_load().or_ternary_gemv_def(_p(t), _p(scales), _p(x), _i64(rows), _i64(k),
                                        ctypes.c_int(frac), _p(y)), "ternary_gemv_def")
+    return y
+
+
+def set_threads(n: int) -> int:
+    """Threads the row-parallel forms use (OpenMP); returns the maximum now
+    in effect."""
+    lib = _load()
+    lib.or_set_threads(ctypes.c_int(int(n)))
+    return int(lib.or_max_threads())
+
+
+def ternary_gemv_def_mt(t: np.ndarray, scales: np.ndarray, x: np.ndarray, frac: int = 0):
+    """The definition form with its rows on all OpenMP threads (identical
+    results; the CPU baseline's all-core leg)."""
+    t = np.ascontiguousarray(t, dtype=np.int8)
+    scales = np.ascontiguousarray(scales, dtype=np.int16)
+    x = np.ascontiguousarray(x, dtype=np.int8)
+    rows, k = t.shape
+    assert scales.shape == (rows, k // 128) and x.shape == (k,)
+    y = np.zeros(rows, dtype=np.int64)
+    _check(_load().or_ternary_gemv_def_mt(_p(t), _p(scales), _p(x), _i64(rows), _i64(k),
+                                          ctypes.c_int(frac), _p(y)), "ternary_gemv_def_mt")
     return y
 
 
@@ -160,6 +185,11 @@ def _lns8_call(fn: str, t, x, hist=False):
 def lns8_direct(t, x):
     """(i) scalar direct routing A[L3] += sign*(1 << E4)."""
     return _lns8_call("or_lns8_direct", t, x)
+
+
+def lns8_direct_mt(t, x):
+    """(i) with the rows on all OpenMP threads (identical results)."""
+    return _lns8_call("or_lns8_direct_mt", t, x)
 
 
 def lns8_tile64(t, x):
@@ -302,6 +332,20 @@ def lmhead_brute(trits, row_scale, h, top_k: int, all_scores: bool = False):
                                    ctypes.c_int(top_k), _p(idx), _p(sc), _p(allsc)),
            "lmhead_brute")
     return (idx, sc, allsc) if all_scores else (idx, sc)
+
+
+def lmhead_brute_mt(trits, row_scale, h, top_k: int):
+    """Brute force with the per-row scores on all OpenMP threads (identical
+    results; the CPU baseline's all-core leg)."""
+    trits = np.ascontiguousarray(trits, dtype=np.int8)
+    row_scale = np.ascontiguousarray(row_scale, dtype=np.int32)
+    h = np.ascontiguousarray(h, dtype=np.int8)
+    V, _, K = trits.shape
+    idx = np.zeros(top_k, dtype=np.int32)
+    sc = np.zeros(top_k, dtype=np.int64)
+    _check(_load().or_lmhead_brute_mt(_p(trits), _p(row_scale), _p(h), _i64(V), _i64(K),
+                                      ctypes.c_int(top_k), _p(idx), _p(sc)), "lmhead_brute_mt")
+    return idx, sc
 
 
 def lmhead_two_stage(trits, row_scale, h, top_k: int, cap: int):

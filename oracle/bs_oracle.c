@@ -647,3 +647,124 @@ int or_lmhead_stage1(const int8_t *trits, const int32_t *row_scale, const int8_t
     }
     return OR_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Row-parallel forms (the benchmark's all-core CPU baseline)                */
+/* ------------------------------------------------------------------------ */
+/*
+ * The definition forms above with their rows shared out over OpenMP threads
+ * (the library is built with -fopenmp).  Each row runs the same loop, in the
+ * same order, as the single-thread form, and rows are independent, so the
+ * results are identical; the input checks run first because a parallel loop
+ * cannot return early.  Only the benchmark's CPU-baseline leg and the test
+ * that compares them with the single-thread forms call these.
+ */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+void or_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int or_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static int trits_ok(const int8_t *t, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        if (t[i] < -1 || t[i] > 1)
+            return 0;
+    return 1;
+}
+
+int or_ternary_gemv_def_mt(const int8_t *t, const int16_t *scale, const int8_t *x,
+                           int64_t rows, int64_t k, int frac, int64_t *y)
+{
+    if (rows < 0 || k < 0 || k % 128 != 0)
+        return OR_E_SHAPE;
+    if (frac < 0 || frac > 62)
+        return OR_E_RANGE;
+    if (!trits_ok(t, rows * k))
+        return OR_E_RANGE;
+    int64_t groups = k / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        int64_t acc = 0;
+        for (int64_t g = 0; g < groups; g++) {
+            int64_t s = 0;
+            for (int64_t i = g * 128; i < g * 128 + 128; i++)
+                s += (int64_t)t[r * k + i] * (int64_t)x[i];
+            acc += floor_shift(s * (int64_t)scale[r * groups + g], frac);
+        }
+        y[r] = acc;
+    }
+    return OR_OK;
+}
+
+int or_lns8_direct_mt(const int8_t *t, const uint8_t *x, int64_t rows, int64_t k, int64_t *acc)
+{
+    if (rows < 0 || k < 0)
+        return OR_E_SHAPE;
+    if (!trits_ok(t, rows * k))
+        return OR_E_RANGE;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        int64_t *A = acc + r * 8;
+        for (int p = 0; p < 8; p++)
+            A[p] = 0;
+        for (int64_t i = 0; i < k; i++) {
+            int8_t w = t[r * k + i];
+            int code = x[i] & 0x7F;
+            int s1 = x[i] >> 7;
+            if (w == 0 || code == 0)
+                continue;
+            int negative = s1 ^ (w < 0);
+            int phase = code & 7, band = code >> 3;
+            int64_t payload = (int64_t)1 << band;
+            A[phase] += negative ? -payload : payload;
+        }
+    }
+    return OR_OK;
+}
+
+/* Brute force with the per-row scores on all threads; the final sort is the
+ * single-thread form's. */
+int or_lmhead_brute_mt(const int8_t *trits, const int32_t *row_scale, const int8_t *h,
+                       int64_t V, int64_t K, int top_k, int32_t *top_idx, int64_t *top_score)
+{
+    if (V < 1 || K < 1 || top_k < 1 || top_k > V)
+        return OR_E_RANGE;
+    if (!trits_ok(trits, V * 8 * K))
+        return OR_E_RANGE;
+    keyed_row *rows = (keyed_row *)malloc((size_t)V * sizeof(keyed_row));
+    if (!rows)
+        return OR_E_RANGE;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < V; r++) {
+        int64_t e = 0;
+        for (int p = 0; p < 8; p++)
+            e += POW3[7 - p] * plane_dot(trits, h, r, p, K);
+        rows[r].key = (int64_t)row_scale[r] * e;
+        rows[r].idx = r;
+    }
+    qsort(rows, (size_t)V, sizeof(keyed_row), cmp_desc);
+    for (int i = 0; i < top_k; i++) {
+        top_idx[i] = (int32_t)rows[i].idx;
+        top_score[i] = rows[i].key;
+    }
+    free(rows);
+    return OR_OK;
+}

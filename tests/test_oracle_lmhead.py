@@ -199,3 +199,13 @@ def test_planes_digits_keep_every_trit():
 
     assert (digits(d03) == trits[:, 0:4, :]).all()
     assert (digits(d47) == trits[:, 4:8, :]).all()
+
+
+def test_brute_row_parallel_matches_single_thread():
+    trits, rs, h = synth.lmhead(700, 256, 9)
+    wi, ws = oracle.lmhead_brute(trits, rs, h, 40)
+    for n in (2, 5):
+        oracle.set_threads(n)
+        gi, gs = oracle.lmhead_brute_mt(trits, rs, h, 40)
+        assert (gi == wi).all() and (gs == ws).all()
+    oracle.set_threads(1)

@@ -199,3 +199,12 @@ def test_materialize_matches_fp64_direct_dot():
     assert (np.abs(s - d) <= bound).all()
     # S is zero exactly when every A[p] is zero (2^(p/8) are independent over Q)
     assert ((s == 0) == (~a.any(1))).all()
+
+
+def test_direct_row_parallel_matches_single_thread():
+    t, x = synth.lns8(257, 1024, 5)
+    want = oracle.lns8_direct(t, x)
+    for n in (2, 7):
+        oracle.set_threads(n)
+        assert (oracle.lns8_direct_mt(t, x) == want).all()
+    oracle.set_threads(1)

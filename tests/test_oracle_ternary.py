@@ -178,3 +178,19 @@ def test_scales_pack_positions():
     assert ps[(4 * 3 + 1) * 16 + 3] == sc[67, 1]
     assert ps[(4 * 3 + 0) * 16 + 6] == 0      # padding row 70
     assert ps[(7 * 3 + 2) * 16 + 15] == 0     # last padding row 127
+
+
+def test_row_parallel_form_matches_single_thread():
+    """The all-core baseline's row-parallel form returns the single-thread
+    definition form's bytes, at several thread counts, including a ragged
+    row count and an out-of-range trit (rejected before any row runs)."""
+    t, sc, x = synth.ternary(301, 1024, 3)
+    want = oracle.ternary_gemv_def(t, sc, x, 2)
+    for n in (1, 3, 8):
+        assert oracle.set_threads(n) == n
+        assert (oracle.ternary_gemv_def_mt(t, sc, x, 2) == want).all()
+    bad = t.copy()
+    bad[150, 7] = 2
+    with pytest.raises(Exception):
+        oracle.ternary_gemv_def_mt(bad, sc, x)
+    oracle.set_threads(1)
