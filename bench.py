@@ -1,37 +1,47 @@
 #!/usr/bin/env python3
 """Benchmark of the batch-1 ternary decode GEMV hot path on one MI355X.
 
-One step = one BitNet-b1.58-2B-shaped decode layer's projections: q, k, v
-(2560, 640, 640 rows x 2560), o (2560 x 2560), gate and up (6912 x 2560 each)
-and down (2560 x 6912), on packed ternary planes (0.25 B/weight) plus int16
-group scales, int8 activations, exact int64 outputs.  The projections that
-share an input are stored concatenated by rows, as decode engines store them:
-q|k|v is one 3840 x 2560 matrix and gate|up one 13824 x 2560 matrix, so a step
-is four dependent launches (qkv, o, gate_up, down) streaming the same bytes as
-the seven separate GEMVs.  q|k|v and gate|up write fresh outputs
-(bs_ternary_gemv); o and down add into the residual stream, as a decoder
-layer's output projections do (bs_ternary_gemv_acc, y += W x).  The seven-launch form of the same
-step (each projection a row range of the same buffers) is timed as well and
-reported in `config`.  Steps walk a pool of distinct layers whose weights
-total more than 1 GiB, so every GEMV streams its weights from HBM rather than
-the 256 MB Infinity Cache; inputs are resident in HBM before the timed region.
+Headline (`value`): weight-stream GB/s of the per-configuration ternary GEMVs
+with K in [2560, 5120], each a separate `bs_ternary_gemv` launch on its own
+weights: the six K = 2560 projections of a BitNet-b1.58-2B decode layer (q,
+k, v, o: 2560/640/640/2560 x 2560; gate, up: 6912 x 2560) and the larger-K
+11008 x 4096 and 13824 x 5120.  One step = those eight launches (44.5 MB of
+packed planes + int16 scales).  Weights are ternary with P(0) = 0.4, int16
+group scales uniform in [1, 4096], int8 activations rint(N(0, 32^2))
+clipped to +-127, seed 0.  Steps walk a pool of distinct weight sets of more
+than 1.1 GB, so every launch streams its weights from HBM rather than the
+256 MB Infinity Cache; inputs are resident in HBM before the timed region.
+The K timed steps are captured in one HIP graph, replayed once (upload),
+then a 512 MB read evicts the caches and the graph is replayed between two
+HIP events on its stream.
 
-Timing: the K timed steps are captured once in a HIP graph and replayed on one
-stream between two HIP events (plus a host wall clock).  `value` is the
-weight-stream throughput of the whole job: weight bytes of all K steps over
-the elapsed time.  The roofline entry is for the dominant kernel (the one
-with the largest share of step time): its algorithmic bytes per launch over
-its average launch duration, measured with HIP events around a graph of
-back-to-back launches of that kernel alone on the same stream.
+`roofline` is for the largest configuration shape, 13824 x 5120: algorithmic
+bytes per launch (planes N*K/4 + scales N*K/64) over the kernel's average
+launch duration, measured with HIP events on the launch stream around a
+graph of back-to-back launches that visits every buffer of a 512 MB pool
+once (the profiler's kernel-trace durations of the same launches agree).
+Every shape of the five configurations also gets, in `ops.gemv`, its back-
+to-back time, a plain read of the same bytes from the same pool (the read
+ceiling, `bs_probe_read`) and the fraction of that ceiling reached.
+`context` holds the empty-kernel launch floor.
 
-Extra entries ("ops") time the other workloads of the path: the larger-K
-GEMVs, the LNS8 eight-phase GEMV (both reductions) and the BITNET_PLANES
-lm_head top-k.  `cpu_baseline` times the plain C oracle, single-threaded, on
-a bounded sample of the same step.
+`ops.f1` holds the activation-reuse sweep (N = 1 .. 8192 rows sharing one
+activation vector, ternary GEMV and both LNS8 paths, with the row count where
+the popcount path overtakes direct routing), the Phase B sweeps of the LNS8
+GEMV (weight zero density, number of distinct activation codes) and the
+fused four-launch layer step.  Other `ops` entries time the rest of the path:
+Q1_0, LNS8 (with the VALU fraction), pure-LNS, the steps either side and the
+lm_head.  `cpu_baseline` times the plain C oracle on the host: all cores
+(OpenMP over rows) and single-threaded, medians of repeated samples.
+
+Every measured block is preceded by a marker launch (an empty kernel whose
+grid encodes the block) so that one `rocprofv3 --kernel-trace` run of this
+script can be split per block and shape by `--trace-summary`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
+                       [--no-cpu-baseline] [--cpu-seconds S]
        python bench.py --trace-summary <rocprofv3 kernel_trace.csv>
-       python bench.py --traffic-run NxK          (workload of the --pmc runs)
+       python bench.py --traffic-run NxK       (workload of the --pmc runs)
        python bench.py --traffic-summary FETCH.csv WRITE.csv NxK
 """
 from __future__ import annotations
@@ -50,13 +60,37 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+VALU_PEAK_OPS = 256 * 64 * 2.4e9   # 256 CUs x 64 int32 lane-ops per clock x 2.4 GHz
+IC_BYTES = 256 << 20           # MI355X Infinity Cache
 METRIC = "ternary GEMV weight-stream GB/s & % HBM peak, batch-1, K=2560..5120"
+# one step: the in-range per-configuration GEMVs, one launch each
+STEP = [("q", 2560, 2560), ("k", 640, 2560), ("v", 640, 2560), ("o", 2560, 2560),
+        ("gate", 6912, 2560), ("up", 6912, 2560), ("c3_11008x4096", 11008, 4096),
+        ("c3_13824x5120", 13824, 5120)]
+IN_RANGE = [(2560, 2560), (640, 2560), (6912, 2560), (11008, 4096), (13824, 5120)]
+REPORTED = [(2560, 6912), (4096, 11008), (5120, 13824)]     # K outside 2560..5120
+ROOF_SHAPE = (13824, 5120)
+STEP_POOL_BYTES = int(1.1 * (1 << 30))
+SHAPE_POOL_BYTES = 2 * IC_BYTES
+# the BitNet-2B layer stored as four launches (f1: shared-activation fusion)
 LAYER = [("q", 2560, 2560), ("k", 640, 2560), ("v", 640, 2560), ("o", 2560, 2560),
          ("gate", 6912, 2560), ("up", 6912, 2560), ("down", 2560, 6912)]
-# launches of one step: (name, member projections stored concatenated by rows)
 FUSED = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")),
          ("down", ("down",))]
-RESIDUAL = ("o", "down")        # output projections: y += W x into the residual stream
+RESIDUAL = ("o", "down")
+# marker ids of the measured blocks (empty-kernel grid = (4096 + id) x 64)
+MARKER_BASE = 4096
+BLOCKS = ["step", "roofline_graph", "context_floor", "ceiling_scrub",
+          "f1_fused_step", "lmhead", "lns8", "flns", "q1", "edges"]
+SHAPE_BLOCKS = ["gemv_%dx%d" % s for s in IN_RANGE + REPORTED]
+SWEEP_BLOCKS = ["f1_reuse_%s_n%d" % (p, n) for p in ("ternary", "direct", "popcount")
+                for n in (1, 8, 32, 128, 512, 2048, 8192)]
+PHASE_B_BLOCKS = (["f1_zero_%s_%s" % (p, z) for p in ("direct", "popcount")
+                   for z in ("0", "1/3", "0.6", "0.9")] +
+                  ["f1_codes_%s_%d" % (p, m) for p in ("direct", "popcount")
+                   for m in (1, 8, 41, 127)])
+ALL_BLOCKS = BLOCKS + SHAPE_BLOCKS + SWEEP_BLOCKS + PHASE_B_BLOCKS
+MARKER_ID = {name: i + 1 for i, name in enumerate(ALL_BLOCKS)}
 
 
 def weight_bytes(rows: int, k: int) -> int:
@@ -69,12 +103,28 @@ def log(msg: str):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-class Timer:
-    """Graph replay timing on one stream with HIP events."""
+class Harness:
+    """Graph-replay timing on one stream with HIP events, plus the
+    measurement kernels (read ceiling, launch floor, markers)."""
 
-    def __init__(self, torch, stream):
+    def __init__(self, torch, dev):
+        from bit_decode_gemv_amd import probe
         self.torch = torch
-        self.stream = stream
+        self.dev = dev
+        self.stream = torch.cuda.Stream(device=dev)
+        self.probe = probe
+        probe.lib()
+        self.scrub_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        self.scrub_sink = probe.sink_for(self.scrub_buf.numel(), 8, dev)
+
+    def marker(self, block: str):
+        with self.torch.cuda.stream(self.stream):
+            self.probe.empty(MARKER_BASE + MARKER_ID[block], 64, self.stream)
+
+    def scrub(self):
+        """Read 512 MB of an unrelated buffer: afterwards no weight line is
+        left in the L2s or the Infinity Cache."""
+        self.probe.read(self.scrub_buf, self.scrub_buf.numel(), 8, self.scrub_sink, self.stream)
 
     def graph(self, fn, n):
         torch = self.torch
@@ -85,101 +135,62 @@ class Timer:
                     fn(i)
         return g
 
-    def replay_us(self, g, reps=1):
+    def replay_us(self, g, scrub=False):
         torch = self.torch
         with torch.cuda.stream(self.stream):
+            if scrub:
+                self.scrub()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
             t0 = time.perf_counter()
             e0.record(self.stream)
-            for _ in range(reps):
-                g.replay()
+            g.replay()
             e1.record(self.stream)
             torch.cuda.synchronize()
             wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) * 1000.0, wall * 1e6
 
+    def per_launch(self, fn, n, reps=3, block=None):
+        """Median over `reps` replays of a graph of n back-to-back launches
+        (each replay visits the whole pool once), in us per launch."""
+        if block:
+            self.marker(block)
+        g = self.graph(fn, n)
+        self.replay_us(g)                       # upload
+        us = sorted(self.replay_us(g)[0] / n for _ in range(reps))
+        del g
+        return us[len(us) // 2]
 
-def per_launch_us(timer, fn, n=200, reps=5):
-    g = timer.graph(fn, n)
-    timer.replay_us(g)                         # warm
-    us, _ = timer.replay_us(g, reps)
-    return us / (n * reps)
+    def ceiling(self, pool, nbytes, n, block=None):
+        """Best back-to-back time of a plain read of `nbytes` from each pool
+        buffer in turn (1, 2, 4 or 8 16-byte loads per thread)."""
+        best = None
+        for u in (2, 4, 8):
+            sink = self.probe.sink_for(nbytes, u, self.dev)
+            us = self.per_launch(lambda i: self.probe.read(pool[i % len(pool)], nbytes, u, sink,
+                                                           self.stream), n, block=block)
+            best = us if best is None else min(best, us)
+        return best
 
 
-def make_pool(torch, bs, synth, dev, rows, k, seed, min_bytes):
-    """Packed planes/scales for one shape, replicated into distinct buffers
-    totalling at least min_bytes."""
+def packed_pool(torch, bs, synth, dev, rows, k, min_bytes, seed=0, max_copies=None):
+    """Packed planes and scales of one seeded shape, copied into distinct
+    device buffers (planes then scales in one allocation) totalling at least
+    min_bytes.  Returns (buffers, views [(planes, scales)], x, bytes each)."""
+    import numpy as np
     t, sc, x = synth.ternary(rows, k, seed)
-    p = torch.from_numpy(bs.ternary_pack(t)).to(dev)
-    s = torch.from_numpy(bs.ternary_pack_scales(sc)).to(dev)
-    n = max(2, -(-min_bytes // weight_bytes(rows, k)))
-    return [p.clone() for _ in range(n)], [s.clone() for _ in range(n)], torch.from_numpy(x).to(dev)
+    pl = bs.ternary_pack(t)
+    ps = bs.ternary_pack_scales(sc)
+    base = torch.from_numpy(np.concatenate([pl, ps.view(np.uint8)])).to(dev)
+    n = max(2, -(-min_bytes // base.numel()))
+    if max_copies:
+        n = min(n, max_copies)
+    bufs = [base.clone() for _ in range(n)]
+    views = [(b[:pl.size], b[pl.size:].view(torch.int16)) for b in bufs]
+    return bufs, views, torch.from_numpy(x).to(dev), base.numel()
 
 
-def cpu_baseline(seconds_target: float):
-    """The oracle's definition-form GEMV, single-threaded, over the step's
-    seven shapes at full size (seed 0), repeated until about seconds_target
-    of CPU time; reported in the metric's unit (weight-stream bytes per
-    second of the packed format the GPU reads)."""
-    import numpy as np
-    import oracle
-    from bit_decode_gemv_amd import synth
-    cases = [synth.ternary(r, k, 0) for _, r, k in LAYER]
-    step_bytes = sum(weight_bytes(r, k) for _, r, k in LAYER)
-    done, t_cpu = 0, 0.0
-    while t_cpu < seconds_target:
-        for t, sc, x in cases:
-            t0 = time.process_time()
-            oracle.ternary_gemv_def(t, sc, x)
-            t_cpu += time.process_time() - t0
-        done += 1
-    gbs = done * step_bytes / t_cpu / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d full step(s) (q,k,v,o,gate,up,down at full size, seed 0) through "
-                      "or_ternary_gemv_def on unpacked int8 trits, single thread, %.1f s CPU"
-                      % (done, t_cpu),
-            "cpu_model": _cpu_model(), "ms_per_step": round(1000.0 * t_cpu / done, 2),
-            "per_config": _oracle_per_config()}
-
-
-def _oracle_per_config():
-    """The oracle's other entry points, single-threaded, each timed once on
-    one seeded input (median of 3 where it takes under a second)."""
-    import numpy as np
-    import oracle
-    from bit_decode_gemv_amd import synth
-
-    def med(fn, reps):
-        ts = []
-        for _ in range(reps):
-            t0 = time.process_time()
-            fn()
-            ts.append(time.process_time() - t0)
-        return statistics.median(ts)
-
-    out = {}
-    t, sc, x = synth.tiny(0)
-    out["ternary_256x512_us"] = round(1e6 * med(lambda: oracle.ternary_gemv_def(t, sc, x), 3), 1)
-    t, sc, x = synth.ternary(13824, 5120, 0)
-    sec = med(lambda: oracle.ternary_gemv_def(t, sc, x), 3)
-    out["ternary_13824x5120_us"] = round(1e6 * sec, 1)
-    out["ternary_13824x5120_GBps"] = round(weight_bytes(13824, 5120) / sec / 1e9, 4)
-    t8, x8 = synth.lns8(4096, 4096, 0)
-    out["lns8_4096x4096_direct_us"] = round(1e6 * med(lambda: oracle.lns8_direct(t8, x8), 3), 1)
-    out["lns8_4096x4096_popcount_us"] = round(
-        1e6 * med(lambda: oracle.lns8_popcount(t8, x8), 1), 1)
-    V = 16384
-    trits, rs, h = synth.lmhead(V, 2560, 0)
-    scale = synth.LMHEAD_SHAPE[0] / V
-    out["lmhead_two_stage_us_scaled_from_16384_rows"] = round(
-        1e6 * scale * med(lambda: oracle.lmhead_two_stage(trits, rs, h, 40, 200), 1), 1)
-    out["lmhead_brute_us_scaled_from_16384_rows"] = round(
-        1e6 * scale * med(lambda: oracle.lmhead_brute(trits, rs, h, 40), 1), 1)
-    del np
-    return out
-
+# ---------------------------------------------------------------- CPU side
 
 def _cpu_model():
     try:
@@ -190,6 +201,101 @@ def _cpu_model():
         pass
     return "unknown"
 
+
+def _baseline_threads():
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(seconds_target: float):
+    """The oracle's definition-form GEMV over the headline step's eight
+    shapes at full size (seed 0), on all host cores (rows shared out by
+    OpenMP; identical results) and on one thread: the median of five
+    samples, each as many steps as fill about seconds_target / 10 of wall
+    time, in the metric's unit (weight-stream bytes of the packed format the
+    GPU reads, per second).  Per-configuration oracle timings beside it."""
+    import oracle
+    from bit_decode_gemv_amd import synth
+    cases = [synth.ternary(r, k, 0) for _, r, k in STEP]
+    step_bytes = sum(weight_bytes(r, k) for _, r, k in STEP)
+    cores = oracle.set_threads(_baseline_threads())
+
+    def sample(fn, budget):
+        done, t0 = 0, time.perf_counter()
+        while True:
+            for t, sc, x in cases:
+                fn(t, sc, x)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return done * step_bytes / el / 1e9, el / done
+
+    mt = sorted(sample(oracle.ternary_gemv_def_mt, seconds_target / 10) for _ in range(5))
+    st = sorted(sample(oracle.ternary_gemv_def, seconds_target / 10) for _ in range(5))
+    out = {"value": round(mt[2][0], 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "sample": "median of 5 samples of %.1f s wall each: full headline steps (the eight "
+                     "per-configuration GEMVs, seed 0) through the definition-form oracle on "
+                     "unpacked int8 trits, rows on %d OpenMP threads" % (seconds_target / 10,
+                                                                         cores),
+           "cpu_model": _cpu_model(), "ms_per_step": round(1000.0 * mt[2][1], 2),
+           "single_thread": {"value": round(st[2][0], 4), "unit": "GB/s", "cores": 1,
+                             "ms_per_step": round(1000.0 * st[2][1], 2)}}
+    out["per_config"] = _oracle_per_config(cores)
+    oracle.set_threads(1)
+    return out
+
+
+def _oracle_per_config(cores):
+    """The oracle's other entry points on one seeded input each, median of
+    three wall times, single thread and (row-parallel forms) all cores."""
+    import oracle
+    from bit_decode_gemv_amd import synth
+
+    def med(fn, reps=3):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts)
+
+    out = {}
+    t, sc, x = synth.tiny(0)
+    oracle.set_threads(1)
+    out["ternary_256x512_us"] = round(1e6 * med(lambda: oracle.ternary_gemv_def(t, sc, x)), 1)
+    t, sc, x = synth.ternary(13824, 5120, 0)
+    for tag, fn, n in (("1t", oracle.ternary_gemv_def, 1), ("mt", oracle.ternary_gemv_def_mt,
+                                                             cores)):
+        oracle.set_threads(n)
+        sec = med(lambda: fn(t, sc, x))
+        out["ternary_13824x5120_%s_us" % tag] = round(1e6 * sec, 1)
+        out["ternary_13824x5120_%s_GBps" % tag] = round(weight_bytes(13824, 5120) / sec / 1e9, 4)
+    t8, x8 = synth.lns8(4096, 4096, 0)
+    oracle.set_threads(1)
+    out["lns8_4096x4096_direct_1t_us"] = round(1e6 * med(lambda: oracle.lns8_direct(t8, x8)), 1)
+    oracle.set_threads(cores)
+    out["lns8_4096x4096_direct_mt_us"] = round(
+        1e6 * med(lambda: oracle.lns8_direct_mt(t8, x8)), 1)
+    oracle.set_threads(1)
+    out["lns8_4096x4096_popcount_1t_us"] = round(
+        1e6 * med(lambda: oracle.lns8_popcount(t8, x8), 1), 1)
+    V = 16384
+    trits, rs, h = synth.lmhead(V, 2560, 0)
+    scale = synth.LMHEAD_SHAPE[0] / V
+    out["lmhead_two_stage_1t_us_scaled_from_16384_rows"] = round(
+        1e6 * scale * med(lambda: oracle.lmhead_two_stage(trits, rs, h, 40, 200), 1), 1)
+    out["lmhead_brute_1t_us_scaled_from_16384_rows"] = round(
+        1e6 * scale * med(lambda: oracle.lmhead_brute(trits, rs, h, 40), 1), 1)
+    oracle.set_threads(cores)
+    out["lmhead_brute_mt_us_scaled_from_16384_rows"] = round(
+        1e6 * scale * med(lambda: oracle.lmhead_brute_mt(trits, rs, h, 40), 1), 1)
+    oracle.set_threads(1)
+    return out
+
+
+# ------------------------------------------------------ records under profiles/
 
 def _source_digest():
     """Digest of the GEMV kernel's source: its file and the headers it
@@ -224,75 +330,263 @@ def _recorded_traffic(shape_tag: str):
         return None
 
 
-def context(torch, dev, timer):
-    """The empty-launch floor (a one-element fill, back to back in a graph)
-    and a 1 GiB read through torch's float32 sum, for scale."""
-    one = torch.zeros(1, dtype=torch.int32, device=dev)
-    floor_us = per_launch_us(timer, lambda i: one.fill_(i), n=200)
-    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    acc = torch.empty(1, dtype=torch.float32, device=dev)
-    # eager, not graph-captured (a multi-block reduction may record memset nodes)
-    with torch.cuda.stream(timer.stream):
-        torch.sum(big, dim=0, keepdim=True, out=acc)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(timer.stream)
-        for _ in range(10):
-            torch.sum(big, dim=0, keepdim=True, out=acc)
-        e1.record(timer.stream)
+# ------------------------------------------------------------ GPU workloads
+
+def run_step(torch, bs, synth, dev, H, steps, warmup):
+    """The headline: K steps of the eight in-range per-configuration GEMVs."""
+    import numpy as np
+    step_bytes = sum(weight_bytes(r, k) for _, r, k in STEP)
+    n_sets = -(-STEP_POOL_BYTES // step_bytes)
+    log("building %d weight sets of the %d-launch step (%.1f MB each, %.2f GB in all)" % (
+        n_sets, len(STEP), step_bytes / 1e6, n_sets * step_bytes / 1e9))
+    bases, xs, ys = {}, {}, {}
+    for name, rows, k in STEP:
+        t, sc, x = synth.ternary(rows, k, 0)
+        pl, ps = bs.ternary_pack(t), bs.ternary_pack_scales(sc)
+        bases[name] = torch.from_numpy(np.concatenate([pl, ps.view(np.uint8)])).to(dev), pl.size
+        xs[k] = torch.from_numpy(x).to(dev) if k not in xs else xs[k]
+        ys[name] = torch.empty(rows, dtype=torch.int64, device=dev)
+        del t
+    sets = []
+    for _ in range(n_sets):
+        s = {}
+        for name, rows, k in STEP:
+            b = bases[name][0].clone()
+            s[name] = (b[:bases[name][1]], b[bases[name][1]:].view(torch.int16))
+        sets.append(s)
+
+    def step(i):
+        s = sets[i % n_sets]
+        for name, rows, k in STEP:
+            bs.ternary_gemv(s[name][0], s[name][1], xs[k], rows, k, out=ys[name],
+                            stream=H.stream)
+
+    with torch.cuda.stream(H.stream):
+        for i in range(warmup):
+            step(n_sets - 1 - (i % n_sets))
     torch.cuda.synchronize()
-    read_us = e0.elapsed_time(e1) * 1000.0 / 10
-    del big
-    return {"launch_floor_us": round(floor_us, 3),
-            "read_1GiB_GBps": round((1 << 30) / read_us / 1e3, 1),
-            "read_1GiB_note": "torch.sum over 2^28 float32 (a reduction, so a lower bound on "
-                              "the read ceiling), 10 eager launches between HIP events"}
+    H.marker("step")
+    g = H.graph(step, steps)
+    H.replay_us(g)                              # first replay uploads the graph
+    us, wall_us = H.replay_us(g, scrub=True)
+    del g
+    distinct = min(steps, n_sets) * step_bytes
+    value = step_bytes * steps / (us * 1e-6) / 1e9
+    log("step (%d launches): %.2f us (events), %.2f us (host wall) -> %.1f GB/s" % (
+        len(STEP), us / steps, wall_us / steps, value))
+    cfg = {"workload": "per-configuration ternary GEMVs with K in [2560, 5120], batch 1, one "
+                       "bs_ternary_gemv launch each: BitNet-b1.58-2B decode projections q, k, v, "
+                       "o (2560/640/640/2560 x 2560), gate, up (6912 x 2560) and the larger-K "
+                       "11008 x 4096 and 13824 x 5120; P(0) = 0.4, int16 scales U[1, 4096], "
+                       "int8 activations rint(N(0, 32^2)), seed 0",
+           "launches": {name: "%dx%d" % (r, k) for name, r, k in STEP},
+           "weight_bytes_per_step": step_bytes, "weight_sets_in_pool": n_sets,
+           "pool_bytes": step_bytes * n_sets, "parallelism": "single GPU",
+           "frac_hbm_peak_whole_job": round(value / HBM_PEAK_GBS, 4),
+           "host_wall_us_per_step": round(wall_us / steps, 3),
+           "timed_region_distinct_bytes": distinct,
+           "timed_region_reuse": ("none: %d steps on %d distinct weight sets" % (steps, n_sets)
+                                  if steps <= n_sets else
+                                  "each weight set re-read after %.2f GB of other sets (> the "
+                                  "256 MB Infinity Cache)" % ((n_sets - 1) * step_bytes / 1e9)),
+           "before_timed_region": "graph upload replay, then a 512 MB read of another buffer "
+                                  "(evicts the L2s and the Infinity Cache)"}
+    del sets, bases
+    torch.cuda.empty_cache()
+    return value, us / steps / 1000.0, cfg
 
 
-def activation_reuse_sweep(torch, bs, synth, dev, timer, k=2560):
-    """us and weight-stream GB/s of one launch as the rows sharing one staged
-    activation vector grow (K = 2560): where the kernel turns bandwidth-bound."""
-    out = {}
-    for rows in (64, 256, 1024, 2560, 6912, 13824, 27648, 55296):
-        ps, ss, x = make_pool(torch, bs, synth, dev, rows, k, 0, 1 << 30)
+def run_shapes(torch, bs, synth, dev, H):
+    """Every configuration shape: back-to-back launch time, its read ceiling
+    and, for the roofline shape, the roofline entry."""
+    out, roof = {}, None
+    for rows, k in IN_RANGE + REPORTED:
+        bufs, views, x, nb = packed_pool(torch, bs, synth, dev, rows, k, SHAPE_POOL_BYTES)
+        n = len(bufs)
         y = torch.empty(rows, dtype=torch.int64, device=dev)
-        us = per_launch_us(timer, lambda i: bs.ternary_gemv(ps[i % len(ps)], ss[i % len(ss)], x,
-                                                            rows, k, out=y), n=100)
         wb = weight_bytes(rows, k)
-        out[str(rows)] = {"us": round(us, 3), "GBps": round(wb / us / 1e3, 1)}
-        del ps, ss
-    log("activation-reuse sweep: " + ", ".join("%s rows %.0f GB/s" % (r, v["GBps"])
-                                                for r, v in out.items()))
+        fn = lambda i: bs.ternary_gemv(views[i % n][0], views[i % n][1], x, rows, k, out=y,
+                                       stream=H.stream)
+        tag = "%dx%d" % (rows, k)
+        us = H.per_launch(fn, n, block="gemv_" + tag)
+        ceil_us = H.ceiling(bufs, wb, n)
+        e = {"us_per_gemv": round(us, 3), "weight_bytes": wb, "GBps": round(wb / us / 1e3, 1),
+             "frac_hbm_peak": round(wb / us / 1e3 / HBM_PEAK_GBS, 4),
+             "ceiling_us": round(ceil_us, 3), "frac_of_ceiling": round(ceil_us / us, 3),
+             "k_in_2560_5120": 2560 <= k <= 5120, "pool_bytes": n * nb}
+        out["ternary_gemv_" + tag] = e
+        log("ternary %s: %.3f us (read ceiling %.3f us, %.0f%%)" % (tag, us, ceil_us,
+                                                                  100.0 * ceil_us / us))
+        if (rows, k) == ROOF_SHAPE:
+            us_r = H.per_launch(fn, n, block="roofline_graph")
+            achieved = wb / us_r / 1e3
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": _recorded_traffic(tag),
+                    "kernel": "bs_ternary_gemv %s (ternary_pipe_kernel)" % tag,
+                    "bytes_per_launch": wb, "us_per_launch": round(us_r, 3),
+                    "ceiling_us": round(ceil_us, 3), "frac_of_ceiling": round(ceil_us / us_r, 3),
+                    "timing": "HIP events on the launch stream around a graph of %d back-to-"
+                              "back launches, one per buffer of a %d MB pool; median of 3 "
+                              "replays" % (n, n * nb >> 20)}
+            log("roofline %s: %.3f us per launch" % (tag, us_r))
+        del bufs, views
+        torch.cuda.empty_cache()
+    return out, roof
+
+
+def run_f1(torch, bs, synth, dev, H):
+    """f1: the activation-reuse sweep, the LNS8 Phase B sweeps and the
+    fused four-launch layer step."""
+    import numpy as np
+    out = {}
+    # reuse sweep at K = 4096 (the LNS8 workload's K): N rows share one x
+    K = 4096
+    sweep = {"ternary": {}, "direct": {}, "popcount": {}}
+    for n_rows in (1, 8, 32, 128, 512, 2048, 8192):
+        bufs, views, x, nb = packed_pool(torch, bs, synth, dev, n_rows, K, SHAPE_POOL_BYTES,
+                                         max_copies=1024)
+        y = torch.empty(n_rows, dtype=torch.int64, device=dev)
+        n = len(bufs)
+        us = H.per_launch(lambda i: bs.ternary_gemv(views[i % n][0], views[i % n][1], x, n_rows,
+                                                    K, out=y, stream=H.stream), n,
+                          block="f1_reuse_ternary_n%d" % n_rows)
+        sweep["ternary"][str(n_rows)] = {"us": round(us, 3),
+                                         "weights_per_ns": round(n_rows * K / us / 1e3, 2)}
+        del bufs, views
+        t8, x8 = synth.lns8(n_rows, K, 0)
+        p8 = torch.from_numpy(bs.ternary_pack(t8)).to(dev)
+        pool = [p8.clone() for _ in range(min(1024, max(2, -(-SHAPE_POOL_BYTES // p8.numel()))))]
+        xd = torch.from_numpy(x8).to(dev)
+        acc = torch.empty((n_rows, 8), dtype=torch.int32, device=dev)
+        s8 = torch.empty(n_rows, dtype=torch.float64, device=dev)
+        ws = torch.zeros(bs.lib().bs_lns8_workspace_bytes(n_rows, K), dtype=torch.uint8,
+                         device=dev)
+        for path, name in ((bs.LNS8_DIRECT, "direct"), (bs.LNS8_POPCOUNT, "popcount")):
+            us = H.per_launch(lambda i: bs.lns8_phase_gemv(pool[i % len(pool)], xd, n_rows, K,
+                                                           path, acc=acc, s=s8, workspace=ws,
+                                                           stream=H.stream), len(pool),
+                              block="f1_reuse_%s_n%d" % (name, n_rows))
+            sweep[name][str(n_rows)] = {"us": round(us, 3),
+                                        "weights_per_ns": round(n_rows * K / us / 1e3, 2)}
+        del pool
+        torch.cuda.empty_cache()
+    cross = None
+    for n_rows in (1, 8, 32, 128, 512, 2048, 8192):
+        if sweep["popcount"][str(n_rows)]["us"] <= sweep["direct"][str(n_rows)]["us"]:
+            cross = n_rows
+            break
+    out["reuse_sweep_k4096"] = {**sweep, "crossover_rows": cross,
+                                "crossover_note": "smallest row count (of those swept) where the "
+                                                  "popcount path is at least as fast as direct "
+                                                  "routing; null if it never is"}
+    log("f1 reuse sweep: crossover at %s rows" % cross)
+    # Phase B: weight zero density and the number of distinct codes, 4096 x 4096
+    R = 4096
+    phase_b = {"zero_density": {}, "distinct_codes": {}}
+    for kind, values in (("zero_density", (0.0, 1.0 / 3.0, 0.6, 0.9)),
+                         ("distinct_codes", (1, 8, 41, 127))):
+        for v in values:
+            if kind == "zero_density":
+                t8, x8 = synth.lns8_sweep(R, K, 0, v, 41)
+                label = {0.0: "0", 0.6: "0.6", 0.9: "0.9"}.get(v, "1/3")
+            else:
+                t8, x8 = synth.lns8_sweep(R, K, 0, 1.0 / 3.0, v)
+                label = str(v)
+            p8 = torch.from_numpy(bs.ternary_pack(t8)).to(dev)
+            pool = [p8.clone() for _ in range(-(-SHAPE_POOL_BYTES // p8.numel()))]
+            xd = torch.from_numpy(x8).to(dev)
+            acc = torch.empty((R, 8), dtype=torch.int32, device=dev)
+            ws = torch.zeros(bs.lib().bs_lns8_workspace_bytes(R, K), dtype=torch.uint8,
+                             device=dev)
+            ent = {}
+            for path, name in ((bs.LNS8_DIRECT, "direct"), (bs.LNS8_POPCOUNT, "popcount")):
+                blk = ("f1_zero_%s_%s" % (name, label) if kind == "zero_density"
+                       else "f1_codes_%s_%d" % (name, v))
+                us = H.per_launch(lambda i: bs.lns8_phase_gemv(pool[i % len(pool)], xd, R, K,
+                                                               path, acc=acc, s=False,
+                                                               workspace=ws, stream=H.stream),
+                                  len(pool), block=blk)
+                ent[name + "_us"] = round(us, 3)
+            phase_b[kind][label] = ent
+            del pool
+            torch.cuda.empty_cache()
+    out["lns8_phase_b_4096x4096"] = phase_b
+    # shared-activation fusion: the layer as four launches (q|k|v and gate|up
+    # stored concatenated by rows; o and down add into the residual stream)
+    shape = {name: (r, k) for name, r, k in LAYER}
+    lbytes = sum(weight_bytes(r, k) for _, r, k in LAYER)
+    n_layers = -(-STEP_POOL_BYTES // lbytes)
+    base = {}
+    for fname, members in FUSED:
+        parts = [synth.ternary(*shape[m], li) for li, m in enumerate(members)]
+        t = np.concatenate([pt[0] for pt in parts])
+        sc = np.concatenate([pt[1] for pt in parts])
+        k = shape[members[0]][1]
+        base[fname] = (torch.from_numpy(bs.ternary_pack(t)).to(dev),
+                       torch.from_numpy(bs.ternary_pack_scales(sc)).to(dev),
+                       torch.from_numpy(parts[0][2]).to(dev), t.shape[0], k)
+    layers = [{f: (base[f][0].clone(), base[f][1].clone()) for f, _ in FUSED}
+              for _ in range(n_layers)]
+    ys = {f: torch.zeros(base[f][3], dtype=torch.int64, device=dev) for f, _ in FUSED}
+
+    def fused_step(i):
+        for fname, _ in FUSED:
+            p, s = layers[i % n_layers][fname]
+            _, _, x, r, k = base[fname]
+            if fname in RESIDUAL:
+                bs.ternary_gemv_acc(p, s, x, r, k, ys[fname], stream=H.stream)
+            else:
+                bs.ternary_gemv(p, s, x, r, k, out=ys[fname], stream=H.stream)
+
+    us = H.per_launch(fused_step, n_layers, block="f1_fused_step")
+    out["fused_layer_step"] = {"us_per_step": round(us, 3), "weight_bytes_per_step": lbytes,
+                               "GBps": round(lbytes / us / 1e3, 1),
+                               "launches": {f: "%dx%d" % (base[f][3], base[f][4])
+                                            for f, _ in FUSED},
+                               "note": "q|k|v and gate|up stored concatenated (shared "
+                                       "activation), o and down as y += W x; not the headline"}
+    log("f1 fused layer step: %.2f us" % us)
+    del layers, base
+    torch.cuda.empty_cache()
     return out
 
 
-def run_extras(torch, bs, synth, dev, timer):
+def lns8_valu_ops(path: int) -> float:
+    """VALU instructions per launch of the LNS8 kernel at 4096 x 4096, from
+    the SQ_INSTS_VALU counter runs recorded under profiles/ (None if absent
+    or taken on other source)."""
+    fn = os.path.join(ROOT, "profiles", "lns8_4096x4096_valu.txt")
+    if not os.path.exists(fn):
+        return None
+    vals = {}
+    for line in open(fn):
+        if ":" in line and not line.startswith("#"):
+            a, b = line.split(":", 1)
+            vals[a.strip()] = b.strip()
+    key = "valu_insts_per_call_" + ("direct" if path == 0 else "popcount")
+    try:
+        return float(vals[key])
+    except (KeyError, ValueError):
+        return None
+
+
+def run_extras(torch, bs, synth, dev, H):
+    import numpy as np
     ops = {}
-    # larger-K GEMVs
-    for rows, k in synth.LARGE_K_SHAPES:
-        ps, ss, x = make_pool(torch, bs, synth, dev, rows, k, 0, 1 << 30)
-        y = torch.empty(rows, dtype=torch.int64, device=dev)
-        us = per_launch_us(timer, lambda i: bs.ternary_gemv(ps[i % len(ps)], ss[i % len(ss)], x,
-                                                            rows, k, out=y), n=100)
-        wb = weight_bytes(rows, k)
-        ops["ternary_gemv_%dx%d" % (rows, k)] = {
-            "us_per_gemv": round(us, 3), "weight_bytes": wb, "GBps": round(wb / us / 1e3, 1),
-            "frac_hbm_peak": round(wb / us / 1e3 / HBM_PEAK_GBS, 4)}
-        del ps, ss
-        log("ternary %dx%d: %.2f us" % (rows, k, us))
-    # Q1_0 (one sign bit per weight): the four launches of a BitNet-2B layer
-    # and the largest K in range
+    # Q1_0 (one sign bit per weight)
     q1_bytes = lambda r, k: r * k // 8 + r * (k // 128) * 2
-    for rows, k in [(3840, 2560), (2560, 2560), (13824, 2560), (2560, 6912), (13824, 5120)]:
+    H.marker("q1")
+    for rows, k in [(2560, 2560), (13824, 2560), (2560, 6912), (13824, 5120)]:
         sgn, sc, x = synth.q1(rows, k, 0)
         b = torch.from_numpy(bs.q1_pack(sgn)).to(dev)
         s = torch.from_numpy(bs.ternary_pack_scales(sc)).to(dev)
-        n = max(2, -(-(1 << 30) // q1_bytes(rows, k)))
+        n = max(2, -(-SHAPE_POOL_BYTES // q1_bytes(rows, k)))
         bp, sp = [b.clone() for _ in range(n)], [s.clone() for _ in range(n)]
         xd = torch.from_numpy(x).to(dev)
         y = torch.empty(rows, dtype=torch.int64, device=dev)
-        us = per_launch_us(timer, lambda i: bs.q1_gemv(bp[i % n], sp[i % n], xd, rows, k,
-                                                       out=y), n=100)
+        us = H.per_launch(lambda i: bs.q1_gemv(bp[i % n], sp[i % n], xd, rows, k, out=y,
+                                               stream=H.stream), n)
         wb = q1_bytes(rows, k)
         ops["q1_gemv_%dx%d" % (rows, k)] = {
             "us_per_gemv": round(us, 3), "weight_bytes": wb, "GBps": round(wb / us / 1e3, 1),
@@ -302,38 +596,45 @@ def run_extras(torch, bs, synth, dev, timer):
     # LNS8 eight-phase GEMV, 4096 x 4096
     t8, x8 = synth.lns8(4096, 4096, 0)
     p8 = torch.from_numpy(bs.ternary_pack(t8)).to(dev)
-    pool8 = [p8.clone() for _ in range(-(-(1 << 30) // p8.numel()))]
+    pool8 = [p8.clone() for _ in range(-(-SHAPE_POOL_BYTES // p8.numel()))]
     xd8 = torch.from_numpy(x8).to(dev)
     acc = torch.empty((4096, 8), dtype=torch.int32, device=dev)
     s8 = torch.empty(4096, dtype=torch.float64, device=dev)
     ws8 = torch.zeros(bs.lib().bs_lns8_workspace_bytes(4096, 4096), dtype=torch.uint8, device=dev)
+    H.marker("lns8")
     for path, name in ((bs.LNS8_DIRECT, "direct"), (bs.LNS8_POPCOUNT, "popcount")):
-        us = per_launch_us(timer, lambda i: bs.lns8_phase_gemv(pool8[i % len(pool8)], xd8, 4096,
-                                                               4096, path, acc=acc, s=s8,
-                                                               workspace=ws8), n=100)
-        ops["lns8_4096x4096_" + name] = {
-            "us_per_gemv": round(us, 3), "weight_bytes": p8.numel(),
-            "GBps": round(p8.numel() / us / 1e3, 1),
-            "frac_hbm_peak": round(p8.numel() / us / 1e3 / HBM_PEAK_GBS, 4),
-            "weights_per_s": round(4096 * 4096 / us * 1e6, 1)}
+        us = H.per_launch(lambda i: bs.lns8_phase_gemv(pool8[i % len(pool8)], xd8, 4096, 4096,
+                                                       path, acc=acc, s=s8, workspace=ws8,
+                                                       stream=H.stream), len(pool8))
+        ent = {"us_per_gemv": round(us, 3), "weight_bytes": p8.numel(),
+               "GBps": round(p8.numel() / us / 1e3, 1),
+               "frac_hbm_peak": round(p8.numel() / us / 1e3 / HBM_PEAK_GBS, 4),
+               "weights_per_s": round(4096 * 4096 / us * 1e6, 1)}
+        valu = lns8_valu_ops(path)
+        if valu is not None:
+            ent["valu_insts_per_call"] = valu
+            ent["valu_lane_ops_per_weight"] = round(valu * 64 / (4096 * 4096), 3)
+            ent["frac_valu_peak"] = round(valu * 64 / (us * 1e-6) / VALU_PEAK_OPS, 4)
+        ops["lns8_4096x4096_" + name] = ent
         log("lns8 %s: %.2f us" % (name, us))
     # pure fractional-LNS reduction of the same products, by internal
-    # precision: time per call and the error of the decoded result against the
-    # exact dyadic S of the linear path above (sign * 2^((L/2^f - 74)/8))
-    import numpy as np
+    # precision: time per call and the error of the decoded result against
+    # the exact dyadic S of the linear path
     s_exact = s8.clone()
-    bs.lns8_phase_gemv(p8, xd8, 4096, 4096, bs.LNS8_DIRECT, acc=acc, s=s_exact, workspace=ws8)
+    bs.lns8_phase_gemv(p8, xd8, 4096, 4096, bs.LNS8_DIRECT, acc=acc, s=s_exact, workspace=ws8,
+                       stream=H.stream)
     torch.cuda.synchronize()
     s_ref = s_exact.cpu().numpy()
     wsf = torch.zeros(bs.lib().bs_flns_workspace_bytes(4096, 4096), dtype=torch.uint8, device=dev)
     outf = torch.empty((4096, 2), dtype=torch.int32, device=dev)
     flns = {}
+    H.marker("flns")
     for f in (0, 2, 4, 8, 12):
         tb = torch.from_numpy(bs.flns_table(f)).to(dev)
-        us = per_launch_us(timer, lambda i: bs.flns_phase_gemv(pool8[i % len(pool8)], xd8, 4096,
-                                                               4096, f, tb, out=outf,
-                                                               workspace=wsf), n=50, reps=3)
-        bs.flns_phase_gemv(p8, xd8, 4096, 4096, f, tb, out=outf, workspace=wsf)
+        us = H.per_launch(lambda i: bs.flns_phase_gemv(pool8[i % len(pool8)], xd8, 4096, 4096, f,
+                                                       tb, out=outf, workspace=wsf,
+                                                       stream=H.stream), 50)
+        bs.flns_phase_gemv(p8, xd8, 4096, 4096, f, tb, out=outf, workspace=wsf, stream=H.stream)
         torch.cuda.synchronize()
         o = outf.cpu().numpy().astype(np.float64)
         val = o[:, 0] * np.exp2((o[:, 1] / float(1 << f) - 74.0) / 8.0) * (o[:, 0] != 0)
@@ -349,29 +650,27 @@ def run_extras(torch, bs, synth, dev, timer):
     ops["flns_4096x4096"] = {"error_vs": "exact dyadic S of the linear eight-phase path "
                                          "(rows with |S| >= 1e-3 x median |S|)", **flns}
     del pool8
-    # steps either side of the GEMVs: absmax int8 quantisation of the
-    # activation vector (the q|k|v and down inputs), LNS8 encoding of the
-    # eight-phase input, and the candidate sampler on a top-40 (one launch
-    # each; a decode step runs them once per vector)
+    # steps either side of the GEMVs
     rng = np.random.default_rng(0)
+    H.marker("edges")
     for k in (2560, 6912):
         xq = torch.from_numpy(rng.integers(-(1 << 40), 1 << 40, k).astype(np.int64)).to(dev)
         qo = torch.empty(k, dtype=torch.int8, device=dev)
         am = torch.empty(1, dtype=torch.int64, device=dev)
         stq = torch.empty(1, dtype=torch.int32, device=dev)
-        us = per_launch_us(timer, lambda i: bs.act_quant_i8(xq, q=qo, absmax=am, status=stq),
-                           n=100)
+        us = H.per_launch(lambda i: bs.act_quant_i8(xq, q=qo, absmax=am, status=stq,
+                                                    stream=H.stream), 100)
         ops["act_quant_i8_k%d" % k] = {"us_per_call": round(us, 3)}
     xe = torch.from_numpy((rng.standard_normal(4096) * 2.0 ** 20).astype(np.int64)).to(dev)
     eo = torch.empty(4096, dtype=torch.uint8, device=dev)
-    ops["lns8_encode_k4096"] = {"us_per_call": round(per_launch_us(
-        timer, lambda i: bs.lns8_encode(xe, 16, out=eo), n=100), 3)}
+    ops["lns8_encode_k4096"] = {"us_per_call": round(H.per_launch(
+        lambda i: bs.lns8_encode(xe, 16, out=eo, stream=H.stream), 100), 3)}
     ci = torch.from_numpy(rng.permutation(128256)[:40].astype(np.int32)).to(dev)
     cs = torch.from_numpy(np.sort(rng.integers(0, 1 << 30, 40))[::-1].copy()).to(dev)
     res = torch.empty(6, dtype=torch.int64, device=dev)
-    ops["sample_candidates_n40"] = {"us_per_call": round(per_launch_us(
-        timer, lambda i: bs.sample_candidates(ci, cs, bs.SAMPLE_DRAW, beta_q16=1 << 10, seed=1,
-                                              position=i, result=res), n=100), 3)}
+    ops["sample_candidates_n40"] = {"us_per_call": round(H.per_launch(
+        lambda i: bs.sample_candidates(ci, cs, bs.SAMPLE_DRAW, beta_q16=1 << 10, seed=1,
+                                       position=i, result=res, stream=H.stream), 100), 3)}
     log("edges: quant %.2f us, encode %.2f us, sample %.2f us" % (
         ops["act_quant_i8_k2560"]["us_per_call"], ops["lns8_encode_k4096"]["us_per_call"],
         ops["sample_candidates_n40"]["us_per_call"]))
@@ -388,32 +687,57 @@ def run_extras(torch, bs, synth, dev, timer):
     info = torch.empty(2, dtype=torch.int32, device=dev)
     wsl = torch.zeros(bs.lib().bs_lmhead_workspace_bytes(V, K, 40, 200), dtype=torch.uint8,
                       device=dev)
-    us = per_launch_us(timer, lambda i: bs.lmhead_planes_topk(
+    us = H.per_launch(lambda i: bs.lmhead_planes_topk(
         pool03[i % 4], d47, drs, dh, V, K, 40, 200, top_idx=idx, top_score=sc, info=info,
-        workspace=wsl), n=20, reps=3)
+        workspace=wsl, stream=H.stream), 20, block="lmhead")
     stage1_bytes = p03.size + rs.nbytes
+    torch.cuda.synchronize()
     ops["lmhead_planes_topk_128256x2560"] = {
         "us_per_call": round(us, 3), "stage1_bytes": stage1_bytes,
         "GBps_stage1_bytes": round(stage1_bytes / us / 1e3, 1),
         "frac_hbm_peak": round(stage1_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
         "n_candidates": int(info[0].item()), "capped": int(info[1].item())}
     log("lm_head: %.2f us" % us)
+    del pool03
+    torch.cuda.empty_cache()
     return ops
 
 
+def context(torch, H):
+    """The empty-kernel floor: back-to-back launches of a kernel that does
+    nothing, at two grid sizes."""
+    out = {}
+    for blocks, threads in ((256, 256), (1024, 1024)):
+        out["launch_floor_us_%dx%d" % (blocks, threads)] = round(H.per_launch(
+            lambda i: H.probe.empty(blocks, threads, H.stream), 200, block="context_floor"), 3)
+    return out
+
+
+# ------------------------------------------------------- profile summaries
+
 def trace_summary(path: str):
-    """Per (kernel, grid) durations from a rocprofv3 --kernel-trace CSV."""
+    """Per-block kernel durations from a rocprofv3 --kernel-trace CSV of this
+    script: dispatches are assigned to the block named by the last marker
+    launch before them (an empty kernel of (4096 + id) x 64 threads)."""
     rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    by_id = {v: k for k, v in MARKER_ID.items()}
+    block = "setup"
     groups = {}
     for r in rows:
         name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
-        key = (name, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        grid, wg = int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"])
+        if "empty_kernel" in name and wg == 64 and grid % 64 == 0 and grid // 64 > MARKER_BASE:
+            block = by_id.get(grid // 64 - MARKER_BASE, "marker?")
+            continue
+        key = (block, name, grid, wg)
         groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     out = []
-    for (name, grid, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        out.append("%-70s grid %8d wg %4d calls %6d avg %8.3f us median %8.3f us min %8.3f us"
-                   % (name[:70], grid, wg, len(d), statistics.mean(d) / 1e3,
-                      statistics.median(d) / 1e3, min(d) / 1e3))
+    for (block, name, grid, wg), d in groups.items():
+        out.append("%-28s %-58s grid %8d wg %4d calls %6d avg %8.3f us median %8.3f us "
+                   "min %8.3f us" % (block[:28], name[:58], grid, wg, len(d),
+                                     statistics.mean(d) / 1e3, statistics.median(d) / 1e3,
+                                     min(d) / 1e3))
     return "\n".join(out)
 
 
@@ -433,14 +757,14 @@ def traffic_run(shape: str, launches: int = 20):
     dev = torch.device("cuda:0")
     a = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device=dev)
     b = torch.empty_like(a)
-    ps, ss, x = make_pool(torch, bs, synth, dev, rows, k, 0, 1 << 30)
+    _, views, x, _ = packed_pool(torch, bs, synth, dev, rows, k, 1 << 30)
     y = torch.empty(rows, dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
     for _ in range(3):
         torch.neg(a, out=b)
     torch.cuda.synchronize()
     for i in range(launches):
-        bs.ternary_gemv(ps[i % len(ps)], ss[i % len(ss)], x, rows, k, out=y)
+        bs.ternary_gemv(views[i % len(views)][0], views[i % len(views)][1], x, rows, k, out=y)
     torch.cuda.synchronize()
     log("traffic run done: 3 calibration launches, %d GEMV launches of %s" % (launches, shape))
 
@@ -458,7 +782,7 @@ def traffic_summary(fetch_csv: str, write_csv: str, shape: str):
                 continue
             v = float(r["Counter_Value"]) * 1024.0
             name = r["Kernel_Name"]
-            if "ternary_rows_kernel" in name or "ternary_tile_kernel" in name:
+            if "ternary_" in name and "_kernel" in name:
                 gemv.append(v)
             elif "neg" in name:
                 calib.append(v)
@@ -490,11 +814,12 @@ def traffic_summary(fetch_csv: str, write_csv: str, shape: str):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extras", action="store_true", help="skip the non-headline workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall time of each of the two all-step baseline legs")
     ap.add_argument("--trace-summary", help="summarise a rocprofv3 kernel_trace.csv and exit")
     ap.add_argument("--traffic-run", metavar="NxK",
                     help="run the workload of the --pmc traffic measurement and exit")
@@ -525,138 +850,22 @@ def main():
 
     dev = torch.device("cuda:0")
     bs.lib()
-    stream = torch.cuda.Stream(device=dev)
-    timer = Timer(torch, stream)
-
-    # layer pool: distinct weights for every layer, > 1 GiB in total.  Each
-    # launch's matrix is its member projections' rows, concatenated; a member
-    # is a row range of it (offsets are multiples of 64 rows, which is a
-    # valid packed matrix in both the plane and the scale layout).
-    import numpy as np
-    shape = {name: (r, k) for name, r, k in LAYER}
-    seed = {name: li for li, (name, _, _) in enumerate(LAYER)}
-    step_bytes = sum(weight_bytes(r, k) for _, r, k in LAYER)
-    n_layers = -(-(1 << 30) // step_bytes) + 1
-    log("building %d layers of synthetic BitNet-2B projections (%.1f MB each)" % (
-        n_layers, step_bytes / 1e6))
-    base = {}
-    for fname, members in FUSED:
-        parts = [synth.ternary(*shape[m], seed[m]) for m in members]
-        t = np.concatenate([pt[0] for pt in parts])
-        sc = np.concatenate([pt[1] for pt in parts])
-        k = shape[members[0]][1]
-        base[fname] = (torch.from_numpy(bs.ternary_pack(t)).to(dev),
-                       torch.from_numpy(bs.ternary_pack_scales(sc)).to(dev),
-                       torch.from_numpy(parts[0][2]).to(dev), t.shape[0], k)
-        del t, sc, parts
-    layers = [{f: (base[f][0].clone(), base[f][1].clone()) for f, _ in FUSED}
-              for _ in range(n_layers)]
-    # outputs; the residual-stream accumulators start at zero and only grow by
-    # |W x| < 2^35 per step, far from int64's range over the run
-    ys = {f: torch.zeros(base[f][3], dtype=torch.int64, device=dev) for f, _ in FUSED}
-    member_of = {}
-    for fname, members in FUSED:
-        row0 = 0
-        for m in members:
-            member_of[m] = (fname, row0)
-            row0 += shape[m][0]
-
-    def launch_fused(i, fname):
-        p, s = layers[i % n_layers][fname]
-        _, _, x, r, k = base[fname]
-        if fname in RESIDUAL:
-            bs.ternary_gemv_acc(p, s, x, r, k, ys[fname])
-        else:
-            bs.ternary_gemv(p, s, x, r, k, out=ys[fname])
-
-    def launch_member(i, m):
-        fname, row0 = member_of[m]
-        p, s = layers[i % n_layers][fname]
-        x, k = base[fname][2], base[fname][4]
-        r = shape[m][0]
-        pv = p[row0 * k // 4:(row0 + r) * k // 4]
-        sv = s[row0 * (k // 128):(row0 + r) * (k // 128)]
-        if fname in RESIDUAL:
-            bs.ternary_gemv_acc(pv, sv, x, r, k, ys[fname][row0:row0 + r])
-        else:
-            bs.ternary_gemv(pv, sv, x, r, k, out=ys[fname][row0:row0 + r])
-
-    def step(i):
-        for fname, _ in FUSED:
-            launch_fused(i, fname)
-
-    def step7(i):
-        for m, _, _ in LAYER:
-            launch_member(i, m)
-
-    # warmup, then the timed graph of exactly `steps` steps
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            step(i)
-    torch.cuda.synchronize()
-    g = timer.graph(lambda i: step(args.warmup + i), args.steps)
-    timer.replay_us(g)                          # first replay uploads the graph
-    us, wall_us = timer.replay_us(g)
-    ms_per_step = us / 1000.0 / args.steps
-    value = step_bytes * args.steps / (us * 1e-6) / 1e9
-    log("step (4 launches): %.3f ms (events), %.3f ms (host wall) -> %.1f GB/s" % (
-        ms_per_step, wall_us / 1000.0 / args.steps, value))
-    del g
-    g7 = timer.graph(lambda i: step7(args.warmup + i), args.steps)
-    timer.replay_us(g7)
-    us7, _ = timer.replay_us(g7)
-    value7 = step_bytes * args.steps / (us7 * 1e-6) / 1e9
-    log("step (7 launches): %.3f ms -> %.1f GB/s" % (us7 / 1000.0 / args.steps, value7))
-    del g7
-
-    # per-launch durations: the step's four launches and the seven members;
-    # the dominant kernel is the step launch with the largest share
-    launch_us = {f: per_launch_us(timer, lambda i, f=f: launch_fused(i, f)) for f, _ in FUSED}
-    member_us = {}
-    for m, r, k in LAYER:
-        if "%dx%d" % (r, k) not in member_us:
-            member_us["%dx%d" % (r, k)] = round(per_launch_us(
-                timer, lambda i, m=m: launch_member(i, m)), 3)
-    dom = max(launch_us, key=lambda f: launch_us[f])
-    dom_us = launch_us[dom]
-    dom_rows, dom_k = base[dom][3], base[dom][4]
-    dom_bytes = weight_bytes(dom_rows, dom_k)
-    achieved = dom_bytes / dom_us / 1e3
-    tag = "%dx%d" % (dom_rows, dom_k)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": _recorded_traffic(tag),
-                "kernel": "%s %s (%s, 1 launch per step)" % (
-                    "bs_ternary_gemv_acc" if dom in RESIDUAL else "bs_ternary_gemv", tag, dom),
-                "us_per_launch": round(dom_us, 3), "bytes_per_launch": dom_bytes}
-
+    H = Harness(torch, dev)
+    value, ms_per_step, cfg = run_step(torch, bs, synth, dev, H, args.steps, args.warmup)
+    gemv, roofline = run_shapes(torch, bs, synth, dev, H)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int64",
-        "data": "synthetic",
-        "config": {"workload": "bitnet-b1.58-2B decode projections q,k,v,o,gate,up,down, "
-                               "batch 1; q|k|v and gate|up stored concatenated by rows: "
-                               "4 dependent launches per step (qkv, gate_up: bs_ternary_gemv; "
-                               "o, down: bs_ternary_gemv_acc into the residual stream)",
-                   "launches": {f: "%dx%d" % (base[f][3], base[f][4]) for f, _ in FUSED},
-                   "weight_bytes_per_step": step_bytes, "layers_in_pool": n_layers,
-                   "pool_bytes": step_bytes * n_layers, "parallelism": "single GPU",
-                   "frac_hbm_peak_whole_job": round(value / HBM_PEAK_GBS, 4),
-                   "host_wall_ms_per_step": round(wall_us / 1000.0 / args.steps, 5),
-                   "us_per_launch": {f: round(v, 3) for f, v in launch_us.items()},
-                   "seven_launch_step": {"ms_per_step": round(us7 / 1000.0 / args.steps, 5),
-                                         "GBps": round(value7, 1),
-                                         "us_per_gemv": member_us}},
-        "roofline": roofline,
+        "data": "synthetic", "config": cfg, "roofline": roofline,
+        "ops": {"gemv": gemv},
     }
+    out["context"] = context(torch, H)
     if not args.no_extras:
-        out["ops"] = run_extras(torch, bs, synth, dev, timer)
-        out["ops"]["activation_reuse_sweep_k2560"] = activation_reuse_sweep(
-            torch, bs, synth, dev, timer)
-        out["context"] = context(torch, dev, timer)
+        out["ops"]["f1"] = run_f1(torch, bs, synth, dev, H)
+        out["ops"].update(run_extras(torch, bs, synth, dev, H))
     if not args.no_cpu_baseline:
-        log("timing the oracle on the host (~%.0f s)" % args.cpu_seconds)
+        log("timing the oracle on the host (~%.0f s)" % (2.5 * args.cpu_seconds))
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out))
     return 0

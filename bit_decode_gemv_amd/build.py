@@ -3,7 +3,8 @@
     python -m bit_decode_gemv_amd.build
 
 compiles every source under ``csrc/`` with hipcc into
-``bit_decode_gemv_amd/libbitstate.so``.  The HIP sources are built with packed
+``bit_decode_gemv_amd/libbitstate.so`` (the hot path) and the measurement
+kernels under ``probe/`` into ``bit_decode_gemv_amd/probe/libbsprobe.so``.  The HIP sources are built with packed
 FP32 instructions disabled (the device pass accepts the feature; the host
 pass warns that it does not know it, which is harmless).
 """
@@ -19,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbitstate.so")
+PROBE_DIR = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PROBE_DIR, "libbsprobe.so")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -32,34 +35,49 @@ def sources():
         glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every source, link libbitstate.so; returns its path."""
-    objdir = os.path.join(PKG, "_build")
-    os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for src in sources():
-        obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [HIPCC] + COMMON_FLAGS
-        if src.endswith(".hip"):
-            cmd += HIP_FLAGS
-        cmd += ["-c", src, "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
-        if res.returncode != 0:
-            raise RuntimeError("hipcc failed for %s:\n%s" % (src, errs))
-        if errs.strip() and verbose:
-            print(errs, file=sys.stderr)
-        objs.append(obj)
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, out, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH] + objs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n%s" % res.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def _compile(srcs, objdir, verbose):
+    """Compile the sources in parallel (one hipcc per source)."""
+    os.makedirs(objdir, exist_ok=True)
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=max(1, min(8, os.cpu_count() or 1))) as ex:
+        return list(ex.map(lambda src: _compile_one(src, objdir, verbose), srcs))
+
+
+def _compile_one(src, objdir, verbose):
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + COMMON_FLAGS
+    if src.endswith(".hip"):
+        cmd += HIP_FLAGS
+    cmd += ["-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (src, errs))
+    if errs.strip() and verbose:
+        print(errs, file=sys.stderr)
+    return obj
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every source, link libbitstate.so (the hot path) and
+    libbsprobe.so (the benchmark's measurement kernels); returns the first."""
+    _link(_compile(sources(), os.path.join(PKG, "_build"), verbose), LIB, verbose)
+    probe_srcs = sorted(glob.glob(os.path.join(PROBE_DIR, "*.hip")))
+    _link(_compile(probe_srcs, os.path.join(PKG, "_build", "probe"), verbose), PROBE_LIB, verbose)
     return LIB
 
 

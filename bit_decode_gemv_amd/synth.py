@@ -46,7 +46,8 @@ def _streams(seed: int, n: int):
 
 def _trits(rng, shape, p_zero: float) -> np.ndarray:
     """iid trits; p_zero = 1/3 gives uniform {-1,0,+1}; p_zero = 0.4 gives
-    P(0) = 0.4 and P(+1) = P(-1) = 0.3."""
+    P(0) = 0.4 and P(+1) = P(-1) = 0.3; any other p_zero in [0, 1] gives
+    P(0) = p_zero with equiprobable signs."""
     if abs(p_zero - 1.0 / 3.0) < 1e-12:
         t = rng.integers(0, 3, size=shape, dtype=np.int8)
         t -= 1
@@ -55,7 +56,12 @@ def _trits(rng, shape, p_zero: float) -> np.ndarray:
         u = rng.integers(0, 10, size=shape, dtype=np.int8)
         lut = np.array([0, 0, 0, 0, 1, 1, 1, -1, -1, -1], dtype=np.int8)
         return lut[u]
-    raise ValueError("p_zero must be 1/3 or 0.4")
+    if not 0.0 <= p_zero <= 1.0:
+        raise ValueError("p_zero must be in [0, 1]")
+    # any other zero density (the Phase B sweeps): P(+1) = P(-1)
+    u = rng.random(size=shape)
+    t = np.where(u < p_zero, 0, np.where(u < p_zero + (1.0 - p_zero) / 2.0, 1, -1))
+    return t.astype(np.int8)
 
 
 def _act_normal32(rng, k: int) -> np.ndarray:
@@ -104,6 +110,23 @@ def lns8(rows: int, k: int, seed: int):
     code = np.where(is_zero, np.uint8(0), code).astype(np.uint8)
     x = ((sign << 7) | code).astype(np.uint8)
     return t, x
+
+
+def lns8_sweep(rows: int, k: int, seed: int, p_zero: float, n_codes: int):
+    """LNS8 inputs for the Phase B sweeps: ternary weights with P(0) = p_zero
+    (signs equiprobable), activations with 5% zero codes and the rest uniform
+    over ``n_codes`` distinct non-zero codes evenly spread over 1..127 (41
+    codes over 60..100 is the workload's own recipe), signs uniform."""
+    if not 1 <= n_codes <= 127:
+        raise ValueError("n_codes must be in 1..127")
+    rt, rsign, rzero, rcode = _streams(seed, 4)
+    t = _trits(rt, (rows, k), p_zero)
+    codes = np.unique(np.rint(np.linspace(1, 127, n_codes)).astype(np.int64)).astype(np.uint8)
+    sign = rsign.integers(0, 2, size=k, dtype=np.uint8)
+    is_zero = rzero.random(size=k) < 0.05
+    code = codes[rcode.integers(0, codes.size, size=k)]
+    code = np.where(is_zero, np.uint8(0), code).astype(np.uint8)
+    return t, ((sign << 7) | code).astype(np.uint8)
 
 
 def lmhead(vocab: int, dim: int, seed: int):

@@ -28,6 +28,26 @@ def test_library_exports_every_header_symbol():
     assert lib.bs_abi_version() == 1
 
 
+def test_probe_library_exports_its_header():
+    """The benchmark's measurement kernels (include/bs_probe.h) are exported
+    by libbsprobe.so; host validation runs without a GPU."""
+    import re
+    from bit_decode_gemv_amd import probe
+    lib = probe.lib()
+    names = sorted(set(re.findall(r"\b(bs_probe_[a-z0-9_]+)\s*\(", open(probe.HEADER).read())))
+    assert names == ["bs_probe_empty", "bs_probe_read", "bs_probe_read_sink_count"]
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.bs_probe_read_sink_count(4096 * 8, 8) == 256
+    assert lib.bs_probe_read_sink_count(4096 * 8 + 1, 8) == 512
+    assert lib.bs_probe_read_sink_count(0, 8) == -3
+    assert lib.bs_probe_read_sink_count((1 << 31) - 15, 8) == -3
+    assert lib.bs_probe_read_sink_count(4096, 3) == -3
+    assert lib.bs_probe_read(None, 4096, 8, FAKE, None) == -1
+    assert lib.bs_probe_empty(0, 64, None) == -3
+    assert lib.bs_probe_empty(1, 100, None) == -3
+
+
 def test_status_strings():
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert bs.status_str(code)

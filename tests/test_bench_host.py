@@ -30,21 +30,44 @@ def _write(path, fields, rows):
 
 
 def test_trace_summary(tmp_path):
+    """Dispatches are split per measured block by the marker launches (empty
+    kernels of (4096 + block id) x 64 threads) that precede them."""
     p = tmp_path / "kernel_trace.csv"
     fields = ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"]
-    rows = [{"Kernel_Name": "void bs::(anonymous namespace)::ternary_rows_kernel<16, 1>(x)",
-             "Grid_Size_X": 1024, "Workgroup_Size_X": 512, "Start_Timestamp": 1000 * i,
-             "End_Timestamp": 1000 * i + d} for i, d in enumerate([3000, 4000, 5000])]
-    _write(p, fields, rows)
-    out = bench.trace_summary(str(p))
-    assert "void bs::ternary_rows_kernel<16, 1>" in out
-    assert "calls      3" in out and "avg    4.000 us" in out and "min    3.000 us" in out
+    gemv = "void bs::(anonymous namespace)::ternary_pipe_kernel<16, 3, 2, 2>(x)"
+
+    def marker(block, t):
+        mid = bench.MARKER_ID[block]
+        return {"Kernel_Name": "(anonymous namespace)::empty_kernel()",
+                "Grid_Size_X": (bench.MARKER_BASE + mid) * 64, "Workgroup_Size_X": 64,
+                "Start_Timestamp": t, "End_Timestamp": t + 100}
+
+    rows = [marker("gemv_2560x2560", 0)]
+    rows += [{"Kernel_Name": gemv, "Grid_Size_X": 30720, "Workgroup_Size_X": 192,
+              "Start_Timestamp": 1000 * (i + 1), "End_Timestamp": 1000 * (i + 1) + d}
+             for i, d in enumerate([3000, 4000, 5000])]
+    rows += [marker("gemv_640x2560", 10000)]
+    rows += [{"Kernel_Name": gemv, "Grid_Size_X": 30720, "Workgroup_Size_X": 192,
+              "Start_Timestamp": 20000, "End_Timestamp": 22000}]
+    _write(p, fields, list(reversed(rows)))            # order restored by start time
+    out = bench.trace_summary(str(p)).splitlines()
+    assert len(out) == 2
+    a = [line for line in out if line.startswith("gemv_2560x2560")][0]
+    b = [line for line in out if line.startswith("gemv_640x2560")][0]
+    assert "void bs::ternary_pipe_kernel<16, 3, 2, 2>" in a
+    assert "calls      3" in a and "avg    4.000 us" in a and "min    3.000 us" in a
+    assert "calls      1" in b and "avg    2.000 us" in b
+
+
+def test_marker_ids_are_distinct_and_small():
+    ids = list(bench.MARKER_ID.values())
+    assert len(set(ids)) == len(ids) and min(ids) >= 1 and max(ids) < 1024
 
 
 def test_traffic_summary(tmp_path):
     fields = ["Kernel_Name", "Counter_Name", "Counter_Value"]
     calib = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>"
-    gemv = "void bs::(anonymous namespace)::ternary_rows_kernel<16, 1>(args)"
+    gemv = "void bs::(anonymous namespace)::ternary_pipe_kernel<16, 3, 2, 2>(args)"
     half = bench.CALIB_BYTES / 1024 / 2          # FETCH_SIZE reads half the known bytes
     _write(tmp_path / "f.csv", fields,
            [{"Kernel_Name": calib, "Counter_Name": "FETCH_SIZE", "Counter_Value": half}] * 3 +
