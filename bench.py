@@ -43,6 +43,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
        python bench.py --trace-summary <rocprofv3 kernel_trace.csv>
        python bench.py --traffic-run NxK       (workload of the --pmc runs)
        python bench.py --traffic-summary FETCH.csv WRITE.csv NxK
+       python bench.py --lns8-counter-run      (workload of the LNS8 --pmc runs)
+       python bench.py --counter-summary COUNTERS.csv
 """
 from __future__ import annotations
 
@@ -769,6 +771,37 @@ def traffic_run(shape: str, launches: int = 20):
     log("traffic run done: 3 calibration launches, %d GEMV launches of %s" % (launches, shape))
 
 
+def lns8_counter_run(launches: int = 10):
+    """Workload for the rocprofv3 --pmc runs behind the LNS8 VALU fraction:
+    `launches` calls of each LNS8 path (direct, then popcount) at 4096 x 4096
+    on distinct weight buffers."""
+    import torch
+    import bit_decode_gemv_amd as bs
+    from bit_decode_gemv_amd import synth
+    dev = torch.device("cuda:0")
+    t8, x8 = synth.lns8(4096, 4096, 0)
+    p8 = torch.from_numpy(bs.ternary_pack(t8)).to(dev)
+    pool = [p8.clone() for _ in range(launches)]
+    xd = torch.from_numpy(x8).to(dev)
+    for path in (bs.LNS8_DIRECT, bs.LNS8_POPCOUNT):
+        for i in range(launches):
+            bs.lns8_phase_gemv(pool[i], xd, 4096, 4096, path)
+        torch.cuda.synchronize()
+    log("LNS8 counter run done: %d calls per path" % launches)
+
+
+def counter_summary(path: str):
+    """Mean of every counter per kernel name (template arguments kept) from
+    a rocprofv3 --pmc counter_collection.csv: one line per (kernel, counter)."""
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+        vals.setdefault((name, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    return "\n".join("%-60s %-20s dispatches %4d mean %.6g" % (n[:60], c, len(v),
+                                                                 statistics.mean(v))
+                     for (n, c), v in sorted(vals.items()))
+
+
 def traffic_summary(fetch_csv: str, write_csv: str, shape: str):
     """HBM bytes per GEMV launch from two rocprofv3 counter CSVs (FETCH_SIZE,
     WRITE_SIZE; KiB per dispatch), each scaled by the calibration kernel's
@@ -825,6 +858,9 @@ def main():
                     help="run the workload of the --pmc traffic measurement and exit")
     ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "NxK"),
                     help="HBM bytes per launch from the two counter CSVs and exit")
+    ap.add_argument("--lns8-counter-run", action="store_true",
+                    help="run the workload of the LNS8 --pmc runs and exit")
+    ap.add_argument("--counter-summary", help="mean counters per kernel of a --pmc CSV and exit")
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
@@ -834,6 +870,12 @@ def main():
         return 0
     if args.traffic_run:
         traffic_run(args.traffic_run)
+        return 0
+    if args.lns8_counter_run:
+        lns8_counter_run()
+        return 0
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary))
         return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the GEMVs would "

@@ -19,10 +19,16 @@
 //               & (sign ^ W_neg)) and A[s & 7] += C_s << (s >> 3): the
 //               histogram H[phase][band] folded into A as it is produced.
 // The wavefronts' A[8] meet in LDS (integer addition is associative, so the
-// order is free).  When K is split over several workgroups per tile, each
-// writes its partial A to the workspace with plain stores and a second
-// kernel sums the partials, writes A and materialises S: no atomics, and the
-// kernel boundary makes every partial visible across the XCDs.
+// order is free).  When K is split over several workgroups per tile (64
+// tiles alone would leave most of the GPU idle), each workgroup writes its
+// partial A to the workspace with agent-scope stores (coherent across the
+// XCDs' L2s: written through, as the compiler implements agent-scope atomic
+// stores), waits for them to complete, and counts itself done on the tile's
+// counter with an agent-scope atomic add; the workgroup that finds itself
+// last reads the partials with agent-scope loads, sums them, writes A and S
+// and returns the counter and the partials to zero for the next call.  One launch, no spin,
+// and no L2 write-back or invalidate: a release/acquire pair on the counter
+// (buffer_wbl2 + buffer_inv) measured 19.5 us per call instead of 10-11.
 #include "kcommon.h"
 
 namespace bs {
@@ -137,8 +143,9 @@ template <int PATH>
 __global__ __launch_bounds__(1024) void lns8_kernel(
     const uint8_t *__restrict__ planes, const uint8_t *__restrict__ x, int rows, int groups,
     int upw, int nsplit, int32_t *__restrict__ acc_out, double *__restrict__ s_out,
-    int *__restrict__ partial) {
+    int *__restrict__ counters, int *__restrict__ partial) {
     __shared__ int red[16][8][64];
+    __shared__ int last;
     const int tile = blockIdx.x / nsplit;
     const int split = blockIdx.x - tile * nsplit;
     const int nw = blockDim.x >> 6;
@@ -163,50 +170,50 @@ __global__ __launch_bounds__(1024) void lns8_kernel(
         red[0][p][j] = t;   // wavefront 0's entry of this pair is read only here
     }
     __syncthreads();
+    if (nsplit > 1) {
+        // this split's partial, then the tile's counter
+        const size_t padded_rows = (size_t)(gridDim.x / nsplit) * 64;
+        for (int idx = threadIdx.x; idx < 512; idx += blockDim.x) {
+            const int p = idx >> 6, j = idx & 63;
+            __hip_atomic_store(partial + ((size_t)split * padded_rows + tile * 64 + j) * 8 + p,
+                               red[0][p][j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's stores are done
+        __syncthreads();
+        if (threadIdx.x == 0)
+            last = __hip_atomic_fetch_add(counters + tile, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+        __syncthreads();
+        if (!last) return;                     // uniform
+        // sum the partials and clear them: every call leaves the whole
+        // workspace zero, so the counters of a later call with more tiles
+        // never land on stale partials
+        for (int idx = threadIdx.x; idx < 512; idx += blockDim.x) {
+            const int p = idx >> 6, j = idx & 63;
+            int t = 0;
+            for (int sp = 0; sp < nsplit; ++sp) {
+                int *src = partial + ((size_t)sp * padded_rows + tile * 64 + j) * 8 + p;
+                t += __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                *src = 0;
+            }
+            red[0][p][j] = t;   // only this thread reads or writes pair (p, j) here
+        }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+    }
     if (threadIdx.x < 64) {
         const int row = tile * 64 + threadIdx.x;
-        int T[8];
+        if (row < rows) {
+            int T[8];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) T[p] = red[0][p][threadIdx.x];
-        if (nsplit == 1) {
-            if (row < rows) {
-#pragma unroll
-                for (int p = 0; p < 8; ++p) acc_out[(size_t)row * 8 + p] = T[p];
-                if (s_out) s_out[row] = materialize(T);
-            }
-        } else {
-            const size_t padded_rows = (size_t)(gridDim.x / nsplit) * 64;
-            int4 *dst = reinterpret_cast<int4 *>(partial + ((size_t)split * padded_rows + row) * 8);
+            for (int p = 0; p < 8; ++p) T[p] = red[0][p][threadIdx.x];
+            int4 *dst = reinterpret_cast<int4 *>(acc_out + (size_t)row * 8);
             dst[0] = make_int4(T[0], T[1], T[2], T[3]);
             dst[1] = make_int4(T[4], T[5], T[6], T[7]);
+            if (s_out) s_out[row] = materialize(T);
         }
     }
-}
-
-// Sum of the nsplit partials: thread (row, p) adds phase p of one row over
-// the splits (four loads in flight); the rows' eight sums meet in LDS for S.
-__global__ __launch_bounds__(256) void lns8_combine(const int *__restrict__ partial, int rows,
-                                                   int padded_rows, int nsplit,
-                                                   int32_t *__restrict__ acc_out,
-                                                   double *__restrict__ s_out) {
-    __shared__ int sums[32][8];
-    const int idx = blockIdx.x * 256 + threadIdx.x;   // = row * 8 + p
-    const int row = idx >> 3, p = idx & 7;
-    int t = 0;
-    if (row < rows) {
-        int sp = 0;
-        for (; sp + 4 <= nsplit; sp += 4) {
-            int v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = partial[((size_t)(sp + u) * padded_rows + row) * 8 + p];
-            t += v[0] + v[1] + v[2] + v[3];
-        }
-        for (; sp < nsplit; ++sp) t += partial[((size_t)sp * padded_rows + row) * 8 + p];
-        acc_out[idx] = t;
-    }
-    sums[threadIdx.x >> 3][p] = t;
-    __syncthreads();
-    if (s_out && p == 0 && row < rows) s_out[row] = materialize(sums[threadIdx.x >> 3]);
 }
 
 }  // namespace
@@ -222,6 +229,7 @@ static constexpr int64_t kLns8MaxK = 65408;
 // scalar/vector dependency chains of the per-product loop), up to 16 per
 // workgroup, each with at least one 64-position unit; K is split over
 // workgroups only when one workgroup per tile cannot hold them.
+
 struct Lns8Plan {
     int64_t tiles, groups;
     int waves, upw, nsplit;
@@ -242,13 +250,26 @@ static Lns8Plan lns8_plan(int64_t rows, int64_t k) {
     return pl;
 }
 
-// Workspace: the partial accumulators, int32[nsplit][R][8] (none when K is
-// not split).  Written before they are read: no initialisation needed.
-static size_t lns8_ws_bytes(int64_t rows, int64_t k) {
+// Workspace, when K is split: one int32 counter per tile (256-byte
+// aligned), then the partial accumulators int32[nsplit][R][8].  It must be
+// zero before the first call, and every call leaves it zero (the last
+// workgroup of a tile clears the tile's counter and partials).
+struct Lns8Ws {
+    size_t counters, partial, total;
+};
+
+static Lns8Ws lns8_ws(int64_t rows, int64_t k) {
     const Lns8Plan pl = lns8_plan(rows, k);
-    const size_t part = pl.nsplit > 1 ? (size_t)pl.nsplit * (size_t)pad64(rows) * 8 * 4 : 0;
-    return align_up(part > 0 ? part : 1, kWsAlign);
+    Lns8Ws w;
+    w.counters = 0;
+    w.partial = pl.nsplit > 1 ? align_up((size_t)pl.tiles * 4, kWsAlign) : 0;
+    w.total = pl.nsplit > 1 ? w.partial + (size_t)pl.nsplit * (size_t)pad64(rows) * 8 * 4
+                            : kWsAlign;
+    w.total = align_up(w.total, kWsAlign);
+    return w;
 }
+
+static size_t lns8_ws_bytes(int64_t rows, int64_t k) { return lns8_ws(rows, k).total; }
 
 extern "C" size_t bs_lns8_workspace_bytes(int64_t rows, int64_t k) {
     if (check_rows_k(rows, k, kLns8MaxK) != BS_OK) return 0;
@@ -268,17 +289,15 @@ extern "C" int32_t bs_lns8_phase_gemv(const uint8_t *planes, const uint8_t *x_ln
     if (!ws_ok(workspace, workspace_bytes, lns8_ws_bytes(rows, k))) return BS_E_WORKSPACE;
 
     const Lns8Plan pl = lns8_plan(rows, k);
+    const Lns8Ws w = lns8_ws(rows, k);
     hipStream_t st = (hipStream_t)stream;
-    int *partial = static_cast<int *>(workspace);
+    unsigned char *base = static_cast<unsigned char *>(workspace);
+    int *counters = reinterpret_cast<int *>(base + w.counters);
+    int *partial = reinterpret_cast<int *>(base + w.partial);
     auto kern = path == BS_LNS8_DIRECT ? lns8_kernel<BS_LNS8_DIRECT> : lns8_kernel<BS_LNS8_POPCOUNT>;
     hipLaunchKernelGGL(kern, dim3((unsigned)(pl.tiles * pl.nsplit)), dim3(pl.waves * 64), 0, st,
                        planes, x_lns8, (int)rows, (int)pl.groups, pl.upw, pl.nsplit, acc, s,
-                       partial);
+                       counters, partial);
     BS_LAUNCH_CHECK();
-    if (pl.nsplit > 1) {
-        hipLaunchKernelGGL(lns8_combine, dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, st,
-                           partial, (int)rows, (int)pad64(rows), pl.nsplit, acc, s);
-        BS_LAUNCH_CHECK();
-    }
     return BS_OK;
 }

@@ -187,10 +187,12 @@ int32_t bs_q1_gemv(const uint8_t *bits, const int16_t *scales, const int8_t *x, 
  *   acc     device int32[rows][8], overwritten, 4-byte aligned
  *   s       device double[rows], or NULL to skip the materialisation
  *   workspace  device scratch of at least bs_lns8_workspace_bytes(rows, k)
- *           bytes, 256-byte aligned, caller-owned: the partial accumulators
- *           when K is split over several workgroups.  Every byte is written
- *           before it is read, so it needs no initialisation; calls that may
- *           overlap need separate workspaces.
+ *           bytes, 256-byte aligned, caller-owned: when K is split over
+ *           several workgroups, a counter per 64-row tile and the partial
+ *           accumulators.  Zero it before its first use; every call leaves
+ *           it zero again, so one workspace serves calls of any shape
+ *           ordered on one stream.  Calls that may overlap need separate
+ *           workspaces.
  * Errors: BS_E_NULL, BS_E_SHAPE, BS_E_OVERFLOW (k), BS_E_RANGE (path),
  *   BS_E_ALIGN, BS_E_WORKSPACE, BS_E_HIP.
  */

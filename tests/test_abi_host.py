@@ -179,10 +179,11 @@ def test_lmhead_vocab_limit():
 
 def test_workspace_sizes_follow_the_launch_plans():
     lib = bs.lib()
-    # LNS8: partials only when K is split over workgroups (int32[nsplit][R][8])
+    # LNS8: when K is split over workgroups, one int32 counter per 64-row tile
+    # (256-byte aligned) and the partials int32[nsplit][R][8]
     assert lib.bs_lns8_workspace_bytes(2000, 128) == 256
-    assert lib.bs_lns8_workspace_bytes(4096, 4096) == 4 * 4096 * 8 * 4
-    assert lib.bs_lns8_workspace_bytes(64, 65408) == 64 * 64 * 8 * 4
+    assert lib.bs_lns8_workspace_bytes(4096, 4096) == 256 + 4 * 4096 * 8 * 4
+    assert lib.bs_lns8_workspace_bytes(64, 65408) == 256 + 64 * 64 * 8 * 4
     # lm_head: grows with the vocabulary, not with top_k beyond the bounds
     a = lib.bs_lmhead_workspace_bytes(128256, 2560, 40, 200)
     assert a == lib.bs_lmhead_workspace_bytes(128256, 2560, 200, 200) > 128256 * 40

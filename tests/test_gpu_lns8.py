@@ -50,7 +50,7 @@ def check(t, x):
     return results[0][1], want_s
 
 
-@pytest.mark.parametrize("seed", range(2))
+@pytest.mark.parametrize("seed", range(5))
 def test_lns8_config(seed):
     s, want = check(*synth.lns8(4096, 4096, seed))
     # exact-then-round on both sides: report, and expect, bit equality
@@ -98,3 +98,36 @@ def test_lns8_max_k_extremes():
     k = 65408
     t = np.ones((64, k), np.int8)
     check(t, np.full(k, 127, np.uint8))
+
+
+def test_split_k_counters_reused_across_calls():
+    """The split-K reduction's last-workgroup counters live in the caller's
+    workspace: one zeroed workspace, many calls of several shapes (both
+    paths, growing and shrinking tile counts), every result exact and the
+    used workspace zero again after each call."""
+    import torch
+    dev = device()
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=dev)
+    cases = [synth.lns8(4096, 4096, 7), synth.lns8(1000, 2560, 8), synth.lns8(8192, 1024, 9),
+             synth.lns8(64, 8192, 10)]
+    want = [oracle.lns8_direct(t, x) for t, x in cases]
+    dev_in = [(to_dev(bs.ternary_pack(t), dev), to_dev(x, dev)) for t, x in cases]
+    for rep in range(6):
+        for ci, ((t, x), (pd, xd)) in enumerate(zip(cases, dev_in)):
+            rows, k = t.shape
+            need = bs.lib().bs_lns8_workspace_bytes(rows, k)
+            assert need <= ws.numel()
+            path = (rep + ci) % 2
+            note("lns8 reuse rep=%d case=%d path=%d" % (rep, ci, path))
+            acc, _ = bs.lns8_phase_gemv(pd, xd, rows, k, path, s=False, workspace=ws)
+            torch.cuda.synchronize()
+            assert (acc.cpu().numpy() == want[ci]).all(), (rep, ci, path)
+            assert int(ws[:need].view(torch.int32).abs().sum().item()) == 0, (rep, ci)
+
+
+@pytest.mark.parametrize("p_zero,n_codes", [(0.0, 41), (0.9, 41), (1 / 3, 1), (1 / 3, 8),
+                                            (1 / 3, 127), (0.6, 127)])
+def test_phase_b_inputs(p_zero, n_codes):
+    """The inputs of the benchmark's Phase B sweeps (weight zero density,
+    number of distinct activation codes)."""
+    check(*synth.lns8_sweep(512, 4096, 3, p_zero, n_codes))
