@@ -20,7 +20,8 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Shape checks shared by the entry points.
 inline int32_t check_rows_k(int64_t rows, int64_t k, int64_t k_max) {
     if (rows < 1 || k < kGroup || k % kGroup != 0) return BS_E_SHAPE;
-    if (rows > (int64_t)1 << 31) return BS_E_SHAPE;
+    // the kernels index rows (and the last tile's padding rows) in int32
+    if (rows > ((int64_t)1 << 31) - 64) return BS_E_SHAPE;
     if (k > k_max) return BS_E_OVERFLOW;
     return BS_OK;
 }

@@ -109,7 +109,8 @@ int32_t bs_ternary_pack_scales(const int16_t *scales, int64_t rows, int64_t k,
  *           bs_ternary_scales_count of them, 2-byte aligned
  *   x       device, int8[k] activations (two's complement, -128 allowed),
  *           8-byte aligned
- *   rows    >= 1;  k >= 128, k % 128 == 0, k <= 2^24
+ *   rows    1 .. 2^31 - 64 (else BS_E_SHAPE);  k >= 128, k % 128 == 0,
+ *           k <= 2^24
  *   frac    0..62: fractional bits of the fixed-point scale; the floor is
  *           applied per group, before the sum over groups
  *   y       device, int64[rows], overwritten, 8-byte aligned
@@ -181,7 +182,7 @@ int32_t bs_q1_gemv(const uint8_t *bits, const int16_t *scales, const int8_t *x, 
  *           (sign XOR W_negative)), H[phase][band] += C_s,
  *           A[p] = sum_b H[p][b] * 2^b ([BS] sections 3.1, 4).
  *           Both paths return identical bytes.
- *   rows    >= 1;  k >= 128, k % 128 == 0, k <= 65408 (|A| <= k*2^15 must
+ *   rows    1 .. 2^31 - 64;  k >= 128, k % 128 == 0, k <= 65408 (|A| <= k*2^15 must
  *           fit int32, else BS_E_OVERFLOW)
  *   planes  device, 16-byte aligned; x_lns8 device uint8[k], 4-byte aligned
  *   acc     device int32[rows][8], overwritten, 4-byte aligned

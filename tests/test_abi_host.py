@@ -262,3 +262,19 @@ def test_edges_steps_validation():
     assert smp(min_p=65537) == bs.BS_E_RANGE
     assert smp(score=ctypes.c_void_p((1 << 20) + 4)) == bs.BS_E_ALIGN
     assert smp(idx=ctypes.c_void_p((1 << 20) + 2)) == bs.BS_E_ALIGN
+
+
+def test_row_counts_past_int32_indexing_are_rejected():
+    """The kernels index rows (with the last tile's padding) in int32: row
+    counts above 2^31 - 64 fail on the host with BS_E_SHAPE, before any HIP
+    call (fake pointers are never dereferenced)."""
+    lib = bs.lib()
+    big = (1 << 31) - 63
+    for rows in (big, 1 << 31, 1 << 40):
+        assert lib.bs_ternary_gemv(FAKE, FAKE, FAKE, rows, 128, 0, FAKE, None) == bs.BS_E_SHAPE
+        assert lib.bs_ternary_gemv_acc(FAKE, FAKE, FAKE, rows, 128, 0, FAKE, None) == \
+            bs.BS_E_SHAPE
+        assert lib.bs_q1_gemv(FAKE, FAKE, FAKE, rows, 128, 0, FAKE, None) == bs.BS_E_SHAPE
+        assert lib.bs_lns8_phase_gemv(FAKE, FAKE, rows, 128, 0, FAKE, FAKE, FAKE, 1 << 20,
+                                      None) == bs.BS_E_SHAPE
+        assert lib.bs_lns8_workspace_bytes(rows, 128) == 0
