@@ -348,18 +348,23 @@ def lmhead_brute_mt(trits, row_scale, h, top_k: int):
     return idx, sc
 
 
-def lmhead_two_stage(trits, row_scale, h, top_k: int, cap: int):
-    """Returns (top_idx int32[k], top_score int64[k], n_candidates, capped)."""
+def lmhead_two_stage(trits, row_scale, h, top_k: int, cap: int, certificate: bool = False):
+    """Returns (top_idx int32[k], top_score int64[k], n_candidates, capped),
+    and with certificate=True also the exactness certificate (1 when the
+    result is provably the exact top-k: nothing dropped, or every dropped
+    candidate's upper bound strictly below the k-th output score)."""
     trits = np.ascontiguousarray(trits, dtype=np.int8)
     row_scale = np.ascontiguousarray(row_scale, dtype=np.int32)
     h = np.ascontiguousarray(h, dtype=np.int8)
     V, _, K = trits.shape
     idx = np.zeros(top_k, dtype=np.int32)
     sc = np.zeros(top_k, dtype=np.int64)
-    info = np.zeros(2, dtype=np.int64)
+    info = np.zeros(3, dtype=np.int64)
     _check(_load().or_lmhead_two_stage(_p(trits), _p(row_scale), _p(h), _i64(V), _i64(K),
                                        ctypes.c_int(top_k), ctypes.c_int(cap), _p(idx),
                                        _p(sc), _p(info)), "lmhead_two_stage")
+    if certificate:
+        return idx, sc, int(info[0]), int(info[1]), int(info[2])
     return idx, sc, int(info[0]), int(info[1])
 
 

@@ -554,7 +554,9 @@ int or_lmhead_brute(const int8_t *trits, const int32_t *row_scale, const int8_t 
  * C = { r : U(r) >= L_k }.  If |C| <= cap every row of C is rescored;
  * otherwise the cap rows of C with the largest S1' (index ascending on ties)
  * are rescored and capped = 1.  Rescoring adds E2 = sum_{p=4..7} 3^(7-p) T_p.h:
- * S' = rs*(81*E1 + E2).  info[0] = |C|, info[1] = capped. */
+ * S' = rs*(81*E1 + E2).  info[0] = |C|, info[1] = capped, info[2] = 1 when
+ * the result is certified exact: nothing dropped, or the largest upper bound
+ * U among the dropped candidates strictly below the k-th output S'. */
 int or_lmhead_two_stage(const int8_t *trits, const int32_t *row_scale, const int8_t *h,
                         int64_t V, int64_t K, int top_k, int cap, int32_t *top_idx,
                         int64_t *top_score, int64_t *info)
@@ -601,10 +603,17 @@ int or_lmhead_two_stage(const int8_t *trits, const int32_t *row_scale, const int
         }
     int64_t keep = n;
     int capped = 0;
+    int64_t umax_dropped = INT64_MIN;
     if (n > cap) {
         qsort(cand, (size_t)n, sizeof(keyed_row), cmp_desc);
         keep = cap;
         capped = 1;
+        /* the largest upper bound among the candidates the cap drops */
+        for (int64_t c = cap; c < n; c++) {
+            int64_t r = cand[c].idx;
+            if (s1[r] + bnd[r] > umax_dropped)
+                umax_dropped = s1[r] + bnd[r];
+        }
     }
     /* rescoring with planes 4..7 */
     for (int64_t c = 0; c < keep; c++) {
@@ -621,6 +630,11 @@ int or_lmhead_two_stage(const int8_t *trits, const int32_t *row_scale, const int
     }
     info[0] = n;
     info[1] = capped;
+    /* certificate: the result is the exact top-k when nothing was dropped,
+     * or when every dropped row's upper bound U >= S' lies strictly below
+     * the k-th output score (then no dropped row can reach the output, ties
+     * included) */
+    info[2] = !capped || umax_dropped < top_score[top_k - 1];
     free(e1);
     free(s1);
     free(bnd);

@@ -209,3 +209,59 @@ def test_brute_row_parallel_matches_single_thread():
         gi, gs = oracle.lmhead_brute_mt(trits, rs, h, 40)
         assert (gi == wi).all() and (gs == ws).all()
     oracle.set_threads(1)
+
+
+def numpy_certificate(trits, rs, h, k, cap):
+    """The exactness certificate from its definition, in NumPy: stage-1
+    scores S1' = 81*rs*E1 and bounds B' = 40*|rs|*sum|h| per row, L_k the
+    k-th largest S1' - B', C = {U >= L_k}; when |C| > cap the rows of C past
+    the top `cap` by (S1' desc, row asc) are dropped, and the certificate
+    holds iff max U over them < the k-th output score (which the brute
+    force gives whenever the result is exact, and the two-stage oracle
+    gives always)."""
+    t = trits.astype(np.int64)
+    hh = h.astype(np.int64)
+    e1 = sum(3 ** (3 - p) * (t[:, p, :] @ hh) for p in range(4))
+    s1 = 81 * rs.astype(np.int64) * e1
+    b = 40 * np.abs(rs.astype(np.int64)) * int(np.abs(hh).sum())
+    lk = np.sort(s1 - b)[::-1][k - 1]
+    c = np.nonzero(s1 + b >= lk)[0]
+    if c.size <= cap:
+        return c.size, 0, None
+    order = c[np.lexsort((c, -s1[c]))]
+    return c.size, 1, (s1 + b)[order[cap:]].max()
+
+
+@pytest.mark.parametrize("V,K,k,cap,seed", [(3000, 256, 10, 10, 92), (4000, 256, 20, 20, 91),
+                                             (2000, 128, 5, 8, 11), (1500, 256, 3, 6, 12),
+                                             (800, 128, 40, 200, 13), (2500, 256, 8, 12, 14)])
+def test_certificate_matches_its_definition_and_is_sound(V, K, k, cap, seed):
+    trits, rs, h = synth.lmhead(V, K, seed)
+    idx, sc, n, capped, cert = oracle.lmhead_two_stage(trits, rs, h, k, cap, certificate=True)
+    nn, ncapped, umax = numpy_certificate(trits, rs, h, k, cap)
+    assert (n, capped) == (nn, ncapped)
+    assert cert == (1 if not capped else int(umax < sc[-1]))
+    bi, bsc = oracle.lmhead_brute(trits, rs, h, k)
+    if cert:   # soundness: a certified result is the exact top-k
+        assert (idx == bi).all() and (sc == bsc).all()
+
+
+def test_certificate_zero_where_the_cap_drops_a_top_row():
+    """The (4000, 256, k = cap = 20) case has a true top-20 row outside the
+    capped set: the result differs from brute force and is not certified."""
+    trits, rs, h = synth.lmhead(4000, 256, 91)
+    idx, sc, n, capped, cert = oracle.lmhead_two_stage(trits, rs, h, 20, 20, certificate=True)
+    bi, bsc = oracle.lmhead_brute(trits, rs, h, 20)
+    assert capped == 1 and not ((idx == bi).all() and (sc == bsc).all())
+    assert cert == 0
+
+
+def test_certificate_capped_and_certified():
+    """Planted peaks far above the rest, cap below the number of candidates:
+    the cap engages and the dropped candidates' upper bounds stay below the
+    k-th score, so the capped result is certified (and equals brute force)."""
+    trits, rs, h, _ = synth.lmhead_planted(2000, 512, 1, n_peaks=64)
+    idx, sc, n, capped, cert = oracle.lmhead_two_stage(trits, rs, h, 3, 6, certificate=True)
+    bi, bsc = oracle.lmhead_brute(trits, rs, h, 3)
+    assert capped == 1 and n == 7 and cert == 1
+    assert (idx == bi).all() and (sc == bsc).all()
