@@ -190,12 +190,15 @@ __global__ __launch_bounds__(1024) void lns8_kernel(
         // never land on stale partials
         for (int idx = threadIdx.x; idx < 512; idx += blockDim.x) {
             const int p = idx >> 6, j = idx & 63;
+            int *src = partial + ((size_t)tile * 64 + j) * 8 + p;
+            const size_t stride = padded_rows * 8;
             int t = 0;
-            for (int sp = 0; sp < nsplit; ++sp) {
-                int *src = partial + ((size_t)sp * padded_rows + tile * 64 + j) * 8 + p;
-                t += __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                *src = 0;
-            }
+            // every load in flight at once, then the clearing stores (a load
+            // and a store to one address in turn would wait for each load)
+            for (int sp = 0; sp < nsplit; ++sp)
+                t += __hip_atomic_load(src + sp * stride, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            for (int sp = 0; sp < nsplit; ++sp) src[sp * stride] = 0;
             red[0][p][j] = t;   // only this thread reads or writes pair (p, j) here
         }
         if (threadIdx.x == 0)
