@@ -686,7 +686,7 @@ def run_extras(torch, bs, synth, dev, H):
     pool03 = [d03] + [d03.clone() for _ in range(3)]       # > 1 GiB of planes 0-3
     idx = torch.empty(40, dtype=torch.int32, device=dev)
     sc = torch.empty(40, dtype=torch.int64, device=dev)
-    info = torch.empty(2, dtype=torch.int32, device=dev)
+    info = torch.empty(3, dtype=torch.int32, device=dev)
     wsl = torch.zeros(bs.lib().bs_lmhead_workspace_bytes(V, K, 40, 200), dtype=torch.uint8,
                       device=dev)
     us = H.per_launch(lambda i: bs.lmhead_planes_topk(
@@ -698,7 +698,8 @@ def run_extras(torch, bs, synth, dev, H):
         "us_per_call": round(us, 3), "stage1_bytes": stage1_bytes,
         "GBps_stage1_bytes": round(stage1_bytes / us / 1e3, 1),
         "frac_hbm_peak": round(stage1_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
-        "n_candidates": int(info[0].item()), "capped": int(info[1].item())}
+        "n_candidates": int(info[0].item()), "capped": int(info[1].item()),
+        "certified_exact": int(info[2].item())}
     log("lm_head: %.2f us" % us)
     del pool03
     torch.cuda.empty_cache()

@@ -367,7 +367,8 @@ def flns_phase_gemv(planes, x_lns8, rows: int, k: int, frac_bits: int, table, sc
 def lmhead_planes_topk(planes03, planes47, row_scale, h, vocab: int, dim: int,
                        top_k: int = 40, max_candidates: int = 200, top_idx=None,
                        top_score=None, info=None, workspace=None, stream=None):
-    """(top_idx int32[top_k], top_score int64[top_k], info int32[2])."""
+    """(top_idx int32[top_k], top_score int64[top_k], info int32[3]: |C|,
+    capped, certified exact)."""
     torch = _torch()
     dev = h.device
     if top_idx is None:
@@ -375,7 +376,7 @@ def lmhead_planes_topk(planes03, planes47, row_scale, h, vocab: int, dim: int,
     if top_score is None:
         top_score = torch.empty(top_k, dtype=torch.int64, device=dev)
     if info is None:
-        info = torch.empty(2, dtype=torch.int32, device=dev)
+        info = torch.empty(3, dtype=torch.int32, device=dev)
     need = lib().bs_lmhead_workspace_bytes(vocab, dim, top_k, max_candidates)
     if need == 0:
         raise BsError(BS_E_RANGE, "bs_lmhead_workspace_bytes")
@@ -385,7 +386,7 @@ def lmhead_planes_topk(planes03, planes47, row_scale, h, vocab: int, dim: int,
     _need(h, dim, "h")
     _need(top_idx, top_k, "top_idx")
     _need(top_score, top_k, "top_score")
-    _need(info, 2, "info")
+    _need(info, 3, "info")
     wp, wn = _ws("lmhead_planes_topk", workspace, need, dev)
     rc = lib().bs_lmhead_planes_topk(
         _dptr(planes03, torch.uint8, "planes03"), _dptr(planes47, torch.uint8, "planes47"),
@@ -414,14 +415,14 @@ def lmhead_planes_topk_noalloc(planes03, planes47, row_scale, h, vocab: int, dim
     if top_score is None:
         top_score = torch.empty(top_k, dtype=torch.int64, device=dev)
     if info is None:
-        info = torch.empty(2, dtype=torch.int32, device=dev)
+        info = torch.empty(3, dtype=torch.int32, device=dev)
     _need(planes03, lib().bs_planes03_bytes(vocab, dim), "planes03")
     _need(planes47, lib().bs_planes47_bytes(vocab, dim), "planes47")
     _need(row_scale, vocab, "row_scale")
     _need(h, dim, "h")
     _need(top_idx, top_k, "top_idx")
     _need(top_score, top_k, "top_score")
-    _need(info, 2, "info")
+    _need(info, 3, "info")
     rc = lib().bs_lmhead_planes_topk_noalloc(
         _dptr(planes03, torch.uint8, "planes03"), _dptr(planes47, torch.uint8, "planes47"),
         _dptr(row_scale, torch.int32, "row_scale"), _dptr(h, torch.int8, "h"), vocab, dim,

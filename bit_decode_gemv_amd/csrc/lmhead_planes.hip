@@ -38,7 +38,11 @@
 //              prefixes are read), then the top_k of the kept rows by
 //              (S' desc, row asc): first among the rows a histogram bound on
 //              S' names, which is the answer when the cap keeps them all,
-//              else by ranking every gathered row in both orders.
+//              else by ranking every gathered row in both orders.  Last,
+//              the exactness certificate: the largest upper bound U among
+//              the dropped candidates (the filter's per-region maxima of the
+//              rows it did not rescore, and the stored rows past the cap)
+//              against the k-th output score.
 #include <mutex>
 
 #include "kcommon.h"
@@ -125,9 +129,12 @@ struct LmhWs {
     int *cand;              // [nwf * 256] candidate rows, per-workgroup regions
     long long *cand_s1;     // [nwf * 256] their S1'
     long long *cand_s;      // [nwf * 256] their S'
+    long long *cand_u;      // [nwf * 256] their upper bound U = S1' + B'
+    long long *region_umax; // [nwf] largest U of the workgroup's candidates not rescored
     int *cc;                // [V] compacted candidates (more regions than one pass scans)
     long long *cc_s1;       // [V]
     long long *cc_s;        // [V]
+    long long *cc_u;        // [V]
 };
 
 // ---------------------------------------------------------------- stage 1
@@ -709,6 +716,7 @@ __global__ __launch_bounds__(kFilterRows) void lmh_filter(const uint8_t *__restr
     __shared__ long long cs1[kFilterRows];
     __shared__ int crow[kFilterRows];
     __shared__ int wcount[4];
+    __shared__ unsigned long long wumax[kFilterRows / 64];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * kFilterRows + (int)threadIdx.x;
@@ -717,16 +725,25 @@ __global__ __launch_bounds__(kFilterRows) void lmh_filter(const uint8_t *__restr
     for (int t = threadIdx.x; t < groups * 16; t += kFilterRows) hs2[t] = h2[t];
     const long long lk = ws.scalars[0], habs = ws.scalars[1], t1 = ws.scalars[2];
     bool cand = false;
-    long long s1 = 0;
+    long long s1 = 0, u = 0;
     int e1 = 0, rs = 0;
     if (row < vocab) {
         rs = row_scale[row];
         e1 = ws.e1[row];
         s1 = 81LL * (long long)rs * (long long)e1;
         const long long ars = rs < 0 ? -(long long)rs : (long long)rs;
-        cand = s1 + 40LL * ars * habs >= lk;
+        u = s1 + 40LL * ars * habs;
+        cand = u >= lk;
     }
     const bool keep = cand && s1 >= t1;
+    // the largest U among this wavefront's candidates that are not rescored
+    // (for the exactness certificate)
+    unsigned long long wu = cand && !keep ? okey(u) : 0ull;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long o = shfl_xor_u64(wu, off);
+        wu = o > wu ? o : wu;
+    }
     // this wavefront's rows to rescore, and the first pass of their planes
     // 4-7 loads, issued before the workgroup-wide steps below so that their
     // latency overlaps them
@@ -755,11 +772,15 @@ __global__ __launch_bounds__(kFilterRows) void lmh_filter(const uint8_t *__restr
             run0[u] = p;
         }
     }
+    if (lane == 0) wumax[wave] = wu;
     const int ncand = __syncthreads_count(cand);
     const int nct = __syncthreads_count(keep);
     if (threadIdx.x == 0) {
         ws.region_count[blockIdx.x] = ncand;
         ws.region_kept[blockIdx.x] = nct;
+        unsigned long long m = wumax[0];
+        for (int w = 1; w < kFilterRows / 64; ++w) m = wumax[w] > m ? wumax[w] : m;
+        ws.region_umax[blockIdx.x] = m ? (long long)(m ^ 0x8000000000000000ull) : kNoRow;
     }
     if (nct == 0) return;   // whole workgroup (no loads were issued)
     if (lane == 0) wcount[wave] = nc;
@@ -816,6 +837,7 @@ __global__ __launch_bounds__(kFilterRows) void lmh_filter(const uint8_t *__restr
         ws.cand[slot] = row;
         ws.cand_s1[slot] = s1;
         ws.cand_s[slot] = (long long)rs * (81LL * (long long)e1 + (long long)e2l[wave][pos]);
+        ws.cand_u[slot] = u;
     }
 }
 
@@ -829,6 +851,7 @@ struct CandSrc {
     const int *rows;
     const long long *s1;
     const long long *s;
+    const long long *u;
 };
 
 __device__ __forceinline__ size_t cand_slot(const CandSrc &c, int i) {
@@ -845,7 +868,7 @@ template <bool REG>
 __device__ __forceinline__ void finish_body(int n, int top_k, int cap, int32_t *__restrict__ top_idx,
                                             int64_t *__restrict__ top_score, const CandSrc &src,
                                             SelShared &sh, long long *tk, int *ti,
-                                            unsigned int *nkept) {
+                                            unsigned int *nkept, long long *sk) {
     constexpr int KPT = kFinKpt;
     long long r_s1[KPT], r_s[KPT];
     int r_id[KPT];
@@ -950,6 +973,7 @@ __device__ __forceinline__ void finish_body(int n, int top_k, int cap, int32_t *
     for (int i = threadIdx.x; i < top_k; i += blockDim.x) {
         top_idx[i] = ti[i];
         top_score[i] = tk[i];
+        if (i == top_k - 1) *sk = tk[i];
     }
 }
 
@@ -957,11 +981,13 @@ __device__ __forceinline__ void finish_body(int n, int top_k, int cap, int32_t *
 // among them, those below top_k written at their rank.  rk: int[blockDim].
 __device__ __forceinline__ void output_by_rank(int m, int top_k, const long long *tk,
                                                const int *ti, int32_t *__restrict__ top_idx,
-                                               int64_t *__restrict__ top_score, int *rk) {
+                                               int64_t *__restrict__ top_score, int *rk,
+                                               long long *sk) {
     auto put = [&](int e, int r) {
         if (r < top_k) {
             top_idx[r] = ti[e];
             top_score[r] = tk[e];
+            if (r == top_k - 1) *sk = tk[e];
         }
     };
     if (m <= (int)blockDim.x) {
@@ -983,8 +1009,11 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     __shared__ long long tk[kMaxCap];
     __shared__ int ti[kMaxCap];
     __shared__ int ro[kBlockThreads];
-    __shared__ long long l1s1[kFinList], l1s[kFinList];
+    __shared__ long long l1s1[kFinList], l1s[kFinList], l1u[kFinList];
     __shared__ int l1id[kFinList];
+    __shared__ int list_all;                   // the l1 list holds every stored candidate
+    __shared__ unsigned long long cert_base1;  // least S1' key of the l1 list
+    __shared__ int cert_packed1;               // (S1', row) fits one 64-bit key
     __shared__ unsigned long long pk1[kFinList], pk2[kFinList];
     __shared__ unsigned long long red4[kBlockThreads / 64][4], fin4[4];
     __shared__ int l2[kFinList];
@@ -993,9 +1022,16 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     __shared__ int wpre[kBlockThreads / 64 + 1];
     __shared__ unsigned int nkept, nl1;
     __shared__ int ncand_sh;
+    __shared__ long long sk_sh;               // the k-th output score
     const int t = (int)threadIdx.x;
     const int wave = t >> 6, lane = t & 63;
     const int nwaves = kBlockThreads / 64;
+    int n = 0;                                // rescored (stored) candidates
+    CandSrc src;
+    // the filter's per-region maxima of U, for the certificate at the end
+    const long long umax0 = t < nwf ? ws.region_umax[t] : kNoRow;
+
+    auto body = [&]() {
 
     // region t's counts, then its first kFinSpec stored entries (its head,
     // the largest S1', first), loaded while the prefix sums below run, so the
@@ -1003,21 +1039,22 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     // no more; entries past a region's count are not loaded
     const int kept0 = t < nwf ? ws.region_kept[t] : 0;
     const int count0 = t < nwf ? ws.region_count[t] : 0;
-    long long sp_s1[kFinSpec], sp_s[kFinSpec];
+    long long sp_s1[kFinSpec], sp_s[kFinSpec], sp_u[kFinSpec];
     int sp_id[kFinSpec];
 #pragma unroll
     for (int u = 0; u < kFinSpec; ++u) {
         const size_t sl = (size_t)t * kFilterRows + u;
         sp_s1[u] = u < kept0 ? ws.cand_s1[sl] : 0;
         sp_s[u] = u < kept0 ? ws.cand_s[sl] : 0;
+        sp_u[u] = u < kept0 ? ws.cand_u[sl] : 0;
         sp_id[u] = u < kept0 ? ws.cand[sl] : 0;
     }
+    if (t == 0) list_all = 0;
     const long long head_pre = sp_s1[0];
     // exclusive prefix sums of the regions' stored counts, 1024 regions at a
     // time, and the number of candidates (wavefront 0 scans the wavefronts'
     // totals once for all)
     if (t == 0) ncand_sh = 0;
-    int n = 0;
     for (int r0 = 0; r0 < nwf; r0 += kBlockThreads) {
         const int r = r0 + t;
         const int c = r0 == 0 ? kept0 : (r < nwf ? ws.region_kept[r] : 0);
@@ -1062,18 +1099,19 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
                     ws.cc[dst + l] = ws.cand[from + l];
                     ws.cc_s1[dst + l] = ws.cand_s1[from + l];
                     ws.cc_s[dst + l] = ws.cand_s[from + l];
+                    ws.cc_u[dst + l] = ws.cand_u[from + l];
                 }
             }
         }
         __syncthreads();   // copies visible to the workgroup, ro and wtot reusable
     }
     const bool regions = nwf <= kBlockThreads;
-    CandSrc src;
     src.ro = regions ? ro : nullptr;
     src.nreg = regions ? nwf : 0;
     src.rows = regions ? ws.cand : ws.cc;
     src.s1 = regions ? ws.cand_s1 : ws.cc_s1;
     src.s = regions ? ws.cand_s : ws.cc_s;
+    src.u = regions ? ws.cand_u : ws.cc_u;
     // n rows were rescored: every candidate, or (T1 above kNoRow) those with
     // S1' >= T1, at least cap rows among which the capped set lies
     n = min(n, vocab);
@@ -1091,7 +1129,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
             ti[i] = src.rows[sl];
         }
         __syncthreads();
-        output_by_rank(n, top_k, tk, ti, top_idx, top_score, ro);   // ro no longer needed
+        output_by_rank(n, top_k, tk, ti, top_idx, top_score, ro, &sk_sh);   // ro no longer needed
         return;
     }
     if (regions) {
@@ -1121,6 +1159,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
                     if (slot < (unsigned)kFinList) {
                         l1s1[slot] = sp_s1[u];
                         l1s[slot] = sp_s[u];
+                        l1u[slot] = sp_u[u];
                         l1id[slot] = sp_id[u];
                     }
                 } else {
@@ -1138,6 +1177,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
                         if (slot < (unsigned)kFinList) {
                             l1s1[slot] = v[u];
                             l1s[slot] = ws.cand_s[base + e0 + u];
+                            l1u[slot] = ws.cand_u[base + e0 + u];
                             l1id[slot] = ws.cand[base + e0 + u];
                         }
                     } else {
@@ -1148,6 +1188,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
         }
         __syncthreads();
         const int nl = (int)nl1;
+        if (t == 0) list_all = nl == n && nl <= kFinList;
         if (nl <= kFinList) {
             // the ranks by (S1' desc, row asc) and by (S' desc, row asc) in
             // one pass: the cap keeps the entries whose first rank is below
@@ -1178,6 +1219,10 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
             const unsigned long long base1 = ~mx[1], base2 = ~mx[3];
             const bool packed = vocab <= (1 << 17) && mx[0] - base1 < (1ull << 47) &&
                                 mx[2] - base2 < (1ull << 47);
+            if (t == 0) {
+                cert_base1 = base1;
+                cert_packed1 = vocab <= (1 << 17) && mx[0] - base1 < (1ull << 47);
+            }
             // The top_k by S' first: T2, the lower edge of the histogram bin
             // (256 bins over the gathered rows' S' span) in which the count
             // from the top reaches top_k; the m rows >= T2 are ranked among
@@ -1238,6 +1283,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
                             const int q = l2[t];
                             top_idx[rb] = l1id[q];
                             top_score[rb] = l1s[q];
+                            if (rb == top_k - 1) sk_sh = l1s[q];
                         }
                         return;
                     }
@@ -1277,6 +1323,7 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
                 if (r < top_k) {
                     top_idx[r] = my_id;
                     top_score[r] = me;
+                    if (r == top_k - 1) sk_sh = me;
                 }
             }
             return;
@@ -1284,9 +1331,122 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
     }
     // fallback: block-wide radix selections over every candidate
     if (n <= kFinKpt * kBlockThreads)
-        finish_body<true>(n, top_k, cap, top_idx, top_score, src, sh, tk, ti, &nkept);
+        finish_body<true>(n, top_k, cap, top_idx, top_score, src, sh, tk, ti, &nkept, &sk_sh);
     else
-        finish_body<false>(n, top_k, cap, top_idx, top_score, src, sh, tk, ti, &nkept);
+        finish_body<false>(n, top_k, cap, top_idx, top_score, src, sh, tk, ti, &nkept, &sk_sh);
+    };   // body
+    body();
+
+    // Exactness certificate (info[2]): 1 when nothing was dropped, or when
+    // the largest upper bound U among the candidates the cap dropped lies
+    // strictly below the k-th output score S'_k; a dropped row's S' <= U,
+    // so it can neither pass nor tie the output.  The dropped rows: every
+    // candidate that was not rescored (the filter's per-region maxima) and
+    // the rescored rows past the top `cap` by (S1' desc, row asc).
+    __syncthreads();
+    const int ncand = min(ncand_sh, vocab);
+    if (ncand <= cap) {
+        if (t == 0) info[2] = 1;
+        return;
+    }
+    unsigned long long m = umax0 != kNoRow ? okey(umax0) : 0ull;
+    for (int r = t + kBlockThreads; r < nwf; r += kBlockThreads) {
+        const long long v = ws.region_umax[r];
+        if (v != kNoRow) m = okey(v) > m ? okey(v) : m;
+    }
+    if (n > cap && list_all) {
+        // every stored row is in the LDS list (n <= 512): a row is dropped
+        // when at least cap rows precede it by (S1' desc, row asc); its rank
+        // counts are shared out over P = blockDim / npad parts of the list
+        const int npad = (n + 63) & ~63;
+        const int P = kBlockThreads / npad;
+        const int e = t % npad, part = t / npad;
+        const int c1 = (n + P - 1) / P;
+        const int j0 = part * c1, j1 = min(n, (part + 1) * c1);
+        int c = 0;
+        if (cert_packed1) {
+            // one 64-bit key per row: ((S1' key - least) << 17) | (2^17 - 1 - row)
+            // orders by (S1' desc, row asc); pk1 is free once the output is written
+            if (t < n)
+                pk1[t] = ((okey(l1s1[t]) - cert_base1) << 17) |
+                         (unsigned long long)((1 << 17) - 1 - l1id[t]);
+            __syncthreads();
+            if (part < P && e < n) {
+                const unsigned long long q = pk1[e];
+#pragma unroll 8
+                for (int j = j0; j < j1; ++j) c += pk1[j] > q ? 1 : 0;
+            }
+        } else if (part < P && e < n) {
+            const long long q1 = l1s1[e];
+            const int qid = l1id[e];
+#pragma unroll 8
+            for (int j = j0; j < j1; ++j) c += better(l1s1[j], l1id[j], q1, qid) ? 1 : 0;
+        }
+        ti[t] = c;   // ti is free once the output is written
+        __syncthreads();
+        if (t < n) {
+            int r1 = 0;
+            for (int q = 0; q < P; ++q) r1 += ti[q * npad + t];
+            if (r1 >= cap) m = okey(l1u[t]) > m ? okey(l1u[t]) : m;
+        }
+    } else if (n > cap) {
+        if (src.ro) {
+            // the output phase reused ro: the regions' exclusive prefix sums
+            const int c = t < nwf ? ws.region_kept[t] : 0;
+            int incl = c;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int o = __shfl_up(incl, off);
+                if (lane >= off) incl += o;
+            }
+            if (lane == 63) wtot[wave] = incl;
+            __syncthreads();
+            int pre = 0;
+            for (int w = 0; w < wave; ++w) pre += wtot[w];
+            ro[t] = pre + incl - c;
+            __syncthreads();
+        }
+        // the cap over the stored rows by (S1' desc, row asc), as the finish
+        // fallback selects it: tau the cap-th largest S1' key, theta the tie
+        // bound among rows at tau
+        auto key1 = [&](int i, int) { return okey(src.s1[cand_slot(src, i)]); };
+        auto all = [](int, int) { return true; };
+        const unsigned long long tau =
+            radix_select_desc<1>(n, (unsigned long long)cap, key1, all, sh);
+        unsigned gt, eq;
+        block_count2<1>(
+            n,
+            [&](int i, int j) {
+                const unsigned long long k = key1(i, j);
+                return k > tau ? 1 : (k == tau ? 2 : 0);
+            },
+            sh, gt, eq);
+        const unsigned need = (unsigned)cap - gt;   // rows tying at tau that are kept
+        unsigned long long theta = 0;
+        if (need < eq)
+            theta = radix_select_desc<1>(
+                n, (unsigned long long)need,
+                [&](int i, int) { return tie_key(src.rows[cand_slot(src, i)]); },
+                [&](int i, int j) { return key1(i, j) == tau; }, sh);
+        for (int i = t; i < n; i += kBlockThreads) {
+            const size_t sl = cand_slot(src, i);
+            const unsigned long long k = okey(src.s1[sl]);
+            if (k < tau || (k == tau && tie_key(src.rows[sl]) < theta))
+                m = okey(src.u[sl]) > m ? okey(src.u[sl]) : m;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long o = shfl_xor_u64(m, off);
+        m = o > m ? o : m;
+    }
+    if (lane == 0) red4[wave][0] = m;
+    __syncthreads();
+    if (t == 0) {
+        unsigned long long mm = 0;
+        for (int w = 0; w < nwaves; ++w) mm = red4[w][0] > mm ? red4[w][0] : mm;
+        info[2] = (mm == 0 || okey(sk_sh) > mm) ? 1 : 0;
+    }
 }
 
 }  // namespace
@@ -1296,7 +1456,7 @@ using namespace bs;
 
 struct LmhLayout {
     size_t scalars, e1, lower, tile_max, wg_max, tile_max_s1, region_count,
-        region_kept, cand, cand_s1, cand_s, cc, cc_s1, cc_s, total;
+        region_kept, region_umax, cand, cand_s1, cand_s, cand_u, cc, cc_s1, cc_s, cc_u, total;
     int tiles, nwg, nwf;
 };
 
@@ -1320,12 +1480,15 @@ static constexpr LmhLayout lmh_layout(int64_t vocab) {
     L.tile_max_s1 = off;  off += align_ws((size_t)L.tiles * 8);
     L.region_count = off; off += align_ws((size_t)L.nwf * 4);
     L.region_kept = off;  off += align_ws((size_t)L.nwf * 4);
+    L.region_umax = off;  off += align_ws((size_t)L.nwf * 8);
     L.cand = off;         off += align_ws(slots * 4);
     L.cand_s1 = off;      off += align_ws(slots * 8);
     L.cand_s = off;       off += align_ws(slots * 8);
+    L.cand_u = off;       off += align_ws(slots * 8);
     L.cc = off;           off += align_ws((size_t)vocab * 4);
     L.cc_s1 = off;        off += align_ws((size_t)vocab * 8);
     L.cc_s = off;         off += align_ws((size_t)vocab * 8);
+    L.cc_u = off;         off += align_ws((size_t)vocab * 8);
     L.total = off;
     return L;
 }
@@ -1378,12 +1541,15 @@ static int32_t lmh_launch(const uint8_t *planes03, const uint8_t *planes47,
     ws.tile_max_s1 = reinterpret_cast<long long *>(base + L.tile_max_s1);
     ws.region_count = reinterpret_cast<int *>(base + L.region_count);
     ws.region_kept = reinterpret_cast<int *>(base + L.region_kept);
+    ws.region_umax = reinterpret_cast<long long *>(base + L.region_umax);
     ws.cand = reinterpret_cast<int *>(base + L.cand);
     ws.cand_s1 = reinterpret_cast<long long *>(base + L.cand_s1);
     ws.cand_s = reinterpret_cast<long long *>(base + L.cand_s);
+    ws.cand_u = reinterpret_cast<long long *>(base + L.cand_u);
     ws.cc = reinterpret_cast<int *>(base + L.cc);
     ws.cc_s1 = reinterpret_cast<long long *>(base + L.cc_s1);
     ws.cc_s = reinterpret_cast<long long *>(base + L.cc_s);
+    ws.cc_u = reinterpret_cast<long long *>(base + L.cc_u);
 
     const int groups = (int)(dim / 128);
     hipLaunchKernelGGL(lmh_stage1, dim3(L.nwg), dim3(kStage1Threads), 0, st, planes03, row_scale,

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define BS_ABI_VERSION 1
+#define BS_ABI_VERSION 2   /* 2: lm_head info carries the exactness certificate */
 
 enum {
     BS_OK = 0,
@@ -320,7 +320,12 @@ int32_t bs_planes_pack(const int8_t *trits, int64_t vocab, int64_t dim,
  *   1 <= top_k <= max_candidates, top_k <= vocab, max_candidates <= 4096
  *   top_idx int32[top_k], top_score int64[top_k]: device, overwritten
  *     (4- and 8-byte aligned)
- *   info    device int32[2]: info[0] = |C|, info[1] = 1 if the cap engaged
+ *   info    device int32[3]: info[0] = |C|, info[1] = 1 if the cap engaged,
+ *           info[2] = 1 if the result is certified to be the exact top_k:
+ *           nothing was dropped, or every candidate the cap dropped has an
+ *           upper bound U strictly below the top_k-th output score (a
+ *           dropped row's S' <= U, so it can neither pass nor tie the
+ *           output); 0 means not certified, not wrong
  *   workspace  device scratch of bs_lmhead_workspace_bytes(...) bytes,
  *     256-byte aligned, caller-owned.  Every byte of it is written before it
  *     is read, so it needs no initialisation and one workspace serves calls
@@ -343,7 +348,7 @@ int32_t bs_lmhead_planes_topk(const uint8_t *planes03, const uint8_t *planes47,
  * loops, harnesses that forbid hipMalloc): the same computation, arguments,
  * outputs and errors, without the workspace arguments.  Its scratch is a
  * file-scope device array of the library, sized for
- * vocab <= BS_LMHEAD_NOALLOC_MAX_VOCAB (13,713,664 bytes; each GPU the library
+ * vocab <= BS_LMHEAD_NOALLOC_MAX_VOCAB (17,916,160 bytes; each GPU the library
  * runs on holds its own copy until the process ends).  The call allocates
  * nothing: no hipMalloc, hipFree or allocating library routine.  Its first
  * call on a device looks up that device's copy of the array

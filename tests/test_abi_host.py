@@ -25,7 +25,7 @@ def test_library_exports_every_header_symbol():
     assert len(names) >= 15
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.bs_abi_version() == 1
+    assert lib.bs_abi_version() == 2
 
 
 def test_probe_library_exports_its_header():

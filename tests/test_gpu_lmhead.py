@@ -32,8 +32,9 @@ def run(trits, rs, h, top_k, cap, packed=None):
 
 def check(trits, rs, h, top_k, cap, packed=None):
     idx, sc, info = run(trits, rs, h, top_k, cap, packed)
-    widx, wsc, n, capped = oracle.lmhead_two_stage(trits, rs, h, top_k, cap)
-    assert info[0] == n and info[1] == capped, (info, n, capped)
+    widx, wsc, n, capped, cert = oracle.lmhead_two_stage(trits, rs, h, top_k, cap,
+                                                         certificate=True)
+    assert list(info) == [n, capped, cert], (info, n, capped, cert)
     assert (idx == widx).all(), (idx[:10], widx[:10])
     assert (sc == wsc).all()
     return idx, sc, n, capped
@@ -103,12 +104,31 @@ def test_full_vocab_config():
     assert lk_gpu == int(np.sort(s1 - bnd)[::-1][39])
     assert t1 != _NO_T1 and t1 >= lk_gpu and int((s1 >= t1).sum()) >= 200
     assert t1 <= int(np.sort(s1)[::-1][199])
-    idx, sc, n, capped = check(trits, rs, h, 40, 200, packed=(p03, p47))
-    bi, bsc = oracle.lmhead_brute(trits, rs, h, 40)
-    same = bool((idx == bi).all() and (sc == bsc).all())
-    print("full vocab: |C| = %d, capped = %d, equals brute force: %s" % (n, capped, same))
-    if not capped:
-        assert same
+    check(trits, rs, h, 40, 200, packed=(p03, p47))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("seed", range(5))
+def test_full_vocab_seeds_against_recorded_brute_force(seed):
+    """The full-vocabulary workload, seeds 0..4, against the oracle's results
+    recorded in tests/golden/lmhead_c5_record.json (written by
+    make_lmhead_c5_record.py from the oracle alone): the GPU equals the
+    two-stage decode bit for bit (indices, scores, |C|, capped, certificate),
+    and where the record shows the two-stage result equal to the brute-force
+    exact top-k, the GPU result is asserted equal to the brute force too."""
+    import json
+    import os
+    rec = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                      "lmhead_c5_record.json")))["seeds"][str(seed)]
+    trits, rs, h = synth.lmhead(*synth.LMHEAD_SHAPE, seed=seed)
+    idx, sc, info = run(trits, rs, h, 40, 200)
+    del trits
+    assert list(info) == [rec["n_candidates"], rec["capped"], rec["certified"]]
+    assert idx.tolist() == rec["two_stage_idx"] and sc.tolist() == rec["two_stage_score"]
+    assert rec["equals_brute_force"] == (rec["two_stage_idx"] == rec["brute_idx"] and
+                                         rec["two_stage_score"] == rec["brute_score"])
+    if rec["equals_brute_force"]:
+        assert idx.tolist() == rec["brute_idx"] and sc.tolist() == rec["brute_score"]
 
 
 def test_workspace_shared_across_shapes():
@@ -130,9 +150,10 @@ def test_workspace_shared_across_shapes():
                                               to_dev(rs, dev), to_dev(h, dev), V, K, k, cap,
                                               workspace=ws)
         torch.cuda.synchronize()
-        widx, wsc, n, capped = oracle.lmhead_two_stage(trits, rs, h, k, cap)
+        widx, wsc, n, capped, cert = oracle.lmhead_two_stage(trits, rs, h, k, cap,
+                                                             certificate=True)
         assert (idx.cpu().numpy() == widx).all() and (sc.cpu().numpy() == wsc).all()
-        assert list(info.cpu().numpy()) == [n, capped]
+        assert list(info.cpu().numpy()) == [n, capped, cert]
 
 
 @pytest.mark.parametrize("V,cap", [(4096, 4096), (4097, 4096), (5000, 200)])
@@ -239,8 +260,8 @@ def test_rescore_bound_branches(case):
         assert t1 >= lk
         assert int((s1 >= t1).sum()) >= cap
         assert t1 <= int(np.sort(s1)[::-1][cap - 1])
-    widx, wsc, n, capped = oracle.lmhead_two_stage(trits, rs, h, k, cap)
-    assert list(info.cpu().numpy()) == [n, capped]
+    widx, wsc, n, capped, cert = oracle.lmhead_two_stage(trits, rs, h, k, cap, certificate=True)
+    assert list(info.cpu().numpy()) == [n, capped, cert]
     assert (idx.cpu().numpy() == widx).all()
     assert (sc.cpu().numpy() == wsc).all()
 

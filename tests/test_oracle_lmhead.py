@@ -265,3 +265,24 @@ def test_certificate_capped_and_certified():
     bi, bsc = oracle.lmhead_brute(trits, rs, h, 3)
     assert capped == 1 and n == 7 and cert == 1
     assert (idx == bi).all() and (sc == bsc).all()
+
+
+def test_recorded_full_vocab_results_are_consistent():
+    """tests/golden/lmhead_c5_record.json (written by make_lmhead_c5_record.py
+    from the oracle alone): five seeds of the full-vocabulary workload, each
+    with the two-stage result, its info, the brute-force top-k and the
+    equality flag, which must agree with the recorded arrays; a certified
+    result must equal the brute force."""
+    import json
+    rec = json.load(open(os.path.join(GOLDEN, "lmhead_c5_record.json")))
+    assert sorted(rec["seeds"]) == ["0", "1", "2", "3", "4"]
+    for seed, r in rec["seeds"].items():
+        assert len(r["two_stage_idx"]) == len(r["brute_idx"]) == 40
+        same = r["two_stage_idx"] == r["brute_idx"] and r["two_stage_score"] == r["brute_score"]
+        assert r["equals_brute_force"] == same, seed
+        assert r["capped"] == int(r["n_candidates"] > 200)
+        if r["certified"]:
+            assert same, seed
+        # brute force: scores descending, ties by lower index
+        s, i = r["brute_score"], r["brute_idx"]
+        assert all((s[j], -i[j]) > (s[j + 1], -i[j + 1]) for j in range(39))

@@ -26,7 +26,7 @@ def _pair(trits, rs, h, k, cap, packed=None):
     # the no-alloc call writes into outputs poisoned beforehand
     i1 = torch.full((k,), -7, dtype=torch.int32, device=dev)
     s1 = torch.full((k,), -7, dtype=torch.int64, device=dev)
-    f1 = torch.full((2,), -7, dtype=torch.int32, device=dev)
+    f1 = torch.full((3,), -7, dtype=torch.int32, device=dev)
     bs.lmhead_planes_topk_noalloc(*a, V, K, k, cap, top_idx=i1, top_score=s1, info=f1)
     torch.cuda.synchronize()
     got = (i1.cpu().numpy(), s1.cpu().numpy(), f1.cpu().numpy())
@@ -46,12 +46,12 @@ def test_noalloc_matches_workspace_entry_point_shrinking_calls():
     del trits
     trits, rs, h = synth.lmhead(20000, 512, 12)
     idx, sc, info = _pair(trits, rs, h, 40, 200)
-    widx, wsc, n, capped = oracle.lmhead_two_stage(trits, rs, h, 40, 200)
-    assert (idx == widx).all() and (sc == wsc).all() and list(info) == [n, capped]
+    widx, wsc, n, capped, cert = oracle.lmhead_two_stage(trits, rs, h, 40, 200, certificate=True)
+    assert (idx == widx).all() and (sc == wsc).all() and list(info) == [n, capped, cert]
     trits, rs, h = synth.lmhead(3000, 256, 13)
     idx, sc, info = _pair(trits, rs, h, 10, 10)
-    widx, wsc, n, capped = oracle.lmhead_two_stage(trits, rs, h, 10, 10)
-    assert (idx == widx).all() and (sc == wsc).all() and list(info) == [n, capped]
+    widx, wsc, n, capped, cert = oracle.lmhead_two_stage(trits, rs, h, 10, 10, certificate=True)
+    assert (idx == widx).all() and (sc == wsc).all() and list(info) == [n, capped, cert]
 
 
 @pytest.mark.gpu
@@ -60,7 +60,7 @@ def test_noalloc_planted_exact_branch_twice():
     trits, rs, h, _ = synth.lmhead_planted(4000, 512, 1, n_peaks=64)
     for _ in range(2):
         idx, sc, info = _pair(trits, rs, h, 40, 200)
-        assert info[1] == 0
+        assert info[1] == 0 and info[2] == 1
         bi, bsc = oracle.lmhead_brute(trits, rs, h, 40)
         assert (idx == bi).all() and (sc == bsc).all()
 
