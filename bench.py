@@ -299,11 +299,11 @@ def _oracle_per_config(cores):
 
 # ------------------------------------------------------ records under profiles/
 
-def _source_digest():
-    """Digest of the GEMV kernel's source: its file and the headers it
-    includes (shared device helpers, status codes, the ABI header)."""
+def _source_digest(kernel_file="ternary_gemv.hip"):
+    """Digest of a kernel's source: its file and the headers it includes
+    (shared device helpers, status codes, the ABI header)."""
     h = hashlib.sha256()
-    for rel in (("bit_decode_gemv_amd", "csrc", "ternary_gemv.hip"),
+    for rel in (("bit_decode_gemv_amd", "csrc", kernel_file),
                 ("bit_decode_gemv_amd", "csrc", "kcommon.h"),
                 ("bit_decode_gemv_amd", "csrc", "bs_internal.h"),
                 ("include", "bs.h")):
@@ -566,6 +566,8 @@ def lns8_valu_ops(path: int) -> float:
         if ":" in line and not line.startswith("#"):
             a, b = line.split(":", 1)
             vals[a.strip()] = b.strip()
+    if vals.get("kernel_source_sha256_16") != _source_digest("lns8_phase.hip"):
+        return None
     key = "valu_insts_per_call_" + ("direct" if path == 0 else "popcount")
     try:
         return float(vals[key])
@@ -803,6 +805,25 @@ def counter_summary(path: str):
                      for (n, c), v in sorted(vals.items()))
 
 
+def lns8_valu_summary(path: str):
+    """The LNS8 counter record: every counter's mean per call of each path
+    (lns8_kernel<0> = direct, <1> = popcount) from a --pmc CSV of
+    --lns8-counter-run, keyed to the kernel source it was taken on."""
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        if "lns8_kernel<" not in name:
+            continue
+        p = "direct" if "lns8_kernel<0" in name else "popcount"
+        vals.setdefault((r["Counter_Name"], p), []).append(float(r["Counter_Value"]))
+    lines = ["kernel_source_sha256_16: %s" % _source_digest("lns8_phase.hip")]
+    for (c, p), v in sorted(vals.items()):
+        key = "valu_insts" if c == "SQ_INSTS_VALU" else c.lower()
+        lines.append("%s_per_call_%s: %.1f" % (key, p, statistics.mean(v)))
+        lines.append("%s_calls_%s: %d" % (key, p, len(v)))
+    return "\n".join(lines)
+
+
 def traffic_summary(fetch_csv: str, write_csv: str, shape: str):
     """HBM bytes per GEMV launch from two rocprofv3 counter CSVs (FETCH_SIZE,
     WRITE_SIZE; KiB per dispatch), each scaled by the calibration kernel's
@@ -862,6 +883,8 @@ def main():
     ap.add_argument("--lns8-counter-run", action="store_true",
                     help="run the workload of the LNS8 --pmc runs and exit")
     ap.add_argument("--counter-summary", help="mean counters per kernel of a --pmc CSV and exit")
+    ap.add_argument("--lns8-valu-summary", metavar="CSV",
+                    help="the LNS8 counter record from a --pmc CSV of --lns8-counter-run, and exit")
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
@@ -877,6 +900,9 @@ def main():
         return 0
     if args.counter_summary:
         print(counter_summary(args.counter_summary))
+        return 0
+    if args.lns8_valu_summary:
+        print(lns8_valu_summary(args.lns8_valu_summary))
         return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the GEMVs would "

@@ -37,7 +37,9 @@ class BsError(RuntimeError):
         super().__init__("%s: %s (status %d)" % (where, status_str(status), status))
 
 
-def _declare(lib):
+def _declare(lib, only=None):
+    """Result and argument types of the exported calls (of those in `only`,
+    when given: a library built from a subset of the sources)."""
     P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     sig = {
         "bs_abi_version": (I32, []),
@@ -71,6 +73,8 @@ def _declare(lib):
                                        ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint64, P, P]),
     }
     for name, (res, args) in sig.items():
+        if only is not None and name not in only:
+            continue
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args

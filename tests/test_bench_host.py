@@ -100,3 +100,36 @@ def test_source_digest_covers_included_headers(tmp_path, monkeypatch):
     with open(tmp_path / "bit_decode_gemv_amd" / "csrc" / "kcommon.h", "a") as f:
         f.write("\n// edit\n")
     assert bench._source_digest() != before
+
+
+def test_lns8_valu_record_round_trip(tmp_path, monkeypatch):
+    """The LNS8 counter record written by --lns8-valu-summary is read back by
+    the bench, and ignored once the LNS8 kernel source changes."""
+    import shutil
+    for rel in (("bit_decode_gemv_amd", "csrc", "lns8_phase.hip"),
+                ("bit_decode_gemv_amd", "csrc", "kcommon.h"),
+                ("bit_decode_gemv_amd", "csrc", "bs_internal.h"),
+                ("include", "bs.h")):
+        dst = tmp_path.joinpath(*rel)
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(bench.ROOT, *rel), dst)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    fields = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    rows = []
+    for p, v in ((0, 1000.0), (1, 700.0)):
+        for i in range(3):
+            rows.append({"Kernel_Name": "void bs::lns8_kernel<%d>(args)" % p,
+                         "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": v + i})
+            rows.append({"Kernel_Name": "void bs::lns8_kernel<%d>(args)" % p,
+                         "Counter_Name": "SQ_WAVES", "Counter_Value": 4096})
+    rows.append({"Kernel_Name": "void at::native::other", "Counter_Name": "SQ_INSTS_VALU",
+                 "Counter_Value": 5.0})
+    _write(tmp_path / "c.csv", fields, rows)
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "lns8_4096x4096_valu.txt").write_text(
+        "# header\n" + bench.lns8_valu_summary(str(tmp_path / "c.csv")) + "\n")
+    assert bench.lns8_valu_ops(0) == pytest.approx(1001.0)
+    assert bench.lns8_valu_ops(1) == pytest.approx(701.0)
+    with open(tmp_path / "bit_decode_gemv_amd" / "csrc" / "lns8_phase.hip", "a") as f:
+        f.write("\n// edit\n")
+    assert bench.lns8_valu_ops(0) is None
