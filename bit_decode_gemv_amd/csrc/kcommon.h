@@ -78,6 +78,12 @@ __device__ __forceinline__ uint4 buffer_load_stream16(__amdgpu_buffer_rsrc_t r, 
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 16 bits, sign-extended, non-temporal.
+__device__ __forceinline__ int buffer_load_stream_i16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                      uint32_t soff) {
+    return (int)(int16_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 2);
+}
+
 __device__ __forceinline__ int buffer_load_i8(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                               uint32_t soff) {
     return (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);

@@ -384,17 +384,25 @@ __global__ __launch_bounds__(NW * 64) void ternary_pipe_kernel(
     const uint32_t w_off = 16u * j;
     const uint32_t sc_off = (uint32_t)(((j >> 4) * groups * 16 + (j & 15)) * 2);
 
+    // Scale loads: with several groups per slice non-temporal, like the
+    // planes (0.13 to 0.3 us less per launch on the tall shapes); a lone
+    // group per slice keeps the default policy (non-temporal measured slower
+    // there: the two workgroups of a 16-row block share each scale line)
+    auto load_scale = [&](uint32_t off) {
+        return NG == 1 ? buffer_load_i16(rs, off, 0) : buffer_load_stream_i16(rs, off, 0);
+    };
     uint2 xv[XP];
 #pragma unroll
     for (int p = 0; p < XP; ++p) xv[p] = buffer_load8(rx, 8u * (threadIdx.x + p * NT));
     __builtin_amdgcn_sched_barrier(0);
     // the first D groups: scales, then planes (the compiler schedules a lone
-    // scale load, NG = 1, after the barrier below; measured faster there)
+    // scale load, NG = 1, after the barrier below; issuing it first measured
+    // no faster)
     uint4 nz[NG], ng[NG];
     int sc[NG];
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
-        if (q < D) sc[q] = buffer_load_i16(rs, sc_off + (uint32_t)(sl + q * NS) * 32u, 0);
+        if (q < D) sc[q] = load_scale(sc_off + (uint32_t)(sl + q * NS) * 32u);
     }
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(NW * 64) void ternary_pipe_kernel(
             const uint32_t g = (uint32_t)(sl + (q + D) * NS);
             nz[q + D] = buffer_load_stream16(rp, g * 2048u + w_off, 0);
             ng[q + D] = buffer_load_stream16(rp, g * 2048u + 1024u + w_off, 0);
-            sc[q + D] = buffer_load_i16(rs, sc_off + g * 32u, 0);
+            sc[q + D] = load_scale(sc_off + g * 32u);
         }
         __builtin_amdgcn_sched_barrier(0);
         const int g = sl + q * NS;
@@ -461,10 +469,11 @@ __global__ __launch_bounds__(NW * 64) void ternary_pipe_kernel(
 //   K <= 8192:  16-row blocks with 2 groups per slice;
 //   K <= 12288: 16-row blocks of 8 wavefronts, 3 groups per slice;
 //   K <= 16384: 32-row blocks of 9 wavefronts, 6 to 8 groups per slice.
-// Measured per launch (events, back-to-back): 2560x2560 3.10 -> 2.68 us,
-// 6912x2560 3.60 -> 3.24, 11008x4096 4.70 -> 4.39, 13824x5120 5.28 -> 5.08,
-// 2560x6912 3.92 -> 3.34, 5120x13824 7.02 -> 6.44 against the row-block and
-// tile kernels.
+// Measured per launch (events, back-to-back, cold weights) against the
+// row-block and tile kernels: 2560x2560 3.10 -> 2.64 us, 6912x2560 3.60 ->
+// 3.12, 11008x4096 4.70 -> 4.44, 13824x5120 5.28 -> 5.29, 2560x6912 3.92 ->
+// 3.21, 5120x13824 7.02 -> 6.66.  A re-sweep of this table (every family
+// member, pipeline depth 2 or all groups up front) found no faster entry.
 struct PipeCfg {
     int R, NW, NG;
 };
