@@ -222,8 +222,9 @@ def _stream_handle(stream, device):
 
 class Workspace:
     """Zero-filled device scratch, one per (entry point, device), grown on
-    demand.  No entry point's result depends on a workspace byte the same
-    call did not write, so one buffer serves every call of that entry point
+    demand.  The split-K entry points (LNS8, pure fractional-LNS) need it
+    zero before their first call and leave it zero; the others write every
+    byte they read.  So one buffer serves every call of that entry point
     ordered on one stream; entry points never share a buffer."""
 
     _cache = {}

@@ -22,11 +22,14 @@
 // dead: those adds are skipped by scalar branches.  The sixteen bands of a
 // phase reduce in registers; the eight Tile128s of the workgroup meet in
 // LDS.  With more than eight Tile128s, each workgroup writes its eight phase
-// partials per row to the workspace and kernel B (lanes = workgroups of one
-// row, shuffles) finishes the tile tree, then the phase tree and the scale.
-// The kernel boundary makes the partials visible across XCDs (a last-arrival
-// reduction inside kernel A, with agent-scope fences, measured 3-4x slower:
-// the L2 write-backs cost more than a second launch).
+// partials per row to the workspace with agent-scope stores (written through
+// to memory, so visible to every XCD), waits for them and counts itself done
+// on the tile's counter (agent-scope atomic add); the workgroup that finds
+// itself last reads the partials back with agent-scope loads, finishes the
+// tile tree across the workgroups (lanes = workgroups of one row, shuffles),
+// then the phase tree and the scale, and returns its counter and partials
+// to zero for the next call.  No release/acquire fences: those write back
+// and invalidate the L2, which measured 3-4x slower than a second launch.
 //
 // Tables.  For frac_bits <= 8 the corrections are int16 and staged in LDS
 // (at most 102,656 bytes); above, they are read from the
@@ -164,9 +167,10 @@ template <bool SMALL>
 __global__ __launch_bounds__(1024) void flns_tile_kernel(
     const uint8_t *__restrict__ planes, const uint8_t *__restrict__ x, int rows, int groups,
     int f, const uint8_t *__restrict__ table, int S, int ld, int nsplit,
-    int32_t *__restrict__ out, int *__restrict__ partial) {
+    int32_t *__restrict__ out, int *__restrict__ counters, int *__restrict__ partial) {
     using E = LutT<SMALL>;
     __shared__ int32_t s_fold[kFlnsFoldSlots];   // entries 0..128 (|cnt| <= 128)
+    __shared__ int last;
     __shared__ uint4 s_lut4[SMALL ? kFlnsSmallMaxEntries * 2 / 16 : 1];
     __shared__ int s_x[kTilesPerWg][8][64];
     __shared__ uint32_t s_present[kTilesPerWg][4];   // codes present in each Tile128
@@ -289,48 +293,57 @@ __global__ __launch_bounds__(1024) void flns_tile_kernel(
             for (int k = 0; k < 8; ++k) ph[k] = s_x[0][k][lane];
             *reinterpret_cast<int2 *>(out + 2 * (size_t)row) = finish(phase_tree(ph, lut, S), ld);
         }
-    } else if (threadIdx.x < 512) {
-        const size_t padded_rows = (size_t)(gridDim.x / nsplit) * 64;
-        partial[((size_t)q * padded_rows + row) * 8 + p] = r;
-    }
-}
-
-// Kernel B: the tile tree across the nsplit workgroups of a row, then the
-// phase tree and the scale.  P (a power of two >= nsplit, <= 64) lanes per
-// row, lane i holding workgroup i's eight phase partials (zero past nsplit);
-// level s pairs lanes i and i ^ s, which is the balanced pairwise tree.
-template <bool SMALL>
-__global__ __launch_bounds__(1024) void flns_combine(const int *__restrict__ partial, int rows,
-                                                    int padded_rows, int nsplit, int P,
-                                                    const uint8_t *__restrict__ table, int S,
-                                                    int ld, int32_t *__restrict__ out) {
-    using E = LutT<SMALL>;
-    __shared__ uint4 s_lut4[SMALL ? kFlnsSmallMaxEntries * 2 / 16 : 1];
-    const int gid = blockIdx.x * blockDim.x + threadIdx.x;
-    const int row = gid / P;
-    const int q = gid - row * P;
-    int v[8];
-    if (row < rows && q < nsplit) {
-        const int4 *src = reinterpret_cast<const int4 *>(partial + ((size_t)q * padded_rows + row) * 8);
-        const int4 a = src[0], b = src[1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     } else {
-#pragma unroll
-        for (int p = 0; p < 8; ++p) v[p] = kZ;
-    }
-    if constexpr (SMALL) {
-        stage16(s_lut4, reinterpret_cast<const uint4 *>(table + kFlnsCorrOff), (2 * S * 2 + 15) / 16);
+        // this workgroup's partials, then the tile's counter
+        const size_t padded_rows = (size_t)(gridDim.x / nsplit) * 64;
+        if (threadIdx.x < 512)
+            __hip_atomic_store(partial + ((size_t)q * padded_rows + row) * 8 + p, r,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's stores are done
         __syncthreads();
-    }
-    const E *lut = SMALL ? reinterpret_cast<const E *>(s_lut4)
-                         : reinterpret_cast<const E *>(table + kFlnsCorrOff);
-    for (int s = 1; s < P; s <<= 1) {
+        if (threadIdx.x == 0)
+            last = __hip_atomic_fetch_add(counters + rtile, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+        __syncthreads();
+        if (!last) return;   // uniform
+        // The tile tree across the nsplit workgroups of each of the tile's
+        // 64 rows, then the phase tree and the scale: P (a power of two >=
+        // nsplit, <= 64) lanes per row, lane i holding workgroup i's eight
+        // phase partials (zero past nsplit); level s pairs lanes i and i ^ s,
+        // which is the balanced pairwise tree.  1024 / P rows per pass.
+        int P = 1;
+        while (P < nsplit) P <<= 1;
+        const int per_pass = (int)blockDim.x / P;
+        const int qi = (int)threadIdx.x % P;
+        for (int r0 = 0; r0 < 64; r0 += per_pass) {   // uniform trip count
+            const int lr = r0 + (int)threadIdx.x / P;  // row within the tile
+            const int grow = rtile * 64 + lr;
+            int v[8];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) v[p] = lns_add(v[p], __shfl_xor(v[p], s), lut, S);
+            for (int k = 0; k < 8; ++k) v[k] = kZ;
+            if (lr < 64 && qi < nsplit) {
+                int *src = partial + ((size_t)qi * padded_rows + grow) * 8;
+                // every load in flight, then the clearing stores
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    v[k] = __hip_atomic_load(src + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) src[k] = 0;
+                if (grow >= rows) {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) v[k] = kZ;
+                }
+            }
+            for (int sh = 1; sh < P; sh <<= 1) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[k] = lns_add(v[k], __shfl_xor(v[k], sh), lut, S);
+            }
+            if (qi == 0 && lr < 64 && grow < rows)
+                *reinterpret_cast<int2 *>(out + 2 * (size_t)grow) = finish(phase_tree(v, lut, S), ld);
+        }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(counters + rtile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (q == 0 && row < rows)
-        *reinterpret_cast<int2 *>(out + 2 * (size_t)row) = finish(phase_tree(v, lut, S), ld);
 }
 
 }  // namespace
@@ -343,13 +356,25 @@ static constexpr int64_t kFlnsMaxK = 65408;
 
 static int64_t flns_nsplit(int64_t k) { return (k / kGroup + kTilesPerWg - 1) / kTilesPerWg; }
 
-// Workspace: the partials int32[nsplit][R][8] when K is split over several
-// workgroups per row tile.  Written before they are read: no initialisation.
-static size_t flns_ws_bytes(int64_t rows, int64_t k) {
+// Workspace, when K is split over several workgroups per row tile: one
+// int32 counter per tile (256-byte aligned), then the partials
+// int32[nsplit][R][8].  It must be zero before the first call, and every
+// call leaves it zero (the last workgroup of a tile clears the tile's
+// counter and partials), so one workspace serves calls of any shape.
+struct FlnsWs {
+    size_t partial, total;
+};
+
+static FlnsWs flns_ws(int64_t rows, int64_t k) {
     const int64_t ns = flns_nsplit(k);
-    const size_t part = ns > 1 ? (size_t)ns * (size_t)pad64(rows) * 8 * 4 : 0;
-    return align_up(part > 0 ? part : 1, kWsAlign);
+    FlnsWs w;
+    w.partial = ns > 1 ? align_up((size_t)(pad64(rows) / 64) * 4, kWsAlign) : 0;
+    w.total = ns > 1 ? w.partial + (size_t)ns * (size_t)pad64(rows) * 8 * 4 : kWsAlign;
+    w.total = align_up(w.total, kWsAlign);
+    return w;
 }
+
+static size_t flns_ws_bytes(int64_t rows, int64_t k) { return flns_ws(rows, k).total; }
 
 extern "C" size_t bs_flns_workspace_bytes(int64_t rows, int64_t k) {
     if (check_rows_k(rows, k, kFlnsMaxK) != BS_OK) return 0;
@@ -377,27 +402,18 @@ extern "C" int32_t bs_flns_phase_gemv(const uint8_t *planes, const uint8_t *x_ln
     const int64_t tiles = pad64(rows) / 64;
     const int64_t groups = k / kGroup;
     const int nsplit = (int)flns_nsplit(k);
-    // both grids within the 2^32 threads of one launch
-    if (tiles * nsplit * kWavesPerWg * 64 >= ((int64_t)1 << 32) ||
-        rows * 64 >= ((int64_t)1 << 32))
-        return BS_E_SHAPE;
+    // the grid within the 2^32 threads of one launch
+    if (tiles * nsplit * kWavesPerWg * 64 >= ((int64_t)1 << 32)) return BS_E_SHAPE;
     hipStream_t st = (hipStream_t)stream;
     const uint8_t *tb = static_cast<const uint8_t *>(table);
-    int *partial = static_cast<int *>(workspace);
+    const FlnsWs w = flns_ws(rows, k);
+    unsigned char *base = static_cast<unsigned char *>(workspace);
+    int *counters = reinterpret_cast<int *>(base);
+    int *partial = reinterpret_cast<int *>(base + w.partial);
     auto kern = small ? flns_tile_kernel<true> : flns_tile_kernel<false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * nsplit)), dim3(kWavesPerWg * 64), 0, st,
                        planes, x_lns8, (int)rows, (int)groups, (int)frac_bits, tb, (int)sz.stride,
-                       (int)ld, nsplit, out, partial);
+                       (int)ld, nsplit, out, counters, partial);
     BS_LAUNCH_CHECK();
-    if (nsplit > 1) {
-        int P = 1;
-        while (P < nsplit) P <<= 1;
-        const int64_t threads = rows * P;
-        auto comb = small ? flns_combine<true> : flns_combine<false>;
-        hipLaunchKernelGGL(comb, dim3((unsigned)((threads + 1023) / 1024)), dim3(1024), 0, st,
-                           partial, (int)rows, (int)pad64(rows), nsplit, P, tb, (int)sz.stride,
-                           (int)ld, out);
-        BS_LAUNCH_CHECK();
-    }
     return BS_OK;
 }

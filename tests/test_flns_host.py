@@ -74,7 +74,7 @@ def test_flns_validation():
     assert _flns(table=None) == bs.BS_E_NULL
     assert _flns(out=None) == bs.BS_E_NULL
     assert _flns(rows=0) == bs.BS_E_SHAPE
-    assert _flns(rows=1 << 27) == bs.BS_E_SHAPE               # launch grid limit
+    assert _flns(rows=1 << 28) == bs.BS_E_SHAPE               # launch grid limit (2^32 threads)
     assert _flns(k=100) == bs.BS_E_SHAPE
     assert _flns(k=65536) == bs.BS_E_OVERFLOW
     assert _flns(f=-1) == bs.BS_E_RANGE
@@ -95,6 +95,8 @@ def test_flns_workspace_sizes():
     lib = bs.lib()
     assert lib.bs_flns_workspace_bytes(0, 128) == 0
     assert lib.bs_flns_workspace_bytes(64, 1024) == 256           # one workgroup per tile
-    assert lib.bs_flns_workspace_bytes(4096, 4096) == 4 * 4096 * 8 * 4
-    assert lib.bs_flns_workspace_bytes(65, 1152) == 2 * 128 * 8 * 4
-    assert lib.bs_flns_workspace_bytes(64, 65408) == 64 * 64 * 8 * 4
+    # split K: a counter per 64-row tile (256-byte aligned), then the partials
+    assert lib.bs_flns_workspace_bytes(4096, 4096) == 256 + 4 * 4096 * 8 * 4
+    assert lib.bs_flns_workspace_bytes(65, 1152) == 256 + 2 * 128 * 8 * 4
+    assert lib.bs_flns_workspace_bytes(64, 65408) == 256 + 64 * 64 * 8 * 4
+    assert lib.bs_flns_workspace_bytes(64 * 65, 2048) == 512 + 2 * 64 * 65 * 8 * 4

@@ -98,13 +98,17 @@ def test_flns_adversarial(case, f):
 
 
 def test_flns_repeated_calls_share_a_workspace():
-    """One workspace serves back-to-back calls of different shapes (one with
-    fewer rows, one with a single workgroup per tile), every result exact."""
+    """One zeroed workspace serves back-to-back calls of different shapes:
+    fewer rows, a single workgroup per tile, and more tiles after fewer (the
+    later call's counters then lie where the earlier call's partials were;
+    every call leaves the workspace zero), every result exact."""
     import torch
     dev = device()
-    ws = torch.zeros(int(bs.lib().bs_flns_workspace_bytes(300, 4096)), dtype=torch.uint8,
-                     device=dev)
-    for rows, k, seed in ((300, 4096, 1), (300, 4096, 2), (130, 2048, 3), (300, 4096, 4)):
+    shapes = ((300, 4096, 1), (300, 4096, 2), (130, 2048, 3), (64, 1024, 5), (1000, 3072, 6),
+              (300, 4096, 4), (1000, 3072, 7))
+    need = max(int(bs.lib().bs_flns_workspace_bytes(r, k)) for r, k, _ in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    for rows, k, seed in shapes:
         t, x = synth.lns8(rows, k, seed)
         want = oracle.flns_gemv(t, x, 8)
         note("flns repeated rows=%d k=%d" % (rows, k))
@@ -112,3 +116,4 @@ def test_flns_repeated_calls_share_a_workspace():
                                  table_dev(8, dev), workspace=ws)
         torch.cuda.synchronize()
         assert (out.cpu().numpy() == want).all()
+        assert int(ws.count_nonzero().item()) == 0      # left zero for the next call
