@@ -754,7 +754,9 @@ def traffic_run(shape: str, launches: int = 20):
     launches of a plain elementwise kernel of known size (int32 negation,
     CALIB_BYTES read and CALIB_BYTES written: the counter calibration), then
     `launches` launches of the ternary GEMV of `shape` on distinct weight
-    buffers (> 1 GiB in total, so they stream from HBM)."""
+    buffers (> 1 GiB in total, so they stream from HBM), then as many plain
+    reads of the same bytes from other buffers of the pool (the read-ceiling
+    kernel, four 16-byte loads per thread), for counters side by side."""
     import torch
     import bit_decode_gemv_amd as bs
     from bit_decode_gemv_amd import synth
@@ -762,8 +764,11 @@ def traffic_run(shape: str, launches: int = 20):
     dev = torch.device("cuda:0")
     a = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device=dev)
     b = torch.empty_like(a)
-    _, views, x, _ = packed_pool(torch, bs, synth, dev, rows, k, 1 << 30)
+    from bit_decode_gemv_amd import probe
+    bufs, views, x, _ = packed_pool(torch, bs, synth, dev, rows, k, 1 << 30)
     y = torch.empty(rows, dtype=torch.int64, device=dev)
+    wb = weight_bytes(rows, k)
+    sink = probe.sink_for(wb, 4, dev)
     torch.cuda.synchronize()
     for _ in range(3):
         torch.neg(a, out=b)
@@ -771,7 +776,11 @@ def traffic_run(shape: str, launches: int = 20):
     for i in range(launches):
         bs.ternary_gemv(views[i % len(views)][0], views[i % len(views)][1], x, rows, k, out=y)
     torch.cuda.synchronize()
-    log("traffic run done: 3 calibration launches, %d GEMV launches of %s" % (launches, shape))
+    for i in range(launches):
+        probe.read(bufs[(launches + i) % len(bufs)], wb, 4, sink, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    log("traffic run done: 3 calibration launches, %d GEMV launches of %s, %d reads of its "
+        "weight bytes" % (launches, shape, launches))
 
 
 def lns8_counter_run(launches: int = 10):
@@ -793,16 +802,42 @@ def lns8_counter_run(launches: int = 10):
     log("LNS8 counter run done: %d calls per path" % launches)
 
 
-def counter_summary(path: str):
-    """Mean of every counter per kernel name (template arguments kept) from
-    a rocprofv3 --pmc counter_collection.csv: one line per (kernel, counter)."""
+SIMDS = 1024                    # 256 CUs x 4 SIMDs
+
+
+def counter_summary(*paths: str):
+    """Mean of every counter per kernel name (template arguments kept) over
+    one or more rocprofv3 --pmc counter_collection.csv files: one line per
+    (kernel, counter), then per kernel the ratios these counters give."""
     vals = {}
-    for r in csv.DictReader(open(path)):
-        name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
-        vals.setdefault((name, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
-    return "\n".join("%-60s %-20s dispatches %4d mean %.6g" % (n[:60], c, len(v),
-                                                                 statistics.mean(v))
-                     for (n, c), v in sorted(vals.items()))
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+            vals.setdefault((name, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    out = ["%-60s %-28s dispatches %4d mean %.6g" % (n[:60], c, len(v), statistics.mean(v))
+           for (n, c), v in sorted(vals.items())]
+    means = {}
+    for (n, c), v in vals.items():
+        means.setdefault(n, {})[c] = statistics.mean(v)
+    for n, m in sorted(means.items()):
+        d = []
+        if "SQ_WAVES" in m:
+            d.append("waves_per_simd %.3f" % (m["SQ_WAVES"] / SIMDS))
+            if "SQ_INSTS_VALU" in m:
+                d.append("valu_insts_per_wave %.1f" % (m["SQ_INSTS_VALU"] / m["SQ_WAVES"]))
+            if "SQ_INSTS_VMEM_RD" in m:
+                d.append("vmem_rd_insts_per_wave %.1f" % (m["SQ_INSTS_VMEM_RD"] / m["SQ_WAVES"]))
+        if m.get("SQ_WAVE_CYCLES"):
+            for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU"):
+                if c in m:
+                    d.append("%s_per_wave_cycle %.3f" % (c.lower(), m[c] / m["SQ_WAVE_CYCLES"]))
+        if m.get("TCP_TCC_READ_REQ_sum"):
+            if "TCP_TCC_READ_REQ_LATENCY_sum" in m:
+                d.append("l2_read_latency_cycles %.1f" % (m["TCP_TCC_READ_REQ_LATENCY_sum"] /
+                                                         m["TCP_TCC_READ_REQ_sum"]))
+        if d:
+            out.append("%-60s derived: %s" % (n[:60], ", ".join(d)))
+    return "\n".join(out)
 
 
 def lns8_valu_summary(path: str):
@@ -882,7 +917,8 @@ def main():
                     help="HBM bytes per launch from the two counter CSVs and exit")
     ap.add_argument("--lns8-counter-run", action="store_true",
                     help="run the workload of the LNS8 --pmc runs and exit")
-    ap.add_argument("--counter-summary", help="mean counters per kernel of a --pmc CSV and exit")
+    ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
+                    help="mean counters per kernel of --pmc CSVs, with their ratios, and exit")
     ap.add_argument("--lns8-valu-summary", metavar="CSV",
                     help="the LNS8 counter record from a --pmc CSV of --lns8-counter-run, and exit")
     args = ap.parse_args()
@@ -899,7 +935,7 @@ def main():
         lns8_counter_run()
         return 0
     if args.counter_summary:
-        print(counter_summary(args.counter_summary))
+        print(counter_summary(*args.counter_summary))
         return 0
     if args.lns8_valu_summary:
         print(lns8_valu_summary(args.lns8_valu_summary))

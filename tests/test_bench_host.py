@@ -133,3 +133,21 @@ def test_lns8_valu_record_round_trip(tmp_path, monkeypatch):
     with open(tmp_path / "bit_decode_gemv_amd" / "csrc" / "lns8_phase.hip", "a") as f:
         f.write("\n// edit\n")
     assert bench.lns8_valu_ops(0) is None
+
+
+def test_counter_summary_ratios(tmp_path):
+    fields = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    k = "void bs::(anonymous namespace)::ternary_pipe_kernel<8, 3, 1, 1>(args)"
+    _write(tmp_path / "a.csv", fields,
+           [{"Kernel_Name": k, "Counter_Name": "SQ_WAVES", "Counter_Value": 2048},
+            {"Kernel_Name": k, "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": 204800},
+            {"Kernel_Name": k, "Counter_Name": "SQ_WAVE_CYCLES", "Counter_Value": 1000},
+            {"Kernel_Name": k, "Counter_Name": "SQ_WAIT_INST_ANY", "Counter_Value": 250}])
+    _write(tmp_path / "b.csv", fields,
+           [{"Kernel_Name": k, "Counter_Name": "TCP_TCC_READ_REQ_sum", "Counter_Value": 10},
+            {"Kernel_Name": k, "Counter_Name": "TCP_TCC_READ_REQ_LATENCY_sum",
+             "Counter_Value": 7000}])
+    out = bench.counter_summary(str(tmp_path / "a.csv"), str(tmp_path / "b.csv"))
+    d = [line for line in out.splitlines() if "derived" in line][0]
+    assert "waves_per_simd 2.000" in d and "valu_insts_per_wave 100.0" in d
+    assert "sq_wait_inst_any_per_wave_cycle 0.250" in d and "l2_read_latency_cycles 700.0" in d
