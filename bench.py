@@ -83,7 +83,7 @@ RESIDUAL = ("o", "down")
 # marker ids of the measured blocks (empty-kernel grid = (4096 + id) x 64)
 MARKER_BASE = 4096
 BLOCKS = ["step", "roofline_graph", "context_floor", "ceiling_scrub",
-          "f1_fused_step", "lmhead", "lns8", "flns", "q1", "edges"]
+          "f1_fused_step", "lmhead", "lns8", "flns", "q1", "edges", "lmhead_ceiling"]
 SHAPE_BLOCKS = ["gemv_%dx%d" % s for s in IN_RANGE + REPORTED]
 SWEEP_BLOCKS = ["f1_reuse_%s_n%d" % (p, n) for p in ("ternary", "direct", "popcount")
                 for n in (1, 8, 32, 128, 512, 2048, 8192)]
@@ -696,10 +696,13 @@ def run_extras(torch, bs, synth, dev, H):
         workspace=wsl, stream=H.stream), 20, block="lmhead")
     stage1_bytes = p03.size + rs.nbytes
     torch.cuda.synchronize()
+    # the read ceiling of stage 1's planes 0-3 bytes over the same pool
+    ceil_us = H.ceiling(pool03, p03.size, 4, block="lmhead_ceiling")
     ops["lmhead_planes_topk_128256x2560"] = {
         "us_per_call": round(us, 3), "stage1_bytes": stage1_bytes,
         "GBps_stage1_bytes": round(stage1_bytes / us / 1e3, 1),
         "frac_hbm_peak": round(stage1_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
+        "planes03_read_ceiling_us": round(ceil_us, 3),
         "n_candidates": int(info[0].item()), "capped": int(info[1].item()),
         "certified_exact": int(info[2].item())}
     log("lm_head: %.2f us" % us)
