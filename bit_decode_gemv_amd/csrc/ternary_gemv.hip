@@ -6,32 +6,27 @@
 // LLMs", section 4.2; the W_nonzero / W_negative planes of "BitState / HSDR
 // PoC Technical Brief - v0.5", section 4).
 //
-// Mapping.  A workgroup owns R complete rows (R = 32 or 16) and all of K,
-// so no partial sum ever leaves the CU.  Its W wavefronts are split into
-// slices: lane l of wavefront w serves row (l mod R) of the block in slice
-// w*(64/R) + l/R, and slice s takes groups s, s + nslices, s + 2*nslices, ...
-// A lane streams the row's 16-byte W_nonzero and W_negative fields of each of
-// its groups (R lanes of a slice read R*16 contiguous bytes of the tiled
-// layout).  Work proceeds in rounds of MAXG (1 or 2) groups per slice: a
-// wavefront issues the activation loads and then every weight load of the
-// round, transposes the activations of its own groups into eight bit planes
-// in a private LDS slot (no workgroup barrier: only the wavefront's own lanes
-// read them), then computes.  The inner loop works on the signed population
-// of the brief's section 4 through the identity t*m = nz*(m xor neg) - neg
-// (t = nz - 2 neg): per 32 weights and activation bit plane b, one
-// AND-XOR (v_bitop3) and one popcount.  Slices meet by cross-lane shuffles
-// inside a wavefront and through LDS across wavefronts; integer sums make
-// the result independent of that order (integer-engine page, section 3.2).
+// Mappings.  Up to K = 16384 (128 groups) both GEMVs run the pipelined
+// mapping (ternary_pipe_kernel): a workgroup owns R = 8, 16 or 32 rows of one
+// 64-row tile and all of K; its wavefronts are split into 64/R slices of R
+// lanes (lane = row) that take interleaved 128-weight groups.  The workgroup
+// reads x once, transposes it into eight bit planes per group in LDS (8x8
+// bit transposes; one barrier), and every lane streams its row's 16-byte
+// plane fields of its groups through buffer resources bounded at the tile,
+// so loads past K read zero and none is predicated.  The inner loop works on
+// the signed population of the brief's section 4 through the identity
+// t*m = nz*(m xor neg) - neg (t = nz - 2 neg): per 32 weights and activation
+// bit plane, one AND-XOR (v_bitop3) and one popcount chained through its
+// addend.  Slices meet by lane permutations, wavefronts in LDS; integer sums
+// make the result independent of that order (integer-engine page, section
+// 3.2), and each row is stored once.
 //
-// Tall matrices (many 64-row tiles, few groups per row) use a second
-// mapping: one workgroup per 64-row tile, lane l of every wavefront serving
-// row 64*tile + l, wavefront w taking groups w, w + W, ...  The activations
-// a wavefront needs are then uniform across it, and their bit planes come
-// from sixteen ballots into scalar registers: no LDS staging, and the LDS
-// only meets the W partial sums per row at the end.  bs_ternary_gemv_acc
-// (y += W x, the residual-stream update of a decoder layer) runs the same
-// mapping split over runs of groups, each workgroup adding its rows' partial
-// sums to y with int64 atomics, so short matrices still fill the GPU.
+// Beyond 128 groups, the row-block mapping (per-wavefront LDS staging, no
+// workgroup barrier) or, for tall matrices, the tile mapping (one workgroup
+// per 64-row tile, activation bit planes from sixteen ballots into scalar
+// registers).  bs_ternary_gemv_acc (y += W x, the residual-stream update of a
+// decoder layer) runs the tile mapping split over runs of groups, each
+// workgroup adding its rows' partial sums to y with int64 atomics.
 //
 // bs_q1_gemv runs the same kernels on Q1_0 weights (integer-engine page,
 // section 4.1): one sign bit per weight (1 = +1, 0 = -1) in the layout of the
@@ -359,7 +354,7 @@ __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t
 // tile, its scale block and x, and a load past the end reads zero, so the
 // wait counts are static and a padding slot contributes 0.  Slices of a
 // wavefront meet by lane permutations, wavefronts in LDS.
-template <int R, int NW, int NG, int D>
+template <int R, int NW, int NG, int D, bool Q1>
 __global__ __launch_bounds__(NW * 64) void ternary_pipe_kernel(
     const uint8_t *__restrict__ planes, const int16_t *__restrict__ pscales,
     const int8_t *__restrict__ x, int rows, int groups, int shift, int64_t *__restrict__ y) {
@@ -376,8 +371,9 @@ __global__ __launch_bounds__(NW * 64) void ternary_pipe_kernel(
     const int row0 = (int)blockIdx.x * R;
     const int tile = row0 >> 6;
     const int j = (row0 & 63) + lane % R;            // row within the tile
+    constexpr uint32_t kBlk = Q1 ? 1024 : 2048;   // plane bytes per (tile, group)
     const __amdgpu_buffer_rsrc_t rp =
-        buffer_rsrc(planes + (size_t)tile * groups * 2048, (uint32_t)groups * 2048);
+        buffer_rsrc(planes + (size_t)tile * groups * kBlk, (uint32_t)groups * kBlk);
     const __amdgpu_buffer_rsrc_t rs =
         buffer_rsrc(pscales + (size_t)tile * 64 * groups, (uint32_t)groups * 128);
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)groups * 128);
@@ -408,8 +404,8 @@ __global__ __launch_bounds__(NW * 64) void ternary_pipe_kernel(
     for (int q = 0; q < NG; ++q) {
         if (q < D) {
             const uint32_t g = (uint32_t)(sl + q * NS);
-            nz[q] = buffer_load_stream16(rp, g * 2048u + w_off, 0);
-            ng[q] = buffer_load_stream16(rp, g * 2048u + 1024u + w_off, 0);
+            nz[q] = buffer_load_stream16(rp, g * kBlk + w_off, 0);
+            if constexpr (!Q1) ng[q] = buffer_load_stream16(rp, g * kBlk + 1024u + w_off, 0);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -421,6 +417,17 @@ __global__ __launch_bounds__(NW * 64) void ternary_pipe_kernel(
         uint8_t *dst = reinterpret_cast<uint8_t *>(xpl + gi * kPlaneStride) + (c & 15);
 #pragma unroll
         for (int b = 0; b < 8; ++b) dst[b * 16] = (uint8_t)(t8 >> (8 * b));
+        if constexpr (Q1) {
+            // block_total of the group in its padding slot: the group's 16
+            // chunks are 16 consecutive lanes (NT is a multiple of 16)
+            const uint64_t raw = (uint64_t)xv[p].x | ((uint64_t)xv[p].y << 32);
+            int sum8 = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sum8 += (int)(int8_t)(raw >> (8 * i));
+#pragma unroll
+            for (int m = 8; m >= 1; m >>= 1) sum8 += __shfl_xor(sum8, m, 16);
+            if ((c & 15) == 0) reinterpret_cast<int *>(xpl + gi * kPlaneStride + 8)[0] = sum8;
+        }
     }
     __syncthreads();
     int64_t acc = 0;
@@ -428,17 +435,24 @@ __global__ __launch_bounds__(NW * 64) void ternary_pipe_kernel(
     for (int q = 0; q < NG; ++q) {
         if (q + D < NG) {
             const uint32_t g = (uint32_t)(sl + (q + D) * NS);
-            nz[q + D] = buffer_load_stream16(rp, g * 2048u + w_off, 0);
-            ng[q + D] = buffer_load_stream16(rp, g * 2048u + 1024u + w_off, 0);
+            nz[q + D] = buffer_load_stream16(rp, g * kBlk + w_off, 0);
+            if constexpr (!Q1) ng[q + D] = buffer_load_stream16(rp, g * kBlk + 1024u + w_off, 0);
             sc[q + D] = load_scale(sc_off + g * 32u);
         }
         __builtin_amdgcn_sched_barrier(0);
         const int g = sl + q * NS;
         const uint4 *xg = xpl + (g < groups ? g : 0) * kPlaneStride;   // padding: any group
-        uint4 xr[8];                      // all eight planes in flight at once
+        uint4 xr[Q1 ? 9 : 8];             // all eight planes (and Q1's total) in flight
 #pragma unroll
-        for (int b = 0; b < 8; ++b) xr[b] = xg[b];
-        const int s = group_dot(nz[q], ng[q], xr);
+        for (int b = 0; b < (Q1 ? 9 : 8); ++b) xr[b] = xg[b];
+        int s;
+        if constexpr (Q1) {
+            // a padding slice's zero bits still give -block_total: its scale
+            // is forced to 0 (the ternary form's zero planes give s = 0)
+            s = g < groups ? q1_group_dot(nz[q], xr) : 0;
+        } else {
+            s = group_dot(nz[q], ng[q], xr);
+        }
         acc += (int64_t)(__mul24(s, sc[q]) >> shift);   // |s * sc| <= 2^29; >> = floor
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -497,55 +511,77 @@ static PipeCfg choose_pipe(int64_t rows, int64_t groups) {
     return {32, 9, cdiv(groups, 18)};
 }
 
-template <int R, int NW, int NG>
+// Q1_0 (half the plane bytes per group), from the same sweep: up to K = 3072
+// 16-row blocks with two groups per slice up to 4096 rows, 32-row blocks of
+// 4 wavefronts above (2560x2560 2.49 us, 13824x2560 3.46, against 2.61 and
+// 4.51 with the ternary entries); the ternary table beyond.
+static PipeCfg choose_pipe_q1(int64_t rows, int64_t groups) {
+    if (groups <= 24) {
+        if (rows <= 4096) return {16, cdiv(groups, 8), 2};
+        return {32, 4, cdiv(groups, 8)};
+    }
+    return choose_pipe(rows, groups);
+}
+
+template <int R, int NW, int NG, bool Q1>
 static void launch_pipe1(hipStream_t st, const uint8_t *planes, const int16_t *scales,
                          const int8_t *x, int rows, int groups, int shift, int64_t *y) {
     constexpr int D = NG < 2 ? NG : 2;
     const unsigned nblk = (unsigned)((rows + R - 1) / R);
-    hipLaunchKernelGGL((ternary_pipe_kernel<R, NW, NG, D>), dim3(nblk), dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((ternary_pipe_kernel<R, NW, NG, D, Q1>), dim3(nblk), dim3(NW * 64), 0, st,
                        planes, scales, x, rows, groups, shift, y);
 }
 
 // Dispatch over NW (R, NG fixed) or over NG (R, NW fixed), LO..HI.
-template <int R, int NG, int NW, int HI>
+template <int R, int NG, int NW, int HI, bool Q1>
 static bool pipe_by_nw(int nw, hipStream_t st, const uint8_t *p, const int16_t *s,
                        const int8_t *x, int rows, int groups, int shift, int64_t *y) {
     if constexpr (NW > HI) {
         return false;
     } else {
         if (nw == NW) {
-            launch_pipe1<R, NW, NG>(st, p, s, x, rows, groups, shift, y);
+            launch_pipe1<R, NW, NG, Q1>(st, p, s, x, rows, groups, shift, y);
             return true;
         }
-        return pipe_by_nw<R, NG, NW + 1, HI>(nw, st, p, s, x, rows, groups, shift, y);
+        return pipe_by_nw<R, NG, NW + 1, HI, Q1>(nw, st, p, s, x, rows, groups, shift, y);
     }
 }
 
-template <int R, int NW, int NG, int HI>
+template <int R, int NW, int NG, int HI, bool Q1>
 static bool pipe_by_ng(int ng, hipStream_t st, const uint8_t *p, const int16_t *s,
                        const int8_t *x, int rows, int groups, int shift, int64_t *y) {
     if constexpr (NG > HI) {
         return false;
     } else {
         if (ng == NG) {
-            launch_pipe1<R, NW, NG>(st, p, s, x, rows, groups, shift, y);
+            launch_pipe1<R, NW, NG, Q1>(st, p, s, x, rows, groups, shift, y);
             return true;
         }
-        return pipe_by_ng<R, NW, NG + 1, HI>(ng, st, p, s, x, rows, groups, shift, y);
+        return pipe_by_ng<R, NW, NG + 1, HI, Q1>(ng, st, p, s, x, rows, groups, shift, y);
     }
 }
 
+// Launches the configuration c, which must cover every group ((64 / R) * NW
+// * NG >= groups: the LDS staging has a slot for each); false (no launch)
+// for a configuration outside the instantiated set.
+template <bool Q1>
 static bool launch_pipe(const PipeCfg &c, hipStream_t st, const uint8_t *p, const int16_t *s,
                         const int8_t *x, int rows, int groups, int shift, int64_t *y) {
-    if (c.R == 8 && c.NG == 1) return pipe_by_nw<8, 1, 1, 3>(c.NW, st, p, s, x, rows, groups, shift, y);
-    if (c.R == 32 && c.NW == 4) return pipe_by_ng<32, 4, 1, 5>(c.NG, st, p, s, x, rows, groups, shift, y);
-    if (c.R == 16 && c.NW == 1) return pipe_by_ng<16, 1, 1, 6>(c.NG, st, p, s, x, rows, groups, shift, y);
-    if (c.R == 16 && c.NG == 2) return pipe_by_nw<16, 2, 1, 8>(c.NW, st, p, s, x, rows, groups, shift, y);
+    if (c.R <= 0 || c.NW <= 0 || c.NG <= 0 || (64 / c.R) * c.NW * c.NG < groups) return false;
+    if (c.R == 8 && c.NG == 1)
+        return pipe_by_nw<8, 1, 1, 3, Q1>(c.NW, st, p, s, x, rows, groups, shift, y);
+    if (c.R == 32 && c.NW == 4)
+        return pipe_by_ng<32, 4, 1, 5, Q1>(c.NG, st, p, s, x, rows, groups, shift, y);
+    if (c.R == 16 && c.NW == 1)
+        return pipe_by_ng<16, 1, 1, 6, Q1>(c.NG, st, p, s, x, rows, groups, shift, y);
+    if (c.R == 16 && c.NG == 2)
+        return pipe_by_nw<16, 2, 1, 8, Q1>(c.NW, st, p, s, x, rows, groups, shift, y);
     if (c.R == 16 && c.NW == 8 && c.NG == 3) {
-        launch_pipe1<16, 8, 3>(st, p, s, x, rows, groups, shift, y);
+        launch_pipe1<16, 8, 3, Q1>(st, p, s, x, rows, groups, shift, y);
         return true;
     }
-    if (c.R == 32 && c.NW == 9) return pipe_by_ng<32, 9, 6, 8>(c.NG, st, p, s, x, rows, groups, shift, y);
+    if (c.R == 32 && c.NW == 9)
+        return pipe_by_ng<32, 9, 6, 8, Q1>(c.NG, st, p, s, x, rows, groups, shift, y);
     return false;
 }
 
@@ -689,8 +725,8 @@ extern "C" int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales,
     const int64_t groups = k / kGroup;
     if (groups <= kPipeMaxGroups) {
         const int shift = frac > 31 ? 31 : frac;   // |scale*s| < 2^31: shift 31 is floor
-        if (!launch_pipe(choose_pipe(rows, groups), (hipStream_t)stream, planes, scales, x,
-                         (int)rows, (int)groups, shift, y))
+        if (!launch_pipe<false>(choose_pipe(rows, groups), (hipStream_t)stream, planes, scales,
+                                x, (int)rows, (int)groups, shift, y))
             return BS_E_RANGE;
         BS_LAUNCH_CHECK();
         return BS_OK;
@@ -702,6 +738,15 @@ extern "C" int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales,
 extern "C" int32_t bs_q1_gemv(const uint8_t *bits, const int16_t *scales, const int8_t *x,
                               int64_t rows, int64_t k, int32_t frac, int64_t *y, void *stream) {
     if (int32_t st = gemv_check(bits, scales, x, rows, k, frac, y)) return st;
+    const int64_t groups = k / kGroup;
+    if (groups <= kPipeMaxGroups) {
+        const int shift = frac > 31 ? 31 : frac;
+        if (!launch_pipe<true>(choose_pipe_q1(rows, groups), (hipStream_t)stream, bits, scales,
+                               x, (int)rows, (int)groups, shift, y))
+            return BS_E_RANGE;
+        BS_LAUNCH_CHECK();
+        return BS_OK;
+    }
     return launch_ternary<true>(choose_cfg(rows, k, true), bits, scales, x, rows, k, frac, y,
                                 (hipStream_t)stream);
 }
