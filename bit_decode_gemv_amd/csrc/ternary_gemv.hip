@@ -475,9 +475,9 @@ __global__ __launch_bounds__(NW * 64) void ternary_pipe_kernel(
 // bit-exact.  Short matrices want many small workgroups (8 rows, one group
 // per slice); taller ones longer per-slice pipelines (3 to 6 groups) on 16-
 // or 32-row blocks; the winners per K range:
-//   K <= 3072:  <= 4096 rows 8-row blocks, 1 group per slice; <= 9000 rows
-//               32-row blocks of 4 wavefronts; taller 16-row blocks of one
-//               wavefront with up to 6 groups per slice;
+//   K <= 3072:  <= 4096 rows 8-row blocks, 1 group per slice; taller
+//               32-row blocks of 4 wavefronts (13824x2560 4.21 -> 4.02 us
+//               against 16-row blocks of one wavefront with 5 groups);
 //   K <= 5120:  from 6400 rows 32-row blocks of 4 wavefronts, else 16-row
 //               blocks with 2 groups per slice;
 //   K <= 8192:  16-row blocks with 2 groups per slice;
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(NW * 64) void ternary_pipe_kernel(
 //   K <= 16384: 32-row blocks of 9 wavefronts, 6 to 8 groups per slice.
 // Measured per launch (events, back-to-back, cold weights) against the
 // row-block and tile kernels: 2560x2560 3.10 -> 2.64 us, 6912x2560 3.60 ->
-// 3.12, 11008x4096 4.70 -> 4.44, 13824x5120 5.28 -> 5.29, 2560x6912 3.92 ->
+// 3.12, 11008x4096 4.70 -> 4.44, 13824x5120 5.58 -> 5.29, 2560x6912 3.92 ->
 // 3.21, 5120x13824 7.02 -> 6.66.  A re-sweep of this table (every family
 // member, pipeline depth 2 or all groups up front) found no faster entry.
 struct PipeCfg {
@@ -499,8 +499,7 @@ static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 static PipeCfg choose_pipe(int64_t rows, int64_t groups) {
     if (groups <= 24) {
         if (rows <= 4096) return {8, cdiv(groups, 8), 1};
-        if (rows <= 9000) return {32, 4, cdiv(groups, 8)};
-        return {16, 1, cdiv(groups, 4)};
+        return {32, 4, cdiv(groups, 8)};
     }
     if (groups <= 40) {
         if (rows >= 6400) return {32, 4, cdiv(groups, 8)};
@@ -572,8 +571,6 @@ static bool launch_pipe(const PipeCfg &c, hipStream_t st, const uint8_t *p, cons
         return pipe_by_nw<8, 1, 1, 3, Q1>(c.NW, st, p, s, x, rows, groups, shift, y);
     if (c.R == 32 && c.NW == 4)
         return pipe_by_ng<32, 4, 1, 5, Q1>(c.NG, st, p, s, x, rows, groups, shift, y);
-    if (c.R == 16 && c.NW == 1)
-        return pipe_by_ng<16, 1, 1, 6, Q1>(c.NG, st, p, s, x, rows, groups, shift, y);
     if (c.R == 16 && c.NG == 2)
         return pipe_by_nw<16, 2, 1, 8, Q1>(c.NW, st, p, s, x, rows, groups, shift, y);
     if (c.R == 16 && c.NW == 8 && c.NG == 3) {

@@ -43,11 +43,20 @@ def test_large_k(shape):
 @pytest.mark.parametrize("rows,k", [(9600, 3840), (9601, 3968), (12800, 6144), (12801, 6272),
                                     (4999, 4224), (5000, 4224), (5001, 12800)])
 def test_mapping_edges(rows, k):
-    """Around the Q1_0 launch-shape bounds: the tile mapping at 150 tiles up to
-    30 groups (30 and 31) and at 200 tiles up to 48 (48 and 49), the two-group
-    rounds of 32-row blocks from 5000 rows beyond 32 groups (4999 and 5000,
-    a ragged last block, and more groups than one round's slots)."""
+    """Tall shapes with 30 to 100 groups (ragged last blocks, more groups than
+    one wavefront's slices)."""
     check(*synth.q1(rows, k, rows ^ k))
+
+
+@pytest.mark.parametrize("rows,k", [(4096, 3072), (4097, 3072), (4097, 128), (1, 128),
+                                    (13824, 2560), (6399, 5120), (6400, 5120), (300, 16384),
+                                    (1, 16384), (2000, 16512), (9, 1152), (17, 4224)])
+def test_pipelined_launch_rule(rows, k):
+    """Either side of the Q1_0 table of the pipelined kernel: up to 24 groups
+    16-row blocks with 2 groups per slice up to 4096 rows, 32-row blocks of 4
+    wavefronts above; the ternary table beyond; 129 groups take the row-block
+    kernel."""
+    check(*synth.q1(rows, k, rows + k))
 
 
 @pytest.mark.parametrize("rows,k", [(1, 128), (63, 128), (65, 256), (130, 384), (127, 6912),

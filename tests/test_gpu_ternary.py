@@ -72,12 +72,15 @@ def test_tile_mapping_edges(rows, k):
 @pytest.mark.parametrize("rows,k", [(1024, 2560), (1025, 2560), (8191, 2560), (8192, 2560),
                                     (8192, 8192), (8192, 8320), (8255, 1024), (2000, 16384),
                                     (2000, 16512), (1023, 128 * 127), (300, 16384),
-                                    (7, 2560), (9, 1152), (17, 4224), (1, 16384)])
+                                    (7, 2560), (9, 1152), (17, 4224), (1, 16384),
+                                    (4096, 3072), (4097, 3072), (4097, 128), (13824, 2560)])
 def test_pipelined_launch_rule(rows, k):
-    """Either side of the pipelined kernel's launch-shape bounds: 8-row blocks
-    up to 1024 rows, the 64-row workgroups from 8192 rows up to 64 groups,
-    16-row blocks otherwise, up to 128 groups (129 takes the row-block
-    kernel); ragged blocks and tiles."""
+    """Either side of the pipelined kernel's launch-shape bounds: up to 24
+    groups 8-row blocks up to 4096 rows and 32-row blocks of 4 wavefronts
+    above; up to 40 groups 32-row blocks from 6400 rows, else 16-row blocks
+    with 2 groups per slice; 8 wavefronts of 16-row blocks up to 96 groups,
+    32-row blocks of 9 up to 128 (129 takes the row-block kernel); ragged
+    blocks and tiles, fewer groups than slices."""
     check(*synth.ternary(rows, k, seed=rows + k, p_zero=1 / 3, act="uniform127"))
 
 
