@@ -1435,12 +1435,8 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, 
                 m = okey(src.u[sl]) > m ? okey(src.u[sl]) : m;
         }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const unsigned long long o = shfl_xor_u64(m, off);
-        m = o > m ? o : m;
-    }
-    if (lane == 0) red4[wave][0] = m;
+    m = wave_max_u64_lane63(m);   // DPP moves, no LDS round trip per step
+    if (lane == 63) red4[wave][0] = m;
     __syncthreads();
     if (t == 0) {
         unsigned long long mm = 0;
