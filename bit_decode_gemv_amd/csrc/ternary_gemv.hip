@@ -22,11 +22,11 @@
 // 3.2), and each row is stored once.
 //
 // Beyond 128 groups, the row-block mapping (per-wavefront LDS staging, no
-// workgroup barrier) or, for tall matrices, the tile mapping (one workgroup
-// per 64-row tile, activation bit planes from sixteen ballots into scalar
-// registers).  bs_ternary_gemv_acc (y += W x, the residual-stream update of a
-// decoder layer) runs the tile mapping split over runs of groups, each
-// workgroup adding its rows' partial sums to y with int64 atomics.
+// workgroup barrier).  bs_ternary_gemv_acc (y += W x, the residual-stream
+// update of a decoder layer) runs the tile mapping (one workgroup per 64-row
+// tile and run of groups, activation bit planes from sixteen ballots into
+// scalar registers), each workgroup adding its rows' partial sums to y with
+// int64 atomics.
 //
 // bs_q1_gemv runs the same kernels on Q1_0 weights (integer-engine page,
 // section 4.1): one sign bit per weight (1 = +1, 0 = -1) in the layout of the
@@ -112,20 +112,6 @@ __device__ __forceinline__ int tile_dot(const uint4 &nz, const uint4 &ng, const 
 #pragma unroll
     for (int d = 0; d < 4; ++d) s = bcnt_add(word(ng, d), s);
     return s;
-}
-
-// Q1_0: 2 * pos_sum - block_total; block_total = sum_b w_b popcount(X_b) is
-// uniform, so the scalar unit counts it.
-__device__ __forceinline__ int tile_q1_dot(const uint4 &bits, const XPlanes &xp) {
-    const int pos = weighted_plane_count([&](int b, int d) { return word(bits, d) & xp.w[b][d]; });
-    int total = 0;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const int t = __builtin_popcount(xp.w[b][0]) + __builtin_popcount(xp.w[b][1]) +
-                      __builtin_popcount(xp.w[b][2]) + __builtin_popcount(xp.w[b][3]);
-        total += (b == 7) ? -t * 128 : t * (1 << b);
-    }
-    return 2 * pos - total;
 }
 
 // v summed with the lane 16 (SWAP32 false) or 32 (true) apart, in every lane:
@@ -272,26 +258,23 @@ __global__ void ternary_rows_kernel(const uint8_t *__restrict__ planes,
 // true: y += W x; the runs of a tile add in any order, exactly, since
 // integer addition is associative).  Rows past `rows` (the tile's zero
 // padding) are computed like the others and not stored.
-template <bool Q1, bool ACC>
-__global__ void ternary_tile_kernel(const uint8_t *__restrict__ planes,
-                                    const int16_t *__restrict__ pscales,
-                                    const int8_t *__restrict__ x, int rows, int groups, int cg,
-                                    int nruns, int shift, int64_t *__restrict__ y) {
+__global__ void ternary_acc_kernel(const uint8_t *__restrict__ planes,
+                                   const int16_t *__restrict__ pscales,
+                                   const int8_t *__restrict__ x, int rows, int groups, int cg,
+                                   int nruns, int shift, int64_t *__restrict__ y) {
     __shared__ int64_t part[16][64];
     const int nwaves = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    // the storing kernel's one run per tile needs no division
-    const int tile = ACC ? (int)blockIdx.x / nruns : (int)blockIdx.x;
-    const int g0 = ACC ? ((int)blockIdx.x - tile * nruns) * cg : 0;
-    const int g1 = ACC ? min(groups, g0 + cg) : groups;
+    const int tile = (int)blockIdx.x / nruns;
+    const int g0 = ((int)blockIdx.x - tile * nruns) * cg;
+    const int g1 = min(groups, g0 + cg);
     const int row = tile * 64 + lane;
     const bool live = row < rows;
     // this tile's planes, its four 16-row scale blocks, and x: the group
     // steps a uniform (scalar) offset, the lane's part is fixed
-    constexpr uint32_t kBlk = Q1 ? 1024 : 2048;
     const __amdgpu_buffer_rsrc_t rp =
-        buffer_rsrc(planes + (size_t)tile * groups * kBlk, (uint32_t)groups * kBlk);
+        buffer_rsrc(planes + (size_t)tile * groups * 2048, (uint32_t)groups * 2048);
     const __amdgpu_buffer_rsrc_t rs =
         buffer_rsrc(pscales + (size_t)tile * 64 * groups, (uint32_t)groups * 128);
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)groups * 128);
@@ -301,13 +284,12 @@ __global__ void ternary_tile_kernel(const uint8_t *__restrict__ planes,
         // padding rows (lane >= rows - 64 * tile) read the tile's zero rows
         const int xa = buffer_load_i8(rx, lane, g * 128);
         const int xb = buffer_load_i8(rx, 64 + lane, g * 128);
-        const uint4 nz = buffer_load_stream16(rp, 16 * lane, g * kBlk);
-        uint4 ng = make_uint4(0, 0, 0, 0);
-        if constexpr (!Q1) ng = buffer_load_stream16(rp, 1024 + 16 * lane, g * kBlk);
+        const uint4 nz = buffer_load_stream16(rp, 16 * lane, g * 2048);
+        const uint4 ng = buffer_load_stream16(rp, 1024 + 16 * lane, g * 2048);
         const int sc = buffer_load_i16(rs, sc_off, g * 32);
         XPlanes xp;
         ballot_planes(xa, xb, xp);
-        const int s = Q1 ? tile_q1_dot(nz, xp) : tile_dot(nz, ng, xp);
+        const int s = tile_dot(nz, ng, xp);
         acc += (int64_t)(__mul24(s, sc) >> shift);   // |s * sc| <= 2^29; >> = floor
     }
     part[wave][lane] = acc;
@@ -315,11 +297,7 @@ __global__ void ternary_tile_kernel(const uint8_t *__restrict__ planes,
     if (threadIdx.x < 64) {
         int64_t tot = 0;
         for (int w = 0; w < nwaves; ++w) tot += part[w][threadIdx.x];
-        if (live) {
-            if constexpr (ACC) atomicAdd(reinterpret_cast<unsigned long long *>(y + row),
-                                         (unsigned long long)tot);
-            else y[row] = tot;
-        }
+        if (live) atomicAdd(reinterpret_cast<unsigned long long *>(y + row), (unsigned long long)tot);
     }
 }
 
@@ -583,8 +561,7 @@ static bool launch_pipe(const PipeCfg &c, hipStream_t st, const uint8_t *p, cons
 }
 
 struct TernaryCfg {
-    bool tile;            // tile mapping (ternary_tile_kernel) with `waves` wavefronts
-    int rows_per_block;   // R: 32 or 16 (64 for the tile mapping)
+    int rows_per_block;   // R: 32 or 16
     int waves;            // wavefronts per block, 1..16
     int maxg;             // groups per slice and round held in registers: 1 or 2
 };
@@ -616,13 +593,6 @@ static int32_t launch_ternary(const TernaryCfg &c, const uint8_t *planes, const 
     const int groups = (int)(k / kGroup);
     const int shift = frac > 31 ? 31 : frac;   // |scale*s| < 2^31: shift 31 is floor
     const int n = (int)rows;
-    if (c.tile) {
-        hipLaunchKernelGGL((ternary_tile_kernel<Q1, false>), dim3((unsigned)(pad64(rows) / 64)),
-                           dim3(c.waves * 64), 0, st, planes, scales, x, n, groups, groups, 1,
-                           shift, y);
-        BS_LAUNCH_CHECK();
-        return BS_OK;
-    }
     bool ok;
     switch (c.rows_per_block) {
     case 32: ok = launch_r<32, Q1>(c.maxg, c.waves, st, planes, scales, x, n, groups, shift, y); break;
@@ -634,49 +604,33 @@ static int32_t launch_ternary(const TernaryCfg &c, const uint8_t *planes, const 
     return BS_OK;
 }
 
-// Launch shape, from sweeps of every (mapping, rows per block, wavefronts,
-// groups per slice) on MI355X with cold weights.  The tile mapping (16
-// wavefronts, one workgroup per 64-row tile) for tall matrices: at least
-// 150 tiles with up to 32 groups per row (Q1_0: 30), or at least 200 tiles
-// with up to 64 groups (Q1_0: 48).  Otherwise row blocks with one group per
-// slice and round (more rounds measured faster than more groups in flight
-// per round): 16-row blocks with 8 wavefronts up to 32 groups; beyond that
-// 32-row blocks with 16 wavefronts for 5000 rows or more (Q1_0, whose group
-// is half the bytes: two groups per slice), else 16-row blocks with 16.
-static TernaryCfg choose_cfg(int64_t rows, int64_t k, bool q1) {
-    const int64_t groups = k / kGroup, tiles = pad64(rows) / 64;
+// Launch shape of the row-block kernel, which takes K > 16384 (more than the
+// pipelined kernel's 128 groups), from sweeps on MI355X with cold weights:
+// one group per slice and round (more rounds measured faster than more
+// groups in flight per round), 32-row blocks of 16 wavefronts from 5000 rows
+// (Q1_0, whose group is half the bytes: two groups per slice and round),
+// else 16-row blocks of 16.
+static TernaryCfg choose_cfg(int64_t rows, bool q1) {
     TernaryCfg c;
-    c.tile = false;
-    c.maxg = 1;
-    const int64_t tile_groups = q1 ? 30 : 32, tall_groups = q1 ? 48 : 64;
-    if (tiles >= 150 && (groups <= tile_groups || (tiles >= 200 && groups <= tall_groups))) {
-        c.tile = true;
-        c.waves = (int)(groups < 16 ? groups : 16);
-        c.rows_per_block = 64;
-        return c;
-    }
-    if (groups <= 32) {
-        c.rows_per_block = 16;
-        c.waves = 8;
-    } else if (rows >= 5000) {
+    if (rows >= 5000) {
         c.rows_per_block = 32;
         c.waves = 16;
         c.maxg = q1 ? 2 : 1;
     } else {
         c.rows_per_block = 16;
         c.waves = 16;
+        c.maxg = 1;
     }
     return c;
 }
 
 // y += W x: the tile mapping, split over runs of cg groups per workgroup.
-// Tall matrices with few groups keep one run per tile (cg = K/128, the
-// store-free tile kernel's shape); otherwise runs of four groups, four
+// Tall matrices with few groups keep one run per tile (cg = K/128);
+// otherwise runs of four groups, four
 // wavefronts (one group each), when that still gives 150+ workgroups, else
 // runs of one group and one wavefront (sweeps on MI355X: 2560x2560 2.70 us,
 // 2560x6912 3.48 us, 6912x2560 3.32 us, against 2.96 / 3.85 / 3.55 us for the
 // storing kernel).  Runs grow so the grid stays below 2^24 workgroups.
-template <bool Q1>
 static int32_t launch_acc(const uint8_t *planes, const int16_t *scales, const int8_t *x,
                           int64_t rows, int64_t k, int32_t frac, int64_t *y, hipStream_t st) {
     const int64_t groups = k / kGroup, tiles = pad64(rows) / 64;
@@ -692,7 +646,7 @@ static int32_t launch_acc(const uint8_t *planes, const int16_t *scales, const in
         waves = cg < 16 ? cg : 16;
     }
     const int64_t nruns = (groups + cg - 1) / cg;
-    hipLaunchKernelGGL((ternary_tile_kernel<Q1, true>), dim3((unsigned)(tiles * nruns)),
+    hipLaunchKernelGGL(ternary_acc_kernel, dim3((unsigned)(tiles * nruns)),
                        dim3((unsigned)waves * 64), 0, st, planes, scales, x, (int)rows,
                        (int)groups, (int)cg, (int)nruns, shift, y);
     BS_LAUNCH_CHECK();
@@ -728,7 +682,7 @@ extern "C" int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales,
         BS_LAUNCH_CHECK();
         return BS_OK;
     }
-    return launch_ternary<false>(choose_cfg(rows, k, false), planes, scales, x, rows, k, frac, y,
+    return launch_ternary<false>(choose_cfg(rows, false), planes, scales, x, rows, k, frac, y,
                                  (hipStream_t)stream);
 }
 
@@ -744,7 +698,7 @@ extern "C" int32_t bs_q1_gemv(const uint8_t *bits, const int16_t *scales, const 
         BS_LAUNCH_CHECK();
         return BS_OK;
     }
-    return launch_ternary<true>(choose_cfg(rows, k, true), bits, scales, x, rows, k, frac, y,
+    return launch_ternary<true>(choose_cfg(rows, true), bits, scales, x, rows, k, frac, y,
                                 (hipStream_t)stream);
 }
 
@@ -752,5 +706,5 @@ extern "C" int32_t bs_ternary_gemv_acc(const uint8_t *planes, const int16_t *sca
                                        const int8_t *x, int64_t rows, int64_t k, int32_t frac,
                                        int64_t *y, void *stream) {
     if (int32_t st = gemv_check(planes, scales, x, rows, k, frac, y)) return st;
-    return launch_acc<false>(planes, scales, x, rows, k, frac, y, (hipStream_t)stream);
+    return launch_acc(planes, scales, x, rows, k, frac, y, (hipStream_t)stream);
 }

@@ -2,8 +2,9 @@
 the oracle.  The method is an approximation whose every rounding is
 specified, so both sides compute the same integers: (sign, L) must match
 bit for bit on every row, at every internal precision.  Sizes span several
-tiles and workgroups, ragged rows, the split into a second kernel, the
-largest K, and the degenerate inputs of the LNS8 path."""
+tiles and workgroups, ragged rows, K split over workgroups (finished by the
+last workgroup of each tile), the largest K, and the degenerate inputs of
+the LNS8 path."""
 import numpy as np
 import pytest
 

@@ -86,9 +86,9 @@ def test_lns8_adversarial(case):
 
 @pytest.mark.parametrize("rows,k", [(64, 65408), (200, 8192), (2000, 128), (70, 2048)])
 def test_lns8_split_and_long_rows(rows, k):
-    """K split over several workgroups per tile (partials combined by a
-    second kernel) and the largest K whose |A| fits int32; 2000 x 128 keeps
-    one wavefront per tile."""
+    """K split over several workgroups per tile (partials combined by the
+    last workgroup of each tile) and the largest K whose |A| fits int32;
+    2000 x 128 keeps one wavefront per tile."""
     check(*synth.lns8(rows, k, seed=k + rows))
 
 

@@ -48,6 +48,13 @@ def test_mapping_edges(rows, k):
     check(*synth.q1(rows, k, rows ^ k))
 
 
+@pytest.mark.parametrize("rows,k", [(4999, 16512), (5000, 16512), (5001, 20480)])
+def test_row_block_kernel_beyond_128_groups(rows, k):
+    """K > 16384 takes the row-block kernel: 16-row blocks below 5000 rows,
+    32-row blocks with two groups per slice and round from 5000."""
+    check(*synth.q1(rows, k, rows + k))
+
+
 @pytest.mark.parametrize("rows,k", [(4096, 3072), (4097, 3072), (4097, 128), (1, 128),
                                     (13824, 2560), (6399, 5120), (6400, 5120), (300, 16384),
                                     (1, 16384), (2000, 16512), (9, 1152), (17, 4224)])

@@ -61,11 +61,9 @@ def test_fused_launches(rows, seed):
                                     (13800, 2560), (12800, 640), (14000, 128),
                                     (9536, 4096), (9600, 4096), (9601, 4224), (12800, 8192),
                                     (12737, 8320), (4999, 4224), (5000, 4224)])
-def test_tile_mapping_edges(rows, k):
-    """Around the launch-shape bounds: the tile mapping from 150 tiles (149
-    and 150 at 32 groups, 33 groups at 151 tiles) and at 200 tiles up to 64
-    groups (64 and 65), the row-block shapes either side of 5000 rows beyond
-    32 groups, ragged last tiles and blocks, fewer groups than wavefronts."""
+def test_tall_shapes(rows, k):
+    """Tall shapes with 1 to 65 groups around 150 and 200 tiles and 5000 rows:
+    ragged last tiles and blocks, fewer groups than wavefronts."""
     check(*synth.ternary(rows, k, seed=rows ^ k, p_zero=1 / 3, act="uniform127"))
 
 
@@ -91,6 +89,13 @@ def test_pipelined_wavefront_counts(groups, rows):
     """Every wavefront count and groups-per-slice of the pipelined kernel
     (padding slots past K, partly filled last rounds)."""
     check(*synth.ternary(rows, 128 * groups, seed=groups * 7 + rows, p_zero=0.4))
+
+
+@pytest.mark.parametrize("rows,k", [(4999, 16512), (5000, 16512), (5001, 20480)])
+def test_row_block_kernel_beyond_128_groups(rows, k):
+    """K > 16384 takes the row-block kernel: 16-row blocks below 5000 rows,
+    32-row blocks from 5000 (ragged last block)."""
+    check(*synth.ternary(rows, k, seed=rows + k, p_zero=1 / 3, act="uniform127"))
 
 
 @pytest.mark.parametrize("seed", range(5))
