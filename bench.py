@@ -165,13 +165,19 @@ class Harness:
 
     def ceiling(self, pool, nbytes, n, block=None):
         """Best back-to-back time of a plain read of `nbytes` from each pool
-        buffer in turn (1, 2, 4 or 8 16-byte loads per thread)."""
+        buffer in turn: one pass with 2, 4 or 8 16-byte loads per thread, or
+        a fixed grid of 512, 1024 or 2048 workgroups striding over it."""
         best = None
         for u in (2, 4, 8):
             sink = self.probe.sink_for(nbytes, u, self.dev)
             us = self.per_launch(lambda i: self.probe.read(pool[i % len(pool)], nbytes, u, sink,
                                                            self.stream), n, block=block)
             best = us if best is None else min(best, us)
+        sink = self.torch.empty(2048 * 256, dtype=self.torch.int64, device=self.dev)
+        for blocks in (512, 1024, 2048):
+            us = self.per_launch(lambda i: self.probe.read_strided(
+                pool[i % len(pool)], nbytes, blocks, sink, self.stream), n, block=block)
+            best = min(best, us)
         return best
 
 

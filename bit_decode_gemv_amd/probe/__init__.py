@@ -26,6 +26,8 @@ def lib():
         h.bs_probe_read_sink_count.argtypes = [ctypes.c_uint64, ctypes.c_int32]
         h.bs_probe_read.restype = ctypes.c_int32
         h.bs_probe_read.argtypes = [P, ctypes.c_uint64, ctypes.c_int32, P, P]
+        h.bs_probe_read_strided.restype = ctypes.c_int32
+        h.bs_probe_read_strided.argtypes = [P, ctypes.c_uint64, ctypes.c_int32, P, P]
         h.bs_probe_empty.restype = ctypes.c_int32
         h.bs_probe_empty.argtypes = [ctypes.c_int32, ctypes.c_int32, P]
         _lib = h
@@ -49,6 +51,20 @@ def read(src, nbytes: int, per_thread: int, sink, stream):
                              ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
     if rc != 0:
         raise RuntimeError("bs_probe_read: status %d" % rc)
+
+
+def read_strided(src, nbytes: int, blocks: int, sink, stream):
+    """Stream ``nbytes`` of ``src`` once with a fixed grid of ``blocks``
+    workgroups (bs_probe_read_strided); ``sink`` holds blocks * 256 int64."""
+    if src.numel() * src.element_size() < nbytes:
+        raise ValueError("src holds fewer than %d bytes" % nbytes)
+    if sink.numel() < blocks * 256:
+        raise ValueError("sink holds fewer than %d values" % (blocks * 256))
+    rc = lib().bs_probe_read_strided(ctypes.c_void_p(src.data_ptr()), int(nbytes), int(blocks),
+                                     ctypes.c_void_p(sink.data_ptr()),
+                                     ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise RuntimeError("bs_probe_read_strided: status %d" % rc)
 
 
 def empty(blocks: int, threads: int, stream):

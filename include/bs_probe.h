@@ -40,6 +40,17 @@ int32_t bs_probe_read(const void *src, uint64_t bytes, int32_t per_thread, int64
                       void *stream);
 
 /*
+ * bs_probe_read_strided -- the same read with a fixed grid: `blocks`
+ * workgroups of 256 threads (1 <= blocks <= 65536), each reading 32 KB
+ * contiguous per step and striding by the grid's span, then one int64 per
+ * thread to `sink` (blocks * 256 of them).  For large buffers, where the
+ * one-pass grid grows with the bytes.  Same limits on src and bytes.
+ * Errors: -1 (NULL), -3 (bytes, blocks, alignment), -5 (launch).
+ */
+int32_t bs_probe_read_strided(const void *src, uint64_t bytes, int32_t blocks, int64_t *sink,
+                              void *stream);
+
+/*
  * bs_probe_empty -- launch `blocks` workgroups of `threads` threads
  * (1 <= blocks <= 2^20, threads 64..1024, a multiple of 64) that do nothing.
  * Errors: -3 (sizes), -5 (launch).

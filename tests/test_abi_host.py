@@ -35,7 +35,8 @@ def test_probe_library_exports_its_header():
     from bit_decode_gemv_amd import probe
     lib = probe.lib()
     names = sorted(set(re.findall(r"\b(bs_probe_[a-z0-9_]+)\s*\(", open(probe.HEADER).read())))
-    assert names == ["bs_probe_empty", "bs_probe_read", "bs_probe_read_sink_count"]
+    assert names == ["bs_probe_empty", "bs_probe_read", "bs_probe_read_sink_count",
+                     "bs_probe_read_strided"]
     for name in names:
         assert hasattr(lib, name), name
     assert lib.bs_probe_read_sink_count(4096 * 8, 8) == 256
@@ -44,6 +45,12 @@ def test_probe_library_exports_its_header():
     assert lib.bs_probe_read_sink_count((1 << 31) - 15, 8) == -3
     assert lib.bs_probe_read_sink_count(4096, 3) == -3
     assert lib.bs_probe_read(None, 4096, 8, FAKE, None) == -1
+    assert lib.bs_probe_read_strided(None, 4096, 512, FAKE, None) == -1
+    assert lib.bs_probe_read_strided(FAKE, 0, 512, FAKE, None) == -3
+    assert lib.bs_probe_read_strided(FAKE, 1 << 31, 512, FAKE, None) == -3
+    assert lib.bs_probe_read_strided(FAKE, 4096, 0, FAKE, None) == -3
+    assert lib.bs_probe_read_strided(FAKE, 4096, 65537, FAKE, None) == -3
+    assert lib.bs_probe_read_strided(ctypes.c_void_p((1 << 20) + 8), 4096, 512, FAKE, None) == -3
     assert lib.bs_probe_empty(0, 64, None) == -3
     assert lib.bs_probe_empty(1, 100, None) == -3
 
