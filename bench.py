@@ -83,7 +83,8 @@ RESIDUAL = ("o", "down")
 # marker ids of the measured blocks (empty-kernel grid = (4096 + id) x 64)
 MARKER_BASE = 4096
 BLOCKS = ["step", "roofline_graph", "context_floor", "ceiling_scrub",
-          "f1_fused_step", "lmhead", "lns8", "flns", "q1", "edges", "lmhead_ceiling"]
+          "f1_fused_step", "lmhead", "lns8", "flns", "q1", "edges", "lmhead_ceiling",
+          "context_stream"]
 SHAPE_BLOCKS = ["gemv_%dx%d" % s for s in IN_RANGE + REPORTED]
 SWEEP_BLOCKS = ["f1_reuse_%s_n%d" % (p, n) for p in ("ternary", "direct", "popcount")
                 for n in (1, 8, 32, 128, 512, 2048, 8192)]
@@ -718,12 +719,25 @@ def run_extras(torch, bs, synth, dev, H):
 
 
 def context(torch, H):
-    """The empty-kernel floor: back-to-back launches of a kernel that does
-    nothing, at two grid sizes."""
+    """The empty-kernel floor (back-to-back launches of a kernel that does
+    nothing, at two grid sizes) and the streaming-read ceiling of the GPU: a
+    plain read of 1 GiB (four times the Infinity Cache) by a fixed grid."""
     out = {}
     for blocks, threads in ((256, 256), (1024, 1024)):
         out["launch_floor_us_%dx%d" % (blocks, threads)] = round(H.per_launch(
             lambda i: H.probe.empty(blocks, threads, H.stream), 200, block="context_floor"), 3)
+    nbytes = 1 << 30
+    big = torch.empty(nbytes, dtype=torch.uint8, device=H.dev)
+    sink = torch.empty(8192 * 256, dtype=torch.int64, device=H.dev)
+    best = None
+    for blocks in (1024, 2048, 4096, 8192):
+        us = H.per_launch(lambda i: H.probe.read_strided(big, nbytes, blocks, sink, H.stream), 4,
+                          block="context_stream")
+        best = us if best is None else min(best, us)
+    out["stream_read_1GiB_us"] = round(best, 2)
+    out["stream_read_1GiB_GBps"] = round(nbytes / best / 1e3, 1)
+    out["stream_read_1GiB_frac_hbm_peak"] = round(nbytes / best / 1e3 / HBM_PEAK_GBS, 4)
+    del big, sink
     return out
 
 
