@@ -202,13 +202,20 @@ def packed_pool(torch, bs, synth, dev, rows, k, min_bytes, seed=0, max_copies=No
 # ---------------------------------------------------------------- CPU side
 
 def _cpu_model():
+    """/proc/cpuinfo's model name, with the family and model numbers (a
+    virtual machine may report only a generic name) and the logical CPUs."""
+    vals = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = line.split(":", 1)
+                vals.setdefault(k.strip(), v.strip())
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = vals.get("model name", "unknown")
+    return "%s (family %s, model %s; %d logical CPUs, %d in this process's affinity)" % (
+        name, vals.get("cpu family", "?"), vals.get("model", "?"), os.cpu_count() or 0,
+        len(os.sched_getaffinity(0)))
 
 
 def _baseline_threads():
