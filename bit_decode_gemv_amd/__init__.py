@@ -319,7 +319,10 @@ def q1_gemv(bits, scales, x, rows: int, k: int, frac: int = 0, out=None, stream=
 
 def lns8_phase_gemv(planes, x_lns8, rows: int, k: int, path: int = LNS8_DIRECT, acc=None,
                     s=True, workspace=None, stream=None):
-    """(acc int32[rows][8], s float64[rows] or None)."""
+    """(acc int32[rows][8], s float64[rows] or None).  ``workspace``, when
+    given, is a uint8 device tensor of at least bs_lns8_workspace_bytes that
+    is zero before its first use (every call leaves it zero); by default a
+    zero-filled one is kept per device."""
     torch = _torch()
     dev = x_lns8.device
     if acc is None:
@@ -348,7 +351,10 @@ def lns8_phase_gemv(planes, x_lns8, rows: int, k: int, path: int = LNS8_DIRECT, 
 def flns_phase_gemv(planes, x_lns8, rows: int, k: int, frac_bits: int, table, scale_d: int = 1,
                     out=None, workspace=None, stream=None):
     """out int32[rows][2] = (sign, L) of the pure fractional-LNS reduction;
-    ``table`` is the device copy of ``flns_table(frac_bits)``."""
+    ``table`` is the device copy of ``flns_table(frac_bits)``.  ``workspace``,
+    when given, is a uint8 device tensor of at least bs_flns_workspace_bytes
+    that is zero before its first use (every call leaves it zero); by
+    default a zero-filled one is kept per device."""
     torch = _torch()
     dev = x_lns8.device
     if out is None:
