@@ -109,14 +109,15 @@ int32_t bs_ternary_pack_scales(const int16_t *scales, int64_t rows, int64_t k,
  *           bs_ternary_scales_count of them, 2-byte aligned
  *   x       device, int8[k] activations (two's complement, -128 allowed),
  *           8-byte aligned
- *   rows    1 .. 2^31 - 64 (else BS_E_SHAPE);  k >= 128, k % 128 == 0,
- *           k <= 2^24
+ *   rows    1 .. 2^31 - 64 (else BS_E_SHAPE);  k >= 128, k % 128 == 0
+ *           (else BS_E_SHAPE), k <= 2^24 (else BS_E_OVERFLOW)
  *   frac    0..62: fractional bits of the fixed-point scale; the floor is
  *           applied per group, before the sum over groups
  *   y       device, int64[rows], overwritten, 8-byte aligned
  *   stream  hipStream_t (as void*) the kernel is enqueued on
  * No scratch memory: each workgroup owns complete rows.
- * Errors: BS_E_NULL, BS_E_SHAPE, BS_E_RANGE (frac), BS_E_ALIGN, BS_E_HIP.
+ * Errors: BS_E_NULL, BS_E_SHAPE, BS_E_OVERFLOW (k), BS_E_RANGE (frac),
+ *   BS_E_ALIGN, BS_E_HIP.
  */
 int32_t bs_ternary_gemv(const uint8_t *planes, const int16_t *scales, const int8_t *x,
                         int64_t rows, int64_t k, int32_t frac, int64_t *y, void *stream);
