@@ -57,7 +57,9 @@ def _child(sanitized, args, tag):
     logs = d / ("logs_" + tag)
     logs.mkdir()
     env = dict(os.environ)
-    env.update({"LD_PRELOAD": asan, "BS_SANITIZED_ORACLE": orc, "BS_SANITIZED_HOST": host,
+    # ASan's runtime must come first; whatever the environment preloads stays
+    preload = asan + (":" + env["LD_PRELOAD"] if env.get("LD_PRELOAD") else "")
+    env.update({"LD_PRELOAD": preload, "BS_SANITIZED_ORACLE": orc, "BS_SANITIZED_HOST": host,
                 # the interpreter and its extension modules are not built with
                 # ASan: leak reports at exit would be theirs
                 "ASAN_OPTIONS": "detect_leaks=0:exitcode=86:log_path=%s/asan" % logs,
