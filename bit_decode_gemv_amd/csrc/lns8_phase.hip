@@ -7,18 +7,17 @@
 // product adds +-(1 << E4) to one of eight int32 accumulators A[L3]; the row
 // result S = 2^-9 * sum_p A[p] * F[p] is materialised once per row.
 //
-// Mapping: a workgroup owns one 64-row tile (lane j of every wavefront =
-// row 64*tile + j, so the activation codes are uniform across a wavefront)
-// and a run of 128-weight groups, one or more per wavefront.  Two
-// reductions, identical in result:
-//   DIRECT   -- per product position (uniform), route +-(1 << E4) to A[L3];
-//   POPCOUNT -- per 64-lane tile, enumerate the active states s with a
-//               ballot loop (AMD has no match-any: find the first remaining
-//               lane, broadcast its code, ballot the lanes holding the same
-//               code), then C_s = popcount(A_s & W_nz) - 2 popcount(A_s & W_nz
-//               & (sign ^ W_neg)) and A[s & 7] += C_s << (s >> 3): the
-//               histogram H[phase][band] folded into A as it is produced.
-// The wavefronts' A[8] meet in LDS (integer addition is associative, so the
+// Two reductions, identical in result:
+//   DIRECT   -- per product position, route +-(1 << E4) to A[L3];
+//   POPCOUNT -- per state s (a code 1..127: the positions holding it), the
+//               signed count C_s of the row's nonzero weights there, added
+//               as C_s << band into A[phase]: the histogram H[phase][band]
+//               folded into A as it is produced.
+//
+// DIRECT mapping: a workgroup owns one 64-row tile (lane j of every
+// wavefront = row 64*tile + j, so the activation codes are uniform across a
+// wavefront) and a run of 64-position units, one or more per wavefront.  The
+// wavefronts' A[8] meet in LDS (integer addition is associative, so the
 // order is free).  When K is split over several workgroups per tile (64
 // tiles alone would leave most of the GPU idle), each workgroup writes its
 // partial A to the workspace with agent-scope stores (coherent across the
@@ -26,9 +25,13 @@
 // stores), waits for them to complete, and counts itself done on the tile's
 // counter with an agent-scope atomic add; the workgroup that finds itself
 // last reads the partials with agent-scope loads, sums them, writes A and S
-// and returns the counter and the partials to zero for the next call.  One launch, no spin,
-// and no L2 write-back or invalidate: a release/acquire pair on the counter
-// (buffer_wbl2 + buffer_inv) measured 19.5 us per call instead of 10-11.
+// and returns the counter and the partials to zero for the next call.  One
+// launch, no spin, and no L2 write-back or invalidate: a release/acquire
+// pair on the counter (buffer_wbl2 + buffer_inv) measured 19.5 us per call
+// instead of 10-11.
+//
+// POPCOUNT mapping (lns8_pc_kernel below): a workgroup owns 16 rows and all
+// of K, with the state sets built once per workgroup in LDS; no workspace.
 #include "kcommon.h"
 
 namespace bs {
@@ -41,22 +44,30 @@ __device__ constexpr double kF[8] = {
 
 // S = 2^-9 * sum_p A[p] F[p], evaluated exactly and rounded once: every F[p]
 // is an integer multiple of 2^-53 (F[p] < 2), so the sum is the integer
-// sum_p A[p] * (F[p] * 2^53) (below 2^88, int128) times 2^-62.  The int128 to
-// binary64 conversion rounds to nearest even; the power-of-two scaling is
-// exact.
+// t = sum_p A[p] * (F[p] * 2^53) (below 2^88) times 2^-62.  With F[p] * 2^53 =
+// Fh * 2^27 + Fl (both below 2^27) the two int64 sums h = sum A Fh and l =
+// sum A Fl (each below 2^61) give t = h * 2^27 + l exactly; regrouped as
+// t = a + b with a = (g >> 26) * 2^53 and b < 2^53, g = h + (l >> 27), both
+// are exact doubles, so the one rounded addition a + b is t rounded to nearest
+// even.  The power-of-two scaling is exact (|t| >= 1 or t = 0).
 __device__ __forceinline__ double materialize(const int A[8]) {
-    __int128 t = 0;
+    int64_t h = 0, l = 0;
 #pragma unroll
-    for (int p = 0; p < 8; ++p)
-        t += (__int128)A[p] * (__int128)(int64_t)(kF[p] * 9007199254740992.0);
-    return ldexp((double)t, -62);
+    for (int p = 0; p < 8; ++p) {
+        const int64_t f = (int64_t)(kF[p] * 9007199254740992.0);
+        h += (int64_t)A[p] * (int)(f >> 27);
+        l += (int64_t)A[p] * (int)(f & ((1 << 27) - 1));
+    }
+    const int64_t g = h + (l >> 27);
+    const double a = (double)(g >> 26) * 9007199254740992.0;
+    const double b = (double)(((g & ((1 << 26) - 1)) << 27) | (l & ((1 << 27) - 1)));
+    return ldexp(a + b, -62);
 }
 
-// One unit of work: 64 positions (half h of group g) for the wavefront's 64
-// rows.  Lane j holds row j's W_nonzero / W_negative bits of those positions
-// (bit i = position 64h + i) and, for the ballots, the activation byte of
-// position 64h + j.
-template <int PATH>
+// One unit of work of DIRECT: 64 positions (half h of group g) for the
+// wavefront's 64 rows.  Lane j holds row j's W_nonzero / W_negative bits of
+// those positions (bit i = position 64h + i) and, for the ballots, the
+// activation byte of position 64h + j.
 __device__ __forceinline__ void lns8_unit(const uint8_t *__restrict__ planes,
                                           const uint8_t *__restrict__ x, int tile, int groups,
                                           int u, int lane, int A[8]) {
@@ -64,82 +75,40 @@ __device__ __forceinline__ void lns8_unit(const uint8_t *__restrict__ planes,
     const size_t blk = (size_t)tile * groups + g;
     const uint2 nzv = *reinterpret_cast<const uint2 *>(planes + blk * 2048 + 16 * lane + 8 * h);
     const uint2 ngv = *reinterpret_cast<const uint2 *>(planes + blk * 2048 + 1024 + 16 * lane + 8 * h);
-    const uint64_t wnz = (uint64_t)nzv.x | ((uint64_t)nzv.y << 32);
-    const uint64_t wng = (uint64_t)ngv.x | ((uint64_t)ngv.y << 32);
     const int b = x[(size_t)g * 128 + 64 * h + lane];
     const int code = b & 0x7F;
-    if (PATH == BS_LNS8_DIRECT) {
-        // Every product is routed on its own.  Lane j first turns position
-        // j's byte into its signed weight w_j = (-1)^S1 * 2^E4 (0 for code
-        // 0); then for each phase p the positions with phase p (a ballot
-        // mask) are walked one by one, and position i adds w_i * t_i to A[p]
-        // of every row, t_i = nz_i - 2 neg_i the row's trit there (so the
-        // product sign is S1 xor [t < 0]).  The walk takes positions 0..31 and
-        // 32..63 from the two 32-bit words in turn.
-        const int mag = code ? 1 << (code >> 3) : 0;
-        const int wv = (b & 0x80) ? -mag : mag;
+    // Every product is routed on its own.  Lane j first turns position
+    // j's byte into its signed weight w_j = (-1)^S1 * 2^E4 (0 for code
+    // 0); then for each phase p the positions with phase p (a ballot
+    // mask) are walked one by one, and position i adds w_i * t_i to A[p]
+    // of every row, t_i = nz_i - 2 neg_i the row's trit there (so the
+    // product sign is S1 xor [t < 0]).  The walk takes positions 0..31 and
+    // 32..63 from the two 32-bit words in turn.
+    const int mag = code ? 1 << (code >> 3) : 0;
+    const int wv = (b & 0x80) ? -mag : mag;
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const uint64_t m = __ballot(code != 0 && (code & 7) == p);
-            int anz = 0, ang = 0;
+    for (int p = 0; p < 8; ++p) {
+        const uint64_t m = __ballot(code != 0 && (code & 7) == p);
+        int anz = 0, ang = 0;
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const uint32_t nzw = half ? nzv.y : nzv.x, ngw = half ? ngv.y : ngv.x;
-                uint32_t mh = (uint32_t)(m >> (32 * half));
-                while (mh) {
-                    const int i = __builtin_ctz(mh);
-                    mh &= mh - 1;
-                    const int w = __builtin_amdgcn_readlane(wv, 32 * half + i);
-                    // bit * w with a 24-bit multiply-add (|w| <= 2^15)
-                    anz = __mul24((int)__builtin_amdgcn_ubfe(nzw, i, 1), w) + anz;
-                    ang = __mul24((int)__builtin_amdgcn_ubfe(ngw, i, 1), w) + ang;
-                }
+        for (int half = 0; half < 2; ++half) {
+            const uint32_t nzw = half ? nzv.y : nzv.x, ngw = half ? ngv.y : ngv.x;
+            uint32_t mh = (uint32_t)(m >> (32 * half));
+            while (mh) {
+                const int i = __builtin_ctz(mh);
+                mh &= mh - 1;
+                const int w = __builtin_amdgcn_readlane(wv, 32 * half + i);
+                // bit * w with a 24-bit multiply-add (|w| <= 2^15)
+                anz = __mul24((int)__builtin_amdgcn_ubfe(nzw, i, 1), w) + anz;
+                ang = __mul24((int)__builtin_amdgcn_ubfe(ngw, i, 1), w) + ang;
             }
-            A[p] += anz - 2 * ang;
         }
-    } else {
-        // pneg: the lanes' positions whose product sign is negative, S1 xor
-        // [t < 0] where t != 0.  With t' = nz - 2 pneg (the product signs) and
-        // any position mask M, sum_{i in M} t'_i = popcount(nz & (M ^ pneg)) -
-        // popcount(pneg) (per position t'm = nz (m ^ pneg) - pneg, as in the
-        // ternary GEMV), so a state costs one bitop3 and one count per 32
-        // positions; the -popcount(pneg) terms of a phase's states add up to
-        // -popcount(pneg) * sum_s 2^band(s), whose sum the scalar unit keeps.
-        const uint64_t sign = __ballot(b >> 7);
-        const uint64_t pneg = wnz & (sign ^ wng);
-        const uint32_t nz0 = (uint32_t)wnz, nz1 = (uint32_t)(wnz >> 32);
-        uint32_t pn0 = (uint32_t)pneg, pn1 = (uint32_t)(pneg >> 32);
-        // opaque to the compiler, which would otherwise fold the nz & of
-        // pneg into nz & (M ^ sign ^ neg) and spend an xor and an and per
-        // word instead of one bitop3
-        asm volatile("" : "+v"(pn0));
-        asm volatile("" : "+v"(pn1));
-        const int npn = bcnt_add(pn1, bcnt_add(pn0, 0));
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            uint64_t rem = __ballot(code != 0 && (code & 7) == p);
-            int sum = 0;
-            uint32_t bands = 0;   // uniform: sum of 2^band over the phase's states
-            while (rem) {
-                const int first = __builtin_ctzll(rem);
-                const int st = lane_value(code, first);
-                const uint64_t as = __ballot(code == st);
-                rem &= ~as;
-                const int band = st >> 3;
-                const int c = bcnt_add(nz1 & ((uint32_t)(as >> 32) ^ pn1),
-                                       bcnt_add(nz0 & ((uint32_t)as ^ pn0), 0));
-                sum += c << band;
-                bands += 1u << band;
-            }
-            // |sum|, npn * bands <= 64 * 64 * 2^15 = 2^27
-            A[p] += sum - __mul24(npn, (int)bands);
-        }
+        A[p] += anz - 2 * ang;
     }
 }
 
 // One workgroup per (64-row tile, split): wavefront w takes the units (64
 // positions each, two per group) [(split * W + w) * upw, ... + upw).
-template <int PATH>
 __global__ __launch_bounds__(1024) void lns8_kernel(
     const uint8_t *__restrict__ planes, const uint8_t *__restrict__ x, int rows, int groups,
     int upw, int nsplit, int32_t *__restrict__ acc_out, double *__restrict__ s_out,
@@ -157,7 +126,7 @@ __global__ __launch_bounds__(1024) void lns8_kernel(
     const int u1 = min(2 * groups, u0 + upw);
 
     int A[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int u = u0; u < u1; ++u) lns8_unit<PATH>(planes, x, tile, groups, u, lane, A);
+    for (int u = u0; u < u1; ++u) lns8_unit(planes, x, tile, groups, u, lane, A);
 #pragma unroll
     for (int p = 0; p < 8; ++p) red[wave][p][lane] = A[p];
     __syncthreads();
@@ -165,8 +134,11 @@ __global__ __launch_bounds__(1024) void lns8_kernel(
     // are shared out over however many threads the workgroup has
     for (int idx = threadIdx.x; idx < 512; idx += blockDim.x) {
         const int p = idx >> 6, j = idx & 63;
+        // all sixteen reads in flight at once; wavefronts past nw (whose
+        // slots were never written) are masked out
         int t = 0;
-        for (int w = 0; w < nw; ++w) t += red[w][p][j];
+#pragma unroll
+        for (int w = 0; w < 16; ++w) t += red[w][p][j] & -(int)(w < nw);
         red[0][p][j] = t;   // wavefront 0's entry of this pair is read only here
     }
     __syncthreads();
@@ -215,6 +187,177 @@ __global__ __launch_bounds__(1024) void lns8_kernel(
             dst[0] = make_int4(T[0], T[1], T[2], T[3]);
             dst[1] = make_int4(T[4], T[5], T[6], T[7]);
             if (s_out) s_out[row] = materialize(T);
+        }
+    }
+}
+
+// POPCOUNT without a split of K.  A workgroup owns 16 rows and all of K: in
+// wavefront w, quarter q (lanes 16q..16q+15, lane = row 16 * block + (lane &
+// 15)) takes unit 4w + q of every chunk of 4 * NW units.  The state sets
+// depend on the activations alone, so per chunk the workgroup builds them
+// once in LDS: for every code 1..127 and unit of the chunk the 64-bit mask of
+// the unit's positions holding that code (code 0 is an exact zero and has no
+// state), and every unit's S1 mask.  A wavefront then walks, phase by phase,
+// the codes present in any of its four units; each lane reads its own
+// unit's mask of the code and adds C_s << band to A[phase].  With pneg =
+// nz & (S1 ^ neg), the positions whose product sign is negative, the product
+// signs are t' = nz - 2 pneg, and over any position mask M
+//   sum_{i in M} t'_i = popcount(nz & (M ^ pneg)) - popcount(pneg)
+// (per position t' m = nz (m ^ pneg) - pneg, the ternary GEMV's identity), so
+// a state costs one bitop3 and one count per 32 positions; a phase's
+// -popcount(pneg) terms add up to -popcount(pneg) * sum_s 2^band(s), and a
+// state the lane's unit lacks (M = 0) adds popcount(pneg) - popcount(pneg)
+// = 0.  The quarters meet by lane swaps, the wavefronts in LDS, and one lane
+// per row stores A and S: no workspace, no second round trip through memory.
+//
+// The mask table's rows are the states in phase-major order (row 16 * phase
+// + band for code 8 * band + phase), each holding the chunk's units plus one
+// padding slot: the presence step, where lane i reads row i, then spreads
+// its lanes over the LDS banks (rows of a whole number of bank widths would
+// put all 64 lanes on the same four banks).
+constexpr int kPcRows = 16;                 // rows per workgroup
+constexpr int kPcMaxUnits = 64;             // units per chunk at 16 wavefronts
+constexpr int kPcTabSlots = 128 * (kPcMaxUnits + 1);   // 64-bit slots
+
+__device__ __forceinline__ int add_quarters(int v) {
+    // the gfx950 lane swaps return v and the value of the partner lane
+    // (32 lanes apart, then 16), whose sum is wanted
+    const auto a = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    v = (int)a[0] + (int)a[1];
+    const auto b = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    return (int)b[0] + (int)b[1];
+}
+
+__global__ __launch_bounds__(1024) void lns8_pc_kernel(
+    const uint8_t *__restrict__ planes, const uint8_t *__restrict__ x, int rows, int groups,
+    int32_t *__restrict__ acc_out, double *__restrict__ s_out) {
+    // tab[(row * (cu + 1) + unit) * 2 + half]: the mask of the unit's
+    // positions 32 * half .. 32 * half + 31 holding the code of state row
+    __shared__ __align__(16) uint32_t tab[kPcTabSlots * 2];
+    __shared__ uint32_t sgn[kPcMaxUnits * 2];
+    __shared__ int red[16][8][kPcRows];
+    const int nw = blockDim.x >> 6;
+    const int cu = 4 * nw;                   // units per chunk
+    const int rs = cu + 1;                   // table row stride, 64-bit slots
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int ul = 4 * wave + (lane >> 4);   // this lane's unit within a chunk
+    const int row = blockIdx.x * kPcRows + (lane & 15);   // < the padded row count
+    const int tile = row >> 6, rit = row & 63;
+    const int units = 2 * groups;
+    const int k = groups * 128;
+
+    int A[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int c0 = 0; c0 < units; c0 += cu) {
+        // this lane's weights, in flight while the table is built
+        const int u = c0 + ul;
+        uint2 nzv = make_uint2(0, 0), ngv = make_uint2(0, 0);
+        if (u < units) {
+            const size_t off = ((size_t)tile * groups + (u >> 1)) * 2048 + 16 * rit + 8 * (u & 1);
+            nzv = *reinterpret_cast<const uint2 *>(planes + off);
+            ngv = *reinterpret_cast<const uint2 *>(planes + off + 1024);
+        }
+        if (c0) __syncthreads();             // the previous chunk's reads are done
+        // clear the chunk's table (128 rows of cu + 1 slots: 256 * nw + 64
+        // 16-byte stores) and masks
+        uint4 *t4 = reinterpret_cast<uint4 *>(tab);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const int j = threadIdx.x + i * blockDim.x;
+            if (j < 64 * rs) t4[j] = make_uint4(0, 0, 0, 0);
+        }
+        if ((int)threadIdx.x < 2 * cu) sgn[threadIdx.x] = 0;
+        __syncthreads();
+        // thread t: positions 4t .. 4t+3 of the chunk (unit t / 16)
+        {
+            const int t = threadIdx.x;
+            const int pos = c0 * 64 + 4 * t;
+            if (pos < k) {
+                const uint32_t v = *reinterpret_cast<const uint32_t *>(x + pos);
+                const int ut = t >> 4, bit = 4 * (t & 15);   // bit of the unit's first position
+                const int half = bit >> 5, sh = bit & 31;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int code = (v >> (8 * i)) & 0x7F;
+                    const int sr = 16 * (code & 7) + (code >> 3);   // state row
+                    if (code) atomicOr(&tab[(sr * rs + ut) * 2 + half], 1u << (sh + i));
+                }
+                const uint32_t sb = ((v >> 7) & 1) | ((v >> 14) & 2) | ((v >> 21) & 4) | ((v >> 28) & 8);
+                if (sb) atomicOr(&sgn[ut * 2 + half], sb << sh);
+            }
+        }
+        __syncthreads();
+        // the states present in the wavefront's four units, phase-major: bit
+        // 16 (p & 3) + band of pres[p >> 2]; lane i looks at row i (then
+        // 64 + i)
+        const uint2 *tab2 = reinterpret_cast<const uint2 *>(tab);
+        uint64_t pres[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const uint2 *r = tab2 + (64 * hh + lane) * rs + 4 * wave;
+            const uint2 a = r[0], b = r[1], c = r[2], d = r[3];
+            pres[hh] = __ballot((a.x | a.y | b.x | b.y | c.x | c.y | d.x | d.y) != 0);
+        }
+        const uint32_t sg0 = sgn[ul * 2], sg1 = sgn[ul * 2 + 1];
+        // pneg; kept opaque to the compiler, which would otherwise fold the
+        // nz & into nz & (M ^ S1 ^ neg) and spend an xor and an and per word
+        // instead of one bitop3
+        uint32_t pn0 = nzv.x & (sg0 ^ ngv.x), pn1 = nzv.y & (sg1 ^ ngv.y);
+        asm volatile("" : "+v"(pn0));
+        asm volatile("" : "+v"(pn1));
+        const int npn = bcnt_add(pn1, bcnt_add(pn0, 0));
+        // the state loop is bound by instruction issue (one scalar and one
+        // vector instruction per cycle per CU): the row stride multiplies on
+        // the vector unit (a per-lane copy of it), the scalar unit keeps only
+        // the band search, the bit clear and the loop test
+        const uint8_t *mrow = reinterpret_cast<const uint8_t *>(tab2 + ul);
+        int rs8v = rs * 8;
+        asm volatile("" : "+v"(rs8v));
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            uint32_t bm = (uint32_t)(pres[p >> 2] >> (16 * (p & 3))) & 0xFFFFu;   // uniform
+            // sum over the phase's states of 2^band: the band mask itself
+            const int wsum = (int)bm;
+            const uint8_t *pb = mrow + 16 * p * rs * 8;
+            int sum = 0;
+            while (bm) {
+                const int band = __builtin_ctz(bm);
+                asm("s_bitset0_b32 %0, %1" : "+s"(bm) : "s"(band));
+                const uint2 m = *reinterpret_cast<const uint2 *>(pb + __mul24(band, rs8v));
+                // two counts chained through the count-and-add instruction
+                const int c = __builtin_popcount(nzv.y & (m.y ^ pn1)) +
+                              __builtin_popcount(nzv.x & (m.x ^ pn0));
+                sum += c << band;
+            }
+            // |sum|, npn * wsum <= 64 * 2^16
+            A[p] += sum - __mul24(npn, wsum);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) A[p] = add_quarters(A[p]);
+    if (lane < kPcRows) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) red[wave][p][lane] = A[p];
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < 8 * kPcRows) {
+        const int p = threadIdx.x >> 4, r = threadIdx.x & 15;
+        int t = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) t += red[w][p][r] & -(int)(w < nw);
+        red[0][p][r] = t;   // wavefront 0's entry of this pair is read only here
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < kPcRows) {
+        const int rr = blockIdx.x * kPcRows + threadIdx.x;
+        if (rr < rows) {
+            int T[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) T[p] = red[0][p][threadIdx.x];
+            int4 *dst = reinterpret_cast<int4 *>(acc_out + (size_t)rr * 8);
+            dst[0] = make_int4(T[0], T[1], T[2], T[3]);
+            dst[1] = make_int4(T[4], T[5], T[6], T[7]);
+            if (s_out) s_out[rr] = materialize(T);
         }
     }
 }
@@ -291,14 +434,23 @@ extern "C" int32_t bs_lns8_phase_gemv(const uint8_t *planes, const uint8_t *x_ln
         return BS_E_ALIGN;
     if (!ws_ok(workspace, workspace_bytes, lns8_ws_bytes(rows, k))) return BS_E_WORKSPACE;
 
+    hipStream_t st = (hipStream_t)stream;
+    if (path == BS_LNS8_POPCOUNT) {
+        // 16 rows and all of K per workgroup; the workspace is not touched
+        const int64_t units = 2 * (k / kGroup);
+        const int64_t nw = units >= 64 ? 16 : (units + 3) / 4;
+        const int64_t blocks = (rows + kPcRows - 1) / kPcRows;
+        hipLaunchKernelGGL(lns8_pc_kernel, dim3((unsigned)blocks), dim3((unsigned)(nw * 64)), 0,
+                           st, planes, x_lns8, (int)rows, (int)(k / kGroup), acc, s);
+        BS_LAUNCH_CHECK();
+        return BS_OK;
+    }
     const Lns8Plan pl = lns8_plan(rows, k);
     const Lns8Ws w = lns8_ws(rows, k);
-    hipStream_t st = (hipStream_t)stream;
     unsigned char *base = static_cast<unsigned char *>(workspace);
     int *counters = reinterpret_cast<int *>(base + w.counters);
     int *partial = reinterpret_cast<int *>(base + w.partial);
-    auto kern = path == BS_LNS8_DIRECT ? lns8_kernel<BS_LNS8_DIRECT> : lns8_kernel<BS_LNS8_POPCOUNT>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(pl.tiles * pl.nsplit)), dim3(pl.waves * 64), 0, st,
+    hipLaunchKernelGGL(lns8_kernel, dim3((unsigned)(pl.tiles * pl.nsplit)), dim3(pl.waves * 64), 0, st,
                        planes, x_lns8, (int)rows, (int)pl.groups, pl.upw, pl.nsplit, acc, s,
                        counters, partial);
     BS_LAUNCH_CHECK();

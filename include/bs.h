@@ -178,7 +178,8 @@ int32_t bs_q1_gemv(const uint8_t *bits, const int16_t *scales, const int8_t *x, 
  * correctly rounded), rounded once to binary64.
  *
  *   path    BS_LNS8_DIRECT (0): per-product routing into A[L3];
- *           BS_LNS8_POPCOUNT (1): per 64-lane tile and active state s,
+ *           BS_LNS8_POPCOUNT (1): per 64-position unit and active state s
+ *           (A_s: the unit's positions holding code s),
  *           C_s = popcount(A_s & W_nonzero) - 2*popcount(A_s & W_nonzero &
  *           (sign XOR W_negative)), H[phase][band] += C_s,
  *           A[p] = sum_b H[p][b] * 2^b ([BS] sections 3.1, 4).
@@ -189,11 +190,12 @@ int32_t bs_q1_gemv(const uint8_t *bits, const int16_t *scales, const int8_t *x, 
  *   acc     device int32[rows][8], overwritten, 4-byte aligned
  *   s       device double[rows], or NULL to skip the materialisation
  *   workspace  device scratch of at least bs_lns8_workspace_bytes(rows, k)
- *           bytes, 256-byte aligned, caller-owned: when K is split over
- *           several workgroups, a counter per 64-row tile and the partial
- *           accumulators.  Zero it before its first use; every call leaves
- *           it zero again, so one workspace serves calls of any shape
- *           ordered on one stream.  Calls that may overlap need separate
+ *           bytes, 256-byte aligned, caller-owned (the same size for both
+ *           paths): when DIRECT splits K over several workgroups, a counter
+ *           per 64-row tile and the partial accumulators; POPCOUNT does not
+ *           touch it.  Zero it before its first use; every call leaves it
+ *           zero again, so one workspace serves calls of any shape ordered
+ *           on one stream.  Calls that may overlap need separate
  *           workspaces.
  * Errors: BS_E_NULL, BS_E_SHAPE, BS_E_OVERFLOW (k), BS_E_RANGE (path),
  *   BS_E_ALIGN, BS_E_WORKSPACE, BS_E_HIP.
