@@ -872,14 +872,18 @@ def counter_summary(*paths: str):
 
 def lns8_valu_summary(path: str):
     """The LNS8 counter record: every counter's mean per call of each path
-    (lns8_kernel<0> = direct, <1> = popcount) from a --pmc CSV of
-    --lns8-counter-run, keyed to the kernel source it was taken on."""
+    (lns8_kernel = direct routing, lns8_pc_kernel = popcount histogram) from a
+    --pmc CSV of --lns8-counter-run, keyed to the kernel source it was taken
+    on."""
     vals = {}
     for r in csv.DictReader(open(path)):
         name = r["Kernel_Name"]
-        if "lns8_kernel<" not in name:
+        if "lns8_pc_kernel" in name:
+            p = "popcount"
+        elif "lns8_kernel" in name:
+            p = "direct"
+        else:
             continue
-        p = "direct" if "lns8_kernel<0" in name else "popcount"
         vals.setdefault((r["Counter_Name"], p), []).append(float(r["Counter_Value"]))
     lines = ["kernel_source_sha256_16: %s" % _source_digest("lns8_phase.hip")]
     for (c, p), v in sorted(vals.items()):

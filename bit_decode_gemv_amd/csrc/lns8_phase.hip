@@ -235,7 +235,7 @@ __global__ __launch_bounds__(1024) void lns8_pc_kernel(
     // positions 32 * half .. 32 * half + 31 holding the code of state row
     __shared__ __align__(16) uint32_t tab[kPcTabSlots * 2];
     __shared__ uint32_t sgn[kPcMaxUnits * 2];
-    __shared__ int red[16][8][kPcRows];
+    __shared__ int red[8][kPcRows];          // A[p] of the 16 rows, summed with ds_add
     const int nw = blockDim.x >> 6;
     const int cu = 4 * nw;                   // units per chunk
     const int rs = cu + 1;                   // table row stride, 64-bit slots
@@ -247,9 +247,12 @@ __global__ __launch_bounds__(1024) void lns8_pc_kernel(
     const int units = 2 * groups;
     const int k = groups * 128;
 
+    for (int i = threadIdx.x; i < 8 * kPcRows; i += blockDim.x) (&red[0][0])[i] = 0;   // before the first barrier
     int A[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int c0 = 0; c0 < units; c0 += cu) {
-        // this lane's weights, in flight while the table is built
+        // this lane's weights and this thread's four activation bytes (the
+        // fill's: positions 4t .. 4t+3 of the chunk, unit t / 16), in flight
+        // while the table is cleared
         const int u = c0 + ul;
         uint2 nzv = make_uint2(0, 0), ngv = make_uint2(0, 0);
         if (u < units) {
@@ -257,6 +260,8 @@ __global__ __launch_bounds__(1024) void lns8_pc_kernel(
             nzv = *reinterpret_cast<const uint2 *>(planes + off);
             ngv = *reinterpret_cast<const uint2 *>(planes + off + 1024);
         }
+        const int pos = c0 * 64 + 4 * (int)threadIdx.x;
+        const uint32_t v = pos < k ? *reinterpret_cast<const uint32_t *>(x + pos) : 0u;
         if (c0) __syncthreads();             // the previous chunk's reads are done
         // clear the chunk's table (128 rows of cu + 1 slots: 256 * nw + 64
         // 16-byte stores) and masks
@@ -268,23 +273,20 @@ __global__ __launch_bounds__(1024) void lns8_pc_kernel(
         }
         if ((int)threadIdx.x < 2 * cu) sgn[threadIdx.x] = 0;
         __syncthreads();
-        // thread t: positions 4t .. 4t+3 of the chunk (unit t / 16)
+        // thread t: positions 4t .. 4t+3 of the chunk (unit t / 16); bytes
+        // past K read as 0 (code 0, no state)
         {
             const int t = threadIdx.x;
-            const int pos = c0 * 64 + 4 * t;
-            if (pos < k) {
-                const uint32_t v = *reinterpret_cast<const uint32_t *>(x + pos);
-                const int ut = t >> 4, bit = 4 * (t & 15);   // bit of the unit's first position
-                const int half = bit >> 5, sh = bit & 31;
+            const int ut = t >> 4, bit = 4 * (t & 15);   // bit of the unit's first position
+            const int half = bit >> 5, sh = bit & 31;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int code = (v >> (8 * i)) & 0x7F;
-                    const int sr = 16 * (code & 7) + (code >> 3);   // state row
-                    if (code) atomicOr(&tab[(sr * rs + ut) * 2 + half], 1u << (sh + i));
-                }
-                const uint32_t sb = ((v >> 7) & 1) | ((v >> 14) & 2) | ((v >> 21) & 4) | ((v >> 28) & 8);
-                if (sb) atomicOr(&sgn[ut * 2 + half], sb << sh);
+            for (int i = 0; i < 4; ++i) {
+                const int code = (v >> (8 * i)) & 0x7F;
+                const int sr = 16 * (code & 7) + (code >> 3);   // state row
+                if (code) atomicOr(&tab[(sr * rs + ut) * 2 + half], 1u << (sh + i));
             }
+            const uint32_t sb = ((v >> 7) & 1) | ((v >> 14) & 2) | ((v >> 21) & 4) | ((v >> 28) & 8);
+            if (sb) atomicOr(&sgn[ut * 2 + half], sb << sh);
         }
         __syncthreads();
         // the states present in the wavefront's four units, phase-major: bit
@@ -333,19 +335,13 @@ __global__ __launch_bounds__(1024) void lns8_pc_kernel(
             A[p] += sum - __mul24(npn, wsum);
         }
     }
+    // the quarters by lane swaps, the wavefronts by LDS atomic adds
+    // (integer addition: the order is free)
 #pragma unroll
     for (int p = 0; p < 8; ++p) A[p] = add_quarters(A[p]);
     if (lane < kPcRows) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) red[wave][p][lane] = A[p];
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < 8 * kPcRows) {
-        const int p = threadIdx.x >> 4, r = threadIdx.x & 15;
-        int t = 0;
-#pragma unroll
-        for (int w = 0; w < 16; ++w) t += red[w][p][r] & -(int)(w < nw);
-        red[0][p][r] = t;   // wavefront 0's entry of this pair is read only here
+        for (int p = 0; p < 8; ++p) atomicAdd(&red[p][lane], A[p]);
     }
     __syncthreads();
     if ((int)threadIdx.x < kPcRows) {
@@ -353,7 +349,7 @@ __global__ __launch_bounds__(1024) void lns8_pc_kernel(
         if (rr < rows) {
             int T[8];
 #pragma unroll
-            for (int p = 0; p < 8; ++p) T[p] = red[0][p][threadIdx.x];
+            for (int p = 0; p < 8; ++p) T[p] = red[p][threadIdx.x];
             int4 *dst = reinterpret_cast<int4 *>(acc_out + (size_t)rr * 8);
             dst[0] = make_int4(T[0], T[1], T[2], T[3]);
             dst[1] = make_int4(T[4], T[5], T[6], T[7]);

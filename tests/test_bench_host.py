@@ -116,11 +116,11 @@ def test_lns8_valu_record_round_trip(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     fields = ["Kernel_Name", "Counter_Name", "Counter_Value"]
     rows = []
-    for p, v in ((0, 1000.0), (1, 700.0)):
+    for name, v in (("lns8_kernel", 1000.0), ("lns8_pc_kernel", 700.0)):
         for i in range(3):
-            rows.append({"Kernel_Name": "void bs::lns8_kernel<%d>(args)" % p,
+            rows.append({"Kernel_Name": "void bs::(anonymous namespace)::%s(args)" % name,
                          "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": v + i})
-            rows.append({"Kernel_Name": "void bs::lns8_kernel<%d>(args)" % p,
+            rows.append({"Kernel_Name": "void bs::(anonymous namespace)::%s(args)" % name,
                          "Counter_Name": "SQ_WAVES", "Counter_Value": 4096})
     rows.append({"Kernel_Name": "void at::native::other", "Counter_Name": "SQ_INSTS_VALU",
                  "Counter_Value": 5.0})
