@@ -106,20 +106,6 @@ __device__ __forceinline__ void stage16(uint4 *__restrict__ dst, const uint4 *__
     }
 }
 
-// A tree node: its per-lane value and whether any leaf below it is live
-// (uniform across the wavefront).
-struct Node {
-    int e;
-    bool live;
-};
-
-template <typename E>
-__device__ __forceinline__ Node join(Node a, Node b, const E *__restrict__ lut, int S) {
-    if (!b.live) return a;
-    if (!a.live) return b;
-    return Node{lns_add(a.e, b.e, lut, S), true};
-}
-
 // Per-lane state of one Tile128: the two activation codes each lane holds
 // (positions lane and 64 + lane), the row's non-zero weights nz and its
 // negative products neg (a subset of nz) as four 32-bit words (positions
@@ -173,7 +159,8 @@ __global__ __launch_bounds__(1024) void flns_tile_kernel(
     __shared__ int last;
     __shared__ uint4 s_lut4[SMALL ? kFlnsSmallMaxEntries * 2 / 16 : 1];
     __shared__ int s_x[kTilesPerWg][8][64];
-    __shared__ uint32_t s_present[kTilesPerWg][4];   // codes present in each Tile128
+    // codes present in each Tile128, phase-major: code 8b + p at bit 16p + b
+    __shared__ uint32_t s_present[kTilesPerWg][4];
 
     const int rtile = blockIdx.x / nsplit;
     const int q = blockIdx.x - rtile * nsplit;
@@ -201,8 +188,9 @@ __global__ __launch_bounds__(1024) void flns_tile_kernel(
     // the set of codes in each Tile128, once for all the rows of the tile
     if (has_tile && half == 0) {
         const int c0 = b0 & 0x7F, c1 = b1 & 0x7F;
-        if (c0) atomicOr(&s_present[slot][c0 >> 5], 1u << (c0 & 31));
-        if (c1) atomicOr(&s_present[slot][c1 >> 5], 1u << (c1 & 31));
+        const int r0 = 16 * (c0 & 7) + (c0 >> 3), r1 = 16 * (c1 & 7) + (c1 >> 3);
+        if (c0) atomicOr(&s_present[slot][r0 >> 5], 1u << (r0 & 31));
+        if (c1) atomicOr(&s_present[slot][r1 >> 5], 1u << (r1 & 31));
     }
     __syncthreads();
     const E *lut = SMALL ? reinterpret_cast<const E *>(s_lut4)
@@ -232,37 +220,50 @@ __global__ __launch_bounds__(1024) void flns_tile_kernel(
             // the bands present in the tile (code 8b + p; code 0 is never
             // present), their populations, their fold reads back to back,
             // then the leaves
-            uint32_t live = 0;   // uniform
-#pragma unroll
-            for (int b = 0; b < 16; ++b)
-                live |= ((pres[b >> 2] >> (8 * (b & 3) + p)) & 1u) << b;
-            int cnt[16];
+            const uint32_t live = (pres[p >> 1] >> (16 * (p & 1))) & 0xFFFFu;   // uniform
+            // each live band's population and its fold read (in flight while
+            // the next bands are counted), then the leaves.  The band mask is
+            // opaque between the two passes, so each test is a bit test and a
+            // branch rather than a saved lane-mask flag.
+            int cnt[16], fv[16];
 #pragma unroll
             for (int b = 0; b < 16; ++b) {
                 cnt[b] = 0;
-                if ((live >> b) & 1) cnt[b] = population(8 * b + p, ts);
-            }
-            int fv[16];
-#pragma unroll
-            for (int b = 0; b < 16; ++b) {
                 fv[b] = 0;
-                if ((live >> b) & 1) fv[b] = s_fold[abs(cnt[b])];
-            }
-            Node v[16];
-#pragma unroll
-            for (int b = 0; b < 16; ++b) {
-                v[b] = Node{kZ, ((live >> b) & 1) != 0};
-                if (v[b].live) {
-                    const int neg = cnt[b] < 0 ? 1 : 0;
-                    const int val = 2 * (((8 * b + p) << f) + fv[b]) + neg;
-                    v[b].e = cnt[b] == 0 ? kZ : val;
+                if ((live >> b) & 1) {
+                    cnt[b] = population(8 * b + p, ts);
+                    fv[b] = s_fold[abs(cnt[b])];
                 }
             }
+            uint32_t lv = live;
+            asm volatile("" : "+s"(lv));
+            // a dead node (no live leaf below it) holds kZ, below every other
+            // value: a node with one live child takes it, which max() picks,
+            // and only a node with two live children adds them
+            int v[16];
 #pragma unroll
-            for (int w = 8; w >= 1; w >>= 1)
+            for (int b = 0; b < 16; ++b) {
+                v[b] = kZ;
+                if ((lv >> b) & 1) {
+                    const int neg = cnt[b] < 0 ? 1 : 0;
+                    const int val = 2 * (((8 * b + p) << f) + fv[b]) + neg;
+                    v[b] = cnt[b] == 0 ? kZ : val;
+                }
+            }
+            // any: bit s*m set when node m of the level (span s) has a live
+            // leaf; both: when both its children do
+            uint32_t any = lv;
 #pragma unroll
-                for (int m = 0; m < w; ++m) v[m] = join(v[2 * m], v[2 * m + 1], lut, S);
-            s_x[slot][p][lane] = v[0].live ? v[0].e : kZ;
+            for (int w = 8, s = 1; w >= 1; w >>= 1, s <<= 1) {
+                const uint32_t both = any & (any >> s);
+#pragma unroll
+                for (int m = 0; m < w; ++m) {
+                    const int a = v[2 * m], c = v[2 * m + 1];
+                    v[m] = (both >> (2 * s * m)) & 1 ? lns_add(a, c, lut, S) : max(a, c);
+                }
+                any |= any >> s;
+            }
+            s_x[slot][p][lane] = v[0];
         }
     } else {
 #pragma unroll
