@@ -92,6 +92,16 @@ def test_lns8_split_and_long_rows(rows, k):
     check(*synth.lns8(rows, k, seed=k + rows))
 
 
+@pytest.mark.parametrize("rows,k", [(17, 4224), (33, 8320), (16, 4096), (15, 256), (48, 384),
+                                    (1, 640), (129, 4096), (3, 65408)])
+def test_lns8_popcount_chunks(rows, k):
+    """The popcount kernel's geometry: 16-row workgroups (ragged last block),
+    one to sixteen wavefronts (up to 64 units per chunk), and K beyond one
+    chunk with a partly filled last chunk (4224: 64 + 2 units; 8320: 64 + 64
+    + 2; 65408: sixteen chunks).  Both paths against the oracle."""
+    check(*synth.lns8(rows, k, seed=rows * 7 + k))
+
+
 def test_lns8_max_k_extremes():
     """k = 65408 with every product +2^15 into one phase: |A| reaches
     65408 * 2^15 = 2^31 - 2^22, the int32 bound the shape limit keeps."""
