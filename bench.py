@@ -44,6 +44,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
        python bench.py --traffic-run NxK       (workload of the --pmc runs)
        python bench.py --traffic-summary FETCH.csv WRITE.csv NxK
        python bench.py --lns8-counter-run      (workload of the LNS8 --pmc runs)
+       python bench.py --flns-counter-run      (workload of the pure-LNS --pmc runs)
        python bench.py --counter-summary COUNTERS.csv
 """
 from __future__ import annotations
@@ -832,6 +833,28 @@ def lns8_counter_run(launches: int = 10):
     log("LNS8 counter run done: %d calls per path" % launches)
 
 
+def flns_counter_run(launches: int = 10):
+    """Workload for the rocprofv3 --pmc runs of the pure fractional-LNS
+    kernel: `launches` calls at 4096 x 4096 for each of f = 0 and f = 8 (LDS
+    tables) and f = 12 (device tables), on distinct weight buffers."""
+    import torch
+    import bit_decode_gemv_amd as bs
+    from bit_decode_gemv_amd import synth
+    dev = torch.device("cuda:0")
+    t8, x8 = synth.lns8(4096, 4096, 0)
+    p8 = torch.from_numpy(bs.ternary_pack(t8)).to(dev)
+    pool = [p8.clone() for _ in range(launches)]
+    xd = torch.from_numpy(x8).to(dev)
+    ws = torch.zeros(bs.lib().bs_flns_workspace_bytes(4096, 4096), dtype=torch.uint8, device=dev)
+    out = torch.empty((4096, 2), dtype=torch.int32, device=dev)
+    for f in (0, 8, 12):
+        tb = torch.from_numpy(bs.flns_table(f)).to(dev)
+        for i in range(launches):
+            bs.flns_phase_gemv(pool[i], xd, 4096, 4096, f, tb, out=out, workspace=ws)
+        torch.cuda.synchronize()
+    log("pure-LNS counter run done: %d calls at each of f = 0, 8, 12" % launches)
+
+
 SIMDS = 1024                    # 256 CUs x 4 SIMDs
 
 
@@ -951,6 +974,8 @@ def main():
                     help="HBM bytes per launch from the two counter CSVs and exit")
     ap.add_argument("--lns8-counter-run", action="store_true",
                     help="run the workload of the LNS8 --pmc runs and exit")
+    ap.add_argument("--flns-counter-run", action="store_true",
+                    help="run the workload of the pure-LNS --pmc runs and exit")
     ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
                     help="mean counters per kernel of --pmc CSVs, with their ratios, and exit")
     ap.add_argument("--lns8-valu-summary", metavar="CSV",
@@ -967,6 +992,9 @@ def main():
         return 0
     if args.lns8_counter_run:
         lns8_counter_run()
+        return 0
+    if args.flns_counter_run:
+        flns_counter_run()
         return 0
     if args.counter_summary:
         print(counter_summary(*args.counter_summary))

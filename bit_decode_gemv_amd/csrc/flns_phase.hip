@@ -231,7 +231,12 @@ __global__ __launch_bounds__(1024) void flns_tile_kernel(
                 cnt[b] = 0;
                 fv[b] = 0;
                 if ((live >> b) & 1) {
-                    cnt[b] = population(8 * b + p, ts);
+                    // the code, opaque: otherwise the compiler hoists code - 8b
+                    // out of the phase loop (sixteen registers) and spends an
+                    // add and a compare per ballot instead of one compare
+                    int code = 8 * b + p;
+                    asm volatile("" : "+s"(code));
+                    cnt[b] = population(code, ts);
                     fv[b] = s_fold[abs(cnt[b])];
                 }
             }
