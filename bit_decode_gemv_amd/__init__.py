@@ -353,8 +353,8 @@ def flns_phase_gemv(planes, x_lns8, rows: int, k: int, frac_bits: int, table, sc
     """out int32[rows][2] = (sign, L) of the pure fractional-LNS reduction;
     ``table`` is the device copy of ``flns_table(frac_bits)``.  ``workspace``,
     when given, is a uint8 device tensor of at least bs_flns_workspace_bytes
-    that is zero before its first use (every call leaves it zero); by
-    default a zero-filled one is kept per device."""
+    (reserved by the interface, never read or written); by default one is
+    kept per device."""
     torch = _torch()
     dev = x_lns8.device
     if out is None:

@@ -11,25 +11,13 @@
 // 2^f (127 + 8 log2 K + 8 log2 d) above, and each of at most 16 tree levels
 // can lower it by |km[1]| ~ N (log2 N + 0.53) < 2^(f+7) below.
 //
-// Mapping.  Kernel A: a workgroup of sixteen wavefronts per (64-row tile, run
-// of eight Tile128s), two per Tile128 with four phases each; lane j of every
-// wavefront is row 64*tile + j, so the
-// activation bytes of a Tile128 are uniform across the wavefront.  Per code
-// c the two 64-position halves are selected by ballots (scalar masks); the
-// signed population of each row is popcount(mask & positive products) -
-// popcount(mask & negative products).  A code absent from the tile is dead
-// for the whole wavefront, and so is every tree node whose leaves are all
-// dead: those adds are skipped by scalar branches.  The sixteen bands of a
-// phase reduce in registers; the eight Tile128s of the workgroup meet in
-// LDS.  With more than eight Tile128s, each workgroup writes its eight phase
-// partials per row to the workspace with agent-scope stores (written through
-// to memory, so visible to every XCD), waits for them and counts itself done
-// on the tile's counter (agent-scope atomic add); the workgroup that finds
-// itself last reads the partials back with agent-scope loads, finishes the
-// tile tree across the workgroups (lanes = workgroups of one row, shuffles),
-// then the phase tree and the scale, and returns its counter and partials
-// to zero for the next call.  No release/acquire fences: those write back
-// and invalidate the L2, which measured 3-4x slower than a second launch.
+// Mapping.  One launch, no workspace: a workgroup of sixteen wavefronts owns
+// 16 rows and all of K (flns_rows_kernel below).  Every leaf, tree node and
+// tree order is the one the brief's reduction fixes; the balanced tile tree
+// runs first in registers, then across the wavefronts in LDS, then across
+// chunks of 32 Tile128s.  Zero-valued leaves and dead subtrees enter the
+// pair adds as kZ, which every pair add with a real operand returns
+// unchanged.
 //
 // Tables.  For frac_bits <= 8 the corrections are int16 and staged in LDS
 // (at most 102,656 bytes); above, they are read from the
@@ -53,8 +41,7 @@ namespace {
 // creates a new zero.
 constexpr int kZ = -(1 << 30);
 constexpr int kZeroBelow = -(1 << 29);   // encoded values below this are zero
-constexpr int kTilesPerWg = 8;
-constexpr int kWavesPerWg = 16;   // two per Tile128, four phases each
+constexpr int kWavesPerWg = 16;
 
 // The pair add of two encoded values.  Symmetric in a, b.  On encoded
 // values max() picks the operand of larger L (equal L: equal values, or a
@@ -106,31 +93,6 @@ __device__ __forceinline__ void stage16(uint4 *__restrict__ dst, const uint4 *__
     }
 }
 
-// Per-lane state of one Tile128: the two activation codes each lane holds
-// (positions lane and 64 + lane), the row's non-zero weights nz and its
-// negative products neg (a subset of nz) as four 32-bit words (positions
-// 0-31, 32-63, 64-95, 96-127), and popcount(neg).
-struct TileState {
-    int code0, code1;
-    uint32_t nz[4], neg[4];
-    int nneg;
-};
-
-// Signed population of code c in the wavefront's Tile128 (per lane = row);
-// the caller has checked that the tile holds code c.  With the product
-// signs t' = nz - 2 neg, sum_{i in M} t'_i = popcount(nz & (M ^ neg)) -
-// popcount(neg) for any position mask M (per position t'm = nz (m ^ neg) -
-// neg): one bitop3 and one chained count per 32 positions.
-__device__ __forceinline__ int population(int c, const TileState &ts) {
-    const uint64_t m0 = __ballot(ts.code0 == c);
-    const uint64_t m1 = __ballot(ts.code1 == c);
-    int s = bcnt_add(ts.nz[0] & ((uint32_t)m0 ^ ts.neg[0]), 0);
-    s = bcnt_add(ts.nz[1] & ((uint32_t)(m0 >> 32) ^ ts.neg[1]), s);
-    s = bcnt_add(ts.nz[2] & ((uint32_t)m1 ^ ts.neg[2]), s);
-    s = bcnt_add(ts.nz[3] & ((uint32_t)(m1 >> 32) ^ ts.neg[3]), s);
-    return s - ts.nneg;
-}
-
 // Final encoding: scale, then (sign, L).
 __device__ __forceinline__ int2 finish(int e, int ld) {
     if (e < kZeroBelow) return make_int2(0, 0);
@@ -149,206 +111,200 @@ __device__ __forceinline__ int phase_tree(const int v[8], const E *__restrict__ 
 template <bool SMALL>
 using LutT = typename std::conditional<SMALL, int16_t, int32_t>::type;
 
-template <bool SMALL>
-__global__ __launch_bounds__(1024) void flns_tile_kernel(
-    const uint8_t *__restrict__ planes, const uint8_t *__restrict__ x, int rows, int groups,
-    int f, const uint8_t *__restrict__ table, int S, int ld, int nsplit,
-    int32_t *__restrict__ out, int *__restrict__ counters, int *__restrict__ partial) {
-    using E = LutT<SMALL>;
-    __shared__ int32_t s_fold[kFlnsFoldSlots];   // entries 0..128 (|cnt| <= 128)
-    __shared__ int last;
-    __shared__ uint4 s_lut4[SMALL ? kFlnsSmallMaxEntries * 2 / 16 : 1];
-    __shared__ int s_x[kTilesPerWg][8][64];
-    // codes present in each Tile128, phase-major: code 8b + p at bit 16p + b
-    __shared__ uint32_t s_present[kTilesPerWg][4];
+// Split-free mapping: a workgroup owns 16 rows and all of K.  Wavefront w
+// takes Tile128s 2w and 2w + 1 of every chunk of 32, one after the other, so
+// all its lanes share one Tile128 at a time (the S1 ballots stay uniform);
+// quarter q (lanes 16q..16q+15, lane = row 16 * block + (lane & 15)) takes
+// phases q and q + 4.  Per Tile128 the wavefront builds, in its own LDS
+// region, the 128-position mask of every code and the phase-major presence
+// of the codes.  The band loop of a phase walks the bands live for any of
+// the four phases in flight: a band the lane's phase lacks has an empty mask,
+// so its population is zero and its leaf kZ, and the pair add of anything
+// with kZ returns it unchanged, so the union's extra leaves and nodes leave
+// every real result as the per-phase tree gives it.  The tile tree keeps its
+// balanced order: Tile128s 2w and 2w + 1 in registers, the 16 wavefronts'
+// nodes in LDS, then the chunks; the phase tree and the scale follow.
+constexpr int kFrRows = 16;
 
-    const int rtile = blockIdx.x / nsplit;
-    const int q = blockIdx.x - rtile * nsplit;
+// Wait for this wavefront's LDS operations; its masks are private to it, so
+// no workgroup barrier is involved.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt untouched
+    __builtin_amdgcn_wave_barrier();
+}
+
+constexpr int kFrChunkTiles = 2 * kWavesPerWg;   // 32 Tile128s per chunk
+constexpr int kFrMaxChunks = 16;                  // 65408 / 128 = 511 Tile128s
+
+template <bool SMALL>
+__global__ __launch_bounds__(1024) void flns_rows_kernel(
+    const uint8_t *__restrict__ planes, const uint8_t *__restrict__ x, int rows, int groups,
+    int f, const uint8_t *__restrict__ table, int S, int ld, int32_t *__restrict__ out) {
+    using E = LutT<SMALL>;
+    __shared__ int32_t s_fold[kFlnsFoldSlots];
+    __shared__ uint4 s_lut4[SMALL ? kFlnsSmallMaxEntries * 2 / 16 : 1];
+    __shared__ uint4 s_mask[kWavesPerWg][128];        // per wavefront: code -> positions
+    __shared__ uint32_t s_pw[kWavesPerWg][4];          // per wavefront: presence, phase-major
+    __shared__ int s_l1[kWavesPerWg][8][kFrRows];      // level-1 tile nodes
+    __shared__ int s_root[kFrMaxChunks][8][kFrRows];   // chunk roots
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int slot = wave & (kTilesPerWg - 1), half = wave >> 3;
-    const int j = q * kTilesPerWg + slot;   // Tile128 = 128-weight group j
-    const bool has_tile = j < groups;       // uniform
+    const int q = lane >> 4, r = lane & 15;
+    const int row = blockIdx.x * kFrRows + r;          // < the padded row count
+    const int rtile = row >> 6, rit = row & 63;
 
-    if (threadIdx.x < kTilesPerWg * 4) s_present[threadIdx.x >> 2][threadIdx.x & 3] = 0;
-    uint4 nz = make_uint4(0, 0, 0, 0), ng = nz;
-    int b0 = 0, b1 = 0;
-    if (has_tile) {
-        const size_t blk = (size_t)rtile * groups + j;
-        nz = *reinterpret_cast<const uint4 *>(planes + blk * 2048 + 16 * lane);
-        ng = *reinterpret_cast<const uint4 *>(planes + blk * 2048 + 1024 + 16 * lane);
-        b0 = x[(size_t)j * 128 + lane];
-        b1 = x[(size_t)j * 128 + 64 + lane];
-    }
     const int32_t *g_fold = reinterpret_cast<const int32_t *>(table + kFlnsHdrBytes);
     for (int i = threadIdx.x; i < kFlnsFoldSlots; i += blockDim.x) s_fold[i] = g_fold[i];
     if constexpr (SMALL)
         stage16(s_lut4, reinterpret_cast<const uint4 *>(table + kFlnsCorrOff), (2 * S * 2 + 15) / 16);
     __syncthreads();
-    // the set of codes in each Tile128, once for all the rows of the tile
-    if (has_tile && half == 0) {
-        const int c0 = b0 & 0x7F, c1 = b1 & 0x7F;
-        const int r0 = 16 * (c0 & 7) + (c0 >> 3), r1 = 16 * (c1 & 7) + (c1 >> 3);
-        if (c0) atomicOr(&s_present[slot][r0 >> 5], 1u << (r0 & 31));
-        if (c1) atomicOr(&s_present[slot][r1 >> 5], 1u << (r1 & 31));
-    }
-    __syncthreads();
     const E *lut = SMALL ? reinterpret_cast<const E *>(s_lut4)
                          : reinterpret_cast<const E *>(table + kFlnsCorrOff);
+    uint4 *mw = s_mask[wave];
+    const int nchunks = (groups + kFrChunkTiles - 1) / kFrChunkTiles;
 
-    if (has_tile) {
-        uint32_t pres[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) pres[w] = __builtin_amdgcn_readfirstlane(s_present[slot][w]);
-        const uint64_t s0 = __ballot(b0 >> 7), s1 = __ballot(b1 >> 7);
-        TileState ts;
-        ts.code0 = b0 & 0x7F;
-        ts.code1 = b1 & 0x7F;
-        // a product is negative iff S1 xor [t < 0]
-        ts.nz[0] = nz.x; ts.nz[1] = nz.y; ts.nz[2] = nz.z; ts.nz[3] = nz.w;
-        ts.neg[0] = nz.x & ((uint32_t)s0 ^ ng.x);
-        ts.neg[1] = nz.y & ((uint32_t)(s0 >> 32) ^ ng.y);
-        ts.neg[2] = nz.z & ((uint32_t)s1 ^ ng.z);
-        ts.neg[3] = nz.w & ((uint32_t)(s1 >> 32) ^ ng.w);
-        // opaque to the compiler, which would otherwise fold the nz & into
-        // each state's mask and spend an xor and an and per word
-#pragma unroll
-        for (int w = 0; w < 4; ++w) asm volatile("" : "+v"(ts.neg[w]));
-        ts.nneg = bcnt_add(ts.neg[3], bcnt_add(ts.neg[2], bcnt_add(ts.neg[1], bcnt_add(ts.neg[0], 0))));
+    for (int ch = 0; ch < nchunks; ++ch) {
+        // the pair's results per phase q + 4i: ra from Tile128 2w, rb from 2w + 1
+        int ra[2] = {kZ, kZ}, rb[2] = {kZ, kZ};
 #pragma unroll 1
-        for (int p = 4 * half; p < 4 * half + 4; ++p) {
-            // the bands present in the tile (code 8b + p; code 0 is never
-            // present), their populations, their fold reads back to back,
-            // then the leaves
-            const uint32_t live = (pres[p >> 1] >> (16 * (p & 1))) & 0xFFFFu;   // uniform
-            // each live band's population and its fold read (in flight while
-            // the next bands are counted), then the leaves.  The band mask is
-            // opaque between the two passes, so each test is a bit test and a
-            // branch rather than a saved lane-mask flag.
-            int cnt[16], fv[16];
-#pragma unroll
-            for (int b = 0; b < 16; ++b) {
-                cnt[b] = 0;
-                fv[b] = 0;
-                if ((live >> b) & 1) {
-                    // the code, opaque: otherwise the compiler hoists code - 8b
-                    // out of the phase loop (sixteen registers) and spends an
-                    // add and a compare per ballot instead of one compare
-                    int code = 8 * b + p;
-                    asm volatile("" : "+s"(code));
-                    cnt[b] = population(code, ts);
-                    fv[b] = s_fold[abs(cnt[b])];
+        for (int tt = 0; tt < 2; ++tt) {
+            const int j = ch * kFrChunkTiles + 2 * wave + tt;   // Tile128 (group) index
+            if (j >= groups) break;   // uniform
+            const size_t blk = (size_t)rtile * groups + j;
+            const uint4 nz = *reinterpret_cast<const uint4 *>(planes + blk * 2048 + 16 * rit);
+            const uint4 ng = *reinterpret_cast<const uint4 *>(planes + blk * 2048 + 1024 + 16 * rit);
+            const int b0 = x[(size_t)j * 128 + lane];
+            const int b1 = x[(size_t)j * 128 + 64 + lane];
+            // this wavefront's masks and presence for Tile128 j
+            mw[lane] = make_uint4(0, 0, 0, 0);
+            mw[64 + lane] = make_uint4(0, 0, 0, 0);
+            if (lane < 4) s_pw[wave][lane] = 0;
+            wave_lds_sync();
+            {
+                const int c0 = b0 & 0x7F, c1 = b1 & 0x7F;
+                uint32_t *m0 = reinterpret_cast<uint32_t *>(mw + c0);
+                uint32_t *m1 = reinterpret_cast<uint32_t *>(mw + c1);
+                const int r0 = 16 * (c0 & 7) + (c0 >> 3), r1 = 16 * (c1 & 7) + (c1 >> 3);
+                if (c0) {
+                    atomicOr(m0 + (lane >> 5), 1u << (lane & 31));
+                    atomicOr(&s_pw[wave][r0 >> 5], 1u << (r0 & 31));
+                }
+                if (c1) {
+                    atomicOr(m1 + 2 + (lane >> 5), 1u << (lane & 31));
+                    atomicOr(&s_pw[wave][r1 >> 5], 1u << (r1 & 31));
                 }
             }
-            uint32_t lv = live;
-            asm volatile("" : "+s"(lv));
-            // a dead node (no live leaf below it) holds kZ, below every other
-            // value: a node with one live child takes it, which max() picks,
-            // and only a node with two live children adds them
+            wave_lds_sync();
+            uint32_t pres[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) pres[w] = __builtin_amdgcn_readfirstlane(s_pw[wave][w]);
+            const uint64_t s0 = __ballot(b0 >> 7), s1 = __ballot(b1 >> 7);
+            uint32_t nzw[4] = {nz.x, nz.y, nz.z, nz.w};
+            uint32_t neg[4];
+            neg[0] = nz.x & ((uint32_t)s0 ^ ng.x);
+            neg[1] = nz.y & ((uint32_t)(s0 >> 32) ^ ng.y);
+            neg[2] = nz.z & ((uint32_t)s1 ^ ng.z);
+            neg[3] = nz.w & ((uint32_t)(s1 >> 32) ^ ng.w);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) asm volatile("" : "+v"(neg[w]));
+            const int nneg = bcnt_add(neg[3], bcnt_add(neg[2], bcnt_add(neg[1], bcnt_add(neg[0], 0))));
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int p = q + 4 * i;   // this lane's phase
+                // bands live for any of phases 4i .. 4i + 3 (uniform)
+                const uint32_t d0 = pres[2 * i], d1 = pres[2 * i + 1];
+                const uint32_t live = (d0 | (d0 >> 16) | d1 | (d1 >> 16)) & 0xFFFFu;
+                const uint4 *mp = mw + p;   // + 8 * band
+                int cnt[16], fv[16];
+#pragma unroll
+                for (int b = 0; b < 16; ++b) {
+                    cnt[b] = 0;
+                    fv[b] = 0;
+                    if ((live >> b) & 1) {
+                        const uint4 m = mp[8 * b];
+                        int c = bcnt_add(nzw[0] & (m.x ^ neg[0]), 0);
+                        c = bcnt_add(nzw[1] & (m.y ^ neg[1]), c);
+                        c = bcnt_add(nzw[2] & (m.z ^ neg[2]), c);
+                        c = bcnt_add(nzw[3] & (m.w ^ neg[3]), c);
+                        cnt[b] = c - nneg;
+                        fv[b] = s_fold[abs(cnt[b])];
+                    }
+                }
+                uint32_t lv = live;
+                asm volatile("" : "+s"(lv));
+                int v[16];
+#pragma unroll
+                for (int b = 0; b < 16; ++b) {
+                    v[b] = kZ;
+                    if ((lv >> b) & 1) {
+                        const int ng1 = cnt[b] < 0 ? 1 : 0;
+                        const int val = 2 * (((8 * b + p) << f) + fv[b]) + ng1;
+                        v[b] = cnt[b] == 0 ? kZ : val;
+                    }
+                }
+                uint32_t any = lv;
+#pragma unroll
+                for (int w = 8, sh = 1; w >= 1; w >>= 1, sh <<= 1) {
+                    const uint32_t both = any & (any >> sh);
+#pragma unroll
+                    for (int m = 0; m < w; ++m) {
+                        const int a = v[2 * m], c = v[2 * m + 1];
+                        v[m] = (both >> (2 * sh * m)) & 1 ? lns_add(a, c, lut, S) : max(a, c);
+                    }
+                    any |= any >> sh;
+                }
+                if (tt == 0)
+                    ra[i] = v[0];
+                else
+                    rb[i] = v[0];
+            }
+            wave_lds_sync();   // the next Tile128 rewrites this wavefront's masks
+        }
+        // level 1 of the tile tree: Tile128s 2w and 2w + 1
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            s_l1[wave][q + 4 * i][r] = lns_add(ra[i], rb[i], lut, S);
+        __syncthreads();
+        // levels 2..5 over the 16 wavefronts' nodes: thread (p, r)
+        if (threadIdx.x < 8 * kFrRows) {
+            const int p = threadIdx.x >> 4, rr = threadIdx.x & 15;
             int v[16];
 #pragma unroll
-            for (int b = 0; b < 16; ++b) {
-                v[b] = kZ;
-                if ((lv >> b) & 1) {
-                    const int neg = cnt[b] < 0 ? 1 : 0;
-                    const int val = 2 * (((8 * b + p) << f) + fv[b]) + neg;
-                    v[b] = cnt[b] == 0 ? kZ : val;
-                }
-            }
-            // any: bit s*m set when node m of the level (span s) has a live
-            // leaf; both: when both its children do
-            uint32_t any = lv;
+            for (int w = 0; w < 16; ++w) v[w] = s_l1[w][p][rr];
 #pragma unroll
-            for (int w = 8, s = 1; w >= 1; w >>= 1, s <<= 1) {
-                const uint32_t both = any & (any >> s);
+            for (int w = 8; w >= 1; w >>= 1)
 #pragma unroll
-                for (int m = 0; m < w; ++m) {
-                    const int a = v[2 * m], c = v[2 * m + 1];
-                    v[m] = (both >> (2 * s * m)) & 1 ? lns_add(a, c, lut, S) : max(a, c);
-                }
-                any |= any >> s;
-            }
-            s_x[slot][p][lane] = v[0];
+                for (int m = 0; m < w; ++m) v[m] = lns_add(v[2 * m], v[2 * m + 1], lut, S);
+            s_root[ch][p][rr] = v[0];
         }
-    } else {
+        __syncthreads();
+    }
+    // the chunk roots in a balanced tree (kZ past the last chunk), then the
+    // phase tree and the scale
+    if (threadIdx.x < 8 * kFrRows) {
+        const int p = threadIdx.x >> 4, rr = threadIdx.x & 15;
+        int v[kFrMaxChunks];
 #pragma unroll
-        for (int p = 4 * half; p < 4 * half + 4; ++p) s_x[slot][p][lane] = kZ;
+        for (int c = 0; c < kFrMaxChunks; ++c) v[c] = c < nchunks ? s_root[c][p][rr] : kZ;
+        // a pair whose right child lies past the last chunk keeps its left
+        // one: the pair add with an all-zero subtree, as the padding gives
+#pragma unroll
+        for (int sh = 1; sh < kFrMaxChunks; sh <<= 1)
+#pragma unroll
+            for (int m = 0; m < kFrMaxChunks; m += 2 * sh)
+                if (m + sh < nchunks) v[m] = lns_add(v[m], v[m + sh], lut, S);
+        s_l1[0][p][rr] = v[0];
     }
     __syncthreads();
-
-    // The workgroup's eight Tile128s per (phase, row): thread t < 512 takes
-    // phase t / 64 of row t % 64.
-    const int p = threadIdx.x >> 6;
-    const int row = rtile * 64 + lane;
-    int r = kZ;
-    if (threadIdx.x < 512) {
-        int v[kTilesPerWg];
-#pragma unroll
-        for (int w = 0; w < kTilesPerWg; ++w) v[w] = s_x[w][p][lane];
-        r = lns_add(lns_add(lns_add(v[0], v[1], lut, S), lns_add(v[2], v[3], lut, S), lut, S),
-                    lns_add(lns_add(v[4], v[5], lut, S), lns_add(v[6], v[7], lut, S), lut, S),
-                    lut, S);
-    }
-    if (nsplit == 1) {
-        __syncthreads();
-        if (threadIdx.x < 512) s_x[0][p][lane] = r;
-        __syncthreads();
-        if (threadIdx.x < 64 && row < rows) {
+    if (threadIdx.x < kFrRows) {
+        const int grow = blockIdx.x * kFrRows + threadIdx.x;
+        if (grow < rows) {
             int ph[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) ph[k] = s_x[0][k][lane];
-            *reinterpret_cast<int2 *>(out + 2 * (size_t)row) = finish(phase_tree(ph, lut, S), ld);
+            for (int k = 0; k < 8; ++k) ph[k] = s_l1[0][k][threadIdx.x];
+            *reinterpret_cast<int2 *>(out + 2 * (size_t)grow) = finish(phase_tree(ph, lut, S), ld);
         }
-    } else {
-        // this workgroup's partials, then the tile's counter
-        const size_t padded_rows = (size_t)(gridDim.x / nsplit) * 64;
-        if (threadIdx.x < 512)
-            __hip_atomic_store(partial + ((size_t)q * padded_rows + row) * 8 + p, r,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's stores are done
-        __syncthreads();
-        if (threadIdx.x == 0)
-            last = __hip_atomic_fetch_add(counters + rtile, 1, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
-        __syncthreads();
-        if (!last) return;   // uniform
-        // The tile tree across the nsplit workgroups of each of the tile's
-        // 64 rows, then the phase tree and the scale: P (a power of two >=
-        // nsplit, <= 64) lanes per row, lane i holding workgroup i's eight
-        // phase partials (zero past nsplit); level s pairs lanes i and i ^ s,
-        // which is the balanced pairwise tree.  1024 / P rows per pass.
-        int P = 1;
-        while (P < nsplit) P <<= 1;
-        const int per_pass = (int)blockDim.x / P;
-        const int qi = (int)threadIdx.x % P;
-        for (int r0 = 0; r0 < 64; r0 += per_pass) {   // uniform trip count
-            const int lr = r0 + (int)threadIdx.x / P;  // row within the tile
-            const int grow = rtile * 64 + lr;
-            int v[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = kZ;
-            if (lr < 64 && qi < nsplit) {
-                int *src = partial + ((size_t)qi * padded_rows + grow) * 8;
-                // every load in flight, then the clearing stores
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    v[k] = __hip_atomic_load(src + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) src[k] = 0;
-                if (grow >= rows) {
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) v[k] = kZ;
-                }
-            }
-            for (int sh = 1; sh < P; sh <<= 1) {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) v[k] = lns_add(v[k], __shfl_xor(v[k], sh), lut, S);
-            }
-            if (qi == 0 && lr < 64 && grow < rows)
-                *reinterpret_cast<int2 *>(out + 2 * (size_t)grow) = finish(phase_tree(v, lut, S), ld);
-        }
-        if (threadIdx.x == 0)
-            __hip_atomic_store(counters + rtile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -360,27 +316,9 @@ using namespace bs;
 // Same K limit as the LNS8 GEMV (k <= 65408).
 static constexpr int64_t kFlnsMaxK = 65408;
 
-static int64_t flns_nsplit(int64_t k) { return (k / kGroup + kTilesPerWg - 1) / kTilesPerWg; }
-
-// Workspace, when K is split over several workgroups per row tile: one
-// int32 counter per tile (256-byte aligned), then the partials
-// int32[nsplit][R][8].  It must be zero before the first call, and every
-// call leaves it zero (the last workgroup of a tile clears the tile's
-// counter and partials), so one workspace serves calls of any shape.
-struct FlnsWs {
-    size_t partial, total;
-};
-
-static FlnsWs flns_ws(int64_t rows, int64_t k) {
-    const int64_t ns = flns_nsplit(k);
-    FlnsWs w;
-    w.partial = ns > 1 ? align_up((size_t)(pad64(rows) / 64) * 4, kWsAlign) : 0;
-    w.total = ns > 1 ? w.partial + (size_t)ns * (size_t)pad64(rows) * 8 * 4 : kWsAlign;
-    w.total = align_up(w.total, kWsAlign);
-    return w;
-}
-
-static size_t flns_ws_bytes(int64_t rows, int64_t k) { return flns_ws(rows, k).total; }
+// The workspace argument is kept for the interface; the reduction needs
+// none, so it is never read or written.
+static size_t flns_ws_bytes(int64_t, int64_t) { return kWsAlign; }
 
 extern "C" size_t bs_flns_workspace_bytes(int64_t rows, int64_t k) {
     if (check_rows_k(rows, k, kFlnsMaxK) != BS_OK) return 0;
@@ -405,21 +343,16 @@ extern "C" int32_t bs_flns_phase_gemv(const uint8_t *planes, const uint8_t *x_ln
     const bool small = frac_bits <= kFlnsSmallMaxFrac;
     if (small && 2 * sz.stride > kFlnsSmallMaxEntries) return BS_E_RANGE;
 
-    const int64_t tiles = pad64(rows) / 64;
     const int64_t groups = k / kGroup;
-    const int nsplit = (int)flns_nsplit(k);
+    const int64_t blocks = (rows + kFrRows - 1) / kFrRows;
     // the grid within the 2^32 threads of one launch
-    if (tiles * nsplit * kWavesPerWg * 64 >= ((int64_t)1 << 32)) return BS_E_SHAPE;
-    hipStream_t st = (hipStream_t)stream;
+    if (blocks * kWavesPerWg * 64 >= ((int64_t)1 << 32)) return BS_E_SHAPE;
+    static_assert(kFlnsMaxK / kGroup <= kFrMaxChunks * kFrChunkTiles, "chunk roots");
     const uint8_t *tb = static_cast<const uint8_t *>(table);
-    const FlnsWs w = flns_ws(rows, k);
-    unsigned char *base = static_cast<unsigned char *>(workspace);
-    int *counters = reinterpret_cast<int *>(base);
-    int *partial = reinterpret_cast<int *>(base + w.partial);
-    auto kern = small ? flns_tile_kernel<true> : flns_tile_kernel<false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * nsplit)), dim3(kWavesPerWg * 64), 0, st,
+    auto kern = small ? flns_rows_kernel<true> : flns_rows_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kWavesPerWg * 64), 0, (hipStream_t)stream,
                        planes, x_lns8, (int)rows, (int)groups, (int)frac_bits, tb, (int)sz.stride,
-                       (int)ld, nsplit, out, counters, partial);
+                       (int)ld, out);
     BS_LAUNCH_CHECK();
     return BS_OK;
 }

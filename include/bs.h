@@ -246,13 +246,11 @@ int32_t bs_lns8_phase_gemv(const uint8_t *planes, const uint8_t *x_lns8, int64_t
  *              (the size identifies f: a table for another f is rejected)
  *   out        device int32[rows][2], 8-byte aligned: (sign, L) per row,
  *              sign -1 / 0 / +1, L = 0 when the result is zero
- *   workspace  device scratch of at least bs_flns_workspace_bytes(rows, k)
- *              bytes, 256-byte aligned, caller-owned: when K is split over
- *              several workgroups (k > 1024), a counter per 64-row tile and
- *              the partial phase sums.  Zero it before its first use; every
- *              call leaves it zero again, so one workspace serves calls of
- *              any shape ordered on one stream.  Calls that may overlap need
- *              separate workspaces.
+ *   workspace  device memory of at least bs_flns_workspace_bytes(rows, k)
+ *              bytes (256), 256-byte aligned, caller-owned: reserved by the
+ *              interface; the reduction runs in one launch per call with
+ *              every partial result on chip, so it is never read or
+ *              written.
  * Errors: BS_E_NULL, BS_E_SHAPE, BS_E_OVERFLOW (k), BS_E_RANGE (frac_bits,
  *   scale_d = 0, table_bytes not that of frac_bits), BS_E_ALIGN,
  *   BS_E_WORKSPACE, BS_E_HIP.

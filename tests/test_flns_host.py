@@ -5,7 +5,8 @@
 * blob header and size, and the errors of bs_flns_table_build;
 * argument validation of bs_flns_phase_gemv returns the documented BS_E_*
   code before any HIP call (only failing calls are made here);
-* the workspace size follows the launch plan (eight Tile128s per workgroup).
+* the workspace size is the interface's reserved 256 bytes for every
+  valid shape (the reduction keeps every partial result on chip).
 """
 import ctypes
 
@@ -93,10 +94,9 @@ def test_flns_validation():
 
 def test_flns_workspace_sizes():
     lib = bs.lib()
-    assert lib.bs_flns_workspace_bytes(0, 128) == 0
-    assert lib.bs_flns_workspace_bytes(64, 1024) == 256           # one workgroup per tile
-    # split K: a counter per 64-row tile (256-byte aligned), then the partials
-    assert lib.bs_flns_workspace_bytes(4096, 4096) == 256 + 4 * 4096 * 8 * 4
-    assert lib.bs_flns_workspace_bytes(65, 1152) == 256 + 2 * 128 * 8 * 4
-    assert lib.bs_flns_workspace_bytes(64, 65408) == 256 + 64 * 64 * 8 * 4
-    assert lib.bs_flns_workspace_bytes(64 * 65, 2048) == 512 + 2 * 64 * 65 * 8 * 4
+    assert lib.bs_flns_workspace_bytes(0, 128) == 0               # invalid shapes
+    assert lib.bs_flns_workspace_bytes(64, 100) == 0
+    assert lib.bs_flns_workspace_bytes(64, 65536) == 0
+    for rows, k in ((1, 128), (64, 1024), (4096, 4096), (65, 1152), (64, 65408),
+                    ((1 << 31) - 64, 4096)):
+        assert lib.bs_flns_workspace_bytes(rows, k) == 256

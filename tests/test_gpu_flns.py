@@ -2,9 +2,9 @@
 the oracle.  The method is an approximation whose every rounding is
 specified, so both sides compute the same integers: (sign, L) must match
 bit for bit on every row, at every internal precision.  Sizes span several
-tiles and workgroups, ragged rows, K split over workgroups (finished by the
-last workgroup of each tile), the largest K, and the degenerate inputs of
-the LNS8 path."""
+16-row workgroups, ragged rows, K over one or several 32-Tile128 chunks
+(the tile tree continued across the chunks), the largest K, and the
+degenerate inputs of the LNS8 path."""
 import numpy as np
 import pytest
 
@@ -54,11 +54,15 @@ def test_flns_every_precision(f):
 
 
 @pytest.mark.parametrize("rows,k", [(1, 128), (63, 256), (65, 1152), (130, 1024), (2000, 128),
-                                    (200, 8192), (64, 65408)])
+                                    (200, 8192), (64, 65408), (16, 4096), (33, 4224),
+                                    (17, 12416)])
 def test_flns_ragged_and_split(rows, k):
-    """One Tile128, a partial last workgroup (k = 1152: nine Tile128s, two
-    workgroups), exactly one workgroup (1024), many split workgroups, and
-    the largest K (511 Tile128s, 64 workgroups per row tile)."""
+    """One Tile128; nine Tile128s (k = 1152: five wavefronts with a tile,
+    one of them with only the first of its pair); eight (1024); one full
+    chunk of 32 (4096); 32 + 1 (4224: the second chunk holds one Tile128);
+    64 (8192: two chunks); 97 (12416: four chunks, the last short); the
+    largest K (511 Tile128s: sixteen chunks).  The last 16-row block is cut
+    short at 1, 63, 65, 130, 33 and 17 rows."""
     check(*synth.lns8(rows, k, rows + k), 8)
 
 
@@ -99,10 +103,8 @@ def test_flns_adversarial(case, f):
 
 
 def test_flns_repeated_calls_share_a_workspace():
-    """One zeroed workspace serves back-to-back calls of different shapes:
-    fewer rows, a single workgroup per tile, and more tiles after fewer (the
-    later call's counters then lie where the earlier call's partials were;
-    every call leaves the workspace zero), every result exact."""
+    """One workspace serves back-to-back calls of different shapes, every
+    result exact; the reduction never writes it, so it stays zero."""
     import torch
     dev = device()
     shapes = ((300, 4096, 1), (300, 4096, 2), (130, 2048, 3), (64, 1024, 5), (1000, 3072, 6),
