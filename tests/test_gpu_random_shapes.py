@@ -76,6 +76,28 @@ def test_flns_random(rows, k, seed, f):
     test_gpu_flns.check(t, x, f)
 
 
+# long K for the chunked kernels (LNS8 popcount: 64 units per chunk; pure
+# LNS: 32 Tile128s per chunk), from a generator of their own so the cases
+# above stay as they were
+_rng2 = np.random.default_rng(20261203)
+LNS8_LONG = [(int(_rng2.integers(1, 80)), 128 * int(_rng2.integers(81, 320)),
+              int(_rng2.integers(0, 1 << 20)), float(_rng2.choice([0.0, 1 / 3])),
+              int(_rng2.choice([8, 41, 127]))) for _ in range(6)]
+FLNS_LONG = [(int(_rng2.integers(1, 70)), 128 * int(_rng2.integers(41, 200)),
+              int(_rng2.integers(0, 1 << 20)), int(_rng2.integers(0, 13))) for _ in range(6)]
+
+
+@pytest.mark.parametrize("rows,k,seed,p_zero,n_codes", LNS8_LONG)
+def test_lns8_random_long_k(rows, k, seed, p_zero, n_codes):
+    test_gpu_lns8.check(*synth.lns8_sweep(rows, k, seed, p_zero, n_codes))
+
+
+@pytest.mark.parametrize("rows,k,seed,f", FLNS_LONG)
+def test_flns_random_long_k(rows, k, seed, f):
+    t, x = synth.lns8(rows, k, seed)
+    test_gpu_flns.check(t, x, f)
+
+
 @pytest.mark.parametrize("V,K,top_k,cap,seed", LMHEAD)
 def test_lmhead_random(V, K, top_k, cap, seed):
     test_gpu_lmhead.check(*synth.lmhead(V, K, seed), top_k, cap)
