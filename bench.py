@@ -590,6 +590,26 @@ def lns8_valu_ops(path: int) -> float:
         return None
 
 
+def flns_valu_ops(small: bool) -> float:
+    """VALU instructions per call of the pure fractional-LNS kernel at 4096 x
+    4096 (LDS tables, f <= 8: the mean of the f = 0 and f = 8 calls; device
+    tables: f = 12), from the SQ counter record under profiles/ (None if
+    absent or taken on other source)."""
+    fn = os.path.join(ROOT, "profiles", "flns_4096x4096_sq_counters.txt")
+    if not os.path.exists(fn):
+        return None
+    want = "flns_rows_kernel<%s>" % ("true" if small else "false")
+    digest, valu = None, None
+    for line in open(fn):
+        if line.startswith("kernel_source_sha256_16:"):
+            digest = line.split(":", 1)[1].strip()
+        elif want in line and " SQ_INSTS_VALU " in line and " mean " in line:
+            valu = float(line.split(" mean ")[1].split()[0])
+    if digest != _source_digest("flns_phase.hip"):
+        return None
+    return valu
+
+
 def run_extras(torch, bs, synth, dev, H):
     import numpy as np
     ops = {}
@@ -665,6 +685,10 @@ def run_extras(torch, bs, synth, dev, H):
                            "rel_err_p99": float("%.3g" % np.quantile(rel, 0.99)),
                            "rel_err_max": float("%.3g" % rel.max()),
                            "rows_compared": int(big.sum())}
+        valu = flns_valu_ops(f <= 8)
+        if valu is not None:
+            flns["f%d" % f]["valu_insts_per_call"] = valu
+            flns["f%d" % f]["frac_valu_peak"] = round(valu * 64 / (us * 1e-6) / VALU_PEAK_OPS, 4)
         log("flns f=%d: %.2f us, median rel err %.3g" % (f, us, np.median(rel)))
     ops["flns_4096x4096"] = {"error_vs": "exact dyadic S of the linear eight-phase path "
                                          "(rows with |S| >= 1e-3 x median |S|)", **flns}

@@ -135,6 +135,38 @@ def test_lns8_valu_record_round_trip(tmp_path, monkeypatch):
     assert bench.lns8_valu_ops(0) is None
 
 
+def test_flns_valu_record_round_trip(tmp_path, monkeypatch):
+    """The pure-LNS counter record (a --counter-summary of --flns-counter-run
+    under a header with the source digest) is read back per table placement
+    and ignored once the kernel source changes."""
+    import shutil
+    for rel in (("bit_decode_gemv_amd", "csrc", "flns_phase.hip"),
+                ("bit_decode_gemv_amd", "csrc", "kcommon.h"),
+                ("bit_decode_gemv_amd", "csrc", "bs_internal.h"),
+                ("include", "bs.h")):
+        dst = tmp_path.joinpath(*rel)
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(bench.ROOT, *rel), dst)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    fields = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    rows = []
+    for small, v in (("true", 4000.0), ("false", 5000.0)):
+        for i in range(2):
+            rows.append({"Kernel_Name": "void bs::(anonymous namespace)::flns_rows_kernel<%s>(a)"
+                                        % small,
+                         "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": v + 2 * i})
+    _write(tmp_path / "c.csv", fields, rows)
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "flns_4096x4096_sq_counters.txt").write_text(
+        "# header\nkernel_source_sha256_16: %s\n%s\n" % (
+            bench._source_digest("flns_phase.hip"), bench.counter_summary(str(tmp_path / "c.csv"))))
+    assert bench.flns_valu_ops(True) == pytest.approx(4001.0)
+    assert bench.flns_valu_ops(False) == pytest.approx(5001.0)
+    with open(tmp_path / "bit_decode_gemv_amd" / "csrc" / "flns_phase.hip", "a") as f:
+        f.write("\n// edit\n")
+    assert bench.flns_valu_ops(True) is None
+
+
 def test_counter_summary_ratios(tmp_path):
     fields = ["Kernel_Name", "Counter_Name", "Counter_Value"]
     k = "void bs::(anonymous namespace)::ternary_pipe_kernel<8, 3, 1, 1>(args)"
