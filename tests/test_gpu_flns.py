@@ -102,6 +102,28 @@ def test_flns_adversarial(case, f):
         assert (got == 0).all()
 
 
+def _adversarial_long():
+    """Adversarial activations over K = 8320 (65 Tile128s: three 32-tile
+    chunks, the last holding one), 33 rows."""
+    rng = np.random.default_rng(31)
+    k = 8320
+    t = rng.integers(-1, 2, (33, k)).astype(np.int8)
+    yield "all_same_code", t, np.full(k, 80, np.uint8)
+    yield "all_bytes", t, rng.integers(0, 256, k).astype(np.uint8)
+    xc = np.full(k, 90, np.uint8)
+    xc[1::2] |= 0x80
+    yield "cancel", np.ones((33, k), np.int8), xc
+    yield "full_tiles_max", -np.ones((33, k), np.int8), np.full(k, 0xFF, np.uint8)
+
+
+@pytest.mark.parametrize("f", [0, 8, 12])
+@pytest.mark.parametrize("case", list(_adversarial_long()), ids=lambda c: c[0])
+def test_flns_adversarial_long_k(case, f):
+    got = check(case[1], case[2], f)
+    if case[0] == "cancel":
+        assert (got == 0).all()
+
+
 def test_flns_repeated_calls_share_a_workspace():
     """One workspace serves back-to-back calls of different shapes, every
     result exact; the reduction never writes it, so it stays zero."""

@@ -84,6 +84,26 @@ def test_lns8_adversarial(case):
     check(case[1], case[2])
 
 
+def _adversarial_long():
+    """The adversarial activations over K = 8320 (three 64-unit chunks of the
+    popcount kernel, the last holding two units), 33 rows."""
+    rng = np.random.default_rng(29)
+    k = 8320
+    t = rng.integers(-1, 2, (33, k)).astype(np.int8)
+    yield "all_same_code", t, np.full(k, 80, np.uint8)
+    yield "code_127_signs", t, (rng.integers(0, 2, k).astype(np.uint8) << 7) | 127
+    yield "all_bytes", t, rng.integers(0, 256, k).astype(np.uint8)
+    xc = np.full(k, 90, np.uint8)
+    xc[1::2] |= 0x80
+    yield "cancel", np.ones((33, k), np.int8), xc
+    yield "max_magnitude", -np.ones((33, k), np.int8), np.full(k, 0xFF, np.uint8)
+
+
+@pytest.mark.parametrize("case", list(_adversarial_long()), ids=lambda c: c[0])
+def test_lns8_adversarial_long_k(case):
+    check(case[1], case[2])
+
+
 @pytest.mark.parametrize("rows,k", [(64, 65408), (200, 8192), (2000, 128), (70, 2048)])
 def test_lns8_split_and_long_rows(rows, k):
     """K split over several workgroups per tile (partials combined by the
