@@ -448,95 +448,96 @@ __global__ __launch_bounds__(NW * 64) void ternary_pipe_kernel(
     }
 }
 
-// Launch shape of the pipelined kernel, from sweeps of (R, wavefronts,
-// groups per slice) on MI355X with cold weights, every configuration checked
-// bit-exact.  Short matrices want many small workgroups (8 rows, one group
-// per slice); taller ones longer per-slice pipelines (3 to 6 groups) on 16-
-// or 32-row blocks; the winners per K range:
-//   K <= 3072:  <= 4096 rows 8-row blocks, 1 group per slice; taller
-//               32-row blocks of 4 wavefronts (13824x2560 4.21 -> 4.02 us
-//               against 16-row blocks of one wavefront with 5 groups);
-//   K <= 5120:  from 6400 rows 32-row blocks of 4 wavefronts, else 16-row
-//               blocks with 2 groups per slice;
-//   K <= 8192:  16-row blocks with 2 groups per slice;
-//   K <= 12288: 16-row blocks of 8 wavefronts, 3 groups per slice;
-//   K <= 16384: 32-row blocks of 9 wavefronts, 6 to 8 groups per slice.
-// Measured per launch (events, back-to-back, cold weights) against the
-// row-block and tile kernels: 2560x2560 3.10 -> 2.64 us, 6912x2560 3.60 ->
-// 3.12, 11008x4096 4.70 -> 4.44, 13824x5120 5.58 -> 5.29, 2560x6912 3.92 ->
-// 3.21, 5120x13824 7.02 -> 6.66.  A re-sweep of this table (every family
-// member, pipeline depth 2 or all groups up front) found no faster entry.
+// Launch shape of the pipelined kernel: R rows per block, NW wavefronts,
+// NG groups per slice, D groups in flight ahead of the one being computed.
+// From sweeps on MI355X with cold weights (every (R, NW) with the fewest NG
+// covering K, D = 1 to 3; each configuration checked bit-exact), the winners
+// per K and row range:
+//   K <= 3072:  under 2048 rows 8-row blocks, 1 group per slice; to 4096
+//               rows 16-row blocks, to 10240 32-row blocks, both with 2
+//               groups per slice and D = 1; taller 64-row blocks (a whole
+//               tile) of 4 wavefronts;
+//   K <= 5120:  from 10240 rows whole tiles of 8 wavefronts; 6400 to 10240
+//               rows 32-row blocks of 4; else 16-row blocks, 2 per slice;
+//   K <= 8192:  16-row blocks, 2 groups per slice, D = 1;
+//   K <= 12288: 16-row blocks of 8 wavefronts, 3 groups per slice, D = 1;
+//   K <= 16384: 32-row blocks of 8 wavefronts, 7 or 8 groups per slice.
+// Per launch (events, back-to-back, cold weights, interleaved medians) against
+// the previous table: 2560x2560 2.63 -> 2.53 us, 6912x2560 3.13 -> 3.08,
+// 13824x2560 4.07 -> 3.81, 11008x4096 4.43 -> 4.21, 13824x5120 5.25 -> 5.22,
+// 2560x6912 3.18 -> 3.09, 4096x11008 4.41 -> 4.34, 5120x13824 6.60 -> 6.07;
+// 640x2560 unchanged (2.42).  Fewer, longer wavefronts won at long K (8 of 7
+// groups beat 9 of 6), and whole-tile blocks on tall short-K matrices: one
+// wavefront's 64 lanes then read a group's 1 KiB plane block as one run.
 struct PipeCfg {
-    int R, NW, NG;
+    int R, NW, NG, D;
 };
 
 constexpr int kPipeMaxGroups = 128;   // K <= 16384; larger K takes the row-block kernel
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+static inline int imin(int a, int b) { return a < b ? a : b; }
 
 static PipeCfg choose_pipe(int64_t rows, int64_t groups) {
     if (groups <= 24) {
-        if (rows <= 4096) return {8, cdiv(groups, 8), 1};
-        return {32, 4, cdiv(groups, 8)};
+        if (rows < 2048) return {8, cdiv(groups, 8), 1, 1};
+        if (rows <= 4096) return {16, cdiv(groups, 8), 2, 1};
+        if (rows < 10240) return {32, cdiv(groups, 4), 2, 1};
+        const int ng = cdiv(groups, 4);
+        return {64, 4, ng, imin(ng, 2)};
     }
     if (groups <= 40) {
-        if (rows >= 6400) return {32, 4, cdiv(groups, 8)};
-        return {16, cdiv(groups, 8), 2};
+        if (rows >= 10240) return {64, 8, cdiv(groups, 8), 2};
+        if (rows >= 6400) return {32, 4, cdiv(groups, 8), 2};
+        return {16, cdiv(groups, 8), 2, 1};
     }
-    if (groups <= 64) return {16, cdiv(groups, 8), 2};
-    if (groups <= 96) return {16, 8, 3};
-    return {32, 9, cdiv(groups, 18)};
+    if (groups <= 64) return {16, cdiv(groups, 8), 2, 1};
+    if (groups <= 96) return {16, 8, 3, 1};
+    return {32, 8, cdiv(groups, 16), 2};
 }
 
 // Q1_0 (half the plane bytes per group), from the same sweep: up to K = 3072
-// 16-row blocks with two groups per slice up to 4096 rows, 32-row blocks of
-// 4 wavefronts above (2560x2560 2.49 us, 13824x2560 3.46, against 2.61 and
-// 4.51 with the ternary entries); the ternary table beyond.
+// 16-row blocks with two groups per slice (D = 2) up to 4096 rows, whole
+// tiles of 4 wavefronts from 10240 (D up to 3), 32-row blocks of 4 between;
+// up to K = 5120 from 10240 rows the ternary table's whole tiles; elsewhere
+// the ternary table's blocks with D = 2 (one group in flight measured slower
+// for Q1_0: 2560x6912 3.04 us against 3.16).  Per launch: 2560x2560 2.47 us,
+// 13824x2560 3.52 -> 3.34, 2560x6912 3.04, 13824x5120 4.87 -> 4.34.
 static PipeCfg choose_pipe_q1(int64_t rows, int64_t groups) {
     if (groups <= 24) {
-        if (rows <= 4096) return {16, cdiv(groups, 8), 2};
-        return {32, 4, cdiv(groups, 8)};
+        const int ng = cdiv(groups, 8);
+        if (rows <= 4096) return {16, ng, 2, 2};
+        if (rows >= 10240) return {64, 4, cdiv(groups, 4), imin(cdiv(groups, 4), 3)};
+        return {32, 4, ng, imin(ng, 2)};
     }
-    return choose_pipe(rows, groups);
+    PipeCfg c = choose_pipe(rows, groups);
+    c.D = imin(c.NG, 2);
+    return c;
 }
 
-template <int R, int NW, int NG, bool Q1>
+template <int R, int NW, int NG, int D, bool Q1>
 static void launch_pipe1(hipStream_t st, const uint8_t *planes, const int16_t *scales,
                          const int8_t *x, int rows, int groups, int shift, int64_t *y) {
-    constexpr int D = NG < 2 ? NG : 2;
     const unsigned nblk = (unsigned)((rows + R - 1) / R);
     hipLaunchKernelGGL((ternary_pipe_kernel<R, NW, NG, D, Q1>), dim3(nblk), dim3(NW * 64), 0, st,
                        planes, scales, x, rows, groups, shift, y);
 }
 
-// Dispatch over NW (R, NG fixed) or over NG (R, NW fixed), LO..HI.
-template <int R, int NG, int NW, int HI, bool Q1>
-static bool pipe_by_nw(int nw, hipStream_t st, const uint8_t *p, const int16_t *s,
-                       const int8_t *x, int rows, int groups, int shift, int64_t *y) {
-    if constexpr (NW > HI) {
-        return false;
-    } else {
-        if (nw == NW) {
-            launch_pipe1<R, NW, NG, Q1>(st, p, s, x, rows, groups, shift, y);
-            return true;
-        }
-        return pipe_by_nw<R, NG, NW + 1, HI, Q1>(nw, st, p, s, x, rows, groups, shift, y);
-    }
-}
-
-template <int R, int NW, int NG, int HI, bool Q1>
-static bool pipe_by_ng(int ng, hipStream_t st, const uint8_t *p, const int16_t *s,
-                       const int8_t *x, int rows, int groups, int shift, int64_t *y) {
-    if constexpr (NG > HI) {
-        return false;
-    } else {
-        if (ng == NG) {
-            launch_pipe1<R, NW, NG, Q1>(st, p, s, x, rows, groups, shift, y);
-            return true;
-        }
-        return pipe_by_ng<R, NW, NG + 1, HI, Q1>(ng, st, p, s, x, rows, groups, shift, y);
-    }
-}
+// The instantiated configurations (R, NW, NG, D): every one the two tables
+// above can return for 1 to 128 groups.
+#define BS_PIPE_CONFIGS(X)                                                                     \
+    X(8, 1, 1, 1) X(8, 2, 1, 1) X(8, 3, 1, 1)                                                  \
+    X(16, 1, 2, 1) X(16, 2, 2, 1) X(16, 3, 2, 1) X(16, 4, 2, 1)                                \
+    X(16, 5, 2, 1) X(16, 6, 2, 1) X(16, 7, 2, 1) X(16, 8, 2, 1)                                \
+    X(16, 1, 2, 2) X(16, 2, 2, 2) X(16, 3, 2, 2) X(16, 4, 2, 2)                                \
+    X(16, 5, 2, 2) X(16, 6, 2, 2) X(16, 7, 2, 2) X(16, 8, 2, 2)                                \
+    X(16, 8, 3, 1) X(16, 8, 3, 2)                                                              \
+    X(32, 1, 2, 1) X(32, 2, 2, 1) X(32, 3, 2, 1) X(32, 4, 2, 1) X(32, 5, 2, 1) X(32, 6, 2, 1) \
+    X(32, 4, 1, 1) X(32, 4, 2, 2) X(32, 4, 3, 2) X(32, 4, 4, 2) X(32, 4, 5, 2)                 \
+    X(32, 8, 7, 2) X(32, 8, 8, 2)                                                              \
+    X(64, 4, 1, 1) X(64, 4, 2, 2) X(64, 4, 3, 2) X(64, 4, 4, 2) X(64, 4, 5, 2) X(64, 4, 6, 2) \
+    X(64, 4, 3, 3) X(64, 4, 4, 3) X(64, 4, 5, 3) X(64, 4, 6, 3)                                \
+    X(64, 8, 4, 2) X(64, 8, 5, 2)
 
 // Launches the configuration c, which must cover every group ((64 / R) * NW
 // * NG >= groups: the LDS staging has a slot for each); false (no launch)
@@ -545,18 +546,13 @@ template <bool Q1>
 static bool launch_pipe(const PipeCfg &c, hipStream_t st, const uint8_t *p, const int16_t *s,
                         const int8_t *x, int rows, int groups, int shift, int64_t *y) {
     if (c.R <= 0 || c.NW <= 0 || c.NG <= 0 || (64 / c.R) * c.NW * c.NG < groups) return false;
-    if (c.R == 8 && c.NG == 1)
-        return pipe_by_nw<8, 1, 1, 3, Q1>(c.NW, st, p, s, x, rows, groups, shift, y);
-    if (c.R == 32 && c.NW == 4)
-        return pipe_by_ng<32, 4, 1, 5, Q1>(c.NG, st, p, s, x, rows, groups, shift, y);
-    if (c.R == 16 && c.NG == 2)
-        return pipe_by_nw<16, 2, 1, 8, Q1>(c.NW, st, p, s, x, rows, groups, shift, y);
-    if (c.R == 16 && c.NW == 8 && c.NG == 3) {
-        launch_pipe1<16, 8, 3, Q1>(st, p, s, x, rows, groups, shift, y);
-        return true;
+#define BS_PIPE_CASE(R_, NW_, NG_, D_)                                                         \
+    if (c.R == R_ && c.NW == NW_ && c.NG == NG_ && c.D == D_) {                                \
+        launch_pipe1<R_, NW_, NG_, D_, Q1>(st, p, s, x, rows, groups, shift, y);               \
+        return true;                                                                           \
     }
-    if (c.R == 32 && c.NW == 9)
-        return pipe_by_ng<32, 9, 6, 8, Q1>(c.NG, st, p, s, x, rows, groups, shift, y);
+    BS_PIPE_CONFIGS(BS_PIPE_CASE)
+#undef BS_PIPE_CASE
     return false;
 }
 

@@ -56,12 +56,15 @@ def test_row_block_kernel_beyond_128_groups(rows, k):
 
 
 @pytest.mark.parametrize("rows,k", [(4096, 3072), (4097, 3072), (4097, 128), (1, 128),
-                                    (13824, 2560), (6399, 5120), (6400, 5120), (300, 16384),
+                                    (13824, 2560), (10239, 2560), (10240, 2560), (10240, 128),
+                                    (10240, 256), (10240, 1152), (12000, 3072), (6399, 5120),
+                                    (6400, 5120), (10239, 5120), (10240, 5120), (300, 16384),
                                     (1, 16384), (2000, 16512), (9, 1152), (17, 4224)])
 def test_pipelined_launch_rule(rows, k):
     """Either side of the Q1_0 table of the pipelined kernel: up to 24 groups
-    16-row blocks with 2 groups per slice up to 4096 rows, 32-row blocks of 4
-    wavefronts above; the ternary table beyond; 129 groups take the row-block
+    16-row blocks with 2 groups per slice up to 4096 rows, whole 64-row tiles
+    of 4 wavefronts from 10240 (1 to 3 groups in flight), 32-row blocks of 4
+    between; the ternary table's blocks beyond; 129 groups take the row-block
     kernel."""
     check(*synth.q1(rows, k, rows + k))
 

@@ -67,24 +67,29 @@ def test_tall_shapes(rows, k):
     check(*synth.ternary(rows, k, seed=rows ^ k, p_zero=1 / 3, act="uniform127"))
 
 
-@pytest.mark.parametrize("rows,k", [(1024, 2560), (1025, 2560), (8191, 2560), (8192, 2560),
-                                    (8192, 8192), (8192, 8320), (8255, 1024), (2000, 16384),
-                                    (2000, 16512), (1023, 128 * 127), (300, 16384),
-                                    (7, 2560), (9, 1152), (17, 4224), (1, 16384),
-                                    (4096, 3072), (4097, 3072), (4097, 128), (13824, 2560)])
+@pytest.mark.parametrize("rows,k", [(1024, 2560), (1025, 2560), (2047, 2560), (2048, 2560),
+                                    (4096, 2560), (4097, 2560), (4097, 256), (8191, 2560),
+                                    (8192, 2560), (10239, 2560), (10240, 2560), (10240, 128),
+                                    (10240, 1152), (12000, 3072), (10239, 4096), (10240, 4096),
+                                    (6399, 5120), (6400, 5120), (10240, 5120), (8192, 8192),
+                                    (8192, 8320), (8255, 1024), (2000, 16384), (2000, 16512),
+                                    (1023, 128 * 127), (300, 16384), (7, 2560), (9, 1152),
+                                    (17, 4224), (1, 16384), (4096, 3072), (4097, 3072),
+                                    (4097, 128), (13824, 2560)])
 def test_pipelined_launch_rule(rows, k):
     """Either side of the pipelined kernel's launch-shape bounds: up to 24
-    groups 8-row blocks up to 4096 rows and 32-row blocks of 4 wavefronts
-    above; up to 40 groups 32-row blocks from 6400 rows, else 16-row blocks
-    with 2 groups per slice; 8 wavefronts of 16-row blocks up to 96 groups,
-    32-row blocks of 9 up to 128 (129 takes the row-block kernel); ragged
-    blocks and tiles, fewer groups than slices."""
+    groups 8-row blocks under 2048 rows, 16-row blocks to 4096, 32-row blocks
+    to 10240 and whole 64-row tiles from there (1 to 6 groups per slice); up
+    to 40 groups whole tiles from 10240 rows, 32-row blocks from 6400, else
+    16-row blocks with 2 groups per slice; 8 wavefronts of 16-row blocks up
+    to 96 groups, 32-row blocks of 8 up to 128 (129 takes the row-block
+    kernel); ragged blocks and tiles, fewer groups than slices."""
     check(*synth.ternary(rows, k, seed=rows + k, p_zero=1 / 3, act="uniform127"))
 
 
 @pytest.mark.parametrize("groups", [1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 40, 63, 64, 65,
                                     86, 100, 108, 120, 127, 128])
-@pytest.mark.parametrize("rows", [40, 1500, 8200])
+@pytest.mark.parametrize("rows", [40, 1500, 8200, 10300])
 def test_pipelined_wavefront_counts(groups, rows):
     """Every wavefront count and groups-per-slice of the pipelined kernel
     (padding slots past K, partly filled last rounds)."""
