@@ -26,8 +26,9 @@ ceiling, `bs_probe_read`) and the fraction of that ceiling reached.
 `context` holds the empty-kernel launch floor.
 
 `ops.f1` holds the activation-reuse sweep (N = 1 .. 8192 rows sharing one
-activation vector, ternary GEMV and both LNS8 paths, with the row count where
-the popcount path overtakes direct routing), the Phase B sweeps of the LNS8
+activation vector, ternary GEMV and the three LNS8 paths, with the row counts
+where popcount overtakes direct routing and matrix overtakes popcount), the
+Phase B sweeps of the LNS8
 GEMV (weight zero density, number of distinct activation codes) and the
 fused four-launch layer step.  Other `ops` entries time the rest of the path:
 Q1_0, LNS8 (with the VALU fraction), pure-LNS, the steps either side and the
@@ -87,14 +88,17 @@ BLOCKS = ["step", "roofline_graph", "context_floor", "ceiling_scrub",
           "f1_fused_step", "lmhead", "lns8", "flns", "q1", "edges", "lmhead_ceiling",
           "context_stream"]
 SHAPE_BLOCKS = ["gemv_%dx%d" % s for s in IN_RANGE + REPORTED]
-SWEEP_BLOCKS = ["f1_reuse_%s_n%d" % (p, n) for p in ("ternary", "direct", "popcount")
+SWEEP_BLOCKS = ["f1_reuse_%s_n%d" % (p, n) for p in ("ternary", "direct", "popcount", "matrix")
                 for n in (1, 8, 32, 128, 512, 2048, 8192)]
-PHASE_B_BLOCKS = (["f1_zero_%s_%s" % (p, z) for p in ("direct", "popcount")
+PHASE_B_BLOCKS = (["f1_zero_%s_%s" % (p, z) for p in ("direct", "popcount", "matrix")
                    for z in ("0", "1/3", "0.6", "0.9")] +
-                  ["f1_codes_%s_%d" % (p, m) for p in ("direct", "popcount")
+                  ["f1_codes_%s_%d" % (p, m) for p in ("direct", "popcount", "matrix")
                    for m in (1, 8, 41, 127)])
 ALL_BLOCKS = BLOCKS + SHAPE_BLOCKS + SWEEP_BLOCKS + PHASE_B_BLOCKS
 MARKER_ID = {name: i + 1 for i, name in enumerate(ALL_BLOCKS)}
+# the LNS8 paths by their bs.h ids (DIRECT, POPCOUNT, MATRIX)
+LNS8_PATHS_BY_ID = ((0, "direct"), (1, "popcount"), (2, "matrix"))
+LNS8_PATHS = LNS8_PATHS_BY_ID
 
 
 def weight_bytes(rows: int, k: int) -> int:
@@ -459,7 +463,7 @@ def run_f1(torch, bs, synth, dev, H):
     out = {}
     # reuse sweep at K = 4096 (the LNS8 workload's K): N rows share one x
     K = 4096
-    sweep = {"ternary": {}, "direct": {}, "popcount": {}}
+    sweep = {"ternary": {}, "direct": {}, "popcount": {}, "matrix": {}}
     for n_rows in (1, 8, 32, 128, 512, 2048, 8192):
         bufs, views, x, nb = packed_pool(torch, bs, synth, dev, n_rows, K, SHAPE_POOL_BYTES,
                                          max_copies=1024)
@@ -479,7 +483,7 @@ def run_f1(torch, bs, synth, dev, H):
         s8 = torch.empty(n_rows, dtype=torch.float64, device=dev)
         ws = torch.zeros(bs.lib().bs_lns8_workspace_bytes(n_rows, K), dtype=torch.uint8,
                          device=dev)
-        for path, name in ((bs.LNS8_DIRECT, "direct"), (bs.LNS8_POPCOUNT, "popcount")):
+        for path, name in LNS8_PATHS:
             us = H.per_launch(lambda i: bs.lns8_phase_gemv(pool[i % len(pool)], xd, n_rows, K,
                                                            path, acc=acc, s=s8, workspace=ws,
                                                            stream=H.stream), len(pool),
@@ -488,15 +492,20 @@ def run_f1(torch, bs, synth, dev, H):
                                         "weights_per_ns": round(n_rows * K / us / 1e3, 2)}
         del pool
         torch.cuda.empty_cache()
-    cross = None
-    for n_rows in (1, 8, 32, 128, 512, 2048, 8192):
-        if sweep["popcount"][str(n_rows)]["us"] <= sweep["direct"][str(n_rows)]["us"]:
-            cross = n_rows
-            break
+    def crossover(a, b):
+        for n_rows in (1, 8, 32, 128, 512, 2048, 8192):
+            if sweep[a][str(n_rows)]["us"] <= sweep[b][str(n_rows)]["us"]:
+                return n_rows
+        return None
+
+    cross = crossover("popcount", "direct")
     out["reuse_sweep_k4096"] = {**sweep, "crossover_rows": cross,
                                 "crossover_note": "smallest row count (of those swept) where the "
                                                   "popcount path is at least as fast as direct "
-                                                  "routing; null if it never is"}
+                                                  "routing; null if it never is",
+                                "matrix_crossover_rows": crossover("matrix", "popcount"),
+                                "matrix_crossover_note": "smallest row count where the matrix "
+                                                         "path is at least as fast as popcount"}
     log("f1 reuse sweep: crossover at %s rows" % cross)
     # Phase B: weight zero density and the number of distinct codes, 4096 x 4096
     R = 4096
@@ -517,7 +526,7 @@ def run_f1(torch, bs, synth, dev, H):
             ws = torch.zeros(bs.lib().bs_lns8_workspace_bytes(R, K), dtype=torch.uint8,
                              device=dev)
             ent = {}
-            for path, name in ((bs.LNS8_DIRECT, "direct"), (bs.LNS8_POPCOUNT, "popcount")):
+            for path, name in LNS8_PATHS:
                 blk = ("f1_zero_%s_%s" % (name, label) if kind == "zero_density"
                        else "f1_codes_%s_%d" % (name, v))
                 us = H.per_launch(lambda i: bs.lns8_phase_gemv(pool[i % len(pool)], xd, R, K,
@@ -583,7 +592,7 @@ def lns8_valu_ops(path: int) -> float:
             vals[a.strip()] = b.strip()
     if vals.get("kernel_source_sha256_16") != _source_digest("lns8_phase.hip"):
         return None
-    key = "valu_insts_per_call_" + ("direct" if path == 0 else "popcount")
+    key = "valu_insts_per_call_" + dict(LNS8_PATHS_BY_ID)[path]
     try:
         return float(vals[key])
     except (KeyError, ValueError):
@@ -641,7 +650,7 @@ def run_extras(torch, bs, synth, dev, H):
     s8 = torch.empty(4096, dtype=torch.float64, device=dev)
     ws8 = torch.zeros(bs.lib().bs_lns8_workspace_bytes(4096, 4096), dtype=torch.uint8, device=dev)
     H.marker("lns8")
-    for path, name in ((bs.LNS8_DIRECT, "direct"), (bs.LNS8_POPCOUNT, "popcount")):
+    for path, name in LNS8_PATHS:
         us = H.per_launch(lambda i: bs.lns8_phase_gemv(pool8[i % len(pool8)], xd8, 4096, 4096,
                                                        path, acc=acc, s=s8, workspace=ws8,
                                                        stream=H.stream), len(pool8))
@@ -840,8 +849,8 @@ def traffic_run(shape: str, launches: int = 20):
 
 def lns8_counter_run(launches: int = 10):
     """Workload for the rocprofv3 --pmc runs behind the LNS8 VALU fraction:
-    `launches` calls of each LNS8 path (direct, then popcount) at 4096 x 4096
-    on distinct weight buffers."""
+    `launches` calls of each LNS8 path (direct, popcount, matrix) at 4096 x
+    4096 on distinct weight buffers."""
     import torch
     import bit_decode_gemv_amd as bs
     from bit_decode_gemv_amd import synth
@@ -850,7 +859,7 @@ def lns8_counter_run(launches: int = 10):
     p8 = torch.from_numpy(bs.ternary_pack(t8)).to(dev)
     pool = [p8.clone() for _ in range(launches)]
     xd = torch.from_numpy(x8).to(dev)
-    for path in (bs.LNS8_DIRECT, bs.LNS8_POPCOUNT):
+    for path, _ in LNS8_PATHS:
         for i in range(launches):
             bs.lns8_phase_gemv(pool[i], xd, 4096, 4096, path)
         torch.cuda.synchronize()
@@ -919,7 +928,8 @@ def counter_summary(*paths: str):
 
 def lns8_valu_summary(path: str):
     """The LNS8 counter record: every counter's mean per call of each path
-    (lns8_kernel = direct routing, lns8_pc_kernel = popcount histogram) from a
+    (lns8_kernel = direct routing, lns8_pc_kernel = popcount histogram,
+    lns8_mx_kernel = the matrix contraction) from a
     --pmc CSV of --lns8-counter-run, keyed to the kernel source it was taken
     on."""
     vals = {}
@@ -927,6 +937,8 @@ def lns8_valu_summary(path: str):
         name = r["Kernel_Name"]
         if "lns8_pc_kernel" in name:
             p = "popcount"
+        elif "lns8_mx_kernel" in name:
+            p = "matrix"
         elif "lns8_kernel" in name:
             p = "direct"
         else:

@@ -26,7 +26,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "bs.h")
 
 BS_OK, BS_E_NULL, BS_E_SHAPE, BS_E_RANGE, BS_E_OVERFLOW, BS_E_HIP, BS_E_WORKSPACE, BS_E_ALIGN = (
     0, -1, -2, -3, -4, -5, -6, -7)
-LNS8_DIRECT, LNS8_POPCOUNT = 0, 1
+LNS8_DIRECT, LNS8_POPCOUNT, LNS8_MATRIX = 0, 1, 2
 
 _lib = None
 

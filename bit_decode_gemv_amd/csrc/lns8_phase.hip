@@ -107,38 +107,27 @@ __device__ __forceinline__ void lns8_unit(const uint8_t *__restrict__ planes,
     }
 }
 
-// One workgroup per (64-row tile, split): wavefront w takes the units (64
-// positions each, two per group) [(split * W + w) * upw, ... + upw).
-__global__ __launch_bounds__(1024) void lns8_kernel(
-    const uint8_t *__restrict__ planes, const uint8_t *__restrict__ x, int rows, int groups,
-    int upw, int nsplit, int32_t *__restrict__ acc_out, double *__restrict__ s_out,
-    int *__restrict__ counters, int *__restrict__ partial) {
-    __shared__ int red[16][8][64];
-    __shared__ int last;
-    const int tile = blockIdx.x / nsplit;
-    const int split = blockIdx.x - tile * nsplit;
-    const int nw = blockDim.x >> 6;
-    // uniform: the activation bytes of DIRECT then come through scalar loads
-    // and the phase routing is a scalar branch
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int u0 = (split * nw + wave) * upw;
-    const int u1 = min(2 * groups, u0 + upw);
-
-    int A[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int u = u0; u < u1; ++u) lns8_unit(planes, x, tile, groups, u, lane, A);
-#pragma unroll
-    for (int p = 0; p < 8; ++p) red[wave][p][lane] = A[p];
-    __syncthreads();
+// The end of a (tile, split) workgroup of the split-K mappings.  red[w][p][j]
+// holds wavefront w's A[p] of row j of the tile (the first nw wavefronts);
+// the wavefronts are summed, the splits of the tile meet through the
+// workspace (the last to arrive sums them), and A and S are stored.  Every
+// thread of the workgroup calls it.
+template <int MAXW>
+__device__ __forceinline__ void tile_finish(int (&red)[MAXW][8][64], int &last, int nw, int tile,
+                                            int split, int nsplit, int rows,
+                                            int32_t *__restrict__ acc_out,
+                                            double *__restrict__ s_out,
+                                            int *__restrict__ counters,
+                                            int *__restrict__ partial) {
     // pair (p, j) sums phase p of row j over the wavefronts; the 512 pairs
     // are shared out over however many threads the workgroup has
     for (int idx = threadIdx.x; idx < 512; idx += blockDim.x) {
         const int p = idx >> 6, j = idx & 63;
-        // all sixteen reads in flight at once; wavefronts past nw (whose
-        // slots were never written) are masked out
+        // all the reads in flight at once; wavefronts past nw (whose slots
+        // were never written) are masked out
         int t = 0;
 #pragma unroll
-        for (int w = 0; w < 16; ++w) t += red[w][p][j] & -(int)(w < nw);
+        for (int w = 0; w < MAXW; ++w) t += red[w][p][j] & -(int)(w < nw);
         red[0][p][j] = t;   // wavefront 0's entry of this pair is read only here
     }
     __syncthreads();
@@ -189,6 +178,32 @@ __global__ __launch_bounds__(1024) void lns8_kernel(
             if (s_out) s_out[row] = materialize(T);
         }
     }
+}
+
+// One workgroup per (64-row tile, split): wavefront w takes the units (64
+// positions each, two per group) [(split * W + w) * upw, ... + upw).
+__global__ __launch_bounds__(1024) void lns8_kernel(
+    const uint8_t *__restrict__ planes, const uint8_t *__restrict__ x, int rows, int groups,
+    int upw, int nsplit, int32_t *__restrict__ acc_out, double *__restrict__ s_out,
+    int *__restrict__ counters, int *__restrict__ partial) {
+    __shared__ int red[16][8][64];
+    __shared__ int last;
+    const int tile = blockIdx.x / nsplit;
+    const int split = blockIdx.x - tile * nsplit;
+    const int nw = blockDim.x >> 6;
+    // uniform: the activation bytes of DIRECT then come through scalar loads
+    // and the phase routing is a scalar branch
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int u0 = (split * nw + wave) * upw;
+    const int u1 = min(2 * groups, u0 + upw);
+
+    int A[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int u = u0; u < u1; ++u) lns8_unit(planes, x, tile, groups, u, lane, A);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) red[wave][p][lane] = A[p];
+    __syncthreads();
+    tile_finish<16>(red, last, nw, tile, split, nsplit, rows, acc_out, s_out, counters, partial);
 }
 
 // POPCOUNT without a split of K.  A workgroup owns 16 rows and all of K: in
@@ -358,6 +373,147 @@ __global__ __launch_bounds__(1024) void lns8_pc_kernel(
     }
 }
 
+// MATRIX: the direct routing written as a contraction.  Over the columns
+// (p, h) of a 16-column matrix X, X[k][(p, h)] = 2^(E4 & 7) when position k
+// has phase p, E4 >> 3 = h and a nonzero code, else 0, and
+//   A[p] = sum_k t'_k X[k][(p, 0)] + 256 * sum_k t'_k X[k][(p, 1)]
+// with t' = nz - 2 pneg the signed trits (pneg = nz & (S1 ^ neg), as in
+// POPCOUNT): each product lands in exactly one column, its phase's, scaled
+// by the band's low three bits.  The contraction runs on the int8 matrix
+// instruction of 16 rows x 16 columns x 64 positions.  X's entries reach
+// 128, one past int8, so the matrix holds X - 1 (0..127 where the code
+// matches the column, -1 elsewhere) and the row's trit sum U = sum_k t'_k,
+// subtracted from every column, is added back: A[p] = C[(p, 0)] + 256 *
+// C[(p, 1)] + 257 * U.
+//
+// Mapping: like POPCOUNT, one workgroup per 16 rows (one slice of a tile)
+// and all of K, so no workspace and no second pass; its wavefronts take
+// whole groups of 128 positions in turn and meet in LDS.  Lane l of a
+// wavefront holds, for its lane group q = l / 16, positions 32q .. 32q+31 of
+// the group: as A operand the trits of row l % 16, as B operand the entries
+// of column l % 16 (the instruction pairs A's and B's bytes by lane group
+// and byte, so any assignment of positions to them serves if both use it;
+// here byte b of step h is position 32q + 16h + b).  The sixteen trits of a
+// step come from the row's nz and pneg bits one nibble at a time: a 24-bit
+// multiply by 0x204081 (0x408102) copies a nibble's bits to the low (second)
+// bit of four bytes without overlap, and a byte permute maps the 2-bit
+// pattern nz + 2 pneg to 0, 1 or 0xFF.  A column's byte is one permute of a
+// table of 2^j - 1 indexed by E4 & 7, the index forced past 12 (byte 0xFF)
+// when the phase or the band half differs.  Code 0 (phase 0, band 0)
+// matches column (0, 0) at index 0, where that column's table holds -1: no
+// product.
+
+// int8 trits n_i - 2 m_i of bits sh .. sh+3 (m a subset of n), byte i = bit sh + i
+__device__ __forceinline__ int trits4(uint32_t n, uint32_t m, int sh) {
+    const uint32_t a = (__builtin_amdgcn_ubfe(n, sh, 4) * 0x204081u) & 0x01010101u;
+    const uint32_t sel = ((__builtin_amdgcn_ubfe(m, sh, 4) * 0x408102u) & 0x02020202u) | a;
+    return (int)__builtin_amdgcn_perm(0u, 0xFF000100u, sel);
+}
+
+// column bytes of four codes: table[E4 & 7] where (code ^ key) & 0x47 is 0
+// (same phase and band half), else 0xFF
+__device__ __forceinline__ int xcol4(uint32_t w, uint32_t key, uint32_t tlo, uint32_t thi) {
+    const uint32_t y = ((w ^ key) & 0x47474747u) + 0x7F7F7F7Fu;   // bit 7: mismatch
+    const uint32_t sel = (y & 0x80808080u) | ((w >> 3) & 0x07070707u);
+    return (int)__builtin_amdgcn_perm(thi, tlo, sel);
+}
+
+typedef int mx_v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kMxRows = 16;   // rows per workgroup
+
+__global__ __launch_bounds__(1024) void lns8_mx_kernel(
+    const uint8_t *__restrict__ planes, const uint8_t *__restrict__ x, int rows, int groups,
+    int32_t *__restrict__ acc_out, double *__restrict__ s_out) {
+    __shared__ int red[8][kMxRows];          // A[p] of the 16 rows, summed with ds_add
+    const int nw = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 15, q = lane >> 4;
+    const int row = blockIdx.x * kMxRows + c;   // < the padded row count
+    const int tile = row >> 6, rit = row & 63;
+    // column (c & 7, c >> 3) of X - 1; table[j] = 2^j - 1, column (0, 0)'s
+    // entry 0 (code 0 only) -1
+    const uint32_t key = (uint32_t)((c & 7) | ((c >> 3) << 6)) * 0x01010101u;
+    const uint32_t tlo = c == 0 ? 0x070301FFu : 0x07030100u, thi = 0x7F3F1F0Fu;
+
+    for (int i = threadIdx.x; i < 8 * kMxRows; i += blockDim.x) (&red[0][0])[i] = 0;
+    mx_v4i acc = {0, 0, 0, 0};
+    int un = 0, ug = 0;
+    const uint8_t *pt = planes + (size_t)tile * groups * 2048 + 16 * rit + 4 * q;
+    // a group's inputs: the lane group's 32 codes, one code per lane for the
+    // sign ballots, and the lane's row's nz and neg words
+    struct In {
+        uint4 w0, w1;
+        int b0, b1;
+        uint32_t n, ng;
+    };
+    auto load = [&](int g) {
+        In v;
+        const uint8_t *xg = x + (size_t)g * 128;
+        v.w0 = *reinterpret_cast<const uint4 *>(xg + 32 * q);
+        v.w1 = *reinterpret_cast<const uint4 *>(xg + 32 * q + 16);
+        v.b0 = xg[lane];
+        v.b1 = xg[64 + lane];
+        v.n = *reinterpret_cast<const uint32_t *>(pt + (size_t)g * 2048);
+        v.ng = *reinterpret_cast<const uint32_t *>(pt + (size_t)g * 2048 + 1024);
+        return v;
+    };
+    // the next group's loads are issued before the current group's
+    // arithmetic
+    In cur = load(wave < groups ? wave : 0);
+    for (int g = wave; g < groups; g += nw) {
+        const In in = cur;
+        if (g + nw < groups) cur = load(g + nw);
+        // S1 of positions 32q .. 32q+31
+        const uint64_t s0 = __ballot(in.b0 & 0x80), s1 = __ballot(in.b1 & 0x80);
+        const uint64_t sq = q < 2 ? s0 : s1;
+        const uint32_t sg = (q & 1) ? (uint32_t)(sq >> 32) : (uint32_t)sq;
+        const uint32_t n = in.n, m = n & (in.ng ^ sg);
+        un = bcnt_add(n, un);
+        ug = bcnt_add(m, ug);
+        const mx_v4i xb0 = {xcol4(in.w0.x, key, tlo, thi), xcol4(in.w0.y, key, tlo, thi),
+                            xcol4(in.w0.z, key, tlo, thi), xcol4(in.w0.w, key, tlo, thi)};
+        const mx_v4i a0 = {trits4(n, m, 0), trits4(n, m, 4), trits4(n, m, 8),
+                           trits4(n, m, 12)};
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, xb0, acc, 0, 0, 0);
+        const mx_v4i xb1 = {xcol4(in.w1.x, key, tlo, thi), xcol4(in.w1.y, key, tlo, thi),
+                            xcol4(in.w1.z, key, tlo, thi), xcol4(in.w1.w, key, tlo, thi)};
+        const mx_v4i a1 = {trits4(n, m, 16), trits4(n, m, 20), trits4(n, m, 24),
+                           trits4(n, m, 28)};
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, xb1, acc, 0, 0, 0);
+    }
+    // lane (c, q) holds C[row 4q + v][column c]; lanes c < 8 combine columns
+    // (c, 0) and (c, 1) (lane c + 8, a DPP rotate by 8 within the 16-lane row)
+    // with the row's U (lane 4q + v once the lane groups' counts are summed),
+    // and the wavefronts meet by LDS atomic adds (integer addition: the order
+    // is free)
+    const int u = add_quarters(un - 2 * ug);
+    __syncthreads();   // red is zero
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int hi = __builtin_amdgcn_mov_dpp(acc[v], 0x128, 0xF, 0xF, false);
+        const int ur = __shfl(u, 4 * q + v);
+        // modulo 2^32 (the sum, A[p], fits int32; its terms need not)
+        if (c < 8)
+            atomicAdd(&red[c][4 * q + v],
+                      (int)((uint32_t)acc[v] + 256u * (uint32_t)hi + 257u * (uint32_t)ur));
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < kMxRows) {
+        const int rr = blockIdx.x * kMxRows + threadIdx.x;
+        if (rr < rows) {
+            int T[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) T[p] = red[p][threadIdx.x];
+            int4 *dst = reinterpret_cast<int4 *>(acc_out + (size_t)rr * 8);
+            dst[0] = make_int4(T[0], T[1], T[2], T[3]);
+            dst[1] = make_int4(T[4], T[5], T[6], T[7]);
+            if (s_out) s_out[rr] = materialize(T);
+        }
+    }
+}
+
 }  // namespace
 }  // namespace bs
 
@@ -424,13 +580,25 @@ extern "C" int32_t bs_lns8_phase_gemv(const uint8_t *planes, const uint8_t *x_ln
                                       void *stream) {
     if (!planes || !x_lns8 || !acc) return BS_E_NULL;
     if (int32_t st = check_rows_k(rows, k, kLns8MaxK)) return st;
-    if (path != BS_LNS8_DIRECT && path != BS_LNS8_POPCOUNT) return BS_E_RANGE;
+    if (path != BS_LNS8_DIRECT && path != BS_LNS8_POPCOUNT && path != BS_LNS8_MATRIX)
+        return BS_E_RANGE;
     if (((uintptr_t)planes & 15) || ((uintptr_t)x_lns8 & 3) || ((uintptr_t)acc & 3) ||
         ((uintptr_t)s & 7))
         return BS_E_ALIGN;
     if (!ws_ok(workspace, workspace_bytes, lns8_ws_bytes(rows, k))) return BS_E_WORKSPACE;
 
     hipStream_t st = (hipStream_t)stream;
+    if (path == BS_LNS8_MATRIX) {
+        // 16 rows and all of K per workgroup, up to 16 wavefronts taking
+        // whole groups; the workspace is not touched
+        const int64_t groups = k / kGroup;
+        const int64_t nw = groups < 16 ? groups : 16;
+        const int64_t blocks = (rows + kMxRows - 1) / kMxRows;
+        hipLaunchKernelGGL(lns8_mx_kernel, dim3((unsigned)blocks), dim3((unsigned)(nw * 64)), 0,
+                           st, planes, x_lns8, (int)rows, (int)groups, acc, s);
+        BS_LAUNCH_CHECK();
+        return BS_OK;
+    }
     if (path == BS_LNS8_POPCOUNT) {
         // 16 rows and all of K per workgroup; the workspace is not touched
         const int64_t units = 2 * (k / kGroup);

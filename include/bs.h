@@ -182,18 +182,23 @@ int32_t bs_q1_gemv(const uint8_t *bits, const int16_t *scales, const int8_t *x, 
  *           (A_s: the unit's positions holding code s),
  *           C_s = popcount(A_s & W_nonzero) - 2*popcount(A_s & W_nonzero &
  *           (sign XOR W_negative)), H[phase][band] += C_s,
- *           A[p] = sum_b H[p][b] * 2^b ([BS] sections 3.1, 4).
- *           Both paths return identical bytes.
+ *           A[p] = sum_b H[p][b] * 2^b ([BS] sections 3.1, 4);
+ *           BS_LNS8_MATRIX (2): the direct routing as a contraction on the
+ *           int8 matrix instructions, A[p] = sum_k t_k X[k][(p, 0)] + 256 *
+ *           sum_k t_k X[k][(p, 1)] with t_k the product sign and X[k][(p, h)]
+ *           = 2^(E4 & 7) where position k has phase p, E4 >> 3 = h and a
+ *           nonzero code.
+ *           All three paths return identical bytes.
  *   rows    1 .. 2^31 - 64;  k >= 128, k % 128 == 0, k <= 65408 (|A| <= k*2^15 must
  *           fit int32, else BS_E_OVERFLOW)
  *   planes  device, 16-byte aligned; x_lns8 device uint8[k], 4-byte aligned
  *   acc     device int32[rows][8], overwritten, 4-byte aligned
  *   s       device double[rows], or NULL to skip the materialisation
  *   workspace  device scratch of at least bs_lns8_workspace_bytes(rows, k)
- *           bytes, 256-byte aligned, caller-owned (the same size for both
- *           paths): when DIRECT splits K over several workgroups, a counter
- *           per 64-row tile and the partial accumulators; POPCOUNT does not
- *           touch it.  Zero it before its first use; every call leaves it
+ *           bytes, 256-byte aligned, caller-owned (the same size for every
+ *           path): when DIRECT splits K over several workgroups, a counter
+ *           per 64-row tile and the partial accumulators; POPCOUNT and
+ *           MATRIX do not touch it.  Zero it before its first use; every call leaves it
  *           zero again, so one workspace serves calls of any shape ordered
  *           on one stream.  Calls that may overlap need separate
  *           workspaces.
@@ -202,6 +207,7 @@ int32_t bs_q1_gemv(const uint8_t *bits, const int16_t *scales, const int8_t *x, 
  */
 #define BS_LNS8_DIRECT 0
 #define BS_LNS8_POPCOUNT 1
+#define BS_LNS8_MATRIX 2
 size_t bs_lns8_workspace_bytes(int64_t rows, int64_t k);
 int32_t bs_lns8_phase_gemv(const uint8_t *planes, const uint8_t *x_lns8, int64_t rows,
                            int64_t k, int32_t path, int32_t *acc, double *s,

@@ -136,7 +136,7 @@ def test_lns8_validation():
     assert _lns8(x=None) == bs.BS_E_NULL
     assert _lns8(acc=None) == bs.BS_E_NULL
     assert _lns8(k=64) == bs.BS_E_SHAPE
-    assert _lns8(path=2) == bs.BS_E_RANGE
+    assert _lns8(path=3) == bs.BS_E_RANGE
     assert _lns8(k=65536) == bs.BS_E_OVERFLOW       # |A| <= k*2^15 would not fit int32
     assert _lns8(ws=None) == bs.BS_E_WORKSPACE
     assert _lns8(wsn=8) == bs.BS_E_WORKSPACE

@@ -116,7 +116,7 @@ def test_lns8_valu_record_round_trip(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     fields = ["Kernel_Name", "Counter_Name", "Counter_Value"]
     rows = []
-    for name, v in (("lns8_kernel", 1000.0), ("lns8_pc_kernel", 700.0)):
+    for name, v in (("lns8_kernel", 1000.0), ("lns8_pc_kernel", 700.0), ("lns8_mx_kernel", 400.0)):
         for i in range(3):
             rows.append({"Kernel_Name": "void bs::(anonymous namespace)::%s(args)" % name,
                          "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": v + i})
@@ -130,6 +130,7 @@ def test_lns8_valu_record_round_trip(tmp_path, monkeypatch):
         "# header\n" + bench.lns8_valu_summary(str(tmp_path / "c.csv")) + "\n")
     assert bench.lns8_valu_ops(0) == pytest.approx(1001.0)
     assert bench.lns8_valu_ops(1) == pytest.approx(701.0)
+    assert bench.lns8_valu_ops(2) == pytest.approx(401.0)
     with open(tmp_path / "bit_decode_gemv_amd" / "csrc" / "lns8_phase.hip", "a") as f:
         f.write("\n// edit\n")
     assert bench.lns8_valu_ops(0) is None
