@@ -393,15 +393,19 @@ __global__ __launch_bounds__(1024) void lns8_pc_kernel(
 // the group: as A operand the trits of row l % 16, as B operand the entries
 // of column l % 16 (the instruction pairs A's and B's bytes by lane group
 // and byte, so any assignment of positions to them serves if both use it;
-// here byte b of step h is position 32q + 16h + b).  The sixteen trits of a
-// step come from the row's nz and pneg bits one nibble at a time: a 24-bit
-// multiply by 0x204081 (0x408102) copies a nibble's bits to the low (second)
-// bit of four bytes without overlap, and a byte permute maps the 2-bit
-// pattern nz + 2 pneg to 0, 1 or 0xFF.  A column's byte is one permute of a
-// table of 2^j - 1 indexed by E4 & 7, the index forced past 12 (byte 0xFF)
-// when the phase or the band half differs.  Code 0 (phase 0, band 0)
-// matches column (0, 0) at index 0, where that column's table holds -1: no
-// product.
+// here byte b of step h is position 32q + 16h + b).
+//
+// The activations are staged once per workgroup in LDS, a chunk of up to 64
+// groups at a time: per position the byte (E4 & 7) | phase << 4 | (E4 >> 3)
+// << 7, and per 64 positions the S1 mask.  A column's byte is then one
+// permute of a table of 2^j - 1 indexed by that byte XOR the column's key
+// (phase << 4 | half << 7): the index is E4 & 7 when phase and band half
+// match and 16 or more (byte 0xFF) when they differ.  Code 0 (phase 0, band
+// 0) matches column (0, 0) at index 0, where that column's table holds -1:
+// no product.  The sixteen trits of a step come from the row's nz and pneg
+// bits one nibble at a time: a 24-bit multiply by 0x204081 (0x408102) copies
+// a nibble's bits to the low (second) bit of four bytes without overlap, and
+// a byte permute maps the 2-bit pattern nz + 2 pneg to 0, 1 or 0xFF.
 
 // int8 trits n_i - 2 m_i of bits sh .. sh+3 (m a subset of n), byte i = bit sh + i
 __device__ __forceinline__ int trits4(uint32_t n, uint32_t m, int sh) {
@@ -410,78 +414,127 @@ __device__ __forceinline__ int trits4(uint32_t n, uint32_t m, int sh) {
     return (int)__builtin_amdgcn_perm(0u, 0xFF000100u, sel);
 }
 
-// column bytes of four codes: table[E4 & 7] where (code ^ key) & 0x47 is 0
-// (same phase and band half), else 0xFF
-__device__ __forceinline__ int xcol4(uint32_t w, uint32_t key, uint32_t tlo, uint32_t thi) {
-    const uint32_t y = ((w ^ key) & 0x47474747u) + 0x7F7F7F7Fu;   // bit 7: mismatch
-    const uint32_t sel = (y & 0x80808080u) | ((w >> 3) & 0x07070707u);
-    return (int)__builtin_amdgcn_perm(thi, tlo, sel);
+// column bytes of four staged positions: table[E4 & 7] where the phase and
+// band half match the column's key, else 0xFF
+__device__ __forceinline__ int xcol4(uint32_t v, uint32_t key, uint32_t tlo, uint32_t thi) {
+    return (int)__builtin_amdgcn_perm(thi, tlo, v ^ key);
+}
+
+// staged byte of four LNS8 codes: E4 & 7 in bits 0-2, the phase in bits 4-6,
+// E4 >> 3 in bit 7 (S1 is dropped; it is staged as a mask)
+__device__ __forceinline__ uint32_t mx_stage4(uint32_t w) {
+    return ((w >> 3) & 0x07070707u) | ((w & 0x07070707u) << 4) | ((w << 1) & 0x80808080u);
 }
 
 typedef int mx_v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kMxRows = 16;   // rows per workgroup
+constexpr int kMxRows = 16;    // rows per workgroup
+constexpr int kMxChunk = 64;   // groups staged in LDS at a time (a multiple of every
+                               // wavefront count the launch uses when groups >= 16)
 
 __global__ __launch_bounds__(1024) void lns8_mx_kernel(
     const uint8_t *__restrict__ planes, const uint8_t *__restrict__ x, int rows, int groups,
     int32_t *__restrict__ acc_out, double *__restrict__ s_out) {
-    __shared__ int red[8][kMxRows];          // A[p] of the 16 rows, summed with ds_add
+    __shared__ uint4 xv[kMxChunk * 8];        // staged bytes, 128 per group
+    __shared__ uint64_t xs[kMxChunk * 2];     // S1 masks, 64 positions each
+    __shared__ int red[8][kMxRows];           // A[p] of the 16 rows, summed with ds_add
     const int nw = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int c = lane & 15, q = lane >> 4;
     const int row = blockIdx.x * kMxRows + c;   // < the padded row count
     const int tile = row >> 6, rit = row & 63;
-    // column (c & 7, c >> 3) of X - 1; table[j] = 2^j - 1, column (0, 0)'s
-    // entry 0 (code 0 only) -1
-    const uint32_t key = (uint32_t)((c & 7) | ((c >> 3) << 6)) * 0x01010101u;
+    // column (c & 7, c >> 3) of X - 1: key phase << 4 | half << 7; table[j] =
+    // 2^j - 1, column (0, 0)'s entry 0 (code 0 only) -1
+    const uint32_t key = (uint32_t)(((c & 7) << 4) | ((c >> 3) << 7)) * 0x01010101u;
     const uint32_t tlo = c == 0 ? 0x070301FFu : 0x07030100u, thi = 0x7F3F1F0Fu;
 
     for (int i = threadIdx.x; i < 8 * kMxRows; i += blockDim.x) (&red[0][0])[i] = 0;
     mx_v4i acc = {0, 0, 0, 0};
     int un = 0, ug = 0;
+    // the lane's row's nz and neg words of a group (positions 32q .. 32q+31)
     const uint8_t *pt = planes + (size_t)tile * groups * 2048 + 16 * rit + 4 * q;
-    // a group's inputs: the lane group's 32 codes, one code per lane for the
-    // sign ballots, and the lane's row's nz and neg words
-    struct In {
-        uint4 w0, w1;
-        int b0, b1;
-        uint32_t n, ng;
+    auto load = [&](int g, uint32_t &n, uint32_t &ng) {
+        n = *reinterpret_cast<const uint32_t *>(pt + (size_t)g * 2048);
+        ng = *reinterpret_cast<const uint32_t *>(pt + (size_t)g * 2048 + 1024);
     };
-    auto load = [&](int g) {
-        In v;
-        const uint8_t *xg = x + (size_t)g * 128;
-        v.w0 = *reinterpret_cast<const uint4 *>(xg + 32 * q);
-        v.w1 = *reinterpret_cast<const uint4 *>(xg + 32 * q + 16);
-        v.b0 = xg[lane];
-        v.b1 = xg[64 + lane];
-        v.n = *reinterpret_cast<const uint32_t *>(pt + (size_t)g * 2048);
-        v.ng = *reinterpret_cast<const uint32_t *>(pt + (size_t)g * 2048 + 1024);
-        return v;
-    };
-    // the next group's loads are issued before the current group's
-    // arithmetic
-    In cur = load(wave < groups ? wave : 0);
-    for (int g = wave; g < groups; g += nw) {
-        const In in = cur;
-        if (g + nw < groups) cur = load(g + nw);
-        // S1 of positions 32q .. 32q+31
-        const uint64_t s0 = __ballot(in.b0 & 0x80), s1 = __ballot(in.b1 & 0x80);
-        const uint64_t sq = q < 2 ? s0 : s1;
-        const uint32_t sg = (q & 1) ? (uint32_t)(sq >> 32) : (uint32_t)sq;
-        const uint32_t n = in.n, m = n & (in.ng ^ sg);
+    // one group of the staged chunk (index gl)
+    auto work = [&](int gl, uint32_t n, uint32_t ng) {
+        const uint32_t sg = reinterpret_cast<const uint32_t *>(xs)[4 * gl + q];
+        const uint4 w0 = xv[8 * gl + 2 * q], w1 = xv[8 * gl + 2 * q + 1];
+        const uint32_t m = n & (ng ^ sg);
         un = bcnt_add(n, un);
         ug = bcnt_add(m, ug);
-        const mx_v4i xb0 = {xcol4(in.w0.x, key, tlo, thi), xcol4(in.w0.y, key, tlo, thi),
-                            xcol4(in.w0.z, key, tlo, thi), xcol4(in.w0.w, key, tlo, thi)};
+        const mx_v4i xb0 = {xcol4(w0.x, key, tlo, thi), xcol4(w0.y, key, tlo, thi),
+                            xcol4(w0.z, key, tlo, thi), xcol4(w0.w, key, tlo, thi)};
         const mx_v4i a0 = {trits4(n, m, 0), trits4(n, m, 4), trits4(n, m, 8),
                            trits4(n, m, 12)};
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, xb0, acc, 0, 0, 0);
-        const mx_v4i xb1 = {xcol4(in.w1.x, key, tlo, thi), xcol4(in.w1.y, key, tlo, thi),
-                            xcol4(in.w1.z, key, tlo, thi), xcol4(in.w1.w, key, tlo, thi)};
+        const mx_v4i xb1 = {xcol4(w1.x, key, tlo, thi), xcol4(w1.y, key, tlo, thi),
+                            xcol4(w1.z, key, tlo, thi), xcol4(w1.w, key, tlo, thi)};
         const mx_v4i a1 = {trits4(n, m, 16), trits4(n, m, 20), trits4(n, m, 24),
                            trits4(n, m, 28)};
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, xb1, acc, 0, 0, 0);
+    };
+    // the wavefront's groups are wave, wave + nw, ...; two register sets
+    // alternate so the next group's words load while one is computed (nw <=
+    // groups, so the first exists)
+    // The activations of a chunk: every byte is loaded before any is used (one
+    // round trip); a chunk holds at most 8 positions per thread (blockDim is
+    // 64 per group below 16 groups, else 1024, and a chunk 128 positions per
+    // group, at most 64 groups).  The bounds are wavefront-uniform: i - lane
+    // is a multiple of 64, and so is a chunk's position count.
+    uint32_t xb[8];
+    auto stage_load = [&](int c0, int npos) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = threadIdx.x + j * blockDim.x;
+            xb[j] = i < npos ? x[(size_t)c0 * 128 + i] : 0u;
+        }
+    };
+    auto stage_store = [&](int npos) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = threadIdx.x + j * blockDim.x;
+            if (i < npos) {
+                reinterpret_cast<uint8_t *>(xv)[i] = (uint8_t)mx_stage4(xb[j]);
+                const uint64_t s1 = __ballot(xb[j] & 0x80);
+                if (lane == 0) xs[i >> 6] = s1;
+            }
+        }
+    };
+    // the wavefront's groups are wave, wave + nw, ...; two register sets
+    // alternate so the next group's words load while one is computed (nw <=
+    // groups, so the first exists).  The first group's words are requested
+    // after the first chunk's bytes, so staging waits on those bytes alone.
+    uint32_t na, nga, nb = 0, ngb = 0;
+    int cend = kMxChunk < groups ? kMxChunk : groups;
+    stage_load(0, cend * 128);
+    load(wave, na, nga);
+    stage_store(cend * 128);
+    __syncthreads();
+    for (int c0 = 0; c0 < groups; c0 += kMxChunk) {
+        cend = c0 + kMxChunk < groups ? c0 + kMxChunk : groups;
+        if (c0) {
+            __syncthreads();   // every wavefront is done with the last chunk
+            stage_load(c0, (cend - c0) * 128);
+            stage_store((cend - c0) * 128);
+            __syncthreads();
+        }
+        // the wavefront's first group of the chunk: c0 is a multiple of nw
+        // whenever there is more than one chunk (nw = 16), and the words of
+        // that group are in na, nga
+        for (int g = c0 + wave; g < cend; g += 2 * nw) {
+            if (g + nw < groups) load(g + nw, nb, ngb);
+            work(g - c0, na, nga);
+            if (g + nw >= cend) {
+                na = nb;
+                nga = ngb;
+                break;
+            }
+            if (g + 2 * nw < groups) load(g + 2 * nw, na, nga);
+            work(g + nw - c0, nb, ngb);
+        }
     }
     // lane (c, q) holds C[row 4q + v][column c]; lanes c < 8 combine columns
     // (c, 0) and (c, 1) (lane c + 8, a DPP rotate by 8 within the 16-lane row)
