@@ -7,12 +7,15 @@
 // product adds +-(1 << E4) to one of eight int32 accumulators A[L3]; the row
 // result S = 2^-9 * sum_p A[p] * F[p] is materialised once per row.
 //
-// Two reductions, identical in result:
+// Three reductions, identical in result:
 //   DIRECT   -- per product position, route +-(1 << E4) to A[L3];
 //   POPCOUNT -- per state s (a code 1..127: the positions holding it), the
 //               signed count C_s of the row's nonzero weights there, added
 //               as C_s << band into A[phase]: the histogram H[phase][band]
-//               folded into A as it is produced.
+//               folded into A as it is produced;
+//   MATRIX   -- the direct routing as a contraction of the row's signed
+//               trits with a 16-column matrix of the activations (one column
+//               per phase and band half), on the int8 matrix instructions.
 //
 // DIRECT mapping: a workgroup owns one 64-row tile (lane j of every
 // wavefront = row 64*tile + j, so the activation codes are uniform across a
@@ -32,6 +35,8 @@
 //
 // POPCOUNT mapping (lns8_pc_kernel below): a workgroup owns 16 rows and all
 // of K, with the state sets built once per workgroup in LDS; no workspace.
+// MATRIX mapping (lns8_mx_kernel below): the same 16 rows and all of K, the
+// activations staged once per workgroup in LDS; no workspace.
 #include "kcommon.h"
 
 namespace bs {
