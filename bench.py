@@ -65,6 +65,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 VALU_PEAK_OPS = 256 * 64 * 2.4e9   # 256 CUs x 64 int32 lane-ops per clock x 2.4 GHz
+MFMA_I8_PEAK_OPS = 5.0e15      # MI355X published dense int8 matrix rate (ops/s)
 IC_BYTES = 256 << 20           # MI355X Infinity Cache
 METRIC = "ternary GEMV weight-stream GB/s & % HBM peak, batch-1, K=2560..5120"
 # one step: the in-range per-configuration GEMVs, one launch each
@@ -578,6 +579,25 @@ def run_f1(torch, bs, synth, dev, H):
     return out
 
 
+def lns8_counter(key: str):
+    """A per-call counter mean from the LNS8 counter record under profiles/
+    (None if absent or taken on other source)."""
+    fn = os.path.join(ROOT, "profiles", "lns8_4096x4096_valu.txt")
+    if not os.path.exists(fn):
+        return None
+    vals = {}
+    for line in open(fn):
+        if ":" in line and not line.startswith("#"):
+            a, b = line.split(":", 1)
+            vals[a.strip()] = b.strip()
+    if vals.get("kernel_source_sha256_16") != _source_digest("lns8_phase.hip"):
+        return None
+    try:
+        return float(vals[key])
+    except (KeyError, ValueError):
+        return None
+
+
 def lns8_valu_ops(path: int) -> float:
     """VALU instructions per launch of the LNS8 kernel at 4096 x 4096, from
     the SQ_INSTS_VALU counter runs recorded under profiles/ (None if absent
@@ -663,6 +683,24 @@ def run_extras(torch, bs, synth, dev, H):
             ent["valu_insts_per_call"] = valu
             ent["valu_lane_ops_per_weight"] = round(valu * 64 / (4096 * 4096), 3)
             ent["frac_valu_peak"] = round(valu * 64 / (us * 1e-6) / VALU_PEAK_OPS, 4)
+        if name == "matrix":
+            # the contraction: 4096 rows x 4096 positions x 16 columns, a
+            # multiply and an add each, on the int8 matrix instructions
+            mops = 4096 * 4096 * 16 * 2
+            ent["mfma_int8_ops_per_call"] = mops
+            ent["frac_mfma_int8_peak"] = round(mops / (us * 1e-6) / MFMA_I8_PEAK_OPS, 4)
+            for key, out in (("sq_insts_valu_mfma_i8_per_call_matrix", "mfma_i8_insts_per_call"),
+                             ("sq_valu_mfma_busy_cycles_per_call_matrix",
+                              "mfma_busy_simd_cycles_per_call")):
+                v = lns8_counter(key)
+                if v is not None:
+                    ent[out] = v
+            busy = lns8_counter("sq_valu_mfma_busy_cycles_per_call_matrix")
+            if busy is not None:
+                # MFMA-busy SIMD-cycles against every SIMD over the timed call
+                # at 2.4 GHz (the profiler's own busy-cycle count per dispatch
+                # includes its serialisation, so the event time is used)
+                ent["frac_simd_cycles_mfma_busy"] = round(busy / (SIMDS * us * 1e-6 * 2.4e9), 4)
         ops["lns8_4096x4096_" + name] = ent
         log("lns8 %s: %.2f us" % (name, us))
     # pure fractional-LNS reduction of the same products, by internal
@@ -926,14 +964,14 @@ def counter_summary(*paths: str):
     return "\n".join(out)
 
 
-def lns8_valu_summary(path: str):
+def lns8_valu_summary(*paths: str):
     """The LNS8 counter record: every counter's mean per call of each path
     (lns8_kernel = direct routing, lns8_pc_kernel = popcount histogram,
-    lns8_mx_kernel = the matrix contraction) from a
-    --pmc CSV of --lns8-counter-run, keyed to the kernel source it was taken
-    on."""
+    lns8_mx_kernel = the matrix contraction) from one or more --pmc CSVs of
+    --lns8-counter-run, keyed to the kernel source it was taken on."""
     vals = {}
-    for r in csv.DictReader(open(path)):
+    rows = [r for path in paths for r in csv.DictReader(open(path))]
+    for r in rows:
         name = r["Kernel_Name"]
         if "lns8_pc_kernel" in name:
             p = "popcount"
@@ -1014,7 +1052,7 @@ def main():
                     help="run the workload of the pure-LNS --pmc runs and exit")
     ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
                     help="mean counters per kernel of --pmc CSVs, with their ratios, and exit")
-    ap.add_argument("--lns8-valu-summary", metavar="CSV",
+    ap.add_argument("--lns8-valu-summary", metavar="CSV", nargs="+",
                     help="the LNS8 counter record from a --pmc CSV of --lns8-counter-run, and exit")
     args = ap.parse_args()
     if args.trace_summary:
@@ -1036,7 +1074,7 @@ def main():
         print(counter_summary(*args.counter_summary))
         return 0
     if args.lns8_valu_summary:
-        print(lns8_valu_summary(args.lns8_valu_summary))
+        print(lns8_valu_summary(*args.lns8_valu_summary))
         return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the GEMVs would "
