@@ -94,7 +94,9 @@ SWEEP_BLOCKS = ["f1_reuse_%s_n%d" % (p, n) for p in ("ternary", "direct", "popco
 PHASE_B_BLOCKS = (["f1_zero_%s_%s" % (p, z) for p in ("direct", "popcount", "matrix")
                    for z in ("0", "1/3", "0.6", "0.9")] +
                   ["f1_codes_%s_%d" % (p, m) for p in ("direct", "popcount", "matrix")
-                   for m in (1, 8, 41, 127)])
+                   for m in (1, 8, 41, 127)] +
+                  ["f1_k_%s_%d" % (p, k) for p in ("direct", "popcount", "matrix")
+                   for k in (1024, 2048, 4096, 8192, 16384, 32768)])
 ALL_BLOCKS = BLOCKS + SHAPE_BLOCKS + SWEEP_BLOCKS + PHASE_B_BLOCKS
 MARKER_ID = {name: i + 1 for i, name in enumerate(ALL_BLOCKS)}
 # the LNS8 paths by their bs.h ids (DIRECT, POPCOUNT, MATRIX)
@@ -538,6 +540,27 @@ def run_f1(torch, bs, synth, dev, H):
             phase_b[kind][label] = ent
             del pool
             torch.cuda.empty_cache()
+    # Phase B over K: 4096 rows, K from 1024 to 32768 (the C4 distributions)
+    ksweep = {}
+    for kk in (1024, 2048, 4096, 8192, 16384, 32768):
+        t8, x8 = synth.lns8(R, kk, 0)
+        p8 = torch.from_numpy(bs.ternary_pack(t8)).to(dev)
+        pool = [p8.clone() for _ in range(-(-SHAPE_POOL_BYTES // p8.numel()))]
+        xd = torch.from_numpy(x8).to(dev)
+        acc = torch.empty((R, 8), dtype=torch.int32, device=dev)
+        ws = torch.zeros(bs.lib().bs_lns8_workspace_bytes(R, kk), dtype=torch.uint8, device=dev)
+        ent = {}
+        for path, name in LNS8_PATHS:
+            us = H.per_launch(lambda i: bs.lns8_phase_gemv(pool[i % len(pool)], xd, R, kk, path,
+                                                           acc=acc, s=False, workspace=ws,
+                                                           stream=H.stream),
+                              len(pool), block="f1_k_%s_%d" % (name, kk))
+            ent[name + "_us"] = round(us, 3)
+            ent[name + "_weights_per_ns"] = round(R * kk / us / 1e3, 1)
+        ksweep[str(kk)] = ent
+        del pool
+        torch.cuda.empty_cache()
+    phase_b["k_rows4096"] = ksweep
     out["lns8_phase_b_4096x4096"] = phase_b
     # shared-activation fusion: the layer as four launches (q|k|v and gate|up
     # stored concatenated by rows; o and down add into the residual stream)
