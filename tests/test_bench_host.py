@@ -125,15 +125,34 @@ def test_lns8_valu_record_round_trip(tmp_path, monkeypatch):
     rows.append({"Kernel_Name": "void at::native::other", "Counter_Name": "SQ_INSTS_VALU",
                  "Counter_Value": 5.0})
     _write(tmp_path / "c.csv", fields, rows)
+    # a second pass (the MFMA counters) merges into the same record
+    mfma = [{"Kernel_Name": "void bs::(anonymous namespace)::lns8_mx_kernel(args)",
+             "Counter_Name": c, "Counter_Value": v}
+            for c, v in (("SQ_INSTS_VALU_MFMA_I8", 16384), ("SQ_VALU_MFMA_BUSY_CYCLES", 262144))]
+    _write(tmp_path / "m.csv", fields, mfma)
     (tmp_path / "profiles").mkdir()
     (tmp_path / "profiles" / "lns8_4096x4096_valu.txt").write_text(
-        "# header\n" + bench.lns8_valu_summary(str(tmp_path / "c.csv")) + "\n")
+        "# header\n" + bench.lns8_valu_summary(str(tmp_path / "c.csv"), str(tmp_path / "m.csv"))
+        + "\n")
     assert bench.lns8_valu_ops(0) == pytest.approx(1001.0)
     assert bench.lns8_valu_ops(1) == pytest.approx(701.0)
     assert bench.lns8_valu_ops(2) == pytest.approx(401.0)
+    assert bench.lns8_counter("sq_insts_valu_mfma_i8_per_call_matrix") == 16384
+    assert bench.lns8_counter("sq_valu_mfma_busy_cycles_per_call_matrix") == 262144
+    assert bench.lns8_counter("sq_valu_mfma_busy_cycles_per_call_direct") is None
     with open(tmp_path / "bit_decode_gemv_amd" / "csrc" / "lns8_phase.hip", "a") as f:
         f.write("\n// edit\n")
     assert bench.lns8_valu_ops(0) is None
+    assert bench.lns8_counter("sq_insts_valu_mfma_i8_per_call_matrix") is None
+
+
+def test_marker_blocks_cover_the_sweeps():
+    """Every block the benchmark marks has an id: the K sweep of Phase B and
+    the concurrent step included."""
+    for p in ("direct", "popcount", "matrix"):
+        for k in (1024, 2048, 4096, 8192, 16384, 32768):
+            assert "f1_k_%s_%d" % (p, k) in bench.MARKER_ID
+    assert "concurrent_step" in bench.MARKER_ID
 
 
 def test_flns_valu_record_round_trip(tmp_path, monkeypatch):
