@@ -202,9 +202,23 @@ def packed_pool(torch, bs, synth, dev, rows, k, min_bytes, seed=0, max_copies=No
     n = max(2, -(-min_bytes // base.numel()))
     if max_copies:
         n = min(n, max_copies)
-    bufs = [base.clone() for _ in range(n)]
+    bufs = carve_copies(torch, base, n, dev)
     views = [(b[:pl.size], b[pl.size:].view(torch.int16)) for b in bufs]
     return bufs, views, torch.from_numpy(x).to(dev), base.numel()
+
+
+def carve_copies(torch, base, n, dev):
+    """n copies of a uint8 device tensor, each 4 KiB-aligned inside one
+    allocation (a model's weights sit in one allocation too; separate
+    allocations per copy measured about 1 % slower on first touch)."""
+    stride = -(-base.numel() // 4096) * 4096
+    big = torch.empty(stride * n, dtype=torch.uint8, device=dev)
+    out = []
+    for i in range(n):
+        b = big[i * stride:i * stride + base.numel()]
+        b.copy_(base)
+        out.append(b)
+    return out
 
 
 # ---------------------------------------------------------------- CPU side
@@ -371,13 +385,11 @@ def run_step(torch, bs, synth, dev, H, steps, warmup):
         xs[k] = torch.from_numpy(x).to(dev) if k not in xs else xs[k]
         ys[name] = torch.empty(rows, dtype=torch.int64, device=dev)
         del t
-    sets = []
-    for _ in range(n_sets):
-        s = {}
-        for name, rows, k in STEP:
-            b = bases[name][0].clone()
-            s[name] = (b[:bases[name][1]], b[bases[name][1]:].view(torch.int16))
-        sets.append(s)
+    # every weight set in one allocation, each buffer 4 KiB-aligned
+    copies = {name: carve_copies(torch, bases[name][0], n_sets, dev) for name, _, _ in STEP}
+    sets = [{name: (copies[name][i][:bases[name][1]],
+                    copies[name][i][bases[name][1]:].view(torch.int16)) for name, _, _ in STEP}
+            for i in range(n_sets)]
 
     def step(i):
         s = sets[i % n_sets]
@@ -416,7 +428,7 @@ def run_step(torch, bs, synth, dev, H, steps, warmup):
            "before_timed_region": "graph upload replay, then a 512 MB read of another buffer "
                                   "(evicts the L2s and the Infinity Cache)"}
     H.concurrent = concurrent_step(torch, bs, H, sets, xs, ys, step_bytes, steps)
-    del sets, bases
+    del sets, bases, copies
     torch.cuda.empty_cache()
     return value, us / steps / 1000.0, cfg
 
