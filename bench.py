@@ -1159,7 +1159,7 @@ def main():
         print(lns8_valu_summary(*args.lns8_valu_summary))
         return 0
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the GEMVs would "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the GEMVs would "
               "shard by rows with one all-gather, or by K with one int64 all-reduce); "
               "run with --gpus 1", file=sys.stderr)
         return 2
