@@ -468,15 +468,17 @@ def concurrent_step(torch, bs, H, sets, xs, ys, step_bytes, steps, nstreams=4):
     H.marker("concurrent_step")
     g = H.graph(step, steps)
     H.replay_us(g)                              # upload
-    us, _ = H.replay_us(g, scrub=True)
+    reps = sorted(H.replay_us(g, scrub=True)[0] / steps for _ in range(3))
     del g
-    log("concurrent step (%d branches): %.2f us" % (nstreams, us / steps))
-    return {"us_per_step": round(us / steps, 3),
-            "GBps": round(step_bytes * steps / (us * 1e-6) / 1e9, 1),
+    us = reps[1]
+    log("concurrent step (%d branches): %.2f us (of %s)" % (nstreams, us, reps))
+    return {"us_per_step": round(us, 3), "us_per_step_min_max": [round(reps[0], 3),
+                                                                round(reps[2], 3)],
+            "GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
             "branches": {name: assign[name] for name, _, _ in STEP},
             "note": "the headline's eight unfused bs_ternary_gemv launches as independent "
-                    "graph branches on %d streams, joined after every step; not the headline"
-                    % nstreams}
+                    "graph branches on %d streams, joined after every step; median of three "
+                    "replays; not the headline" % nstreams}
 
 
 def run_shapes(torch, bs, synth, dev, H):
