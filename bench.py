@@ -336,13 +336,15 @@ def _oracle_per_config(cores):
 # ------------------------------------------------------ records under profiles/
 
 def _source_digest(kernel_file="ternary_gemv.hip"):
-    """Digest of a kernel's source: its file and the headers it includes
-    (shared device helpers, status codes, the ABI header)."""
+    """Digest of a kernel's source: its file, the headers it includes
+    (shared device helpers, status codes, the ABI header) and the build
+    script that holds the compiler flags."""
     h = hashlib.sha256()
     for rel in (("bit_decode_gemv_amd", "csrc", kernel_file),
                 ("bit_decode_gemv_amd", "csrc", "kcommon.h"),
                 ("bit_decode_gemv_amd", "csrc", "bs_internal.h"),
-                ("include", "bs.h")):
+                ("include", "bs.h"),
+                ("bit_decode_gemv_amd", "build.py")):
         with open(os.path.join(ROOT, *rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -91,7 +91,8 @@ def test_source_digest_covers_included_headers(tmp_path, monkeypatch):
     for rel in (("bit_decode_gemv_amd", "csrc", "ternary_gemv.hip"),
                 ("bit_decode_gemv_amd", "csrc", "kcommon.h"),
                 ("bit_decode_gemv_amd", "csrc", "bs_internal.h"),
-                ("include", "bs.h")):
+                ("include", "bs.h"),
+                ("bit_decode_gemv_amd", "build.py")):
         dst = tmp_path.joinpath(*rel)
         dst.parent.mkdir(parents=True, exist_ok=True)
         shutil.copy(os.path.join(bench.ROOT, *rel), dst)
@@ -100,6 +101,11 @@ def test_source_digest_covers_included_headers(tmp_path, monkeypatch):
     with open(tmp_path / "bit_decode_gemv_amd" / "csrc" / "kcommon.h", "a") as f:
         f.write("\n// edit\n")
     assert bench._source_digest() != before
+    # so is a change of the compiler flags
+    after_header = bench._source_digest()
+    with open(tmp_path / "bit_decode_gemv_amd" / "build.py", "a") as f:
+        f.write("\n# edit\n")
+    assert bench._source_digest() != after_header
 
 
 def test_lns8_valu_record_round_trip(tmp_path, monkeypatch):
@@ -109,7 +115,8 @@ def test_lns8_valu_record_round_trip(tmp_path, monkeypatch):
     for rel in (("bit_decode_gemv_amd", "csrc", "lns8_phase.hip"),
                 ("bit_decode_gemv_amd", "csrc", "kcommon.h"),
                 ("bit_decode_gemv_amd", "csrc", "bs_internal.h"),
-                ("include", "bs.h")):
+                ("include", "bs.h"),
+                ("bit_decode_gemv_amd", "build.py")):
         dst = tmp_path.joinpath(*rel)
         dst.parent.mkdir(parents=True, exist_ok=True)
         shutil.copy(os.path.join(bench.ROOT, *rel), dst)
@@ -163,7 +170,8 @@ def test_flns_valu_record_round_trip(tmp_path, monkeypatch):
     for rel in (("bit_decode_gemv_amd", "csrc", "flns_phase.hip"),
                 ("bit_decode_gemv_amd", "csrc", "kcommon.h"),
                 ("bit_decode_gemv_amd", "csrc", "bs_internal.h"),
-                ("include", "bs.h")):
+                ("include", "bs.h"),
+                ("bit_decode_gemv_amd", "build.py")):
         dst = tmp_path.joinpath(*rel)
         dst.parent.mkdir(parents=True, exist_ok=True)
         shutil.copy(os.path.join(bench.ROOT, *rel), dst)
