@@ -541,8 +541,21 @@ __device__ __forceinline__ void hist_edge(const unsigned *hist, unsigned want,
 }
 
 // ----------------------------------------------------------------- select
-__global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles, int nwg,
-                                                            int top_k, int cap, LmhWs ws) {
+// The tail kernels take the workspace arrays (and sizes) they read first as
+// leading arguments: the first 14 argument dwords are preloaded into scalar
+// registers at wave launch, where the fields of the struct argument are
+// loaded from memory.
+__global__ __launch_bounds__(kBlockThreads) void lmh_select(
+    const long long *__restrict__ tile_max, const long long *__restrict__ tile_max_s1,
+    const long long *__restrict__ wg_max, long long *__restrict__ scalars,
+    const long long *__restrict__ lower, int vocab, int tiles, int nwg, int top_k, int cap,
+    LmhWs wsk) {
+    LmhWs ws = wsk;
+    ws.tile_max = const_cast<long long *>(tile_max);
+    ws.tile_max_s1 = const_cast<long long *>(tile_max_s1);
+    ws.wg_max = const_cast<long long *>(wg_max);
+    ws.scalars = scalars;
+    ws.lower = const_cast<long long *>(lower);
     __shared__ SelShared sh;
     __shared__ unsigned long long list[kSelList];
     __shared__ int tlist[kSelTiles];
@@ -706,10 +719,13 @@ __global__ __launch_bounds__(kBlockThreads) void lmh_select(int vocab, int tiles
 // with S1' >= T1 are rescored and go to slots [256 * blockIdx.x,
 // 256 * blockIdx.x + kept), sorted by (S1' desc, row asc); the number of
 // candidates goes to region_count[blockIdx.x], kept to region_kept.
-__global__ __launch_bounds__(kFilterRows) void lmh_filter(const uint8_t *__restrict__ planes47,
-                                                          const int32_t *__restrict__ row_scale,
-                                                          const int8_t *__restrict__ h,
-                                                          int vocab, int groups, LmhWs ws) {
+__global__ __launch_bounds__(kFilterRows) void lmh_filter(
+    const long long *__restrict__ scalars, const int *__restrict__ e1p,
+    const uint8_t *__restrict__ planes47, const int32_t *__restrict__ row_scale,
+    const int8_t *__restrict__ h, int vocab, int groups, LmhWs wsk) {
+    LmhWs ws = wsk;
+    ws.scalars = const_cast<long long *>(scalars);
+    ws.e1 = const_cast<int *>(e1p);
     __shared__ uint4 hs[kMaxGroups * 8];   // h, 16 positions per entry
     __shared__ int rowtab[4][64];
     __shared__ int e2l[4][64];
@@ -1001,10 +1017,21 @@ __device__ __forceinline__ void output_by_rank(int m, int top_k, const long long
     }
 }
 
-__global__ __launch_bounds__(kBlockThreads) void lmh_finish(int vocab, int nwf, int top_k,
-                                                            int cap, int32_t *__restrict__ top_idx,
-                                                            int64_t *__restrict__ top_score,
-                                                            int32_t *__restrict__ info, LmhWs ws) {
+__global__ __launch_bounds__(kBlockThreads) void lmh_finish(
+    const long long *__restrict__ region_umax, const int *__restrict__ region_kept,
+    const int *__restrict__ region_count, int nwf, int vocab,
+    const long long *__restrict__ cand_s1, const long long *__restrict__ cand_s,
+    const long long *__restrict__ cand_u, const int *__restrict__ cand, int top_k, int cap,
+    int32_t *__restrict__ top_idx, int64_t *__restrict__ top_score, int32_t *__restrict__ info,
+    LmhWs wsk) {
+    LmhWs ws = wsk;
+    ws.region_umax = const_cast<long long *>(region_umax);
+    ws.region_kept = const_cast<int *>(region_kept);
+    ws.region_count = const_cast<int *>(region_count);
+    ws.cand_s1 = const_cast<long long *>(cand_s1);
+    ws.cand_s = const_cast<long long *>(cand_s);
+    ws.cand_u = const_cast<long long *>(cand_u);
+    ws.cand = const_cast<int *>(cand);
     __shared__ SelShared sh;
     __shared__ long long tk[kMaxCap];
     __shared__ int ti[kMaxCap];
@@ -1551,14 +1578,16 @@ static int32_t lmh_launch(const uint8_t *planes03, const uint8_t *planes47,
     hipLaunchKernelGGL(lmh_stage1, dim3(L.nwg), dim3(kStage1Threads), 0, st, planes03, row_scale,
                        reinterpret_cast<const int32_t *>(h), (int)vocab, groups, ws);
     BS_LAUNCH_CHECK();
-    hipLaunchKernelGGL(lmh_select, dim3(1), dim3(kBlockThreads), 0, st, (int)vocab, L.tiles, L.nwg,
+    hipLaunchKernelGGL(lmh_select, dim3(1), dim3(kBlockThreads), 0, st, ws.tile_max,
+                       ws.tile_max_s1, ws.wg_max, ws.scalars, ws.lower, (int)vocab, L.tiles, L.nwg,
                        top_k, max_candidates, ws);
     BS_LAUNCH_CHECK();
-    hipLaunchKernelGGL(lmh_filter, dim3((unsigned)L.nwf), dim3(kFilterRows), 0, st, planes47,
-                       row_scale, h, (int)vocab, groups, ws);
+    hipLaunchKernelGGL(lmh_filter, dim3((unsigned)L.nwf), dim3(kFilterRows), 0, st, ws.scalars,
+                       ws.e1, planes47, row_scale, h, (int)vocab, groups, ws);
     BS_LAUNCH_CHECK();
-    hipLaunchKernelGGL(lmh_finish, dim3(1), dim3(kBlockThreads), 0, st, (int)vocab, L.nwf, top_k,
-                       max_candidates, top_idx, top_score, info, ws);
+    hipLaunchKernelGGL(lmh_finish, dim3(1), dim3(kBlockThreads), 0, st, ws.region_umax,
+                       ws.region_kept, ws.region_count, L.nwf, (int)vocab, ws.cand_s1, ws.cand_s,
+                       ws.cand_u, ws.cand, top_k, max_candidates, top_idx, top_score, info, ws);
     BS_LAUNCH_CHECK();
     return BS_OK;
 }
